@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module only draws random tensors with the shapes and distributions of the
+workloads; it contains none of the layer's arithmetic, so the GPU path and the
+fp64 oracle can both be fed from it without sharing any computation.
+
+Distributions (per-token tensors are [B,T,H,d], states [B,H,dk,dv]):
+  Gated DeltaNet: q, k ~ N(0,1) then L2-normalised per (token, head);
+                  v ~ N(0,1); beta = sigmoid(N(0,1)); g = log alpha = -softplus(N(0,1));
+                  S_in = 0.1 * N(0,1); dO ~ N(0,1); dS_out ~ N(0,1).
+  GLA:            q, k, v ~ N(0,1); g = logsigmoid(N(0,1)) / 16 per key channel;
+                  S_in = 0.1 * N(0,1); dO ~ N(0,1); dS_out ~ N(0,1).
+Draw order: q, k, v, g, beta (GDN only), S_in, dO, dS_out, all float32 from a
+numpy PCG64 generator.  For dtype "bf16" every per-token tensor (including dO)
+is rounded to bfloat16 (round-to-nearest-even) and returned as the exact
+float32 value of that bfloat16; states stay float32.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Workloads (name -> parameters).  "N" is the number of sequence chunks the
+# sequence is split into with boundary-state hand-off.
+CONFIGS = {
+    "gdn_fp32_T256_d32": dict(kind="gdn", dtype="fp32", B=1, H=1, T=256, dk=32, dv=32, N=4),
+    "gdn_bf16_H16_T8192_d128": dict(kind="gdn", dtype="bf16", B=1, H=16, T=8192, dk=128, dv=128, N=4),
+    "gla_bf16_B4_H16_T4096_dk128_dv256": dict(kind="gla", dtype="bf16", B=4, H=16, T=4096, dk=128, dv=256, N=1),
+    "gdn_bf16_H32_T65536_d128": dict(kind="gdn", dtype="bf16", B=1, H=32, T=65536, dk=128, dv=128, N=16),
+    "gdn_bf16_H16_T262144_d128": dict(kind="gdn", dtype="bf16", B=1, H=16, T=262144, dk=128, dv=128, N=64),
+}
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+    NaN stays NaN."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    nan = np.isnan(x)
+    out = rounded.astype(np.uint16)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> exact float32 values."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    return bf16_value(bf16_bits(x))
+
+
+def _sigmoid(x):
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+def _softplus(x):
+    x = x.astype(np.float64)
+    return (np.maximum(x, 0) + np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
+
+
+def _l2n(x):
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (x / np.maximum(n, 1e-12)).astype(np.float32)
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def make_gdn(B, T, H, dk, dv, dtype="fp32", seed=0, slow_decay=False):
+    """Gated DeltaNet inputs.  slow_decay=True draws g = -softplus(N(0,1))/64
+    (a stress case where the state survives for ~100 tokens)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _l2n(_normal(rng, (B, T, H, dk)))
+    k = _l2n(_normal(rng, (B, T, H, dk)))
+    v = _normal(rng, (B, T, H, dv))
+    g = -_softplus(_normal(rng, (B, T, H)))
+    if slow_decay:
+        g = (g / 64.0).astype(np.float32)
+    beta = _sigmoid(_normal(rng, (B, T, H)))
+    S_in = (0.1 * _normal(rng, (B, H, dk, dv))).astype(np.float32)
+    dO = _normal(rng, (B, T, H, dv))
+    dS_out = _normal(rng, (B, H, dk, dv))
+    d = dict(q=q, k=k, v=v, g=g, beta=beta, S_in=S_in, dO=dO, dS_out=dS_out)
+    if dtype == "bf16":
+        for key in ("q", "k", "v", "g", "beta", "dO"):
+            d[key] = bf16_round(d[key])
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return d
+
+
+def make_gla(B, T, H, dk, dv, dtype="bf16", seed=0, gate_scale=1.0 / 16.0):
+    """GLA inputs.  gate_scale=1 gives the strong-gate stress case."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _normal(rng, (B, T, H, dk))
+    k = _normal(rng, (B, T, H, dk))
+    v = _normal(rng, (B, T, H, dv))
+    z = _normal(rng, (B, T, H, dk)).astype(np.float64)
+    logsig = -(np.maximum(-z, 0) + np.log1p(np.exp(-np.abs(z))))
+    g = (logsig * gate_scale).astype(np.float32)
+    S_in = (0.1 * _normal(rng, (B, H, dk, dv))).astype(np.float32)
+    dO = _normal(rng, (B, T, H, dv))
+    dS_out = _normal(rng, (B, H, dk, dv))
+    d = dict(q=q, k=k, v=v, g=g, S_in=S_in, dO=dO, dS_out=dS_out)
+    if dtype == "bf16":
+        for key in ("q", "k", "v", "g", "dO"):
+            d[key] = bf16_round(d[key])
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return d
+
+
+def make(cfg: dict, seed: int, **kw):
+    f = make_gdn if cfg["kind"] == "gdn" else make_gla
+    return f(cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], cfg["dtype"], seed, **kw)
