@@ -1,0 +1,157 @@
+// clr_device.h -- device-side building blocks for the gfx950 (CDNA4) kernels.
+//
+// Matrix products use the wave64 matrix cores through one abstraction: a
+// "k32 step" multiplies a 16 x 32 A tile by a 32 x 16 B tile into a 16 x 16
+// fp32 accumulator tile.
+//
+//   lane l, r = l & 15, g = l >> 4 (0..3)
+//   accumulator (D) tile:  lane holds D[4g + i][r],            i = 0..3
+//   A fragment:            lane holds A[r][kmap(g, i)],        i = 0..7
+//   B fragment:            lane holds B[kmap(g, i)][r],        i = 0..7
+//   kmap(g, i) = 4g + i for i < 4,  16 + 4g + (i - 4) for i >= 4.
+//
+// The k ordering inside an MFMA is immaterial as long as A and B agree, and
+// this kmap makes two vertically adjacent accumulator tiles (rows 0..15 and
+// 16..31 of a 32-row block) *exactly* a B fragment, and the transpose of an
+// A fragment.  Chained products therefore stay in registers.
+//
+// bf16 elements use v_mfma_f32_16x16x32_bf16 (one instruction per k32 step);
+// fp32 elements use eight v_mfma_f32_16x16x4_f32 (lane group g supplies k
+// slot g of each).  Accumulation is fp32 in both cases.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace clr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BLK = 64;  // tokens per kernel-level block (chunk)
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename E> __device__ __forceinline__ E from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---------------------------------------------------------------------------
+// Fragments
+// ---------------------------------------------------------------------------
+template <typename E> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+// Four contiguous elements <-> f32x4.
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 ld4(const bf16* p) {
+    bf16x4 t = *(const bf16x4*)p;
+    return f32x4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *(f32x4*)p = v; }
+__device__ __forceinline__ void st4(bf16* p, f32x4 v) {
+    bf16x4 t;
+    t[0] = (bf16)v[0]; t[1] = (bf16)v[1]; t[2] = (bf16)v[2]; t[3] = (bf16)v[3];
+    *(bf16x4*)p = t;
+}
+
+// A fragment from a row-major tile whose k index is contiguous:
+// p points at X[m0 + r][k0 + 4g]; the second half is 16 elements further.
+__device__ __forceinline__ Frag<bf16> ldfrag(const bf16* p) {
+    Frag<bf16> f;
+    bf16x4 a = *(const bf16x4*)p;
+    bf16x4 b = *(const bf16x4*)(p + 16);
+    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+__device__ __forceinline__ Frag<float> ldfrag(const float* p) {
+    Frag<float> f;
+    f.lo = *(const f32x4*)p;
+    f.hi = *(const f32x4*)(p + 16);
+    return f;
+}
+// ldfrag of row `row` of a token-major tile (row stride ld), zero if the
+// row lies past the end of the sequence (row >= nvalid).
+template <typename E>
+__device__ __forceinline__ Frag<E> ldfrag_row(const E* base, int row, int nvalid, size_t ld, int col) {
+    if (row < nvalid) return ldfrag(base + (size_t)row * ld + col);
+    Frag<E> f;
+    if constexpr (sizeof(E) == 2) {
+        f.v = bf16x8{};
+    } else {
+        f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+        f.hi = f.lo;
+    }
+    return f;
+}
+
+// A fragment whose elements are scaled by s[i] (per k index) before rounding.
+__device__ __forceinline__ Frag<bf16> ldfrag_scaled(const bf16* p, f32x4 slo, f32x4 shi) {
+    f32x4 a = ld4(p), b = ld4(p + 16);
+    Frag<bf16> f;
+    f.v = bf16x8{(bf16)(a[0] * slo[0]), (bf16)(a[1] * slo[1]), (bf16)(a[2] * slo[2]), (bf16)(a[3] * slo[3]),
+                 (bf16)(b[0] * shi[0]), (bf16)(b[1] * shi[1]), (bf16)(b[2] * shi[2]), (bf16)(b[3] * shi[3])};
+    return f;
+}
+__device__ __forceinline__ Frag<float> ldfrag_scaled(const float* p, f32x4 slo, f32x4 shi) {
+    Frag<float> f;
+    f.lo = ld4(p) * slo;
+    f.hi = ld4(p + 16) * shi;
+    return f;
+}
+
+// B fragment (or transposed A fragment) from two vertically adjacent
+// accumulator tiles: rows 0..15 in lo, rows 16..31 in hi.
+template <typename E> __device__ __forceinline__ Frag<E> frag_from_acc(f32x4 lo, f32x4 hi);
+template <> __device__ __forceinline__ Frag<bf16> frag_from_acc<bf16>(f32x4 lo, f32x4 hi) {
+    Frag<bf16> f;
+    f.v = bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+                 (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> frag_from_acc<float>(f32x4 lo, f32x4 hi) {
+    Frag<float> f;
+    f.lo = lo;
+    f.hi = hi;
+    return f;
+}
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[0], b.lo[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[1], b.lo[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[2], b.lo[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[3], b.lo[3], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[0], b.hi[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[1], b.hi[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane order).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    const int l = lane_id();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float y = __shfl_up(x, off, 64);
+        if (l >= off) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+}  // namespace clr

@@ -1,0 +1,114 @@
+// clr_kernels.h -- kernel argument blocks and host launchers (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "clr_device.h"
+
+namespace clr {
+
+// Head sizes (dk, dv) instantiated for the delta-rule kernels.
+#define CLR_FOR_GDN_SHAPES(E) \
+    CLR_CASE(E, 32, 32)       \
+    CLR_CASE(E, 64, 64)       \
+    CLR_CASE(E, 128, 128)
+
+// Workspace of the Gated DeltaNet path.  Block-major: index
+// ((b * H + h) * NC + n) selects the 64-token block n of head h in batch b.
+struct GdnWs {
+    float* gam;   // [.., 64]       in-block cumulative log gate
+    void* W;      // [.., 64, dk]   W = T Diag(beta Gam) K           (token-major)
+    void* KhT;    // [.., dk, 64]   (Diag(exp(gamma_C - gamma)) K)^T
+    void* UtT;    // [.., dv, 64]   (T Diag(beta) V)^T
+    void* hT;     // [.., dv, dk]   state entering the block, transposed
+    void* UT;     // [.., dv, 64]   U^T (delta-rule new values)
+    // backward only
+    void* QgT;    // [.., dk, 64]   (Diag(Gam) Q)^T
+    void* WT;     // [.., dk, 64]   W^T
+    void* Kh;     // [.., 64, dk]   Diag(exp(gamma_C - gamma)) K      (token-major)
+    void* dOT;    // [.., dv, 64]   dO^T
+    void* dvlT;   // [.., dv, 64]   ((Q K^T * G * tril)^T dO)^T
+    void* dhT;    // [.., dv, dk]   gradient w.r.t. the state leaving the block, transposed
+    void* dUT;    // [.., dv, 64]   dU^T
+};
+
+struct GdnLaunch {
+    int B, T, H, NC, dk, dv;
+    bool bf16;
+    const void *q, *k, *v, *g, *beta;
+    const float* S_in;
+    void* o;
+    float* S_out;
+    // backward
+    const void* dO;
+    const float* dS_out;
+    void *dq, *dk_, *dv_, *dg, *dbeta;
+    float* dS_in;
+    GdnWs ws;
+};
+
+template <typename E> struct GdnPrepArgs {
+    const E *k, *v, *g, *beta;
+    int T, H, NC;
+    float* gam;
+    E *W, *KhT, *UtT;
+};
+
+template <typename E> struct GdnScanArgs {
+    const float* gam;
+    const E *W, *KhT, *UtT;
+    const float* S_in;
+    float* S_out;
+    E *hT, *UT;
+    int H, NC;
+};
+
+template <typename E> struct GdnOutArgs {
+    const E *q, *k;
+    const float* gam;
+    const E *hT, *UT;
+    E* o;
+    int T, H, NC;
+};
+
+hipError_t launch_gdn_fwd(const GdnLaunch& L, hipStream_t st);
+hipError_t launch_gdn_bwd(const GdnLaunch& L, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// GLA
+// ---------------------------------------------------------------------------
+#define CLR_FOR_GLA_SHAPES(E) \
+    CLR_CASE(E, 32, 32)       \
+    CLR_CASE(E, 64, 64)       \
+    CLR_CASE(E, 128, 128)     \
+    CLR_CASE(E, 128, 256)
+
+struct GlaWs {
+    float* bcum;  // [.., 64, dk]  in-block cumulative log gate per channel
+    void* hT;     // [.., dv, dk]  state entering the block, transposed
+    void* dhT;    // [.., dv, dk]  gradient w.r.t. the state leaving the block, transposed
+};
+
+struct GlaLaunch {
+    int B, T, H, NC, dk, dv;
+    bool bf16;
+    const void *q, *k, *v, *g;
+    const float* S_in;
+    void* o;
+    float* S_out;
+    const void* dO;
+    const float* dS_out;
+    void *dq, *dk_, *dv_, *dg;
+    float* dS_in;
+    GlaWs ws;
+};
+
+hipError_t launch_gla_fwd(const GlaLaunch& L, hipStream_t st);
+hipError_t launch_gla_bwd(const GlaLaunch& L, hipStream_t st);
+
+// Probe of the fragment abstraction: C[16][16] = A[16][32] * Bt[16][32]^T
+// (dtype 0 = fp32, 1 = bf16), computed with ldfrag/mma.
+hipError_t launch_probe_mma(int bf16, const void* A, const void* Bt, float* C, hipStream_t st);
+
+}  // namespace clr

@@ -1,0 +1,194 @@
+"""Thin ctypes binding of ``libclr.so`` (the C ABI declared in include/clr.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels.
+Tensors are torch tensors on the GPU (torch supplies device memory and the
+current stream); the functions allocate the outputs and the workspace and
+enqueue one library call on ``torch.cuda.current_stream()``.
+
+If the library is missing, loading raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libclr.so")
+
+CLR_OK, CLR_EINVAL, CLR_ENOTSUP, CLR_EWORKSPACE, CLR_EHIP = range(5)
+CLR_F32, CLR_BF16 = 0, 1
+OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD = range(4)
+
+
+class ClrShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class ClrError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libclr.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError(f"{p} not found: build it with `python -m chunked_linear_recurrence_chunk_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    sp = ctypes.POINTER(ClrShape)
+    lib.clr_workspace_bytes.argtypes = [sp, i]
+    lib.clr_workspace_bytes.restype = sz
+    for name in ("gdn_fwd", "gla_fwd"):
+        f = getattr(lib, name)
+        f.argtypes = [sp] + [vp] * 9 + [sz, vp]
+        f.restype = i
+    for name in ("gdn_bwd", "gla_bwd"):
+        f = getattr(lib, name)
+        f.argtypes = [sp] + [vp] * 15 + [sz, vp]
+        f.restype = i
+    lib.clr_status_string.argtypes = [i]
+    lib.clr_status_string.restype = ctypes.c_char_p
+    lib.clr_version.argtypes = []
+    lib.clr_version.restype = i
+    lib.clr_probe_mma.argtypes = [i, vp, vp, vp, vp]
+    lib.clr_probe_mma.restype = i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(s: int) -> str:
+    return load().clr_status_string(int(s)).decode()
+
+
+def _check(fn, rc):
+    if rc != CLR_OK:
+        raise ClrError(fn, rc, status_string(rc))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CLR_BF16
+    if t.dtype == torch.float32:
+        return CLR_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_shape(q, v, dtype_code=None) -> ClrShape:
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    return ClrShape(B, T, H, dk, dv, _dtype_code(q) if dtype_code is None else dtype_code)
+
+
+def workspace_bytes(shape: ClrShape, op: int) -> int:
+    return int(load().clr_workspace_bytes(ctypes.byref(shape), op))
+
+
+def _workspace(shape, op, device):
+    import torch
+    n = workspace_bytes(shape, op)
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+
+
+def _check_inputs(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _fwd(name, op, q, k, v, g, beta, S_in, want_state, ws):
+    import torch
+    _check_inputs(q, k, v, g, beta, S_in)
+    shape = make_shape(q, v)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
+    if ws is None:
+        ws, n = _workspace(shape, op, q.device)
+    else:
+        n = ws.numel()
+    rc = getattr(load(), name)(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(S_in), _ptr(o), _ptr(S_out), _ptr(ws), n, _stream())
+    _check(name, rc)
+    return o, S_out
+
+
+def gdn_fwd(q, k, v, g, beta, S_in=None, want_state=True, ws=None):
+    """Gated DeltaNet chunk forward.  Returns (o, S_out)."""
+    return _fwd("gdn_fwd", OP_GDN_FWD, q, k, v, g, beta, S_in, want_state, ws)
+
+
+def gla_fwd(q, k, v, g, S_in=None, want_state=True, ws=None):
+    """GLA chunk forward (per-key-channel gate g).  Returns (o, S_out)."""
+    return _fwd("gla_fwd", OP_GLA_FWD, q, k, v, g, None, S_in, want_state, ws)
+
+
+def _bwd(name, op, q, k, v, g, beta, S_in, dO, dS_out, ws):
+    import torch
+    _check_inputs(q, k, v, g, beta, S_in, dO, dS_out)
+    shape = make_shape(q, v)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(g)
+    dbeta = torch.empty_like(beta) if beta is not None else None
+    dS_in = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws, n = _workspace(shape, op, q.device)
+    else:
+        n = ws.numel()
+    rc = getattr(load(), name)(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(S_in), _ptr(dO), _ptr(dS_out), _ptr(dq), _ptr(dk_), _ptr(dv_),
+                               _ptr(dg), _ptr(dbeta), _ptr(dS_in), _ptr(ws), n, _stream())
+    _check(name, rc)
+    r = dict(dq=dq, dk=dk_, dv=dv_, dg=dg, dS_in=dS_in)
+    if dbeta is not None:
+        r["dbeta"] = dbeta
+    return r
+
+
+def gdn_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, ws=None):
+    """Gated DeltaNet chunk backward.  Returns dict dq, dk, dv, dg, dbeta, dS_in."""
+    return _bwd("gdn_bwd", OP_GDN_BWD, q, k, v, g, beta, S_in, dO, dS_out, ws)
+
+
+def gla_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None):
+    """GLA chunk backward.  Returns dict dq, dk, dv, dg, dS_in."""
+    return _bwd("gla_bwd", OP_GLA_BWD, q, k, v, g, None, S_in, dO, dS_out, ws)
+
+
+def probe_mma(A, Bt):
+    """C = A @ Bt.T (16x32 each) through the kernels' fragment layout, plus the
+    same product through the accumulator-chaining path (rows 16..31 of C)."""
+    import torch
+    _check_inputs(A, Bt)
+    C = torch.empty((32, 16), dtype=torch.float32, device=A.device)
+    rc = load().clr_probe_mma(_dtype_code(A), _ptr(A), _ptr(Bt), _ptr(C), _stream())
+    _check("clr_probe_mma", rc)
+    return C

@@ -1,0 +1,136 @@
+/*
+ * clr.h -- C ABI of the chunked gated linear recurrence layer for AMD MI355X
+ * (gfx950).  Hand-written HIP kernels; plain pointers and sizes only.
+ *
+ * The operations
+ * --------------
+ * A sequence chunk of T tokens is processed with an incoming boundary state
+ * and produces the outgoing one, as in the chunk forward / backward of the
+ * StateFlow paper ("StateFlow: Sequence Pipeline Parallelism for Long-Context
+ * Modeling with Linear Recurrence", Sec. 3.1, "Forward Computation" and
+ * "Backward Computation"):
+ *     fwd:  (o, S_out)            = Fwd(q, k, v, g, beta; S_in)
+ *     bwd:  (dq, dk, dv, dg, dbeta, dS_in)
+ *                                 = Bwd(q, k, v, g, beta, S_in; dO, dS_out)
+ * so that feeding S_out of chunk i as S_in of chunk i+1, and dS_in of chunk
+ * i+1 as dS_out of chunk i, reproduces the unchunked sequence (the boundary
+ * chains S_{i+1}^in = S_i^out and dS_i^out = dS_{i+1}^in of the same paper).
+ *
+ * The recurrence is the matrix-state family of that paper's Sec. 2.1 (Eq. 1)
+ * with its Gated DeltaNet and Gated Linear Attention transitions, written with
+ * a key-major state S in R^{dk x dv} per (batch, head):
+ *     GDN:  S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     GLA:  S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T      (alpha_t in R^dk)
+ *     both: o_t = S_t^T q_t,   alpha_t = exp(g_t),  g = log alpha (<= 0).
+ * No query scaling is applied.  The gradients are those of
+ *     L = sum_t <dO_t, o_t> + <dS_out, S_out>_F
+ * with respect to q, k, v, g, beta and S_in.
+ *
+ * Layouts (all tensors contiguous, row-major, device memory)
+ * ----------------------------------------------------------
+ *     q, k, dq, dk      [B, T, H, dk]      element type = shape.dtype
+ *     v, o, dO, dv      [B, T, H, dv]      element type = shape.dtype
+ *     g, dg             GDN: [B, T, H]     GLA: [B, T, H, dk]   (shape.dtype)
+ *     beta, dbeta       GDN: [B, T, H]     GLA: must be NULL     (shape.dtype)
+ *     S_in, S_out, dS_out, dS_in   [B, H, dk, dv]  always float32
+ * Supported head sizes: GDN (dk, dv) in {(32,32), (64,64), (128,128)};
+ * GLA additionally (128, 256).  Any T >= 0 (a ragged last 64-token block is
+ * handled by treating the missing tokens as identity steps).
+ *
+ * Ownership and execution
+ * -----------------------
+ * The caller allocates every buffer, including the workspace `ws` of at least
+ * clr_workspace_bytes() bytes (256-byte aligned).  The library allocates
+ * nothing, keeps no state between calls and is re-entrant; calls are enqueued
+ * asynchronously on `stream` (a hipStream_t; NULL = the default stream).
+ * Inputs are never modified; outputs are overwritten.  Calls that share a
+ * workspace must be ordered on one stream.
+ * Nullable: S_in (zero state), dS_out (zero), S_out (not wanted), o (not
+ * wanted; GDN/GLA fwd).
+ *
+ * Errors
+ * ------
+ * Every argument is validated on the host before anything is enqueued; on a
+ * non-zero status nothing has been launched and no output was touched:
+ *     CLR_EINVAL      null required pointer, bad sizes, misaligned pointer
+ *                     (tensors need 16-byte alignment), or an output that
+ *                     overlaps an input / another output
+ *     CLR_ENOTSUP     unsupported dtype or head size
+ *     CLR_EWORKSPACE  ws is NULL or smaller than clr_workspace_bytes()
+ *     CLR_EHIP        a HIP launch error (reported after enqueueing)
+ * No exception or abort crosses the ABI.  Loading the library needs no GPU.
+ */
+#ifndef CLR_H
+#define CLR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CLR_OK = 0,
+    CLR_EINVAL = 1,
+    CLR_ENOTSUP = 2,
+    CLR_EWORKSPACE = 3,
+    CLR_EHIP = 4
+} clr_status_t;
+
+typedef enum { CLR_F32 = 0, CLR_BF16 = 1 } clr_dtype_t;
+
+typedef enum {
+    CLR_OP_GDN_FWD = 0,
+    CLR_OP_GDN_BWD = 1,
+    CLR_OP_GLA_FWD = 2,
+    CLR_OP_GLA_BWD = 3
+} clr_op_t;
+
+typedef struct {
+    int32_t B, T, H, dk, dv;
+    int32_t dtype; /* clr_dtype_t */
+} clr_shape_t;
+
+/* Workspace bytes needed by `op` (clr_op_t) at `shape`; 0 on invalid input. */
+size_t clr_workspace_bytes(const clr_shape_t* shape, int op);
+
+/* Gated DeltaNet chunk forward (see the header comment for the definition). */
+int gdn_fwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+            const void* g, const void* beta, const float* S_in, void* o, float* S_out,
+            void* ws, size_t ws_bytes, void* stream);
+
+/* Gated DeltaNet chunk backward.  Recomputes the forward from (q, k, v, g,
+ * beta, S_in); dS_out may be NULL (zero).  All gradient outputs required. */
+int gdn_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+            const void* g, const void* beta, const float* S_in, const void* dO,
+            const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+            float* dS_in, void* ws, size_t ws_bytes, void* stream);
+
+/* GLA chunk forward; `beta` must be NULL (no delta term, no write scale). */
+int gla_fwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+            const void* g, const void* beta, const float* S_in, void* o, float* S_out,
+            void* ws, size_t ws_bytes, void* stream);
+
+/* GLA chunk backward; `beta` and `dbeta` must be NULL. */
+int gla_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+            const void* g, const void* beta, const float* S_in, const void* dO,
+            const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+            float* dS_in, void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* clr_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int clr_version(void);
+
+/* Self-check of the matrix-core fragment layout used by every kernel:
+ * C[16][16] = A[16][32] * Bt[16][32]^T for device buffers of `dtype`
+ * (A, Bt row-major; C float32).  For tests. */
+int clr_probe_mma(int dtype, const void* A, const void* Bt, float* C, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLR_H */
