@@ -21,12 +21,14 @@ bool gla_shape_ok(int dk, int dv) { return gdn_shape_ok(dk, dv) || (dk == 128 &&
 
 size_t esize(int dtype) { return dtype == CLR_BF16 ? 2 : 4; }
 
-// Basic shape validation shared by every entry point.
-int check_shape(const clr_shape_t* s, bool gla) {
+// Basic shape validation shared by every entry point.  The fp32 backward
+// kernels are instantiated for dk = dv = 32 only.
+int check_shape(const clr_shape_t* s, bool gla, bool bwd) {
     if (!s) return CLR_EINVAL;
     if (s->B < 1 || s->H < 1 || s->T < 0 || s->dk < 1 || s->dv < 1) return CLR_EINVAL;
     if (s->dtype != CLR_F32 && s->dtype != CLR_BF16) return CLR_ENOTSUP;
     if (gla ? !gla_shape_ok(s->dk, s->dv) : !gdn_shape_ok(s->dk, s->dv)) return CLR_ENOTSUP;
+    if (bwd && s->dtype == CLR_F32 && !(s->dk == 32 && s->dv == 32)) return CLR_ENOTSUP;
     // 64-bit element counts must stay addressable
     const double tok = (double)s->B * s->T * s->H * (s->dk > s->dv ? s->dk : s->dv);
     if (tok > 9.0e15) return CLR_EINVAL;
@@ -140,9 +142,9 @@ const char* clr_status_string(int s) {
 size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
     const bool gla = (op == CLR_OP_GLA_FWD || op == CLR_OP_GLA_BWD);
     if (op < CLR_OP_GDN_FWD || op > CLR_OP_GLA_BWD) return 0;
-    if (check_shape(s, gla) != CLR_OK) return 0;
-    size_t total = 0;
     const bool bwd = (op == CLR_OP_GDN_BWD || op == CLR_OP_GLA_BWD);
+    if (check_shape(s, gla, bwd) != CLR_OK) return 0;
+    size_t total = 0;
     if (gla) carve_gla(s, bwd, nullptr, &total);
     else carve_gdn(s, bwd, nullptr, &total);
     return total;
@@ -151,7 +153,7 @@ size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
 static int fwd_common(bool gla, const clr_shape_t* s, const void* q, const void* k, const void* v,
                       const void* g, const void* beta, const float* S_in, void* o, float* S_out,
                       void* ws, size_t ws_bytes, void* stream) {
-    int rc = check_shape(s, gla);
+    int rc = check_shape(s, gla, false);
     if (rc) return rc;
     if (!q || !k || !v || !g) return CLR_EINVAL;
     if (gla ? beta != nullptr : beta == nullptr) return CLR_EINVAL;
@@ -203,7 +205,7 @@ static int bwd_common(bool gla, const clr_shape_t* s, const void* q, const void*
                       const void* g, const void* beta, const float* S_in, const void* dO,
                       const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
                       float* dS_in, void* ws, size_t ws_bytes, void* stream) {
-    int rc = check_shape(s, gla);
+    int rc = check_shape(s, gla, true);
     if (rc) return rc;
     if (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg || !dS_in) return CLR_EINVAL;
     if (gla ? (beta != nullptr || dbeta != nullptr) : (beta == nullptr || dbeta == nullptr))

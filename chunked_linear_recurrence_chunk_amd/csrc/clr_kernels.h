@@ -13,6 +13,8 @@ namespace clr {
     CLR_CASE(E, 32, 32)       \
     CLR_CASE(E, 64, 64)       \
     CLR_CASE(E, 128, 128)
+// fp32 backward: the block-adjoint kernel's LDS tiles fit only for d = 32.
+#define CLR_FOR_GDN_BWD_SHAPES_F32(E) CLR_CASE(E, 32, 32)
 
 // Workspace of the Gated DeltaNet path.  Block-major: index
 // ((b * H + h) * NC + n) selects the 64-token block n of head h in batch b.

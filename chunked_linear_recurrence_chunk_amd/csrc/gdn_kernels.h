@@ -1,0 +1,376 @@
+// gdn_kernels.h -- Gated DeltaNet chunk-forward kernels on gfx950 (shared by
+// the forward and by the backward, which recomputes the forward).
+//
+// The layer (key-major state S in R^{dk x dv}):
+//   S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,  o_t = S_t^T q_t,
+// i.e. the scalar-plus-low-rank transition of the StateFlow paper ("StateFlow:
+// Sequence Pipeline Parallelism for Long-Context Modeling with Linear
+// Recurrence", Sec. 2.1, Eq. 1), run in the chunkwise Pre / ST / Out split of
+// its Sec. 2.2 (Eq. 2) over 64-token blocks:
+//
+//   prep  (Pre, parallel over blocks):  gamma = cumsum(g), the UT transform
+//         T = (I + Diag(beta) strict_lower(K K^T * G))^-1 and the WY pair
+//         W = T Diag(beta Gam) K, Ut = T Diag(beta) V   (Gam = exp(gamma),
+//         G[r,s] = exp(gamma_r - gamma_s)); also Kh^T = (Diag(exp(gamma_C - gamma)) K)^T.
+//   scan  (ST, sequential over blocks, parallel over heads x 16-wide value
+//         slices): h_n = S;  U_n = Ut_n - W_n S;  S <- Gam_C S + Kh_n^T U_n.
+//   out   (Out, parallel over blocks):  O = Diag(Gam) Q h_n + (Q K^T * G * tril) U_n.
+//
+// U_n is the delta rule's "new value" V^new of Eq. 2.  Workspace layouts are
+// chosen so that every scan operand is read with contiguous 8/16-byte loads
+// straight into matrix-core fragments (see clr_device.h).
+#pragma once
+
+#include "clr_kernels.h"
+
+namespace clr {
+
+// LDS row pitch (elements) of a 64-token-wide transposed tile.
+constexpr int PT = BLK + 8;
+
+// ---------------------------------------------------------------------------
+// Unit-lower-triangular inverse T = (I + A)^-1 of a 64 x 64 fp32 matrix in
+// LDS (A strictly lower).  16 x 16 diagonal blocks are inverted by forward
+// substitution, one wave each, then the off-diagonal row blocks are formed as
+// T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, one 16-row block at a time.
+// Requires 256 threads.  Am and Tm have row pitch 65 (floats).
+// ---------------------------------------------------------------------------
+__device__ inline void tri_inverse_64(const float* Am, float* Tm, float* Xs) {
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, c = l & 15, rg = l >> 4;
+    {
+        // wave w inverts diagonal block w; lane (c, rg) owns rows 4rg..4rg+3, column c
+        const int o = 16 * w;
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 16; ++r) {
+            float p = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 4 * rg + i;
+                if (s < r) p += Am[(o + r) * 65 + o + s] * x[i];
+            }
+            p += __shfl_xor(p, 16, 64);
+            p += __shfl_xor(p, 32, 64);
+            if ((r >> 2) == rg) {
+                const float val = (r == c ? 1.f : 0.f) - p;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if ((r & 3) == i) x[i] = val;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Tm[(o + 4 * rg + i) * 65 + o + c] = x[i];
+        // zero the strictly-upper part of this block row
+        for (int j = 0; j < 4; ++j)
+            if (j > w)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Tm[(o + 4 * rg + i) * 65 + 16 * j + c] = 0.f;
+    }
+    __syncthreads();
+    const int r = tid >> 4, cc = tid & 15;  // one element of a 16 x 16 block per thread
+    for (int i = 1; i < 4; ++i) {
+        for (int j = 0; j < i; ++j) {
+            // X = sum_{k=j}^{i-1} A_ik T_kj   (rows 16i.., cols 16j..)
+            float acc = 0.f;
+            for (int s = 16 * j; s < 16 * i; ++s) acc += Am[(16 * i + r) * 65 + s] * Tm[s * 65 + 16 * j + cc];
+            Xs[r * 17 + cc] = acc;
+            __syncthreads();
+            float t = 0.f;
+            for (int u = 0; u <= r; ++u) t += Tm[(16 * i + r) * 65 + 16 * i + u] * Xs[u * 17 + cc];
+            __syncthreads();
+            Tm[(16 * i + r) * 65 + 16 * j + cc] = -t;
+        }
+        __syncthreads();
+    }
+}
+
+// Transposed staging of an R x CC tile (row stride ld elements in global
+// memory) into LDS dst[CC][DP]:  dst[c][r] = src[r][c].  Rows r >= nvalid
+// (tokens past the end of the sequence) are staged as zeros.
+template <typename E, int R, int CC, int DP>
+__device__ void stage_T(const E* __restrict__ src, size_t ld, E* dst, int nvalid) {
+    constexpr int VEC = 16 / sizeof(E);  // elements per 16-byte load
+    constexpr int PER_ROW = CC / VEC;
+    for (int idx = threadIdx.x; idx < R * PER_ROW; idx += blockDim.x) {
+        const int t = idx / PER_ROW, cb = idx % PER_ROW;
+        E tmp[VEC];
+        if (t < nvalid) *(uint4*)tmp = *(const uint4*)(src + (size_t)t * ld + cb * VEC);
+        else *(uint4*)tmp = uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ii = 0; ii < VEC; ++ii) {
+            const int i = (ii + cb) % VEC;  // rotate to spread LDS banks
+            dst[(cb * VEC + i) * DP + t] = tmp[i];
+        }
+    }
+}
+// 64-token x D token-major tile -> dst[D][PT] (token index contiguous).
+template <typename E, int D>
+__device__ void stage_transposed(const E* __restrict__ src, size_t ld, E* dst, int nvalid) {
+    stage_T<E, BLK, D, PT>(src, ld, dst, nvalid);
+}
+
+// ---------------------------------------------------------------------------
+// prep: one work-group (4 waves) per (block n, head h, batch b).
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int T = a.T, H = a.H, NC = a.NC;
+    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;  // first token (b, n*64)
+    const size_t chunk = ((size_t)b * H + h) * NC + n;    // workspace block index
+    const int nvalid = min(BLK, T - n * BLK);             // tokens of this block inside the sequence
+
+    __shared__ float s_gam[BLK], s_bet[BLK], s_Gam[BLK];
+    __shared__ float Am[BLK * 65], Tm[BLK * 65], Xs[16 * 17];
+    __shared__ E Kt[DK * PT], Vt[DV * PT], T1[BLK * PT], T2[BLK * PT];
+
+    if (w == 0) {
+        // tokens past the end are identity steps: g = 0, beta = 0
+        const size_t ig = (tok0 + l) * H + h;
+        const float gv = l < nvalid ? to_f(a.g[ig]) : 0.f;
+        const float gam = wave_prefix_sum(gv);
+        s_gam[l] = gam;
+        s_Gam[l] = __expf(gam);
+        s_bet[l] = l < nvalid ? to_f(a.beta[ig]) : 0.f;
+        a.gam[chunk * BLK + l] = gam;
+    }
+    stage_transposed<E, DK>(a.k + tok0 * H * DK + (size_t)h * DK, (size_t)H * DK, Kt, nvalid);
+    stage_transposed<E, DV>(a.v + tok0 * H * DV + (size_t)h * DV, (size_t)H * DV, Vt, nvalid);
+    __syncthreads();
+
+    // Gram block row w: A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s), s < r.
+    {
+        const E* kb = a.k + tok0 * H * DK + (size_t)h * DK;
+        const size_t ld = (size_t)H * DK;
+        Frag<E> fa[DK / 32];
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) fa[kk] = ldfrag_row(kb, 16 * w + r, nvalid, ld, 32 * kk + 4 * g);
+        for (int j = 0; j < 4; ++j) {
+            f32x4 acc = zero4();
+            if (j <= w) {
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    Frag<E> fb = ldfrag_row(kb, 16 * j + r, nvalid, ld, 32 * kk + 4 * g);
+                    mma(acc, fa[kk], fb);
+                }
+            }
+            // D tile rows = 16w + 4g + i (r index "row"), cols = 16j + r (s index)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * w + 4 * g + i, col = 16 * j + r;
+                float val = 0.f;
+                if (col < row) val = s_bet[row] * __expf(s_gam[row] - s_gam[col]) * acc[i];
+                Am[row * 65 + col] = val;
+            }
+        }
+    }
+    __syncthreads();
+    tri_inverse_64(Am, Tm, Xs);
+    __syncthreads();
+    // T1 = T Diag(beta Gam), T2 = T Diag(beta), rounded to the element type.
+    for (int idx = tid; idx < BLK * BLK; idx += 256) {
+        const int t = idx >> 6, s = idx & 63;
+        const float tv = Tm[t * 65 + s];
+        T1[t * PT + s] = from_f<E>(tv * s_bet[s] * s_Gam[s]);
+        T2[t * PT + s] = from_f<E>(tv * s_bet[s]);
+    }
+    __syncthreads();
+
+    // W^T[d][t] = sum_s Kt[d][s] T1[t][s]  -> written as W[t][d] (token-major)
+    E* Wout = a.W + chunk * BLK * DK;
+    for (int tile = w; tile < (DK / 16) * 4; tile += 4) {
+        const int db = tile >> 2, tb = tile & 3;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            Frag<E> fa = ldfrag(Kt + (16 * db + r) * PT + 32 * j + 4 * g);
+            Frag<E> fb = ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g);
+            mma(acc, fa, fb);
+        }
+        st4(Wout + (size_t)(16 * tb + r) * DK + 16 * db + 4 * g, acc);
+    }
+    // Ut[t][v] = sum_s T2[t][s] Vt[v][s]  -> written as Ut^T[v][t]
+    E* Uout = a.UtT + chunk * BLK * DV;
+    for (int tile = w; tile < 4 * (DV / 16); tile += 4) {
+        const int tb = tile % 4, vb = tile / 4;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            Frag<E> fa = ldfrag(T2 + (16 * tb + r) * PT + 32 * j + 4 * g);
+            Frag<E> fb = ldfrag(Vt + (16 * vb + r) * PT + 32 * j + 4 * g);
+            mma(acc, fa, fb);
+        }
+        st4(Uout + (size_t)(16 * vb + r) * BLK + 16 * tb + 4 * g, acc);
+    }
+    // Kh^T[d][t] = exp(gamma_C - gamma_t) K[t][d]
+    E* Khout = a.KhT + chunk * BLK * DK;
+    const float gC = s_gam[BLK - 1];
+    for (int idx = tid; idx < DK * (BLK / 4); idx += 256) {
+        const int d = idx / (BLK / 4), t4 = (idx % (BLK / 4)) * 4;
+        f32x4 x = ld4(Kt + d * PT + t4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] *= __expf(gC - s_gam[t4 + i]);
+        st4(Khout + (size_t)d * BLK + t4, x);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// scan: one wave per (16-wide value slice, head, batch); sequential over the
+// blocks.  The fp32 state slice S[0:DK][v0:v0+16] lives in accumulator tiles.
+// Writes h_n^T[v][d] (state entering block n) and U_n^T[v][t].
+// ---------------------------------------------------------------------------
+// HNAT selects the layout of the saved states: false -> h^T[v][d] (read by the
+// forward's out kernel), true -> h[d][v] (read by the backward).
+template <typename E, int DK, int DV, bool HNAT>
+__global__ __launch_bounds__(64) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
+    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int l = threadIdx.x, r = l & 15, g = l >> 4;
+    const int H = a.H, NC = a.NC;
+    const int v0 = 16 * vb;
+    constexpr int ND = DK / 16;
+    const size_t bh = (size_t)b * H + h;
+
+    f32x4 S[ND];
+    const float* Sin = a.S_in ? a.S_in + bh * DK * DV : nullptr;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[db][i] = Sin ? Sin[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
+
+    for (int n = 0; n < NC; ++n) {
+        const size_t chunk = bh * NC + n;
+        const E* W = a.W + chunk * BLK * DK;
+        const E* KhT = a.KhT + chunk * BLK * DK;
+        const E* UtT = a.UtT + chunk * BLK * DV;
+        const float GC = __expf(a.gam[chunk * BLK + BLK - 1]);
+
+        // state entering block n
+        if (a.hT) {
+            E* hT = a.hT + chunk * DK * DV;
+            if constexpr (HNAT) {
+#pragma unroll
+                for (int db = 0; db < ND; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hT[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = from_f<E>(S[db][i]);
+            } else {
+#pragma unroll
+                for (int db = 0; db < ND; ++db) st4(hT + (size_t)(v0 + r) * DK + 16 * db + 4 * g, S[db]);
+            }
+        }
+        // U = Ut - W S    (tiles: rows t = 16tb + 4g + i, col v0 + r)
+        Frag<E> fs[DK / 32];
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
+        f32x4 U[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                Frag<E> fw = ldfrag(W + (size_t)(16 * tb + r) * DK + 32 * kk + 4 * g);
+                mma(acc, fw, fs[kk]);
+            }
+            f32x4 ut = ld4(UtT + (size_t)(v0 + r) * BLK + 16 * tb + 4 * g);
+            U[tb] = ut - acc;
+        }
+        if (a.UT) {
+            E* UT = a.UT + chunk * BLK * DV;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) st4(UT + (size_t)(v0 + r) * BLK + 16 * tb + 4 * g, U[tb]);
+        }
+        // S <- Gam_C S + Kh^T U
+        Frag<E> fu[2];
+        fu[0] = frag_from_acc<E>(U[0], U[1]);
+        fu[1] = frag_from_acc<E>(U[2], U[3]);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            f32x4 acc = S[db] * GC;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                Frag<E> fk = ldfrag(KhT + (size_t)(16 * db + r) * BLK + 32 * j + 4 * g);
+                mma(acc, fk, fu[j]);
+            }
+            S[db] = acc;
+        }
+    }
+    if (a.S_out) {
+        float* So = a.S_out + bh * DK * DV;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) So[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = S[db][i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// out: one work-group (4 waves) per (block, head, batch); wave w owns tokens
+// 16w..16w+15 of the block.  Computes O^T tiles so that each lane writes four
+// contiguous output values.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int T = a.T, H = a.H, NC = a.NC;
+    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
+    const size_t chunk = ((size_t)b * H + h) * NC + n;
+    const float* gam = a.gam + chunk * BLK;
+    const E* qb = a.q + tok0 * H * DK + (size_t)h * DK;
+    const E* kb = a.k + tok0 * H * DK + (size_t)h * DK;
+    const size_t ldk = (size_t)H * DK;
+    const int nvalid = min(BLK, T - n * BLK);
+
+    // Q as B operand: Bt[t][d] = Q[t][d]
+    Frag<E> fq[DK / 32];
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) fq[kk] = ldfrag_row(qb, 16 * w + r, nvalid, ldk, 32 * kk + 4 * g);
+
+    const int t_lane = 16 * w + r;  // this lane's token (column of every O^T / P^T tile)
+    const float gt = gam[t_lane];
+    // P^T[s][t] = (k_s . q_t) exp(gamma_t - gamma_s) for s <= t
+    f32x4 P[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+        f32x4 acc = zero4();
+        if (sb <= w) {
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                Frag<E> fk = ldfrag_row(kb, 16 * sb + r, nvalid, ldk, 32 * kk + 4 * g);
+                mma(acc, fk, fq[kk]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * sb + 4 * g + i;
+                acc[i] = (s <= t_lane) ? acc[i] * __expf(gt - gam[s]) : 0.f;
+            }
+        }
+        P[sb] = acc;
+    }
+    Frag<E> fp[2];
+    fp[0] = frag_from_acc<E>(P[0], P[1]);
+    fp[1] = frag_from_acc<E>(P[2], P[3]);
+    const float Gt = __expf(gt);
+    const E* hT = a.hT + chunk * DK * DV;
+    const E* UT = a.UT + chunk * BLK * DV;
+    E* ob = a.o + tok0 * H * DV + (size_t)h * DV;
+    for (int vb = 0; vb < DV / 16; ++vb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            Frag<E> fh = ldfrag(hT + (size_t)(16 * vb + r) * DK + 32 * kk + 4 * g);
+            mma(acc, fh, fq[kk]);
+        }
+        acc = acc * Gt;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (2 * j <= w) {
+                Frag<E> fu = ldfrag(UT + (size_t)(16 * vb + r) * BLK + 32 * j + 4 * g);
+                mma(acc, fu, fp[j]);
+            }
+        }
+        if (t_lane < nvalid) st4(ob + (size_t)t_lane * H * DV + 16 * vb + 4 * g, acc);
+    }
+}
+
+}  // namespace clr

@@ -34,7 +34,8 @@
  *     beta, dbeta       GDN: [B, T, H]     GLA: must be NULL     (shape.dtype)
  *     S_in, S_out, dS_out, dS_in   [B, H, dk, dv]  always float32
  * Supported head sizes: GDN (dk, dv) in {(32,32), (64,64), (128,128)};
- * GLA additionally (128, 256).  Any T >= 0 (a ragged last 64-token block is
+ * GLA additionally (128, 256).  The float32 backward supports (32, 32) only
+ * (CLR_ENOTSUP otherwise).  Any T >= 0 (a ragged last 64-token block is
  * handled by treating the missing tokens as identity steps).
  *
  * Ownership and execution

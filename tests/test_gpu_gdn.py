@@ -73,3 +73,49 @@ def test_gdn_fwd_slow_decay_bf16():
     print("slow decay errors", rel_err(o, o_ref), rel_err(S, S_ref))
     assert rel_err(o, o_ref) < tol("bf16", "o")
     assert rel_err(S, S_ref) < tol("bf16", "S_out")
+
+
+def _run_bwd(x, dtype, with_dS=True):
+    ops = _ops()
+    d = {k: to_dev(x[k], dtype) for k in ("q", "k", "v", "g", "beta", "dO")}
+    S_in = to_dev(x["S_in"], "fp32")
+    dS_out = to_dev(x["dS_out"], "fp32") if with_dS else None
+    r = ops.gdn_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S_in, d["dO"], dS_out)
+    return {k: to_np(v) for k, v in r.items()}
+
+
+BWD_CASES = [
+    (1, 256, 1, 32, 32, "fp32", 21),
+    (2, 200, 3, 32, 32, "fp32", 22),    # ragged tail
+    (1, 512, 2, 128, 128, "bf16", 23),
+    (2, 320, 2, 64, 64, "bf16", 24),
+    (1, 100, 2, 128, 128, "bf16", 25),  # ragged, < 2 blocks
+    (1, 256, 3, 32, 32, "bf16", 26),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"B{c[0]}T{c[1]}H{c[2]}d{c[3]}-{c[5]}" for c in BWD_CASES])
+def test_gdn_bwd_matches_oracle(case):
+    from chunked_linear_recurrence_chunk_amd import inputs
+    from oracle import oracle
+    B, T, H, dk, dv, dtype, seed = case
+    print(f"[gdn bwd] case {case}", flush=True)
+    x = inputs.make_gdn(B, T, H, dk, dv, dtype, seed)
+    got = _run_bwd(x, dtype)
+    ref = oracle.gdn_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S_in"], x["dO"], x["dS_out"])
+    errs = {k: rel_err(got[k], ref[k]) for k in ref}
+    print("  errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, e in errs.items():
+        assert e < tol(dtype, k), (k, e)
+
+
+def test_gdn_bwd_slow_decay_and_null_dS_out():
+    from chunked_linear_recurrence_chunk_amd import inputs
+    from oracle import oracle
+    x = inputs.make_gdn(1, 1024, 2, 128, 128, "bf16", 27, slow_decay=True)
+    got = _run_bwd(x, "bf16", with_dS=False)
+    ref = oracle.gdn_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S_in"], x["dO"], None)
+    errs = {k: rel_err(got[k], ref[k]) for k in ref}
+    print("  errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, e in errs.items():
+        assert e < tol("bf16", k), (k, e)
