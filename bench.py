@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark: Gated DeltaNet chunked forward + backward on one MI355X.
+
+One step = the whole hot path over one batch: the forward over the N
+sequence chunks in order (boundary state handed S_out -> S_in) and the
+backward over the chunks in reverse (dS_in -> dS_out), every kernel in the
+HIP library through its C ABI.  Inputs are seeded synthetic tensors, resident
+in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line (see README of the JSON fields in the design doc).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec, gated-delta-rule fwd+bwd (H=16,dk=dv=128); MFMA util %"
+DEFAULT_WORKLOAD = "gdn_bf16_H16_T8192_d128"
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/byte
+
+
+def kernel_work(name: str, D: int, es: int, C: int = 64):
+    """Algorithmic (bytes, flops) of one kernel per 64-token block and head,
+    for dk = dv = D and element size es.  Bytes count each tensor the kernel
+    must read or write once; flops count the dense products as executed
+    (2 m n k each).  Definitions are listed per kernel in the design doc."""
+    CD, DD, CC = C * D, D * D, C * C
+    f4 = 4
+    if name == "gdn_prep":
+        byts = 2 * CD * es + 2 * C * es + C * f4 + 3 * CD * es
+        flops = 2 * CC * D + 2 * (2 * CC * D) + (C ** 3) // 3
+    elif name == "gdn_prep2":
+        byts = 4 * CD * es + C * f4 + 5 * CD * es
+        flops = 2 * (2 * CC * D)
+    elif name in ("gdn_scan_fwd", "gdn_scan_fwd_rec"):
+        byts = C * f4 + 3 * CD * es + DD * es + CD * es
+        flops = 2 * (2 * C * DD)
+    elif name == "gdn_out":
+        byts = 2 * CD * es + C * f4 + DD * es + CD * es + CD * es
+        flops = 2 * CC * D + 2 * C * DD + 2 * CC * D
+    elif name == "gdn_scan_bwd":
+        byts = C * f4 + 5 * CD * es + DD * es + CD * es
+        flops = 3 * (2 * C * DD)
+    elif name == "gdn_bwd_intra":
+        byts = 4 * CD * es + C * es + C * f4 + 2 * DD * es + 2 * CD * es + 3 * CD * es + 2 * C * es
+        flops = 3 * (2 * C * DD) + 10 * (2 * CC * D) + 2 * (2 * C ** 3) + 2 * CC * D
+    else:
+        return None
+    return byts, flops
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources (ties stored counter data to a kernel build)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_linear_recurrence_chunk_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, fn), "rb") as f:
+                h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if absent or taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload, {}).get(kernel)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg: dict, x: dict, budget_chunks: int):
+    """The fp64 oracle (as it stands) on the host cores over a bounded sample:
+    the first `budget_chunks` sequence chunks of the workload, forward then
+    backward with boundary-state hand-off."""
+    import numpy as np
+    from oracle import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    T, N = cfg["T"], cfg["N"]
+    L = T // N
+    n = max(1, min(budget_chunks, N))
+    Ts = L * n
+    sl = {k: (np.ascontiguousarray(v[:, :Ts]).astype(np.float64) if v.ndim >= 3 and k not in ("S_in", "dS_out")
+              else v.astype(np.float64)) for k, v in x.items()}
+    t0 = time.perf_counter()
+    if cfg["kind"] == "gdn":
+        oracle.gdn_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], None, n)
+    else:
+        oracle.gla_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], None, n)
+    dt = time.perf_counter() - t0
+    return {"value": cfg["B"] * Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {N} sequence chunks ({cfg['B']}x{Ts} tokens, all {cfg['H']} heads), "
+                      f"fp64 fwd+bwd, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-chunks", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards by heads with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from chunked_linear_recurrence_chunk_amd import inputs, ops, stateflow
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ops.load()  # fail loudly if the HIP library is missing
+
+    cfg = inputs.CONFIGS[args.workload]
+    B, T, H, dk, dv, N = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], cfg["N"]
+    dtype = cfg["dtype"]
+    x = inputs.make(cfg, seed=2)
+
+    def dev(a, dt):
+        if dt == "bf16":
+            bits = inputs.bf16_bits(a)
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    keys = ("q", "k", "v", "g", "beta", "dO") if cfg["kind"] == "gdn" else ("q", "k", "v", "g", "dO")
+    d = {k: dev(x[k], dtype) for k in keys}
+    S_in = dev(x["S_in"], "fp32")
+    if cfg["kind"] == "gdn":
+        drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
+    else:
+        drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
+    o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device="cuda")
+    grads = {k: torch.empty_like(d[k.replace("d", "", 1)] if k != "dbeta" else d["beta"])
+             for k in (("dq", "dk", "dv", "dg", "dbeta") if cfg["kind"] == "gdn" else ("dq", "dk", "dv", "dg"))}
+
+    def step():
+        drv.forward(S_in, o=o)
+        drv.backward(d["dO"], None, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    value = B * T / (ms / 1e3)
+    print(f"[bench] {args.workload}: {ms:.3f} ms/step, {value / 1e6:.2f} M tokens/s", file=sys.stderr, flush=True)
+
+    # per-kernel durations, measured with start/stop events on the launch stream
+    ops.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    rep = ops.timing_report()
+    ops.timing_enable(False)
+    es = 2 if dtype == "bf16" else 4
+    NC = (T // N) // 64
+    blocks_per_launch = B * H * NC
+    kernels = {}
+    tot_ms = sum(v[1] for v in rep.values())
+    tot_flops = 0.0
+    for name, (launches, total_ms) in rep.items():
+        avg_us = total_ms / launches * 1e3
+        work = kernel_work(name, dk, es)
+        ent = {"launches_per_step": launches // args.steps, "avg_us": round(avg_us, 2),
+               "share": round(total_ms / tot_ms, 3)}
+        if work:
+            byts, flops = work[0] * blocks_per_launch, work[1] * blocks_per_launch
+            tot_flops += flops * launches / args.steps
+            ent.update(alg_bytes=byts, alg_flops=flops,
+                       gbs=round(byts / (avg_us * 1e-6) / 1e9, 1),
+                       tflops=round(flops / (avg_us * 1e-6) / 1e12, 2))
+        kernels[name] = ent
+        print(f"[bench]   {name:18s} {ent}", file=sys.stderr, flush=True)
+    dom = max(rep, key=lambda k: rep[k][1])
+    dk_ent = kernels[dom]
+    bound = "hbm" if dk_ent["alg_flops"] / dk_ent["alg_bytes"] < RIDGE else "mfma"
+    peak_flops = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+    if bound == "hbm":
+        achieved, peak, unit = dk_ent["gbs"], PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = dk_ent["tflops"], peak_flops, "TFLOP/s"
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": load_traffic(args.workload, dom),
+                "kernel": dom, "avg_us": dk_ent["avg_us"], "alg_bytes_per_launch": dk_ent["alg_bytes"],
+                "alg_flops_per_launch": dk_ent["alg_flops"]}
+    mfma_util = tot_flops / (ms * 1e-3) / (peak_flops * 1e12)
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+           "data": "synthetic",
+           "config": {"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "H": H, "dk": dk,
+                      "dv": dv, "seq_chunks": N, "block": 64},
+           "mfma_util": round(mfma_util, 4),
+           "roofline": roofline, "kernels": kernels}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_chunks)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

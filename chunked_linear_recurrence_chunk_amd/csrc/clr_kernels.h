@@ -5,6 +5,7 @@
 #include <stddef.h>
 
 #include "clr_device.h"
+#include "clr_launch.h"
 
 namespace clr {
 

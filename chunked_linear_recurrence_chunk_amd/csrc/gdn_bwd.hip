@@ -568,20 +568,20 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const GdnWs& ws = L.ws;
     GdnPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                       ws.gam, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
-    hipLaunchKernelGGL((gdn_prep_kernel<E, DK, DV>), gblk, dim3(256), 0, st, pa);
+    launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, gblk, dim3(256), st, pa);
     GdnPrep2Args<E> p2{(const E*)L.q, (const E*)L.k, (const E*)L.dO, ws.gam, (const E*)ws.W,
                        (E*)ws.QgT, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dOT, (E*)ws.dvlT, L.T, L.H, L.NC};
-    hipLaunchKernelGGL((gdn_prep2_kernel<E, DK, DV>), gblk, dim3(256), 0, st, p2);
+    launch("gdn_prep2", gdn_prep2_kernel<E, DK, DV>, gblk, dim3(256), st, p2);
     GdnScanArgs<E> sa{ws.gam, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, (E*)ws.UT, L.H, L.NC};
-    hipLaunchKernelGGL((gdn_scan_fwd_kernel<E, DK, DV, true>), dim3(DV / 16, L.H, L.B), dim3(64), 0, st, sa);
+    launch("gdn_scan_fwd_rec", gdn_scan_fwd_kernel<E, DK, DV, true>, dim3(DV / 16, L.H, L.B), dim3(64), st, sa);
     GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.QgT, (const E*)ws.WT, (const E*)ws.dOT,
                          (const E*)ws.dvlT, L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC};
-    hipLaunchKernelGGL((gdn_scan_bwd_kernel<E, DK, DV>), dim3(DV / 16, L.H, L.B), dim3(64), 0, st, sb);
+    launch("gdn_scan_bwd", gdn_scan_bwd_kernel<E, DK, DV>, dim3(DV / 16, L.H, L.B), dim3(64), st, sb);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const E*)ws.dUT,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};
-    hipLaunchKernelGGL((gdn_bwd_intra_kernel<E, DK, DV>), gblk, dim3(256), 0, st, ia);
+    launch("gdn_bwd_intra", gdn_bwd_intra_kernel<E, DK, DV>, gblk, dim3(256), st, ia);
     return hipGetLastError();
 }
 

@@ -26,6 +26,10 @@ class ClrShape(ctypes.Structure):
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
+
+
 class ClrError(RuntimeError):
     def __init__(self, fn, status, msg):
         super().__init__(f"{fn} failed: status {status} ({msg})")
@@ -62,6 +66,10 @@ def load(path: Optional[str] = None):
     lib.clr_version.restype = i
     lib.clr_probe_mma.argtypes = [i, vp, vp, vp, vp]
     lib.clr_probe_mma.restype = i
+    lib.clr_timing_enable.argtypes = [i]
+    lib.clr_timing_enable.restype = i
+    lib.clr_timing_report.argtypes = [ctypes.POINTER(KernelTime), i]
+    lib.clr_timing_report.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -121,14 +129,38 @@ def _check_inputs(*ts):
             raise ValueError("tensors must be contiguous")
 
 
-def _fwd(name, op, q, k, v, g, beta, S_in, want_state, ws):
+def timing_enable(on: bool = True) -> None:
+    """Time every library kernel with start/stop events (profiling aid)."""
+    load().clr_timing_enable(1 if on else 0)
+
+
+def timing_report() -> dict:
+    """Wait for the timed kernels and return {name: (launches, total_ms)}; clears."""
+    buf = (KernelTime * 64)()
+    n = load().clr_timing_report(buf, 64)
+    if n < 0:
+        raise ClrError("clr_timing_report", -n, status_string(-n))
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n)}
+
+
+def _out(t, shape, dtype, device):
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"output tensor must be contiguous {dtype} of shape {shape}")
+    return t
+
+
+def _fwd(name, op, q, k, v, g, beta, S_in, want_state, ws, o=None, S_out=None):
     import torch
     _check_inputs(q, k, v, g, beta, S_in)
     shape = make_shape(q, v)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
-    S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
+    o = _out(o, (B, T, H, dv), q.dtype, q.device)
+    if want_state or S_out is not None:
+        S_out = _out(S_out, (B, H, dk, dv), torch.float32, q.device)
     if ws is None:
         ws, n = _workspace(shape, op, q.device)
     else:
@@ -139,26 +171,30 @@ def _fwd(name, op, q, k, v, g, beta, S_in, want_state, ws):
     return o, S_out
 
 
-def gdn_fwd(q, k, v, g, beta, S_in=None, want_state=True, ws=None):
-    """Gated DeltaNet chunk forward.  Returns (o, S_out)."""
-    return _fwd("gdn_fwd", OP_GDN_FWD, q, k, v, g, beta, S_in, want_state, ws)
+def gdn_fwd(q, k, v, g, beta, S_in=None, want_state=True, ws=None, o=None, S_out=None):
+    """Gated DeltaNet chunk forward.  Returns (o, S_out).  ``o`` / ``S_out``
+    may be preallocated contiguous outputs (e.g. views of a larger tensor)."""
+    return _fwd("gdn_fwd", OP_GDN_FWD, q, k, v, g, beta, S_in, want_state, ws, o, S_out)
 
 
-def gla_fwd(q, k, v, g, S_in=None, want_state=True, ws=None):
+def gla_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None):
     """GLA chunk forward (per-key-channel gate g).  Returns (o, S_out)."""
-    return _fwd("gla_fwd", OP_GLA_FWD, q, k, v, g, None, S_in, want_state, ws)
+    return _fwd("gla_fwd", OP_GLA_FWD, q, k, v, g, None, S_in, want_state, ws, o, S_out)
 
 
-def _bwd(name, op, q, k, v, g, beta, S_in, dO, dS_out, ws):
+def _bwd(name, op, q, k, v, g, beta, S_in, dO, dS_out, ws, out=None):
     import torch
     _check_inputs(q, k, v, g, beta, S_in, dO, dS_out)
     shape = make_shape(q, v)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dg = torch.empty_like(g)
-    dbeta = torch.empty_like(beta) if beta is not None else None
-    dS_in = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    out = out or {}
+    dq = _out(out.get("dq"), q.shape, q.dtype, q.device)
+    dk_ = _out(out.get("dk"), k.shape, k.dtype, k.device)
+    dv_ = _out(out.get("dv"), v.shape, v.dtype, v.device)
+    dg = _out(out.get("dg"), g.shape, g.dtype, g.device)
+    dbeta = _out(out.get("dbeta"), beta.shape, beta.dtype, beta.device) if beta is not None else None
+    dS_in = _out(out.get("dS_in"), (B, H, dk, dv), torch.float32, q.device)
     if ws is None:
         ws, n = _workspace(shape, op, q.device)
     else:
@@ -173,14 +209,15 @@ def _bwd(name, op, q, k, v, g, beta, S_in, dO, dS_out, ws):
     return r
 
 
-def gdn_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, ws=None):
-    """Gated DeltaNet chunk backward.  Returns dict dq, dk, dv, dg, dbeta, dS_in."""
-    return _bwd("gdn_bwd", OP_GDN_BWD, q, k, v, g, beta, S_in, dO, dS_out, ws)
+def gdn_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, ws=None, out=None):
+    """Gated DeltaNet chunk backward.  Returns dict dq, dk, dv, dg, dbeta, dS_in
+    (``out`` may hold preallocated contiguous tensors under those names)."""
+    return _bwd("gdn_bwd", OP_GDN_BWD, q, k, v, g, beta, S_in, dO, dS_out, ws, out)
 
 
-def gla_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None):
+def gla_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None, out=None):
     """GLA chunk backward.  Returns dict dq, dk, dv, dg, dS_in."""
-    return _bwd("gla_bwd", OP_GLA_BWD, q, k, v, g, None, S_in, dO, dS_out, ws)
+    return _bwd("gla_bwd", OP_GLA_BWD, q, k, v, g, None, S_in, dO, dS_out, ws, out)
 
 
 def probe_mma(A, Bt):

@@ -1,0 +1,153 @@
+"""StateFlow-style sequence-chunk driver on one GPU.
+
+A sequence X = C_0 || C_1 || ... || C_{N-1} (StateFlow paper, Sec. 3.1,
+Eq. 3) is processed chunk by chunk: the forward runs i = 0..N-1 with
+S_{i+1}^in = S_i^out, the backward runs i = N-1..0 with
+dS_i^out = dS_{i+1}^in, and a chunk's saved state is released right after its
+backward (the chunk-level activation release of the same section).  Only the
+boundary state S_i^in (fp32, dk x dv per head) is kept per chunk; the backward
+recomputes the chunk's internals from it.
+
+Every chunk call goes through the C ABI (``ops``); this module only slices
+tensors (views, no copies, when B == 1) and orders the calls on the current
+stream.  One workspace sized for the chunk length is reused by all calls.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+
+def _bounds(T: int, N: int):
+    if N < 1 or T % N:
+        raise ValueError(f"sequence length {T} is not divisible into {N} chunks")
+    L = T // N
+    return [(i * L, (i + 1) * L) for i in range(N)]
+
+
+def _sl(t, a, b):
+    """Token slice [a, b) of a [B, T, ...] tensor (a view if B == 1)."""
+    s = t[:, a:b]
+    return s if s.is_contiguous() else s.contiguous()
+
+
+class GdnChunked:
+    """Forward/backward of one Gated DeltaNet layer over N sequence chunks."""
+
+    kind = "gdn"
+
+    def __init__(self, q, k, v, g, beta, N: int):
+        from . import ops
+        self.ops = ops
+        self.q, self.k, self.v, self.g, self.beta = q, k, v, g, beta
+        self.N = N
+        self.bounds = _bounds(q.shape[1], N)
+        L = self.bounds[0][1]
+        B, _, H, dk = q.shape
+        dv = v.shape[-1]
+        import torch
+        shape = ops.ClrShape(B, L, H, dk, dv, ops._dtype_code(q))
+        nbytes = max(ops.workspace_bytes(shape, ops.OP_GDN_FWD), ops.workspace_bytes(shape, ops.OP_GDN_BWD))
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+        self.saved = [None] * N
+        self.contig = B == 1
+
+    def _chunk(self, i):
+        a, b = self.bounds[i]
+        return tuple(_sl(t, a, b) for t in (self.q, self.k, self.v, self.g, self.beta))
+
+    def forward(self, S_in=None, o=None):
+        """Returns (o, S_out); keeps each chunk's S^in for the backward."""
+        import torch
+        B, T, H, dk = self.q.shape
+        dv = self.v.shape[-1]
+        if o is None:
+            o = torch.empty((B, T, H, dv), dtype=self.q.dtype, device=self.q.device)
+        S = S_in
+        for i in range(self.N):
+            a, b = self.bounds[i]
+            self.saved[i] = S
+            oi = o[:, a:b] if self.contig else None
+            oi, S = self.ops.gdn_fwd(*self._chunk(i), S, ws=self.ws, o=oi)
+            if not self.contig:
+                o[:, a:b] = oi
+        return o, S
+
+    def backward(self, dO, dS_out=None, grads: Optional[dict] = None):
+        """Returns dict dq, dk, dv, dg, dbeta, dS_in; releases saved states."""
+        import torch
+        if grads is None:
+            grads = dict(dq=torch.empty_like(self.q), dk=torch.empty_like(self.k),
+                         dv=torch.empty_like(self.v), dg=torch.empty_like(self.g),
+                         dbeta=torch.empty_like(self.beta))
+        dS = dS_out
+        for i in reversed(range(self.N)):
+            a, b = self.bounds[i]
+            out = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg", "dbeta")} if self.contig else None
+            r = self.ops.gdn_bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
+            if not self.contig:
+                for key in ("dq", "dk", "dv", "dg", "dbeta"):
+                    grads[key][:, a:b] = r[key]
+            dS = r["dS_in"]
+            self.saved[i] = None
+        grads["dS_in"] = dS
+        return grads
+
+
+class GlaChunked(GdnChunked):
+    """Forward/backward of one GLA layer over N sequence chunks."""
+
+    kind = "gla"
+
+    def __init__(self, q, k, v, g, N: int):
+        from . import ops
+        self.ops = ops
+        self.q, self.k, self.v, self.g, self.beta = q, k, v, g, None
+        self.N = N
+        self.bounds = _bounds(q.shape[1], N)
+        L = self.bounds[0][1]
+        B, _, H, dk = q.shape
+        dv = v.shape[-1]
+        import torch
+        shape = ops.ClrShape(B, L, H, dk, dv, ops._dtype_code(q))
+        nbytes = max(ops.workspace_bytes(shape, ops.OP_GLA_FWD), ops.workspace_bytes(shape, ops.OP_GLA_BWD))
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+        self.saved = [None] * N
+        self.contig = B == 1
+
+    def _chunk(self, i):
+        a, b = self.bounds[i]
+        return tuple(_sl(t, a, b) for t in (self.q, self.k, self.v, self.g))
+
+    def forward(self, S_in=None, o=None):
+        import torch
+        B, T, H, dk = self.q.shape
+        dv = self.v.shape[-1]
+        if o is None:
+            o = torch.empty((B, T, H, dv), dtype=self.q.dtype, device=self.q.device)
+        S = S_in
+        for i in range(self.N):
+            a, b = self.bounds[i]
+            self.saved[i] = S
+            oi = o[:, a:b] if self.contig else None
+            oi, S = self.ops.gla_fwd(*self._chunk(i), S, ws=self.ws, o=oi)
+            if not self.contig:
+                o[:, a:b] = oi
+        return o, S
+
+    def backward(self, dO, dS_out=None, grads: Optional[dict] = None):
+        import torch
+        if grads is None:
+            grads = dict(dq=torch.empty_like(self.q), dk=torch.empty_like(self.k),
+                         dv=torch.empty_like(self.v), dg=torch.empty_like(self.g))
+        dS = dS_out
+        for i in reversed(range(self.N)):
+            a, b = self.bounds[i]
+            out = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg")} if self.contig else None
+            r = self.ops.gla_bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
+            if not self.contig:
+                for key in ("dq", "dk", "dv", "dg"):
+                    grads[key][:, a:b] = r[key]
+            dS = r["dS_in"]
+            self.saved[i] = None
+        grads["dS_in"] = dS
+        return grads

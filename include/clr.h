@@ -125,6 +125,21 @@ const char* clr_status_string(int status);
 /* Library ABI version (major * 100 + minor). */
 int clr_version(void);
 
+/* Profiling aid.  While enabled, every kernel the library launches is
+ * bracketed by a start/stop event pair (hipExtLaunchKernelGGL) on the stream
+ * it runs on.  clr_timing_report waits for the recorded events, writes one
+ * entry per kernel name (launch count and summed duration, in launch order of
+ * first appearance) into out[0..max_entries), clears the record and returns
+ * the number of entries (or -CLR_EHIP).  Process-global; meant for
+ * single-threaded benchmarking, not for concurrent use. */
+typedef struct {
+    char name[48];
+    int launches;
+    double total_ms;
+} clr_kernel_time_t;
+int clr_timing_enable(int on);
+int clr_timing_report(clr_kernel_time_t* out, int max_entries);
+
 /* Self-check of the matrix-core fragment layout used by every kernel:
  * C[16][16] = A[16][32] * Bt[16][32]^T for device buffers of `dtype`
  * (A, Bt row-major; C float32).  For tests. */

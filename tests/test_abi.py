@@ -1,0 +1,129 @@
+"""The C-ABI library loads without a GPU, exports every symbol declared in
+include/clr.h, and rejects bad arguments on the host before launching
+anything (so these run on the CPU: every call here fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "clr.h")
+
+
+def _lib():
+    from chunked_linear_recurrence_chunk_amd import ops
+    return ops, ops.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gdn_fwd", "gdn_bwd", "gla_fwd", "gla_bwd", "clr_workspace_bytes", "clr_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    ops, lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    ops, lib = _lib()
+    assert lib.clr_version() >= 100
+    for s in range(5):
+        assert ops.status_string(s)
+
+
+def _shape(ops, B=1, T=128, H=2, dk=128, dv=128, dtype=1):
+    return ops.ClrShape(B, T, H, dk, dv, dtype)
+
+
+def test_workspace_sizes():
+    ops, lib = _lib()
+    s = _shape(ops)
+    f = ops.workspace_bytes(s, ops.OP_GDN_FWD)
+    b = ops.workspace_bytes(s, ops.OP_GDN_BWD)
+    assert 0 < f < b
+    assert ops.workspace_bytes(_shape(ops, dk=96, dv=96), ops.OP_GDN_FWD) == 0      # unsupported
+    assert ops.workspace_bytes(_shape(ops, dk=128, dv=256), ops.OP_GDN_FWD) == 0    # GDN needs dk == dv
+    assert ops.workspace_bytes(_shape(ops, dk=128, dv=256), ops.OP_GLA_FWD) > 0
+    assert ops.workspace_bytes(_shape(ops, dtype=0), ops.OP_GDN_BWD) == 0          # fp32 bwd only d=32
+    assert ops.workspace_bytes(_shape(ops, dk=32, dv=32, dtype=0), ops.OP_GDN_BWD) > 0
+    # linear in the number of 64-token blocks
+    assert ops.workspace_bytes(_shape(ops, T=256), ops.OP_GDN_FWD) < 2.1 * ops.workspace_bytes(_shape(ops, T=128), ops.OP_GDN_FWD)
+
+
+P = ctypes.c_void_p
+
+
+def _fake(addr):
+    return P(addr)
+
+
+def _fwd(lib, ops, s, q=0x10000, k=0x20000, v=0x30000, g=0x40000, beta=0x50000, S_in=None, o=0x60000,
+         S_out=0x70000, ws=0x100000, nws=1 << 40, name="gdn_fwd"):
+    f = getattr(lib, name)
+    args = [ctypes.byref(s)] + [None if a is None else _fake(a) for a in (q, k, v, g, beta, S_in, o, S_out, ws)]
+    return f(*args, nws, None)
+
+
+def test_validation_errors_are_returned_before_any_launch():
+    ops, lib = _lib()
+    s = _shape(ops, T=64, H=1, dk=32, dv=32)
+    # the fake device addresses are never dereferenced: each call fails validation
+    assert _fwd(lib, ops, s, q=None) == ops.CLR_EINVAL                     # null input
+    assert _fwd(lib, ops, s, beta=None) == ops.CLR_EINVAL                  # GDN needs beta
+    assert _fwd(lib, ops, s, q=0x10008) == ops.CLR_EINVAL                  # misaligned
+    assert _fwd(lib, ops, s, o=0x10000) == ops.CLR_EINVAL                  # output aliases q
+    assert _fwd(lib, ops, s, ws=None) == ops.CLR_EWORKSPACE                # no workspace
+    assert _fwd(lib, ops, s, nws=16) == ops.CLR_EWORKSPACE                 # too small
+    assert _fwd(lib, ops, s, ws=0x100010) == ops.CLR_EWORKSPACE            # workspace misaligned
+    assert _fwd(lib, ops, _shape(ops, dk=96, dv=96)) == ops.CLR_ENOTSUP
+    assert _fwd(lib, ops, _shape(ops, dtype=7)) == ops.CLR_ENOTSUP
+    assert _fwd(lib, ops, _shape(ops, B=0)) == ops.CLR_EINVAL
+    assert _fwd(lib, ops, _shape(ops, T=-1)) == ops.CLR_EINVAL
+    # GLA rejects beta
+    assert _fwd(lib, ops, _shape(ops, dk=128, dv=256), name="gla_fwd") == ops.CLR_EINVAL
+    assert lib.gdn_fwd(None, *([None] * 9), 0, None) == ops.CLR_EINVAL
+
+
+def test_bwd_validation():
+    ops, lib = _lib()
+    s = _shape(ops, T=64, H=1, dk=32, dv=32)
+    ptrs = [_fake(0x10000 * (i + 1)) for i in range(14)] + [_fake(0x1000000)]
+    bad = list(ptrs)
+    bad[8] = None  # dq missing
+    assert lib.gdn_bwd(ctypes.byref(s), *bad, 1 << 40, None) == ops.CLR_EINVAL
+    bad = list(ptrs)
+    bad[12] = None  # dbeta missing for GDN
+    assert lib.gdn_bwd(ctypes.byref(s), *bad, 1 << 40, None) == ops.CLR_EINVAL
+    bad = list(ptrs)
+    bad[13] = bad[0]  # dS_in aliases q
+    assert lib.gdn_bwd(ctypes.byref(s), *bad, 1 << 40, None) == ops.CLR_EINVAL
+    # GLA: beta / dbeta must be NULL
+    sg = _shape(ops, T=64, H=1, dk=32, dv=32)
+    assert lib.gla_bwd(ctypes.byref(sg), *ptrs, 1 << 40, None) == ops.CLR_EINVAL
+    # fp32 backward at d = 64 is not supported
+    s64 = _shape(ops, T=64, H=1, dk=64, dv=64, dtype=0)
+    assert lib.gdn_bwd(ctypes.byref(s64), *ptrs, 1 << 40, None) == ops.CLR_ENOTSUP
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The package never imports the oracle and the binding refuses to run
+    without the built library."""
+    pkg = os.path.join(ROOT, "chunked_linear_recurrence_chunk_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert not re.search(r"^\s*(from|import)\s+oracle", src, flags=re.M), fn
+            assert "clr_oracle" not in src, fn
+    from chunked_linear_recurrence_chunk_amd import ops
+    with pytest.raises(OSError):
+        ops.load(os.path.join(ROOT, "does_not_exist.so"))
