@@ -62,10 +62,9 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     w.hT = c.take(nb * dk * dv * es);
     w.UT = c.take(nb * BLK * dv * es);
     if (bwd) {
-        w.QgT = c.take(nb * BLK * dk * es);
+        w.Rt = (float*)c.take(nb * dk * dv * 4);
         w.WT = c.take(nb * BLK * dk * es);
         w.Kh = c.take(nb * BLK * dk * es);
-        w.dOT = c.take(nb * BLK * dv * es);
         w.dvlT = c.take(nb * BLK * dv * es);
         w.dhT = c.take(nb * dk * dv * es);
         w.dUT = c.take(nb * BLK * dv * es);
@@ -79,8 +78,14 @@ GlaWs carve_gla(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
     GlaWs w{};
     w.bcum = (float*)c.take(nb * BLK * dk * 4);
+    w.KhT = c.take(nb * BLK * dk * es);
     w.hT = c.take(nb * dk * dv * es);
-    if (bwd) w.dhT = c.take(nb * dk * dv * es);
+    if (bwd) {
+        w.QgT = c.take(nb * BLK * dk * es);
+        w.Kh = c.take(nb * BLK * dk * es);
+        w.dh = c.take(nb * dk * dv * es);
+        w.dVs = c.take(nb * BLK * dv * es);
+    }
     if (total) *total = c.off;
     return w;
 }

@@ -137,6 +137,56 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// ---------------------------------------------------------------------------
+// Fragment-packed ("kmap-32") order.  Within every aligned group of 32
+// indices, index kmap(g, i) is stored at position 8g + i, so the eight
+// elements of one lane's fragment are contiguous (one 16-byte load for bf16).
+// Four consecutive indices starting at a multiple of 4 stay consecutive.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int kperm(int idx) {  // index -> stored position
+    const int c = idx & 31;
+    const int p = c < 16 ? ((c >> 2) << 3) + (c & 3) : (((c - 16) >> 2) << 3) + 4 + (c & 3);
+    return (idx & ~31) + p;
+}
+__device__ __forceinline__ int kunperm(int pos) {  // stored position -> index
+    const int p = pos & 31, g = p >> 3, i = p & 7;
+    return (pos & ~31) + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+}
+// Fragment from packed storage: p points at X[row][k0 + 8g].
+__device__ __forceinline__ Frag<bf16> ldfragP(const bf16* p) {
+    Frag<bf16> f;
+    f.v = *(const bf16x8*)p;
+    return f;
+}
+__device__ __forceinline__ Frag<float> ldfragP(const float* p) {
+    Frag<float> f;
+    f.lo = *(const f32x4*)p;
+    f.hi = *(const f32x4*)(p + 4);
+    return f;
+}
+// Store two vertically adjacent accumulator tiles (rows 0..15 in lo, 16..31
+// in hi) of one lane into packed storage at p = &X[col][k0 + 8g].
+__device__ __forceinline__ void st8P(bf16* p, f32x4 lo, f32x4 hi) {
+    *(bf16x8*)p = bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+                         (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+}
+__device__ __forceinline__ void st8P(float* p, f32x4 lo, f32x4 hi) {
+    *(f32x4*)p = lo;
+    *(f32x4*)(p + 4) = hi;
+}
+
+// Four contiguous elements kept in their storage type (fewer registers than
+// f32x4 for bf16), converted on use.
+template <typename E> struct Raw4;
+template <> struct Raw4<bf16> { bf16x4 v; };
+template <> struct Raw4<float> { f32x4 v; };
+__device__ __forceinline__ Raw4<bf16> ldraw4(const bf16* p) { return Raw4<bf16>{*(const bf16x4*)p}; }
+__device__ __forceinline__ Raw4<float> ldraw4(const float* p) { return Raw4<float>{*(const f32x4*)p}; }
+__device__ __forceinline__ f32x4 cvt4(Raw4<bf16> x) {
+    return f32x4{(float)x.v[0], (float)x.v[1], (float)x.v[2], (float)x.v[3]};
+}
+__device__ __forceinline__ f32x4 cvt4(Raw4<float> x) { return x.v; }
+
 // Inclusive prefix sum over the 64 lanes of a wave (lane order).
 __device__ __forceinline__ float wave_prefix_sum(float x) {
     const int l = lane_id();

@@ -27,11 +27,10 @@ struct GdnWs {
     void* hT;     // [.., dv, dk]   state entering the block, transposed
     void* UT;     // [.., dv, 64]   U^T (delta-rule new values)
     // backward only
-    void* QgT;    // [.., dk, 64]   (Diag(Gam) Q)^T
+    float* Rt;    // [.., dv, dk]   R^T, R = (Diag(Gam) Q)^T dO - W^T dvloc  (fp32)
     void* WT;     // [.., dk, 64]   W^T
     void* Kh;     // [.., 64, dk]   Diag(exp(gamma_C - gamma)) K      (token-major)
-    void* dOT;    // [.., dv, 64]   dO^T
-    void* dvlT;   // [.., dv, 64]   ((Q K^T * G * tril)^T dO)^T
+    void* dvlT;   // [.., dv, 64]   dvloc^T, dvloc = (Q K^T * G * tril)^T dO
     void* dhT;    // [.., dv, dk]   gradient w.r.t. the state leaving the block, transposed
     void* dUT;    // [.., dv, 64]   dU^T
 };
@@ -88,9 +87,15 @@ hipError_t launch_gdn_bwd(const GdnLaunch& L, hipStream_t st);
     CLR_CASE(E, 128, 256)
 
 struct GlaWs {
-    float* bcum;  // [.., 64, dk]  in-block cumulative log gate per channel
-    void* hT;     // [.., dv, dk]  state entering the block, transposed
-    void* dhT;    // [.., dv, dk]  gradient w.r.t. the state leaving the block, transposed
+    float* bcum;  // [.., 64, dk]  in-block cumulative log gate per channel (fp32)
+    void* KhT;    // [.., dk, 64]  (K * exp(b_C - b))^T, token index fragment-packed
+    void* hT;     // [.., dv, dk]  fwd: state entering the block as h^T (d packed);
+                  //               bwd: key-major h[d][v]
+    // backward only
+    void* QgT;    // [.., dk, 64]  (Q * exp(b))^T, token index fragment-packed
+    void* Kh;     // [.., 64, dk]  K * exp(b_C - b), d fragment-packed
+    void* dh;     // [.., dk, dv]  key-major gradient w.r.t. the state leaving the block
+    void* dVs;    // [.., 64, dv]  Kh dh (state part of dV), token-major
 };
 
 struct GlaLaunch {

@@ -6,11 +6,13 @@
 // recomputation, as in that paper's Sec. 4.1 setup), then:
 //
 //   prep   (as in the forward)        gamma, T, W, Ut, Kh^T
-//   prep2  (parallel over blocks)     (Diag(Gam) Q)^T, W^T, Kh, dO^T and
-//                                     dvloc = (Q K^T * G * tril)^T dO
+//   prep2  (parallel over blocks)     W^T, Kh, dvloc = (Q K^T * G * tril)^T dO and
+//                                     R = (Diag(Gam) Q)^T dO - W^T dvloc (the dS-independent
+//                                     part of the reverse state step)
 //   scan   (forward recompute)        h_n (state entering block n, key-major), U_n
 //   dscan  (reverse, sequential)      dh_n = dL/dS_{n+1};  dU_n = dvloc_n + Kh_n dh_n;
 //                                     dS_n = Gam_C dh_n + (Diag(Gam) Q_n)^T dO_n - W_n^T dU_n
+//                                          = Gam_C dh_n + R_n - W_n^T (Kh_n dh_n)
 //   intra  (parallel over blocks)     dq, dk, dv, dbeta, dg of every block from
 //                                     (h_n, dh_n, U_n, dU_n) by the block adjoints:
 //     dQ  = Diag(Gam) dO h^T + dPm K,   dPm = (dO U^T) * G * tril
@@ -34,13 +36,15 @@ template <typename E> struct GdnPrep2Args {
     const E *q, *k, *dO;
     const float* gam;
     const E* W;
-    E *QgT, *WT, *Kh, *dOT, *dvlT;
+    float* Rt;
+    E *WT, *Kh, *dvlT;
     int T, H, NC;
 };
 
 template <typename E> struct GdnScanBwdArgs {
     const float* gam;
-    const E *Kh, *QgT, *WT, *dOT, *dvlT;
+    const E *Kh, *WT, *dvlT;
+    const float* Rt;
     const float* dS_out;
     float* dS_in;
     E *dh, *dUT;
@@ -72,36 +76,26 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
     const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
 
     __shared__ float s_gam[BLK];
-    __shared__ E Qt[DK * PT], dOt[DV * PT], Wt[DK * PT];
+    __shared__ E Qt[DK * PT], dOt[DV * PT], Wt[DK * PT], dvlt[DV * PT];
 
     if (tid < BLK) s_gam[tid] = a.gam[chunk * BLK + tid];
     stage_transposed<E, DK>(qb, ldk, Qt, nvalid);
     stage_transposed<E, DV>(dob, ldv, dOt, nvalid);
-    stage_transposed<E, DK>(a.W + chunk * BLK * DK, DK, Wt, BLK);
+    stage_T<E, BLK, DK, PT, true>(a.W + chunk * BLK * DK, DK, Wt, BLK);  // W columns are fragment-packed
     __syncthreads();
 
     const float gC = s_gam[BLK - 1];
-    E* QgT = a.QgT + chunk * BLK * DK;
     E* WT = a.WT + chunk * BLK * DK;
     for (int idx = tid; idx < DK * (BLK / 4); idx += 256) {
         const int d = idx / (BLK / 4), t4 = (idx % (BLK / 4)) * 4;
-        f32x4 x = ld4(Qt + d * PT + t4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] *= __expf(s_gam[t4 + i]);
-        st4(QgT + (size_t)d * BLK + t4, x);
-        st4(WT + (size_t)d * BLK + t4, ld4(Wt + d * PT + t4));
+        st4(WT + (size_t)d * BLK + kperm(t4), ld4(Wt + d * PT + t4));
     }
-    E* dOT = a.dOT + chunk * BLK * DV;
-    for (int idx = tid; idx < DV * (BLK / 4); idx += 256) {
-        const int d = idx / (BLK / 4), t4 = (idx % (BLK / 4)) * 4;
-        st4(dOT + (size_t)d * BLK + t4, ld4(dOt + d * PT + t4));
-    }
-    // Kh[t][d] = exp(gamma_C - gamma_t) K[t][d]   (token-major)
+    // Kh[t][d] = exp(gamma_C - gamma_t) K[t][d]   (token-major, d fragment-packed)
     E* Kh = a.Kh + chunk * BLK * DK;
     for (int idx = tid; idx < BLK * (DK / 4); idx += 256) {
         const int t = idx / (DK / 4), d4 = (idx % (DK / 4)) * 4;
         f32x4 x = t < nvalid ? ld4(kb + (size_t)t * ldk + d4) : zero4();
-        st4(Kh + (size_t)t * DK + d4, x * __expf(gC - s_gam[t]));
+        st4(Kh + (size_t)t * DK + kperm(d4), x * __expf(gC - s_gam[t]));
     }
     // dvloc[s][v] = sum_t P[t][s] dO[t][v],  P[t][s] = (q_t . k_s) exp(gamma_t - gamma_s), s <= t.
     // Wave w owns s-block w: P[tb][w] tiles (rows t, cols s) chain into A = P^T.
@@ -133,13 +127,113 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag(dOt + (16 * vb + r) * PT + 32 * j + 4 * g));
-        st4(dvlT + (size_t)(16 * vb + r) * BLK + 16 * w + 4 * g, acc);
+        st4(dvlT + (size_t)(16 * vb + r) * BLK + kperm(16 * w + 4 * g), acc);
+        st4(dvlt + (16 * vb + r) * PT + 16 * w + 4 * g, acc);
+    }
+    // Qt <- (Diag(Gam) Q)^T in place
+    for (int idx = tid; idx < DK * (BLK / 4); idx += 256) {
+        const int d = idx / (BLK / 4), t4 = (idx % (BLK / 4)) * 4;
+        f32x4 x = ld4(Qt + d * PT + t4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] *= __expf(s_gam[t4 + i]);
+        st4(Qt + d * PT + t4, x);
+    }
+    __syncthreads();
+    // R[d][v] = sum_t Qg^T[d][t] dO[t][v] - sum_t W^T[d][t] dvloc[t][v]   -> stored as R^T[v][d] (fp32)
+    float* Rt = a.Rt + chunk * DK * DV;
+    for (int tile = w; tile < (DK / 16) * (DV / 16); tile += 4) {
+        const int db = tile % (DK / 16), vb = tile / (DK / 16);
+        f32x4 acc = zero4(), acc2 = zero4();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            mma(acc, ldfrag(Qt + (16 * db + r) * PT + 32 * j + 4 * g), ldfrag(dOt + (16 * vb + r) * PT + 32 * j + 4 * g));
+            mma(acc2, ldfrag(Wt + (16 * db + r) * PT + 32 * j + 4 * g), ldfrag(dvlt + (16 * vb + r) * PT + 32 * j + 4 * g));
+        }
+        *(f32x4*)(Rt + (size_t)(16 * vb + r) * DK + 16 * db + 4 * g) = acc - acc2;
     }
 }
 
 // ---------------------------------------------------------------------------
 // dscan: one wave per (16-wide value slice, head, batch), blocks in reverse.
 // ---------------------------------------------------------------------------
+template <typename E, int DK> struct ScanBwdOps {
+    Frag<E> kh[4][DK / 32];   // Kh rows (A: m = t, k = d)
+    Frag<E> wt[DK / 16][2];   // W^T rows (A: m = d, k = t)
+    f32x4 rt[DK / 16];        // R^T[v0 + r][16 db + 4 g ..]
+    Frag<E> dvl[2];           // dvloc^T[v0 + r][token tile pairs] (accumulator layout)
+    float gC;
+};
+
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void scan_bwd_load(ScanBwdOps<E, DK>& o, const GdnScanBwdArgs<E>& a, size_t chunk,
+                                              int v0, int r, int g) {
+    const E* Kh = a.Kh + chunk * BLK * DK;
+    const E* WT = a.WT + chunk * BLK * DK;
+    const float* Rt = a.Rt + chunk * DK * DV;
+    const E* dvlT = a.dvlT + chunk * BLK * DV;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) o.kh[tb][kk] = ldfragP(Kh + (size_t)(16 * tb + r) * DK + 32 * kk + 8 * g);
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o.wt[db][j] = ldfragP(WT + (size_t)(16 * db + r) * BLK + 32 * j + 8 * g);
+        o.rt[db] = *(const f32x4*)(Rt + (size_t)(v0 + r) * DK + 16 * db + 4 * g);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) o.dvl[j] = ldfragP(dvlT + (size_t)(v0 + r) * BLK + 32 * j + 8 * g);
+    o.gC = a.gam[chunk * BLK + BLK - 1];
+}
+
+// One reverse step: on entry dS = dL/dS_{n+1}; writes dh_n = dS and
+// dU_n = dvloc_n + Kh_n dS; leaves dS = dL/dS_n = Gam_C dS + R_n - W_n^T (Kh_n dS).
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 (&dS)[DK / 16],
+                                              const GdnScanBwdArgs<E>& a, size_t chunk, int v0, int r, int g,
+                                              E* tile) {
+    constexpr int ND = DK / 16;
+    store_state_kmajor<E, DK, DV>(a.dh + chunk * DK * DV, dS, tile, v0, r, g);
+    Frag<E> fs[DK / 32];
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+    f32x4 dUp[4];
+    E* dUT = a.dUT + chunk * BLK * DV;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, o.kh[tb][kk], fs[kk]);
+        dUp[tb] = acc;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const Frag<E>& f = o.dvl[j];
+        f32x4 lo, hi;
+        if constexpr (sizeof(E) == 2) {
+            lo = f32x4{(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]};
+            hi = f32x4{(float)f.v[4], (float)f.v[5], (float)f.v[6], (float)f.v[7]};
+        } else {
+            lo = f.lo;
+            hi = f.hi;
+        }
+        st8P(dUT + (size_t)(v0 + r) * BLK + 32 * j + 8 * g, dUp[2 * j] + lo, dUp[2 * j + 1] + hi);
+    }
+    Frag<E> fu[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fu[j] = frag_from_acc<E>(-dUp[2 * j], -dUp[2 * j + 1]);
+    const float GC = __expf(o.gC);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+        f32x4 acc = dS[db] * GC + o.rt[db];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma(acc, o.wt[db][j], fu[j]);
+        dS[db] = acc;
+    }
+}
+
+// dscan: one wave per (16-wide value slice, head, batch), blocks in reverse,
+// operands of the next block prefetched into a second register buffer.
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(64) void gdn_scan_bwd_kernel(GdnScanBwdArgs<E> a) {
     const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -156,51 +250,15 @@ __global__ __launch_bounds__(64) void gdn_scan_bwd_kernel(GdnScanBwdArgs<E> a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dS[db][i] = dSo ? dSo[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
 
-    for (int n = NC - 1; n >= 0; --n) {
-        const size_t chunk = bh * NC + n;
-        const float GC = __expf(a.gam[chunk * BLK + BLK - 1]);
-        const E* Kh = a.Kh + chunk * BLK * DK;
-        const E* QgT = a.QgT + chunk * BLK * DK;
-        const E* WT = a.WT + chunk * BLK * DK;
-        const E* dOT = a.dOT + chunk * BLK * DV;
-        const E* dvlT = a.dvlT + chunk * BLK * DV;
-        // dh_n (gradient w.r.t. the state leaving block n), key-major
-        E* dh = a.dh + chunk * DK * DV;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dh[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = from_f<E>(dS[db][i]);
-        // dU = dvloc + Kh dS
-        Frag<E> fs[DK / 32];
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
-        f32x4 dU[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            f32x4 acc = ld4(dvlT + (size_t)(v0 + r) * BLK + 16 * tb + 4 * g);
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk)
-                mma(acc, ldfrag(Kh + (size_t)(16 * tb + r) * DK + 32 * kk + 4 * g), fs[kk]);
-            dU[tb] = acc;
-            st4(a.dUT + chunk * BLK * DV + (size_t)(v0 + r) * BLK + 16 * tb + 4 * g, acc);
-        }
-        // dS <- Gam_C dS + (Diag(Gam) Q)^T dO - W^T dU
-        Frag<E> fo[2], fu[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            fo[j] = ldfrag(dOT + (size_t)(v0 + r) * BLK + 32 * j + 4 * g);
-            fu[j] = frag_from_acc<E>(-dU[2 * j], -dU[2 * j + 1]);
-        }
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            f32x4 acc = dS[db] * GC;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                mma(acc, ldfrag(QgT + (size_t)(16 * db + r) * BLK + 32 * j + 4 * g), fo[j]);
-                mma(acc, ldfrag(WT + (size_t)(16 * db + r) * BLK + 32 * j + 4 * g), fu[j]);
-            }
-            dS[db] = acc;
-        }
+    __shared__ __align__(16) E tile[DK * 16];
+    ScanBwdOps<E, DK> A, B;
+    if (NC > 0) scan_bwd_load<E, DK, DV>(A, a, bh * NC + NC - 1, v0, r, g);
+    for (int n = NC - 1; n >= 0; n -= 2) {
+        if (n - 1 >= 0) scan_bwd_load<E, DK, DV>(B, a, bh * NC + n - 1, v0, r, g);
+        scan_bwd_step<E, DK, DV>(A, dS, a, bh * NC + n, v0, r, g, tile);
+        if (n - 1 < 0) break;
+        if (n - 2 >= 0) scan_bwd_load<E, DK, DV>(A, a, bh * NC + n - 2, v0, r, g);
+        scan_bwd_step<E, DK, DV>(B, dS, a, bh * NC + n - 1, v0, r, g, tile);
     }
     float* dSi = a.dS_in + bh * DK * DV;
 #pragma unroll
@@ -309,7 +367,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     E* Qt = (E*)(lds + Lay::pA_Qt);
     E* Us = (E*)(lds + Lay::pA_U);
     stage_transposed<E, DK>(qb, ldk, Qt, nvalid);
-    stage_T<E, DV, BLK, PDV>(UT, BLK, Us, DV);  // Us[t][v] = U[t][v]
+    stage_T<E, DV, BLK, PDV, true>(UT, BLK, Us, DV);  // Us[t][v] = U[t][v]
     __syncthreads();
 
     const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
@@ -425,7 +483,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     E* dWT = (E*)(lds + Lay::pB_dWT);
     E* dTT = (E*)(lds + Lay::pB_dTT);
     E* Ms = (E*)(lds + Lay::pB_Ms);
-    stage_T<E, DV, BLK, PDV>(dUT, BLK, dUs, DV);  // dUs[t][v]
+    stage_T<E, DV, BLK, PDV, true>(dUT, BLK, dUs, DV);  // dUs[t][v]
     __syncthreads();
     // dW^T[db][w] = -(S0 dU^T): rows d, cols t = tw
     {
@@ -508,7 +566,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            mma(acc, ldfrag(dUT + (size_t)(16 * vb + r) * BLK + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
+            mma(acc, ldfragP(dUT + (size_t)(16 * vb + r) * BLK + 32 * j + 8 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
         if (tw < nvalid) {
             const f32x4 vv = ld4(vbase + (size_t)tw * ldv + 16 * vb + 4 * g);
             dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
@@ -570,13 +628,13 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
                       ws.gam, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
     launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, gblk, dim3(256), st, pa);
     GdnPrep2Args<E> p2{(const E*)L.q, (const E*)L.k, (const E*)L.dO, ws.gam, (const E*)ws.W,
-                       (E*)ws.QgT, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dOT, (E*)ws.dvlT, L.T, L.H, L.NC};
+                       ws.Rt, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dvlT, L.T, L.H, L.NC};
     launch("gdn_prep2", gdn_prep2_kernel<E, DK, DV>, gblk, dim3(256), st, p2);
     GdnScanArgs<E> sa{ws.gam, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, (E*)ws.UT, L.H, L.NC};
     launch("gdn_scan_fwd_rec", gdn_scan_fwd_kernel<E, DK, DV, true>, dim3(DV / 16, L.H, L.B), dim3(64), st, sa);
-    GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.QgT, (const E*)ws.WT, (const E*)ws.dOT,
-                         (const E*)ws.dvlT, L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC};
+    GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
+                         L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC};
     launch("gdn_scan_bwd", gdn_scan_bwd_kernel<E, DK, DV>, dim3(DV / 16, L.H, L.B), dim3(64), st, sb);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const E*)ws.dUT,

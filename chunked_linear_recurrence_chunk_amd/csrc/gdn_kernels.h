@@ -87,7 +87,9 @@ __device__ inline void tri_inverse_64(const float* Am, float* Tm, float* Xs) {
 // Transposed staging of an R x CC tile (row stride ld elements in global
 // memory) into LDS dst[CC][DP]:  dst[c][r] = src[r][c].  Rows r >= nvalid
 // (tokens past the end of the sequence) are staged as zeros.
-template <typename E, int R, int CC, int DP>
+// With PERM the source columns are in fragment-packed order and are restored
+// to natural order in dst.
+template <typename E, int R, int CC, int DP, bool PERM = false>
 __device__ void stage_T(const E* __restrict__ src, size_t ld, E* dst, int nvalid) {
     constexpr int VEC = 16 / sizeof(E);  // elements per 16-byte load
     constexpr int PER_ROW = CC / VEC;
@@ -99,7 +101,8 @@ __device__ void stage_T(const E* __restrict__ src, size_t ld, E* dst, int nvalid
 #pragma unroll
         for (int ii = 0; ii < VEC; ++ii) {
             const int i = (ii + cb) % VEC;  // rotate to spread LDS banks
-            dst[(cb * VEC + i) * DP + t] = tmp[i];
+            const int c = PERM ? kunperm(cb * VEC + i) : cb * VEC + i;
+            dst[c * DP + t] = tmp[i];
         }
     }
 }
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
             Frag<E> fb = ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g);
             mma(acc, fa, fb);
         }
-        st4(Wout + (size_t)(16 * tb + r) * DK + 16 * db + 4 * g, acc);
+        st4(Wout + (size_t)(16 * tb + r) * DK + kperm(16 * db + 4 * g), acc);
     }
     // Ut[t][v] = sum_s T2[t][s] Vt[v][s]  -> written as Ut^T[v][t]
     E* Uout = a.UtT + chunk * BLK * DV;
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
             Frag<E> fb = ldfrag(Vt + (16 * vb + r) * PT + 32 * j + 4 * g);
             mma(acc, fa, fb);
         }
-        st4(Uout + (size_t)(16 * vb + r) * BLK + 16 * tb + 4 * g, acc);
+        st4(Uout + (size_t)(16 * vb + r) * BLK + kperm(16 * tb + 4 * g), acc);
     }
     // Kh^T[d][t] = exp(gamma_C - gamma_t) K[t][d]
     E* Khout = a.KhT + chunk * BLK * DK;
@@ -211,15 +214,128 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         f32x4 x = ld4(Kt + d * PT + t4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] *= __expf(gC - s_gam[t4 + i]);
-        st4(Khout + (size_t)d * BLK + t4, x);
+        st4(Khout + (size_t)d * BLK + kperm(t4), x);
     }
 }
 
 // ---------------------------------------------------------------------------
 // scan: one wave per (16-wide value slice, head, batch); sequential over the
 // blocks.  The fp32 state slice S[0:DK][v0:v0+16] lives in accumulator tiles.
-// Writes h_n^T[v][d] (state entering block n) and U_n^T[v][t].
+// Writes the state entering each block and U_n^T[v][t].  The operands of
+// block n+1 are loaded while block n is computed (two register buffers,
+// loop unrolled by two so the buffers never need copying).
 // ---------------------------------------------------------------------------
+template <typename E, int DK> struct ScanFwdOps {
+    Frag<E> w[4][DK / 32];    // W rows (A: m = t, k = d)
+    Frag<E> kh[DK / 16][2];   // Kh^T rows (A: m = d, k = t)
+    Frag<E> ut[2];            // Ut^T[v0 + r][token pair-tiles 2j, 2j+1] (accumulator layout)
+    float gC;                 // gamma at the last token of the block
+};
+
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void scan_fwd_load(ScanFwdOps<E, DK>& o, const GdnScanArgs<E>& a, size_t chunk,
+                                              int v0, int r, int g) {
+    const E* W = a.W + chunk * BLK * DK;
+    const E* KhT = a.KhT + chunk * BLK * DK;
+    const E* UtT = a.UtT + chunk * BLK * DV;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) o.w[tb][kk] = ldfragP(W + (size_t)(16 * tb + r) * DK + 32 * kk + 8 * g);
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o.kh[db][j] = ldfragP(KhT + (size_t)(16 * db + r) * BLK + 32 * j + 8 * g);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) o.ut[j] = ldfragP(UtT + (size_t)(v0 + r) * BLK + 32 * j + 8 * g);
+    o.gC = a.gam[chunk * BLK + BLK - 1];
+}
+
+// Store the fp32 state slice (accumulator tiles, rows d, column v0 + r) in
+// key-major h[d][v] layout: staged through LDS (tile[d][16 v]) so that each
+// lane writes whole 16-byte rows instead of scattered elements.
+// More generally: store ROWS x 16 accumulator tiles (rows 16 rb + 4 g + i,
+// column c0 + r) into a row-major matrix with row stride ld, through LDS.
+template <typename E, int ROWS>
+__device__ __forceinline__ void store_rows16(E* dst, size_t ld, const f32x4 (&X)[ROWS / 16], E* tile, int c0, int r,
+                                             int g) {
+    const int l = 16 * g + r;
+#pragma unroll
+    for (int rb = 0; rb < ROWS / 16; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tile[(16 * rb + 4 * g + i) * 16 + r] = from_f<E>(X[rb][i]);
+    __syncthreads();  // single-wave work-group: orders the LDS writes before the reads
+    constexpr int VEC = 16 / sizeof(E), PER_ROW = 16 / VEC;
+#pragma unroll
+    for (int c = l; c < ROWS * PER_ROW; c += 64) {
+        const int d = c / PER_ROW, part = c % PER_ROW;
+        *(uint4*)(dst + (size_t)d * ld + c0 + part * VEC) = *(const uint4*)(tile + d * 16 + part * VEC);
+    }
+    __syncthreads();  // reads done before the tile is rewritten
+}
+
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void store_state_kmajor(E* h, const f32x4 (&S)[DK / 16], E* tile, int v0, int r, int g) {
+    store_rows16<E, DK>(h, DV, S, tile, v0, r, g);
+}
+
+template <typename E, int DK, int DV, bool HNAT>
+__device__ __forceinline__ void scan_fwd_step(const ScanFwdOps<E, DK>& o, f32x4 (&S)[DK / 16],
+                                              const GdnScanArgs<E>& a, size_t chunk, int v0, int r, int g,
+                                              E* tile) {
+    constexpr int ND = DK / 16;
+    // state entering block n
+    if (a.hT) {
+        E* hT = a.hT + chunk * DK * DV;
+        if constexpr (HNAT) {
+            store_state_kmajor<E, DK, DV>(hT, S, tile, v0, r, g);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) st8P(hT + (size_t)(v0 + r) * DK + 32 * kk + 8 * g, S[2 * kk], S[2 * kk + 1]);
+        }
+    }
+    // U = Ut - W S    (tiles: rows t = 16tb + 4g + i, col v0 + r)
+    Frag<E> fs[DK / 32];
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
+    f32x4 U[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, o.w[tb][kk], fs[kk]);
+        U[tb] = acc;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const Frag<E>& f = o.ut[j];
+        if constexpr (sizeof(E) == 2) {
+            U[2 * j] = f32x4{(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]} - U[2 * j];
+            U[2 * j + 1] = f32x4{(float)f.v[4], (float)f.v[5], (float)f.v[6], (float)f.v[7]} - U[2 * j + 1];
+        } else {
+            U[2 * j] = f.lo - U[2 * j];
+            U[2 * j + 1] = f.hi - U[2 * j + 1];
+        }
+    }
+    if (a.UT) {
+        E* UT = a.UT + chunk * BLK * DV;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) st8P(UT + (size_t)(v0 + r) * BLK + 32 * j + 8 * g, U[2 * j], U[2 * j + 1]);
+    }
+    // S <- Gam_C S + Kh^T U
+    Frag<E> fu[2];
+    fu[0] = frag_from_acc<E>(U[0], U[1]);
+    fu[1] = frag_from_acc<E>(U[2], U[3]);
+    const float GC = __expf(o.gC);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+        f32x4 acc = S[db] * GC;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma(acc, o.kh[db][j], fu[j]);
+        S[db] = acc;
+    }
+}
+
 // HNAT selects the layout of the saved states: false -> h^T[v][d] (read by the
 // forward's out kernel), true -> h[d][v] (read by the backward).
 template <typename E, int DK, int DV, bool HNAT>
@@ -238,61 +354,15 @@ __global__ __launch_bounds__(64) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[db][i] = Sin ? Sin[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
 
-    for (int n = 0; n < NC; ++n) {
-        const size_t chunk = bh * NC + n;
-        const E* W = a.W + chunk * BLK * DK;
-        const E* KhT = a.KhT + chunk * BLK * DK;
-        const E* UtT = a.UtT + chunk * BLK * DV;
-        const float GC = __expf(a.gam[chunk * BLK + BLK - 1]);
-
-        // state entering block n
-        if (a.hT) {
-            E* hT = a.hT + chunk * DK * DV;
-            if constexpr (HNAT) {
-#pragma unroll
-                for (int db = 0; db < ND; ++db)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) hT[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = from_f<E>(S[db][i]);
-            } else {
-#pragma unroll
-                for (int db = 0; db < ND; ++db) st4(hT + (size_t)(v0 + r) * DK + 16 * db + 4 * g, S[db]);
-            }
-        }
-        // U = Ut - W S    (tiles: rows t = 16tb + 4g + i, col v0 + r)
-        Frag<E> fs[DK / 32];
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
-        f32x4 U[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                Frag<E> fw = ldfrag(W + (size_t)(16 * tb + r) * DK + 32 * kk + 4 * g);
-                mma(acc, fw, fs[kk]);
-            }
-            f32x4 ut = ld4(UtT + (size_t)(v0 + r) * BLK + 16 * tb + 4 * g);
-            U[tb] = ut - acc;
-        }
-        if (a.UT) {
-            E* UT = a.UT + chunk * BLK * DV;
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) st4(UT + (size_t)(v0 + r) * BLK + 16 * tb + 4 * g, U[tb]);
-        }
-        // S <- Gam_C S + Kh^T U
-        Frag<E> fu[2];
-        fu[0] = frag_from_acc<E>(U[0], U[1]);
-        fu[1] = frag_from_acc<E>(U[2], U[3]);
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            f32x4 acc = S[db] * GC;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                Frag<E> fk = ldfrag(KhT + (size_t)(16 * db + r) * BLK + 32 * j + 4 * g);
-                mma(acc, fk, fu[j]);
-            }
-            S[db] = acc;
-        }
+    __shared__ __align__(16) E tile[HNAT ? DK * 16 : 8];
+    ScanFwdOps<E, DK> A, B;
+    if (NC > 0) scan_fwd_load<E, DK, DV>(A, a, bh * NC, v0, r, g);
+    for (int n = 0; n < NC; n += 2) {
+        if (n + 1 < NC) scan_fwd_load<E, DK, DV>(B, a, bh * NC + n + 1, v0, r, g);
+        scan_fwd_step<E, DK, DV, HNAT>(A, S, a, bh * NC + n, v0, r, g, tile);
+        if (n + 1 >= NC) break;
+        if (n + 2 < NC) scan_fwd_load<E, DK, DV>(A, a, bh * NC + n + 2, v0, r, g);
+        scan_fwd_step<E, DK, DV, HNAT>(B, S, a, bh * NC + n + 1, v0, r, g, tile);
     }
     if (a.S_out) {
         float* So = a.S_out + bh * DK * DV;
@@ -358,14 +428,14 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
-            Frag<E> fh = ldfrag(hT + (size_t)(16 * vb + r) * DK + 32 * kk + 4 * g);
+            Frag<E> fh = ldfragP(hT + (size_t)(16 * vb + r) * DK + 32 * kk + 8 * g);
             mma(acc, fh, fq[kk]);
         }
         acc = acc * Gt;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             if (2 * j <= w) {
-                Frag<E> fu = ldfrag(UT + (size_t)(16 * vb + r) * BLK + 32 * j + 4 * g);
+                Frag<E> fu = ldfragP(UT + (size_t)(16 * vb + r) * BLK + 32 * j + 8 * g);
                 mma(acc, fu, fp[j]);
             }
         }

@@ -1,7 +1,706 @@
-// gla.hip -- GLA chunk forward/backward on gfx950 (in progress).
-#include "clr_kernels.h"
+// gla.hip -- Gated Linear Attention (per-key-channel decay, no delta term)
+// chunk forward and backward on gfx950.
+//
+// The layer (key-major state S in R^{dk x dv}, gate g_t in R^{dk}, g <= 0):
+//   S_t = Diag(exp(g_t)) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t,
+// the "rank-1" (element-wise) gated transition of the StateFlow paper
+// ("StateFlow: Sequence Pipeline Parallelism for Long-Context Modeling with
+// Linear Recurrence", Sec. 2.1).  Per 64-token block, b = cumsum(g) per
+// channel, S0 the state entering the block:
+//   O  = (Q * exp(b)) S0 + P V,   P[t][s] = sum_i q_t[i] k_s[i] exp(b_t[i] - b_s[i])  (s <= t)
+//   S1 = Diag(exp(b_C)) S0 + (K * exp(b_C - b))^T V
+// Following the numerics notes on the GLA paper's page (relative decay in log
+// space, 16-token secondary tiles, reciprocal rescaling bounded by e^80 so the
+// diagonal tiles can also use dense matrix products), P is formed per pair of
+// 16-token tiles (R, S): off-diagonal pairs use the boundary before tile R as
+// reference, so both rescaling factors are <= 1 and the product is exact for
+// any gates; diagonal pairs use the tile's middle token as reference, exact
+// while the decay within half a tile stays within 80 nats per channel (factors
+// are clamped at e^80 beyond that, which keeps everything finite).
+//
+// Kernels:  prep (b, Kh^T; backward also (Q*exp(b))^T and Kh),
+//           scan (sequential over blocks: S <- exp(b_C) * S + Kh^T V, saving h_n),
+//           out  (parallel over blocks),
+//           dscan (reverse: dS <- exp(b_C) * dS + (Q*exp(b))^T dO, saving dh_n and Kh dh_n),
+//           intra (parallel over blocks: dq, dk, dv, dg by the block adjoints; dg by the
+//                  per-channel gate scaling identity
+//                  dg_r[i] = sum_{tau >= r}(q dq - k dk)[i] + rowsum(S1 * dh)[i]).
+#include "gdn_kernels.h"
 
 namespace clr {
-hipError_t launch_gla_fwd(const GlaLaunch&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_gla_bwd(const GlaLaunch&, hipStream_t) { return hipErrorNotSupported; }
+
+// exp clamped at e^80 (the rescaling bound of the diagonal tiles)
+__device__ __forceinline__ float expu(float x) { return __expf(fminf(x, 80.f)); }
+
+template <typename E> struct GlaPrepArgs {
+    const E *q, *k, *g;
+    int T, H, NC;
+    float* bcum;
+    E *KhT, *QgT, *Kh;
+};
+template <typename E> struct GlaScanArgs {
+    const float* bcum;
+    const E *KhT, *v;
+    const float* S_in;
+    float* S_out;
+    E* hT;
+    int T, H, NC;
+};
+template <typename E> struct GlaOutArgs {
+    const E *q, *k, *v;
+    const float* bcum;
+    const E* hT;
+    E* o;
+    int T, H, NC;
+};
+template <typename E> struct GlaScanBwdArgs {
+    const float* bcum;
+    const E *Kh, *QgT, *dO;
+    const float* dS_out;
+    float* dS_in;
+    E *dh, *dVs;
+    int T, H, NC;
+};
+template <typename E> struct GlaIntraArgs {
+    const E *q, *k, *v, *dO;
+    const float* bcum;
+    const E *h, *dh, *dVs;
+    E *dq, *dk, *dv, *dg;
+    int T, H, NC;
+};
+
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *(const f32x4*)p; }
+
+__device__ __forceinline__ Frag<bf16> zero_frag(bf16*) {
+    Frag<bf16> f;
+    f.v = bf16x8{};
+    return f;
+}
+__device__ __forceinline__ Frag<float> zero_frag(float*) {
+    Frag<float> f;
+    f.lo = zero4();
+    f.hi = zero4();
+    return f;
+}
+
+// Fragment of token-major row `row` (k = feature index col + kmap(g, .)),
+// each element scaled by exp(bA[c] - bB[c]) (bB may be null: exp(bA[c])).
+template <typename E>
+__device__ __forceinline__ Frag<E> ldfrag_decay(const E* base, size_t ld, int row, int nvalid, int col,
+                                                const float* bA, const float* bB) {
+    if (row >= nvalid) return zero_frag((E*)nullptr);
+    f32x4 a0 = ld4f(bA + col), a1 = ld4f(bA + col + 16);
+    if (bB) {
+        a0 = a0 - ld4f(bB + col);
+        a1 = a1 - ld4f(bB + col + 16);
+    }
+    f32x4 s0, s1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s0[i] = expu(a0[i]);
+        s1[i] = expu(a1[i]);
+    }
+    return ldfrag_scaled(base + (size_t)row * ld + col, s0, s1);
+}
+
+// Fragment of a transposed LDS tile X^T[m][k] (m = feature row, k = token,
+// pitch PT) scaled per element by exp(sgn * (bT[m][k] - ref)), and zero for
+// tokens outside [klo, khi).  bT is the transposed gate tile (pitch BPT).
+constexpr int BPT = BLK + 4;
+template <typename E>
+__device__ __forceinline__ Frag<E> ldfragT_decay(const E* X, const float* bT, int m, int k0, float ref, float sgn,
+                                                 int klo, int khi) {
+    const int g = (threadIdx.x & 63) >> 4;
+    f32x4 s0, s1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ka = k0 + 4 * g + i, kb = k0 + 16 + 4 * g + i;
+        s0[i] = (ka >= klo && ka < khi) ? expu(sgn * (bT[m * BPT + ka] - ref)) : 0.f;
+        s1[i] = (kb >= klo && kb < khi) ? expu(sgn * (bT[m * BPT + kb] - ref)) : 0.f;
+    }
+    return ldfrag_scaled(X + m * PT + k0 + 4 * g, s0, s1);
+}
+
+// B fragment of a token-major tensor with k = token (t = 32 j + kmap(g, i)),
+// n = column c: eight element loads (rows past the sequence end are zero).
+template <typename E>
+__device__ __forceinline__ Frag<E> ldfrag_tokcol(const E* base, size_t ld, int j, int g, int c, int nvalid) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = 32 * j + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+        x[i] = t < nvalid ? to_f(base[(size_t)t * ld + c]) : 0.f;
+    }
+    return frag_from_acc<E>(f32x4{x[0], x[1], x[2], x[3]}, f32x4{x[4], x[5], x[6], x[7]});
+}
+
+// ---------------------------------------------------------------------------
+// prep: one work-group per (block, head, batch).
+// ---------------------------------------------------------------------------
+template <typename E, int DK, bool BWD>
+__global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int T = a.T, H = a.H, NC = a.NC;
+    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
+    const size_t chunk = ((size_t)b * H + h) * NC + n;
+    const int nvalid = min(BLK, T - n * BLK);
+    const size_t ldk = (size_t)H * DK;
+    constexpr int SB = DK + 4;
+
+    __shared__ float sb[BLK * SB];
+    __shared__ E Kt[DK * PT];
+    __shared__ E Qt[BWD ? DK * PT : 8];
+
+    if (tid < DK) {
+        float run = 0.f;
+        float* bc = a.bcum + chunk * BLK * DK;
+        for (int t = 0; t < BLK; ++t) {
+            run += t < nvalid ? to_f(a.g[(tok0 + t) * ldk + (size_t)h * DK + tid]) : 0.f;
+            sb[t * SB + tid] = run;
+            bc[(size_t)t * DK + tid] = run;
+        }
+    }
+    stage_transposed<E, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, Kt, nvalid);
+    if constexpr (BWD) stage_transposed<E, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, Qt, nvalid);
+    __syncthreads();
+
+    E* KhT = a.KhT + chunk * BLK * DK;
+    E* QgT = BWD ? a.QgT + chunk * BLK * DK : nullptr;
+    for (int idx = tid; idx < DK * (BLK / 4); idx += 256) {
+        const int d = idx / (BLK / 4), t4 = (idx % (BLK / 4)) * 4;
+        const float bC = sb[(BLK - 1) * SB + d];
+        f32x4 x = ld4(Kt + d * PT + t4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] *= __expf(bC - sb[(t4 + i) * SB + d]);
+        st4(KhT + (size_t)d * BLK + kperm(t4), x);
+        if constexpr (BWD) {
+            f32x4 y = ld4(Qt + d * PT + t4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] *= __expf(sb[(t4 + i) * SB + d]);
+            st4(QgT + (size_t)d * BLK + kperm(t4), y);
+        }
+    }
+    if constexpr (BWD) {
+        E* Kh = a.Kh + chunk * BLK * DK;
+        const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
+        for (int idx = tid; idx < BLK * (DK / 4); idx += 256) {
+            const int t = idx / (DK / 4), d4 = (idx % (DK / 4)) * 4;
+            f32x4 x = t < nvalid ? ld4(kb + (size_t)t * ldk + d4) : zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] *= __expf(sb[(BLK - 1) * SB + d4 + i] - sb[t * SB + d4 + i]);
+            st4(Kh + (size_t)t * DK + kperm(d4), x);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// scan: one wave per (16-wide value slice, head, batch).  The per-channel
+// decay makes the state update element-wise plus one product, Kh^T V, that
+// does not depend on S; operands of block n+1 are prefetched during block n.
+// ---------------------------------------------------------------------------
+template <typename E, int DK> struct GlaScanOps {
+    Frag<E> kh[DK / 16][2];  // Kh^T rows (A: m = d, k = t)
+    Frag<E> vb[2];           // V (B: k = t, n = v0 + r)
+    f32x4 bC[DK / 16];       // b_C for rows d = 16 db + 4 g + i
+};
+
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void gla_scan_load(GlaScanOps<E, DK>& o, const GlaScanArgs<E>& a, int b, int h, int n,
+                                              size_t chunk, int v0, int r, int g) {
+    const size_t tok0 = (size_t)b * a.T + (size_t)n * BLK;
+    const int nvalid = min(BLK, a.T - n * BLK);
+    const E* KhT = a.KhT + chunk * BLK * DK;
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o.kh[db][j] = ldfragP(KhT + (size_t)(16 * db + r) * BLK + 32 * j + 8 * g);
+        o.bC[db] = ld4f(a.bcum + (chunk * BLK + BLK - 1) * DK + 16 * db + 4 * g);
+    }
+    const size_t ldv = (size_t)a.H * DV;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) o.vb[j] = ldfrag_tokcol(a.v + tok0 * ldv + (size_t)h * DV, ldv, j, g, v0 + r, nvalid);
+}
+
+template <typename E, int DK, int DV, bool HNAT>
+__device__ __forceinline__ void gla_scan_step(const GlaScanOps<E, DK>& o, f32x4 (&S)[DK / 16],
+                                              const GlaScanArgs<E>& a, size_t chunk, int v0, int r, int g, E* tile) {
+    if (a.hT) {
+        E* hT = a.hT + chunk * DK * DV;
+        if constexpr (HNAT) {
+            store_state_kmajor<E, DK, DV>(hT, S, tile, v0, r, g);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) st8P(hT + (size_t)(v0 + r) * DK + 32 * kk + 8 * g, S[2 * kk], S[2 * kk + 1]);
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db) {
+        f32x4 dec;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dec[i] = __expf(o.bC[db][i]);
+        f32x4 acc = S[db] * dec;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma(acc, o.kh[db][j], o.vb[j]);
+        S[db] = acc;
+    }
+}
+
+template <typename E, int DK, int DV, bool HNAT>
+__global__ __launch_bounds__(64) void gla_scan_fwd_kernel(GlaScanArgs<E> a) {
+    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int l = threadIdx.x, r = l & 15, g = l >> 4;
+    const int H = a.H, NC = a.NC;
+    const int v0 = 16 * vb;
+    constexpr int ND = DK / 16;
+    const size_t bh = (size_t)b * H + h;
+    f32x4 S[ND];
+    const float* Sin = a.S_in ? a.S_in + bh * DK * DV : nullptr;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[db][i] = Sin ? Sin[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
+
+    __shared__ __align__(16) E tile[HNAT ? DK * 16 : 8];
+    GlaScanOps<E, DK> A, B;
+    if (NC > 0) gla_scan_load<E, DK, DV>(A, a, b, h, 0, bh * NC, v0, r, g);
+    for (int n = 0; n < NC; n += 2) {
+        if (n + 1 < NC) gla_scan_load<E, DK, DV>(B, a, b, h, n + 1, bh * NC + n + 1, v0, r, g);
+        gla_scan_step<E, DK, DV, HNAT>(A, S, a, bh * NC + n, v0, r, g, tile);
+        if (n + 1 >= NC) break;
+        if (n + 2 < NC) gla_scan_load<E, DK, DV>(A, a, b, h, n + 2, bh * NC + n + 2, v0, r, g);
+        gla_scan_step<E, DK, DV, HNAT>(B, S, a, bh * NC + n + 1, v0, r, g, tile);
+    }
+    if (a.S_out) {
+        float* So = a.S_out + bh * DK * DV;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) So[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = S[db][i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// out: one work-group (4 waves) per (block, head, batch); wave R owns tokens
+// 16R..16R+15.  O^T tiles: inter part (h^T (Q*exp(b))^T) plus P V.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void gla_out_kernel(GlaOutArgs<E> a) {
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, R = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int T = a.T, H = a.H, NC = a.NC;
+    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
+    const size_t chunk = ((size_t)b * H + h) * NC + n;
+    const int nvalid = min(BLK, T - n * BLK);
+    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
+    const E* qb = a.q + tok0 * ldk + (size_t)h * DK;
+    const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
+    const float* bc = a.bcum + chunk * BLK * DK;
+
+    __shared__ E Vt[DV * PT];
+    stage_transposed<E, DV>(a.v + tok0 * ldv + (size_t)h * DV, ldv, Vt, nvalid);
+    __syncthreads();
+
+    __shared__ float zrow[DK];
+    if (tid < DK) zrow[tid] = 0.f;
+    __syncthreads();
+    const int tl = 16 * R + r;
+    const float* bt = bc + (size_t)tl * DK;
+    const float* refO = R > 0 ? bc + (size_t)(16 * R - 1) * DK : zrow;  // boundary before tile R
+    const float* refD = bc + (size_t)(16 * R + 7) * DK;                 // middle of tile R
+    Frag<E> qi[DK / 32], qo[DK / 32], qd[DK / 32];
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) {
+        qi[kk] = ldfrag_decay(qb, ldk, tl, nvalid, 32 * kk + 4 * g, bt, (const float*)nullptr);
+        qo[kk] = ldfrag_decay(qb, ldk, tl, nvalid, 32 * kk + 4 * g, bt, refO);
+        qd[kk] = ldfrag_decay(qb, ldk, tl, nvalid, 32 * kk + 4 * g, bt, refD);
+    }
+    // P^T[sb][R]: rows s, column t = tl
+    f32x4 P[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+        f32x4 acc = zero4();
+        if (sb <= R) {
+            const int s = 16 * sb + r;
+            const float* ref = sb < R ? refO : refD;
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                Frag<E> fk = ldfrag_decay(kb, ldk, s, nvalid, 32 * kk + 4 * g, ref, bc + (size_t)s * DK);
+                mma(acc, fk, sb < R ? qo[kk] : qd[kk]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * sb + 4 * g + i > tl) acc[i] = 0.f;
+        }
+        P[sb] = acc;
+    }
+    Frag<E> fp[2];
+    fp[0] = frag_from_acc<E>(P[0], P[1]);
+    fp[1] = frag_from_acc<E>(P[2], P[3]);
+    const E* hT = a.hT + chunk * DK * DV;
+    E* ob = a.o + tok0 * ldv + (size_t)h * DV;
+    for (int vb = 0; vb < DV / 16; ++vb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, ldfragP(hT + (size_t)(16 * vb + r) * DK + 32 * kk + 8 * g), qi[kk]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (2 * j <= R) mma(acc, ldfrag(Vt + (16 * vb + r) * PT + 32 * j + 4 * g), fp[j]);
+        if (tl < nvalid) st4(ob + (size_t)tl * ldv + 16 * vb + 4 * g, acc);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dscan: one wave per (16-wide value slice, head, batch), blocks in reverse.
+// Saves dh_n (key-major) and dVs_n = Kh_n dh_n (the state part of dV).
+// ---------------------------------------------------------------------------
+template <typename E, int DK> struct GlaScanBwdOps {
+    Frag<E> kh[4][DK / 32];  // Kh rows (A: m = t, k = d)
+    Frag<E> qg[DK / 16][2];  // (Q*exp(b))^T rows (A: m = d, k = t)
+    Frag<E> dob[2];          // dO (B: k = t, n = v0 + r)
+    f32x4 bC[DK / 16];
+};
+
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void gla_dscan_load(GlaScanBwdOps<E, DK>& o, const GlaScanBwdArgs<E>& a, int b, int h,
+                                               int n, size_t chunk, int v0, int r, int g) {
+    const size_t tok0 = (size_t)b * a.T + (size_t)n * BLK;
+    const int nvalid = min(BLK, a.T - n * BLK);
+    const E* Kh = a.Kh + chunk * BLK * DK;
+    const E* QgT = a.QgT + chunk * BLK * DK;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) o.kh[tb][kk] = ldfragP(Kh + (size_t)(16 * tb + r) * DK + 32 * kk + 8 * g);
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o.qg[db][j] = ldfragP(QgT + (size_t)(16 * db + r) * BLK + 32 * j + 8 * g);
+        o.bC[db] = ld4f(a.bcum + (chunk * BLK + BLK - 1) * DK + 16 * db + 4 * g);
+    }
+    const size_t ldv = (size_t)a.H * DV;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) o.dob[j] = ldfrag_tokcol(a.dO + tok0 * ldv + (size_t)h * DV, ldv, j, g, v0 + r, nvalid);
+}
+
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void gla_dscan_step(const GlaScanBwdOps<E, DK>& o, f32x4 (&dS)[DK / 16],
+                                               const GlaScanBwdArgs<E>& a, size_t chunk, int v0, int r, int g, E* tile) {
+    store_state_kmajor<E, DK, DV>(a.dh + chunk * DK * DV, dS, tile, v0, r, g);
+    Frag<E> fs[DK / 32];
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+    f32x4 dVs[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, o.kh[tb][kk], fs[kk]);
+        dVs[tb] = acc;
+    }
+    store_rows16<E, BLK>(a.dVs + chunk * BLK * DV, DV, dVs, tile, v0, r, g);
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db) {
+        f32x4 dec;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dec[i] = __expf(o.bC[db][i]);
+        f32x4 acc = dS[db] * dec;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma(acc, o.qg[db][j], o.dob[j]);
+        dS[db] = acc;
+    }
+}
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(64) void gla_scan_bwd_kernel(GlaScanBwdArgs<E> a) {
+    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int l = threadIdx.x, r = l & 15, g = l >> 4;
+    const int H = a.H, NC = a.NC;
+    const int v0 = 16 * vb;
+    constexpr int ND = DK / 16;
+    const size_t bh = (size_t)b * H + h;
+    f32x4 dS[ND];
+    const float* dSo = a.dS_out ? a.dS_out + bh * DK * DV : nullptr;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dS[db][i] = dSo ? dSo[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
+
+    __shared__ __align__(16) E tile[(DK > BLK ? DK : BLK) * 16];
+    GlaScanBwdOps<E, DK> A, B;
+    if (NC > 0) gla_dscan_load<E, DK, DV>(A, a, b, h, NC - 1, bh * NC + NC - 1, v0, r, g);
+    for (int n = NC - 1; n >= 0; n -= 2) {
+        if (n - 1 >= 0) gla_dscan_load<E, DK, DV>(B, a, b, h, n - 1, bh * NC + n - 1, v0, r, g);
+        gla_dscan_step<E, DK, DV>(A, dS, a, bh * NC + n, v0, r, g, tile);
+        if (n - 1 < 0) break;
+        if (n - 2 >= 0) gla_dscan_load<E, DK, DV>(A, a, b, h, n - 2, bh * NC + n - 2, v0, r, g);
+        gla_dscan_step<E, DK, DV>(B, dS, a, bh * NC + n - 1, v0, r, g, tile);
+    }
+    float* dSi = a.dS_in + bh * DK * DV;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dSi[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = dS[db][i];
+}
+
+// ---------------------------------------------------------------------------
+// intra: one work-group (4 waves) per (block, head, batch); wave R owns tokens
+// 16R..16R+15 (as t for dq, as s for dk and dv).  All output tiles are
+// transposed ([feature][token]) so each lane stores four contiguous values.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, R = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int T = a.T, H = a.H, NC = a.NC;
+    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
+    const size_t chunk = ((size_t)b * H + h) * NC + n;
+    const int nvalid = min(BLK, T - n * BLK);
+    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
+    const E* qb = a.q + tok0 * ldk + (size_t)h * DK;
+    const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
+    const E* vbase = a.v + tok0 * ldv + (size_t)h * DV;
+    const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
+    const float* bc = a.bcum + chunk * BLK * DK;
+    const E* S0 = a.h + chunk * DK * DV;
+    const E* dS1 = a.dh + chunk * DK * DV;
+
+    __shared__ E Kt[DK * PT], Qt[DK * PT], dOt[DV * PT];
+    __shared__ float bT[DK * BPT];
+    __shared__ float dgb[BLK * (DK + 1)];
+    __shared__ float rsum[4][DK];
+    __shared__ float zrow[DK];
+
+    stage_transposed<E, DK>(kb, ldk, Kt, nvalid);
+    stage_transposed<E, DK>(qb, ldk, Qt, nvalid);
+    stage_transposed<E, DV>(dob, ldv, dOt, nvalid);
+    for (int idx = tid; idx < BLK * DK; idx += 256) {
+        const int t = idx / DK, d = idx % DK;
+        bT[d * BPT + t] = bc[idx];
+    }
+    if (tid < DK) zrow[tid] = 0.f;
+    __syncthreads();
+
+    const int tl = 16 * R + r;  // this lane's token (column of every transposed tile)
+    const float* bt = bc + (size_t)tl * DK;
+    const float* refO = R > 0 ? bc + (size_t)(16 * R - 1) * DK : zrow;
+    const float* refD = bc + (size_t)(16 * R + 7) * DK;
+    const float* refE = bc + (size_t)(16 * R + 15) * DK;
+    const float* bC = bc + (size_t)(BLK - 1) * DK;
+
+    Frag<E> fdo[DV / 32], fv[DV / 32];
+#pragma unroll
+    for (int kk = 0; kk < DV / 32; ++kk) {
+        fdo[kk] = ldfrag_row(dob, tl, nvalid, ldv, 32 * kk + 4 * g);    // Bt = dO, rows of tile R
+        fv[kk] = ldfrag_row(vbase, tl, nvalid, ldv, 32 * kk + 4 * g);   // Bt = V, rows of tile R
+    }
+    // (1) dP^T[sb][R] (rows s, col t = tl), (2) dP[tb][R] (rows t, col s = tl),
+    // (3) P[tb][R] (rows t, col s = tl); all masked to s <= t.
+    f32x4 dPT[4], dP[4], P[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        f32x4 acc = zero4();
+        if (x <= R) {
+#pragma unroll
+            for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfrag_row(vbase, 16 * x + r, nvalid, ldv, 32 * kk + 4 * g), fdo[kk]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * x + 4 * g + i > tl) acc[i] = 0.f;
+        }
+        dPT[x] = acc;
+        f32x4 acc2 = zero4(), acc3 = zero4();
+        if (x >= R) {
+#pragma unroll
+            for (int kk = 0; kk < DV / 32; ++kk) mma(acc2, ldfrag_row(dob, 16 * x + r, nvalid, ldv, 32 * kk + 4 * g), fv[kk]);
+            const float* ref = x > R ? refE : refD;
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                Frag<E> fq = ldfrag_decay(qb, ldk, 16 * x + r, nvalid, 32 * kk + 4 * g, bc + (size_t)(16 * x + r) * DK, ref);
+                Frag<E> fk = ldfrag_decay(kb, ldk, tl, nvalid, 32 * kk + 4 * g, ref, bt);
+                mma(acc3, fq, fk);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * x + 4 * g + i < tl) {
+                    acc2[i] = 0.f;
+                    acc3[i] = 0.f;
+                }
+        }
+        dP[x] = acc2;
+        P[x] = acc3;
+    }
+    // split dP^T into off-diagonal (s < 16R) and diagonal (s in tile R) parts,
+    // dP into later (t >= 16R + 16) and diagonal parts
+    Frag<E> fptO[2], fptD[2], fpL[2], fpD[2], fP[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        f32x4 o0 = (2 * j < R) ? dPT[2 * j] : zero4(), o1 = (2 * j + 1 < R) ? dPT[2 * j + 1] : zero4();
+        f32x4 d0 = (2 * j == R) ? dPT[2 * j] : zero4(), d1 = (2 * j + 1 == R) ? dPT[2 * j + 1] : zero4();
+        fptO[j] = frag_from_acc<E>(o0, o1);
+        fptD[j] = frag_from_acc<E>(d0, d1);
+        f32x4 l0 = (2 * j > R) ? dP[2 * j] : zero4(), l1 = (2 * j + 1 > R) ? dP[2 * j + 1] : zero4();
+        f32x4 e0 = (2 * j == R) ? dP[2 * j] : zero4(), e1 = (2 * j + 1 == R) ? dP[2 * j + 1] : zero4();
+        fpL[j] = frag_from_acc<E>(l0, l1);
+        fpD[j] = frag_from_acc<E>(e0, e1);
+        fP[j] = frag_from_acc<E>(P[2 * j], P[2 * j + 1]);
+    }
+    float rpart[DK / 16][4];
+    // (4) dQ^T and (5) dK^T, per 16-row block of features d
+    for (int db = 0; db < DK / 16; ++db) {
+        const int dm = 16 * db + r;  // feature row of this lane's A fragments
+        // dQ: inter  exp(b_t) (S0 dO^T)
+        f32x4 qi = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk) mma(qi, ldfrag(S0 + (size_t)dm * DV + 32 * kk + 4 * g), fdo[kk]);
+        // dQ: intra, off-diagonal (reference b_{16R-1}) and diagonal (reference b_{16R+7})
+        f32x4 qo = zero4(), qd = zero4();
+        const float rO = refO[dm], rD = refD[dm], rE = refE[dm];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (32 * j < 16 * R) mma(qo, ldfragT_decay(Kt, bT, dm, 32 * j, rO, -1.f, 0, 16 * R), fptO[j]);
+            if (32 * j <= 16 * R && 16 * R < 32 * j + 32)
+                mma(qd, ldfragT_decay(Kt, bT, dm, 32 * j, rD, -1.f, 16 * R, 16 * R + 16), fptD[j]);
+        }
+        // dK: intra, later tiles (reference b_{16R+15}) and diagonal; state part
+        f32x4 kl = zero4(), kd = zero4(), ks = zero4();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (32 * j + 32 > 16 * R + 16) mma(kl, ldfragT_decay(Qt, bT, dm, 32 * j, rE, 1.f, 16 * R + 16, BLK), fpL[j]);
+            if (32 * j <= 16 * R && 16 * R < 32 * j + 32)
+                mma(kd, ldfragT_decay(Qt, bT, dm, 32 * j, rD, 1.f, 16 * R, 16 * R + 16), fpD[j]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk) mma(ks, ldfrag(dS1 + (size_t)dm * DV + 32 * kk + 4 * g), fv[kk]);
+        // element-wise factors: rows d = 16 db + 4 g + i, column token tl
+        const int d0 = 16 * db + 4 * g;
+        const f32x4 btv = ld4f(bt + d0), rOv = ld4f(refO + d0), rDv = ld4f(refD + d0), rEv = ld4f(refE + d0);
+        const f32x4 bCv = ld4f(bC + d0);
+        f32x4 dq, dk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dq[i] = qi[i] * __expf(btv[i]) + qo[i] * __expf(btv[i] - rOv[i]) + qd[i] * expu(btv[i] - rDv[i]);
+            const float es = __expf(bCv[i] - btv[i]);
+            dk[i] = kl[i] * __expf(rEv[i] - btv[i]) + kd[i] * expu(rDv[i] - btv[i]) + ks[i] * es;
+        }
+        float qk[4] = {0.f, 0.f, 0.f, 0.f};
+        if (tl < nvalid) {
+            const f32x4 qv = ld4(qb + (size_t)tl * ldk + d0), kv = ld4(kb + (size_t)tl * ldk + d0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qk[i] = qv[i] * dq[i] - kv[i] * dk[i];
+                rpart[db][i] = kv[i] * __expf(bCv[i] - btv[i]) * ks[i];
+            }
+            st4(a.dq + (tok0 + tl) * ldk + (size_t)h * DK + d0, dq);
+            st4(a.dk + (tok0 + tl) * ldk + (size_t)h * DK + d0, dk);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rpart[db][i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dgb[tl * (DK + 1) + d0 + i] = qk[i];
+    }
+    // sum_s Kh[s][d] X[d][s] over this wave's 16 tokens
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x = rpart[db][i];
+            x += __shfl_xor(x, 1, 64);
+            x += __shfl_xor(x, 2, 64);
+            x += __shfl_xor(x, 4, 64);
+            x += __shfl_xor(x, 8, 64);
+            if (r == 0) rsum[R][16 * db + 4 * g + i] = x;
+        }
+    // (6) dV^T[vb][R] = dO^T P + (Kh dh)^T   (rows v, col s = tl)
+    const E* dVs = a.dVs + chunk * BLK * DV;
+    for (int vb = 0; vb < DV / 16; ++vb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (32 * j + 32 > 16 * R) mma(acc, ldfrag(dOt + (16 * vb + r) * PT + 32 * j + 4 * g), fP[j]);
+        if (tl < nvalid) {
+            acc = acc + ld4(dVs + (size_t)tl * DV + 16 * vb + 4 * g);
+            st4(a.dv + (tok0 + tl) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc);
+        }
+    }
+    __syncthreads();
+    // (7) dg[t][d] = sum_{tau >= t} dgb[tau][d] + rowsum(S1 * dh)[d]
+    for (int d = tid; d < DK; d += 256) {
+        float row = 0.f;
+        constexpr int VEC = 16 / sizeof(E);
+        for (int v = 0; v < DV; v += VEC) {
+            E x[VEC], y[VEC];
+            *(uint4*)x = *(const uint4*)(S0 + (size_t)d * DV + v);
+            *(uint4*)y = *(const uint4*)(dS1 + (size_t)d * DV + v);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) row += to_f(x[i]) * to_f(y[i]);
+        }
+        float acc = __expf(bC[d]) * row + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
+        for (int t = BLK - 1; t >= 0; --t) {
+            acc += dgb[t * (DK + 1) + d];
+            if (t < nvalid) a.dg[(tok0 + t) * ldk + (size_t)h * DK + d] = from_f<E>(acc);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+hipError_t launch_gla_fwd_t(const GlaLaunch& L, hipStream_t st) {
+    const dim3 gblk(L.NC, L.H, L.B);
+    const GlaWs& ws = L.ws;
+    GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC, ws.bcum, (E*)ws.KhT, nullptr, nullptr};
+    launch("gla_prep", gla_prep_kernel<E, DK, false>, gblk, dim3(256), st, pa);
+    GlaScanArgs<E> sa{ws.bcum, (const E*)ws.KhT, (const E*)L.v, L.S_in, L.S_out, (E*)ws.hT, L.T, L.H, L.NC};
+    launch("gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(DV / 16, L.H, L.B), dim3(64), st, sa);
+    if (L.o) {
+        GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)L.v, ws.bcum, (const E*)ws.hT, (E*)L.o, L.T, L.H, L.NC};
+        launch("gla_out", gla_out_kernel<E, DK, DV>, gblk, dim3(256), st, oa);
+    }
+    return hipGetLastError();
+}
+
+template <typename E, int DK, int DV>
+hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
+    const dim3 gblk(L.NC, L.H, L.B);
+    const GlaWs& ws = L.ws;
+    GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC,
+                      ws.bcum, (E*)ws.KhT, (E*)ws.QgT, (E*)ws.Kh};
+    launch("gla_prep_bwd", gla_prep_kernel<E, DK, true>, gblk, dim3(256), st, pa);
+    GlaScanArgs<E> sa{ws.bcum, (const E*)ws.KhT, (const E*)L.v, L.S_in, nullptr, (E*)ws.hT, L.T, L.H, L.NC};
+    launch("gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(DV / 16, L.H, L.B), dim3(64), st, sa);
+    GlaScanBwdArgs<E> sb{ws.bcum, (const E*)ws.Kh, (const E*)ws.QgT, (const E*)L.dO, L.dS_out, L.dS_in,
+                         (E*)ws.dh, (E*)ws.dVs, L.T, L.H, L.NC};
+    launch("gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(DV / 16, L.H, L.B), dim3(64), st, sb);
+    GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.dO, ws.bcum, (const E*)ws.hT,
+                       (const E*)ws.dh, (const E*)ws.dVs, (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, L.T, L.H, L.NC};
+    launch("gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV>, gblk, dim3(256), st, ia);
+    return hipGetLastError();
+}
+
+hipError_t launch_gla_fwd(const GlaLaunch& L, hipStream_t st) {
+#define CLR_CASE(E, DK, DV) \
+    if (L.dk == DK && L.dv == DV) return launch_gla_fwd_t<E, DK, DV>(L, st);
+    if (L.bf16) {
+        CLR_FOR_GLA_SHAPES(bf16)
+    } else {
+        CLR_FOR_GLA_SHAPES(float)
+    }
+#undef CLR_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gla_bwd(const GlaLaunch& L, hipStream_t st) {
+#define CLR_CASE(E, DK, DV) \
+    if (L.dk == DK && L.dv == DV) return launch_gla_bwd_t<E, DK, DV>(L, st);
+    if (L.bf16) {
+        CLR_FOR_GLA_SHAPES(bf16)
+    } else {
+        CLR_FOR_GDN_BWD_SHAPES_F32(float)
+    }
+#undef CLR_CASE
+    return hipErrorInvalidValue;
+}
+
 }  // namespace clr
