@@ -21,10 +21,11 @@
 //     dA  = -T^T dT T^T (strictly lower),  M = dA * beta_r * G,
 //     dV  = Diag(beta) T^T dU,
 //     dbeta_s = (T^T dU)_s . v_s + Gam_s (T^T dW)_s . k_s + sum_c dA[s,c] (K K^T * G)[s,c],
-//     dg_r = sum_{tau >= r in block} (q.dq - v.dv) + <S_{n+1}, dh_n>   (gate scaling identity:
-//            scaling alpha_r by e^eps equals scaling v_tau (tau >= r) by e^-eps and the
-//            outputs and later states by e^eps), with
-//            <S_{n+1}, dh_n> = Gam_C <h_n, dh_n> + sum_s exp(gamma_C - gamma_s) k_s . (U dh^T)_s.
+//     dg_u = sum_{t >= u} y_t + sum_{t >= u > s} (dP*P + dA*A)[t][s] + sum_{r < u} z_r
+//            + Gam_C <h_n, dh_n>,   the chain rule through gamma = cumsum(g) with the
+//            within-suffix pair terms (which cancel exactly) left out:
+//            y_t = q_t . (Gam_t h_n do_t) + beta_t Gam_t (T^T dW)_t . k_t,
+//            z_r = exp(gamma_C - gamma_r) k_r . (U dh^T)_r.
 // Products run on the matrix cores (bf16 operands, fp32 accumulation; fp32
 // operands for fp32 inputs); each work-group computes transposed ([feature][token])
 // output tiles so that every lane stores four contiguous values.
@@ -279,7 +280,8 @@ template <typename E, int DK, int DV> struct IntraLds {
     static constexpr size_t o_KKG = o_Kt + sizeof(E) * DK * PT;        // f32[64][65]   (K K^T * G), strictly lower
     static constexpr size_t o_TT = o_KKG + 4 * BLK * 65;               // E[64][PT]     TT[s][t] = T[t][s]
     static constexpr size_t o_Tr = o_TT + sizeof(E) * BLK * PT;        // E[64][PT]     T row-major
-    static constexpr size_t o_U = o_Tr + sizeof(E) * BLK * PT;         // union starts here
+    static constexpr size_t o_E = o_Tr + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms)
+    static constexpr size_t o_U = o_E + 4 * BLK * 65;                  // union starts here
     // phase 0: Am f32[64][65], Tm f32[64][65], Xs f32[16][17]
     static constexpr size_t p0_Am = o_U, p0_Tm = p0_Am + 4 * BLK * 65, p0_Xs = p0_Tm + 4 * BLK * 65;
     static constexpr size_t p0_end = p0_Xs + 4 * 16 * 17;
@@ -306,8 +308,9 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     float* KKG = (float*)(lds + Lay::o_KKG);
     E* TT = (E*)(lds + Lay::o_TT);
     E* Tr = (E*)(lds + Lay::o_Tr);
+    float* Eb = (float*)(lds + Lay::o_E);
 
-    __shared__ float s_gam[BLK], s_bet[BLK], s_qdq[BLK], s_vdv[BLK], s_kdk[BLK], s_dbg[BLK], s_red[4];
+    __shared__ float s_gam[BLK], s_bet[BLK], s_y[BLK], s_kdk[BLK], s_dbg[BLK], s_red[4];
 
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
@@ -395,7 +398,24 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         }
         dPT[sb] = acc;
     }
-    // dQ^T[db][w] = Gam_t (S0 dO^T) + K^T dPm^T
+    // Gate cross terms of the output path: E[t][s] = dP[t][s] P[t][s]
+    // = dPm[t][s] (q_t . k_s)  (s <= t), with (Q K^T)^T tiles rows s, col t = tw.
+    {
+        Frag<E> fq[DK / 32];
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) fq[kk] = ldfrag_row(qb, tw, nvalid, ldk, 32 * kk + 4 * g);
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            f32x4 qk = zero4();
+            if (sb <= w) {
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) mma(qk, ldfrag_row(kb, 16 * sb + r, nvalid, ldk, 32 * kk + 4 * g), fq[kk]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Eb[tw * 65 + 16 * sb + 4 * g + i] = dPT[sb][i] * qk[i];
+        }
+    }
+    // dQ^T[db][w] = Gam_t (S0 dO^T) + K^T dPm^T;  y_t = q_t . (inter part of dq_t)
     {
         Frag<E> fpt[2];
         fpt[0] = frag_from_acc<E>(dPT[0], dPT[1]);
@@ -407,17 +427,18 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
 #pragma unroll
             for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfrag(S0 + (size_t)(16 * db + r) * DV + 32 * kk + 4 * g), fdo[kk]);
             acc = acc * Gt;
+            f32x4 qv = zero4();
+            if (tw < nvalid) {
+                qv = ld4(qb + (size_t)tw * ldk + 16 * db + 4 * g);
+                qdq += qv[0] * acc[0] + qv[1] * acc[1] + qv[2] * acc[2] + qv[3] * acc[3];
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) mma(acc, ldfrag(Kt + (16 * db + r) * PT + 32 * j + 4 * g), fpt[j]);
-            if (tw < nvalid) {
-                const f32x4 qv = ld4(qb + (size_t)tw * ldk + 16 * db + 4 * g);
-                qdq += qv[0] * acc[0] + qv[1] * acc[1] + qv[2] * acc[2] + qv[3] * acc[3];
-                st4(a.dq + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, acc);
-            }
+            if (tw < nvalid) st4(a.dq + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, acc);
         }
         qdq += __shfl_xor(qdq, 16, 64);
         qdq += __shfl_xor(qdq, 32, 64);
-        if (g == 0) s_qdq[tw] = qdq;
+        if (g == 0) s_y[tw] = qdq;
     }
     // dPm[tb][w]: rows t, cols s = tw
     f32x4 dP[4];
@@ -543,6 +564,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
                 const int row = 16 * w + 4 * g + i;
                 const float dA = (c < row) ? -acc[i] : 0.f;
                 gram[i] += dA * KKG[row * 65 + c];
+                Eb[row * 65 + c] += dA * s_bet[row] * KKG[row * 65 + c];  // gate cross term dA * A
                 const float m = dA * s_bet[row] * __expf(s_gam[row] - s_gam[c]);
                 if (c <= row) Ms[row * PT + c] = from_f<E>(c < row ? m : 0.f);
                 if (c < row) Ms[c * PT + row] = from_f<E>(m);
@@ -597,23 +619,39 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     dbk += __shfl_xor(dbk, 16, 64);
     dbk += __shfl_xor(dbk, 32, 64);
     if (g == 0) {
-        s_vdv[tw] = dbv * bet_tw;  // v . dv
+        s_y[tw] += bet_tw * Gs * dbk;  // W path: dgamma_t from Gam_t in W = T Diag(beta Gam) K
         const float dbeta = dbv + Gs * dbk + s_dbg[tw];
         if (tw < nvalid) a.dbeta[(tok0 + tw) * H + h] = from_f<E>(dbeta);
     }
     __syncthreads();
-    // dg: reverse prefix over the block of (q.dq - v.dv) plus <S_{n+1}, dh_n>
+    // Gate gradient, summing only contributions that cross the token boundary
+    // (exact, and free of the cancellation a suffix sum of per-token terms has):
+    //   dg_u = sum_{t>=u} y_t + sum_{t>=u>s} E[t][s] + sum_{r<u} z_r + Gam_C <h_n, dh_n>
+    // with y_t the S0 -> token-t terms, E the pair terms (dP*P + dA*A) and
+    // z_r = kh_r . (U dh^T)_r the Kh-path terms.
+    if (tid < BLK) {  // exclusive prefix over s of each row t, in place
+        float run = 0.f;
+        for (int s2 = 0; s2 < BLK; ++s2) {
+            const float e = Eb[tid * 65 + s2];
+            Eb[tid * 65 + s2] = run;
+            run += e;
+        }
+    }
+    __syncthreads();
     if (w == 0) {
-        float kdk = wave_sum(s_kdk[l]);
-        const float end = __expf(gC) * (s_red[0] + s_red[1] + s_red[2] + s_red[3]) + kdk;
-        // reverse inclusive scan: lane l sums x over lanes >= l
-        float x = s_qdq[l] - s_vdv[l];
+        float F = 0.f;
+        for (int t = l; t < BLK; ++t) F += Eb[t * 65 + l];
+        // reverse inclusive scan of y: lane l sums y over lanes >= l
+        float x = s_y[l];
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             float y = __shfl_down(x, off, 64);
             if (l + off < 64) x += y;
         }
-        if (l < nvalid) a.dg[(tok0 + l) * H + h] = from_f<E>(x + end);
+        const float z = s_kdk[l];
+        const float zex = wave_prefix_sum(z) - z;
+        const float end = __expf(gC) * (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+        if (l < nvalid) a.dg[(tok0 + l) * H + h] = from_f<E>(x + F + zex + end);
     }
 }
 

@@ -1,0 +1,124 @@
+"""Parity at the full workload sizes, in the launch configuration the bench
+times (the sequence-chunk driver):
+
+  * the oracle recomputes whole sampled heads (every head is an independent
+    recurrence, so a head slice of the inputs is an exact sub-problem);
+  * identities that hold for the exact layer at any size are checked on every
+    head of the GPU result (q.dq = o.do per token; GDN k.dk + v.dv = 2 beta dbeta;
+    GLA k.dk = v.dv; joint linearity sum v.dv + <S_in, dS_in> = sum o.do + <S_out, dS_out>);
+  * the chunked run equals the unchunked run bit for bit.
+"""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+
+from tests.conftest import gpu_available
+from tests.gpu_util import rel_err, to_dev, to_np, tol
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _run(cfg, x, N):
+    import torch
+    from chunked_linear_recurrence_chunk_amd import stateflow
+    dt = cfg["dtype"]
+    keys = ("q", "k", "v", "g", "beta", "dO") if cfg["kind"] == "gdn" else ("q", "k", "v", "g", "dO")
+    d = {k: to_dev(x[k], dt) for k in keys}
+    S_in, dS_out = to_dev(x["S_in"], "fp32"), to_dev(x["dS_out"], "fp32")
+    if cfg["kind"] == "gdn":
+        drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
+    else:
+        drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
+    o, S = drv.forward(S_in)
+    gr = drv.backward(d["dO"], dS_out)
+    torch.cuda.synchronize()
+    out = dict(o=o, S_out=S, **gr)
+    del d, drv
+    return out
+
+
+def _oracle_heads(cfg, x, pairs):
+    """Oracle on the given (b, h) pairs, each as an independent sub-problem."""
+    from oracle import oracle
+
+    def one(bh):
+        b, h = bh
+        sl = {k: (v[b:b + 1, :, h:h + 1] if v.ndim >= 3 and k not in ("S_in", "dS_out") else v[b:b + 1, h:h + 1])
+              for k, v in x.items()}
+        sl = {k: np.ascontiguousarray(v, dtype=np.float64) for k, v in sl.items()}
+        if cfg["kind"] == "gdn":
+            o, S = oracle.gdn_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"])
+            r = oracle.gdn_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], sl["dS_out"])
+        else:
+            o, S = oracle.gla_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"])
+            r = oracle.gla_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], sl["dS_out"])
+        r.update(o=o, S_out=S)
+        return bh, r
+
+    with cf.ThreadPoolExecutor(len(pairs)) as ex:
+        return dict(ex.map(one, pairs))
+
+
+def _check_sampled(cfg, got, refs):
+    for (b, h), ref in refs.items():
+        for key, r in ref.items():
+            g = got[key]
+            gs = g[b:b + 1, :, h:h + 1] if key not in ("S_out", "dS_in") else g[b:b + 1, h:h + 1]
+            e = rel_err(to_np(gs), r)
+            print(f"   (b={b},h={h}) {key}: {e:.2e}", flush=True)
+            assert e < tol(cfg["dtype"], key), (b, h, key, e)
+
+
+def _check_identities(cfg, x, got):
+    f = {k: to_np(v) for k, v in got.items()}
+    q, k, v, dO = (x[n].astype(np.float64) for n in ("q", "k", "v", "dO"))
+    qdq = np.sum(q * f["dq"], -1)
+    odo = np.sum(f["o"] * dO, -1)
+    assert rel_err(qdq, odo) < 3e-2, rel_err(qdq, odo)
+    kdk, vdv = np.sum(k * f["dk"], -1), np.sum(v * f["dv"], -1)
+    if cfg["kind"] == "gdn":
+        e = rel_err(kdk + vdv, 2 * x["beta"] * f["dbeta"])
+    else:
+        e = rel_err(kdk, vdv)
+    assert e < 3e-2, e
+    lhs = vdv.sum(1) + np.sum(x["S_in"] * f["dS_in"], (2, 3))
+    rhs = odo.sum(1) + np.sum(f["S_out"] * x["dS_out"], (2, 3))
+    assert rel_err(lhs, rhs) < 3e-2, rel_err(lhs, rhs)
+
+
+def _full(name, pairs, compare_unchunked):
+    import torch
+    from chunked_linear_recurrence_chunk_amd import inputs
+    cfg = inputs.CONFIGS[name]
+    print(f"[fullsize] {name}: generating inputs", flush=True)
+    x = inputs.make(cfg, seed=100)
+    print(f"[fullsize] {name}: GPU run, {cfg['N']} sequence chunks", flush=True)
+    got = _run(cfg, x, cfg["N"])
+    if compare_unchunked:
+        print(f"[fullsize] {name}: GPU unchunked run", flush=True)
+        one = _run(cfg, x, 1)
+        for key in got:
+            assert torch.equal(got[key], one[key]), key
+        del one
+    print(f"[fullsize] {name}: identities on all heads", flush=True)
+    _check_identities(cfg, x, got)
+    print(f"[fullsize] {name}: oracle on {pairs}", flush=True)
+    refs = _oracle_heads(cfg, x, pairs)
+    _check_sampled(cfg, got, refs)
+
+
+def test_full_gdn_H16_T8192():
+    _full("gdn_bf16_H16_T8192_d128", [(0, 0), (0, 9)], True)
+
+
+def test_full_gla_B4_H16_T4096():
+    _full("gla_bf16_B4_H16_T4096_dk128_dv256", [(1, 5), (3, 12)], False)
+
+
+def test_full_gdn_H32_T65536():
+    _full("gdn_bf16_H32_T65536_d128", [(0, 17)], True)
+
+
+def test_full_gdn_H16_T262144():
+    _full("gdn_bf16_H16_T262144_d128", [(0, 3)], True)
