@@ -33,34 +33,37 @@ PEAK_FP32_TFLOPS = 157.3
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/byte
 
 
-def kernel_work(name: str, D: int, es: int, C: int = 64):
-    """Algorithmic (bytes, flops) of one kernel per 64-token block and head,
-    for dk = dv = D and element size es.  Bytes count each tensor the kernel
-    must read or write once; flops count the dense products as executed
-    (2 m n k each).  Definitions are listed per kernel in the design doc."""
-    CD, DD, CC = C * D, D * D, C * C
-    f4 = 4
-    if name == "gdn_prep":
-        byts = 2 * CD * es + 2 * C * es + C * f4 + 3 * CD * es
-        flops = 2 * CC * D + 2 * (2 * CC * D) + (C ** 3) // 3
-    elif name == "gdn_prep2":
-        byts = 4 * CD * es + C * f4 + 5 * CD * es
-        flops = 2 * (2 * CC * D)
-    elif name in ("gdn_scan_fwd", "gdn_scan_fwd_rec"):
-        byts = C * f4 + 3 * CD * es + DD * es + CD * es
-        flops = 2 * (2 * C * DD)
-    elif name == "gdn_out":
-        byts = 2 * CD * es + C * f4 + DD * es + CD * es + CD * es
-        flops = 2 * CC * D + 2 * C * DD + 2 * CC * D
-    elif name == "gdn_scan_bwd":
-        byts = C * f4 + 5 * CD * es + DD * es + CD * es
-        flops = 3 * (2 * C * DD)
-    elif name == "gdn_bwd_intra":
-        byts = 4 * CD * es + C * es + C * f4 + 2 * DD * es + 2 * CD * es + 3 * CD * es + 2 * C * es
-        flops = 3 * (2 * C * DD) + 10 * (2 * CC * D) + 2 * (2 * C ** 3) + 2 * CC * D
-    else:
-        return None
-    return byts, flops
+def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
+    """Algorithmic (bytes, flops) of one kernel per 64-token block and head
+    (element size es; fp32 for gates and states kept in fp32).  Bytes count
+    every tensor the kernel reads or writes once; flops count its dense
+    products as executed (2 m n k each).  The definitions are listed per
+    kernel in DESIGN.md."""
+    Ck, Cv, kv, CC, f4 = C * dk, C * dv, dk * dv, C * C, 4
+    W = {
+        # Gated DeltaNet (dk == dv)
+        "gdn_prep": (2 * Ck * es + 2 * C * es + C * f4 + 3 * Ck * es,
+                     2 * CC * dk + 2 * (2 * CC * dk) + C ** 3 // 3),
+        "gdn_prep2": (4 * Ck * es + C * f4 + 3 * Ck * es + kv * f4,
+                      2 * (2 * CC * dk) + 2 * (2 * C * kv)),
+        "gdn_scan_fwd": (C * f4 + 3 * Ck * es + kv * es + Cv * es, 2 * (2 * C * kv)),
+        "gdn_out": (2 * Ck * es + C * f4 + kv * es + Cv * es + Cv * es,
+                    2 * CC * dk + 2 * C * kv + 2 * CC * dv),
+        "gdn_scan_bwd": (C * f4 + 2 * Ck * es + kv * f4 + Cv * es + kv * es + Cv * es, 2 * (2 * C * kv)),
+        "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 2 * kv * es + 2 * Cv * es + 3 * Ck * es + 2 * C * es,
+                          3 * (2 * C * kv) + 11 * (2 * CC * dk) + 2 * (2 * C ** 3) + 2 * CC * dk),
+        # GLA
+        "gla_prep": (2 * Ck * es + Ck * f4 + Ck * es, 0),
+        "gla_prep_bwd": (3 * Ck * es + Ck * f4 + 3 * Ck * es, 0),
+        "gla_scan_fwd": (Ck * es + Cv * es + dk * f4 + kv * es, 2 * C * kv),
+        "gla_out": (2 * Ck * es + Cv * es + Ck * f4 + kv * es + Cv * es, 2 * CC * dk + 2 * C * kv + 2 * CC * dv),
+        "gla_scan_bwd": (2 * Ck * es + Cv * es + dk * f4 + kv * es + Cv * es, 2 * (2 * C * kv)),
+        "gla_bwd_intra": (2 * Ck * es + 2 * Cv * es + Ck * f4 + 2 * kv * es + Cv * es + 2 * Ck * es + Cv * es + Ck * es,
+                          2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv),
+    }
+    W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
+    W["gla_scan_fwd_rec"] = W["gla_scan_fwd"]
+    return W.get(name)
 
 
 def source_hash() -> str:
@@ -102,15 +105,22 @@ def cpu_baseline(cfg: dict, x: dict, budget_chunks: int):
     Ts = L * n
     sl = {k: (np.ascontiguousarray(v[:, :Ts]).astype(np.float64) if v.ndim >= 3 and k not in ("S_in", "dS_out")
               else v.astype(np.float64)) for k, v in x.items()}
+    def once():
+        if cfg["kind"] == "gdn":
+            oracle.gdn_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], None, n)
+        else:
+            oracle.gla_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], None, n)
     t0 = time.perf_counter()
-    if cfg["kind"] == "gdn":
-        oracle.gdn_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], None, n)
-    else:
-        oracle.gla_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], None, n)
-    dt = time.perf_counter() - t0
-    return {"value": cfg["B"] * Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {N} sequence chunks ({cfg['B']}x{Ts} tokens, all {cfg['H']} heads), "
-                      f"fp64 fwd+bwd, {dt:.1f} s"}
+    once()
+    reps, dt = 1, time.perf_counter() - t0
+    # repeat a cheap sample until about 10 s of oracle work has been timed
+    while dt < 10.0 and reps < 40:
+        once()
+        reps += 1
+        dt = time.perf_counter() - t0
+    return {"value": cfg["B"] * Ts * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{'all' if n == N else f'first {n} of'} {N} sequence chunks ({cfg['B']}x{Ts} tokens, "
+                      f"all {cfg['H']} heads), fp64 fwd+bwd, {reps} run(s), {dt:.1f} s"}
 
 
 def main():
@@ -120,8 +130,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-chunks", type=int, default=2)
+    ap.add_argument("--cpu-chunks", type=int, default=64, help="sequence chunks in the CPU-baseline sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer shards by heads with no communication; see DESIGN.md)", file=sys.stderr)
@@ -189,7 +210,7 @@ def main():
     tot_flops = 0.0
     for name, (launches, total_ms) in rep.items():
         avg_us = total_ms / launches * 1e3
-        work = kernel_work(name, dk, es)
+        work = kernel_work(name, dk, dv, es)
         ent = {"launches_per_step": launches // args.steps, "avg_us": round(avg_us, 2),
                "share": round(total_ms / tot_ms, 3)}
         if work:

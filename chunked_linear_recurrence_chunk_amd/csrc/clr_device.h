@@ -40,6 +40,24 @@ template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// XCD-aware placement of the sequential scans.  Work-groups are dispatched to
+// the 8 XCDs round-robin (group i -> XCD i % 8) and each XCD has its own L2.
+// All value slices of one (batch, head) read the same per-block operands, so
+// they are put on one XCD: group w -> (batch * H + head) index
+// p = (w % 8) + 8 * (w / (8 NV)), value slice vb = (w / 8) % NV.
+// Returns false for the padding groups of the last round (p >= BH).
+constexpr int NXCD = 8;
+__device__ __forceinline__ bool scan_coords(int NV, int BH, int H, int& b, int& h, int& vb) {
+    const int w = blockIdx.x;
+    const int p = (w % NXCD) + NXCD * (w / (NXCD * NV));
+    vb = (w / NXCD) % NV;
+    if (p >= BH) return false;
+    b = p / H;
+    h = p % H;
+    return true;
+}
+inline unsigned scan_grid(int NV, int BH) { return (unsigned)(((BH + NXCD - 1) / NXCD) * NXCD * NV); }
+
 // ---------------------------------------------------------------------------
 // Fragments
 // ---------------------------------------------------------------------------

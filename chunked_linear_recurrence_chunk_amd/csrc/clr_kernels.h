@@ -63,7 +63,7 @@ template <typename E> struct GdnScanArgs {
     const float* S_in;
     float* S_out;
     E *hT, *UT;
-    int H, NC;
+    int H, NC, BH;
 };
 
 template <typename E> struct GdnOutArgs {

@@ -49,7 +49,7 @@ template <typename E> struct GdnScanBwdArgs {
     const float* dS_out;
     float* dS_in;
     E *dh, *dUT;
-    int H, NC;
+    int H, NC, BH;
 };
 
 template <typename E> struct GdnIntraArgs {
@@ -237,9 +237,10 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 
 // operands of the next block prefetched into a second register buffer.
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(64) void gdn_scan_bwd_kernel(GdnScanBwdArgs<E> a) {
-    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int l = threadIdx.x, r = l & 15, g = l >> 4;
     const int H = a.H, NC = a.NC;
+    int b, h, vb;
+    if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
+    const int l = threadIdx.x, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
     constexpr int ND = DK / 16;
     const size_t bh = (size_t)b * H + h;
@@ -669,11 +670,11 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
                        ws.Rt, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dvlT, L.T, L.H, L.NC};
     launch("gdn_prep2", gdn_prep2_kernel<E, DK, DV>, gblk, dim3(256), st, p2);
     GdnScanArgs<E> sa{ws.gam, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
-                      (E*)ws.hT, (E*)ws.UT, L.H, L.NC};
-    launch("gdn_scan_fwd_rec", gdn_scan_fwd_kernel<E, DK, DV, true>, dim3(DV / 16, L.H, L.B), dim3(64), st, sa);
+                      (E*)ws.hT, (E*)ws.UT, L.H, L.NC, L.B * L.H};
+    launch("gdn_scan_fwd_rec", gdn_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sa);
     GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
-                         L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC};
-    launch("gdn_scan_bwd", gdn_scan_bwd_kernel<E, DK, DV>, dim3(DV / 16, L.H, L.B), dim3(64), st, sb);
+                         L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC, L.B * L.H};
+    launch("gdn_scan_bwd", gdn_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sb);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const E*)ws.dUT,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};

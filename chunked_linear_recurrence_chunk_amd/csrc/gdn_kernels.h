@@ -340,9 +340,10 @@ __device__ __forceinline__ void scan_fwd_step(const ScanFwdOps<E, DK>& o, f32x4 
 // forward's out kernel), true -> h[d][v] (read by the backward).
 template <typename E, int DK, int DV, bool HNAT>
 __global__ __launch_bounds__(64) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
-    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int l = threadIdx.x, r = l & 15, g = l >> 4;
     const int H = a.H, NC = a.NC;
+    int b, h, vb;
+    if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
+    const int l = threadIdx.x, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
     constexpr int ND = DK / 16;
     const size_t bh = (size_t)b * H + h;

@@ -44,7 +44,7 @@ template <typename E> struct GlaScanArgs {
     const float* S_in;
     float* S_out;
     E* hT;
-    int T, H, NC;
+    int T, H, NC, BH;
 };
 template <typename E> struct GlaOutArgs {
     const E *q, *k, *v;
@@ -59,7 +59,7 @@ template <typename E> struct GlaScanBwdArgs {
     const float* dS_out;
     float* dS_in;
     E *dh, *dVs;
-    int T, H, NC;
+    int T, H, NC, BH;
 };
 template <typename E> struct GlaIntraArgs {
     const E *q, *k, *v, *dO;
@@ -248,9 +248,10 @@ __device__ __forceinline__ void gla_scan_step(const GlaScanOps<E, DK>& o, f32x4 
 
 template <typename E, int DK, int DV, bool HNAT>
 __global__ __launch_bounds__(64) void gla_scan_fwd_kernel(GlaScanArgs<E> a) {
-    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int l = threadIdx.x, r = l & 15, g = l >> 4;
     const int H = a.H, NC = a.NC;
+    int b, h, vb;
+    if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
+    const int l = threadIdx.x, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
     constexpr int ND = DK / 16;
     const size_t bh = (size_t)b * H + h;
@@ -413,9 +414,10 @@ __device__ __forceinline__ void gla_dscan_step(const GlaScanBwdOps<E, DK>& o, f3
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(64) void gla_scan_bwd_kernel(GlaScanBwdArgs<E> a) {
-    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int l = threadIdx.x, r = l & 15, g = l >> 4;
     const int H = a.H, NC = a.NC;
+    int b, h, vb;
+    if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
+    const int l = threadIdx.x, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
     constexpr int ND = DK / 16;
     const size_t bh = (size_t)b * H + h;
@@ -652,8 +654,8 @@ hipError_t launch_gla_fwd_t(const GlaLaunch& L, hipStream_t st) {
     const GlaWs& ws = L.ws;
     GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC, ws.bcum, (E*)ws.KhT, nullptr, nullptr};
     launch("gla_prep", gla_prep_kernel<E, DK, false>, gblk, dim3(256), st, pa);
-    GlaScanArgs<E> sa{ws.bcum, (const E*)ws.KhT, (const E*)L.v, L.S_in, L.S_out, (E*)ws.hT, L.T, L.H, L.NC};
-    launch("gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(DV / 16, L.H, L.B), dim3(64), st, sa);
+    GlaScanArgs<E> sa{ws.bcum, (const E*)ws.KhT, (const E*)L.v, L.S_in, L.S_out, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
+    launch("gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sa);
     if (L.o) {
         GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)L.v, ws.bcum, (const E*)ws.hT, (E*)L.o, L.T, L.H, L.NC};
         launch("gla_out", gla_out_kernel<E, DK, DV>, gblk, dim3(256), st, oa);
@@ -668,11 +670,11 @@ hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
     GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC,
                       ws.bcum, (E*)ws.KhT, (E*)ws.QgT, (E*)ws.Kh};
     launch("gla_prep_bwd", gla_prep_kernel<E, DK, true>, gblk, dim3(256), st, pa);
-    GlaScanArgs<E> sa{ws.bcum, (const E*)ws.KhT, (const E*)L.v, L.S_in, nullptr, (E*)ws.hT, L.T, L.H, L.NC};
-    launch("gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(DV / 16, L.H, L.B), dim3(64), st, sa);
+    GlaScanArgs<E> sa{ws.bcum, (const E*)ws.KhT, (const E*)L.v, L.S_in, nullptr, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
+    launch("gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sa);
     GlaScanBwdArgs<E> sb{ws.bcum, (const E*)ws.Kh, (const E*)ws.QgT, (const E*)L.dO, L.dS_out, L.dS_in,
-                         (E*)ws.dh, (E*)ws.dVs, L.T, L.H, L.NC};
-    launch("gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(DV / 16, L.H, L.B), dim3(64), st, sb);
+                         (E*)ws.dh, (E*)ws.dVs, L.T, L.H, L.NC, L.B * L.H};
+    launch("gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sb);
     GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.dO, ws.bcum, (const E*)ws.hT,
                        (const E*)ws.dh, (const E*)ws.dVs, (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, L.T, L.H, L.NC};
     launch("gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV>, gblk, dim3(256), st, ia);

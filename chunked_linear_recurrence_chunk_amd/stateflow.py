@@ -49,7 +49,6 @@ class GdnChunked:
         nbytes = max(ops.workspace_bytes(shape, ops.OP_GDN_FWD), ops.workspace_bytes(shape, ops.OP_GDN_BWD))
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         self.saved = [None] * N
-        self.contig = B == 1
 
     def _chunk(self, i):
         a, b = self.bounds[i]
@@ -66,10 +65,10 @@ class GdnChunked:
         for i in range(self.N):
             a, b = self.bounds[i]
             self.saved[i] = S
-            oi = o[:, a:b] if self.contig else None
-            oi, S = self.ops.gdn_fwd(*self._chunk(i), S, ws=self.ws, o=oi)
-            if not self.contig:
-                o[:, a:b] = oi
+            view = o[:, a:b]
+            oi, S = self.ops.gdn_fwd(*self._chunk(i), S, ws=self.ws, o=view if view.is_contiguous() else None)
+            if oi.data_ptr() != view.data_ptr():
+                view.copy_(oi)
         return o, S
 
     def backward(self, dO, dS_out=None, grads: Optional[dict] = None):
@@ -82,11 +81,12 @@ class GdnChunked:
         dS = dS_out
         for i in reversed(range(self.N)):
             a, b = self.bounds[i]
-            out = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg", "dbeta")} if self.contig else None
+            views = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg", "dbeta")}
+            out = {key: t for key, t in views.items() if t.is_contiguous()}
             r = self.ops.gdn_bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
-            if not self.contig:
-                for key in ("dq", "dk", "dv", "dg", "dbeta"):
-                    grads[key][:, a:b] = r[key]
+            for key, t in views.items():
+                if r[key].data_ptr() != t.data_ptr():
+                    t.copy_(r[key])
             dS = r["dS_in"]
             self.saved[i] = None
         grads["dS_in"] = dS
@@ -112,7 +112,6 @@ class GlaChunked(GdnChunked):
         nbytes = max(ops.workspace_bytes(shape, ops.OP_GLA_FWD), ops.workspace_bytes(shape, ops.OP_GLA_BWD))
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         self.saved = [None] * N
-        self.contig = B == 1
 
     def _chunk(self, i):
         a, b = self.bounds[i]
@@ -128,10 +127,10 @@ class GlaChunked(GdnChunked):
         for i in range(self.N):
             a, b = self.bounds[i]
             self.saved[i] = S
-            oi = o[:, a:b] if self.contig else None
-            oi, S = self.ops.gla_fwd(*self._chunk(i), S, ws=self.ws, o=oi)
-            if not self.contig:
-                o[:, a:b] = oi
+            view = o[:, a:b]
+            oi, S = self.ops.gla_fwd(*self._chunk(i), S, ws=self.ws, o=view if view.is_contiguous() else None)
+            if oi.data_ptr() != view.data_ptr():
+                view.copy_(oi)
         return o, S
 
     def backward(self, dO, dS_out=None, grads: Optional[dict] = None):
@@ -142,11 +141,12 @@ class GlaChunked(GdnChunked):
         dS = dS_out
         for i in reversed(range(self.N)):
             a, b = self.bounds[i]
-            out = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg")} if self.contig else None
+            views = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg")}
+            out = {key: t for key, t in views.items() if t.is_contiguous()}
             r = self.ops.gla_bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
-            if not self.contig:
-                for key in ("dq", "dk", "dv", "dg"):
-                    grads[key][:, a:b] = r[key]
+            for key, t in views.items():
+                if r[key].data_ptr() != t.data_ptr():
+                    t.copy_(r[key])
             dS = r["dS_in"]
             self.saved[i] = None
         grads["dS_in"] = dS
