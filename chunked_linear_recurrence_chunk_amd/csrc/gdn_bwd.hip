@@ -124,6 +124,7 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
     fp[0] = frag_from_acc<E>(P[0], P[1]);
     fp[1] = frag_from_acc<E>(P[2], P[3]);
     E* dvlT = a.dvlT + chunk * BLK * DV;
+    #pragma unroll
     for (int vb = 0; vb < DV / 16; ++vb) {
         f32x4 acc = zero4();
 #pragma unroll
@@ -278,14 +279,14 @@ template <typename E, int DK, int DV> struct IntraLds {
     static constexpr int PDK = DK + 8, PDV = DV + 8;
     // persistent
     static constexpr size_t o_Kt = 0;                                  // E[DK][PT]     K^T
-    static constexpr size_t o_KKG = o_Kt + sizeof(E) * DK * PT;        // f32[64][65]   (K K^T * G), strictly lower
-    static constexpr size_t o_TT = o_KKG + 4 * BLK * 65;               // E[64][PT]     TT[s][t] = T[t][s]
+    static constexpr size_t o_KKG = o_Kt + sizeof(E) * DK * PT;        // f32[64][AP]   (K K^T * G), strictly lower
+    static constexpr size_t o_TT = o_KKG + 4 * BLK * AP;               // E[64][PT]     TT[s][t] = T[t][s]
     static constexpr size_t o_Tr = o_TT + sizeof(E) * BLK * PT;        // E[64][PT]     T row-major
     static constexpr size_t o_E = o_Tr + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms)
     static constexpr size_t o_U = o_E + 4 * BLK * 65;                  // union starts here
-    // phase 0: Am f32[64][65], Tm f32[64][65], Xs f32[16][17]
-    static constexpr size_t p0_Am = o_U, p0_Tm = p0_Am + 4 * BLK * 65, p0_Xs = p0_Tm + 4 * BLK * 65;
-    static constexpr size_t p0_end = p0_Xs + 4 * 16 * 17;
+    // phase 0: Am f32[64][AP], Td f32[4][16][16]
+    static constexpr size_t p0_Am = o_U, p0_Td = p0_Am + 4 * BLK * AP;
+    static constexpr size_t p0_end = p0_Td + 4 * 4 * 256;
     // phase A: Qt E[DK][PT], U E[64][PDV]
     static constexpr size_t pA_Qt = o_U, pA_U = pA_Qt + sizeof(E) * DK * PT;
     static constexpr size_t pA_end = pA_U + sizeof(E) * BLK * PDV;
@@ -351,19 +352,20 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * w + 4 * g + i, col = 16 * j + r;
                 const float kkg = col < row ? acc[i] * __expf(s_gam[row] - s_gam[col]) : 0.f;
-                KKG[row * 65 + col] = kkg;
-                Am[row * 65 + col] = s_bet[row] * kkg;
+                KKG[row * AP + col] = kkg;
+                Am[row * AP + col] = s_bet[row] * kkg;
             }
         }
         __syncthreads();
-        float* Tm = (float*)(lds + Lay::p0_Tm);
-        tri_inverse_64(Am, Tm, (float*)(lds + Lay::p0_Xs));
-        __syncthreads();
-        for (int idx = tid; idx < BLK * BLK; idx += 256) {
-            const int t = idx >> 6, s = idx & 63;
-            const E tv = from_f<E>(Tm[t * 65 + s]);
-            Tr[t * PT + s] = tv;
-            TT[s * PT + t] = tv;
+        f32x4 tc[4];
+        tri_inverse_cols(Am, (float*)(lds + Lay::p0_Td), tc);
+        // wave w holds column block w of T: write T row-major (Tr) and transposed (TT)
+        const int s = 16 * w + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) Tr[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii]);
+            st4(TT + s * PT + 16 * i + 4 * g, tc[i]);
         }
         __syncthreads();
     }
@@ -423,6 +425,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         fpt[1] = frag_from_acc<E>(dPT[2], dPT[3]);
         const float Gt = __expf(gam_tw);
         float qdq = 0.f;
+        #pragma unroll
         for (int db = 0; db < DK / 16; ++db) {
             f32x4 acc = zero4();
 #pragma unroll
@@ -466,6 +469,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         fpm[1] = frag_from_acc<E>(dP[2], dP[3]);
         const float ek = __expf(gC - gam_tw);
         float kdk = 0.f;
+        #pragma unroll
         for (int db = 0; db < DK / 16; ++db) {
             f32x4 acc = zero4();
 #pragma unroll
@@ -512,6 +516,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         Frag<E> fdu[DV / 32];
 #pragma unroll
         for (int kk = 0; kk < DV / 32; ++kk) fdu[kk] = ldfrag(dUs + tw * PDV + 32 * kk + 4 * g);
+        #pragma unroll
         for (int db = 0; db < DK / 16; ++db) {
             f32x4 acc = zero4();
 #pragma unroll
@@ -564,8 +569,8 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * w + 4 * g + i;
                 const float dA = (c < row) ? -acc[i] : 0.f;
-                gram[i] += dA * KKG[row * 65 + c];
-                Eb[row * 65 + c] += dA * s_bet[row] * KKG[row * 65 + c];  // gate cross term dA * A
+                gram[i] += dA * KKG[row * AP + c];
+                Eb[row * 65 + c] += dA * s_bet[row] * KKG[row * AP + c];  // gate cross term dA * A
                 const float m = dA * s_bet[row] * __expf(s_gam[row] - s_gam[c]);
                 if (c <= row) Ms[row * PT + c] = from_f<E>(c < row ? m : 0.f);
                 if (c < row) Ms[c * PT + row] = from_f<E>(m);
@@ -585,6 +590,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     // dV^T[vb][w] = beta_s (dU^T T): rows v, cols s = tw;   dbeta V-term
     const float bet_tw = s_bet[tw];
     float dbv = 0.f;
+    #pragma unroll
     for (int vb = 0; vb < DV / 16; ++vb) {
         f32x4 acc = zero4();
 #pragma unroll
@@ -601,6 +607,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     // dK^T += beta_s Gam_s (dW^T T) + K^T Msym ;  dbeta K-term
     const float Gs = __expf(gam_tw);
     float dbk = 0.f;
+    #pragma unroll
     for (int db = 0; db < DK / 16; ++db) {
         f32x4 acc = zero4();
 #pragma unroll

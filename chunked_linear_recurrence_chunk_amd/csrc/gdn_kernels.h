@@ -29,58 +29,72 @@ namespace clr {
 constexpr int PT = BLK + 8;
 
 // ---------------------------------------------------------------------------
-// Unit-lower-triangular inverse T = (I + A)^-1 of a 64 x 64 fp32 matrix in
-// LDS (A strictly lower).  16 x 16 diagonal blocks are inverted by forward
-// substitution, one wave each, then the off-diagonal row blocks are formed as
-// T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, one 16-row block at a time.
-// Requires 256 threads.  Am and Tm have row pitch 65 (floats).
+// Unit-lower-triangular inverse T = (I + A)^-1 of a 64 x 64 fp32 matrix A
+// (strictly lower) held in LDS with row pitch AP, on the fp32 matrix cores.
+//
+// 16 x 16 products: mma16(acc, a, b) with a = A[r][4g + j] and b = B[4g + j][r]
+// (j = 0..3), i.e. `a` is the accumulator tile of A^T and `b` that of B.
+//
+//  1. Wave w inverts its diagonal block N = A_ww (nilpotent, N^16 = 0) by
+//     doubling: (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8), exactly.
+//  2. Wave w then forms its column block: T_iw = -T_ii sum_{k=w}^{i-1} A_ik T_kw
+//     for i = w+1..3, keeping T_kw in registers.
+// Requires 256 threads.  Td is LDS scratch of 4 x 16 x 16 floats.  Returns
+// in tiles[i] the accumulator tile T[16 i + 4 g + .][16 w + r].
 // ---------------------------------------------------------------------------
-__device__ inline void tri_inverse_64(const float* Am, float* Tm, float* Xs) {
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, c = l & 15, rg = l >> 4;
-    {
-        // wave w inverts diagonal block w; lane (c, rg) owns rows 4rg..4rg+3, column c
-        const int o = 16 * w;
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int r = 0; r < 16; ++r) {
-            float p = 0.f;
+constexpr int AP = BLK + 4;  // row pitch of the fp32 64 x 64 LDS matrices
+
+__device__ __forceinline__ void mma16f(f32x4& acc, f32x4 a, f32x4 b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+}
+
+__device__ inline void tri_inverse_cols(const float* Am, float* Td, f32x4 (&tiles)[4]) {
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int o = 16 * w;
+    // N = A_ww as tiles of N (rows 4g+i, col r) and of N^T
+    f32x4 N, NT;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s = 4 * rg + i;
-                if (s < r) p += Am[(o + r) * 65 + o + s] * x[i];
-            }
-            p += __shfl_xor(p, 16, 64);
-            p += __shfl_xor(p, 32, 64);
-            if ((r >> 2) == rg) {
-                const float val = (r == c ? 1.f : 0.f) - p;
+    for (int i = 0; i < 4; ++i) N[i] = Am[(o + 4 * g + i) * AP + o + r];
+    NT = *(const f32x4*)(Am + (o + r) * AP + o + 4 * g);
+    f32x4 N2 = zero4(), N2T = zero4(), N4 = zero4(), N4T = zero4(), N8 = zero4();
+    mma16f(N2, NT, N);
+    mma16f(N2T, N, NT);
+    mma16f(N4, N2T, N2);
+    mma16f(N4T, N2, N2T);
+    mma16f(N8, N4T, N4);
+    f32x4 Y = N8;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if ((r & 3) == i) x[i] = val;
-            }
-        }
+    for (int i = 0; i < 4; ++i)
+        if (4 * g + i == r) Y[i] += 1.f;
+    mma16f(Y, N4T, Y);   // (I + N^4)(I + N^8)
+    mma16f(Y, N2T, Y);   // (I + N^2)(...)
+    mma16f(Y, -NT, Y);   // (I - N)(...)
+    // diagonal block to LDS (row-major 16 x 16) for the other waves
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Tm[(o + 4 * rg + i) * 65 + o + c] = x[i];
-        // zero the strictly-upper part of this block row
-        for (int j = 0; j < 4; ++j)
-            if (j > w)
+    for (int i = 0; i < 4; ++i) Td[w * 256 + (4 * g + i) * 16 + r] = Y[i];
+    // (loops fully unrolled so the tiles stay in registers; w is wave-uniform)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Tm[(o + 4 * rg + i) * 65 + 16 * j + c] = 0.f;
-    }
+    for (int i = 0; i < 4; ++i) tiles[i] = (i == w) ? Y : zero4();
     __syncthreads();
-    const int r = tid >> 4, cc = tid & 15;  // one element of a 16 x 16 block per thread
+#pragma unroll
     for (int i = 1; i < 4; ++i) {
-        for (int j = 0; j < i; ++j) {
-            // X = sum_{k=j}^{i-1} A_ik T_kj   (rows 16i.., cols 16j..)
-            float acc = 0.f;
-            for (int s = 16 * j; s < 16 * i; ++s) acc += Am[(16 * i + r) * 65 + s] * Tm[s * 65 + 16 * j + cc];
-            Xs[r * 17 + cc] = acc;
-            __syncthreads();
-            float t = 0.f;
-            for (int u = 0; u <= r; ++u) t += Tm[(16 * i + r) * 65 + 16 * i + u] * Xs[u * 17 + cc];
-            __syncthreads();
-            Tm[(16 * i + r) * 65 + 16 * j + cc] = -t;
+        if (i > w) {
+            f32x4 X = zero4();
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                if (k >= w && k < i) {
+                    const f32x4 a = *(const f32x4*)(Am + (16 * i + r) * AP + 16 * k + 4 * g);  // A_ik^T tile
+                    mma16f(X, a, tiles[k]);
+                }
+            }
+            const f32x4 tii = *(const f32x4*)(Td + i * 256 + r * 16 + 4 * g);  // T_ii^T tile
+            f32x4 Tiw = zero4();
+            mma16f(Tiw, -tii, X);
+            tiles[i] = Tiw;
         }
-        __syncthreads();
     }
 }
 
@@ -125,7 +139,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     const int nvalid = min(BLK, T - n * BLK);             // tokens of this block inside the sequence
 
     __shared__ float s_gam[BLK], s_bet[BLK], s_Gam[BLK];
-    __shared__ float Am[BLK * 65], Tm[BLK * 65], Xs[16 * 17];
+    __shared__ float Am[BLK * AP], Td[4 * 256];
     __shared__ E Kt[DK * PT], Vt[DV * PT], T1[BLK * PT], T2[BLK * PT];
 
     if (w == 0) {
@@ -164,19 +178,26 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
                 const int row = 16 * w + 4 * g + i, col = 16 * j + r;
                 float val = 0.f;
                 if (col < row) val = s_bet[row] * __expf(s_gam[row] - s_gam[col]) * acc[i];
-                Am[row * 65 + col] = val;
+                Am[row * AP + col] = val;
             }
         }
     }
     __syncthreads();
-    tri_inverse_64(Am, Tm, Xs);
-    __syncthreads();
-    // T1 = T Diag(beta Gam), T2 = T Diag(beta), rounded to the element type.
-    for (int idx = tid; idx < BLK * BLK; idx += 256) {
-        const int t = idx >> 6, s = idx & 63;
-        const float tv = Tm[t * 65 + s];
-        T1[t * PT + s] = from_f<E>(tv * s_bet[s] * s_Gam[s]);
-        T2[t * PT + s] = from_f<E>(tv * s_bet[s]);
+    {
+        // T = (I + A)^-1; wave w holds column block w.  T1 = T Diag(beta Gam),
+        // T2 = T Diag(beta), rounded to the element type.
+        f32x4 tc[4];
+        tri_inverse_cols(Am, Td, tc);
+        const int s = 16 * w + r;
+        const float b1 = s_bet[s] * s_Gam[s], b2 = s_bet[s];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int t = 16 * i + 4 * g + ii;
+                T1[t * PT + s] = from_f<E>(tc[i][ii] * b1);
+                T2[t * PT + s] = from_f<E>(tc[i][ii] * b2);
+            }
     }
     __syncthreads();
 

@@ -340,6 +340,7 @@ __global__ __launch_bounds__(256) void gla_out_kernel(GlaOutArgs<E> a) {
     fp[1] = frag_from_acc<E>(P[2], P[3]);
     const E* hT = a.hT + chunk * DK * DV;
     E* ob = a.o + tok0 * ldv + (size_t)h * DV;
+    #pragma unroll
     for (int vb = 0; vb < DV / 16; ++vb) {
         f32x4 acc = zero4();
 #pragma unroll
@@ -548,6 +549,7 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     }
     float rpart[DK / 16][4];
     // (4) dQ^T and (5) dK^T, per 16-row block of features d
+    #pragma unroll
     for (int db = 0; db < DK / 16; ++db) {
         const int dm = 16 * db + r;  // feature row of this lane's A fragments
         // dQ: inter  exp(b_t) (S0 dO^T)
@@ -615,6 +617,7 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
         }
     // (6) dV^T[vb][R] = dO^T P + (Kh dh)^T   (rows v, col s = tl)
     const E* dVs = a.dVs + chunk * BLK * DV;
+    #pragma unroll
     for (int vb = 0; vb < DV / 16; ++vb) {
         f32x4 acc = zero4();
 #pragma unroll
