@@ -678,7 +678,7 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     launch("gdn_prep2", gdn_prep2_kernel<E, DK, DV>, gblk, dim3(256), st, p2);
     GdnScanArgs<E> sa{ws.gam, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, (E*)ws.UT, L.H, L.NC, L.B * L.H};
-    launch("gdn_scan_fwd_rec", gdn_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sa);
+    launch("gdn_scan_fwd_rec", gdn_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(256), st, sa);
     GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
                          L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC, L.B * L.H};
     launch("gdn_scan_bwd", gdn_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sb);

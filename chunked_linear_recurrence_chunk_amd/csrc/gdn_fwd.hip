@@ -15,7 +15,7 @@ hipError_t launch_gdn_fwd_t(const GdnLaunch& L, hipStream_t st) {
     launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, gblk, dim3(256), st, pa);
     GdnScanArgs<E> sa{L.ws.gam, (const E*)L.ws.W, (const E*)L.ws.KhT, (const E*)L.ws.UtT, L.S_in, L.S_out,
                       (E*)L.ws.hT, (E*)L.ws.UT, L.H, L.NC, L.B * L.H};
-    launch("gdn_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sa);
+    launch("gdn_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(256), st, sa);
     if (L.o) {
         GdnOutArgs<E> oa{(const E*)L.q, (const E*)L.k, L.ws.gam, (const E*)L.ws.hT, (const E*)L.ws.UT, (E*)L.o,
                          L.T, L.H, L.NC};

@@ -22,6 +22,7 @@
 #pragma once
 
 #include "clr_kernels.h"
+#include "clr_ring.h"
 
 namespace clr {
 
@@ -285,14 +286,15 @@ __device__ __forceinline__ void store_rows16(E* dst, size_t ld, const f32x4 (&X)
     for (int rb = 0; rb < ROWS / 16; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) tile[(16 * rb + 4 * g + i) * 16 + r] = from_f<E>(X[rb][i]);
-    __syncthreads();  // single-wave work-group: orders the LDS writes before the reads
+    // only this wave uses the tile; LDS operations of one wave execute in order
+    asm volatile("" ::: "memory");
     constexpr int VEC = 16 / sizeof(E), PER_ROW = 16 / VEC;
 #pragma unroll
     for (int c = l; c < ROWS * PER_ROW; c += 64) {
         const int d = c / PER_ROW, part = c % PER_ROW;
         *(uint4*)(dst + (size_t)d * ld + c0 + part * VEC) = *(const uint4*)(tile + d * 16 + part * VEC);
     }
-    __syncthreads();  // reads done before the tile is rewritten
+    asm volatile("" ::: "memory");
 }
 
 template <typename E, int DK, int DV>
@@ -357,17 +359,74 @@ __device__ __forceinline__ void scan_fwd_step(const ScanFwdOps<E, DK>& o, f32x4 
     }
 }
 
+// Operands of one block from a ring slot (see clr_ring.h for the layout).
+template <typename E, int DK, int NU>
+__device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK>& o, const char* slot, int l) {
+    constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * (DK / 16);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) o.w[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o.kh[db][j] = ring_frag(slot, NWF + 2 * db + j, l, (E*)nullptr);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, NWF + NKF + j, l, (E*)nullptr);
+    o.gC = ring_small<NU>(slot, BLK - 1);
+}
+
 // HNAT selects the layout of the saved states: false -> h^T[v][d] (read by the
 // forward's out kernel), true -> h[d][v] (read by the backward).
+// Work-group: wave 0 runs the recurrence, waves 1..3 stream the operands of
+// the next blocks into the LDS ring (clr_ring.h).
 template <typename E, int DK, int DV, bool HNAT>
-__global__ __launch_bounds__(64) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
+__global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
     const int H = a.H, NC = a.NC;
     int b, h, vb;
     if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
-    const int l = threadIdx.x, r = l & 15, g = l >> 4;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
     constexpr int ND = DK / 16;
+    constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 16-byte units per fragment
+    constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * ND, NU = (NWF + NKF + 2) * UPF;
+    using G = RingGeom<NU>;
+    constexpr int TILE = HNAT ? DK * 16 * (int)sizeof(E) : 16;
+    constexpr int PF = (144 * 1024 - TILE) / G::SLOT;
+    constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
+    __shared__ __align__(16) char ring[P * G::SLOT];
+    __shared__ __align__(16) E tile[TILE / sizeof(E)];
     const size_t bh = (size_t)b * H + h;
+
+    if (w > 0) {  // producers
+        const int pid = w - 1;
+        auto issue = [&](int n) {
+            const size_t c = bh * NC + n;
+            const E* W = a.W + c * BLK * DK;
+            const E* KhT = a.KhT + c * BLK * DK;
+            const E* UtT = a.UtT + c * BLK * DV;
+            auto src = [&](int u) -> const void* {
+                const int f = u / UPF, half = u % UPF;
+                const E* p;
+                if (f < NWF) p = W + (size_t)(16 * (f / KK) + r) * DK + 32 * (f % KK) + 8 * g;
+                else if (f < NWF + NKF) p = KhT + (size_t)(16 * ((f - NWF) / 2) + r) * BLK + 32 * ((f - NWF) % 2) + 8 * g;
+                else p = UtT + (size_t)(v0 + r) * BLK + 32 * (f - NWF - NKF) + 8 * g;
+                return p + 4 * half;
+            };
+            ring_issue<NU>(ring + (n % P) * G::SLOT, pid, src, a.gam + c * BLK + l);
+        };
+        const int pre = NC < P - 1 ? NC : P - 1;
+        for (int n = 0; n < pre; ++n) issue(n);
+        ring_wait<G::NU_MIN>(pre - 1);  // block 0 has landed
+        ring_barrier();
+        for (int n = 0; n < NC; ++n) {
+            if (n + P - 1 < NC) issue(n + P - 1);
+            const int last = (n + P - 1 < NC ? n + P - 1 : NC - 1);
+            ring_wait<G::NU_MIN>(last - (n + 1));  // block n + 1 has landed
+            ring_barrier();
+        }
+        return;
+    }
 
     f32x4 S[ND];
     const float* Sin = a.S_in ? a.S_in + bh * DK * DV : nullptr;
@@ -375,16 +434,12 @@ __global__ __launch_bounds__(64) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
     for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[db][i] = Sin ? Sin[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
-
-    __shared__ __align__(16) E tile[HNAT ? DK * 16 : 8];
-    ScanFwdOps<E, DK> A, B;
-    if (NC > 0) scan_fwd_load<E, DK, DV>(A, a, bh * NC, v0, r, g);
-    for (int n = 0; n < NC; n += 2) {
-        if (n + 1 < NC) scan_fwd_load<E, DK, DV>(B, a, bh * NC + n + 1, v0, r, g);
-        scan_fwd_step<E, DK, DV, HNAT>(A, S, a, bh * NC + n, v0, r, g, tile);
-        if (n + 1 >= NC) break;
-        if (n + 2 < NC) scan_fwd_load<E, DK, DV>(A, a, bh * NC + n + 2, v0, r, g);
-        scan_fwd_step<E, DK, DV, HNAT>(B, S, a, bh * NC + n + 1, v0, r, g, tile);
+    ring_barrier();
+    for (int n = 0; n < NC; ++n) {
+        ScanFwdOps<E, DK> o;
+        scan_fwd_from_ring<E, DK, NU>(o, ring + (n % P) * G::SLOT, l);
+        scan_fwd_step<E, DK, DV, HNAT>(o, S, a, bh * NC + n, v0, r, g, tile);
+        ring_barrier();
     }
     if (a.S_out) {
         float* So = a.S_out + bh * DK * DV;
