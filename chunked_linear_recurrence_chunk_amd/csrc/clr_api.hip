@@ -4,7 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/clr.h"
+#include "clr.h"
 #include "clr_kernels.h"
 
 using namespace clr;

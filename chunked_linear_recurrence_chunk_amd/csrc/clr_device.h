@@ -193,6 +193,111 @@ __device__ __forceinline__ void st8P(float* p, f32x4 lo, f32x4 hi) {
     *(f32x4*)(p + 4) = hi;
 }
 
+// ---------------------------------------------------------------------------
+// Tiled ("fragment-major") storage of a block-local matrix X[R][C], C a
+// multiple of 32.  The 16 x 32 fragment f = (row / 16) * (C / 32) + col / 32
+// is one contiguous run in lane order: lane l = 16g + r holds the A-fragment
+// elements X[16 (f / (C/32)) + r][32 (f % (C/32)) + kmap(g, i)], i = 0..7.
+//   bf16: 64 lanes x 16 bytes = 1 KB per fragment;
+//   fp32: 2 KB per fragment, i = 0..3 in the first KB, i = 4..7 in the second.
+// One wave therefore reads or writes a fragment as whole 1-KB runs (eight
+// full 128-byte lines per instruction) instead of sixteen partial rows, which
+// is what bounds a scan's operand stream on this chip.  Four consecutive
+// columns starting at a multiple of 4 stay contiguous.
+// ---------------------------------------------------------------------------
+template <typename E>
+__device__ __forceinline__ size_t toff(int row, int col, int C) {
+    const int f = (row >> 4) * (C >> 5) + (col >> 5);
+    const int p = kperm(col & 31);
+    const int lane = ((p >> 3) << 4) + (row & 15), i = p & 7;
+    if constexpr (sizeof(E) == 2) return ((size_t)f * 64 + lane) * 8 + i;
+    else return (((size_t)f * 2 + (i >> 2)) * 64 + lane) * 4 + (i & 3);
+}
+// Elements per 1-KB unit, and this lane's offset inside a unit.
+template <typename E> constexpr int UNIT_ELEMS = 1024 / (int)sizeof(E);
+template <typename E> constexpr int LANE_ELEMS = 16 / (int)sizeof(E);
+// Fragment f of a tiled matrix.
+__device__ __forceinline__ Frag<bf16> ldfragT(const bf16* base, int f, int l) {
+    Frag<bf16> x;
+    x.v = *(const bf16x8*)(base + ((size_t)f * 64 + l) * 8);
+    return x;
+}
+__device__ __forceinline__ Frag<float> ldfragT(const float* base, int f, int l) {
+    Frag<float> x;
+    x.lo = *(const f32x4*)(base + ((size_t)(2 * f) * 64 + l) * 4);
+    x.hi = *(const f32x4*)(base + ((size_t)(2 * f + 1) * 64 + l) * 4);
+    return x;
+}
+// Store two vertically adjacent accumulator tiles (rows 0..15 in lo, 16..31
+// in hi), which are exactly an A fragment of the transposed 32 x 16 block, as
+// fragment f of a tiled matrix.
+__device__ __forceinline__ void st8T(bf16* base, int f, int l, f32x4 lo, f32x4 hi) {
+    *(bf16x8*)(base + ((size_t)f * 64 + l) * 8) = bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+                                                         (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+}
+__device__ __forceinline__ void st8T(float* base, int f, int l, f32x4 lo, f32x4 hi) {
+    *(f32x4*)(base + ((size_t)(2 * f) * 64 + l) * 4) = lo;
+    *(f32x4*)(base + ((size_t)(2 * f + 1) * 64 + l) * 4) = hi;
+}
+__device__ __forceinline__ void st8T(bf16* base, int f, int l, const Frag<bf16>& x) {
+    *(bf16x8*)(base + ((size_t)f * 64 + l) * 8) = x.v;
+}
+
+// Tiled global storage of X[R][C], one 16-byte unit per thread and iteration
+// (coalesced 1-KB runs).  get4(row, col) returns X[row][col .. col + 3]
+// (col a multiple of 4) as fp32; the values are rounded to E on the store.
+template <typename E, int R, int C, typename F>
+__device__ __forceinline__ void store_tiled(E* __restrict__ dst, F get4) {
+    constexpr int UNITS = R * C * (int)sizeof(E) / 16;
+    for (int u = threadIdx.x; u < UNITS; u += blockDim.x) {
+        int f, lane, half;
+        if constexpr (sizeof(E) == 2) { f = u >> 6; lane = u & 63; half = 0; }
+        else { f = u >> 7; half = (u >> 6) & 1; lane = u & 63; }
+        const int row = 16 * (f / (C / 32)) + (lane & 15), g = lane >> 4, c0 = 32 * (f % (C / 32));
+        if constexpr (sizeof(E) == 2) {
+            const f32x4 lo = get4(row, c0 + 4 * g), hi = get4(row, c0 + 16 + 4 * g);
+            *(bf16x8*)(dst + (size_t)u * 8) = bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+                                                     (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+        } else {
+            *(f32x4*)(dst + (size_t)u * 4) = get4(row, c0 + (half ? 16 : 0) + 4 * g);
+        }
+    }
+}
+
+// Tiled global X[R][C] -> transposed LDS dst[c * DP + r] = X[r][c]
+// (coalesced 16-byte reads).
+template <typename E, int R, int C, int DP>
+__device__ __forceinline__ void stage_T_tiled(const E* __restrict__ src, E* dst) {
+    constexpr int UNITS = R * C * (int)sizeof(E) / 16;
+    for (int u = threadIdx.x; u < UNITS; u += blockDim.x) {
+        int f, lane, half;
+        if constexpr (sizeof(E) == 2) { f = u >> 6; lane = u & 63; half = 0; }
+        else { f = u >> 7; half = (u >> 6) & 1; lane = u & 63; }
+        const int row = 16 * (f / (C / 32)) + (lane & 15), g = lane >> 4, c0 = 32 * (f % (C / 32));
+        if constexpr (sizeof(E) == 2) {
+            const bf16x8 v = *(const bf16x8*)(src + (size_t)u * 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dst[(c0 + 4 * g + i) * DP + row] = v[i];
+                dst[(c0 + 16 + 4 * g + i) * DP + row] = v[4 + i];
+            }
+        } else {
+            const f32x4 v = *(const f32x4*)(src + (size_t)u * 4);
+            const int c = c0 + (half ? 16 : 0) + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(c + i) * DP + row] = v[i];
+        }
+    }
+}
+
+// Accumulator-tiled fp32 storage of an [M][N] matrix: the 16 x 16 tile
+// (mb, nb) is 1 KB in lane order, lane l = 16g + r holding rows 16 mb + 4g + i
+// (i = 0..3) of column 16 nb + r.  Tiles are ordered nb-major: tile index
+// nb * (M / 16) + mb, so one 16-column slice is contiguous.
+__device__ __forceinline__ size_t atoff(int mb, int nb, int M, int l) {
+    return ((size_t)nb * (M / 16) + mb) * 256 + (size_t)l * 4;
+}
+
 // Four contiguous elements kept in their storage type (fewer registers than
 // f32x4 for bf16), converted on use.
 template <typename E> struct Raw4;

@@ -7,7 +7,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/clr.h"
+#include "clr.h"
 #include "clr_launch.h"
 
 namespace clr {

@@ -82,22 +82,15 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
     if (tid < BLK) s_gam[tid] = a.gam[chunk * BLK + tid];
     stage_transposed<E, DK>(qb, ldk, Qt, nvalid);
     stage_transposed<E, DV>(dob, ldv, dOt, nvalid);
-    stage_T<E, BLK, DK, PT, true>(a.W + chunk * BLK * DK, DK, Wt, BLK);  // W columns are fragment-packed
+    stage_T_tiled<E, BLK, DK, PT>(a.W + chunk * BLK * DK, Wt);  // Wt[d][t] = W[t][d]
     __syncthreads();
 
     const float gC = s_gam[BLK - 1];
-    E* WT = a.WT + chunk * BLK * DK;
-    for (int idx = tid; idx < DK * (BLK / 4); idx += 256) {
-        const int d = idx / (BLK / 4), t4 = (idx % (BLK / 4)) * 4;
-        st4(WT + (size_t)d * BLK + kperm(t4), ld4(Wt + d * PT + t4));
-    }
-    // Kh[t][d] = exp(gamma_C - gamma_t) K[t][d]   (token-major, d fragment-packed)
-    E* Kh = a.Kh + chunk * BLK * DK;
-    for (int idx = tid; idx < BLK * (DK / 4); idx += 256) {
-        const int t = idx / (DK / 4), d4 = (idx % (DK / 4)) * 4;
-        f32x4 x = t < nvalid ? ld4(kb + (size_t)t * ldk + d4) : zero4();
-        st4(Kh + (size_t)t * DK + kperm(d4), x * __expf(gC - s_gam[t]));
-    }
+    // W^T[d][t] and Kh[t][d] = exp(gamma_C - gamma_t) K[t][d], both tiled
+    store_tiled<E, DK, BLK>(a.WT + chunk * BLK * DK, [&](int d, int t) { return ld4(Wt + d * PT + t); });
+    store_tiled<E, BLK, DK>(a.Kh + chunk * BLK * DK, [&](int t, int d) {
+        return t < nvalid ? ld4(kb + (size_t)t * ldk + d) * __expf(gC - s_gam[t]) : zero4();
+    });
     // dvloc[s][v] = sum_t P[t][s] dO[t][v],  P[t][s] = (q_t . k_s) exp(gamma_t - gamma_s), s <= t.
     // Wave w owns s-block w: P[tb][w] tiles (rows t, cols s) chain into A = P^T.
     f32x4 P[4];
@@ -129,7 +122,7 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag(dOt + (16 * vb + r) * PT + 32 * j + 4 * g));
-        st4(dvlT + (size_t)(16 * vb + r) * BLK + kperm(16 * w + 4 * g), acc);
+        st4(dvlT + toff<E>(16 * vb + r, 16 * w + 4 * g, BLK), acc);
         st4(dvlt + (16 * vb + r) * PT + 16 * w + 4 * g, acc);
     }
     // Qt <- (Diag(Gam) Q)^T in place
@@ -141,7 +134,7 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
         st4(Qt + d * PT + t4, x);
     }
     __syncthreads();
-    // R[d][v] = sum_t Qg^T[d][t] dO[t][v] - sum_t W^T[d][t] dvloc[t][v]   -> stored as R^T[v][d] (fp32)
+    // R[d][v] = sum_t Qg^T[d][t] dO[t][v] - sum_t W^T[d][t] dvloc[t][v]   (fp32, accumulator-tiled)
     float* Rt = a.Rt + chunk * DK * DV;
     for (int tile = w; tile < (DK / 16) * (DV / 16); tile += 4) {
         const int db = tile % (DK / 16), vb = tile / (DK / 16);
@@ -151,51 +144,61 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
             mma(acc, ldfrag(Qt + (16 * db + r) * PT + 32 * j + 4 * g), ldfrag(dOt + (16 * vb + r) * PT + 32 * j + 4 * g));
             mma(acc2, ldfrag(Wt + (16 * db + r) * PT + 32 * j + 4 * g), ldfrag(dvlt + (16 * vb + r) * PT + 32 * j + 4 * g));
         }
-        *(f32x4*)(Rt + (size_t)(16 * vb + r) * DK + 16 * db + 4 * g) = acc - acc2;
+        *(f32x4*)(Rt + atoff(db, vb, DK, l)) = acc - acc2;
     }
 }
 
 // ---------------------------------------------------------------------------
-// dscan: one wave per (16-wide value slice, head, batch), blocks in reverse.
+// dscan: one work-group per (16-wide value slice, head, batch), blocks in
+// reverse.  Wave 0 runs the reverse recurrence with dS in accumulator tiles;
+// waves 1..3 stream the operands of the next blocks into the LDS ring
+// (clr_ring.h).  Ring unit u of a block is the contiguous 1-KB run u of
+// [Kh | W^T | R tiles (., vb) | dvloc^T fragments (vb, 0..1)], all tiled.
 // ---------------------------------------------------------------------------
 template <typename E, int DK> struct ScanBwdOps {
     Frag<E> kh[4][DK / 32];   // Kh rows (A: m = t, k = d)
     Frag<E> wt[DK / 16][2];   // W^T rows (A: m = d, k = t)
-    f32x4 rt[DK / 16];        // R^T[v0 + r][16 db + 4 g ..]
+    f32x4 rt[DK / 16];        // R accumulator tiles (rows d, column v0 + r)
     Frag<E> dvl[2];           // dvloc^T[v0 + r][token tile pairs] (accumulator layout)
     float gC;
 };
 
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void scan_bwd_load(ScanBwdOps<E, DK>& o, const GdnScanBwdArgs<E>& a, size_t chunk,
-                                              int v0, int r, int g) {
-    const E* Kh = a.Kh + chunk * BLK * DK;
-    const E* WT = a.WT + chunk * BLK * DK;
-    const float* Rt = a.Rt + chunk * DK * DV;
-    const E* dvlT = a.dvlT + chunk * BLK * DV;
+template <typename E, int DK> struct ScanBwdRing {
+    static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;
+    static constexpr int KK = DK / 32, ND = DK / 16;
+    static constexpr int NKU = 4 * KK * UPF, NWU = 2 * ND * UPF, NRU = ND, NDU = 2 * UPF;
+    static constexpr int NU = NKU + NWU + NRU + NDU;
+};
+
+template <typename E, int DK, int NU>
+__device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK>& o, const char* slot, int l) {
+    using Rg = ScanBwdRing<E, DK>;
+    constexpr int KK = DK / 32, UPF = Rg::UPF;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) o.kh[tb][kk] = ldfragP(Kh + (size_t)(16 * tb + r) * DK + 32 * kk + 8 * g);
+        for (int kk = 0; kk < KK; ++kk) o.kh[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
 #pragma unroll
     for (int db = 0; db < DK / 16; ++db) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) o.wt[db][j] = ldfragP(WT + (size_t)(16 * db + r) * BLK + 32 * j + 8 * g);
-        o.rt[db] = *(const f32x4*)(Rt + (size_t)(v0 + r) * DK + 16 * db + 4 * g);
+        for (int j = 0; j < 2; ++j) o.wt[db][j] = ring_frag(slot, Rg::NKU / UPF + 2 * db + j, l, (E*)nullptr);
+        o.rt[db] = *(const f32x4*)(slot + (Rg::NKU + Rg::NWU + db) * RING_UNIT + l * 16);
     }
+    // dvloc fragments start at unit NKU + NWU + NRU, i.e. fragment index (that) / UPF
+    static_assert((Rg::NKU + Rg::NWU + Rg::NRU) % UPF == 0, "fragment alignment");
 #pragma unroll
-    for (int j = 0; j < 2; ++j) o.dvl[j] = ldfragP(dvlT + (size_t)(v0 + r) * BLK + 32 * j + 8 * g);
-    o.gC = a.gam[chunk * BLK + BLK - 1];
+    for (int j = 0; j < 2; ++j)
+        o.dvl[j] = ring_frag(slot, (Rg::NKU + Rg::NWU + Rg::NRU) / UPF + j, l, (E*)nullptr);
+    o.gC = ring_small<NU>(slot, BLK - 1);
 }
 
 // One reverse step: on entry dS = dL/dS_{n+1}; writes dh_n = dS and
 // dU_n = dvloc_n + Kh_n dS; leaves dS = dL/dS_n = Gam_C dS + R_n - W_n^T (Kh_n dS).
 template <typename E, int DK, int DV>
 __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 (&dS)[DK / 16],
-                                              const GdnScanBwdArgs<E>& a, size_t chunk, int v0, int r, int g,
-                                              E* tile) {
+                                              const GdnScanBwdArgs<E>& a, size_t chunk, int vb, int l, E* tile) {
     constexpr int ND = DK / 16;
-    store_state_kmajor<E, DK, DV>(a.dh + chunk * DK * DV, dS, tile, v0, r, g);
+    store_state_tiled<E, DK, DV>(a.dh + chunk * DK * DV, dS, tile, 16 * vb, l);
     Frag<E> fs[DK / 32];
 #pragma unroll
     for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
@@ -219,7 +222,7 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 
             lo = f.lo;
             hi = f.hi;
         }
-        st8P(dUT + (size_t)(v0 + r) * BLK + 32 * j + 8 * g, dUp[2 * j] + lo, dUp[2 * j + 1] + hi);
+        st8T(dUT, 2 * vb + j, l, dUp[2 * j] + lo, dUp[2 * j + 1] + hi);
     }
     Frag<E> fu[2];
 #pragma unroll
@@ -234,17 +237,54 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 
     }
 }
 
-// dscan: one wave per (16-wide value slice, head, batch), blocks in reverse,
-// operands of the next block prefetched into a second register buffer.
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(64) void gdn_scan_bwd_kernel(GdnScanBwdArgs<E> a) {
+__global__ __launch_bounds__(256) void gdn_scan_bwd_kernel(GdnScanBwdArgs<E> a) {
     const int H = a.H, NC = a.NC;
     int b, h, vb;
     if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
-    const int l = threadIdx.x, r = l & 15, g = l >> 4;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
     constexpr int ND = DK / 16;
+    using Rg = ScanBwdRing<E, DK>;
+    constexpr int NU = Rg::NU, UPF = Rg::UPF;
+    constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
+    using G = RingGeom<NU>;
+    constexpr int TILE = DK * 16 * (int)sizeof(E);
+    constexpr int PF = (144 * 1024 - TILE) / G::SLOT;
+    constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
+    __shared__ __align__(16) char ring[P * G::SLOT];
+    __shared__ __align__(16) E tile[TILE / sizeof(E)];
     const size_t bh = (size_t)b * H + h;
+
+    // round m handles block NC - 1 - m
+    if (w > 0) {  // producers
+        const int pid = w - 1;
+        auto issue = [&](int m) {
+            const size_t c = bh * NC + (NC - 1 - m);
+            const E* Kh = a.Kh + c * BLK * DK + l * LE;
+            const E* WT = a.WT + c * BLK * DK + l * LE;
+            const float* Rt = a.Rt + c * DK * DV + (size_t)vb * ND * 256 + l * 4;
+            const E* dvl = a.dvlT + c * BLK * DV + (size_t)(2 * vb * UPF) * UE + l * LE;
+            auto src = [&](int u) -> const void* {
+                if (u < Rg::NKU) return Kh + u * UE;
+                if (u < Rg::NKU + Rg::NWU) return WT + (u - Rg::NKU) * UE;
+                if (u < Rg::NKU + Rg::NWU + Rg::NRU) return Rt + (u - Rg::NKU - Rg::NWU) * 256;
+                return dvl + (u - Rg::NKU - Rg::NWU - Rg::NRU) * UE;
+            };
+            ring_issue<NU>(ring + (m % P) * G::SLOT, pid, src, a.gam + c * BLK + l);
+        };
+        const int pre = NC < P - 1 ? NC : P - 1;
+        for (int m = 0; m < pre; ++m) issue(m);
+        ring_wait<G::NU_MIN>(pre - 1);  // round 0 has landed
+        ring_barrier();
+        for (int m = 0; m < NC; ++m) {
+            if (m + P - 1 < NC) issue(m + P - 1);
+            const int last = (m + P - 1 < NC ? m + P - 1 : NC - 1);
+            ring_wait<G::NU_MIN>(last - (m + 1));  // round m + 1 has landed
+            ring_barrier();
+        }
+        return;
+    }
 
     f32x4 dS[ND];
     const float* dSo = a.dS_out ? a.dS_out + bh * DK * DV : nullptr;
@@ -252,16 +292,12 @@ __global__ __launch_bounds__(64) void gdn_scan_bwd_kernel(GdnScanBwdArgs<E> a) {
     for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dS[db][i] = dSo ? dSo[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
-
-    __shared__ __align__(16) E tile[DK * 16];
-    ScanBwdOps<E, DK> A, B;
-    if (NC > 0) scan_bwd_load<E, DK, DV>(A, a, bh * NC + NC - 1, v0, r, g);
-    for (int n = NC - 1; n >= 0; n -= 2) {
-        if (n - 1 >= 0) scan_bwd_load<E, DK, DV>(B, a, bh * NC + n - 1, v0, r, g);
-        scan_bwd_step<E, DK, DV>(A, dS, a, bh * NC + n, v0, r, g, tile);
-        if (n - 1 < 0) break;
-        if (n - 2 >= 0) scan_bwd_load<E, DK, DV>(A, a, bh * NC + n - 2, v0, r, g);
-        scan_bwd_step<E, DK, DV>(B, dS, a, bh * NC + n - 1, v0, r, g, tile);
+    ring_barrier();
+    for (int m = 0; m < NC; ++m) {
+        ScanBwdOps<E, DK> o;
+        scan_bwd_from_ring<E, DK, NU>(o, ring + (m % P) * G::SLOT, l);
+        scan_bwd_step<E, DK, DV>(o, dS, a, bh * NC + (NC - 1 - m), vb, l, tile);
+        ring_barrier();
     }
     float* dSi = a.dS_in + bh * DK * DV;
 #pragma unroll
@@ -325,8 +361,8 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
     const E* vbase = a.v + tok0 * ldv + (size_t)h * DV;
     const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
-    const E* S0 = a.h + chunk * DK * DV;   // h_n  [d][v]
-    const E* dS1 = a.dh + chunk * DK * DV; // dh_n [d][v]
+    const E* S0 = a.h + chunk * DK * DV;   // h_n  [d][v], tiled
+    const E* dS1 = a.dh + chunk * DK * DV; // dh_n [d][v], tiled
     const E* UT = a.UT + chunk * BLK * DV;
     const E* dUT = a.dUT + chunk * BLK * DV;
 
@@ -373,7 +409,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     E* Qt = (E*)(lds + Lay::pA_Qt);
     E* Us = (E*)(lds + Lay::pA_U);
     stage_transposed<E, DK>(qb, ldk, Qt, nvalid);
-    stage_T<E, DV, BLK, PDV, true>(UT, BLK, Us, DV);  // Us[t][v] = U[t][v]
+    stage_T_tiled<E, DV, BLK, PDV>(UT, Us);  // Us[t][v] = U[t][v]
     __syncthreads();
 
     const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
@@ -429,7 +465,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         for (int db = 0; db < DK / 16; ++db) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfrag(S0 + (size_t)(16 * db + r) * DV + 32 * kk + 4 * g), fdo[kk]);
+            for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfragT(S0, db * (DV / 32) + kk, l), fdo[kk]);
             acc = acc * Gt;
             f32x4 qv = zero4();
             if (tw < nvalid) {
@@ -476,7 +512,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             for (int j = 0; j < 2; ++j) mma(acc, ldfrag(Qt + (16 * db + r) * PT + 32 * j + 4 * g), fpm[j]);
             f32x4 accb = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) mma(accb, ldfrag(dS1 + (size_t)(16 * db + r) * DV + 32 * kk + 4 * g), fU[kk]);
+            for (int kk = 0; kk < DV / 32; ++kk) mma(accb, ldfragT(dS1, db * (DV / 32) + kk, l), fU[kk]);
             if (tw < nvalid) {
                 const f32x4 kv = ld4(kb + (size_t)tw * ldk + 16 * db + 4 * g);
                 kdk += kv[0] * accb[0] + kv[1] * accb[1] + kv[2] * accb[2] + kv[3] * accb[3];
@@ -509,7 +545,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     E* dWT = (E*)(lds + Lay::pB_dWT);
     E* dTT = (E*)(lds + Lay::pB_dTT);
     E* Ms = (E*)(lds + Lay::pB_Ms);
-    stage_T<E, DV, BLK, PDV, true>(dUT, BLK, dUs, DV);  // dUs[t][v]
+    stage_T_tiled<E, DV, BLK, PDV>(dUT, dUs);  // dUs[t][v]
     __syncthreads();
     // dW^T[db][w] = -(S0 dU^T): rows d, cols t = tw
     {
@@ -520,7 +556,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         for (int db = 0; db < DK / 16; ++db) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfrag(S0 + (size_t)(16 * db + r) * DV + 32 * kk + 4 * g), fdu[kk]);
+            for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfragT(S0, db * (DV / 32) + kk, l), fdu[kk]);
             acc = -acc;
             st4(dWs + tw * PDK + 16 * db + 4 * g, acc);
 #pragma unroll
@@ -595,7 +631,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            mma(acc, ldfragP(dUT + (size_t)(16 * vb + r) * BLK + 32 * j + 8 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
+            mma(acc, ldfragT(dUT, 2 * vb + j, l), ldfrag(TT + tw * PT + 32 * j + 4 * g));
         if (tw < nvalid) {
             const f32x4 vv = ld4(vbase + (size_t)tw * ldv + 16 * vb + 4 * g);
             dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
@@ -681,7 +717,7 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     launch("gdn_scan_fwd_rec", gdn_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(256), st, sa);
     GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
                          L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC, L.B * L.H};
-    launch("gdn_scan_bwd", gdn_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sb);
+    launch("gdn_scan_bwd", gdn_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(256), st, sb);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const E*)ws.dUT,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};

@@ -16,9 +16,10 @@
 //         slices): h_n = S;  U_n = Ut_n - W_n S;  S <- Gam_C S + Kh_n^T U_n.
 //   out   (Out, parallel over blocks):  O = Diag(Gam) Q h_n + (Q K^T * G * tril) U_n.
 //
-// U_n is the delta rule's "new value" V^new of Eq. 2.  Workspace layouts are
-// chosen so that every scan operand is read with contiguous 8/16-byte loads
-// straight into matrix-core fragments (see clr_device.h).
+// U_n is the delta rule's "new value" V^new of Eq. 2.  Every per-block matrix
+// in the workspace (W, Kh^T, Ut^T, the saved states, U^T) is kept in the tiled
+// fragment-major layout of clr_device.h, so that each wave moves whole 1-KB
+// runs straight into (or out of) matrix-core fragments.
 #pragma once
 
 #include "clr_kernels.h"
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     }
     __syncthreads();
 
-    // W^T[d][t] = sum_s Kt[d][s] T1[t][s]  -> written as W[t][d] (token-major)
+    // W^T[d][t] = sum_s Kt[d][s] T1[t][s]  -> stored as W[t][d] (tiled)
     E* Wout = a.W + chunk * BLK * DK;
     for (int tile = w; tile < (DK / 16) * 4; tile += 4) {
         const int db = tile >> 2, tb = tile & 3;
@@ -213,9 +214,9 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
             Frag<E> fb = ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g);
             mma(acc, fa, fb);
         }
-        st4(Wout + (size_t)(16 * tb + r) * DK + kperm(16 * db + 4 * g), acc);
+        st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
     }
-    // Ut[t][v] = sum_s T2[t][s] Vt[v][s]  -> written as Ut^T[v][t]
+    // Ut[t][v] = sum_s T2[t][s] Vt[v][s]  -> stored as Ut^T[v][t] (tiled)
     E* Uout = a.UtT + chunk * BLK * DV;
     for (int tile = w; tile < 4 * (DV / 16); tile += 4) {
         const int tb = tile % 4, vb = tile / 4;
@@ -226,26 +227,22 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
             Frag<E> fb = ldfrag(Vt + (16 * vb + r) * PT + 32 * j + 4 * g);
             mma(acc, fa, fb);
         }
-        st4(Uout + (size_t)(16 * vb + r) * BLK + kperm(16 * tb + 4 * g), acc);
+        st4(Uout + toff<E>(16 * vb + r, 16 * tb + 4 * g, BLK), acc);
     }
     // Kh^T[d][t] = exp(gamma_C - gamma_t) K[t][d]
-    E* Khout = a.KhT + chunk * BLK * DK;
     const float gC = s_gam[BLK - 1];
-    for (int idx = tid; idx < DK * (BLK / 4); idx += 256) {
-        const int d = idx / (BLK / 4), t4 = (idx % (BLK / 4)) * 4;
-        f32x4 x = ld4(Kt + d * PT + t4);
+    store_tiled<E, DK, BLK>(a.KhT + chunk * BLK * DK, [&](int d, int t) {
+        f32x4 x = ld4(Kt + d * PT + t);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] *= __expf(gC - s_gam[t4 + i]);
-        st4(Khout + (size_t)d * BLK + kperm(t4), x);
-    }
+        for (int i = 0; i < 4; ++i) x[i] *= __expf(gC - s_gam[t + i]);
+        return x;
+    });
 }
 
 // ---------------------------------------------------------------------------
-// scan: one wave per (16-wide value slice, head, batch); sequential over the
-// blocks.  The fp32 state slice S[0:DK][v0:v0+16] lives in accumulator tiles.
-// Writes the state entering each block and U_n^T[v][t].  The operands of
-// block n+1 are loaded while block n is computed (two register buffers,
-// loop unrolled by two so the buffers never need copying).
+// scan: one work-group per (16-wide value slice, head, batch), sequential over
+// the blocks.  The fp32 state slice S[0:DK][v0:v0+16] lives in accumulator
+// tiles of the consumer wave.  Writes the state entering each block and U_n^T.
 // ---------------------------------------------------------------------------
 template <typename E, int DK> struct ScanFwdOps {
     Frag<E> w[4][DK / 32];    // W rows (A: m = t, k = d)
@@ -253,25 +250,6 @@ template <typename E, int DK> struct ScanFwdOps {
     Frag<E> ut[2];            // Ut^T[v0 + r][token pair-tiles 2j, 2j+1] (accumulator layout)
     float gC;                 // gamma at the last token of the block
 };
-
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void scan_fwd_load(ScanFwdOps<E, DK>& o, const GdnScanArgs<E>& a, size_t chunk,
-                                              int v0, int r, int g) {
-    const E* W = a.W + chunk * BLK * DK;
-    const E* KhT = a.KhT + chunk * BLK * DK;
-    const E* UtT = a.UtT + chunk * BLK * DV;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) o.w[tb][kk] = ldfragP(W + (size_t)(16 * tb + r) * DK + 32 * kk + 8 * g);
-#pragma unroll
-    for (int db = 0; db < DK / 16; ++db)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) o.kh[db][j] = ldfragP(KhT + (size_t)(16 * db + r) * BLK + 32 * j + 8 * g);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) o.ut[j] = ldfragP(UtT + (size_t)(v0 + r) * BLK + 32 * j + 8 * g);
-    o.gC = a.gam[chunk * BLK + BLK - 1];
-}
 
 // Store the fp32 state slice (accumulator tiles, rows d, column v0 + r) in
 // key-major h[d][v] layout: staged through LDS (tile[d][16 v]) so that each
@@ -302,31 +280,59 @@ __device__ __forceinline__ void store_state_kmajor(E* h, const f32x4 (&S)[DK / 1
     store_rows16<E, DK>(h, DV, S, tile, v0, r, g);
 }
 
+// Store a state slice (accumulator tiles: rows d = 16 db + 4g + i, column
+// v0 + r) into the tiled key-major h[d][v] (R = DK, C = DV).  A lane's values
+// belong to four different lane units of that layout, so the slice is
+// transposed through LDS (tile[d][16], used by the calling wave only); lane
+// l then writes columns v0 + 4 (l >> 4) .. +3 of row 16 db + (l & 15), which
+// is one contiguous half of a lane unit.
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void store_state_tiled(E* h, const f32x4 (&S)[DK / 16], E* tile, int v0, int l) {
+    const int r = l & 15, g = l >> 4;
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tile[(16 * db + 4 * g + i) * 16 + r] = from_f<E>(S[db][i]);
+    // LDS operations of one wave complete in order
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db) {
+        const int d = 16 * db + r;
+        E* dst = h + toff<E>(d, v0 + 4 * g, DV);
+        const E* src = tile + d * 16 + 4 * g;
+        if constexpr (sizeof(E) == 2) *(bf16x4*)dst = *(const bf16x4*)src;
+        else *(f32x4*)dst = *(const f32x4*)src;
+    }
+    asm volatile("" ::: "memory");
+}
+
+// One block of the recurrence.  HNAT selects the layout of the saved states:
+// false -> tiled h^T[v][d] (read by the forward's out kernel), true -> tiled
+// h[d][v] (read by the backward).
 template <typename E, int DK, int DV, bool HNAT>
 __device__ __forceinline__ void scan_fwd_step(const ScanFwdOps<E, DK>& o, f32x4 (&S)[DK / 16],
-                                              const GdnScanArgs<E>& a, size_t chunk, int v0, int r, int g,
-                                              E* tile) {
-    constexpr int ND = DK / 16;
+                                              const GdnScanArgs<E>& a, size_t chunk, int vb, int l, E* tile) {
+    constexpr int ND = DK / 16, KK = DK / 32;
+    Frag<E> fs[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
     // state entering block n
     if (a.hT) {
         E* hT = a.hT + chunk * DK * DV;
         if constexpr (HNAT) {
-            store_state_kmajor<E, DK, DV>(hT, S, tile, v0, r, g);
+            store_state_tiled<E, DK, DV>(hT, S, tile, 16 * vb, l);
         } else {
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) st8P(hT + (size_t)(v0 + r) * DK + 32 * kk + 8 * g, S[2 * kk], S[2 * kk + 1]);
+            for (int kk = 0; kk < KK; ++kk) st8T(hT, vb * KK + kk, l, S[2 * kk], S[2 * kk + 1]);
         }
     }
     // U = Ut - W S    (tiles: rows t = 16tb + 4g + i, col v0 + r)
-    Frag<E> fs[DK / 32];
-#pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
     f32x4 U[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, o.w[tb][kk], fs[kk]);
+        for (int kk = 0; kk < KK; ++kk) mma(acc, o.w[tb][kk], fs[kk]);
         U[tb] = acc;
     }
 #pragma unroll
@@ -340,15 +346,16 @@ __device__ __forceinline__ void scan_fwd_step(const ScanFwdOps<E, DK>& o, f32x4 
             U[2 * j + 1] = f.hi - U[2 * j + 1];
         }
     }
-    if (a.UT) {
-        E* UT = a.UT + chunk * BLK * DV;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) st8P(UT + (size_t)(v0 + r) * BLK + 32 * j + 8 * g, U[2 * j], U[2 * j + 1]);
-    }
-    // S <- Gam_C S + Kh^T U
+    // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles
     Frag<E> fu[2];
     fu[0] = frag_from_acc<E>(U[0], U[1]);
     fu[1] = frag_from_acc<E>(U[2], U[3]);
+    if (a.UT) {
+        E* UT = a.UT + chunk * BLK * DV;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) st8T(UT, 2 * vb + j, l, U[2 * j], U[2 * j + 1]);
+    }
+    // S <- Gam_C S + Kh^T U
     const float GC = __expf(o.gC);
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
@@ -376,10 +383,10 @@ __device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK>& o, const c
     o.gC = ring_small<NU>(slot, BLK - 1);
 }
 
-// HNAT selects the layout of the saved states: false -> h^T[v][d] (read by the
-// forward's out kernel), true -> h[d][v] (read by the backward).
 // Work-group: wave 0 runs the recurrence, waves 1..3 stream the operands of
-// the next blocks into the LDS ring (clr_ring.h).
+// the next blocks into the LDS ring (clr_ring.h).  All operands are tiled, so
+// ring unit u of a block is the contiguous 1-KB run u of
+// [W | Kh^T | Ut^T fragments (vb, 0..1)].
 template <typename E, int DK, int DV, bool HNAT>
 __global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
     const int H = a.H, NC = a.NC;
@@ -388,8 +395,9 @@ __global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
     constexpr int ND = DK / 16;
-    constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 16-byte units per fragment
-    constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * ND, NU = (NWF + NKF + 2) * UPF;
+    constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 1-KB units per fragment
+    constexpr int KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF, NU = NWU + NKU + 2 * UPF;
+    constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
     using G = RingGeom<NU>;
     constexpr int TILE = HNAT ? DK * 16 * (int)sizeof(E) : 16;
     constexpr int PF = (144 * 1024 - TILE) / G::SLOT;
@@ -402,16 +410,13 @@ __global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
         const int pid = w - 1;
         auto issue = [&](int n) {
             const size_t c = bh * NC + n;
-            const E* W = a.W + c * BLK * DK;
-            const E* KhT = a.KhT + c * BLK * DK;
-            const E* UtT = a.UtT + c * BLK * DV;
+            const E* W = a.W + c * BLK * DK + l * LE;
+            const E* KhT = a.KhT + c * BLK * DK + l * LE;
+            const E* UtT = a.UtT + c * BLK * DV + (size_t)(2 * vb * UPF) * UE + l * LE;
             auto src = [&](int u) -> const void* {
-                const int f = u / UPF, half = u % UPF;
-                const E* p;
-                if (f < NWF) p = W + (size_t)(16 * (f / KK) + r) * DK + 32 * (f % KK) + 8 * g;
-                else if (f < NWF + NKF) p = KhT + (size_t)(16 * ((f - NWF) / 2) + r) * BLK + 32 * ((f - NWF) % 2) + 8 * g;
-                else p = UtT + (size_t)(v0 + r) * BLK + 32 * (f - NWF - NKF) + 8 * g;
-                return p + 4 * half;
+                if (u < NWU) return W + u * UE;
+                if (u < NWU + NKU) return KhT + (u - NWU) * UE;
+                return UtT + (u - NWU - NKU) * UE;
             };
             ring_issue<NU>(ring + (n % P) * G::SLOT, pid, src, a.gam + c * BLK + l);
         };
@@ -438,7 +443,7 @@ __global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
     for (int n = 0; n < NC; ++n) {
         ScanFwdOps<E, DK> o;
         scan_fwd_from_ring<E, DK, NU>(o, ring + (n % P) * G::SLOT, l);
-        scan_fwd_step<E, DK, DV, HNAT>(o, S, a, bh * NC + n, v0, r, g, tile);
+        scan_fwd_step<E, DK, DV, HNAT>(o, S, a, bh * NC + n, vb, l, tile);
         ring_barrier();
     }
     if (a.S_out) {
@@ -505,14 +510,14 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
-            Frag<E> fh = ldfragP(hT + (size_t)(16 * vb + r) * DK + 32 * kk + 8 * g);
+            Frag<E> fh = ldfragT(hT, vb * (DK / 32) + kk, l);
             mma(acc, fh, fq[kk]);
         }
         acc = acc * Gt;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             if (2 * j <= w) {
-                Frag<E> fu = ldfragP(UT + (size_t)(16 * vb + r) * BLK + 32 * j + 8 * g);
+                Frag<E> fu = ldfragT(UT, 2 * vb + j, l);
                 mma(acc, fu, fp[j]);
             }
         }
