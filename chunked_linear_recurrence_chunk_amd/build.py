@@ -4,7 +4,8 @@
 
 Each ``csrc/*.hip`` file is compiled with hipcc (device code for gfx950 only)
 into ``_build/`` and linked into ``libclr.so`` next to this file.  Packed
-fp32 vector instructions are disabled for all device code.
+fp32 vector instructions are disabled for all device code, and matrix-core
+accumulators are kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -25,6 +26,10 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in VGPRs: the recurrences touch their fp32
+    # state with vector ALU work every block, which AGPR accumulators would
+    # turn into accvgpr copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
 
