@@ -194,6 +194,74 @@ __device__ __forceinline__ void st8P(float* p, f32x4 lo, f32x4 hi) {
 }
 
 // ---------------------------------------------------------------------------
+// Row-major LDS tiles and transposing fragment reads.
+//
+// A 16-bit ds_read_b64_tr_b16 works on groups of 16 lanes: lane L' of a group
+// points at four consecutive elements M[L'][0..3], and lane i of the group
+// receives M[4j + (i >> 2)][i & 3], j = 0..3.  With lane L' = 16g + 4j + q
+// pointing at X[k0 + 4g + j][n0 + 4q], lane (r, g) receives
+// X[k0 + 4g + j][n0 + r], j = 0..3: the k-half of a B fragment of a
+// row-major X[k][n] (equivalently an A fragment of X^T).  Every matrix a
+// block kernel needs in both orientations is therefore staged once, row-major
+// (whole 16-byte LDS writes), and read transposed where needed.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// B fragment (k = k0 .. k0 + 31, n = n0 .. n0 + 15) of a row-major matrix
+// X[k][n] in LDS with row pitch P elements (P a multiple of 4).
+__device__ __forceinline__ Frag<bf16> ldfrag_tr(const bf16* X, int P, int k0, int n0, int l) {
+    const int g = l >> 4, j = (l >> 2) & 3, q = l & 3;
+    const bf16* p = X + (k0 + 4 * g + j) * P + n0 + 4 * q;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * P));
+    Frag<bf16> f;
+    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+__device__ __forceinline__ Frag<float> ldfrag_tr(const float* X, int P, int k0, int n0, int l) {
+    const int r = l & 15, g = l >> 4;
+    Frag<float> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.lo[i] = X[(k0 + 4 * g + i) * P + n0 + r];
+        f.hi[i] = X[(k0 + 16 + 4 * g + i) * P + n0 + r];
+    }
+    return f;
+}
+
+// Coalesced staging of an R x CC token-major tile (global row stride ld) by a
+// 256-thread work-group, in two steps so that a kernel can put the loads of
+// several tiles in flight together: load_rows() issues every 16-byte load at
+// once (rows >= nvalid read as zeros), store_rows() writes the registers
+// row-major into LDS with row pitch P (whole 16-byte writes).
+template <typename E, int R, int CC> struct RowsRegs {
+    static constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = CC / VEC, N = R * PER_ROW / 256;
+    static_assert(R * PER_ROW % 256 == 0, "tile must split evenly over 256 threads");
+    uint4 u[N];
+};
+template <typename E, int R, int CC>
+__device__ __forceinline__ RowsRegs<E, R, CC> load_rows(const E* __restrict__ src, size_t ld, int nvalid) {
+    using X = RowsRegs<E, R, CC>;
+    X x;
+#pragma unroll
+    for (int j = 0; j < X::N; ++j) {
+        const int idx = threadIdx.x + 256 * j, t = idx / X::PER_ROW, cb = idx % X::PER_ROW;
+        x.u[j] = t < nvalid ? *(const uint4*)(src + (size_t)t * ld + cb * X::VEC) : uint4{0u, 0u, 0u, 0u};
+    }
+    return x;
+}
+template <typename E, int R, int CC, int P>
+__device__ __forceinline__ void store_rows(const RowsRegs<E, R, CC>& x, E* dst) {
+    using X = RowsRegs<E, R, CC>;
+    static_assert(P % X::VEC == 0, "row pitch must keep 16-byte alignment");
+#pragma unroll
+    for (int j = 0; j < X::N; ++j) {
+        const int idx = threadIdx.x + 256 * j, t = idx / X::PER_ROW, cb = idx % X::PER_ROW;
+        *(uint4*)(dst + t * P + cb * X::VEC) = x.u[j];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Tiled ("fragment-major") storage of a block-local matrix X[R][C], C a
 // multiple of 32.  The 16 x 32 fragment f = (row / 16) * (C / 32) + col / 32
 // is one contiguous run in lane order: lane l = 16g + r holds the A-fragment

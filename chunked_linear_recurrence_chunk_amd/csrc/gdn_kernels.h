@@ -128,8 +128,34 @@ __device__ void stage_transposed(const E* __restrict__ src, size_t ld, E* dst, i
     stage_T<E, BLK, D, PT>(src, ld, dst, nvalid);
 }
 
+// Row pitch (elements) of a row-major LDS tile with D columns: keeps rows
+// 16-byte aligned and spreads consecutive rows over the LDS banks.
+template <typename E, int D> constexpr int RP = D + 16 / (int)sizeof(E);
+
+// Scale element i of a fragment whose k index runs over k0 + kmap(g, i) by s[k].
+__device__ __forceinline__ void frag_scale_k(Frag<bf16>& x, const float* s, int k0, int g) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x.v[i] = (bf16)((float)x.v[i] * s[k0 + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4)]);
+}
+__device__ __forceinline__ void frag_scale_k(Frag<float>& x, const float* s, int k0, int g) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x.lo[i] *= s[k0 + 4 * g + i];
+        x.hi[i] *= s[k0 + 16 + 4 * g + i];
+    }
+}
+__device__ __forceinline__ void st_fragT(bf16* base, int f, int l, const Frag<bf16>& x) {
+    *(bf16x8*)(base + ((size_t)f * 64 + l) * 8) = x.v;
+}
+__device__ __forceinline__ void st_fragT(float* base, int f, int l, const Frag<float>& x) {
+    *(f32x4*)(base + ((size_t)(2 * f) * 64 + l) * 4) = x.lo;
+    *(f32x4*)(base + ((size_t)(2 * f + 1) * 64 + l) * 4) = x.hi;
+}
+
 // ---------------------------------------------------------------------------
-// prep: one work-group (4 waves) per (block n, head h, batch b).
+// prep: one work-group (4 waves) per (block n, head h, batch b).  K and V are
+// staged row-major in LDS with all loads in flight at once; products that
+// contract over the token index read them transposed (ldfrag_tr).
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
@@ -139,40 +165,42 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;  // first token (b, n*64)
     const size_t chunk = ((size_t)b * H + h) * NC + n;    // workspace block index
     const int nvalid = min(BLK, T - n * BLK);             // tokens of this block inside the sequence
+    constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
 
-    __shared__ float s_gam[BLK], s_bet[BLK], s_Gam[BLK];
+    __shared__ float s_gam[BLK], s_bet[BLK], s_Gam[BLK], s_ek[BLK];
     __shared__ float Am[BLK * AP], Td[4 * 256];
-    __shared__ E Kt[DK * PT], Vt[DV * PT], T1[BLK * PT], T2[BLK * PT];
+    __shared__ __align__(16) E Ks[BLK * PK], Vs[BLK * PV], T1[BLK * PT], T2[BLK * PT];
 
+    const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * H * DK + (size_t)h * DK, (size_t)H * DK, nvalid);
+    const auto vx = load_rows<E, BLK, DV>(a.v + tok0 * H * DV + (size_t)h * DV, (size_t)H * DV, nvalid);
     if (w == 0) {
         // tokens past the end are identity steps: g = 0, beta = 0
         const size_t ig = (tok0 + l) * H + h;
         const float gv = l < nvalid ? to_f(a.g[ig]) : 0.f;
+        const float bv = l < nvalid ? to_f(a.beta[ig]) : 0.f;
         const float gam = wave_prefix_sum(gv);
+        const float gC = __shfl(gam, BLK - 1, 64);
         s_gam[l] = gam;
         s_Gam[l] = __expf(gam);
-        s_bet[l] = l < nvalid ? to_f(a.beta[ig]) : 0.f;
+        s_ek[l] = __expf(gC - gam);
+        s_bet[l] = bv;
         a.gam[chunk * BLK + l] = gam;
     }
-    stage_transposed<E, DK>(a.k + tok0 * H * DK + (size_t)h * DK, (size_t)H * DK, Kt, nvalid);
-    stage_transposed<E, DV>(a.v + tok0 * H * DV + (size_t)h * DV, (size_t)H * DV, Vt, nvalid);
+    store_rows<E, BLK, DK, PK>(kx, Ks);
+    store_rows<E, BLK, DV, PV>(vx, Vs);
     __syncthreads();
 
     // Gram block row w: A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s), s < r.
     {
-        const E* kb = a.k + tok0 * H * DK + (size_t)h * DK;
-        const size_t ld = (size_t)H * DK;
         Frag<E> fa[DK / 32];
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) fa[kk] = ldfrag_row(kb, 16 * w + r, nvalid, ld, 32 * kk + 4 * g);
+        for (int kk = 0; kk < DK / 32; ++kk) fa[kk] = ldfrag(Ks + (16 * w + r) * PK + 32 * kk + 4 * g);
+#pragma unroll
         for (int j = 0; j < 4; ++j) {
             f32x4 acc = zero4();
             if (j <= w) {
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) {
-                    Frag<E> fb = ldfrag_row(kb, 16 * j + r, nvalid, ld, 32 * kk + 4 * g);
-                    mma(acc, fa[kk], fb);
-                }
+                for (int kk = 0; kk < DK / 32; ++kk) mma(acc, fa[kk], ldfrag(Ks + (16 * j + r) * PK + 32 * kk + 4 * g));
             }
             // D tile rows = 16w + 4g + i (r index "row"), cols = 16j + r (s index)
 #pragma unroll
@@ -203,40 +231,38 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     }
     __syncthreads();
 
-    // W^T[d][t] = sum_s Kt[d][s] T1[t][s]  -> stored as W[t][d] (tiled)
+    // W^T[d][t] = sum_s K^T[d][s] T1[t][s]  -> stored as W[t][d] (tiled)
     E* Wout = a.W + chunk * BLK * DK;
+#pragma unroll
     for (int tile = w; tile < (DK / 16) * 4; tile += 4) {
         const int db = tile >> 2, tb = tile & 3;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            Frag<E> fa = ldfrag(Kt + (16 * db + r) * PT + 32 * j + 4 * g);
-            Frag<E> fb = ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g);
-            mma(acc, fa, fb);
-        }
+        for (int j = 0; j < 2; ++j)
+            mma(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g));
         st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
     }
-    // Ut[t][v] = sum_s T2[t][s] Vt[v][s]  -> stored as Ut^T[v][t] (tiled)
+    // Ut[t][v] = sum_s T2[t][s] V[s][v]  -> stored as Ut^T[v][t] (tiled)
     E* Uout = a.UtT + chunk * BLK * DV;
+#pragma unroll
     for (int tile = w; tile < 4 * (DV / 16); tile += 4) {
         const int tb = tile % 4, vb = tile / 4;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            Frag<E> fa = ldfrag(T2 + (16 * tb + r) * PT + 32 * j + 4 * g);
-            Frag<E> fb = ldfrag(Vt + (16 * vb + r) * PT + 32 * j + 4 * g);
-            mma(acc, fa, fb);
-        }
+        for (int j = 0; j < 2; ++j)
+            mma(acc, ldfrag(T2 + (16 * tb + r) * PT + 32 * j + 4 * g), ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
         st4(Uout + toff<E>(16 * vb + r, 16 * tb + 4 * g, BLK), acc);
     }
-    // Kh^T[d][t] = exp(gamma_C - gamma_t) K[t][d]
-    const float gC = s_gam[BLK - 1];
-    store_tiled<E, DK, BLK>(a.KhT + chunk * BLK * DK, [&](int d, int t) {
-        f32x4 x = ld4(Kt + d * PT + t);
+    // Kh^T[d][t] = exp(gamma_C - gamma_t) K[t][d] (tiled): its fragment (db, j)
+    // is the B fragment of Kh over tokens 32j.., columns 16db..
+    E* Khout = a.KhT + chunk * BLK * DK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] *= __expf(gC - s_gam[t + i]);
-        return x;
-    });
+    for (int f = w; f < 2 * (DK / 16); f += 4) {
+        const int db = f >> 1, j = f & 1;
+        Frag<E> x = ldfrag_tr(Ks, PK, 32 * j, 16 * db, l);
+        frag_scale_k(x, s_ek, 32 * j, g);
+        st_fragT(Khout, f, l, x);
+    }
 }
 
 // ---------------------------------------------------------------------------
