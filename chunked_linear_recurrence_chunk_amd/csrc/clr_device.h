@@ -358,6 +358,39 @@ __device__ __forceinline__ void stage_T_tiled(const E* __restrict__ src, E* dst)
     }
 }
 
+// Tiled global X[R][C] -> row-major LDS (row pitch P), in two steps like
+// load_rows / store_rows: every 16-byte unit is loaded at once, then each
+// unit's two 4-element halves are written to their rows.
+template <typename E, int R, int C> struct TiledRegs {
+    static constexpr int UNITS = R * C * (int)sizeof(E) / 16, N = UNITS / 256;
+    static_assert(UNITS % 256 == 0, "tile must split evenly over 256 threads");
+    uint4 u[N];
+};
+template <typename E, int R, int C>
+__device__ __forceinline__ TiledRegs<E, R, C> load_tiled(const E* __restrict__ src) {
+    TiledRegs<E, R, C> x;
+#pragma unroll
+    for (int j = 0; j < x.N; ++j) x.u[j] = *(const uint4*)(src + (size_t)(threadIdx.x + 256 * j) * (16 / sizeof(E)));
+    return x;
+}
+template <typename E, int R, int C, int P>
+__device__ __forceinline__ void store_untiled(const TiledRegs<E, R, C>& x, E* dst) {
+#pragma unroll
+    for (int j = 0; j < x.N; ++j) {
+        const int u = threadIdx.x + 256 * j;
+        if constexpr (sizeof(E) == 2) {
+            const int f = u >> 6, lane = u & 63;
+            const int row = 16 * (f / (C / 32)) + (lane & 15), c = 32 * (f % (C / 32)) + 4 * (lane >> 4);
+            *(uint2*)(dst + row * P + c) = uint2{x.u[j].x, x.u[j].y};
+            *(uint2*)(dst + row * P + c + 16) = uint2{x.u[j].z, x.u[j].w};
+        } else {
+            const int f = u >> 7, half = (u >> 6) & 1, lane = u & 63;
+            const int row = 16 * (f / (C / 32)) + (lane & 15), c = 32 * (f % (C / 32)) + 16 * half + 4 * (lane >> 4);
+            *(uint4*)(dst + row * P + c) = x.u[j];
+        }
+    }
+}
+
 // Accumulator-tiled fp32 storage of an [M][N] matrix: the 16 x 16 tile
 // (mb, nb) is 1 KB in lane order, lane l = 16g + r holding rows 16 mb + 4g + i
 // (i = 0..3) of column 16 nb + r.  Tiles are ordered nb-major: tile index

@@ -61,7 +61,10 @@ template <typename E> struct GdnIntraArgs {
 };
 
 // ---------------------------------------------------------------------------
-// prep2: one work-group (4 waves) per (block, head, batch).
+// prep2: one work-group (4 waves) per (block, head, batch).  Q, dO and W are
+// staged row-major in LDS (all loads in flight at once) and read transposed
+// where a product contracts over tokens; wave w keeps K rows 16w.. in
+// registers (B operand of P and the rows of Kh it writes).
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
@@ -75,22 +78,51 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
     const E* qb = a.q + tok0 * ldk + (size_t)h * DK;
     const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
     const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
+    constexpr int PQ = RP<E, DK>, PO = RP<E, DV>, KK = DK / 32, ND = DK / 16, NVB = DV / 16;
 
-    __shared__ float s_gam[BLK];
-    __shared__ E Qt[DK * PT], dOt[DV * PT], Wt[DK * PT], dvlt[DV * PT];
+    __shared__ float s_gam[BLK], s_Gam[BLK];
+    __shared__ __align__(16) E Qs[BLK * PQ], dOs[BLK * PO], Ws[BLK * PQ], dvlt[DV * PT];
 
-    if (tid < BLK) s_gam[tid] = a.gam[chunk * BLK + tid];
-    stage_transposed<E, DK>(qb, ldk, Qt, nvalid);
-    stage_transposed<E, DV>(dob, ldv, dOt, nvalid);
-    stage_T_tiled<E, BLK, DK, PT>(a.W + chunk * BLK * DK, Wt);  // Wt[d][t] = W[t][d]
+    const auto qx = load_rows<E, BLK, DK>(qb, ldk, nvalid);
+    const auto ox = load_rows<E, BLK, DV>(dob, ldv, nvalid);
+    const auto wx = load_tiled<E, BLK, DK>(a.W + chunk * BLK * DK);
+    Frag<E> fk[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) fk[kk] = ldfrag_row(kb, 16 * w + r, nvalid, ldk, 32 * kk + 4 * g);
+    if (tid < BLK) {
+        const float gm = a.gam[chunk * BLK + tid];
+        s_gam[tid] = gm;
+        s_Gam[tid] = __expf(gm);
+    }
+    store_rows<E, BLK, DK, PQ>(qx, Qs);
+    store_rows<E, BLK, DV, PO>(ox, dOs);
+    store_untiled<E, BLK, DK, PQ>(wx, Ws);
     __syncthreads();
 
     const float gC = s_gam[BLK - 1];
-    // W^T[d][t] and Kh[t][d] = exp(gamma_C - gamma_t) K[t][d], both tiled
-    store_tiled<E, DK, BLK>(a.WT + chunk * BLK * DK, [&](int d, int t) { return ld4(Wt + d * PT + t); });
-    store_tiled<E, BLK, DK>(a.Kh + chunk * BLK * DK, [&](int t, int d) {
-        return t < nvalid ? ld4(kb + (size_t)t * ldk + d) * __expf(gC - s_gam[t]) : zero4();
-    });
+    // W^T (tiled; A: m = d, k = t): fragment (db, j) is the B fragment of W
+    // over tokens 32j.., columns 16db..
+    E* WT = a.WT + chunk * BLK * DK;
+#pragma unroll
+    for (int f = w; f < 2 * ND; f += 4) st_fragT(WT, f, l, ldfrag_tr(Ws, PQ, 32 * (f & 1), 16 * (f >> 1), l));
+    // Kh[t][d] = exp(gamma_C - gamma_t) K[t][d] (tiled; A: m = t, k = d):
+    // fragments (w, kk) are this wave's K rows.
+    {
+        E* Kh = a.Kh + chunk * BLK * DK;
+        const float ek = __expf(gC - s_gam[16 * w + r]);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            Frag<E> x = fk[kk];
+            if constexpr (sizeof(E) == 2) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x.v[i] = (bf16)((float)x.v[i] * ek);
+            } else {
+                x.lo = x.lo * ek;
+                x.hi = x.hi * ek;
+            }
+            st_fragT(Kh, w * KK + kk, l, x);
+        }
+    }
     // dvloc[s][v] = sum_t P[t][s] dO[t][v],  P[t][s] = (q_t . k_s) exp(gamma_t - gamma_s), s <= t.
     // Wave w owns s-block w: P[tb][w] tiles (rows t, cols s) chain into A = P^T.
     f32x4 P[4];
@@ -99,11 +131,7 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
         f32x4 acc = zero4();
         if (tb >= w) {
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                Frag<E> fq = ldfrag_row(qb, 16 * tb + r, nvalid, ldk, 32 * kk + 4 * g);
-                Frag<E> fk = ldfrag_row(kb, 16 * w + r, nvalid, ldk, 32 * kk + 4 * g);
-                mma(acc, fq, fk);
-            }
+            for (int kk = 0; kk < KK; ++kk) mma(acc, ldfrag(Qs + (16 * tb + r) * PQ + 32 * kk + 4 * g), fk[kk]);
             const int s = 16 * w + r;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -117,32 +145,34 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
     fp[0] = frag_from_acc<E>(P[0], P[1]);
     fp[1] = frag_from_acc<E>(P[2], P[3]);
     E* dvlT = a.dvlT + chunk * BLK * DV;
-    #pragma unroll
-    for (int vb = 0; vb < DV / 16; ++vb) {
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag(dOt + (16 * vb + r) * PT + 32 * j + 4 * g));
+        for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
         st4(dvlT + toff<E>(16 * vb + r, 16 * w + 4 * g, BLK), acc);
         st4(dvlt + (16 * vb + r) * PT + 16 * w + 4 * g, acc);
     }
-    // Qt <- (Diag(Gam) Q)^T in place
-    for (int idx = tid; idx < DK * (BLK / 4); idx += 256) {
-        const int d = idx / (BLK / 4), t4 = (idx % (BLK / 4)) * 4;
-        f32x4 x = ld4(Qt + d * PT + t4);
+    __syncthreads();
+    // Qs <- Diag(Gam) Q in place
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] *= __expf(s_gam[t4 + i]);
-        st4(Qt + d * PT + t4, x);
+    for (int j = 0; j < RowsRegs<E, BLK, DK>::N; ++j) {
+        constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = DK / VEC;
+        const int idx = tid + 256 * j, t = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
+        const float G = s_Gam[t];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) Qs[t * PQ + c + i] = from_f<E>(to_f(Qs[t * PQ + c + i]) * G);
     }
     __syncthreads();
     // R[d][v] = sum_t Qg^T[d][t] dO[t][v] - sum_t W^T[d][t] dvloc[t][v]   (fp32, accumulator-tiled)
     float* Rt = a.Rt + chunk * DK * DV;
-    for (int tile = w; tile < (DK / 16) * (DV / 16); tile += 4) {
-        const int db = tile % (DK / 16), vb = tile / (DK / 16);
+    for (int tile = w; tile < ND * NVB; tile += 4) {
+        const int db = tile % ND, vb = tile / ND;
         f32x4 acc = zero4(), acc2 = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            mma(acc, ldfrag(Qt + (16 * db + r) * PT + 32 * j + 4 * g), ldfrag(dOt + (16 * vb + r) * PT + 32 * j + 4 * g));
-            mma(acc2, ldfrag(Wt + (16 * db + r) * PT + 32 * j + 4 * g), ldfrag(dvlt + (16 * vb + r) * PT + 32 * j + 4 * g));
+            mma(acc, ldfrag_tr(Qs, PQ, 32 * j, 16 * db, l), ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
+            mma(acc2, ldfrag_tr(Ws, PQ, 32 * j, 16 * db, l), ldfrag(dvlt + (16 * vb + r) * PT + 32 * j + 4 * g));
         }
         *(f32x4*)(Rt + atoff(db, vb, DK, l)) = acc - acc2;
     }

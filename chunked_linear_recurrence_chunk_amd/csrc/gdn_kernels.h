@@ -484,7 +484,9 @@ __global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
 // ---------------------------------------------------------------------------
 // out: one work-group (4 waves) per (block, head, batch); wave w owns tokens
 // 16w..16w+15 of the block.  Computes O^T tiles so that each lane writes four
-// contiguous output values.
+// contiguous output values.  Q and K are staged row-major in LDS (all loads
+// in flight at once); the tiled h^T / U^T fragments of the next value slice
+// are loaded while the current one is computed.
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
@@ -494,17 +496,33 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
     const size_t chunk = ((size_t)b * H + h) * NC + n;
     const float* gam = a.gam + chunk * BLK;
-    const E* qb = a.q + tok0 * H * DK + (size_t)h * DK;
-    const E* kb = a.k + tok0 * H * DK + (size_t)h * DK;
     const size_t ldk = (size_t)H * DK;
     const int nvalid = min(BLK, T - n * BLK);
+    constexpr int PK = RP<E, DK>, KK = DK / 32, NV = DV / 16;
+    static_assert(NV % 2 == 0, "value slices are processed in pairs");
+    __shared__ __align__(16) E Qs[BLK * PK], Ks[BLK * PK];
+
+    const E* hT = a.hT + chunk * DK * DV;
+    const E* UT = a.UT + chunk * BLK * DV;
+    Frag<E> fh[2][KK], fu[2][2];
+    auto load_slice = [&](int buf, int vb) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) fh[buf][kk] = ldfragT(hT, vb * KK + kk, l);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fu[buf][j] = ldfragT(UT, 2 * vb + j, l);
+    };
+    const auto qx = load_rows<E, BLK, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+    const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+    load_slice(0, 0);
+    store_rows<E, BLK, DK, PK>(qx, Qs);
+    store_rows<E, BLK, DK, PK>(kx, Ks);
+    __syncthreads();
 
     // Q as B operand: Bt[t][d] = Q[t][d]
-    Frag<E> fq[DK / 32];
-#pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) fq[kk] = ldfrag_row(qb, 16 * w + r, nvalid, ldk, 32 * kk + 4 * g);
-
     const int t_lane = 16 * w + r;  // this lane's token (column of every O^T / P^T tile)
+    Frag<E> fq[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) fq[kk] = ldfrag(Qs + t_lane * PK + 32 * kk + 4 * g);
     const float gt = gam[t_lane];
     // P^T[s][t] = (k_s . q_t) exp(gamma_t - gamma_s) for s <= t
     f32x4 P[4];
@@ -513,14 +531,11 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
         f32x4 acc = zero4();
         if (sb <= w) {
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                Frag<E> fk = ldfrag_row(kb, 16 * sb + r, nvalid, ldk, 32 * kk + 4 * g);
-                mma(acc, fk, fq[kk]);
-            }
+            for (int kk = 0; kk < KK; ++kk) mma(acc, ldfrag(Ks + (16 * sb + r) * PK + 32 * kk + 4 * g), fq[kk]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int s = 16 * sb + 4 * g + i;
-                acc[i] = (s <= t_lane) ? acc[i] * __expf(gt - gam[s]) : 0.f;
+                const int s2 = 16 * sb + 4 * g + i;
+                acc[i] = (s2 <= t_lane) ? acc[i] * __expf(gt - gam[s2]) : 0.f;
             }
         }
         P[sb] = acc;
@@ -529,25 +544,23 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
     fp[0] = frag_from_acc<E>(P[0], P[1]);
     fp[1] = frag_from_acc<E>(P[2], P[3]);
     const float Gt = __expf(gt);
-    const E* hT = a.hT + chunk * DK * DV;
-    const E* UT = a.UT + chunk * BLK * DV;
     E* ob = a.o + tok0 * H * DV + (size_t)h * DV;
-    for (int vb = 0; vb < DV / 16; ++vb) {
+    auto compute_slice = [&](int buf, int vb) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            Frag<E> fh = ldfragT(hT, vb * (DK / 32) + kk, l);
-            mma(acc, fh, fq[kk]);
-        }
+        for (int kk = 0; kk < KK; ++kk) mma(acc, fh[buf][kk], fq[kk]);
         acc = acc * Gt;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (2 * j <= w) {
-                Frag<E> fu = ldfragT(UT, 2 * vb + j, l);
-                mma(acc, fu, fp[j]);
-            }
-        }
+        for (int j = 0; j < 2; ++j)
+            if (2 * j <= w) mma(acc, fu[buf][j], fp[j]);
         if (t_lane < nvalid) st4(ob + (size_t)t_lane * H * DV + 16 * vb + 4 * g, acc);
+    };
+#pragma unroll
+    for (int vb = 0; vb < NV; vb += 2) {
+        load_slice(1, vb + 1);
+        compute_slice(0, vb);
+        if (vb + 2 < NV) load_slice(0, vb + 2);
+        compute_slice(1, vb + 1);
     }
 }
 
