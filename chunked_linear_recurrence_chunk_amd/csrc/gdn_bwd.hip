@@ -339,13 +339,17 @@ __global__ __launch_bounds__(256) void gdn_scan_bwd_kernel(GdnScanBwdArgs<E> a) 
 // ---------------------------------------------------------------------------
 // intra: one work-group (4 waves) per (block, head, batch).  Wave w owns the
 // 16 tokens 16w..16w+15 of the block, both as "t" (rows of dQ) and as "s"
-// (rows of dK, dV, dbeta).
+// (rows of dK, dV, dbeta).  K, Q, dO and V are staged row-major, U^T and dU^T
+// as [v][t]; every global load of a phase is issued at once, and products
+// that contract over the other index read the tiles transposed (ldfrag_tr).
+// The tiled h_n / dh_n fragments are read from global memory one 16-row
+// block ahead of their use.
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV> struct IntraLds {
-    static constexpr int PDK = DK + 8, PDV = DV + 8;
+    static constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
     // persistent
-    static constexpr size_t o_Kt = 0;                                  // E[DK][PT]     K^T
-    static constexpr size_t o_KKG = o_Kt + sizeof(E) * DK * PT;        // f32[64][AP]   (K K^T * G), strictly lower
+    static constexpr size_t o_Ks = 0;                                  // E[64][PK]     K
+    static constexpr size_t o_KKG = o_Ks + sizeof(E) * BLK * PK;       // f32[64][AP]   (K K^T * G), strictly lower
     static constexpr size_t o_TT = o_KKG + 4 * BLK * AP;               // E[64][PT]     TT[s][t] = T[t][s]
     static constexpr size_t o_Tr = o_TT + sizeof(E) * BLK * PT;        // E[64][PT]     T row-major
     static constexpr size_t o_E = o_Tr + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms)
@@ -353,15 +357,16 @@ template <typename E, int DK, int DV> struct IntraLds {
     // phase 0: Am f32[64][AP], Td f32[4][16][16]
     static constexpr size_t p0_Am = o_U, p0_Td = p0_Am + 4 * BLK * AP;
     static constexpr size_t p0_end = p0_Td + 4 * 4 * 256;
-    // phase A: Qt E[DK][PT], U E[64][PDV]
-    static constexpr size_t pA_Qt = o_U, pA_U = pA_Qt + sizeof(E) * DK * PT;
-    static constexpr size_t pA_end = pA_U + sizeof(E) * BLK * PDV;
-    // phase B: dU E[64][PDV], dW E[64][PDK], dWT E[DK][PT], dTT E[64][PT], Ms E[64][PT]
-    static constexpr size_t pB_dU = o_U, pB_dW = pB_dU + sizeof(E) * BLK * PDV;
-    static constexpr size_t pB_dWT = pB_dW + sizeof(E) * BLK * PDK;
-    static constexpr size_t pB_dTT = pB_dWT + sizeof(E) * DK * PT;
+    // phase A: Qs E[64][PK], dOs E[64][PV], UTs E[DV][PT]
+    static constexpr size_t pA_Q = o_U, pA_dO = pA_Q + sizeof(E) * BLK * PK;
+    static constexpr size_t pA_UT = pA_dO + sizeof(E) * BLK * PV;
+    static constexpr size_t pA_end = pA_UT + sizeof(E) * DV * PT;
+    // phase B: dUTs E[DV][PT], dWs E[64][PK], dTT E[64][PT], Ms E[64][PT], Vs E[64][PV]
+    static constexpr size_t pB_dUT = o_U, pB_dW = pB_dUT + sizeof(E) * DV * PT;
+    static constexpr size_t pB_dTT = pB_dW + sizeof(E) * BLK * PK;
     static constexpr size_t pB_Ms = pB_dTT + sizeof(E) * BLK * PT;
-    static constexpr size_t pB_end = pB_Ms + sizeof(E) * BLK * PT;
+    static constexpr size_t pB_V = pB_Ms + sizeof(E) * BLK * PT;
+    static constexpr size_t pB_end = pB_V + sizeof(E) * BLK * PV;
     static constexpr size_t m01 = p0_end > pA_end ? p0_end : pA_end;
     static constexpr size_t total = m01 > pB_end ? m01 : pB_end;
 };
@@ -369,10 +374,10 @@ template <typename E, int DK, int DV> struct IntraLds {
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     using Lay = IntraLds<E, DK, DV>;
-    constexpr int PDK = Lay::PDK, PDV = Lay::PDV;
+    constexpr int PK = Lay::PK, PV = Lay::PV, KK = DK / 32, KV = DV / 32, ND = DK / 16;
     static_assert(Lay::total <= 150 * 1024, "LDS budget");
     __shared__ __align__(16) char lds[Lay::total];
-    E* Kt = (E*)(lds + Lay::o_Kt);
+    E* Ks = (E*)(lds + Lay::o_Ks);
     float* KKG = (float*)(lds + Lay::o_KKG);
     E* TT = (E*)(lds + Lay::o_TT);
     E* Tr = (E*)(lds + Lay::o_Tr);
@@ -396,23 +401,28 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     const E* UT = a.UT + chunk * BLK * DV;
     const E* dUT = a.dUT + chunk * BLK * DV;
 
-    // ---------------- phase 0: gates, K^T, Q^T, U, Gram, T -----------------
+    // ---------------- phase 0: gates, K, Gram, T -----------------------------
+    const auto kx = load_rows<E, BLK, DK>(kb, ldk, nvalid);
+    const auto qx = load_rows<E, BLK, DK>(qb, ldk, nvalid);
+    const auto ox = load_rows<E, BLK, DV>(dob, ldv, nvalid);
+    const auto ux = load_tiled<E, DV, BLK>(UT);
     if (tid < BLK) {
         s_gam[tid] = a.gam[chunk * BLK + tid];
         s_bet[tid] = tid < nvalid ? to_f(a.beta[(tok0 + tid) * H + h]) : 0.f;
     }
-    stage_transposed<E, DK>(kb, ldk, Kt, nvalid);
+    store_rows<E, BLK, DK, PK>(kx, Ks);
     __syncthreads();
     {
         float* Am = (float*)(lds + Lay::p0_Am);
-        Frag<E> fa[DK / 32];
+        Frag<E> fa[KK];
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) fa[kk] = ldfrag_row(kb, 16 * w + r, nvalid, ldk, 32 * kk + 4 * g);
+        for (int kk = 0; kk < KK; ++kk) fa[kk] = ldfrag(Ks + (16 * w + r) * PK + 32 * kk + 4 * g);
+#pragma unroll
         for (int j = 0; j < 4; ++j) {
             f32x4 acc = zero4();
             if (j <= w) {
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) mma(acc, fa[kk], ldfrag_row(kb, 16 * j + r, nvalid, ldk, 32 * kk + 4 * g));
+                for (int kk = 0; kk < KK; ++kk) mma(acc, fa[kk], ldfrag(Ks + (16 * j + r) * PK + 32 * kk + 4 * g));
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -436,20 +446,25 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         __syncthreads();
     }
     // ---------------- phase A: dQ, and the output / state-update parts of dK ---
-    E* Qt = (E*)(lds + Lay::pA_Qt);
-    E* Us = (E*)(lds + Lay::pA_U);
-    stage_transposed<E, DK>(qb, ldk, Qt, nvalid);
-    stage_T_tiled<E, DV, BLK, PDV>(UT, Us);  // Us[t][v] = U[t][v]
+    E* Qs = (E*)(lds + Lay::pA_Q);
+    E* dOs = (E*)(lds + Lay::pA_dO);
+    E* UTs = (E*)(lds + Lay::pA_UT);
+    // phase B operands: in flight during phase A
+    const auto vx = load_rows<E, BLK, DV>(vbase, ldv, nvalid);
+    const auto dux = load_tiled<E, DV, BLK>(dUT);
+    store_rows<E, BLK, DK, PK>(qx, Qs);
+    store_rows<E, BLK, DV, PV>(ox, dOs);
+    store_untiled<E, DV, BLK, PT>(ux, UTs);
     __syncthreads();
 
     const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
     const float gam_tw = s_gam[tw];
     const float gC = s_gam[BLK - 1];
-    Frag<E> fdo[DV / 32], fU[DV / 32];
+    Frag<E> fdo[KV], fU[KV];
 #pragma unroll
-    for (int kk = 0; kk < DV / 32; ++kk) {
-        fdo[kk] = ldfrag_row(dob, tw, nvalid, ldv, 32 * kk + 4 * g);  // Bt = dO[t][v], rows of block w
-        fU[kk] = ldfrag(Us + tw * PDV + 32 * kk + 4 * g);               // Bt = U[s][v], rows of block w
+    for (int kk = 0; kk < KV; ++kk) {
+        fdo[kk] = ldfrag(dOs + tw * PV + 32 * kk + 4 * g);    // Bt = dO[t][v], rows of block w
+        fU[kk] = ldfrag_tr(UTs, PT, 32 * kk, 16 * w, l);     // Bt = U[s][v], rows of block w
     }
     // dPm^T[sb][w]: rows s, cols t = tw
     f32x4 dPT[4];
@@ -458,7 +473,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         f32x4 acc = zero4();
         if (sb <= w) {
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfrag(Us + (16 * sb + r) * PDV + 32 * kk + 4 * g), fdo[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag_tr(UTs, PT, 32 * kk, 16 * sb, l), fdo[kk]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = 16 * sb + 4 * g + i;
@@ -470,15 +485,15 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     // Gate cross terms of the output path: E[t][s] = dP[t][s] P[t][s]
     // = dPm[t][s] (q_t . k_s)  (s <= t), with (Q K^T)^T tiles rows s, col t = tw.
     {
-        Frag<E> fq[DK / 32];
+        Frag<E> fq[KK];
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) fq[kk] = ldfrag_row(qb, tw, nvalid, ldk, 32 * kk + 4 * g);
+        for (int kk = 0; kk < KK; ++kk) fq[kk] = ldfrag(Qs + tw * PK + 32 * kk + 4 * g);
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             f32x4 qk = zero4();
             if (sb <= w) {
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) mma(qk, ldfrag_row(kb, 16 * sb + r, nvalid, ldk, 32 * kk + 4 * g), fq[kk]);
+                for (int kk = 0; kk < KK; ++kk) mma(qk, ldfrag(Ks + (16 * sb + r) * PK + 32 * kk + 4 * g), fq[kk]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) Eb[tw * 65 + 16 * sb + 4 * g + i] = dPT[sb][i] * qk[i];
@@ -491,19 +506,23 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         fpt[1] = frag_from_acc<E>(dPT[2], dPT[3]);
         const float Gt = __expf(gam_tw);
         float qdq = 0.f;
-        #pragma unroll
-        for (int db = 0; db < DK / 16; ++db) {
+        Frag<E> fh[2][KV];
+#pragma unroll
+        for (int kk = 0; kk < KV; ++kk) fh[0][kk] = ldfragT(S0, kk, l);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            if (db + 1 < ND) {
+#pragma unroll
+                for (int kk = 0; kk < KV; ++kk) fh[(db + 1) & 1][kk] = ldfragT(S0, (db + 1) * KV + kk, l);
+            }
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfragT(S0, db * (DV / 32) + kk, l), fdo[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma(acc, fh[db & 1][kk], fdo[kk]);
             acc = acc * Gt;
-            f32x4 qv = zero4();
-            if (tw < nvalid) {
-                qv = ld4(qb + (size_t)tw * ldk + 16 * db + 4 * g);
-                qdq += qv[0] * acc[0] + qv[1] * acc[1] + qv[2] * acc[2] + qv[3] * acc[3];
-            }
+            const f32x4 qv = ld4(Qs + tw * PK + 16 * db + 4 * g);
+            qdq += qv[0] * acc[0] + qv[1] * acc[1] + qv[2] * acc[2] + qv[3] * acc[3];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag(Kt + (16 * db + r) * PT + 32 * j + 4 * g), fpt[j]);
+            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fpt[j]);
             if (tw < nvalid) st4(a.dq + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, acc);
         }
         qdq += __shfl_xor(qdq, 16, 64);
@@ -517,8 +536,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         f32x4 acc = zero4();
         if (tb >= w) {
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk)
-                mma(acc, ldfrag_row(dob, 16 * tb + r, nvalid, ldv, 32 * kk + 4 * g), fU[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag(dOs + (16 * tb + r) * PV + 32 * kk + 4 * g), fU[kk]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * g + i;
@@ -528,85 +546,109 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         dP[tb] = acc;
     }
     // dK^T accumulators: rows d, cols s = tw
-    f32x4 dKT[DK / 16];
+    f32x4 dKT[ND];
     {
         Frag<E> fpm[2];
         fpm[0] = frag_from_acc<E>(dP[0], dP[1]);
         fpm[1] = frag_from_acc<E>(dP[2], dP[3]);
         const float ek = __expf(gC - gam_tw);
         float kdk = 0.f;
-        #pragma unroll
-        for (int db = 0; db < DK / 16; ++db) {
+        Frag<E> fd[2][KV];
+#pragma unroll
+        for (int kk = 0; kk < KV; ++kk) fd[0][kk] = ldfragT(dS1, kk, l);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            if (db + 1 < ND) {
+#pragma unroll
+                for (int kk = 0; kk < KV; ++kk) fd[(db + 1) & 1][kk] = ldfragT(dS1, (db + 1) * KV + kk, l);
+            }
             f32x4 acc = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag(Qt + (16 * db + r) * PT + 32 * j + 4 * g), fpm[j]);
+            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(Qs, PK, 32 * j, 16 * db, l), fpm[j]);
             f32x4 accb = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) mma(accb, ldfragT(dS1, db * (DV / 32) + kk, l), fU[kk]);
-            if (tw < nvalid) {
-                const f32x4 kv = ld4(kb + (size_t)tw * ldk + 16 * db + 4 * g);
-                kdk += kv[0] * accb[0] + kv[1] * accb[1] + kv[2] * accb[2] + kv[3] * accb[3];
-            }
+            for (int kk = 0; kk < KV; ++kk) mma(accb, fd[db & 1][kk], fU[kk]);
+            const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
+            kdk += kv[0] * accb[0] + kv[1] * accb[1] + kv[2] * accb[2] + kv[3] * accb[3];
             dKT[db] = acc + accb * ek;
         }
         kdk += __shfl_xor(kdk, 16, 64);
         kdk += __shfl_xor(kdk, 32, 64);
         if (g == 0) s_kdk[tw] = kdk * ek;
     }
-    // <h_n, dh_n>
+    // <h_n, dh_n> (both tiled the same way)
     {
+        constexpr int VEC = 16 / sizeof(E), NU = DK * DV / VEC, NIT = (NU + 255) / 256;
+        uint4 xs[NIT], ys[NIT];
+#pragma unroll
+        for (int j = 0; j < NIT; ++j) {
+            const int u = tid + 256 * j;
+            xs[j] = u < NU ? *(const uint4*)(S0 + (size_t)u * VEC) : uint4{0u, 0u, 0u, 0u};
+            ys[j] = u < NU ? *(const uint4*)(dS1 + (size_t)u * VEC) : uint4{0u, 0u, 0u, 0u};
+        }
         float part = 0.f;
-        constexpr int VEC = 16 / sizeof(E);
-        for (int idx = tid; idx < DK * DV / VEC; idx += 256) {
+#pragma unroll
+        for (int j = 0; j < NIT; ++j) {
             E x[VEC], y[VEC];
-            *(uint4*)x = *(const uint4*)(S0 + (size_t)idx * VEC);
-            *(uint4*)y = *(const uint4*)(dS1 + (size_t)idx * VEC);
+            *(uint4*)x = xs[j];
+            *(uint4*)y = ys[j];
 #pragma unroll
             for (int i = 0; i < VEC; ++i) part += to_f(x[i]) * to_f(y[i]);
         }
         part = wave_sum(part);
         if (l == 0) s_red[w] = part;
     }
-    __syncthreads();  // phase A done: Qt, Us free
+    __syncthreads();  // phase A done: Qs, dOs, UTs free
 
     // ---------------- phase B: WY-transform adjoints ------------------------
-    E* dUs = (E*)(lds + Lay::pB_dU);
+    E* dUTs = (E*)(lds + Lay::pB_dUT);
     E* dWs = (E*)(lds + Lay::pB_dW);
-    E* dWT = (E*)(lds + Lay::pB_dWT);
     E* dTT = (E*)(lds + Lay::pB_dTT);
     E* Ms = (E*)(lds + Lay::pB_Ms);
-    stage_T_tiled<E, DV, BLK, PDV>(dUT, dUs);  // dUs[t][v]
+    E* Vs = (E*)(lds + Lay::pB_V);
+    store_untiled<E, DV, BLK, PT>(dux, dUTs);
+    store_rows<E, BLK, DV, PV>(vx, Vs);
     __syncthreads();
-    // dW^T[db][w] = -(S0 dU^T): rows d, cols t = tw
+    // dW^T[db][w] = -(S0 dU^T): rows d, cols t = tw;  stored as dW[t][d]
     {
-        Frag<E> fdu[DV / 32];
+        Frag<E> fdu[KV];
 #pragma unroll
-        for (int kk = 0; kk < DV / 32; ++kk) fdu[kk] = ldfrag(dUs + tw * PDV + 32 * kk + 4 * g);
-        #pragma unroll
-        for (int db = 0; db < DK / 16; ++db) {
+        for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr(dUTs, PT, 32 * kk, 16 * w, l);
+        Frag<E> fh[2][KV];
+#pragma unroll
+        for (int kk = 0; kk < KV; ++kk) fh[0][kk] = ldfragT(S0, kk, l);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            if (db + 1 < ND) {
+#pragma unroll
+                for (int kk = 0; kk < KV; ++kk) fh[(db + 1) & 1][kk] = ldfragT(S0, (db + 1) * KV + kk, l);
+            }
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfragT(S0, db * (DV / 32) + kk, l), fdu[kk]);
-            acc = -acc;
-            st4(dWs + tw * PDK + 16 * db + 4 * g, acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dWT[(16 * db + 4 * g + i) * PT + tw] = from_f<E>(acc[i]);
+            for (int kk = 0; kk < KV; ++kk) mma(acc, fh[db & 1][kk], fdu[kk]);
+            st4(dWs + tw * PK + 16 * db + 4 * g, -acc);
         }
     }
     __syncthreads();
     // dT[w][sb] = beta_s (dU V^T) + beta_s Gam_s (dW K^T): rows t, cols s;  stored as dT^T[s][t]
-    for (int sb = 0; sb < 4; ++sb) {
-        f32x4 a1 = zero4(), a2 = zero4();
+    {
+        Frag<E> fdu[KV], fdw[KK];
 #pragma unroll
-        for (int kk = 0; kk < DV / 32; ++kk)
-            mma(a1, ldfrag(dUs + (16 * w + r) * PDV + 32 * kk + 4 * g), ldfrag_row(vbase, 16 * sb + r, nvalid, ldv, 32 * kk + 4 * g));
+        for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr(dUTs, PT, 32 * kk, 16 * w, l);
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk)
-            mma(a2, ldfrag(dWs + (16 * w + r) * PDK + 32 * kk + 4 * g), ldfrag_row(kb, 16 * sb + r, nvalid, ldk, 32 * kk + 4 * g));
-        const int s = 16 * sb + r;
-        const float bs = s_bet[s];
-        const f32x4 dt = a1 * bs + a2 * (bs * __expf(s_gam[s]));
-        st4(dTT + s * PT + 16 * w + 4 * g, dt);
+        for (int kk = 0; kk < KK; ++kk) fdw[kk] = ldfrag(dWs + (16 * w + r) * PK + 32 * kk + 4 * g);
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            f32x4 a1 = zero4(), a2 = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KV; ++kk) mma(a1, fdu[kk], ldfrag(Vs + (16 * sb + r) * PV + 32 * kk + 4 * g));
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) mma(a2, fdw[kk], ldfrag(Ks + (16 * sb + r) * PK + 32 * kk + 4 * g));
+            const int s = 16 * sb + r;
+            const float bs = s_bet[s];
+            const f32x4 dt = a1 * bs + a2 * (bs * __expf(s_gam[s]));
+            st4(dTT + s * PT + 16 * w + 4 * g, dt);
+        }
     }
     __syncthreads();
     // X^T[sb][w] = dT^T T  (rows s, cols r' = tw);  dA[w][cb] = -X T^T (rows r', cols c)
@@ -624,6 +666,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         fx[0] = frag_from_acc<E>(XT[0], XT[1]);
         fx[1] = frag_from_acc<E>(XT[2], XT[3]);
         float gram[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             f32x4 acc = zero4();
             if (cb <= w) {
@@ -656,39 +699,33 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     // dV^T[vb][w] = beta_s (dU^T T): rows v, cols s = tw;   dbeta V-term
     const float bet_tw = s_bet[tw];
     float dbv = 0.f;
-    #pragma unroll
+#pragma unroll
     for (int vb = 0; vb < DV / 16; ++vb) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            mma(acc, ldfragT(dUT, 2 * vb + j, l), ldfrag(TT + tw * PT + 32 * j + 4 * g));
-        if (tw < nvalid) {
-            const f32x4 vv = ld4(vbase + (size_t)tw * ldv + 16 * vb + 4 * g);
-            dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
-            st4(a.dv + (tok0 + tw) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc * bet_tw);
-        }
+            mma(acc, ldfrag(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
+        const f32x4 vv = ld4(Vs + tw * PV + 16 * vb + 4 * g);
+        dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
+        if (tw < nvalid) st4(a.dv + (tok0 + tw) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc * bet_tw);
     }
     dbv += __shfl_xor(dbv, 16, 64);
     dbv += __shfl_xor(dbv, 32, 64);
     // dK^T += beta_s Gam_s (dW^T T) + K^T Msym ;  dbeta K-term
     const float Gs = __expf(gam_tw);
     float dbk = 0.f;
-    #pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            mma(acc, ldfrag(dWT + (16 * db + r) * PT + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
+        for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(dWs, PK, 32 * j, 16 * db, l), ldfrag(TT + tw * PT + 32 * j + 4 * g));
         f32x4 accm = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            mma(accm, ldfrag(Kt + (16 * db + r) * PT + 32 * j + 4 * g), ldfrag(Ms + tw * PT + 32 * j + 4 * g));
-        if (tw < nvalid) {
-            const f32x4 kv = ld4(kb + (size_t)tw * ldk + 16 * db + 4 * g);
-            dbk += kv[0] * acc[0] + kv[1] * acc[1] + kv[2] * acc[2] + kv[3] * acc[3];
-            const f32x4 res = dKT[db] + acc * (bet_tw * Gs) + accm;
-            st4(a.dk + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, res);
-        }
+        for (int j = 0; j < 2; ++j) mma(accm, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), ldfrag(Ms + tw * PT + 32 * j + 4 * g));
+        const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
+        dbk += kv[0] * acc[0] + kv[1] * acc[1] + kv[2] * acc[2] + kv[3] * acc[3];
+        const f32x4 res = dKT[db] + acc * (bet_tw * Gs) + accm;
+        if (tw < nvalid) st4(a.dk + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, res);
     }
     dbk += __shfl_xor(dbk, 16, 64);
     dbk += __shfl_xor(dbk, 32, 64);
