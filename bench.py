@@ -62,6 +62,8 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
                           2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv),
     }
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
+    # one launch running the forward recompute and the reverse scan side by side
+    W["gdn_scan_pair"] = tuple(x + y for x, y in zip(W["gdn_scan_fwd"], W["gdn_scan_bwd"]))
     W["gla_scan_fwd_rec"] = W["gla_scan_fwd"]
     return W.get(name)
 

@@ -47,14 +47,16 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // p = (w % 8) + 8 * (w / (8 NV)), value slice vb = (w / 8) % NV.
 // Returns false for the padding groups of the last round (p >= BH).
 constexpr int NXCD = 8;
-__device__ __forceinline__ bool scan_coords(int NV, int BH, int H, int& b, int& h, int& vb) {
-    const int w = blockIdx.x;
+__device__ __forceinline__ bool scan_coords(int w, int NV, int BH, int H, int& b, int& h, int& vb) {
     const int p = (w % NXCD) + NXCD * (w / (NXCD * NV));
     vb = (w / NXCD) % NV;
     if (p >= BH) return false;
     b = p / H;
     h = p % H;
     return true;
+}
+__device__ __forceinline__ bool scan_coords(int NV, int BH, int H, int& b, int& h, int& vb) {
+    return scan_coords((int)blockIdx.x, NV, BH, H, b, h, vb);
 }
 inline unsigned scan_grid(int NV, int BH) { return (unsigned)(((BH + NXCD - 1) / NXCD) * NXCD * NV); }
 

@@ -267,23 +267,30 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 
     }
 }
 
+template <typename E, int DK> struct ScanBwdGeom {
+    static constexpr int NU = ScanBwdRing<E, DK>::NU;
+    static constexpr int SLOT = RingGeom<NU>::SLOT;
+    static constexpr int TILE = DK * 16 * (int)sizeof(E);
+    static constexpr int PF = (144 * 1024 - TILE) / SLOT;
+    static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
+    static constexpr int LDS = P * SLOT + TILE;
+};
+
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_scan_bwd_kernel(GdnScanBwdArgs<E> a) {
+__device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, int wgi, char* smem) {
     const int H = a.H, NC = a.NC;
     int b, h, vb;
-    if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
+    if (!scan_coords(wgi, DV / 16, a.BH, H, b, h, vb)) return;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
     constexpr int ND = DK / 16;
     using Rg = ScanBwdRing<E, DK>;
-    constexpr int NU = Rg::NU, UPF = Rg::UPF;
+    using SG = ScanBwdGeom<E, DK>;
+    constexpr int NU = Rg::NU, UPF = Rg::UPF, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
     using G = RingGeom<NU>;
-    constexpr int TILE = DK * 16 * (int)sizeof(E);
-    constexpr int PF = (144 * 1024 - TILE) / G::SLOT;
-    constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
-    __shared__ __align__(16) char ring[P * G::SLOT];
-    __shared__ __align__(16) E tile[TILE / sizeof(E)];
+    char* ring = smem;
+    E* tile = (E*)(smem + P * G::SLOT);
     const size_t bh = (size_t)b * H + h;
 
     // round m handles block NC - 1 - m
@@ -334,6 +341,17 @@ __global__ __launch_bounds__(256) void gdn_scan_bwd_kernel(GdnScanBwdArgs<E> a) 
     for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dSi[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = dS[db][i];
+}
+
+// The forward recompute (state entering every block) and the reverse scan are
+// independent given the prep outputs; one launch runs both, work-groups
+// [0, G) the former and [G, 2G) the latter, so together they fill the chip.
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_scan_pair_kernel(GdnScanArgs<E> fa, GdnScanBwdArgs<E> ba, int G) {
+    constexpr int LF = ScanFwdGeom<E, DK, DV, true>::LDS, LB = ScanBwdGeom<E, DK>::LDS;
+    __shared__ __align__(16) char smem[LF > LB ? LF : LB];
+    if ((int)blockIdx.x < G) gdn_scan_fwd_body<E, DK, DV, true>(fa, blockIdx.x, smem);
+    else gdn_scan_bwd_body<E, DK, DV>(ba, blockIdx.x - G, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -781,10 +799,10 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     launch("gdn_prep2", gdn_prep2_kernel<E, DK, DV>, gblk, dim3(256), st, p2);
     GdnScanArgs<E> sa{ws.gam, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, (E*)ws.UT, L.H, L.NC, L.B * L.H};
-    launch("gdn_scan_fwd_rec", gdn_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(256), st, sa);
     GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
                          L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC, L.B * L.H};
-    launch("gdn_scan_bwd", gdn_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(256), st, sb);
+    const int G = (int)scan_grid(DV / 16, L.B * L.H);
+    launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV>, dim3(2 * G), dim3(256), st, sa, sb, G);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const E*)ws.dUT,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};

@@ -413,23 +413,32 @@ __device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK>& o, const c
 // the next blocks into the LDS ring (clr_ring.h).  All operands are tiled, so
 // ring unit u of a block is the contiguous 1-KB run u of
 // [W | Kh^T | Ut^T fragments (vb, 0..1)].
+template <typename E, int DK, int DV, bool HNAT> struct ScanFwdGeom {
+    static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 1-KB units per fragment
+    static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF;
+    static constexpr int NU = NWU + NKU + 2 * UPF;
+    static constexpr int SLOT = RingGeom<NU>::SLOT;
+    static constexpr int TILE = HNAT ? DK * 16 * (int)sizeof(E) : 16;
+    static constexpr int PF = (144 * 1024 - TILE) / SLOT;
+    static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
+    static constexpr int LDS = P * SLOT + TILE;  // ring, then the state-store tile
+};
+
+// Scan body for work-group `wgi` of the scan grid; `smem` holds
+// ScanFwdGeom::LDS bytes (16-byte aligned).
 template <typename E, int DK, int DV, bool HNAT>
-__global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
+__device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int wgi, char* smem) {
     const int H = a.H, NC = a.NC;
     int b, h, vb;
-    if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
+    if (!scan_coords(wgi, DV / 16, a.BH, H, b, h, vb)) return;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
-    constexpr int ND = DK / 16;
-    constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 1-KB units per fragment
-    constexpr int KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF, NU = NWU + NKU + 2 * UPF;
+    using SG = ScanFwdGeom<E, DK, DV, HNAT>;
+    constexpr int ND = SG::ND, UPF = SG::UPF, NWU = SG::NWU, NKU = SG::NKU, NU = SG::NU, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
     using G = RingGeom<NU>;
-    constexpr int TILE = HNAT ? DK * 16 * (int)sizeof(E) : 16;
-    constexpr int PF = (144 * 1024 - TILE) / G::SLOT;
-    constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
-    __shared__ __align__(16) char ring[P * G::SLOT];
-    __shared__ __align__(16) E tile[TILE / sizeof(E)];
+    char* ring = smem;
+    E* tile = (E*)(smem + P * G::SLOT);
     const size_t bh = (size_t)b * H + h;
 
     if (w > 0) {  // producers
@@ -479,6 +488,12 @@ __global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) So[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = S[db][i];
     }
+}
+
+template <typename E, int DK, int DV, bool HNAT>
+__global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
+    __shared__ __align__(16) char smem[ScanFwdGeom<E, DK, DV, HNAT>::LDS];
+    gdn_scan_fwd_body<E, DK, DV, HNAT>(a, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
