@@ -242,7 +242,8 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
             mma(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g));
         st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
     }
-    // Ut[t][v] = sum_s T2[t][s] V[s][v]  -> stored as Ut^T[v][t] (tiled)
+    // Ut[t][v] = sum_s T2[t][s] V[s][v]  -> stored negated as -Ut^T[v][t] (tiled),
+    // so that the scan forms -U = W S - Ut by accumulating onto it
     E* Uout = a.UtT + chunk * BLK * DV;
 #pragma unroll
     for (int tile = w; tile < 4 * (DV / 16); tile += 4) {
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             mma(acc, ldfrag(T2 + (16 * tb + r) * PT + 32 * j + 4 * g), ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
-        st4(Uout + toff<E>(16 * vb + r, 16 * tb + 4 * g, BLK), acc);
+        st4(Uout + toff<E>(16 * vb + r, 16 * tb + 4 * g, BLK), -acc);
     }
     // Kh^T[d][t] = exp(gamma_C - gamma_t) K[t][d] (tiled): its fragment (db, j)
     // is the B fragment of Kh over tokens 32j.., columns 16db..
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
 template <typename E, int DK> struct ScanFwdOps {
     Frag<E> w[4][DK / 32];    // W rows (A: m = t, k = d)
     Frag<E> kh[DK / 16][2];   // Kh^T rows (A: m = d, k = t)
-    Frag<E> ut[2];            // Ut^T[v0 + r][token pair-tiles 2j, 2j+1] (accumulator layout)
+    Frag<E> ut[2];            // -Ut^T[v0 + r][token pair-tiles 2j, 2j+1] (accumulator layout)
     float gC;                 // gamma at the last token of the block
 };
 
@@ -335,9 +336,13 @@ __device__ __forceinline__ void store_state_tiled(E* h, const f32x4 (&S)[DK / 16
 // One block of the recurrence.  HNAT selects the layout of the saved states:
 // false -> tiled h^T[v][d] (read by the forward's out kernel), true -> tiled
 // h[d][v] (read by the backward).
-template <typename E, int DK, int DV, bool HNAT>
-__device__ __forceinline__ void scan_fwd_step(const ScanFwdOps<E, DK>& o, f32x4 (&S)[DK / 16],
-                                              const GdnScanArgs<E>& a, size_t chunk, int vb, int l, E* tile) {
+template <typename E, int DK, int NU>
+__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK>& o, const char* slot, int l);
+
+template <typename E, int DK, int DV, bool HNAT, int NU>
+__device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[DK / 16],
+                                              const GdnScanArgs<E>& a, size_t chunk, int vb, int l, E* tile,
+                                              const char* slot) {
     constexpr int ND = DK / 16, KK = DK / 32;
     Frag<E> fs[KK];
 #pragma unroll
@@ -352,26 +357,29 @@ __device__ __forceinline__ void scan_fwd_step(const ScanFwdOps<E, DK>& o, f32x4 
             for (int kk = 0; kk < KK; ++kk) st8T(hT, vb * KK + kk, l, S[2 * kk], S[2 * kk + 1]);
         }
     }
-    // U = Ut - W S    (tiles: rows t = 16tb + 4g + i, col v0 + r)
+    // -U = W S - Ut, accumulated onto the stored -Ut  (tiles: rows t = 16tb + 4g + i, col v0 + r)
     f32x4 U[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) mma(acc, o.w[tb][kk], fs[kk]);
-        U[tb] = acc;
-    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const Frag<E>& f = o.ut[j];
         if constexpr (sizeof(E) == 2) {
-            U[2 * j] = f32x4{(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]} - U[2 * j];
-            U[2 * j + 1] = f32x4{(float)f.v[4], (float)f.v[5], (float)f.v[6], (float)f.v[7]} - U[2 * j + 1];
+            U[2 * j] = f32x4{(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]};
+            U[2 * j + 1] = f32x4{(float)f.v[4], (float)f.v[5], (float)f.v[6], (float)f.v[7]};
         } else {
-            U[2 * j] = f.lo - U[2 * j];
-            U[2 * j + 1] = f.hi - U[2 * j + 1];
+            U[2 * j] = f.lo;
+            U[2 * j + 1] = f.hi;
         }
     }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) mma(U[tb], o.w[tb][kk], fs[kk]);
+    }
+    // the Kh^T reads go out while the products above run
+    asm volatile("" ::: "memory");
+    scan_fwd_from_ring_kh<E, DK, NU>(o, slot, l);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) U[tb] = -U[tb];
     // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles
     Frag<E> fu[2];
     fu[0] = frag_from_acc<E>(U[0], U[1]);
@@ -401,12 +409,17 @@ __device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK>& o, const c
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) o.w[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
 #pragma unroll
+    for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, NWF + NKF + j, l, (E*)nullptr);
+    o.gC = ring_small<NU>(slot, BLK - 1);
+}
+// Kh^T operands of a block (read after the W S products have been issued).
+template <typename E, int DK, int NU>
+__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK>& o, const char* slot, int l) {
+    constexpr int KK = DK / 32, NWF = 4 * KK;
+#pragma unroll
     for (int db = 0; db < DK / 16; ++db)
 #pragma unroll
         for (int j = 0; j < 2; ++j) o.kh[db][j] = ring_frag(slot, NWF + 2 * db + j, l, (E*)nullptr);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, NWF + NKF + j, l, (E*)nullptr);
-    o.gC = ring_small<NU>(slot, BLK - 1);
 }
 
 // Work-group: wave 0 runs the recurrence, waves 1..3 stream the operands of
@@ -477,8 +490,9 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
     ring_barrier();
     for (int n = 0; n < NC; ++n) {
         ScanFwdOps<E, DK> o;
-        scan_fwd_from_ring<E, DK, NU>(o, ring + (n % P) * G::SLOT, l);
-        scan_fwd_step<E, DK, DV, HNAT>(o, S, a, bh * NC + n, vb, l, tile);
+        const char* slot = ring + (n % P) * G::SLOT;
+        scan_fwd_from_ring<E, DK, NU>(o, slot, l);
+        scan_fwd_step<E, DK, DV, HNAT, NU>(o, S, a, bh * NC + n, vb, l, tile, slot);
         ring_barrier();
     }
     if (a.S_out) {
