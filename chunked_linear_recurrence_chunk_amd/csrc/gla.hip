@@ -62,8 +62,7 @@ template <typename E> struct GlaScanBwdArgs {
     int T, H, NC, BH;
 };
 template <typename E> struct GlaIntraArgs {
-    const E *q, *k, *v, *dO;
-    const float* bcum;
+    const E *q, *k, *v, *dO, *g;
     const E *h, *dh, *dVs;
     E *dq, *dk, *dv, *dg;
     int T, H, NC;
@@ -228,10 +227,10 @@ __device__ __forceinline__ void gla_scan_step(const GlaScanOps<E, DK>& o, f32x4 
     if (a.hT) {
         E* hT = a.hT + chunk * DK * DV;
         if constexpr (HNAT) {
-            store_state_kmajor<E, DK, DV>(hT, S, tile, v0, r, g);
+            store_state_tiled<E, DK, DV>(hT, S, tile, v0, 16 * g + r);
         } else {
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) st8P(hT + (size_t)(v0 + r) * DK + 32 * kk + 8 * g, S[2 * kk], S[2 * kk + 1]);
+            for (int kk = 0; kk < DK / 32; ++kk) st8T(hT, (v0 / 16) * (DK / 32) + kk, 16 * g + r, S[2 * kk], S[2 * kk + 1]);
         }
     }
 #pragma unroll
@@ -344,7 +343,7 @@ __global__ __launch_bounds__(256) void gla_out_kernel(GlaOutArgs<E> a) {
     for (int vb = 0; vb < DV / 16; ++vb) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, ldfragP(hT + (size_t)(16 * vb + r) * DK + 32 * kk + 8 * g), qi[kk]);
+        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, ldfragT(hT, vb * (DK / 32) + kk, l), qi[kk]);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             if (2 * j <= R) mma(acc, ldfrag(Vt + (16 * vb + r) * PT + 32 * j + 4 * g), fp[j]);
@@ -388,7 +387,7 @@ __device__ __forceinline__ void gla_dscan_load(GlaScanBwdOps<E, DK>& o, const Gl
 template <typename E, int DK, int DV>
 __device__ __forceinline__ void gla_dscan_step(const GlaScanBwdOps<E, DK>& o, f32x4 (&dS)[DK / 16],
                                                const GlaScanBwdArgs<E>& a, size_t chunk, int v0, int r, int g, E* tile) {
-    store_state_kmajor<E, DK, DV>(a.dh + chunk * DK * DV, dS, tile, v0, r, g);
+    store_state_tiled<E, DK, DV>(a.dh + chunk * DK * DV, dS, tile, v0, 16 * g + r);
     Frag<E> fs[DK / 32];
 #pragma unroll
     for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
@@ -447,12 +446,102 @@ __global__ __launch_bounds__(64) void gla_scan_bwd_kernel(GlaScanBwdArgs<E> a) {
 }
 
 // ---------------------------------------------------------------------------
+// Block gate cumsum b[t][d] = sum_{s <= t} g[s][d] (tokens past the end of
+// the sequence contribute 0), from a row-major g tile in LDS (pitch PG) into
+// fp32 LDS (pitch PB).  One thread per channel, tokens in order, so every
+// kernel that forms b gets bit-identical values.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int PG, int PB>
+__device__ __forceinline__ void gate_cumsum(const E* gs, float* bs, int nvalid) {
+    const int d = threadIdx.x;
+    if (d < DK) {
+        float run = 0.f;
+#pragma unroll 16
+        for (int t = 0; t < BLK; ++t) {
+            run += t < nvalid ? to_f(gs[t * PG + d]) : 0.f;
+            bs[t * PB + d] = run;
+        }
+    }
+}
+
+// A fragment of row `row` of a row-major LDS tile X (k = column c = col +
+// kmap(g, i)), element c scaled by exp(sgn * (brow[c] - ref[c])).
+template <typename E>
+__device__ __forceinline__ Frag<E> frag_row_decay(const E* X, int PX, int row, int col, const float* brow,
+                                                  const float* ref, float sgn) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const int c0 = col + 4 * g, c1 = col + 16 + 4 * g;
+    const f32x4 d0 = ld4f(brow + c0) - ld4f(ref + c0), d1 = ld4f(brow + c1) - ld4f(ref + c1);
+    f32x4 s0, s1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s0[i] = expu(sgn * d0[i]);
+        s1[i] = expu(sgn * d1[i]);
+    }
+    return ldfrag_scaled(X + row * PX + col + 4 * g, s0, s1);
+}
+
+// A fragment of X^T (m = feature m0 + r, k = token s = k0 + kmap(g, i)) from
+// a row-major LDS tile X[s][feature], element scaled by
+// exp(sgn * (b[s][m] - ref[m])) and zero for tokens outside [klo, khi).
+template <typename E>
+__device__ __forceinline__ Frag<E> frag_col_decay(const E* X, int PX, const float* bs, int PB, int m0, int k0,
+                                                  const float* ref, float sgn, int klo, int khi) {
+    const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+    const int m = m0 + r;
+    const float rm = ref[m];
+    Frag<E> x = ldfrag_tr(X, PX, k0, m0, l);
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int k = k0 + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+        sc[i] = (k >= klo && k < khi) ? expu(sgn * (bs[k * PB + m] - rm)) : 0.f;
+    }
+    if constexpr (sizeof(E) == 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x.v[i] = (bf16)((float)x.v[i] * sc[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x.lo[i] *= sc[i];
+            x.hi[i] *= sc[4 + i];
+        }
+    }
+    return x;
+}
+
+// ---------------------------------------------------------------------------
 // intra: one work-group (4 waves) per (block, head, batch); wave R owns tokens
 // 16R..16R+15 (as t for dq, as s for dk and dv).  All output tiles are
 // transposed ([feature][token]) so each lane stores four contiguous values.
+// K, Q, V, dO and the gate tile are staged row-major in LDS with every load
+// of a stage in flight at once; the block gate cumsum is formed in LDS.
 // ---------------------------------------------------------------------------
+template <typename E, int DK, int DV> struct GlaIntraLds {
+    static constexpr int PK = RP<E, DK>, PV = RP<E, DV>, PB = DK + 4, PD = DK + 1;
+    static constexpr size_t o_K = 0;                                   // E[64][PK]
+    static constexpr size_t o_Q = o_K + sizeof(E) * BLK * PK;          // E[64][PK]
+    static constexpr size_t o_B = o_Q + sizeof(E) * BLK * PK;          // f32[64][PB]  b = cumsum(g)
+    static constexpr size_t o_U = o_B + 4 * BLK * PB;                  // union:
+    static constexpr size_t u_G = o_U;                                 //   g staging E[64][PK]
+    static constexpr size_t u_dO = o_U, u_V = u_dO + sizeof(E) * BLK * PV;  //   dO, V  E[64][PV]
+    static constexpr size_t u_dg = o_U;                                //   dgb f32[64][PD]
+    static constexpr size_t end1 = u_V + sizeof(E) * BLK * PV, end2 = u_dg + 4 * BLK * PD;
+    static constexpr size_t total = end1 > end2 ? end1 : end2;
+};
+
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
+    using Lay = GlaIntraLds<E, DK, DV>;
+    constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, PD = Lay::PD, KV = DV / 32, KK = DK / 32;
+    static_assert(Lay::total <= 150 * 1024, "LDS budget");
+    __shared__ __align__(16) char lds[Lay::total];
+    __shared__ float rsum[4][DK], rowhd[DK];
+    __shared__ __align__(16) float zrow[DK];
+    E* Ks = (E*)(lds + Lay::o_K);
+    E* Qs = (E*)(lds + Lay::o_Q);
+    float* Bs = (float*)(lds + Lay::o_B);
+
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, R = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
     const int T = a.T, H = a.H, NC = a.NC;
@@ -464,38 +553,44 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
     const E* vbase = a.v + tok0 * ldv + (size_t)h * DV;
     const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
-    const float* bc = a.bcum + chunk * BLK * DK;
-    const E* S0 = a.h + chunk * DK * DV;
-    const E* dS1 = a.dh + chunk * DK * DV;
+    const E* S0 = a.h + chunk * DK * DV;    // tiled [d][v]
+    const E* dS1 = a.dh + chunk * DK * DV;  // tiled [d][v]
 
-    __shared__ E Kt[DK * PT], Qt[DK * PT], dOt[DV * PT];
-    __shared__ float bT[DK * BPT];
-    __shared__ float dgb[BLK * (DK + 1)];
-    __shared__ float rsum[4][DK];
-    __shared__ float zrow[DK];
-
-    stage_transposed<E, DK>(kb, ldk, Kt, nvalid);
-    stage_transposed<E, DK>(qb, ldk, Qt, nvalid);
-    stage_transposed<E, DV>(dob, ldv, dOt, nvalid);
-    for (int idx = tid; idx < BLK * DK; idx += 256) {
-        const int t = idx / DK, d = idx % DK;
-        bT[d * BPT + t] = bc[idx];
+    // ---- staging: K, Q, g; then dO, V while the gate cumsum runs ----
+    {
+        const auto kx = load_rows<E, BLK, DK>(kb, ldk, nvalid);
+        const auto qx = load_rows<E, BLK, DK>(qb, ldk, nvalid);
+        const auto gx = load_rows<E, BLK, DK>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        store_rows<E, BLK, DK, PK>(kx, Ks);
+        store_rows<E, BLK, DK, PK>(qx, Qs);
+        store_rows<E, BLK, DK, PK>(gx, (E*)(lds + Lay::u_G));
+        if (tid < DK) zrow[tid] = 0.f;
     }
-    if (tid < DK) zrow[tid] = 0.f;
     __syncthreads();
+    {
+        const auto ox = load_rows<E, BLK, DV>(dob, ldv, nvalid);
+        const auto vx = load_rows<E, BLK, DV>(vbase, ldv, nvalid);
+        gate_cumsum<E, DK, PK, PB>((const E*)(lds + Lay::u_G), Bs, nvalid);
+        __syncthreads();
+        store_rows<E, BLK, DV, PV>(ox, (E*)(lds + Lay::u_dO));
+        store_rows<E, BLK, DV, PV>(vx, (E*)(lds + Lay::u_V));
+    }
+    __syncthreads();
+    const E* dOs = (const E*)(lds + Lay::u_dO);
+    const E* Vs = (const E*)(lds + Lay::u_V);
 
     const int tl = 16 * R + r;  // this lane's token (column of every transposed tile)
-    const float* bt = bc + (size_t)tl * DK;
-    const float* refO = R > 0 ? bc + (size_t)(16 * R - 1) * DK : zrow;
-    const float* refD = bc + (size_t)(16 * R + 7) * DK;
-    const float* refE = bc + (size_t)(16 * R + 15) * DK;
-    const float* bC = bc + (size_t)(BLK - 1) * DK;
+    const float* bt = Bs + tl * PB;
+    const float* refO = R > 0 ? Bs + (16 * R - 1) * PB : zrow;  // boundary before tile R
+    const float* refD = Bs + (16 * R + 7) * PB;                 // middle of tile R
+    const float* refE = Bs + (16 * R + 15) * PB;                // end of tile R
+    const float* bC = Bs + (BLK - 1) * PB;
 
-    Frag<E> fdo[DV / 32], fv[DV / 32];
+    Frag<E> fdo[KV], fv[KV];
 #pragma unroll
-    for (int kk = 0; kk < DV / 32; ++kk) {
-        fdo[kk] = ldfrag_row(dob, tl, nvalid, ldv, 32 * kk + 4 * g);    // Bt = dO, rows of tile R
-        fv[kk] = ldfrag_row(vbase, tl, nvalid, ldv, 32 * kk + 4 * g);   // Bt = V, rows of tile R
+    for (int kk = 0; kk < KV; ++kk) {
+        fdo[kk] = ldfrag(dOs + tl * PV + 32 * kk + 4 * g);  // Bt = dO, rows of tile R
+        fv[kk] = ldfrag(Vs + tl * PV + 32 * kk + 4 * g);    // Bt = V, rows of tile R
     }
     // (1) dP^T[sb][R] (rows s, col t = tl), (2) dP[tb][R] (rows t, col s = tl),
     // (3) P[tb][R] (rows t, col s = tl); all masked to s <= t.
@@ -505,7 +600,7 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
         f32x4 acc = zero4();
         if (x <= R) {
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) mma(acc, ldfrag_row(vbase, 16 * x + r, nvalid, ldv, 32 * kk + 4 * g), fdo[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag(Vs + (16 * x + r) * PV + 32 * kk + 4 * g), fdo[kk]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (16 * x + 4 * g + i > tl) acc[i] = 0.f;
@@ -514,12 +609,13 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
         f32x4 acc2 = zero4(), acc3 = zero4();
         if (x >= R) {
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) mma(acc2, ldfrag_row(dob, 16 * x + r, nvalid, ldv, 32 * kk + 4 * g), fv[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma(acc2, ldfrag(dOs + (16 * x + r) * PV + 32 * kk + 4 * g), fv[kk]);
             const float* ref = x > R ? refE : refD;
+            const int t = 16 * x + r;
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                Frag<E> fq = ldfrag_decay(qb, ldk, 16 * x + r, nvalid, 32 * kk + 4 * g, bc + (size_t)(16 * x + r) * DK, ref);
-                Frag<E> fk = ldfrag_decay(kb, ldk, tl, nvalid, 32 * kk + 4 * g, ref, bt);
+            for (int kk = 0; kk < KK; ++kk) {
+                Frag<E> fq = frag_row_decay(Qs, PK, t, 32 * kk, Bs + t * PB, ref, 1.f);
+                Frag<E> fk = frag_row_decay(Ks, PK, tl, 32 * kk, bt, ref, -1.f);
                 mma(acc3, fq, fk);
             }
 #pragma unroll
@@ -547,34 +643,56 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
         fpD[j] = frag_from_acc<E>(e0, e1);
         fP[j] = frag_from_acc<E>(P[2 * j], P[2 * j + 1]);
     }
+    // (6) dV^T[vb][R] = dO^T P + (Kh dh)^T   (rows v, col s = tl)
+    {
+        const E* dVs = a.dVs + chunk * BLK * DV;
+        f32x4 ds[DV / 16];
+#pragma unroll
+        for (int vb = 0; vb < DV / 16; ++vb) ds[vb] = tl < nvalid ? ld4(dVs + (size_t)tl * DV + 16 * vb + 4 * g) : zero4();
+#pragma unroll
+        for (int vb = 0; vb < DV / 16; ++vb) {
+            f32x4 acc = ds[vb];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (32 * j + 32 > 16 * R) mma(acc, ldfrag_tr(dOs, PV, 32 * j, 16 * vb, l), fP[j]);
+            if (tl < nvalid) st4(a.dv + (tok0 + tl) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc);
+        }
+    }
+    __syncthreads();  // dO, V no longer read from LDS: the union becomes dgb
+    float* dgb = (float*)(lds + Lay::u_dg);
     float rpart[DK / 16][4];
     // (4) dQ^T and (5) dK^T, per 16-row block of features d
-    #pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
-        const int dm = 16 * db + r;  // feature row of this lane's A fragments
-        // dQ: inter  exp(b_t) (S0 dO^T)
-        f32x4 qi = zero4();
 #pragma unroll
-        for (int kk = 0; kk < DV / 32; ++kk) mma(qi, ldfrag(S0 + (size_t)dm * DV + 32 * kk + 4 * g), fdo[kk]);
+    for (int db = 0; db < DK / 16; ++db) {
+        Frag<E> fh[KV], fd[KV];
+#pragma unroll
+        for (int kk = 0; kk < KV; ++kk) {
+            fh[kk] = ldfragT(S0, db * KV + kk, l);
+            fd[kk] = ldfragT(dS1, db * KV + kk, l);
+        }
         // dQ: intra, off-diagonal (reference b_{16R-1}) and diagonal (reference b_{16R+7})
         f32x4 qo = zero4(), qd = zero4();
-        const float rO = refO[dm], rD = refD[dm], rE = refE[dm];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            if (32 * j < 16 * R) mma(qo, ldfragT_decay(Kt, bT, dm, 32 * j, rO, -1.f, 0, 16 * R), fptO[j]);
+            if (32 * j < 16 * R) mma(qo, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, refO, -1.f, 0, 16 * R), fptO[j]);
             if (32 * j <= 16 * R && 16 * R < 32 * j + 32)
-                mma(qd, ldfragT_decay(Kt, bT, dm, 32 * j, rD, -1.f, 16 * R, 16 * R + 16), fptD[j]);
+                mma(qd, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, refD, -1.f, 16 * R, 16 * R + 16), fptD[j]);
         }
-        // dK: intra, later tiles (reference b_{16R+15}) and diagonal; state part
-        f32x4 kl = zero4(), kd = zero4(), ks = zero4();
+        // dK: intra, later tiles (reference b_{16R+15}) and diagonal
+        f32x4 kl = zero4(), kd = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            if (32 * j + 32 > 16 * R + 16) mma(kl, ldfragT_decay(Qt, bT, dm, 32 * j, rE, 1.f, 16 * R + 16, BLK), fpL[j]);
+            if (32 * j + 32 > 16 * R + 16) mma(kl, frag_col_decay(Qs, PK, Bs, PB, 16 * db, 32 * j, refE, 1.f, 16 * R + 16, BLK), fpL[j]);
             if (32 * j <= 16 * R && 16 * R < 32 * j + 32)
-                mma(kd, ldfragT_decay(Qt, bT, dm, 32 * j, rD, 1.f, 16 * R, 16 * R + 16), fpD[j]);
+                mma(kd, frag_col_decay(Qs, PK, Bs, PB, 16 * db, 32 * j, refD, 1.f, 16 * R, 16 * R + 16), fpD[j]);
         }
+        // dQ inter exp(b_t) (S0 dO^T) and the state part of dK
+        f32x4 qi = zero4(), ks = zero4();
 #pragma unroll
-        for (int kk = 0; kk < DV / 32; ++kk) mma(ks, ldfrag(dS1 + (size_t)dm * DV + 32 * kk + 4 * g), fv[kk]);
+        for (int kk = 0; kk < KV; ++kk) {
+            mma(qi, fh[kk], fdo[kk]);
+            mma(ks, fd[kk], fv[kk]);
+        }
         // element-wise factors: rows d = 16 db + 4 g + i, column token tl
         const int d0 = 16 * db + 4 * g;
         const f32x4 btv = ld4f(bt + d0), rOv = ld4f(refO + d0), rDv = ld4f(refD + d0), rEv = ld4f(refE + d0);
@@ -587,21 +705,18 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
             dk[i] = kl[i] * __expf(rEv[i] - btv[i]) + kd[i] * expu(rDv[i] - btv[i]) + ks[i] * es;
         }
         float qk[4] = {0.f, 0.f, 0.f, 0.f};
-        if (tl < nvalid) {
-            const f32x4 qv = ld4(qb + (size_t)tl * ldk + d0), kv = ld4(kb + (size_t)tl * ldk + d0);
+        const f32x4 qv = ld4(Qs + tl * PK + d0), kv = ld4(Ks + tl * PK + d0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qk[i] = qv[i] * dq[i] - kv[i] * dk[i];
-                rpart[db][i] = kv[i] * __expf(bCv[i] - btv[i]) * ks[i];
-            }
+        for (int i = 0; i < 4; ++i) {
+            qk[i] = qv[i] * dq[i] - kv[i] * dk[i];
+            rpart[db][i] = kv[i] * __expf(bCv[i] - btv[i]) * ks[i];
+        }
+        if (tl < nvalid) {
             st4(a.dq + (tok0 + tl) * ldk + (size_t)h * DK + d0, dq);
             st4(a.dk + (tok0 + tl) * ldk + (size_t)h * DK + d0, dk);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rpart[db][i] = 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dgb[tl * (DK + 1) + d0 + i] = qk[i];
+        for (int i = 0; i < 4; ++i) dgb[tl * PD + d0 + i] = qk[i];
     }
     // sum_s Kh[s][d] X[d][s] over this wave's 16 tokens
 #pragma unroll
@@ -615,34 +730,41 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
             x += __shfl_xor(x, 8, 64);
             if (r == 0) rsum[R][16 * db + 4 * g + i] = x;
         }
-    // (6) dV^T[vb][R] = dO^T P + (Kh dh)^T   (rows v, col s = tl)
-    const E* dVs = a.dVs + chunk * BLK * DV;
-    #pragma unroll
-    for (int vb = 0; vb < DV / 16; ++vb) {
-        f32x4 acc = zero4();
+    // rowsum(S0 * dh)[d] over the tiled states: the 16-byte units of row d
+    // (fragment columns c, lane groups g') summed in a fixed order by a pair
+    // of threads, so the result is reproducible
+    {
+        constexpr int HALVES = sizeof(E) == 2 ? 1 : 2, U = KV * 4 * HALVES, VEC = 16 / sizeof(E);
+        const int d = tid >> 1, half = tid & 1;
+        float part = 0.f;
+        if (d < DK) {
+            uint4 xs[U / 2], ys[U / 2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            if (32 * j + 32 > 16 * R) mma(acc, ldfrag(dOt + (16 * vb + r) * PT + 32 * j + 4 * g), fP[j]);
-        if (tl < nvalid) {
-            acc = acc + ld4(dVs + (size_t)tl * DV + 16 * vb + 4 * g);
-            st4(a.dv + (tok0 + tl) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc);
+            for (int q = 0; q < U / 2; ++q) {
+                const int qq = half * (U / 2) + q;
+                const int c = qq / (4 * HALVES), hh = (qq / 4) % HALVES, gq = qq % 4;
+                const size_t u = ((size_t)((d / 16) * KV + c) * HALVES + hh) * 64 + 16 * gq + (d % 16);
+                xs[q] = *(const uint4*)(S0 + u * VEC);
+                ys[q] = *(const uint4*)(dS1 + u * VEC);
+            }
+#pragma unroll
+            for (int q = 0; q < U / 2; ++q) {
+                E x[VEC], y[VEC];
+                *(uint4*)x = xs[q];
+                *(uint4*)y = ys[q];
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) part += to_f(x[i]) * to_f(y[i]);
+            }
         }
+        part += __shfl_xor(part, 1, 64);
+        if (d < DK && half == 0) rowhd[d] = part;
     }
     __syncthreads();
     // (7) dg[t][d] = sum_{tau >= t} dgb[tau][d] + rowsum(S1 * dh)[d]
     for (int d = tid; d < DK; d += 256) {
-        float row = 0.f;
-        constexpr int VEC = 16 / sizeof(E);
-        for (int v = 0; v < DV; v += VEC) {
-            E x[VEC], y[VEC];
-            *(uint4*)x = *(const uint4*)(S0 + (size_t)d * DV + v);
-            *(uint4*)y = *(const uint4*)(dS1 + (size_t)d * DV + v);
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) row += to_f(x[i]) * to_f(y[i]);
-        }
-        float acc = __expf(bC[d]) * row + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
+        float acc = __expf(bC[d]) * rowhd[d] + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
         for (int t = BLK - 1; t >= 0; --t) {
-            acc += dgb[t * (DK + 1) + d];
+            acc += dgb[t * PD + d];
             if (t < nvalid) a.dg[(tok0 + t) * ldk + (size_t)h * DK + d] = from_f<E>(acc);
         }
     }
@@ -678,7 +800,7 @@ hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
     GlaScanBwdArgs<E> sb{ws.bcum, (const E*)ws.Kh, (const E*)ws.QgT, (const E*)L.dO, L.dS_out, L.dS_in,
                          (E*)ws.dh, (E*)ws.dVs, L.T, L.H, L.NC, L.B * L.H};
     launch("gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sb);
-    GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.dO, ws.bcum, (const E*)ws.hT,
+    GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.dO, (const E*)L.g, (const E*)ws.hT,
                        (const E*)ws.dh, (const E*)ws.dVs, (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, L.T, L.H, L.NC};
     launch("gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV>, gblk, dim3(256), st, ia);
     return hipGetLastError();
