@@ -592,6 +592,13 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
         fdo[kk] = ldfrag(dOs + tl * PV + 32 * kk + 4 * g);  // Bt = dO, rows of tile R
         fv[kk] = ldfrag(Vs + tl * PV + 32 * kk + 4 * g);    // Bt = V, rows of tile R
     }
+    // K row tl scaled for the two references of (3)
+    Frag<E> fkD[KK], fkE[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        fkD[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, bt, refD, -1.f);
+        fkE[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, bt, refE, -1.f);
+    }
     // (1) dP^T[sb][R] (rows s, col t = tl), (2) dP[tb][R] (rows t, col s = tl),
     // (3) P[tb][R] (rows t, col s = tl); all masked to s <= t.
     f32x4 dPT[4], dP[4], P[4];
@@ -615,8 +622,7 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 Frag<E> fq = frag_row_decay(Qs, PK, t, 32 * kk, Bs + t * PB, ref, 1.f);
-                Frag<E> fk = frag_row_decay(Ks, PK, tl, 32 * kk, bt, ref, -1.f);
-                mma(acc3, fq, fk);
+                mma(acc3, fq, x > R ? fkE[kk] : fkD[kk]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -661,14 +667,45 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     __syncthreads();  // dO, V no longer read from LDS: the union becomes dgb
     float* dgb = (float*)(lds + Lay::u_dg);
     float rpart[DK / 16][4];
-    // (4) dQ^T and (5) dK^T, per 16-row block of features d
+    // (4) dQ^T and (5) dK^T, per 16-row block of features d.  The state
+    // fragments of block db + 1 are loaded while block db's decay terms run.
+    Frag<E> fh[KV], fd[KV];
+#pragma unroll
+    for (int kk = 0; kk < KV; ++kk) {
+        fh[kk] = ldfragT(S0, kk, l);
+        fd[kk] = ldfragT(dS1, kk, l);
+    }
 #pragma unroll
     for (int db = 0; db < DK / 16; ++db) {
-        Frag<E> fh[KV], fd[KV];
+        // dQ inter exp(b_t) (S0 dO^T), the state part of dK, and (wave 0) the
+        // row sums of S0 * dh for rows 16 db + r
+        f32x4 qi = zero4(), ks = zero4();
+        float hd = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KV; ++kk) {
-            fh[kk] = ldfragT(S0, db * KV + kk, l);
-            fd[kk] = ldfragT(dS1, db * KV + kk, l);
+            mma(qi, fh[kk], fdo[kk]);
+            mma(ks, fd[kk], fv[kk]);
+            if (R == 0) {
+                if constexpr (sizeof(E) == 2) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) hd += (float)fh[kk].v[i] * (float)fd[kk].v[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hd += fh[kk].lo[i] * fd[kk].lo[i] + fh[kk].hi[i] * fd[kk].hi[i];
+                }
+            }
+        }
+        if (R == 0) {
+            hd += __shfl_xor(hd, 16, 64);
+            hd += __shfl_xor(hd, 32, 64);
+            if (g == 0) rowhd[16 * db + r] = hd;
+        }
+        if (db + 1 < DK / 16) {
+#pragma unroll
+            for (int kk = 0; kk < KV; ++kk) {
+                fh[kk] = ldfragT(S0, (db + 1) * KV + kk, l);
+                fd[kk] = ldfragT(dS1, (db + 1) * KV + kk, l);
+            }
         }
         // dQ: intra, off-diagonal (reference b_{16R-1}) and diagonal (reference b_{16R+7})
         f32x4 qo = zero4(), qd = zero4();
@@ -685,13 +722,6 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
             if (32 * j + 32 > 16 * R + 16) mma(kl, frag_col_decay(Qs, PK, Bs, PB, 16 * db, 32 * j, refE, 1.f, 16 * R + 16, BLK), fpL[j]);
             if (32 * j <= 16 * R && 16 * R < 32 * j + 32)
                 mma(kd, frag_col_decay(Qs, PK, Bs, PB, 16 * db, 32 * j, refD, 1.f, 16 * R, 16 * R + 16), fpD[j]);
-        }
-        // dQ inter exp(b_t) (S0 dO^T) and the state part of dK
-        f32x4 qi = zero4(), ks = zero4();
-#pragma unroll
-        for (int kk = 0; kk < KV; ++kk) {
-            mma(qi, fh[kk], fdo[kk]);
-            mma(ks, fd[kk], fv[kk]);
         }
         // element-wise factors: rows d = 16 db + 4 g + i, column token tl
         const int d0 = 16 * db + 4 * g;
@@ -730,35 +760,6 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
             x += __shfl_xor(x, 8, 64);
             if (r == 0) rsum[R][16 * db + 4 * g + i] = x;
         }
-    // rowsum(S0 * dh)[d] over the tiled states: the 16-byte units of row d
-    // (fragment columns c, lane groups g') summed in a fixed order by a pair
-    // of threads, so the result is reproducible
-    {
-        constexpr int HALVES = sizeof(E) == 2 ? 1 : 2, U = KV * 4 * HALVES, VEC = 16 / sizeof(E);
-        const int d = tid >> 1, half = tid & 1;
-        float part = 0.f;
-        if (d < DK) {
-            uint4 xs[U / 2], ys[U / 2];
-#pragma unroll
-            for (int q = 0; q < U / 2; ++q) {
-                const int qq = half * (U / 2) + q;
-                const int c = qq / (4 * HALVES), hh = (qq / 4) % HALVES, gq = qq % 4;
-                const size_t u = ((size_t)((d / 16) * KV + c) * HALVES + hh) * 64 + 16 * gq + (d % 16);
-                xs[q] = *(const uint4*)(S0 + u * VEC);
-                ys[q] = *(const uint4*)(dS1 + u * VEC);
-            }
-#pragma unroll
-            for (int q = 0; q < U / 2; ++q) {
-                E x[VEC], y[VEC];
-                *(uint4*)x = xs[q];
-                *(uint4*)y = ys[q];
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) part += to_f(x[i]) * to_f(y[i]);
-            }
-        }
-        part += __shfl_xor(part, 1, 64);
-        if (d < DK && half == 0) rowhd[d] = part;
-    }
     __syncthreads();
     // (7) dg[t][d] = sum_{tau >= t} dgb[tau][d] + rowsum(S1 * dh)[d]
     for (int d = tid; d < DK; d += 256) {
