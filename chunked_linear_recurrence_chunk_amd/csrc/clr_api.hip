@@ -77,7 +77,7 @@ GlaWs carve_gla(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     Carver c{base};
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
     GlaWs w{};
-    w.bcum = (float*)c.take(nb * BLK * dk * 4);
+    w.eC = (float*)c.take(nb * dk * 4);
     w.KhT = c.take(nb * BLK * dk * es);
     w.hT = c.take(nb * dk * dv * es);
     if (bwd) {

@@ -87,14 +87,14 @@ hipError_t launch_gdn_bwd(const GdnLaunch& L, hipStream_t st);
     CLR_CASE(E, 128, 256)
 
 struct GlaWs {
-    float* bcum;  // [.., 64, dk]  in-block cumulative log gate per channel (fp32)
-    void* KhT;    // [.., dk, 64]  (K * exp(b_C - b))^T, token index fragment-packed
-    void* hT;     // [.., dv, dk]  fwd: state entering the block as h^T (d packed);
-                  //               bwd: key-major h[d][v]
+    float* eC;    // [.., dk]      exp(b_C): the block's total decay per channel (fp32)
+    void* KhT;    // [.., dk, 64]  (K * exp(b_C - b))^T, tiled
+    void* hT;     // fwd: [.., dv, dk] state entering the block as h^T, tiled;
+                  // bwd: [.., dk, dv] key-major h, tiled
     // backward only
-    void* QgT;    // [.., dk, 64]  (Q * exp(b))^T, token index fragment-packed
-    void* Kh;     // [.., 64, dk]  K * exp(b_C - b), d fragment-packed
-    void* dh;     // [.., dk, dv]  key-major gradient w.r.t. the state leaving the block
+    void* QgT;    // [.., dk, 64]  (Q * exp(b))^T, tiled
+    void* Kh;     // [.., 64, dk]  K * exp(b_C - b), tiled
+    void* dh;     // [.., dk, dv]  key-major gradient w.r.t. the state leaving the block, tiled
     void* dVs;    // [.., 64, dv]  Kh dh (state part of dV), token-major
 };
 

@@ -29,10 +29,10 @@ constexpr int NPROD = 3;         // producer waves
 // s_waitcnt immediate for vmcnt(n), other counters unconstrained (gfx9 encoding).
 constexpr unsigned vmcnt_imm(int n) { return (unsigned)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8)); }
 
-template <int NU>
+template <int NU, int NP = NPROD>
 struct RingGeom {
     static constexpr int SLOT = NU * RING_UNIT + RING_SMALL;
-    static constexpr int NU_MIN = NU / NPROD;  // loads per producer per block, lower bound
+    static constexpr int NU_MIN = NU / NP;  // loads per producer per block, lower bound
     static_assert(2 * NU_MIN <= 63, "vmcnt range");
 };
 
@@ -58,6 +58,14 @@ __device__ __forceinline__ void ring_issue(char* slot, int pid, F unit_src, cons
     for (int u = 0; u < NU; ++u)
         if (u % NPROD == pid) __builtin_amdgcn_global_load_lds(unit_src(u), CLR_LDS(slot + u * RING_UNIT), 16, 0, 0);
     if (pid == NPROD - 1) __builtin_amdgcn_global_load_lds(small_src, CLR_LDS(slot + NU * RING_UNIT), 4, 0, 0);
+}
+
+// Issue one block's units with NP producer waves and no small unit.
+template <int NU, int NP, typename F>
+__device__ __forceinline__ void ring_issue_units(char* slot, int pid, F unit_src) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+        if (u % NP == pid) __builtin_amdgcn_global_load_lds(unit_src(u), CLR_LDS(slot + u * RING_UNIT), 16, 0, 0);
 }
 
 // Fragment f of a slot (bf16: one unit per fragment; fp32: two).

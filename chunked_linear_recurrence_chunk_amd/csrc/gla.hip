@@ -35,11 +35,11 @@ __device__ __forceinline__ float expu(float x) { return __expf(fminf(x, 80.f)); 
 template <typename E> struct GlaPrepArgs {
     const E *q, *k, *g;
     int T, H, NC;
-    float* bcum;
+    float* eC;
     E *KhT, *QgT, *Kh;
 };
 template <typename E> struct GlaScanArgs {
-    const float* bcum;
+    const float* eC;
     const E *KhT, *v;
     const float* S_in;
     float* S_out;
@@ -47,14 +47,13 @@ template <typename E> struct GlaScanArgs {
     int T, H, NC, BH;
 };
 template <typename E> struct GlaOutArgs {
-    const E *q, *k, *v;
-    const float* bcum;
+    const E *q, *k, *v, *g;
     const E* hT;
     E* o;
     int T, H, NC;
 };
 template <typename E> struct GlaScanBwdArgs {
-    const float* bcum;
+    const float* eC;
     const E *Kh, *QgT, *dO;
     const float* dS_out;
     float* dS_in;
@@ -70,56 +69,6 @@ template <typename E> struct GlaIntraArgs {
 
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *(const f32x4*)p; }
 
-__device__ __forceinline__ Frag<bf16> zero_frag(bf16*) {
-    Frag<bf16> f;
-    f.v = bf16x8{};
-    return f;
-}
-__device__ __forceinline__ Frag<float> zero_frag(float*) {
-    Frag<float> f;
-    f.lo = zero4();
-    f.hi = zero4();
-    return f;
-}
-
-// Fragment of token-major row `row` (k = feature index col + kmap(g, .)),
-// each element scaled by exp(bA[c] - bB[c]) (bB may be null: exp(bA[c])).
-template <typename E>
-__device__ __forceinline__ Frag<E> ldfrag_decay(const E* base, size_t ld, int row, int nvalid, int col,
-                                                const float* bA, const float* bB) {
-    if (row >= nvalid) return zero_frag((E*)nullptr);
-    f32x4 a0 = ld4f(bA + col), a1 = ld4f(bA + col + 16);
-    if (bB) {
-        a0 = a0 - ld4f(bB + col);
-        a1 = a1 - ld4f(bB + col + 16);
-    }
-    f32x4 s0, s1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        s0[i] = expu(a0[i]);
-        s1[i] = expu(a1[i]);
-    }
-    return ldfrag_scaled(base + (size_t)row * ld + col, s0, s1);
-}
-
-// Fragment of a transposed LDS tile X^T[m][k] (m = feature row, k = token,
-// pitch PT) scaled per element by exp(sgn * (bT[m][k] - ref)), and zero for
-// tokens outside [klo, khi).  bT is the transposed gate tile (pitch BPT).
-constexpr int BPT = BLK + 4;
-template <typename E>
-__device__ __forceinline__ Frag<E> ldfragT_decay(const E* X, const float* bT, int m, int k0, float ref, float sgn,
-                                                 int klo, int khi) {
-    const int g = (threadIdx.x & 63) >> 4;
-    f32x4 s0, s1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ka = k0 + 4 * g + i, kb = k0 + 16 + 4 * g + i;
-        s0[i] = (ka >= klo && ka < khi) ? expu(sgn * (bT[m * BPT + ka] - ref)) : 0.f;
-        s1[i] = (kb >= klo && kb < khi) ? expu(sgn * (bT[m * BPT + kb] - ref)) : 0.f;
-    }
-    return ldfrag_scaled(X + m * PT + k0 + 4 * g, s0, s1);
-}
-
 // B fragment of a token-major tensor with k = token (t = 32 j + kmap(g, i)),
 // n = column c: eight element loads (rows past the sequence end are zero).
 template <typename E>
@@ -131,318 +80,6 @@ __device__ __forceinline__ Frag<E> ldfrag_tokcol(const E* base, size_t ld, int j
         x[i] = t < nvalid ? to_f(base[(size_t)t * ld + c]) : 0.f;
     }
     return frag_from_acc<E>(f32x4{x[0], x[1], x[2], x[3]}, f32x4{x[4], x[5], x[6], x[7]});
-}
-
-// ---------------------------------------------------------------------------
-// prep: one work-group per (block, head, batch).
-// ---------------------------------------------------------------------------
-template <typename E, int DK, bool BWD>
-__global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x;
-    const int T = a.T, H = a.H, NC = a.NC;
-    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
-    const size_t chunk = ((size_t)b * H + h) * NC + n;
-    const int nvalid = min(BLK, T - n * BLK);
-    const size_t ldk = (size_t)H * DK;
-    constexpr int SB = DK + 4;
-
-    __shared__ float sb[BLK * SB];
-    __shared__ E Kt[DK * PT];
-    __shared__ E Qt[BWD ? DK * PT : 8];
-
-    if (tid < DK) {
-        float run = 0.f;
-        float* bc = a.bcum + chunk * BLK * DK;
-        for (int t = 0; t < BLK; ++t) {
-            run += t < nvalid ? to_f(a.g[(tok0 + t) * ldk + (size_t)h * DK + tid]) : 0.f;
-            sb[t * SB + tid] = run;
-            bc[(size_t)t * DK + tid] = run;
-        }
-    }
-    stage_transposed<E, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, Kt, nvalid);
-    if constexpr (BWD) stage_transposed<E, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, Qt, nvalid);
-    __syncthreads();
-
-    E* KhT = a.KhT + chunk * BLK * DK;
-    E* QgT = BWD ? a.QgT + chunk * BLK * DK : nullptr;
-    for (int idx = tid; idx < DK * (BLK / 4); idx += 256) {
-        const int d = idx / (BLK / 4), t4 = (idx % (BLK / 4)) * 4;
-        const float bC = sb[(BLK - 1) * SB + d];
-        f32x4 x = ld4(Kt + d * PT + t4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] *= __expf(bC - sb[(t4 + i) * SB + d]);
-        st4(KhT + (size_t)d * BLK + kperm(t4), x);
-        if constexpr (BWD) {
-            f32x4 y = ld4(Qt + d * PT + t4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] *= __expf(sb[(t4 + i) * SB + d]);
-            st4(QgT + (size_t)d * BLK + kperm(t4), y);
-        }
-    }
-    if constexpr (BWD) {
-        E* Kh = a.Kh + chunk * BLK * DK;
-        const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
-        for (int idx = tid; idx < BLK * (DK / 4); idx += 256) {
-            const int t = idx / (DK / 4), d4 = (idx % (DK / 4)) * 4;
-            f32x4 x = t < nvalid ? ld4(kb + (size_t)t * ldk + d4) : zero4();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] *= __expf(sb[(BLK - 1) * SB + d4 + i] - sb[t * SB + d4 + i]);
-            st4(Kh + (size_t)t * DK + kperm(d4), x);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// scan: one wave per (16-wide value slice, head, batch).  The per-channel
-// decay makes the state update element-wise plus one product, Kh^T V, that
-// does not depend on S; operands of block n+1 are prefetched during block n.
-// ---------------------------------------------------------------------------
-template <typename E, int DK> struct GlaScanOps {
-    Frag<E> kh[DK / 16][2];  // Kh^T rows (A: m = d, k = t)
-    Frag<E> vb[2];           // V (B: k = t, n = v0 + r)
-    f32x4 bC[DK / 16];       // b_C for rows d = 16 db + 4 g + i
-};
-
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void gla_scan_load(GlaScanOps<E, DK>& o, const GlaScanArgs<E>& a, int b, int h, int n,
-                                              size_t chunk, int v0, int r, int g) {
-    const size_t tok0 = (size_t)b * a.T + (size_t)n * BLK;
-    const int nvalid = min(BLK, a.T - n * BLK);
-    const E* KhT = a.KhT + chunk * BLK * DK;
-#pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) o.kh[db][j] = ldfragP(KhT + (size_t)(16 * db + r) * BLK + 32 * j + 8 * g);
-        o.bC[db] = ld4f(a.bcum + (chunk * BLK + BLK - 1) * DK + 16 * db + 4 * g);
-    }
-    const size_t ldv = (size_t)a.H * DV;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) o.vb[j] = ldfrag_tokcol(a.v + tok0 * ldv + (size_t)h * DV, ldv, j, g, v0 + r, nvalid);
-}
-
-template <typename E, int DK, int DV, bool HNAT>
-__device__ __forceinline__ void gla_scan_step(const GlaScanOps<E, DK>& o, f32x4 (&S)[DK / 16],
-                                              const GlaScanArgs<E>& a, size_t chunk, int v0, int r, int g, E* tile) {
-    if (a.hT) {
-        E* hT = a.hT + chunk * DK * DV;
-        if constexpr (HNAT) {
-            store_state_tiled<E, DK, DV>(hT, S, tile, v0, 16 * g + r);
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) st8T(hT, (v0 / 16) * (DK / 32) + kk, 16 * g + r, S[2 * kk], S[2 * kk + 1]);
-        }
-    }
-#pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
-        f32x4 dec;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dec[i] = __expf(o.bC[db][i]);
-        f32x4 acc = S[db] * dec;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc, o.kh[db][j], o.vb[j]);
-        S[db] = acc;
-    }
-}
-
-template <typename E, int DK, int DV, bool HNAT>
-__global__ __launch_bounds__(64) void gla_scan_fwd_kernel(GlaScanArgs<E> a) {
-    const int H = a.H, NC = a.NC;
-    int b, h, vb;
-    if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
-    const int l = threadIdx.x, r = l & 15, g = l >> 4;
-    const int v0 = 16 * vb;
-    constexpr int ND = DK / 16;
-    const size_t bh = (size_t)b * H + h;
-    f32x4 S[ND];
-    const float* Sin = a.S_in ? a.S_in + bh * DK * DV : nullptr;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[db][i] = Sin ? Sin[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
-
-    __shared__ __align__(16) E tile[HNAT ? DK * 16 : 8];
-    GlaScanOps<E, DK> A, B;
-    if (NC > 0) gla_scan_load<E, DK, DV>(A, a, b, h, 0, bh * NC, v0, r, g);
-    for (int n = 0; n < NC; n += 2) {
-        if (n + 1 < NC) gla_scan_load<E, DK, DV>(B, a, b, h, n + 1, bh * NC + n + 1, v0, r, g);
-        gla_scan_step<E, DK, DV, HNAT>(A, S, a, bh * NC + n, v0, r, g, tile);
-        if (n + 1 >= NC) break;
-        if (n + 2 < NC) gla_scan_load<E, DK, DV>(A, a, b, h, n + 2, bh * NC + n + 2, v0, r, g);
-        gla_scan_step<E, DK, DV, HNAT>(B, S, a, bh * NC + n + 1, v0, r, g, tile);
-    }
-    if (a.S_out) {
-        float* So = a.S_out + bh * DK * DV;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) So[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = S[db][i];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// out: one work-group (4 waves) per (block, head, batch); wave R owns tokens
-// 16R..16R+15.  O^T tiles: inter part (h^T (Q*exp(b))^T) plus P V.
-// ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void gla_out_kernel(GlaOutArgs<E> a) {
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, R = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
-    const int T = a.T, H = a.H, NC = a.NC;
-    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
-    const size_t chunk = ((size_t)b * H + h) * NC + n;
-    const int nvalid = min(BLK, T - n * BLK);
-    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
-    const E* qb = a.q + tok0 * ldk + (size_t)h * DK;
-    const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
-    const float* bc = a.bcum + chunk * BLK * DK;
-
-    __shared__ E Vt[DV * PT];
-    stage_transposed<E, DV>(a.v + tok0 * ldv + (size_t)h * DV, ldv, Vt, nvalid);
-    __syncthreads();
-
-    __shared__ float zrow[DK];
-    if (tid < DK) zrow[tid] = 0.f;
-    __syncthreads();
-    const int tl = 16 * R + r;
-    const float* bt = bc + (size_t)tl * DK;
-    const float* refO = R > 0 ? bc + (size_t)(16 * R - 1) * DK : zrow;  // boundary before tile R
-    const float* refD = bc + (size_t)(16 * R + 7) * DK;                 // middle of tile R
-    Frag<E> qi[DK / 32], qo[DK / 32], qd[DK / 32];
-#pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) {
-        qi[kk] = ldfrag_decay(qb, ldk, tl, nvalid, 32 * kk + 4 * g, bt, (const float*)nullptr);
-        qo[kk] = ldfrag_decay(qb, ldk, tl, nvalid, 32 * kk + 4 * g, bt, refO);
-        qd[kk] = ldfrag_decay(qb, ldk, tl, nvalid, 32 * kk + 4 * g, bt, refD);
-    }
-    // P^T[sb][R]: rows s, column t = tl
-    f32x4 P[4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-        f32x4 acc = zero4();
-        if (sb <= R) {
-            const int s = 16 * sb + r;
-            const float* ref = sb < R ? refO : refD;
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                Frag<E> fk = ldfrag_decay(kb, ldk, s, nvalid, 32 * kk + 4 * g, ref, bc + (size_t)s * DK);
-                mma(acc, fk, sb < R ? qo[kk] : qd[kk]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (16 * sb + 4 * g + i > tl) acc[i] = 0.f;
-        }
-        P[sb] = acc;
-    }
-    Frag<E> fp[2];
-    fp[0] = frag_from_acc<E>(P[0], P[1]);
-    fp[1] = frag_from_acc<E>(P[2], P[3]);
-    const E* hT = a.hT + chunk * DK * DV;
-    E* ob = a.o + tok0 * ldv + (size_t)h * DV;
-    #pragma unroll
-    for (int vb = 0; vb < DV / 16; ++vb) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, ldfragT(hT, vb * (DK / 32) + kk, l), qi[kk]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            if (2 * j <= R) mma(acc, ldfrag(Vt + (16 * vb + r) * PT + 32 * j + 4 * g), fp[j]);
-        if (tl < nvalid) st4(ob + (size_t)tl * ldv + 16 * vb + 4 * g, acc);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// dscan: one wave per (16-wide value slice, head, batch), blocks in reverse.
-// Saves dh_n (key-major) and dVs_n = Kh_n dh_n (the state part of dV).
-// ---------------------------------------------------------------------------
-template <typename E, int DK> struct GlaScanBwdOps {
-    Frag<E> kh[4][DK / 32];  // Kh rows (A: m = t, k = d)
-    Frag<E> qg[DK / 16][2];  // (Q*exp(b))^T rows (A: m = d, k = t)
-    Frag<E> dob[2];          // dO (B: k = t, n = v0 + r)
-    f32x4 bC[DK / 16];
-};
-
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void gla_dscan_load(GlaScanBwdOps<E, DK>& o, const GlaScanBwdArgs<E>& a, int b, int h,
-                                               int n, size_t chunk, int v0, int r, int g) {
-    const size_t tok0 = (size_t)b * a.T + (size_t)n * BLK;
-    const int nvalid = min(BLK, a.T - n * BLK);
-    const E* Kh = a.Kh + chunk * BLK * DK;
-    const E* QgT = a.QgT + chunk * BLK * DK;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) o.kh[tb][kk] = ldfragP(Kh + (size_t)(16 * tb + r) * DK + 32 * kk + 8 * g);
-#pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) o.qg[db][j] = ldfragP(QgT + (size_t)(16 * db + r) * BLK + 32 * j + 8 * g);
-        o.bC[db] = ld4f(a.bcum + (chunk * BLK + BLK - 1) * DK + 16 * db + 4 * g);
-    }
-    const size_t ldv = (size_t)a.H * DV;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) o.dob[j] = ldfrag_tokcol(a.dO + tok0 * ldv + (size_t)h * DV, ldv, j, g, v0 + r, nvalid);
-}
-
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void gla_dscan_step(const GlaScanBwdOps<E, DK>& o, f32x4 (&dS)[DK / 16],
-                                               const GlaScanBwdArgs<E>& a, size_t chunk, int v0, int r, int g, E* tile) {
-    store_state_tiled<E, DK, DV>(a.dh + chunk * DK * DV, dS, tile, v0, 16 * g + r);
-    Frag<E> fs[DK / 32];
-#pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
-    f32x4 dVs[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, o.kh[tb][kk], fs[kk]);
-        dVs[tb] = acc;
-    }
-    store_rows16<E, BLK>(a.dVs + chunk * BLK * DV, DV, dVs, tile, v0, r, g);
-#pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
-        f32x4 dec;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dec[i] = __expf(o.bC[db][i]);
-        f32x4 acc = dS[db] * dec;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc, o.qg[db][j], o.dob[j]);
-        dS[db] = acc;
-    }
-}
-
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(64) void gla_scan_bwd_kernel(GlaScanBwdArgs<E> a) {
-    const int H = a.H, NC = a.NC;
-    int b, h, vb;
-    if (!scan_coords(DV / 16, a.BH, H, b, h, vb)) return;
-    const int l = threadIdx.x, r = l & 15, g = l >> 4;
-    const int v0 = 16 * vb;
-    constexpr int ND = DK / 16;
-    const size_t bh = (size_t)b * H + h;
-    f32x4 dS[ND];
-    const float* dSo = a.dS_out ? a.dS_out + bh * DK * DV : nullptr;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dS[db][i] = dSo ? dSo[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
-
-    __shared__ __align__(16) E tile[(DK > BLK ? DK : BLK) * 16];
-    GlaScanBwdOps<E, DK> A, B;
-    if (NC > 0) gla_dscan_load<E, DK, DV>(A, a, b, h, NC - 1, bh * NC + NC - 1, v0, r, g);
-    for (int n = NC - 1; n >= 0; n -= 2) {
-        if (n - 1 >= 0) gla_dscan_load<E, DK, DV>(B, a, b, h, n - 1, bh * NC + n - 1, v0, r, g);
-        gla_dscan_step<E, DK, DV>(A, dS, a, bh * NC + n, v0, r, g, tile);
-        if (n - 1 < 0) break;
-        if (n - 2 >= 0) gla_dscan_load<E, DK, DV>(A, a, b, h, n - 2, bh * NC + n - 2, v0, r, g);
-        gla_dscan_step<E, DK, DV>(B, dS, a, bh * NC + n - 1, v0, r, g, tile);
-    }
-    float* dSi = a.dS_in + bh * DK * DV;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dSi[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = dS[db][i];
 }
 
 // ---------------------------------------------------------------------------
@@ -508,6 +145,415 @@ __device__ __forceinline__ Frag<E> frag_col_decay(const E* X, int PX, const floa
         }
     }
     return x;
+}
+
+// ---------------------------------------------------------------------------
+// prep: one work-group per (block, head, batch).  Writes exp(b_C) and the
+// tiled Kh^T (backward also the tiled (Q*exp(b))^T and Kh), all from
+// row-major LDS tiles staged with every load in flight at once.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, bool BWD>
+__global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int T = a.T, H = a.H, NC = a.NC;
+    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
+    const size_t chunk = ((size_t)b * H + h) * NC + n;
+    const int nvalid = min(BLK, T - n * BLK);
+    const size_t ldk = (size_t)H * DK;
+    constexpr int PK = RP<E, DK>, PB = DK + 4, ND = DK / 16, KK = DK / 32;
+
+    __shared__ __align__(16) E Ks[BLK * PK], Gs[BLK * PK], Qs[BWD ? BLK * PK : 8];
+    __shared__ __align__(16) float Bs[BLK * PB];
+    __shared__ __align__(16) float zrow[DK];
+
+    {
+        const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto gx = load_rows<E, BLK, DK>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        store_rows<E, BLK, DK, PK>(kx, Ks);
+        store_rows<E, BLK, DK, PK>(gx, Gs);
+        if constexpr (BWD) {
+            const auto qx = load_rows<E, BLK, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+            store_rows<E, BLK, DK, PK>(qx, Qs);
+        }
+        if (tid < DK) zrow[tid] = 0.f;
+    }
+    __syncthreads();
+    gate_cumsum<E, DK, PK, PB>(Gs, Bs, nvalid);
+    __syncthreads();
+    const float* bC = Bs + (BLK - 1) * PB;
+    if (tid < DK) a.eC[chunk * DK + tid] = __expf(bC[tid]);
+    // Kh^T (A: m = d, k = t) fragment (db, j) = B fragment of K * exp(b_C - b)
+    E* KhT = a.KhT + chunk * BLK * DK;
+    E* QgT = BWD ? a.QgT + chunk * BLK * DK : nullptr;
+#pragma unroll
+    for (int f = w; f < 2 * ND; f += 4) {
+        const int db = f >> 1, j = f & 1;
+        st_fragT(KhT, f, l, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, bC, -1.f, 0, BLK));
+        if constexpr (BWD) st_fragT(QgT, f, l, frag_col_decay(Qs, PK, Bs, PB, 16 * db, 32 * j, zrow, 1.f, 0, BLK));
+    }
+    if constexpr (BWD) {
+        // Kh (A: m = t, k = d) fragment (tb, kk)
+        E* Kh = a.Kh + chunk * BLK * DK;
+#pragma unroll
+        for (int f = w; f < 4 * KK; f += 4) {
+            const int tb = f / KK, kk = f % KK, t = 16 * tb + (l & 15);
+            st_fragT(Kh, f, l, frag_row_decay(Ks, PK, t, 32 * kk, Bs + t * PB, bC, -1.f));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scans.  One work-group per (NS value slices of 16, head, batch): NS
+// consumer waves each run the recurrence of one slice with its fp32 state
+// in accumulator tiles, NPW producer waves stream the block operands into
+// an LDS ring (clr_ring.h).  The per-channel decay makes each step
+// element-wise plus one product that does not depend on the state.
+// A slot holds the tiled block operands shared by the slices, then each
+// slice's 64 x 16 rows of V (or dO) row-major (read transposed), then exp(b_C).
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV> struct GlaSlices {
+    static constexpr int NS = DV / 16 < 4 ? DV / 16 : 4, NG = DV / 16 / NS, NPW = 4;
+    static constexpr int UPF = sizeof(E) == 2 ? 1 : 2, NVU = (int)sizeof(E);  // units per 64 x 16 slice
+    static constexpr int LPR = (int)sizeof(E), VEC = 16 / (int)sizeof(E);      // lanes per 16-value row
+    static constexpr int THREADS = 64 * (NS + NPW);
+};
+
+// Source of unit q (0 .. NVU-1) of the token-major 64 x 16 slice starting at
+// `rows` (row stride ld); rows past the sequence end repeat the last valid one
+// (its operands there are zero, so the values only have to be finite).
+template <typename E, int DV>
+__device__ __forceinline__ const void* slice_src(const E* rows, size_t ld, int q, int l, int nvalid) {
+    using SL = GlaSlices<E, 16, DV>;
+    const int t = q * (64 / SL::LPR) + l / SL::LPR, part = l % SL::LPR;
+    const int ts = t < nvalid ? t : nvalid - 1;
+    return rows + (size_t)ts * ld + part * SL::VEC;
+}
+
+template <typename E, int DK, int DV, bool HNAT> struct GlaScanGeom : GlaSlices<E, DK, DV> {
+    using SL = GlaSlices<E, DK, DV>;
+    static constexpr int ND = DK / 16, NKU = 2 * ND * SL::UPF;
+    static constexpr int NU = NKU + SL::NS * SL::NVU + 1;  // Kh^T | V slices | exp(b_C)
+    static constexpr int SLOT = RingGeom<NU, SL::NPW>::SLOT;
+    static constexpr int TILE = HNAT ? DK * 16 * (int)sizeof(E) : 16;  // per consumer wave
+    static constexpr int PF = (144 * 1024 - SL::NS * TILE) / SLOT;
+    static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
+};
+
+template <typename E, int DK, int DV, bool HNAT>
+__global__ __launch_bounds__((GlaSlices<E, DK, DV>::THREADS)) void gla_scan_fwd_kernel(GlaScanArgs<E> a) {
+    using SG = GlaScanGeom<E, DK, DV, HNAT>;
+    constexpr int ND = SG::ND, KK = DK / 32, NS = SG::NS, NU = SG::NU, P = SG::P, NKU = SG::NKU, NVU = SG::NVU;
+    constexpr int NPW = SG::NPW, UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
+    using G = RingGeom<NU, NPW>;
+    __shared__ __align__(16) char ring[P * G::SLOT];
+    __shared__ __align__(16) E tiles[NS * SG::TILE / sizeof(E)];
+    const int H = a.H, NC = a.NC;
+    int b, h, vg;
+    if (!scan_coords(SG::NG, a.BH, H, b, h, vg)) return;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+    const size_t bh = (size_t)b * H + h, ldv = (size_t)H * DV;
+
+    if (w >= NS) {  // producers
+        const int pid = w - NS;
+        auto issue = [&](int n) {
+            const size_t c = bh * NC + n;
+            const int nvalid = min(BLK, a.T - n * BLK);
+            const E* KhT = a.KhT + c * BLK * DK + l * LE;
+            const E* vrows = a.v + ((size_t)b * a.T + (size_t)n * BLK) * ldv + (size_t)h * DV + 16 * NS * vg;
+            const float* eC = a.eC + c * DK + 4 * min(l, DK / 4 - 1);
+            auto src = [&](int u) -> const void* {
+                if (u < NKU) return KhT + u * UE;
+                if (u < NKU + NS * NVU) {
+                    const int q = u - NKU;
+                    return slice_src<E, DV>(vrows + 16 * (q / NVU), ldv, q % NVU, l, nvalid);
+                }
+                return eC;
+            };
+            ring_issue_units<NU, NPW>(ring + (n % P) * G::SLOT, pid, src);
+        };
+        const int pre = NC < P - 1 ? NC : P - 1;
+        for (int n = 0; n < pre; ++n) issue(n);
+        ring_wait<G::NU_MIN>(pre - 1);  // block 0 has landed
+        ring_barrier();
+        for (int n = 0; n < NC; ++n) {
+            if (n + P - 1 < NC) issue(n + P - 1);
+            const int last = (n + P - 1 < NC ? n + P - 1 : NC - 1);
+            ring_wait<G::NU_MIN>(last - (n + 1));  // block n + 1 has landed
+            ring_barrier();
+        }
+        return;
+    }
+
+    // consumer wave w: value slice vb
+    const int vb = NS * vg + w, v0 = 16 * vb;
+    E* tile = tiles + w * (SG::TILE / (int)sizeof(E));
+    f32x4 S[ND];
+    const float* Sin = a.S_in ? a.S_in + bh * DK * DV : nullptr;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[db][i] = Sin ? Sin[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
+    ring_barrier();
+    for (int n = 0; n < NC; ++n) {
+        const char* slot = ring + (n % P) * G::SLOT;
+        if (a.hT) {
+            E* hT = a.hT + (bh * NC + n) * DK * DV;
+            if constexpr (HNAT) {
+                store_state_tiled<E, DK, DV>(hT, S, tile, v0, l);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) st8T(hT, vb * KK + kk, l, S[2 * kk], S[2 * kk + 1]);
+            }
+        }
+        const E* Vs = (const E*)(slot + (NKU + w * NVU) * RING_UNIT);
+        const float* eCs = (const float*)(slot + (NU - 1) * RING_UNIT);
+        Frag<E> vf[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) vf[j] = ldfrag_tr(Vs, 16, 32 * j, 0, l);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            f32x4 acc = S[db] * ld4f(eCs + 16 * db + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mma(acc, ring_frag(slot, 2 * db + j, l, (E*)nullptr), vf[j]);
+            S[db] = acc;
+        }
+        ring_barrier();
+    }
+    if (a.S_out) {
+        float* So = a.S_out + bh * DK * DV;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) So[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = S[db][i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// out: one work-group (4 waves) per (block, head, batch); wave R owns tokens
+// 16R..16R+15.  O^T tiles: inter part (h^T (Q*exp(b))^T) plus P V.  Q, K,
+// V and the gate are staged row-major in LDS (V read transposed; when V does
+// not fit, its fragments are gathered from global memory).
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV> struct GlaOutLds {
+    static constexpr int PK = RP<E, DK>, PV = RP<E, DV>, PB = DK + 4;
+    static constexpr size_t o_Q = 0, o_K = o_Q + sizeof(E) * BLK * PK, o_B = o_K + sizeof(E) * BLK * PK;
+    static constexpr size_t o_V = o_B + 4 * BLK * PB;  // V rows; g is staged here first
+    static constexpr size_t vbytes = sizeof(E) * BLK * (PV > PK ? PV : PK);
+    static constexpr bool VLDS = o_V + vbytes <= 150 * 1024;
+    static constexpr size_t total = o_V + (VLDS ? vbytes : sizeof(E) * BLK * PK);
+};
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void gla_out_kernel(GlaOutArgs<E> a) {
+    using Lay = GlaOutLds<E, DK, DV>;
+    constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, KK = DK / 32, NV = DV / 16;
+    static_assert(NV % 2 == 0, "value slices are processed in pairs");
+    __shared__ __align__(16) char lds[Lay::total];
+    __shared__ __align__(16) float zrow[DK];
+    E* Qs = (E*)(lds + Lay::o_Q);
+    E* Ks = (E*)(lds + Lay::o_K);
+    float* Bs = (float*)(lds + Lay::o_B);
+    E* Vs = (E*)(lds + Lay::o_V);
+
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, R = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int T = a.T, H = a.H, NC = a.NC;
+    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
+    const size_t chunk = ((size_t)b * H + h) * NC + n;
+    const int nvalid = min(BLK, T - n * BLK);
+    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
+    const E* vbase = a.v + tok0 * ldv + (size_t)h * DV;
+    const E* hT = a.hT + chunk * DK * DV;
+
+    Frag<E> fh[2][KK];
+    auto load_slice = [&](int buf, int vb) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) fh[buf][kk] = ldfragT(hT, vb * KK + kk, l);
+    };
+    {
+        const auto qx = load_rows<E, BLK, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto gx = load_rows<E, BLK, DK>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        load_slice(0, 0);
+        store_rows<E, BLK, DK, PK>(qx, Qs);
+        store_rows<E, BLK, DK, PK>(kx, Ks);
+        store_rows<E, BLK, DK, PK>(gx, Vs);
+        if (tid < DK) zrow[tid] = 0.f;
+    }
+    __syncthreads();
+    if constexpr (Lay::VLDS) {
+        const auto vx = load_rows<E, BLK, DV>(vbase, ldv, nvalid);
+        gate_cumsum<E, DK, PK, PB>(Vs, Bs, nvalid);
+        __syncthreads();
+        store_rows<E, BLK, DV, PV>(vx, Vs);
+    } else {
+        gate_cumsum<E, DK, PK, PB>(Vs, Bs, nvalid);
+    }
+    __syncthreads();
+
+    const int tl = 16 * R + r;
+    const float* bt = Bs + tl * PB;
+    const float* refO = R > 0 ? Bs + (16 * R - 1) * PB : zrow;  // boundary before tile R
+    const float* refD = Bs + (16 * R + 7) * PB;                 // middle of tile R
+    Frag<E> qi[KK], qo[KK], qd[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        qi[kk] = frag_row_decay(Qs, PK, tl, 32 * kk, bt, zrow, 1.f);
+        qo[kk] = frag_row_decay(Qs, PK, tl, 32 * kk, bt, refO, 1.f);
+        qd[kk] = frag_row_decay(Qs, PK, tl, 32 * kk, bt, refD, 1.f);
+    }
+    // P^T[sb][R]: rows s, column t = tl
+    f32x4 P[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+        f32x4 acc = zero4();
+        if (sb <= R) {
+            const int s = 16 * sb + r;
+            const float* ref = sb < R ? refO : refD;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                mma(acc, frag_row_decay(Ks, PK, s, 32 * kk, Bs + s * PB, ref, -1.f), sb < R ? qo[kk] : qd[kk]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * sb + 4 * g + i > tl) acc[i] = 0.f;
+        }
+        P[sb] = acc;
+    }
+    Frag<E> fp[2];
+    fp[0] = frag_from_acc<E>(P[0], P[1]);
+    fp[1] = frag_from_acc<E>(P[2], P[3]);
+    E* ob = a.o + tok0 * ldv + (size_t)h * DV;
+    auto compute_slice = [&](int buf, int vb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) mma(acc, fh[buf][kk], qi[kk]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (2 * j <= R) {
+                if constexpr (Lay::VLDS) mma(acc, ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l), fp[j]);
+                else mma(acc, ldfrag_tokcol(vbase, ldv, j, g, 16 * vb + r, nvalid), fp[j]);
+            }
+        if (tl < nvalid) st4(ob + (size_t)tl * ldv + 16 * vb + 4 * g, acc);
+    };
+#pragma unroll
+    for (int vb = 0; vb < NV; vb += 2) {
+        load_slice(1, vb + 1);
+        compute_slice(0, vb);
+        if (vb + 2 < NV) load_slice(0, vb + 2);
+        compute_slice(1, vb + 1);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dscan: reverse over the blocks, same work-group shape as the forward scan.
+// Saves dh_n (tiled, key-major) and dVs_n = Kh_n dh_n (the state part of dV,
+// token-major).  Slot: Kh | (Q*exp(b))^T | dO slices | exp(b_C).
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV> struct GlaDscanGeom : GlaSlices<E, DK, DV> {
+    using SL = GlaSlices<E, DK, DV>;
+    static constexpr int ND = DK / 16, KK = DK / 32;
+    static constexpr int NHU = 4 * KK * SL::UPF, NQU = 2 * ND * SL::UPF;
+    static constexpr int NU = NHU + NQU + SL::NS * SL::NVU + 1;
+    static constexpr int SLOT = RingGeom<NU, SL::NPW>::SLOT;
+    static constexpr int TILE = (DK > BLK ? DK : BLK) * 16 * (int)sizeof(E);
+    static constexpr int PF = (144 * 1024 - SL::NS * TILE) / SLOT;
+    static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
+};
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__((GlaSlices<E, DK, DV>::THREADS)) void gla_scan_bwd_kernel(GlaScanBwdArgs<E> a) {
+    using SG = GlaDscanGeom<E, DK, DV>;
+    constexpr int ND = SG::ND, KK = SG::KK, NS = SG::NS, NU = SG::NU, P = SG::P, NHU = SG::NHU, NQU = SG::NQU;
+    constexpr int NVU = SG::NVU, UPF = SG::UPF, NPW = SG::NPW, UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
+    using G = RingGeom<NU, NPW>;
+    __shared__ __align__(16) char ring[P * G::SLOT];
+    __shared__ __align__(16) E tiles[NS * SG::TILE / sizeof(E)];
+    const int H = a.H, NC = a.NC;
+    int b, h, vg;
+    if (!scan_coords(SG::NG, a.BH, H, b, h, vg)) return;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+    const size_t bh = (size_t)b * H + h, ldv = (size_t)H * DV;
+
+    // round m handles block NC - 1 - m
+    if (w >= NS) {  // producers
+        const int pid = w - NS;
+        auto issue = [&](int m) {
+            const int n = NC - 1 - m;
+            const size_t c = bh * NC + n;
+            const int nvalid = min(BLK, a.T - n * BLK);
+            const E* Kh = a.Kh + c * BLK * DK + l * LE;
+            const E* QgT = a.QgT + c * BLK * DK + l * LE;
+            const E* drows = a.dO + ((size_t)b * a.T + (size_t)n * BLK) * ldv + (size_t)h * DV + 16 * NS * vg;
+            const float* eC = a.eC + c * DK + 4 * min(l, DK / 4 - 1);
+            auto src = [&](int u) -> const void* {
+                if (u < NHU) return Kh + u * UE;
+                if (u < NHU + NQU) return QgT + (u - NHU) * UE;
+                if (u < NHU + NQU + NS * NVU) {
+                    const int q = u - NHU - NQU;
+                    return slice_src<E, DV>(drows + 16 * (q / NVU), ldv, q % NVU, l, nvalid);
+                }
+                return eC;
+            };
+            ring_issue_units<NU, NPW>(ring + (m % P) * G::SLOT, pid, src);
+        };
+        const int pre = NC < P - 1 ? NC : P - 1;
+        for (int m = 0; m < pre; ++m) issue(m);
+        ring_wait<G::NU_MIN>(pre - 1);  // round 0 has landed
+        ring_barrier();
+        for (int m = 0; m < NC; ++m) {
+            if (m + P - 1 < NC) issue(m + P - 1);
+            const int last = (m + P - 1 < NC ? m + P - 1 : NC - 1);
+            ring_wait<G::NU_MIN>(last - (m + 1));  // round m + 1 has landed
+            ring_barrier();
+        }
+        return;
+    }
+
+    const int vb = NS * vg + w, v0 = 16 * vb;
+    E* tile = tiles + w * (SG::TILE / (int)sizeof(E));
+    f32x4 dS[ND];
+    const float* dSo = a.dS_out ? a.dS_out + bh * DK * DV : nullptr;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dS[db][i] = dSo ? dSo[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
+    ring_barrier();
+    for (int m = 0; m < NC; ++m) {
+        const size_t c = bh * NC + (NC - 1 - m);
+        const char* slot = ring + (m % P) * G::SLOT;
+        store_state_tiled<E, DK, DV>(a.dh + c * DK * DV, dS, tile, v0, l);
+        Frag<E> fs[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+        f32x4 dVs[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) mma(acc, ring_frag(slot, tb * KK + kk, l, (E*)nullptr), fs[kk]);
+            dVs[tb] = acc;
+        }
+        store_rows16<E, BLK>(a.dVs + c * BLK * DV, DV, dVs, tile, v0, r, g);
+        const E* dOs = (const E*)(slot + (NHU + NQU + w * NVU) * RING_UNIT);
+        const float* eCs = (const float*)(slot + (NU - 1) * RING_UNIT);
+        Frag<E> df[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) df[j] = ldfrag_tr(dOs, 16, 32 * j, 0, l);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            f32x4 acc = dS[db] * ld4f(eCs + 16 * db + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mma(acc, ring_frag(slot, NHU / UPF + 2 * db + j, l, (E*)nullptr), df[j]);
+            dS[db] = acc;
+        }
+        ring_barrier();
+    }
+    float* dSi = a.dS_in + bh * DK * DV;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dSi[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = dS[db][i];
 }
 
 // ---------------------------------------------------------------------------
@@ -778,12 +824,13 @@ template <typename E, int DK, int DV>
 hipError_t launch_gla_fwd_t(const GlaLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GlaWs& ws = L.ws;
-    GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC, ws.bcum, (E*)ws.KhT, nullptr, nullptr};
+    using SL = GlaSlices<E, DK, DV>;
+    GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC, ws.eC, (E*)ws.KhT, nullptr, nullptr};
     launch("gla_prep", gla_prep_kernel<E, DK, false>, gblk, dim3(256), st, pa);
-    GlaScanArgs<E> sa{ws.bcum, (const E*)ws.KhT, (const E*)L.v, L.S_in, L.S_out, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
-    launch("gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sa);
+    GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, L.S_out, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
+    launch("gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
     if (L.o) {
-        GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)L.v, ws.bcum, (const E*)ws.hT, (E*)L.o, L.T, L.H, L.NC};
+        GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)ws.hT, (E*)L.o, L.T, L.H, L.NC};
         launch("gla_out", gla_out_kernel<E, DK, DV>, gblk, dim3(256), st, oa);
     }
     return hipGetLastError();
@@ -793,14 +840,15 @@ template <typename E, int DK, int DV>
 hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GlaWs& ws = L.ws;
+    using SL = GlaSlices<E, DK, DV>;
     GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC,
-                      ws.bcum, (E*)ws.KhT, (E*)ws.QgT, (E*)ws.Kh};
+                      ws.eC, (E*)ws.KhT, (E*)ws.QgT, (E*)ws.Kh};
     launch("gla_prep_bwd", gla_prep_kernel<E, DK, true>, gblk, dim3(256), st, pa);
-    GlaScanArgs<E> sa{ws.bcum, (const E*)ws.KhT, (const E*)L.v, L.S_in, nullptr, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
-    launch("gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sa);
-    GlaScanBwdArgs<E> sb{ws.bcum, (const E*)ws.Kh, (const E*)ws.QgT, (const E*)L.dO, L.dS_out, L.dS_in,
+    GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, nullptr, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
+    launch("gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
+    GlaScanBwdArgs<E> sb{ws.eC, (const E*)ws.Kh, (const E*)ws.QgT, (const E*)L.dO, L.dS_out, L.dS_in,
                          (E*)ws.dh, (E*)ws.dVs, L.T, L.H, L.NC, L.B * L.H};
-    launch("gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(64), st, sb);
+    launch("gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sb);
     GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.dO, (const E*)L.g, (const E*)ws.hT,
                        (const E*)ws.dh, (const E*)ws.dVs, (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, L.T, L.H, L.NC};
     launch("gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV>, gblk, dim3(256), st, ia);
