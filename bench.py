@@ -53,12 +53,12 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
         "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 2 * kv * es + 2 * Cv * es + 3 * Ck * es + 2 * C * es,
                           3 * (2 * C * kv) + 11 * (2 * CC * dk) + 2 * (2 * C ** 3) + 2 * CC * dk),
         # GLA
-        "gla_prep": (2 * Ck * es + Ck * f4 + Ck * es, 0),
-        "gla_prep_bwd": (3 * Ck * es + Ck * f4 + 3 * Ck * es, 0),
+        "gla_prep": (2 * Ck * es + dk * f4 + Ck * es, 0),
+        "gla_prep_bwd": (3 * Ck * es + dk * f4 + 3 * Ck * es, 0),
         "gla_scan_fwd": (Ck * es + Cv * es + dk * f4 + kv * es, 2 * C * kv),
-        "gla_out": (2 * Ck * es + Cv * es + Ck * f4 + kv * es + Cv * es, 2 * CC * dk + 2 * C * kv + 2 * CC * dv),
+        "gla_out": (2 * Ck * es + Cv * es + Ck * es + kv * es + Cv * es, 2 * CC * dk + 2 * C * kv + 2 * CC * dv),
         "gla_scan_bwd": (2 * Ck * es + Cv * es + dk * f4 + kv * es + Cv * es, 2 * (2 * C * kv)),
-        "gla_bwd_intra": (2 * Ck * es + 2 * Cv * es + Ck * f4 + 2 * kv * es + Cv * es + 2 * Ck * es + Cv * es + Ck * es,
+        "gla_bwd_intra": (2 * Ck * es + 2 * Cv * es + Ck * es + 2 * kv * es + Cv * es + 2 * Ck * es + Cv * es + Ck * es,
                           2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv),
     }
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
