@@ -370,8 +370,8 @@ template <typename E, int DK, int DV> struct IntraLds {
     static constexpr size_t o_KKG = o_Ks + sizeof(E) * BLK * PK;       // f32[64][AP]   (K K^T * G), strictly lower
     static constexpr size_t o_TT = o_KKG + 4 * BLK * AP;               // E[64][PT]     TT[s][t] = T[t][s]
     static constexpr size_t o_Tr = o_TT + sizeof(E) * BLK * PT;        // E[64][PT]     T row-major
-    static constexpr size_t o_E = o_Tr + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms)
-    static constexpr size_t o_U = o_E + 4 * BLK * 65;                  // union starts here
+    static constexpr size_t o_E = o_Tr + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms), + 256 spare
+    static constexpr size_t o_U = o_E + 4 * (BLK * 65 + 256);          // union starts here
     // phase 0: Am f32[64][AP], Td f32[4][16][16]
     static constexpr size_t p0_Am = o_U, p0_Td = p0_Am + 4 * BLK * AP;
     static constexpr size_t p0_end = p0_Td + 4 * 4 * 256;
@@ -517,36 +517,6 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             for (int i = 0; i < 4; ++i) Eb[tw * 65 + 16 * sb + 4 * g + i] = dPT[sb][i] * qk[i];
         }
     }
-    // dQ^T[db][w] = Gam_t (S0 dO^T) + K^T dPm^T;  y_t = q_t . (inter part of dq_t)
-    {
-        Frag<E> fpt[2];
-        fpt[0] = frag_from_acc<E>(dPT[0], dPT[1]);
-        fpt[1] = frag_from_acc<E>(dPT[2], dPT[3]);
-        const float Gt = __expf(gam_tw);
-        float qdq = 0.f;
-        Frag<E> fh[2][KV];
-#pragma unroll
-        for (int kk = 0; kk < KV; ++kk) fh[0][kk] = ldfragT(S0, kk, l);
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            if (db + 1 < ND) {
-#pragma unroll
-                for (int kk = 0; kk < KV; ++kk) fh[(db + 1) & 1][kk] = ldfragT(S0, (db + 1) * KV + kk, l);
-            }
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(acc, fh[db & 1][kk], fdo[kk]);
-            acc = acc * Gt;
-            const f32x4 qv = ld4(Qs + tw * PK + 16 * db + 4 * g);
-            qdq += qv[0] * acc[0] + qv[1] * acc[1] + qv[2] * acc[2] + qv[3] * acc[3];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fpt[j]);
-            if (tw < nvalid) st4(a.dq + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, acc);
-        }
-        qdq += __shfl_xor(qdq, 16, 64);
-        qdq += __shfl_xor(qdq, 32, 64);
-        if (g == 0) s_y[tw] = qdq;
-    }
     // dPm[tb][w]: rows t, cols s = tw
     f32x4 dP[4];
 #pragma unroll
@@ -563,58 +533,74 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         }
         dP[tb] = acc;
     }
-    // dK^T accumulators: rows d, cols s = tw
+    // One pass over the 16-row blocks of h_n and dh_n (fragments of block
+    // db + 1 loaded while block db is used):
+    //   dQ^T[db][w] = Gam_t (S0 dO^T) + K^T dPm^T,   y_t = q_t . (inter part of dq_t);
+    //   dK^T[db][w] = Q^T dPm + exp(gamma_C - gamma_s) (dh U^T),   z_s = kh_s . (U dh^T)_s;
+    //   <h_n, dh_n>, wave w summing the blocks db = w mod 4.
     f32x4 dKT[ND];
     {
-        Frag<E> fpm[2];
+        Frag<E> fpt[2], fpm[2];
+        fpt[0] = frag_from_acc<E>(dPT[0], dPT[1]);
+        fpt[1] = frag_from_acc<E>(dPT[2], dPT[3]);
         fpm[0] = frag_from_acc<E>(dP[0], dP[1]);
         fpm[1] = frag_from_acc<E>(dP[2], dP[3]);
-        const float ek = __expf(gC - gam_tw);
-        float kdk = 0.f;
-        Frag<E> fd[2][KV];
+        const float Gt = __expf(gam_tw), ek = __expf(gC - gam_tw);
+        float qdq = 0.f, kdk = 0.f, hdh = 0.f;
+        Frag<E> fh[KV], fd[KV];
 #pragma unroll
-        for (int kk = 0; kk < KV; ++kk) fd[0][kk] = ldfragT(dS1, kk, l);
+        for (int kk = 0; kk < KV; ++kk) {
+            fh[kk] = ldfragT(S0, kk, l);
+            fd[kk] = ldfragT(dS1, kk, l);
+        }
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
+            f32x4 acc = zero4(), accb = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KV; ++kk) {
+                mma(acc, fh[kk], fdo[kk]);
+                mma(accb, fd[kk], fU[kk]);
+            }
+            if ((db & 3) == w) {
+#pragma unroll
+                for (int kk = 0; kk < KV; ++kk) {
+                    if constexpr (sizeof(E) == 2) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) hdh += (float)fh[kk].v[i] * (float)fd[kk].v[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hdh += fh[kk].lo[i] * fd[kk].lo[i] + fh[kk].hi[i] * fd[kk].hi[i];
+                    }
+                }
+            }
             if (db + 1 < ND) {
 #pragma unroll
-                for (int kk = 0; kk < KV; ++kk) fd[(db + 1) & 1][kk] = ldfragT(dS1, (db + 1) * KV + kk, l);
+                for (int kk = 0; kk < KV; ++kk) {
+                    fh[kk] = ldfragT(S0, (db + 1) * KV + kk, l);
+                    fd[kk] = ldfragT(dS1, (db + 1) * KV + kk, l);
+                }
             }
-            f32x4 acc = zero4();
+            acc = acc * Gt;
+            const f32x4 qv = ld4(Qs + tw * PK + 16 * db + 4 * g);
+            qdq += qv[0] * acc[0] + qv[1] * acc[1] + qv[2] * acc[2] + qv[3] * acc[3];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(Qs, PK, 32 * j, 16 * db, l), fpm[j]);
-            f32x4 accb = zero4();
+            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fpt[j]);
+            if (tw < nvalid) st4(a.dq + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, acc);
+            f32x4 acck = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(accb, fd[db & 1][kk], fU[kk]);
+            for (int j = 0; j < 2; ++j) mma(acck, ldfrag_tr(Qs, PK, 32 * j, 16 * db, l), fpm[j]);
             const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
             kdk += kv[0] * accb[0] + kv[1] * accb[1] + kv[2] * accb[2] + kv[3] * accb[3];
-            dKT[db] = acc + accb * ek;
+            dKT[db] = acck + accb * ek;
         }
+        qdq += __shfl_xor(qdq, 16, 64);
+        qdq += __shfl_xor(qdq, 32, 64);
+        if (g == 0) s_y[tw] = qdq;
         kdk += __shfl_xor(kdk, 16, 64);
         kdk += __shfl_xor(kdk, 32, 64);
         if (g == 0) s_kdk[tw] = kdk * ek;
-    }
-    // <h_n, dh_n> (both tiled the same way)
-    {
-        constexpr int VEC = 16 / sizeof(E), NU = DK * DV / VEC, NIT = (NU + 255) / 256;
-        uint4 xs[NIT], ys[NIT];
-#pragma unroll
-        for (int j = 0; j < NIT; ++j) {
-            const int u = tid + 256 * j;
-            xs[j] = u < NU ? *(const uint4*)(S0 + (size_t)u * VEC) : uint4{0u, 0u, 0u, 0u};
-            ys[j] = u < NU ? *(const uint4*)(dS1 + (size_t)u * VEC) : uint4{0u, 0u, 0u, 0u};
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int j = 0; j < NIT; ++j) {
-            E x[VEC], y[VEC];
-            *(uint4*)x = xs[j];
-            *(uint4*)y = ys[j];
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) part += to_f(x[i]) * to_f(y[i]);
-        }
-        part = wave_sum(part);
-        if (l == 0) s_red[w] = part;
+        hdh = wave_sum(hdh);
+        if (l == 0) s_red[w] = hdh;
     }
     __syncthreads();  // phase A done: Qs, dOs, UTs free
 
@@ -758,18 +744,22 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     //   dg_u = sum_{t>=u} y_t + sum_{t>=u>s} E[t][s] + sum_{r<u} z_r + Gam_C <h_n, dh_n>
     // with y_t the S0 -> token-t terms, E the pair terms (dP*P + dA*A) and
     // z_r = kh_r . (U dh^T)_r the Kh-path terms.
-    if (tid < BLK) {  // exclusive prefix over s of each row t, in place
-        float run = 0.f;
-        for (int s2 = 0; s2 < BLK; ++s2) {
-            const float e = Eb[tid * 65 + s2];
-            Eb[tid * 65 + s2] = run;
-            run += e;
+    // F_u = sum_{t >= u} sum_{s < u} E[t][s]: wave w takes rows t = 16w..16w+15,
+    // lane = column u; each row's exclusive prefix over s is a wave scan.
+    {
+        float Fp = 0.f;
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {
+            const int t = 16 * w + i;
+            const float e = Eb[t * 65 + l];
+            const float ex = wave_prefix_sum(e) - e;
+            if (t >= l) Fp += ex;
         }
+        Eb[64 * 65 + w * 64 + l] = Fp;  // spare row after E: the four wave partials
     }
     __syncthreads();
     if (w == 0) {
-        float F = 0.f;
-        for (int t = l; t < BLK; ++t) F += Eb[t * 65 + l];
+        const float F = Eb[64 * 65 + l] + Eb[64 * 65 + 64 + l] + Eb[64 * 65 + 128 + l] + Eb[64 * 65 + 192 + l];
         // reverse inclusive scan of y: lane l sums y over lanes >= l
         float x = s_y[l];
 #pragma unroll
