@@ -52,20 +52,25 @@ __device__ __forceinline__ void ring_barrier() {
 
 // Issue one block's units.  unit_src(u) gives this lane's 16-byte source of
 // unit u; small_src this lane's 4-byte source of the small unit.
-template <int NU, typename F>
-__device__ __forceinline__ void ring_issue(char* slot, int pid, F unit_src, const void* small_src) {
-#pragma unroll
-    for (int u = 0; u < NU; ++u)
-        if (u % NPROD == pid) __builtin_amdgcn_global_load_lds(unit_src(u), CLR_LDS(slot + u * RING_UNIT), 16, 0, 0);
-    if (pid == NPROD - 1) __builtin_amdgcn_global_load_lds(small_src, CLR_LDS(slot + NU * RING_UNIT), 4, 0, 0);
-}
-
-// Issue one block's units with NP producer waves and no small unit.
+// Producer pid issues units pid, pid + NP, ...  pid is wave-uniform; it is
+// read into a scalar register so that the unit loop is straight-line code:
+// a per-unit exec-masked branch costs more issue time than the loads.
 template <int NU, int NP, typename F>
 __device__ __forceinline__ void ring_issue_units(char* slot, int pid, F unit_src) {
+    const int p = __builtin_amdgcn_readfirstlane(pid);
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
-        if (u % NP == pid) __builtin_amdgcn_global_load_lds(unit_src(u), CLR_LDS(slot + u * RING_UNIT), 16, 0, 0);
+    for (int j = 0; j < (NU + NP - 1) / NP; ++j) {
+        const int u = p + NP * j;
+        if (NP * (j + 1) <= NU || u < NU)
+            __builtin_amdgcn_global_load_lds(unit_src(u), CLR_LDS(slot + u * RING_UNIT), 16, 0, 0);
+    }
+}
+
+template <int NU, typename F>
+__device__ __forceinline__ void ring_issue(char* slot, int pid, F unit_src, const void* small_src) {
+    ring_issue_units<NU, NPROD>(slot, pid, unit_src);
+    if (__builtin_amdgcn_readfirstlane(pid) == NPROD - 1)
+        __builtin_amdgcn_global_load_lds(small_src, CLR_LDS(slot + NU * RING_UNIT), 4, 0, 0);
 }
 
 // Fragment f of a slot (bf16: one unit per fragment; fp32: two).
