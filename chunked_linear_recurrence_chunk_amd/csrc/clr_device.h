@@ -236,30 +236,31 @@ __device__ __forceinline__ Frag<float> ldfrag_tr(const float* X, int P, int k0, 
 // several tiles in flight together: load_rows() issues every 16-byte load at
 // once (rows >= nvalid read as zeros), store_rows() writes the registers
 // row-major into LDS with row pitch P (whole 16-byte writes).
-template <typename E, int R, int CC> struct RowsRegs {
-    static constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = CC / VEC, N = R * PER_ROW / 256;
-    static_assert(R * PER_ROW % 256 == 0, "tile must split evenly over 256 threads");
+template <typename E, int R, int CC, int NT = 256> struct RowsRegs {
+    static constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = CC / VEC, UNITS = R * PER_ROW;
+    static constexpr int N = (UNITS + NT - 1) / NT;
     uint4 u[N];
 };
-template <typename E, int R, int CC>
-__device__ __forceinline__ RowsRegs<E, R, CC> load_rows(const E* __restrict__ src, size_t ld, int nvalid) {
-    using X = RowsRegs<E, R, CC>;
+template <typename E, int R, int CC, int NT = 256>
+__device__ __forceinline__ RowsRegs<E, R, CC, NT> load_rows(const E* __restrict__ src, size_t ld, int nvalid) {
+    using X = RowsRegs<E, R, CC, NT>;
     X x;
 #pragma unroll
     for (int j = 0; j < X::N; ++j) {
-        const int idx = threadIdx.x + 256 * j, t = idx / X::PER_ROW, cb = idx % X::PER_ROW;
-        x.u[j] = t < nvalid ? *(const uint4*)(src + (size_t)t * ld + cb * X::VEC) : uint4{0u, 0u, 0u, 0u};
+        const int idx = threadIdx.x + NT * j, t = idx / X::PER_ROW, cb = idx % X::PER_ROW;
+        x.u[j] = (idx < X::UNITS && t < nvalid) ? *(const uint4*)(src + (size_t)t * ld + cb * X::VEC)
+                                                : uint4{0u, 0u, 0u, 0u};
     }
     return x;
 }
-template <typename E, int R, int CC, int P>
-__device__ __forceinline__ void store_rows(const RowsRegs<E, R, CC>& x, E* dst) {
-    using X = RowsRegs<E, R, CC>;
+template <typename E, int R, int CC, int P, int NT = 256>
+__device__ __forceinline__ void store_rows(const RowsRegs<E, R, CC, NT>& x, E* dst) {
+    using X = RowsRegs<E, R, CC, NT>;
     static_assert(P % X::VEC == 0, "row pitch must keep 16-byte alignment");
 #pragma unroll
     for (int j = 0; j < X::N; ++j) {
-        const int idx = threadIdx.x + 256 * j, t = idx / X::PER_ROW, cb = idx % X::PER_ROW;
-        *(uint4*)(dst + t * P + cb * X::VEC) = x.u[j];
+        const int idx = threadIdx.x + NT * j, t = idx / X::PER_ROW, cb = idx % X::PER_ROW;
+        if (idx < X::UNITS) *(uint4*)(dst + t * P + cb * X::VEC) = x.u[j];
     }
 }
 
@@ -363,23 +364,26 @@ __device__ __forceinline__ void stage_T_tiled(const E* __restrict__ src, E* dst)
 // Tiled global X[R][C] -> row-major LDS (row pitch P), in two steps like
 // load_rows / store_rows: every 16-byte unit is loaded at once, then each
 // unit's two 4-element halves are written to their rows.
-template <typename E, int R, int C> struct TiledRegs {
-    static constexpr int UNITS = R * C * (int)sizeof(E) / 16, N = UNITS / 256;
-    static_assert(UNITS % 256 == 0, "tile must split evenly over 256 threads");
+template <typename E, int R, int C, int NT = 256> struct TiledRegs {
+    static constexpr int UNITS = R * C * (int)sizeof(E) / 16, N = (UNITS + NT - 1) / NT;
     uint4 u[N];
 };
-template <typename E, int R, int C>
-__device__ __forceinline__ TiledRegs<E, R, C> load_tiled(const E* __restrict__ src) {
-    TiledRegs<E, R, C> x;
-#pragma unroll
-    for (int j = 0; j < x.N; ++j) x.u[j] = *(const uint4*)(src + (size_t)(threadIdx.x + 256 * j) * (16 / sizeof(E)));
-    return x;
-}
-template <typename E, int R, int C, int P>
-__device__ __forceinline__ void store_untiled(const TiledRegs<E, R, C>& x, E* dst) {
+template <typename E, int R, int C, int NT = 256>
+__device__ __forceinline__ TiledRegs<E, R, C, NT> load_tiled(const E* __restrict__ src) {
+    TiledRegs<E, R, C, NT> x;
 #pragma unroll
     for (int j = 0; j < x.N; ++j) {
-        const int u = threadIdx.x + 256 * j;
+        const int u = threadIdx.x + NT * j;
+        x.u[j] = u < x.UNITS ? *(const uint4*)(src + (size_t)u * (16 / sizeof(E))) : uint4{0u, 0u, 0u, 0u};
+    }
+    return x;
+}
+template <typename E, int R, int C, int P, int NT = 256>
+__device__ __forceinline__ void store_untiled(const TiledRegs<E, R, C, NT>& x, E* dst) {
+#pragma unroll
+    for (int j = 0; j < x.N; ++j) {
+        const int u = threadIdx.x + NT * j;
+        if (u >= x.UNITS) continue;
         if constexpr (sizeof(E) == 2) {
             const int f = u >> 6, lane = u & 63;
             const int row = 16 * (f / (C / 32)) + (lane & 15), c = 32 * (f % (C / 32)) + 4 * (lane >> 4);

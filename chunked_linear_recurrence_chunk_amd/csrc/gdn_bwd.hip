@@ -390,9 +390,11 @@ template <typename E, int DK, int DV> struct IntraLds {
 };
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
+__global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     using Lay = IntraLds<E, DK, DV>;
-    constexpr int PK = Lay::PK, PV = Lay::PV, KK = DK / 32, KV = DV / 32, ND = DK / 16;
+    constexpr int NT = 512;
+    constexpr int PK = Lay::PK, PV = Lay::PV, KK = DK / 32, KV = DV / 32, ND = DK / 16, NDH = ND / 2;
+    constexpr int NVH = DV / 32;  // value blocks per half
     static_assert(Lay::total <= 150 * 1024, "LDS budget");
     __shared__ __align__(16) char lds[Lay::total];
     E* Ks = (E*)(lds + Lay::o_Ks);
@@ -401,10 +403,14 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     E* Tr = (E*)(lds + Lay::o_Tr);
     float* Eb = (float*)(lds + Lay::o_E);
 
-    __shared__ float s_gam[BLK], s_bet[BLK], s_y[BLK], s_kdk[BLK], s_dbg[BLK], s_red[4];
+    // per-token partial sums of the two halves, combined in a fixed order
+    __shared__ float s_gam[BLK], s_bet[BLK], s_y[BLK], s_kdk[BLK], s_red[8];
+    __shared__ float s_q2[2][BLK], s_k2[2][BLK], s_g2[2][BLK], s_v2[2][BLK], s_b2[2][BLK];
 
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    // wave w8: token block w = w8 & 3, half hf = w8 >> 2 (halves split the
+    // feature / value / token-block loops of each phase)
+    const int tid = threadIdx.x, w8 = tid >> 6, w = w8 & 3, hf = w8 >> 2, l = tid & 63, r = l & 15, g = l >> 4;
     const int T = a.T, H = a.H, NC = a.NC;
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
     const size_t chunk = ((size_t)b * H + h) * NC + n;
@@ -420,15 +426,15 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     const E* dUT = a.dUT + chunk * BLK * DV;
 
     // ---------------- phase 0: gates, K, Gram, T -----------------------------
-    const auto kx = load_rows<E, BLK, DK>(kb, ldk, nvalid);
-    const auto qx = load_rows<E, BLK, DK>(qb, ldk, nvalid);
-    const auto ox = load_rows<E, BLK, DV>(dob, ldv, nvalid);
-    const auto ux = load_tiled<E, DV, BLK>(UT);
+    const auto kx = load_rows<E, BLK, DK, NT>(kb, ldk, nvalid);
+    const auto qx = load_rows<E, BLK, DK, NT>(qb, ldk, nvalid);
+    const auto ox = load_rows<E, BLK, DV, NT>(dob, ldv, nvalid);
+    const auto ux = load_tiled<E, DV, BLK, NT>(UT);
     if (tid < BLK) {
         s_gam[tid] = a.gam[chunk * BLK + tid];
         s_bet[tid] = tid < nvalid ? to_f(a.beta[(tok0 + tid) * H + h]) : 0.f;
     }
-    store_rows<E, BLK, DK, PK>(kx, Ks);
+    store_rows<E, BLK, DK, PK, NT>(kx, Ks);
     __syncthreads();
     {
         float* Am = (float*)(lds + Lay::p0_Am);
@@ -437,6 +443,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         for (int kk = 0; kk < KK; ++kk) fa[kk] = ldfrag(Ks + (16 * w + r) * PK + 32 * kk + 4 * g);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            if ((j & 1) != hf) continue;
             f32x4 acc = zero4();
             if (j <= w) {
 #pragma unroll
@@ -451,15 +458,19 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             }
         }
         __syncthreads();
-        f32x4 tc[4];
-        tri_inverse_cols(Am, (float*)(lds + Lay::p0_Td), tc);
-        // wave w holds column block w of T: write T row-major (Tr) and transposed (TT)
-        const int s = 16 * w + r;
+        if (hf == 0) {
+            f32x4 tc[4];
+            tri_inverse_cols(Am, (float*)(lds + Lay::p0_Td), tc);  // waves 0..3; one barrier inside
+            // wave w holds column block w of T: write T row-major (Tr) and transposed (TT)
+            const int s = 16 * w + r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) Tr[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii]);
-            st4(TT + s * PT + 16 * i + 4 * g, tc[i]);
+                for (int ii = 0; ii < 4; ++ii) Tr[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii]);
+                st4(TT + s * PT + 16 * i + 4 * g, tc[i]);
+            }
+        } else {
+            __syncthreads();  // matches the barrier inside tri_inverse_cols
         }
         __syncthreads();
     }
@@ -468,11 +479,11 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     E* dOs = (E*)(lds + Lay::pA_dO);
     E* UTs = (E*)(lds + Lay::pA_UT);
     // phase B operands: in flight during phase A
-    const auto vx = load_rows<E, BLK, DV>(vbase, ldv, nvalid);
-    const auto dux = load_tiled<E, DV, BLK>(dUT);
-    store_rows<E, BLK, DK, PK>(qx, Qs);
-    store_rows<E, BLK, DV, PV>(ox, dOs);
-    store_untiled<E, DV, BLK, PT>(ux, UTs);
+    const auto vx = load_rows<E, BLK, DV, NT>(vbase, ldv, nvalid);
+    const auto dux = load_tiled<E, DV, BLK, NT>(dUT);
+    store_rows<E, BLK, DK, PK, NT>(qx, Qs);
+    store_rows<E, BLK, DV, PV, NT>(ox, dOs);
+    store_untiled<E, DV, BLK, PT, NT>(ux, UTs);
     __syncthreads();
 
     const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
@@ -508,6 +519,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         for (int kk = 0; kk < KK; ++kk) fq[kk] = ldfrag(Qs + tw * PK + 32 * kk + 4 * g);
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
+            if ((sb & 1) != hf) continue;
             f32x4 qk = zero4();
             if (sb <= w) {
 #pragma unroll
@@ -533,12 +545,12 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         }
         dP[tb] = acc;
     }
-    // One pass over the 16-row blocks of h_n and dh_n (fragments of block
-    // db + 1 loaded while block db is used):
+    // One pass over this half's 16-row blocks of h_n and dh_n (fragments of the
+    // next block loaded while the current one is used):
     //   dQ^T[db][w] = Gam_t (S0 dO^T) + K^T dPm^T,   y_t = q_t . (inter part of dq_t);
     //   dK^T[db][w] = Q^T dPm + exp(gamma_C - gamma_s) (dh U^T),   z_s = kh_s . (U dh^T)_s;
-    //   <h_n, dh_n>, wave w summing the blocks db = w mod 4.
-    f32x4 dKT[ND];
+    //   <h_n, dh_n>, each wave summing one block in four.
+    f32x4 dKT[NDH];
     {
         Frag<E> fpt[2], fpm[2];
         fpt[0] = frag_from_acc<E>(dPT[0], dPT[1]);
@@ -550,18 +562,19 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         Frag<E> fh[KV], fd[KV];
 #pragma unroll
         for (int kk = 0; kk < KV; ++kk) {
-            fh[kk] = ldfragT(S0, kk, l);
-            fd[kk] = ldfragT(dS1, kk, l);
+            fh[kk] = ldfragT(S0, (hf * NDH) * KV + kk, l);
+            fd[kk] = ldfragT(dS1, (hf * NDH) * KV + kk, l);
         }
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
+        for (int jd = 0; jd < NDH; ++jd) {
+            const int db = hf * NDH + jd;
             f32x4 acc = zero4(), accb = zero4();
 #pragma unroll
             for (int kk = 0; kk < KV; ++kk) {
                 mma(acc, fh[kk], fdo[kk]);
                 mma(accb, fd[kk], fU[kk]);
             }
-            if ((db & 3) == w) {
+            if ((jd & 3) == w) {
 #pragma unroll
                 for (int kk = 0; kk < KV; ++kk) {
                     if constexpr (sizeof(E) == 2) {
@@ -573,7 +586,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
                     }
                 }
             }
-            if (db + 1 < ND) {
+            if (jd + 1 < NDH) {
 #pragma unroll
                 for (int kk = 0; kk < KV; ++kk) {
                     fh[kk] = ldfragT(S0, (db + 1) * KV + kk, l);
@@ -591,16 +604,18 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             for (int j = 0; j < 2; ++j) mma(acck, ldfrag_tr(Qs, PK, 32 * j, 16 * db, l), fpm[j]);
             const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
             kdk += kv[0] * accb[0] + kv[1] * accb[1] + kv[2] * accb[2] + kv[3] * accb[3];
-            dKT[db] = acck + accb * ek;
+            dKT[jd] = acck + accb * ek;
         }
         qdq += __shfl_xor(qdq, 16, 64);
         qdq += __shfl_xor(qdq, 32, 64);
-        if (g == 0) s_y[tw] = qdq;
         kdk += __shfl_xor(kdk, 16, 64);
         kdk += __shfl_xor(kdk, 32, 64);
-        if (g == 0) s_kdk[tw] = kdk * ek;
+        if (g == 0) {
+            s_q2[hf][tw] = qdq;
+            s_k2[hf][tw] = kdk * ek;
+        }
         hdh = wave_sum(hdh);
-        if (l == 0) s_red[w] = hdh;
+        if (l == 0) s_red[w8] = hdh;
     }
     __syncthreads();  // phase A done: Qs, dOs, UTs free
 
@@ -610,26 +625,27 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     E* dTT = (E*)(lds + Lay::pB_dTT);
     E* Ms = (E*)(lds + Lay::pB_Ms);
     E* Vs = (E*)(lds + Lay::pB_V);
-    store_untiled<E, DV, BLK, PT>(dux, dUTs);
-    store_rows<E, BLK, DV, PV>(vx, Vs);
+    store_untiled<E, DV, BLK, PT, NT>(dux, dUTs);
+    store_rows<E, BLK, DV, PV, NT>(vx, Vs);
     __syncthreads();
     // dW^T[db][w] = -(S0 dU^T): rows d, cols t = tw;  stored as dW[t][d]
     {
         Frag<E> fdu[KV];
 #pragma unroll
         for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr(dUTs, PT, 32 * kk, 16 * w, l);
-        Frag<E> fh[2][KV];
+        Frag<E> fh[KV];
 #pragma unroll
-        for (int kk = 0; kk < KV; ++kk) fh[0][kk] = ldfragT(S0, kk, l);
+        for (int kk = 0; kk < KV; ++kk) fh[kk] = ldfragT(S0, (hf * NDH) * KV + kk, l);
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            if (db + 1 < ND) {
-#pragma unroll
-                for (int kk = 0; kk < KV; ++kk) fh[(db + 1) & 1][kk] = ldfragT(S0, (db + 1) * KV + kk, l);
-            }
+        for (int jd = 0; jd < NDH; ++jd) {
+            const int db = hf * NDH + jd;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(acc, fh[db & 1][kk], fdu[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma(acc, fh[kk], fdu[kk]);
+            if (jd + 1 < NDH) {
+#pragma unroll
+                for (int kk = 0; kk < KV; ++kk) fh[kk] = ldfragT(S0, (db + 1) * KV + kk, l);
+            }
             st4(dWs + tw * PK + 16 * db + 4 * g, -acc);
         }
     }
@@ -643,6 +659,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         for (int kk = 0; kk < KK; ++kk) fdw[kk] = ldfrag(dWs + (16 * w + r) * PK + 32 * kk + 4 * g);
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
+            if ((sb & 1) != hf) continue;
             f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
             for (int kk = 0; kk < KV; ++kk) mma(a1, fdu[kk], ldfrag(Vs + (16 * sb + r) * PV + 32 * kk + 4 * g));
@@ -672,6 +689,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         float gram[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
+            if ((cb & 1) != hf) continue;
             f32x4 acc = zero4();
             if (cb <= w) {
 #pragma unroll
@@ -696,57 +714,69 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             x += __shfl_xor(x, 2, 64);
             x += __shfl_xor(x, 4, 64);
             x += __shfl_xor(x, 8, 64);
-            if (r == 0) s_dbg[16 * w + 4 * g + i] = x;
+            if (r == 0) s_g2[hf][16 * w + 4 * g + i] = x;
         }
     }
     __syncthreads();
     // dV^T[vb][w] = beta_s (dU^T T): rows v, cols s = tw;   dbeta V-term
     const float bet_tw = s_bet[tw];
-    float dbv = 0.f;
+    {
+        float dbv = 0.f;
 #pragma unroll
-    for (int vb = 0; vb < DV / 16; ++vb) {
-        f32x4 acc = zero4();
+        for (int jv = 0; jv < NVH; ++jv) {
+            const int vb = hf * NVH + jv;
+            f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            mma(acc, ldfrag(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
-        const f32x4 vv = ld4(Vs + tw * PV + 16 * vb + 4 * g);
-        dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
-        if (tw < nvalid) st4(a.dv + (tok0 + tw) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc * bet_tw);
+            for (int j = 0; j < 2; ++j)
+                mma(acc, ldfrag(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
+            const f32x4 vv = ld4(Vs + tw * PV + 16 * vb + 4 * g);
+            dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
+            if (tw < nvalid) st4(a.dv + (tok0 + tw) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc * bet_tw);
+        }
+        dbv += __shfl_xor(dbv, 16, 64);
+        dbv += __shfl_xor(dbv, 32, 64);
+        if (g == 0) s_v2[hf][tw] = dbv;
     }
-    dbv += __shfl_xor(dbv, 16, 64);
-    dbv += __shfl_xor(dbv, 32, 64);
     // dK^T += beta_s Gam_s (dW^T T) + K^T Msym ;  dbeta K-term
     const float Gs = __expf(gam_tw);
-    float dbk = 0.f;
+    {
+        float dbk = 0.f;
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-        f32x4 acc = zero4();
+        for (int jd = 0; jd < NDH; ++jd) {
+            const int db = hf * NDH + jd;
+            f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(dWs, PK, 32 * j, 16 * db, l), ldfrag(TT + tw * PT + 32 * j + 4 * g));
-        f32x4 accm = zero4();
+            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(dWs, PK, 32 * j, 16 * db, l), ldfrag(TT + tw * PT + 32 * j + 4 * g));
+            f32x4 accm = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma(accm, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), ldfrag(Ms + tw * PT + 32 * j + 4 * g));
-        const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
-        dbk += kv[0] * acc[0] + kv[1] * acc[1] + kv[2] * acc[2] + kv[3] * acc[3];
-        const f32x4 res = dKT[db] + acc * (bet_tw * Gs) + accm;
-        if (tw < nvalid) st4(a.dk + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, res);
-    }
-    dbk += __shfl_xor(dbk, 16, 64);
-    dbk += __shfl_xor(dbk, 32, 64);
-    if (g == 0) {
-        s_y[tw] += bet_tw * Gs * dbk;  // W path: dgamma_t from Gam_t in W = T Diag(beta Gam) K
-        const float dbeta = dbv + Gs * dbk + s_dbg[tw];
-        if (tw < nvalid) a.dbeta[(tok0 + tw) * H + h] = from_f<E>(dbeta);
+            for (int j = 0; j < 2; ++j) mma(accm, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), ldfrag(Ms + tw * PT + 32 * j + 4 * g));
+            const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
+            dbk += kv[0] * acc[0] + kv[1] * acc[1] + kv[2] * acc[2] + kv[3] * acc[3];
+            const f32x4 res = dKT[jd] + acc * (bet_tw * Gs) + accm;
+            if (tw < nvalid) st4(a.dk + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, res);
+        }
+        dbk += __shfl_xor(dbk, 16, 64);
+        dbk += __shfl_xor(dbk, 32, 64);
+        if (g == 0) s_b2[hf][tw] = dbk;
     }
     __syncthreads();
+    if (tid < BLK) {  // combine the halves (fixed order)
+        const int t = tid;
+        const float Gt = __expf(s_gam[t]);
+        const float dbk = s_b2[0][t] + s_b2[1][t];
+        s_y[t] = (s_q2[0][t] + s_q2[1][t]) + s_bet[t] * Gt * dbk;  // W path: dgamma_t from Gam_t in W
+        s_kdk[t] = s_k2[0][t] + s_k2[1][t];
+        const float dbeta = (s_v2[0][t] + s_v2[1][t]) + Gt * dbk + (s_g2[0][t] + s_g2[1][t]);
+        if (t < nvalid) a.dbeta[(tok0 + t) * H + h] = from_f<E>(dbeta);
+    }
     // Gate gradient, summing only contributions that cross the token boundary
     // (exact, and free of the cancellation a suffix sum of per-token terms has):
     //   dg_u = sum_{t>=u} y_t + sum_{t>=u>s} E[t][s] + sum_{r<u} z_r + Gam_C <h_n, dh_n>
     // with y_t the S0 -> token-t terms, E the pair terms (dP*P + dA*A) and
     // z_r = kh_r . (U dh^T)_r the Kh-path terms.
-    // F_u = sum_{t >= u} sum_{s < u} E[t][s]: wave w takes rows t = 16w..16w+15,
+    // F_u = sum_{t >= u} sum_{s < u} E[t][s]: waves 0..3 take rows t = 16w..16w+15,
     // lane = column u; each row's exclusive prefix over s is a wave scan.
-    {
+    if (w8 < 4) {
         float Fp = 0.f;
 #pragma unroll 4
         for (int i = 0; i < 16; ++i) {
@@ -758,7 +788,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         Eb[64 * 65 + w * 64 + l] = Fp;  // spare row after E: the four wave partials
     }
     __syncthreads();
-    if (w == 0) {
+    if (w8 == 0) {
         const float F = Eb[64 * 65 + l] + Eb[64 * 65 + 64 + l] + Eb[64 * 65 + 128 + l] + Eb[64 * 65 + 192 + l];
         // reverse inclusive scan of y: lane l sums y over lanes >= l
         float x = s_y[l];
@@ -769,7 +799,8 @@ __global__ __launch_bounds__(256) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         }
         const float z = s_kdk[l];
         const float zex = wave_prefix_sum(z) - z;
-        const float end = __expf(gC) * (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+        const float hd = ((s_red[0] + s_red[1]) + (s_red[2] + s_red[3])) + ((s_red[4] + s_red[5]) + (s_red[6] + s_red[7]));
+        const float end = __expf(gC) * hd;
         if (l < nvalid) a.dg[(tok0 + l) * H + h] = from_f<E>(x + F + zex + end);
     }
 }
@@ -796,7 +827,7 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const E*)ws.dUT,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};
-    launch("gdn_bwd_intra", gdn_bwd_intra_kernel<E, DK, DV>, gblk, dim3(256), st, ia);
+    launch("gdn_bwd_intra", gdn_bwd_intra_kernel<E, DK, DV>, gblk, dim3(512), st, ia);
     return hipGetLastError();
 }
 
