@@ -577,8 +577,9 @@ template <typename E, int DK, int DV> struct GlaIntraLds {
 };
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
+__global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     using Lay = GlaIntraLds<E, DK, DV>;
+    constexpr int NT = 512;
     constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, PD = Lay::PD, KV = DV / 32, KK = DK / 32;
     static_assert(Lay::total <= 150 * 1024, "LDS budget");
     __shared__ __align__(16) char lds[Lay::total];
@@ -589,7 +590,9 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     float* Bs = (float*)(lds + Lay::o_B);
 
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, R = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    // wave w8: token tile R = w8 & 3, half hf = w8 >> 2 (halves split the value
+    // and feature loops)
+    const int tid = threadIdx.x, w8 = tid >> 6, R = w8 & 3, hf = w8 >> 2, l = tid & 63, r = l & 15, g = l >> 4;
     const int T = a.T, H = a.H, NC = a.NC;
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
     const size_t chunk = ((size_t)b * H + h) * NC + n;
@@ -604,22 +607,22 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 
     // ---- staging: K, Q, g; then dO, V while the gate cumsum runs ----
     {
-        const auto kx = load_rows<E, BLK, DK>(kb, ldk, nvalid);
-        const auto qx = load_rows<E, BLK, DK>(qb, ldk, nvalid);
-        const auto gx = load_rows<E, BLK, DK>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        store_rows<E, BLK, DK, PK>(kx, Ks);
-        store_rows<E, BLK, DK, PK>(qx, Qs);
-        store_rows<E, BLK, DK, PK>(gx, (E*)(lds + Lay::u_G));
+        const auto kx = load_rows<E, BLK, DK, NT>(kb, ldk, nvalid);
+        const auto qx = load_rows<E, BLK, DK, NT>(qb, ldk, nvalid);
+        const auto gx = load_rows<E, BLK, DK, NT>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        store_rows<E, BLK, DK, PK, NT>(kx, Ks);
+        store_rows<E, BLK, DK, PK, NT>(qx, Qs);
+        store_rows<E, BLK, DK, PK, NT>(gx, (E*)(lds + Lay::u_G));
         if (tid < DK) zrow[tid] = 0.f;
     }
     __syncthreads();
     {
-        const auto ox = load_rows<E, BLK, DV>(dob, ldv, nvalid);
-        const auto vx = load_rows<E, BLK, DV>(vbase, ldv, nvalid);
+        const auto ox = load_rows<E, BLK, DV, NT>(dob, ldv, nvalid);
+        const auto vx = load_rows<E, BLK, DV, NT>(vbase, ldv, nvalid);
         gate_cumsum<E, DK, PK, PB>((const E*)(lds + Lay::u_G), Bs, nvalid);
         __syncthreads();
-        store_rows<E, BLK, DV, PV>(ox, (E*)(lds + Lay::u_dO));
-        store_rows<E, BLK, DV, PV>(vx, (E*)(lds + Lay::u_V));
+        store_rows<E, BLK, DV, PV, NT>(ox, (E*)(lds + Lay::u_dO));
+        store_rows<E, BLK, DV, PV, NT>(vx, (E*)(lds + Lay::u_V));
     }
     __syncthreads();
     const E* dOs = (const E*)(lds + Lay::u_dO);
@@ -698,12 +701,15 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     // (6) dV^T[vb][R] = dO^T P + (Kh dh)^T   (rows v, col s = tl)
     {
         const E* dVs = a.dVs + chunk * BLK * DV;
-        f32x4 ds[DV / 16];
+        constexpr int NVH = DV / 32;  // value blocks per half
+        f32x4 ds[NVH];
 #pragma unroll
-        for (int vb = 0; vb < DV / 16; ++vb) ds[vb] = tl < nvalid ? ld4(dVs + (size_t)tl * DV + 16 * vb + 4 * g) : zero4();
+        for (int jv = 0; jv < NVH; ++jv)
+            ds[jv] = tl < nvalid ? ld4(dVs + (size_t)tl * DV + 16 * (hf * NVH + jv) + 4 * g) : zero4();
 #pragma unroll
-        for (int vb = 0; vb < DV / 16; ++vb) {
-            f32x4 acc = ds[vb];
+        for (int jv = 0; jv < NVH; ++jv) {
+            const int vb = hf * NVH + jv;
+            f32x4 acc = ds[jv];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 if (32 * j + 32 > 16 * R) mma(acc, ldfrag_tr(dOs, PV, 32 * j, 16 * vb, l), fP[j]);
@@ -712,17 +718,20 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     }
     __syncthreads();  // dO, V no longer read from LDS: the union becomes dgb
     float* dgb = (float*)(lds + Lay::u_dg);
-    float rpart[DK / 16][4];
-    // (4) dQ^T and (5) dK^T, per 16-row block of features d.  The state
-    // fragments of block db + 1 are loaded while block db's decay terms run.
+    constexpr int NDH = DK / 32;  // feature blocks per half
+    float rpart[NDH][4];
+    // (4) dQ^T and (5) dK^T, per 16-row block of features d (this half's
+    // blocks).  The state fragments of the next block are loaded while the
+    // current block's decay terms run.
     Frag<E> fh[KV], fd[KV];
 #pragma unroll
     for (int kk = 0; kk < KV; ++kk) {
-        fh[kk] = ldfragT(S0, kk, l);
-        fd[kk] = ldfragT(dS1, kk, l);
+        fh[kk] = ldfragT(S0, (hf * NDH) * KV + kk, l);
+        fd[kk] = ldfragT(dS1, (hf * NDH) * KV + kk, l);
     }
 #pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
+    for (int jd = 0; jd < NDH; ++jd) {
+        const int db = hf * NDH + jd;
         // dQ inter exp(b_t) (S0 dO^T), the state part of dK, and (wave 0) the
         // row sums of S0 * dh for rows 16 db + r
         f32x4 qi = zero4(), ks = zero4();
@@ -746,7 +755,7 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
             hd += __shfl_xor(hd, 32, 64);
             if (g == 0) rowhd[16 * db + r] = hd;
         }
-        if (db + 1 < DK / 16) {
+        if (jd + 1 < NDH) {
 #pragma unroll
             for (int kk = 0; kk < KV; ++kk) {
                 fh[kk] = ldfragT(S0, (db + 1) * KV + kk, l);
@@ -785,7 +794,7 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             qk[i] = qv[i] * dq[i] - kv[i] * dk[i];
-            rpart[db][i] = kv[i] * __expf(bCv[i] - btv[i]) * ks[i];
+            rpart[jd][i] = kv[i] * __expf(bCv[i] - btv[i]) * ks[i];
         }
         if (tl < nvalid) {
             st4(a.dq + (tok0 + tl) * ldk + (size_t)h * DK + d0, dq);
@@ -796,10 +805,11 @@ __global__ __launch_bounds__(256) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     }
     // sum_s Kh[s][d] X[d][s] over this wave's 16 tokens
 #pragma unroll
-    for (int db = 0; db < DK / 16; ++db)
+    for (int jd = 0; jd < NDH; ++jd)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float x = rpart[db][i];
+            const int db = hf * NDH + jd;
+            float x = rpart[jd][i];
             x += __shfl_xor(x, 1, 64);
             x += __shfl_xor(x, 2, 64);
             x += __shfl_xor(x, 4, 64);
@@ -851,7 +861,7 @@ hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
     launch("gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sb);
     GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.dO, (const E*)L.g, (const E*)ws.hT,
                        (const E*)ws.dh, (const E*)ws.dVs, (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, L.T, L.H, L.NC};
-    launch("gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV>, gblk, dim3(256), st, ia);
+    launch("gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV>, gblk, dim3(512), st, ia);
     return hipGetLastError();
 }
 
