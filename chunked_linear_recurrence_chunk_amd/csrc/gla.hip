@@ -85,19 +85,32 @@ __device__ __forceinline__ Frag<E> ldfrag_tokcol(const E* base, size_t ld, int j
 // ---------------------------------------------------------------------------
 // Block gate cumsum b[t][d] = sum_{s <= t} g[s][d] (tokens past the end of
 // the sequence contribute 0), from a row-major g tile in LDS (pitch PG) into
-// fp32 LDS (pitch PB).  One thread per channel, tokens in order, so every
-// kernel that forms b gets bit-identical values.
+// fp32 LDS (pitch PB).  256 threads take 256 / DK token segments per channel:
+// each sums its segment in token order, then adds the totals of the earlier
+// segments in order.  The split does not depend on the work-group size, so
+// every kernel that forms b gets bit-identical values.  `seg` is 256 floats
+// of LDS scratch; all threads of the work-group must call this.
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int PG, int PB>
-__device__ __forceinline__ void gate_cumsum(const E* gs, float* bs, int nvalid) {
-    const int d = threadIdx.x;
-    if (d < DK) {
+__device__ __forceinline__ void gate_cumsum(const E* gs, float* bs, float* seg, int nvalid) {
+    constexpr int S = 256 / DK, L = BLK / S;  // segments per channel, tokens per segment
+    const int tid = threadIdx.x, d = tid % DK, sg = tid / DK;
+    if (tid < 256) {
         float run = 0.f;
-#pragma unroll 16
-        for (int t = 0; t < BLK; ++t) {
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int t = sg * L + i;
             run += t < nvalid ? to_f(gs[t * PG + d]) : 0.f;
             bs[t * PB + d] = run;
         }
+        seg[tid] = run;
+    }
+    __syncthreads();
+    if (tid < 256 && sg > 0) {
+        float off = 0.f;
+        for (int k = 0; k < sg; ++k) off += seg[k * DK + d];
+#pragma unroll
+        for (int i = 0; i < L; ++i) bs[(sg * L + i) * PB + d] += off;
     }
 }
 
@@ -166,6 +179,7 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
     __shared__ __align__(16) E Ks[BLK * PK], Gs[BLK * PK], Qs[BWD ? BLK * PK : 8];
     __shared__ __align__(16) float Bs[BLK * PB];
     __shared__ __align__(16) float zrow[DK];
+    __shared__ float seg[256];
 
     {
         const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
@@ -179,7 +193,7 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
         if (tid < DK) zrow[tid] = 0.f;
     }
     __syncthreads();
-    gate_cumsum<E, DK, PK, PB>(Gs, Bs, nvalid);
+    gate_cumsum<E, DK, PK, PB>(Gs, Bs, seg, nvalid);
     __syncthreads();
     const float* bC = Bs + (BLK - 1) * PB;
     if (tid < DK) a.eC[chunk * DK + tid] = __expf(bC[tid]);
@@ -345,19 +359,21 @@ template <typename E, int DK, int DV> struct GlaOutLds {
 };
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void gla_out_kernel(GlaOutArgs<E> a) {
+__global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     using Lay = GlaOutLds<E, DK, DV>;
-    constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, KK = DK / 32, NV = DV / 16;
-    static_assert(NV % 2 == 0, "value slices are processed in pairs");
+    constexpr int NT = 512;
+    constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, KK = DK / 32, NVH = DV / 32;  // value slices per half
     __shared__ __align__(16) char lds[Lay::total];
     __shared__ __align__(16) float zrow[DK];
+    __shared__ float seg[256];
     E* Qs = (E*)(lds + Lay::o_Q);
     E* Ks = (E*)(lds + Lay::o_K);
     float* Bs = (float*)(lds + Lay::o_B);
     E* Vs = (E*)(lds + Lay::o_V);
 
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, R = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    // wave w8: token tile R = w8 & 3, half hf = w8 >> 2 (halves split the value slices)
+    const int tid = threadIdx.x, w8 = tid >> 6, R = w8 & 3, hf = w8 >> 2, l = tid & 63, r = l & 15, g = l >> 4;
     const int T = a.T, H = a.H, NC = a.NC;
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
     const size_t chunk = ((size_t)b * H + h) * NC + n;
@@ -372,23 +388,23 @@ __global__ __launch_bounds__(256) void gla_out_kernel(GlaOutArgs<E> a) {
         for (int kk = 0; kk < KK; ++kk) fh[buf][kk] = ldfragT(hT, vb * KK + kk, l);
     };
     {
-        const auto qx = load_rows<E, BLK, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        const auto gx = load_rows<E, BLK, DK>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        load_slice(0, 0);
-        store_rows<E, BLK, DK, PK>(qx, Qs);
-        store_rows<E, BLK, DK, PK>(kx, Ks);
-        store_rows<E, BLK, DK, PK>(gx, Vs);
+        const auto qx = load_rows<E, BLK, DK, NT>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto gx = load_rows<E, BLK, DK, NT>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        load_slice(0, hf * NVH);
+        store_rows<E, BLK, DK, PK, NT>(qx, Qs);
+        store_rows<E, BLK, DK, PK, NT>(kx, Ks);
+        store_rows<E, BLK, DK, PK, NT>(gx, Vs);
         if (tid < DK) zrow[tid] = 0.f;
     }
     __syncthreads();
     if constexpr (Lay::VLDS) {
-        const auto vx = load_rows<E, BLK, DV>(vbase, ldv, nvalid);
-        gate_cumsum<E, DK, PK, PB>(Vs, Bs, nvalid);
+        const auto vx = load_rows<E, BLK, DV, NT>(vbase, ldv, nvalid);
+        gate_cumsum<E, DK, PK, PB>(Vs, Bs, seg, nvalid);
         __syncthreads();
-        store_rows<E, BLK, DV, PV>(vx, Vs);
+        store_rows<E, BLK, DV, PV, NT>(vx, Vs);
     } else {
-        gate_cumsum<E, DK, PK, PB>(Vs, Bs, nvalid);
+        gate_cumsum<E, DK, PK, PB>(Vs, Bs, seg, nvalid);
     }
     __syncthreads();
 
@@ -437,11 +453,9 @@ __global__ __launch_bounds__(256) void gla_out_kernel(GlaOutArgs<E> a) {
         if (tl < nvalid) st4(ob + (size_t)tl * ldv + 16 * vb + 4 * g, acc);
     };
 #pragma unroll
-    for (int vb = 0; vb < NV; vb += 2) {
-        load_slice(1, vb + 1);
-        compute_slice(0, vb);
-        if (vb + 2 < NV) load_slice(0, vb + 2);
-        compute_slice(1, vb + 1);
+    for (int jv = 0; jv < NVH; ++jv) {
+        if (jv + 1 < NVH) load_slice((jv + 1) & 1, hf * NVH + jv + 1);
+        compute_slice(jv & 1, hf * NVH + jv);
     }
 }
 
@@ -583,7 +597,7 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, PD = Lay::PD, KV = DV / 32, KK = DK / 32;
     static_assert(Lay::total <= 150 * 1024, "LDS budget");
     __shared__ __align__(16) char lds[Lay::total];
-    __shared__ float rsum[4][DK], rowhd[DK];
+    __shared__ float rsum[4][DK], rowhd[DK], seg[256];
     __shared__ __align__(16) float zrow[DK];
     E* Ks = (E*)(lds + Lay::o_K);
     E* Qs = (E*)(lds + Lay::o_Q);
@@ -619,7 +633,7 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     {
         const auto ox = load_rows<E, BLK, DV, NT>(dob, ldv, nvalid);
         const auto vx = load_rows<E, BLK, DV, NT>(vbase, ldv, nvalid);
-        gate_cumsum<E, DK, PK, PB>((const E*)(lds + Lay::u_G), Bs, nvalid);
+        gate_cumsum<E, DK, PK, PB>((const E*)(lds + Lay::u_G), Bs, seg, nvalid);
         __syncthreads();
         store_rows<E, BLK, DV, PV, NT>(ox, (E*)(lds + Lay::u_dO));
         store_rows<E, BLK, DV, PV, NT>(vx, (E*)(lds + Lay::u_V));
@@ -841,7 +855,7 @@ hipError_t launch_gla_fwd_t(const GlaLaunch& L, hipStream_t st) {
     launch("gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
     if (L.o) {
         GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)ws.hT, (E*)L.o, L.T, L.H, L.NC};
-        launch("gla_out", gla_out_kernel<E, DK, DV>, gblk, dim3(256), st, oa);
+        launch("gla_out", gla_out_kernel<E, DK, DV>, gblk, dim3(512), st, oa);
     }
     return hipGetLastError();
 }
