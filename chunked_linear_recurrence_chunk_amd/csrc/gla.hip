@@ -176,7 +176,8 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
     const size_t ldk = (size_t)H * DK;
     constexpr int PK = RP<E, DK>, PB = DK + 4, ND = DK / 16, KK = DK / 32;
 
-    __shared__ __align__(16) E Ks[BLK * PK], Gs[BLK * PK], Qs[BWD ? BLK * PK : 8];
+    // g is staged in the Q tile's space (Q is stored there once the cumsum is done)
+    __shared__ __align__(16) E Ks[BLK * PK], Qs[BLK * PK];
     __shared__ __align__(16) float Bs[BLK * PB];
     __shared__ __align__(16) float zrow[DK];
     __shared__ float seg[256];
@@ -184,17 +185,19 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
     {
         const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
         const auto gx = load_rows<E, BLK, DK>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        RowsRegs<E, BLK, DK> qx;
+        if constexpr (BWD) qx = load_rows<E, BLK, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
         store_rows<E, BLK, DK, PK>(kx, Ks);
-        store_rows<E, BLK, DK, PK>(gx, Gs);
-        if constexpr (BWD) {
-            const auto qx = load_rows<E, BLK, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-            store_rows<E, BLK, DK, PK>(qx, Qs);
-        }
+        store_rows<E, BLK, DK, PK>(gx, Qs);
         if (tid < DK) zrow[tid] = 0.f;
+        __syncthreads();
+        gate_cumsum<E, DK, PK, PB>(Qs, Bs, seg, nvalid);
+        __syncthreads();
+        if constexpr (BWD) {
+            store_rows<E, BLK, DK, PK>(qx, Qs);
+            __syncthreads();
+        }
     }
-    __syncthreads();
-    gate_cumsum<E, DK, PK, PB>(Gs, Bs, seg, nvalid);
-    __syncthreads();
     const float* bC = Bs + (BLK - 1) * PB;
     if (tid < DK) a.eC[chunk * DK + tid] = __expf(bC[tid]);
     // Kh^T (A: m = d, k = t) fragment (db, j) = B fragment of K * exp(b_C - b)
