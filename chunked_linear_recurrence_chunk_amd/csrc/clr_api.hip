@@ -61,6 +61,7 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     w.UtT = c.take(nb * BLK * dv * es);
     w.hT = c.take(nb * dk * dv * es);
     w.UT = c.take(nb * BLK * dv * es);
+    w.Smid = (float*)c.take((size_t)s->B * s->H * dk * dv * 4);
     if (bwd) {
         w.Rt = (float*)c.take(nb * dk * dv * 4);
         w.WT = c.take(nb * BLK * dk * es);

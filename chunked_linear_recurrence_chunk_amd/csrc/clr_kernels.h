@@ -26,6 +26,7 @@ struct GdnWs {
     void* UtT;    // [.., dv, 64]   (T Diag(beta) V)^T
     void* hT;     // [.., dv, dk]   state entering the block, transposed
     void* UT;     // [.., dv, 64]   U^T (delta-rule new values)
+    float* Smid;  // [B, H, dk, dv] state at the split point of a split forward
     // backward only
     float* Rt;    // [.., dv, dk]   R^T, R = (Diag(Gam) Q)^T dO - W^T dvloc  (fp32)
     void* WT;     // [.., dk, 64]   W^T
@@ -55,6 +56,7 @@ template <typename E> struct GdnPrepArgs {
     int T, H, NC;
     float* gam;
     E *W, *KhT, *UtT;
+    int n0 = 0;  // first block of the launch (grid x covers blocks n0 ..)
 };
 
 template <typename E> struct GdnScanArgs {
@@ -64,6 +66,7 @@ template <typename E> struct GdnScanArgs {
     float* S_out;
     E *hT, *UT;
     int H, NC, BH;
+    int n0 = 0, n1 = 1 << 30;  // blocks [n0, min(n1, NC)) are scanned
 };
 
 template <typename E> struct GdnOutArgs {
@@ -72,6 +75,7 @@ template <typename E> struct GdnOutArgs {
     const E *hT, *UT;
     E* o;
     int T, H, NC;
+    int n0 = 0;  // first block of the launch
 };
 
 hipError_t launch_gdn_fwd(const GdnLaunch& L, hipStream_t st);

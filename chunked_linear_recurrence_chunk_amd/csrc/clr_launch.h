@@ -9,7 +9,30 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 namespace clr {
+
+// Split-and-overlap forward: share of a call's blocks (per mille) in the first
+// part, 0 = no split.  Set through clr_set_fwd_split.  Off by default: each
+// dependency between the two streams' hardware queues costs 10-20 us on
+// MI355X (measured), more than the overlap can hide.
+constexpr int FWD_SPLIT_DEFAULT = 0;
+int fwd_split_permille();
+
+// The auxiliary stream of the current device and its events, held under a
+// process-wide lock for the lifetime of the guard.  `stream` stays null when
+// no auxiliary stream is available (creation failed, or `main` belongs to
+// another device); the caller then runs the unsplit schedule.
+constexpr int AUX_EVENTS = 4;
+struct AuxGuard {
+    explicit AuxGuard(hipStream_t main);
+    hipStream_t stream = nullptr;
+    hipEvent_t* ev = nullptr;
+
+  private:
+    std::lock_guard<std::mutex> lk_;
+};
 
 bool timing_on();
 // Returns false if events could not be obtained (then the launch is untimed).

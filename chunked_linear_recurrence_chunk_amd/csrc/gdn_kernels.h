@@ -159,7 +159,7 @@ __device__ __forceinline__ void st_fragT(float* base, int f, int l, const Frag<f
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int n = a.n0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
     const int T = a.T, H = a.H, NC = a.NC;
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;  // first token (b, n*64)
@@ -442,6 +442,8 @@ template <typename E, int DK, int DV, bool HNAT> struct ScanFwdGeom {
 template <typename E, int DK, int DV, bool HNAT>
 __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int wgi, char* smem) {
     const int H = a.H, NC = a.NC;
+    // blocks n0 .. n0 + NB - 1 of each head are scanned (ring index j = n - n0)
+    const int n0 = a.n0, NB = (a.n1 < NC ? a.n1 : NC) - a.n0;
     int b, h, vb;
     if (!scan_coords(wgi, DV / 16, a.BH, H, b, h, vb)) return;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
@@ -457,7 +459,7 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
     if (w > 0) {  // producers
         const int pid = w - 1;
         auto issue = [&](int n) {
-            const size_t c = bh * NC + n;
+            const size_t c = bh * NC + n0 + n;
             const E* W = a.W + c * BLK * DK + l * LE;
             const E* KhT = a.KhT + c * BLK * DK + l * LE;
             const E* UtT = a.UtT + c * BLK * DV + (size_t)(2 * vb * UPF) * UE + l * LE;
@@ -468,13 +470,13 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
             };
             ring_issue<NU>(ring + (n % P) * G::SLOT, pid, src, a.gam + c * BLK + l);
         };
-        const int pre = NC < P - 1 ? NC : P - 1;
+        const int pre = NB < P - 1 ? NB : P - 1;
         for (int n = 0; n < pre; ++n) issue(n);
         ring_wait<G::NU_MIN>(pre - 1);  // block 0 has landed
         ring_barrier();
-        for (int n = 0; n < NC; ++n) {
-            if (n + P - 1 < NC) issue(n + P - 1);
-            const int last = (n + P - 1 < NC ? n + P - 1 : NC - 1);
+        for (int n = 0; n < NB; ++n) {
+            if (n + P - 1 < NB) issue(n + P - 1);
+            const int last = (n + P - 1 < NB ? n + P - 1 : NB - 1);
             ring_wait<G::NU_MIN>(last - (n + 1));  // block n + 1 has landed
             ring_barrier();
         }
@@ -488,11 +490,11 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[db][i] = Sin ? Sin[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
     ring_barrier();
-    for (int n = 0; n < NC; ++n) {
+    for (int n = 0; n < NB; ++n) {
         ScanFwdOps<E, DK> o;
         const char* slot = ring + (n % P) * G::SLOT;
         scan_fwd_from_ring<E, DK, NU>(o, slot, l);
-        scan_fwd_step<E, DK, DV, HNAT, NU>(o, S, a, bh * NC + n, vb, l, tile, slot);
+        scan_fwd_step<E, DK, DV, HNAT, NU>(o, S, a, bh * NC + n0 + n, vb, l, tile, slot);
         ring_barrier();
     }
     if (a.S_out) {
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int n = a.n0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
     const int T = a.T, H = a.H, NC = a.NC;
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;

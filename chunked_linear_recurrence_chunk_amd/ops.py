@@ -60,6 +60,10 @@ def load(path: Optional[str] = None):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 15 + [sz, vp]
         f.restype = i
+    lib.clr_set_fwd_split.argtypes = [i]
+    lib.clr_set_fwd_split.restype = i
+    lib.clr_get_fwd_split.argtypes = []
+    lib.clr_get_fwd_split.restype = i
     lib.clr_status_string.argtypes = [i]
     lib.clr_status_string.restype = ctypes.c_char_p
     lib.clr_version.argtypes = []
@@ -127,6 +131,16 @@ def _check_inputs(*ts):
             raise ValueError("tensors must be on the GPU")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def set_fwd_split(permille: int) -> None:
+    """Split point of the split-and-overlap GDN forward (per mille of the
+    blocks in the first part; 0 disables the split)."""
+    _check("clr_set_fwd_split", load().clr_set_fwd_split(int(permille)))
+
+
+def get_fwd_split() -> int:
+    return int(load().clr_get_fwd_split())
 
 
 def timing_enable(on: bool = True) -> None:

@@ -41,11 +41,15 @@
  * Ownership and execution
  * -----------------------
  * The caller allocates every buffer, including the workspace `ws` of at least
- * clr_workspace_bytes() bytes (256-byte aligned).  The library allocates
- * nothing, keeps no state between calls and is re-entrant; calls are enqueued
- * asynchronously on `stream` (a hipStream_t; NULL = the default stream).
+ * clr_workspace_bytes() bytes (256-byte aligned).  The library allocates no
+ * device memory and is re-entrant; calls are enqueued asynchronously on
+ * `stream` (a hipStream_t of the current device; NULL = the default stream).
  * Inputs are never modified; outputs are overwritten.  Calls that share a
- * workspace must be ordered on one stream.
+ * workspace must be ordered on one stream.  The only state kept between calls
+ * is the split setting below and, per device, one auxiliary stream with four
+ * events that the split forward creates on first use (kept until exit); work
+ * put on it is joined back into `stream` before the call's last operation, so
+ * ordering on `stream` alone remains sufficient for the caller.
  * Nullable: S_in (zero state), dS_out (zero), S_out (not wanted), o (not
  * wanted; GDN/GLA fwd).
  *
@@ -118,6 +122,20 @@ int gla_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* 
             const void* g, const void* beta, const float* S_in, const void* dO,
             const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
             float* dS_in, void* ws, size_t ws_bytes, void* stream);
+
+/* Split-and-overlap forward (StateFlow paper, Sec. 3.4.2, "Split and
+ * Overlap", forward wavefront).  gdn_fwd with o != NULL and at least 16
+ * 64-token blocks splits its blocks into two parts at `permille`/1000 of the
+ * blocks (each part keeps at least 8) and runs
+ *     Pre(1) -> (ST(1) || Pre(2)) -> (ST(2) || Out(1)) -> Out(2)
+ * with the bracketed pairs on `stream` and the auxiliary stream.  The results
+ * are bit-identical to the unsplit schedule.  permille = 0 disables the split
+ * and is the default: on MI355X each wait between the two streams costs
+ * 10-20 us, more than the overlap hides at the supported sizes (opt in to
+ * measure it).  Process-global.  Returns CLR_EINVAL unless
+ * 0 <= permille < 1000.  clr_get_fwd_split returns the current value. */
+int clr_set_fwd_split(int permille);
+int clr_get_fwd_split(void);
 
 /* Human-readable text of a status code (static storage). */
 const char* clr_status_string(int status);

@@ -45,6 +45,22 @@ def _shape(ops, B=1, T=128, H=2, dk=128, dv=128, dtype=1):
     return ops.ClrShape(B, T, H, dk, dv, dtype)
 
 
+def test_fwd_split_setting():
+    ops, lib = _lib()
+    old = ops.get_fwd_split()
+    assert 0 <= old < 1000
+    assert lib.clr_set_fwd_split(-1) == ops.CLR_EINVAL
+    assert lib.clr_set_fwd_split(1000) == ops.CLR_EINVAL
+    assert ops.get_fwd_split() == old
+    try:
+        ops.set_fwd_split(0)
+        assert ops.get_fwd_split() == 0
+        ops.set_fwd_split(250)
+        assert ops.get_fwd_split() == 250
+    finally:
+        ops.set_fwd_split(old)
+
+
 def test_workspace_sizes():
     ops, lib = _lib()
     s = _shape(ops)

@@ -75,6 +75,55 @@ def test_gdn_fwd_slow_decay_bf16():
     assert rel_err(S, S_ref) < tol("bf16", "S_out")
 
 
+SPLIT_CASES = [
+    # (B, T, H, dk, dv, dtype, seed, split per mille)
+    (1, 1024, 2, 128, 128, "bf16", 21, 500),   # 16 blocks: the smallest split
+    (2, 1500, 3, 64, 64, "bf16", 22, 500),     # ragged last block in part 2
+    (1, 2048, 16, 128, 128, "bf16", 23, 250),
+    (1, 2048, 16, 128, 128, "bf16", 23, 750),
+    (1, 1100, 2, 32, 32, "fp32", 24, 500),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"B{c[0]}T{c[1]}H{c[2]}d{c[3]}-{c[5]}-s{c[7]}" for c in SPLIT_CASES])
+def test_gdn_fwd_split_is_bit_identical(case):
+    """The split-and-overlap forward gives the unsplit forward's bits."""
+    import torch
+    from chunked_linear_recurrence_chunk_amd import inputs
+    ops = _ops()
+    B, T, H, dk, dv, dtype, seed, pm = case
+    print(f"[gdn fwd split] case {case}", flush=True)
+    x = inputs.make_gdn(B, T, H, dk, dv, dtype, seed)
+    old = ops.get_fwd_split()
+    try:
+        ops.set_fwd_split(0)
+        o0, S0 = _run_fwd(x, dtype)
+        ops.set_fwd_split(pm)
+        o1, S1 = _run_fwd(x, dtype)
+        o2, S2 = _run_fwd(x, dtype)  # again: the auxiliary stream is reused
+    finally:
+        ops.set_fwd_split(old)
+    torch.cuda.synchronize()
+    assert np.array_equal(o0, o1) and np.array_equal(S0, S1)
+    assert np.array_equal(o0, o2) and np.array_equal(S0, S2)
+
+
+def test_gdn_fwd_split_matches_oracle():
+    from chunked_linear_recurrence_chunk_amd import inputs
+    from oracle import oracle
+    ops = _ops()
+    x = inputs.make_gdn(2, 1500, 3, 64, 64, "bf16", 25)
+    old = ops.get_fwd_split()
+    try:
+        ops.set_fwd_split(400)
+        o, S = _run_fwd(x, "bf16")
+    finally:
+        ops.set_fwd_split(old)
+    o_ref, S_ref = oracle.gdn_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S_in"])
+    assert rel_err(o, o_ref) < tol("bf16", "o"), rel_err(o, o_ref)
+    assert rel_err(S, S_ref) < tol("bf16", "S_out"), rel_err(S, S_ref)
+
+
 def _run_bwd(x, dtype, with_dS=True):
     ops = _ops()
     d = {k: to_dev(x[k], dtype) for k in ("q", "k", "v", "g", "beta", "dO")}
