@@ -16,12 +16,14 @@
  *     - Gated DeltaNet: F_t is scalar-plus-low-rank,
  *         F_t = alpha_t (I - beta_t k_t k_t^T),  write term beta_t v_t k_t^T;
  *     - Gated Linear Attention: per-key-channel (diagonal) decay alpha_t,
- *         write term v_t k_t^T.
+ *         write term v_t k_t^T;
+ *     - Mamba-2: F_t is a scalar times the identity, write term v_t k_t^T.
  *   Here the state is stored key-major, S in R^{dk x dv} (the transpose of the
  *   paper's value-major S), so the same maps read
- *     GDN: S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
- *     GLA: S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T
- *     both: o_t = S_t^T q_t,   alpha_t = exp(g_t)  (g = log alpha <= 0).
+ *     GDN:     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     GLA:     S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T     (alpha_t in R^dk)
+ *     Mamba-2: S_t = alpha_t S_{t-1} + k_t v_t^T            (alpha_t scalar)
+ *     all: o_t = S_t^T q_t,   alpha_t = exp(g_t)  (g = log alpha <= 0).
  *
  *   The chunk entry points take a boundary state S_in and return S_out (the
  *   chunk forward of the StateFlow paper, Sec. 3.1, "Forward Computation"),
@@ -44,7 +46,7 @@
  * Layouts (all contiguous, row-major, fp64, host memory):
  *   q, k        [B, T, H, dk]
  *   v, o, dO    [B, T, H, dv]
- *   g           GDN: [B, T, H]       GLA: [B, T, H, dk]
+ *   g           GDN, Mamba-2: [B, T, H]       GLA: [B, T, H, dk]
  *   beta        GDN: [B, T, H]       (GLA has none)
  *   S_in, S_out, dS_in, dS_out   [B, H, dk, dv]
  * S_in / dS_out may be NULL (zero); S_out may be NULL (not wanted).
@@ -428,6 +430,145 @@ int ref_gla_bwd(int B, int T, int H, int dk, int dv,
                               g + tok(b, t, h, T, H, dk), dk, dv,
                               dq + tok(b, t, h, T, H, dk), dk_ + tok(b, t, h, T, H, dk),
                               dv_ + tok(b, t, h, T, H, dv), dg + tok(b, t, h, T, H, dk));
+            }
+        }
+        memcpy(dS_in + st(b, h, H, dk, dv), dS, ns * sizeof(double));
+        free(ck); free(seg); free(dS);
+    }
+    return fail ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Mamba-2 (scalar gate, no delta term)                                       */
+/* ------------------------------------------------------------------------ */
+
+/* S <- exp(g) S + k v^T  (one scalar decay for the whole state) */
+static void m2_token_fwd(double *S, const double *kt, const double *vt,
+                         double gt, int dk, int dv)
+{
+    const double al = exp(gt);
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j)
+            S[(size_t)i * dv + j] = al * S[(size_t)i * dv + j] + kt[i] * vt[j];
+}
+
+int ref_m2_fwd(int B, int T, int H, int dk, int dv,
+               const double *q, const double *k, const double *v,
+               const double *g, const double *S_in, double *o, double *S_out)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
+    if (!q || !k || !v || !g || !o) return -1;
+    const size_t ns = (size_t)dk * dv;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(ref_get_max_threads()) reduction(|:fail)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        double *S = (double *)malloc(ns * sizeof(double));
+        if (!S) { fail |= 1; continue; }
+        load_state(S, S_in, st(b, h, H, dk, dv), ns);
+        for (int t = 0; t < T; ++t) {
+            m2_token_fwd(S, k + tok(b, t, h, T, H, dk), v + tok(b, t, h, T, H, dv),
+                         g[hd(b, t, h, T, H)], dk, dv);
+            out_token(S, q + tok(b, t, h, T, H, dk), dk, dv, o + tok(b, t, h, T, H, dv));
+        }
+        if (S_out) memcpy(S_out + st(b, h, H, dk, dv), S, ns * sizeof(double));
+        free(S);
+    }
+    return fail ? -1 : 0;
+}
+
+/*
+ * Reverse-mode step for one token, S_t = alpha S_{t-1} + k v^T, o = S_t^T q:
+ *   dS_t     += q do^T ;  dq = S_t do
+ *   dk        = dS_t v ;  dv = dS_t^T k
+ *   dalpha    = <dS_t, S_{t-1}>_F ,  dg = alpha dalpha
+ *   dS_{t-1}  = alpha dS_t
+ */
+static void m2_token_bwd(double *dS, const double *Sp, const double *St,
+                         const double *qt, const double *kt, const double *vt,
+                         const double *dot, double gt, int dk, int dv,
+                         double *dqt, double *dkt, double *dvt, double *dgt)
+{
+    const double al = exp(gt);
+    for (int i = 0; i < dk; ++i) {
+        double *dSi = dS + (size_t)i * dv;
+        const double *Si = St + (size_t)i * dv;
+        double acc = 0.0;
+        for (int j = 0; j < dv; ++j) {
+            dSi[j] += qt[i] * dot[j];
+            acc += Si[j] * dot[j];
+        }
+        dqt[i] = acc;
+    }
+    /* dk_i = sum_j dS[i,j] v_j */
+    for (int i = 0; i < dk; ++i) {
+        double x = 0.0;
+        for (int j = 0; j < dv; ++j) x += dS[(size_t)i * dv + j] * vt[j];
+        dkt[i] = x;
+    }
+    /* dv_j = sum_i dS[i,j] k_i */
+    for (int j = 0; j < dv; ++j) {
+        double y = 0.0;
+        for (int i = 0; i < dk; ++i) y += dS[(size_t)i * dv + j] * kt[i];
+        dvt[j] = y;
+    }
+    /* dg = alpha <dS_t, S_{t-1}>_F */
+    double frob = 0.0;
+    for (size_t e = 0; e < (size_t)dk * dv; ++e) frob += dS[e] * Sp[e];
+    *dgt = al * frob;
+    for (size_t e = 0; e < (size_t)dk * dv; ++e) dS[e] *= al;
+}
+
+int ref_m2_bwd(int B, int T, int H, int dk, int dv,
+               const double *q, const double *k, const double *v,
+               const double *g, const double *S_in, const double *dO,
+               const double *dS_out, double *dq, double *dk_, double *dv_,
+               double *dg, double *dS_in)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
+    if (!q || !k || !v || !g || !dO) return -1;
+    if (!dq || !dk_ || !dv_ || !dg || !dS_in) return -1;
+    const size_t ns = (size_t)dk * dv;
+    const int nck = T / CKPT + 1;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(ref_get_max_threads()) reduction(|:fail)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        double *ck = (double *)malloc((size_t)nck * ns * sizeof(double));
+        double *seg = (double *)malloc((size_t)(CKPT + 1) * ns * sizeof(double));
+        double *dS = (double *)malloc(ns * sizeof(double));
+        if (!ck || !seg || !dS) {
+            free(ck); free(seg); free(dS);
+            fail |= 1;
+            continue;
+        }
+        double *S = seg;
+        load_state(S, S_in, st(b, h, H, dk, dv), ns);
+        for (int t = 0; t < T; ++t) {
+            if (t % CKPT == 0) memcpy(ck + (size_t)(t / CKPT) * ns, S, ns * sizeof(double));
+            m2_token_fwd(S, k + tok(b, t, h, T, H, dk), v + tok(b, t, h, T, H, dv),
+                         g[hd(b, t, h, T, H)], dk, dv);
+        }
+        if (dS_out) memcpy(dS, dS_out + st(b, h, H, dk, dv), ns * sizeof(double));
+        else memset(dS, 0, ns * sizeof(double));
+        const int nseg = (T + CKPT - 1) / CKPT;
+        for (int sgi = nseg - 1; sgi >= 0; --sgi) {
+            const int t0 = sgi * CKPT;
+            const int t1 = (t0 + CKPT < T) ? t0 + CKPT : T;
+            memcpy(seg, ck + (size_t)sgi * ns, ns * sizeof(double));
+            for (int t = t0; t < t1; ++t) {
+                double *nx = seg + (size_t)(t - t0 + 1) * ns;
+                memcpy(nx, seg + (size_t)(t - t0) * ns, ns * sizeof(double));
+                m2_token_fwd(nx, k + tok(b, t, h, T, H, dk), v + tok(b, t, h, T, H, dv),
+                             g[hd(b, t, h, T, H)], dk, dv);
+            }
+            for (int t = t1 - 1; t >= t0; --t) {
+                m2_token_bwd(dS, seg + (size_t)(t - t0) * ns, seg + (size_t)(t - t0 + 1) * ns,
+                             q + tok(b, t, h, T, H, dk), k + tok(b, t, h, T, H, dk),
+                             v + tok(b, t, h, T, H, dv), dO + tok(b, t, h, T, H, dv),
+                             g[hd(b, t, h, T, H)], dk, dv,
+                             dq + tok(b, t, h, T, H, dk), dk_ + tok(b, t, h, T, H, dk),
+                             dv_ + tok(b, t, h, T, H, dv), dg + hd(b, t, h, T, H));
             }
         }
         memcpy(dS_in + st(b, h, H, dk, dv), dS, ns * sizeof(double));

@@ -9,7 +9,8 @@ adjoints; see that file's header for the definitions and their source in the
 StateFlow paper, Sec. 2.1 Eq. 1 and Sec. 3.1).  All arrays are numpy float64,
 contiguous, in the layouts
 
-    q, k [B,T,H,dk]; v, o, dO [B,T,H,dv]; g: GDN [B,T,H], GLA [B,T,H,dk];
+    q, k [B,T,H,dk]; v, o, dO [B,T,H,dv]; g: GDN and Mamba-2 [B,T,H],
+    GLA [B,T,H,dk];
     beta [B,T,H]; states S_in, S_out, dS_in, dS_out [B,H,dk,dv].
 
 ``build()`` compiles the C file with gcc into ``oracle/_build``.
@@ -65,7 +66,10 @@ def load(path: Optional[str] = None):
     lib.ref_gdn_bwd.argtypes = [i] * 5 + [dp] * 14
     lib.ref_gla_fwd.argtypes = [i] * 5 + [dp] * 7
     lib.ref_gla_bwd.argtypes = [i] * 5 + [dp] * 12
-    for f in (lib.ref_gdn_fwd, lib.ref_gdn_bwd, lib.ref_gla_fwd, lib.ref_gla_bwd):
+    lib.ref_m2_fwd.argtypes = [i] * 5 + [dp] * 7
+    lib.ref_m2_bwd.argtypes = [i] * 5 + [dp] * 12
+    for f in (lib.ref_gdn_fwd, lib.ref_gdn_bwd, lib.ref_gla_fwd, lib.ref_gla_bwd,
+              lib.ref_m2_fwd, lib.ref_m2_bwd):
         f.restype = ctypes.c_int
     lib.ref_set_threads.argtypes = [i]
     lib.ref_set_threads.restype = None
@@ -162,6 +166,35 @@ def gla_bwd(q, k, v, g, S_in, dO, dS_out=None, lib=None):
     return r
 
 
+def mamba2_fwd(q, k, v, g, S_in=None, lib=None):
+    """Scalar-gate (Mamba-2) chunk forward, g [B,T,H]: returns (o, S_out)."""
+    lib = lib or load()
+    q, k, v, g, S_in = map(_c, (q, k, v, g, S_in))
+    B, T, H, dk, dv = _dims(q, v)
+    o = np.zeros((B, T, H, dv))
+    S_out = np.zeros((B, H, dk, dv))
+    rc = lib.ref_m2_fwd(B, T, H, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(S_in),
+                        _p(o), _p(S_out))
+    if rc != 0:
+        raise RuntimeError("ref_m2_fwd failed")
+    return o, S_out
+
+
+def mamba2_bwd(q, k, v, g, S_in, dO, dS_out=None, lib=None):
+    """Scalar-gate (Mamba-2) chunk backward: returns dict dq, dk, dv, dg, dS_in."""
+    lib = lib or load()
+    q, k, v, g, S_in, dO, dS_out = map(_c, (q, k, v, g, S_in, dO, dS_out))
+    B, T, H, dk, dv = _dims(q, v)
+    r = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+             dg=np.zeros((B, T, H)), dS_in=np.zeros((B, H, dk, dv)))
+    rc = lib.ref_m2_bwd(B, T, H, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(S_in),
+                        _p(dO), _p(dS_out), _p(r["dq"]), _p(r["dk"]), _p(r["dv"]),
+                        _p(r["dg"]), _p(r["dS_in"]))
+    if rc != 0:
+        raise RuntimeError("ref_m2_bwd failed")
+    return r
+
+
 # ---------------------------------------------------------------------------
 # Sequence-chunk chaining (StateFlow paper, Sec. 3.1, Eqs. 3, 4 and 6, with
 # the chain rules S_{i+1}^in = S_i^out and dS_i^out = dS_{i+1}^in).
@@ -215,6 +248,29 @@ def gla_chunked(q, k, v, g, S_in, dO, dS_out, N, lib=None):
     for i in reversed(range(N)):
         a, b = bounds[i]
         r = gla_bwd(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b], states[i], dO[:, a:b], dS, lib=lib)
+        parts[i] = r
+        dS = r["dS_in"]
+    grads = {key: np.concatenate([p[key] for p in parts], axis=1)
+             for key in ("dq", "dk", "dv", "dg")}
+    grads["dS_in"] = dS
+    return np.concatenate(outs, axis=1), S_out, grads
+
+
+def mamba2_chunked(q, k, v, g, S_in, dO, dS_out, N, lib=None):
+    B, T, H, dk, dv = _dims(q, v)
+    bounds = _split_bounds(T, N)
+    S = S_in
+    states, outs = [], []
+    for a, b in bounds:
+        states.append(S)
+        o_i, S = mamba2_fwd(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b], S, lib=lib)
+        outs.append(o_i)
+    S_out = S
+    dS = dS_out
+    parts = [None] * N
+    for i in reversed(range(N)):
+        a, b = bounds[i]
+        r = mamba2_bwd(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b], states[i], dO[:, a:b], dS, lib=lib)
         parts[i] = r
         dS = r["dS_in"]
     grads = {key: np.concatenate([p[key] for p in parts], axis=1)

@@ -28,6 +28,14 @@ MUTANTS = [
     ("gla: dv wrong index", "dvt[j] += dSi[j] * kt[i];", "dvt[j] += dSi[j] * kt[j % dk];"),
     ("gla: dg missing alpha", "dgt[i] = al * frob;", "dgt[i] = frob;"),
     ("gla: decay on write", "Si[j] = al * Si[j] + kt[i] * vt[j];", "Si[j] = al * (Si[j] + kt[i] * vt[j]);"),
+    ("m2: dg missing alpha", "*dgt = al * frob;", "*dgt = frob;"),
+    ("m2: decay on write", "S[(size_t)i * dv + j] = al * S[(size_t)i * dv + j] + kt[i] * vt[j];",
+     "S[(size_t)i * dv + j] = al * (S[(size_t)i * dv + j] + kt[i] * vt[j]);"),
+    ("m2: dv transposed", "for (int i = 0; i < dk; ++i) y += dS[(size_t)i * dv + j] * kt[i];",
+     "for (int i = 0; i < dk; ++i) y += dS[(size_t)i * dv + j] * kt[j % dk];"),
+    ("m2: dS_{t-1} not decayed", "for (size_t e = 0; e < (size_t)dk * dv; ++e) dS[e] *= al;",
+     "for (size_t e = 0; e < (size_t)dk * dv; ++e) dS[e] *= 1.0;"),
+    ("m2: dk uses S_{t-1} adjoint before the q term", "dkt[i] = x;\n    }\n    /* dv_j", "dkt[i] = -x;\n    }\n    /* dv_j"),
     ("bwd: checkpoint off by one token", "if (t % CKPT == 0) memcpy(ck + (size_t)(t / CKPT) * ns, S, ns * sizeof(double));\n            gdn_token_fwd",
      "if (t % CKPT == 1 || t == 0) memcpy(ck + (size_t)(t / CKPT) * ns, S, ns * sizeof(double));\n            gdn_token_fwd"),
 ]
@@ -38,13 +46,16 @@ def _pins_pass(lib):
     from tests import test_oracle_fd as fd
     rng = np.random.default_rng(3)
     ok = True
-    for kind in ("gdn", "gla"):
+    for kind in ("gdn", "gla", "m2"):
         for shape in [(1, 6, 1, 3, 2), (1, 70, 1, 2, 2)]:
             B, T, H, dk, dv = shape
             if kind == "gdn":
                 x = fd._rand_gdn(rng, *shape)
+            elif kind == "gla":
+                x = fd._rand_gla(rng, *shape)
             else:
                 x = fd._rand_gla(rng, *shape)
+                x["g"] = x["g"][..., 0].copy()
             dO = rng.standard_normal((B, T, H, dv))
             dS = rng.standard_normal((B, H, dk, dv))
             if kind == "gdn":
@@ -54,10 +65,13 @@ def _pins_pass(lib):
                 r = oracle.gdn_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S_in"], dO, dS, lib=lib)
                 names = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", S_in="dS_in")
             else:
-                def loss(xx, a, b):
-                    o, S = oracle.gla_fwd(xx["q"], xx["k"], xx["v"], xx["g"], xx["S_in"], lib=lib)
+                fwd = oracle.gla_fwd if kind == "gla" else oracle.mamba2_fwd
+                bwd = oracle.gla_bwd if kind == "gla" else oracle.mamba2_bwd
+
+                def loss(xx, a, b, fwd=fwd):
+                    o, S = fwd(xx["q"], xx["k"], xx["v"], xx["g"], xx["S_in"], lib=lib)
                     return float(np.sum(o * a) + np.sum(S * b))
-                r = oracle.gla_bwd(x["q"], x["k"], x["v"], x["g"], x["S_in"], dO, dS, lib=lib)
+                r = bwd(x["q"], x["k"], x["v"], x["g"], x["S_in"], dO, dS, lib=lib)
                 names = dict(q="dq", k="dk", v="dv", g="dg", S_in="dS_in")
             for key, gname in names.items():
                 f = fd._fd(loss, x, key, dO, dS)
