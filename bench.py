@@ -52,19 +52,24 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
         "gdn_scan_bwd": (C * f4 + 2 * Ck * es + kv * f4 + Cv * es + kv * es + Cv * es, 2 * (2 * C * kv)),
         "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 2 * kv * es + 2 * Cv * es + 3 * Ck * es + 2 * C * es,
                           3 * (2 * C * kv) + 11 * (2 * CC * dk) + 2 * (2 * C ** 3) + 2 * CC * dk),
-        # GLA
-        "gla_prep": (2 * Ck * es + dk * f4 + Ck * es, 0),
-        "gla_prep_bwd": (3 * Ck * es + dk * f4 + 3 * Ck * es, 0),
-        "gla_scan_fwd": (Ck * es + Cv * es + dk * f4 + kv * es, 2 * C * kv),
-        "gla_out": (2 * Ck * es + Cv * es + Ck * es + kv * es + Cv * es, 2 * CC * dk + 2 * C * kv + 2 * CC * dv),
-        "gla_scan_bwd": (2 * Ck * es + Cv * es + dk * f4 + kv * es + Cv * es, 2 * (2 * C * kv)),
-        "gla_bwd_intra": (2 * Ck * es + 2 * Cv * es + Ck * es + 2 * kv * es + Cv * es + 2 * Ck * es + Cv * es + Ck * es,
-                          2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv),
     }
+    # GLA (per-channel gate, gk = dk gate values per token) and its scalar-gate
+    # Mamba-2 member on the same kernels (gk = 1)
+    for pre, gk in (("gla", dk), ("m2", 1)):
+        Cg = C * gk
+        W[pre + "_prep"] = (Ck * es + Cg * es + dk * f4 + Ck * es, 0)
+        W[pre + "_prep_bwd"] = (2 * Ck * es + Cg * es + dk * f4 + 3 * Ck * es, 0)
+        W[pre + "_scan_fwd"] = (Ck * es + Cv * es + dk * f4 + kv * es, 2 * C * kv)
+        W[pre + "_out"] = (2 * Ck * es + Cv * es + Cg * es + kv * es + Cv * es,
+                           2 * CC * dk + 2 * C * kv + 2 * CC * dv)
+        W[pre + "_scan_bwd"] = (2 * Ck * es + Cv * es + dk * f4 + kv * es + Cv * es, 2 * (2 * C * kv))
+        W[pre + "_bwd_intra"] = (2 * Ck * es + 2 * Cv * es + Cg * es + 2 * kv * es + Cv * es + 2 * Ck * es
+                                 + Cv * es + Cg * es,
+                                 2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv)
+        W[pre + "_scan_fwd_rec"] = W[pre + "_scan_fwd"]
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
     # one launch running the forward recompute and the reverse scan side by side
     W["gdn_scan_pair"] = tuple(x + y for x, y in zip(W["gdn_scan_fwd"], W["gdn_scan_bwd"]))
-    W["gla_scan_fwd_rec"] = W["gla_scan_fwd"]
     return W.get(name)
 
 
@@ -110,8 +115,10 @@ def cpu_baseline(cfg: dict, x: dict, budget_chunks: int):
     def once():
         if cfg["kind"] == "gdn":
             oracle.gdn_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], None, n)
-        else:
+        elif cfg["kind"] == "gla":
             oracle.gla_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], None, n)
+        else:
+            oracle.mamba2_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], None, n)
     t0 = time.perf_counter()
     once()
     reps, dt = 1, time.perf_counter() - t0
@@ -174,8 +181,10 @@ def main():
     S_in = dev(x["S_in"], "fp32")
     if cfg["kind"] == "gdn":
         drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
-    else:
+    elif cfg["kind"] == "gla":
         drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
+    else:
+        drv = stateflow.Mamba2Chunked(d["q"], d["k"], d["v"], d["g"], N)
     o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device="cuda")
     grads = {k: torch.empty_like(d[k.replace("d", "", 1)] if k != "dbeta" else d["beta"])
              for k in (("dq", "dk", "dv", "dg", "dbeta") if cfg["kind"] == "gdn" else ("dq", "dk", "dv", "dg"))}

@@ -146,9 +146,10 @@ const char* clr_status_string(int s) {
 }
 
 size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
-    const bool gla = (op == CLR_OP_GLA_FWD || op == CLR_OP_GLA_BWD);
-    if (op < CLR_OP_GDN_FWD || op > CLR_OP_GLA_BWD) return 0;
-    const bool bwd = (op == CLR_OP_GDN_BWD || op == CLR_OP_GLA_BWD);
+    if (op < CLR_OP_GDN_FWD || op > CLR_OP_M2_BWD) return 0;
+    // the Mamba-2 member runs on the GLA kernels
+    const bool gla = op != CLR_OP_GDN_FWD && op != CLR_OP_GDN_BWD;
+    const bool bwd = op == CLR_OP_GDN_BWD || op == CLR_OP_GLA_BWD || op == CLR_OP_M2_BWD;
     if (check_shape(s, gla, bwd) != CLR_OK) return 0;
     size_t total = 0;
     if (gla) carve_gla(s, bwd, nullptr, &total);
@@ -156,9 +157,13 @@ size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
     return total;
 }
 
-static int fwd_common(bool gla, const clr_shape_t* s, const void* q, const void* k, const void* v,
+// Which member of the family an entry point computes.
+enum Kind { K_GDN, K_GLA, K_M2 };
+
+static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void* k, const void* v,
                       const void* g, const void* beta, const float* S_in, void* o, float* S_out,
                       void* ws, size_t ws_bytes, void* stream) {
+    const bool gla = kind != K_GDN;
     int rc = check_shape(s, gla, false);
     if (rc) return rc;
     if (!q || !k || !v || !g) return CLR_EINVAL;
@@ -166,7 +171,7 @@ static int fwd_common(bool gla, const clr_shape_t* s, const void* q, const void*
     const size_t es = esize(s->dtype);
     const size_t ntok = (size_t)s->B * s->T * s->H, nst = (size_t)s->B * s->H * s->dk * s->dv;
     Buf bufs[] = {{q, ntok * s->dk * es, false}, {k, ntok * s->dk * es, false},
-                  {v, ntok * s->dv * es, false}, {g, ntok * (gla ? s->dk : 1) * es, false},
+                  {v, ntok * s->dv * es, false}, {g, ntok * (kind == K_GLA ? s->dk : 1) * es, false},
                   {beta, ntok * es, false},      {S_in, nst * 4, false},
                   {o, ntok * s->dv * es, true},  {S_out, nst * 4, true},
                   {ws, ws_bytes, true}};
@@ -189,6 +194,7 @@ static int fwd_common(bool gla, const clr_shape_t* s, const void* q, const void*
         GlaLaunch L{};
         L.B = s->B; L.T = s->T; L.H = s->H; L.NC = NC; L.dk = s->dk; L.dv = s->dv;
         L.bf16 = s->dtype == CLR_BF16;
+        L.scalar_gate = kind == K_M2;
         L.q = q; L.k = k; L.v = v; L.g = g; L.S_in = S_in; L.o = o; L.S_out = S_out;
         L.ws = carve_gla(s, false, (char*)ws, nullptr);
         return hip_status(launch_gla_fwd(L, st));
@@ -198,19 +204,26 @@ static int fwd_common(bool gla, const clr_shape_t* s, const void* q, const void*
 int gdn_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
             const void* beta, const float* S_in, void* o, float* S_out, void* ws, size_t ws_bytes,
             void* stream) {
-    return fwd_common(false, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream);
+    return fwd_common(K_GDN, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream);
 }
 
 int gla_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
             const void* beta, const float* S_in, void* o, float* S_out, void* ws, size_t ws_bytes,
             void* stream) {
-    return fwd_common(true, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream);
+    return fwd_common(K_GLA, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream);
 }
 
-static int bwd_common(bool gla, const clr_shape_t* s, const void* q, const void* k, const void* v,
+int mamba2_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+               const void* beta, const float* S_in, void* o, float* S_out, void* ws, size_t ws_bytes,
+               void* stream) {
+    return fwd_common(K_M2, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream);
+}
+
+static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void* k, const void* v,
                       const void* g, const void* beta, const float* S_in, const void* dO,
                       const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
                       float* dS_in, void* ws, size_t ws_bytes, void* stream) {
+    const bool gla = kind != K_GDN;
     int rc = check_shape(s, gla, true);
     if (rc) return rc;
     if (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg || !dS_in) return CLR_EINVAL;
@@ -218,7 +231,7 @@ static int bwd_common(bool gla, const clr_shape_t* s, const void* q, const void*
         return CLR_EINVAL;
     const size_t es = esize(s->dtype);
     const size_t ntok = (size_t)s->B * s->T * s->H, nst = (size_t)s->B * s->H * s->dk * s->dv;
-    const size_t gn = ntok * (gla ? s->dk : 1) * es;
+    const size_t gn = ntok * (kind == K_GLA ? s->dk : 1) * es;
     Buf bufs[] = {{q, ntok * s->dk * es, false},  {k, ntok * s->dk * es, false},
                   {v, ntok * s->dv * es, false},  {g, gn, false},
                   {beta, ntok * es, false},       {S_in, nst * 4, false},
@@ -246,6 +259,7 @@ static int bwd_common(bool gla, const clr_shape_t* s, const void* q, const void*
         GlaLaunch L{};
         L.B = s->B; L.T = s->T; L.H = s->H; L.NC = NC; L.dk = s->dk; L.dv = s->dv;
         L.bf16 = s->dtype == CLR_BF16;
+        L.scalar_gate = kind == K_M2;
         L.q = q; L.k = k; L.v = v; L.g = g; L.S_in = S_in;
         L.dO = dO; L.dS_out = dS_out; L.dq = dq; L.dk_ = dk; L.dv_ = dv; L.dg = dg; L.dS_in = dS_in;
         L.ws = carve_gla(s, true, (char*)ws, nullptr);
@@ -257,7 +271,7 @@ int gdn_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v, c
             const void* beta, const float* S_in, const void* dO, const float* dS_out, void* dq,
             void* dk, void* dv, void* dg, void* dbeta, float* dS_in, void* ws, size_t ws_bytes,
             void* stream) {
-    return bwd_common(false, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
+    return bwd_common(K_GDN, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
                       ws_bytes, stream);
 }
 
@@ -265,7 +279,15 @@ int gla_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v, c
             const void* beta, const float* S_in, const void* dO, const float* dS_out, void* dq,
             void* dk, void* dv, void* dg, void* dbeta, float* dS_in, void* ws, size_t ws_bytes,
             void* stream) {
-    return bwd_common(true, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
+    return bwd_common(K_GLA, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
+                      ws_bytes, stream);
+}
+
+int mamba2_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+               const void* beta, const float* S_in, const void* dO, const float* dS_out, void* dq,
+               void* dk, void* dv, void* dg, void* dbeta, float* dS_in, void* ws, size_t ws_bytes,
+               void* stream) {
+    return bwd_common(K_M2, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
                       ws_bytes, stream);
 }
 

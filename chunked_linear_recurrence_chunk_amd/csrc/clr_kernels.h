@@ -105,6 +105,7 @@ struct GlaWs {
 struct GlaLaunch {
     int B, T, H, NC, dk, dv;
     bool bf16;
+    bool scalar_gate;  // Mamba-2 member: g and dg are [B, T, H], broadcast over dk
     const void *q, *k, *v, *g;
     const float* S_in;
     void* o;

@@ -114,6 +114,35 @@ __device__ __forceinline__ void gate_cumsum(const E* gs, float* bs, float* seg, 
     }
 }
 
+// The gate rows of one block as a [64][DK] tile in registers (staged into LDS
+// with store_rows): the per-channel gate g[t][d], or with SG the per-token
+// scalar gate of the Mamba-2 member broadcast over the DK channels (the
+// scalar-identity transition of the StateFlow paper, Sec. 2.1, Eq. 1).
+// Tokens at or past nvalid read as 0 (an identity step).
+template <bool SG, typename E, int DK, int NT = 256>
+__device__ __forceinline__ RowsRegs<E, BLK, DK, NT> load_gate(const E* g, size_t tok0, int h, int H, int nvalid) {
+    if constexpr (!SG) {
+        const size_t ldk = (size_t)H * DK;
+        return load_rows<E, BLK, DK, NT>(g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+    } else {
+        using X = RowsRegs<E, BLK, DK, NT>;
+        X x;
+#pragma unroll
+        for (int j = 0; j < X::N; ++j) {
+            const int idx = threadIdx.x + NT * j, t = idx / X::PER_ROW;
+            const E gv = (idx < X::UNITS && t < nvalid) ? g[(tok0 + t) * H + h] : from_f<E>(0.f);
+            union {
+                uint4 u;
+                E e[X::VEC];
+            } c;
+#pragma unroll
+            for (int v = 0; v < X::VEC; ++v) c.e[v] = gv;
+            x.u[j] = c.u;
+        }
+        return x;
+    }
+}
+
 // A fragment of row `row` of a row-major LDS tile X (k = column c = col +
 // kmap(g, i)), element c scaled by exp(sgn * (brow[c] - ref[c])).
 template <typename E>
@@ -165,7 +194,7 @@ __device__ __forceinline__ Frag<E> frag_col_decay(const E* X, int PX, const floa
 // tiled Kh^T (backward also the tiled (Q*exp(b))^T and Kh), all from
 // row-major LDS tiles staged with every load in flight at once.
 // ---------------------------------------------------------------------------
-template <typename E, int DK, bool BWD>
+template <typename E, int DK, bool BWD, bool SG>
 __global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -184,7 +213,7 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
 
     {
         const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        const auto gx = load_rows<E, BLK, DK>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto gx = load_gate<SG, E, DK>(a.g, tok0, h, H, nvalid);
         RowsRegs<E, BLK, DK> qx;
         if constexpr (BWD) qx = load_rows<E, BLK, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
         store_rows<E, BLK, DK, PK>(kx, Ks);
@@ -361,7 +390,7 @@ template <typename E, int DK, int DV> struct GlaOutLds {
     static constexpr size_t total = o_V + (VLDS ? vbytes : sizeof(E) * BLK * PK);
 };
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool SG>
 __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     using Lay = GlaOutLds<E, DK, DV>;
     constexpr int NT = 512;
@@ -393,7 +422,7 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     {
         const auto qx = load_rows<E, BLK, DK, NT>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
         const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        const auto gx = load_rows<E, BLK, DK, NT>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto gx = load_gate<SG, E, DK, NT>(a.g, tok0, h, H, nvalid);
         load_slice(0, hf * NVH);
         store_rows<E, BLK, DK, PK, NT>(qx, Qs);
         store_rows<E, BLK, DK, PK, NT>(kx, Ks);
@@ -593,7 +622,7 @@ template <typename E, int DK, int DV> struct GlaIntraLds {
     static constexpr size_t total = end1 > end2 ? end1 : end2;
 };
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool SG>
 __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     using Lay = GlaIntraLds<E, DK, DV>;
     constexpr int NT = 512;
@@ -626,7 +655,7 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     {
         const auto kx = load_rows<E, BLK, DK, NT>(kb, ldk, nvalid);
         const auto qx = load_rows<E, BLK, DK, NT>(qb, ldk, nvalid);
-        const auto gx = load_rows<E, BLK, DK, NT>(a.g + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto gx = load_gate<SG, E, DK, NT>(a.g, tok0, h, H, nvalid);
         store_rows<E, BLK, DK, PK, NT>(kx, Ks);
         store_rows<E, BLK, DK, PK, NT>(qx, Qs);
         store_rows<E, BLK, DK, PK, NT>(gx, (E*)(lds + Lay::u_G));
@@ -834,12 +863,47 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
             if (r == 0) rsum[R][16 * db + 4 * g + i] = x;
         }
     __syncthreads();
-    // (7) dg[t][d] = sum_{tau >= t} dgb[tau][d] + rowsum(S1 * dh)[d]
-    for (int d = tid; d < DK; d += 256) {
-        float acc = __expf(bC[d]) * rowhd[d] + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
-        for (int t = BLK - 1; t >= 0; --t) {
-            acc += dgb[t * PD + d];
-            if (t < nvalid) a.dg[(tok0 + t) * ldk + (size_t)h * DK + d] = from_f<E>(acc);
+    if constexpr (!SG) {
+        // (7) dg[t][d] = sum_{tau >= t} dgb[tau][d] + rowsum(S1 * dh)[d]
+        for (int d = tid; d < DK; d += 256) {
+            float acc = __expf(bC[d]) * rowhd[d] + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
+            for (int t = BLK - 1; t >= 0; --t) {
+                acc += dgb[t * PD + d];
+                if (t < nvalid) a.dg[(tok0 + t) * ldk + (size_t)h * DK + d] = from_f<E>(acc);
+            }
+        }
+    } else {
+        // (7) scalar gate: the channel sum of the per-channel dg above,
+        //   dg[t] = sum_{tau >= t} sum_d dgb[tau][d] + sum_d c_d,
+        //   c_d = exp(b_C[d]) rowsum(S0 * dh)[d] + sum_s Kh[s][d] X[d][s].
+        // Row sums by eight lanes per token; c by wave 1; the reverse scan over
+        // the 64 tokens by wave 0 (fixed order throughout).
+        {
+            const int t = tid >> 3, p = tid & 7;
+            float x = 0.f;
+            for (int d = p; d < DK; d += 8) x += dgb[t * PD + d];
+            x += __shfl_xor(x, 1, 64);
+            x += __shfl_xor(x, 2, 64);
+            x += __shfl_xor(x, 4, 64);
+            if (p == 0) seg[t] = x;
+        }
+        if (w8 == 1) {
+            float c = 0.f;
+            for (int d = l; d < DK; d += 64)
+                c += __expf(bC[d]) * rowhd[d] + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
+            if (l == 0) seg[BLK] = c;
+        }
+        __syncthreads();
+        if (w8 == 0) {
+            float x = seg[l];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_down(x, off, 64);
+                if (l + off < 64) x += y;
+            }
+            if (l < nvalid) a.dg[(tok0 + l) * H + h] = from_f<E>(x + seg[BLK]);
         }
     }
 }
@@ -847,44 +911,45 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool SG>
 hipError_t launch_gla_fwd_t(const GlaLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GlaWs& ws = L.ws;
     using SL = GlaSlices<E, DK, DV>;
     GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC, ws.eC, (E*)ws.KhT, nullptr, nullptr};
-    launch("gla_prep", gla_prep_kernel<E, DK, false>, gblk, dim3(256), st, pa);
+    launch(SG ? "m2_prep" : "gla_prep", gla_prep_kernel<E, DK, false, SG>, gblk, dim3(256), st, pa);
     GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, L.S_out, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
-    launch("gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
+    launch(SG ? "m2_scan_fwd" : "gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
     if (L.o) {
         GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)ws.hT, (E*)L.o, L.T, L.H, L.NC};
-        launch("gla_out", gla_out_kernel<E, DK, DV>, gblk, dim3(512), st, oa);
+        launch(SG ? "m2_out" : "gla_out", gla_out_kernel<E, DK, DV, SG>, gblk, dim3(512), st, oa);
     }
     return hipGetLastError();
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool SG>
 hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GlaWs& ws = L.ws;
     using SL = GlaSlices<E, DK, DV>;
     GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC,
                       ws.eC, (E*)ws.KhT, (E*)ws.QgT, (E*)ws.Kh};
-    launch("gla_prep_bwd", gla_prep_kernel<E, DK, true>, gblk, dim3(256), st, pa);
+    launch(SG ? "m2_prep_bwd" : "gla_prep_bwd", gla_prep_kernel<E, DK, true, SG>, gblk, dim3(256), st, pa);
     GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, nullptr, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
-    launch("gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
+    launch(SG ? "m2_scan_fwd_rec" : "gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
     GlaScanBwdArgs<E> sb{ws.eC, (const E*)ws.Kh, (const E*)ws.QgT, (const E*)L.dO, L.dS_out, L.dS_in,
                          (E*)ws.dh, (E*)ws.dVs, L.T, L.H, L.NC, L.B * L.H};
-    launch("gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sb);
+    launch(SG ? "m2_scan_bwd" : "gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sb);
     GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.dO, (const E*)L.g, (const E*)ws.hT,
                        (const E*)ws.dh, (const E*)ws.dVs, (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, L.T, L.H, L.NC};
-    launch("gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV>, gblk, dim3(512), st, ia);
+    launch(SG ? "m2_bwd_intra" : "gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV, SG>, gblk, dim3(512), st, ia);
     return hipGetLastError();
 }
 
 hipError_t launch_gla_fwd(const GlaLaunch& L, hipStream_t st) {
 #define CLR_CASE(E, DK, DV) \
-    if (L.dk == DK && L.dv == DV) return launch_gla_fwd_t<E, DK, DV>(L, st);
+    if (L.dk == DK && L.dv == DV) \
+        return L.scalar_gate ? launch_gla_fwd_t<E, DK, DV, true>(L, st) : launch_gla_fwd_t<E, DK, DV, false>(L, st);
     if (L.bf16) {
         CLR_FOR_GLA_SHAPES(bf16)
     } else {
@@ -896,7 +961,8 @@ hipError_t launch_gla_fwd(const GlaLaunch& L, hipStream_t st) {
 
 hipError_t launch_gla_bwd(const GlaLaunch& L, hipStream_t st) {
 #define CLR_CASE(E, DK, DV) \
-    if (L.dk == DK && L.dv == DV) return launch_gla_bwd_t<E, DK, DV>(L, st);
+    if (L.dk == DK && L.dv == DV) \
+        return L.scalar_gate ? launch_gla_bwd_t<E, DK, DV, true>(L, st) : launch_gla_bwd_t<E, DK, DV, false>(L, st);
     if (L.bf16) {
         CLR_FOR_GLA_SHAPES(bf16)
     } else {

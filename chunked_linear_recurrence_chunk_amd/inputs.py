@@ -10,6 +10,7 @@ Distributions (per-token tensors are [B,T,H,d], states [B,H,dk,dv]):
                   S_in = 0.1 * N(0,1); dO ~ N(0,1); dS_out ~ N(0,1).
   GLA:            q, k, v ~ N(0,1); g = logsigmoid(N(0,1)) / 16 per key channel;
                   S_in = 0.1 * N(0,1); dO ~ N(0,1); dS_out ~ N(0,1).
+  Mamba-2:        as GLA, but one gate per (token, head): g [B,T,H].
 Draw order: q, k, v, g, beta (GDN only), S_in, dO, dS_out, all float32 from a
 numpy PCG64 generator.  For dtype "bf16" every per-token tensor (including dO)
 is rounded to bfloat16 (round-to-nearest-even) and returned as the exact
@@ -27,6 +28,8 @@ CONFIGS = {
     "gla_bf16_B4_H16_T4096_dk128_dv256": dict(kind="gla", dtype="bf16", B=4, H=16, T=4096, dk=128, dv=256, N=1),
     "gdn_bf16_H32_T65536_d128": dict(kind="gdn", dtype="bf16", B=1, H=32, T=65536, dk=128, dv=128, N=16),
     "gdn_bf16_H16_T262144_d128": dict(kind="gdn", dtype="bf16", B=1, H=16, T=262144, dk=128, dv=128, N=64),
+    # scalar-gate member at the GLA workload's shape
+    "mamba2_bf16_B4_H16_T4096_dk128_dv256": dict(kind="mamba2", dtype="bf16", B=4, H=16, T=4096, dk=128, dv=256, N=1),
 }
 
 
@@ -114,6 +117,27 @@ def make_gla(B, T, H, dk, dv, dtype="bf16", seed=0, gate_scale=1.0 / 16.0):
     return d
 
 
+def make_mamba2(B, T, H, dk, dv, dtype="bf16", seed=0, gate_scale=1.0 / 16.0):
+    """Scalar-gate (Mamba-2 member) inputs: the GLA recipe with g [B,T,H]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _normal(rng, (B, T, H, dk))
+    k = _normal(rng, (B, T, H, dk))
+    v = _normal(rng, (B, T, H, dv))
+    z = _normal(rng, (B, T, H)).astype(np.float64)
+    logsig = -(np.maximum(-z, 0) + np.log1p(np.exp(-np.abs(z))))
+    g = (logsig * gate_scale).astype(np.float32)
+    S_in = (0.1 * _normal(rng, (B, H, dk, dv))).astype(np.float32)
+    dO = _normal(rng, (B, T, H, dv))
+    dS_out = _normal(rng, (B, H, dk, dv))
+    d = dict(q=q, k=k, v=v, g=g, S_in=S_in, dO=dO, dS_out=dS_out)
+    if dtype == "bf16":
+        for key in ("q", "k", "v", "g", "dO"):
+            d[key] = bf16_round(d[key])
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return d
+
+
 def make(cfg: dict, seed: int, **kw):
-    f = make_gdn if cfg["kind"] == "gdn" else make_gla
+    f = {"gdn": make_gdn, "gla": make_gla, "mamba2": make_mamba2}[cfg["kind"]]
     return f(cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], cfg["dtype"], seed, **kw)

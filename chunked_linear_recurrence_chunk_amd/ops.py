@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libclr.so")
 
 CLR_OK, CLR_EINVAL, CLR_ENOTSUP, CLR_EWORKSPACE, CLR_EHIP = range(5)
 CLR_F32, CLR_BF16 = 0, 1
-OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD = range(4)
+OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD, OP_M2_FWD, OP_M2_BWD = range(6)
 
 
 class ClrShape(ctypes.Structure):
@@ -52,11 +52,11 @@ def load(path: Optional[str] = None):
     sp = ctypes.POINTER(ClrShape)
     lib.clr_workspace_bytes.argtypes = [sp, i]
     lib.clr_workspace_bytes.restype = sz
-    for name in ("gdn_fwd", "gla_fwd"):
+    for name in ("gdn_fwd", "gla_fwd", "mamba2_fwd"):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 9 + [sz, vp]
         f.restype = i
-    for name in ("gdn_bwd", "gla_bwd"):
+    for name in ("gdn_bwd", "gla_bwd", "mamba2_bwd"):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 15 + [sz, vp]
         f.restype = i
@@ -232,6 +232,16 @@ def gdn_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, ws=None, out=None):
 def gla_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None, out=None):
     """GLA chunk backward.  Returns dict dq, dk, dv, dg, dS_in."""
     return _bwd("gla_bwd", OP_GLA_BWD, q, k, v, g, None, S_in, dO, dS_out, ws, out)
+
+
+def mamba2_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None):
+    """Scalar-gate (Mamba-2 member) chunk forward, g [B,T,H].  Returns (o, S_out)."""
+    return _fwd("mamba2_fwd", OP_M2_FWD, q, k, v, g, None, S_in, want_state, ws, o, S_out)
+
+
+def mamba2_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None, out=None):
+    """Scalar-gate (Mamba-2 member) chunk backward.  Returns dict dq, dk, dv, dg, dS_in."""
+    return _bwd("mamba2_bwd", OP_M2_BWD, q, k, v, g, None, S_in, dO, dS_out, ws, out)
 
 
 def probe_mma(A, Bt):

@@ -112,6 +112,7 @@ class GlaChunked(GdnChunked):
         nbytes = max(ops.workspace_bytes(shape, ops.OP_GLA_FWD), ops.workspace_bytes(shape, ops.OP_GLA_BWD))
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         self.saved = [None] * N
+        self._fwd, self._bwd = ops.gla_fwd, ops.gla_bwd
 
     def _chunk(self, i):
         a, b = self.bounds[i]
@@ -128,7 +129,7 @@ class GlaChunked(GdnChunked):
             a, b = self.bounds[i]
             self.saved[i] = S
             view = o[:, a:b]
-            oi, S = self.ops.gla_fwd(*self._chunk(i), S, ws=self.ws, o=view if view.is_contiguous() else None)
+            oi, S = self._fwd(*self._chunk(i), S, ws=self.ws, o=view if view.is_contiguous() else None)
             if oi.data_ptr() != view.data_ptr():
                 view.copy_(oi)
         return o, S
@@ -143,7 +144,7 @@ class GlaChunked(GdnChunked):
             a, b = self.bounds[i]
             views = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg")}
             out = {key: t for key, t in views.items() if t.is_contiguous()}
-            r = self.ops.gla_bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
+            r = self._bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
             for key, t in views.items():
                 if r[key].data_ptr() != t.data_ptr():
                     t.copy_(r[key])
@@ -151,3 +152,26 @@ class GlaChunked(GdnChunked):
             self.saved[i] = None
         grads["dS_in"] = dS
         return grads
+
+
+class Mamba2Chunked(GlaChunked):
+    """Forward/backward of one scalar-gate (Mamba-2 member) layer over N
+    sequence chunks."""
+
+    kind = "mamba2"
+
+    def __init__(self, q, k, v, g, N: int):
+        from . import ops
+        self.ops = ops
+        self.q, self.k, self.v, self.g, self.beta = q, k, v, g, None
+        self.N = N
+        self.bounds = _bounds(q.shape[1], N)
+        L = self.bounds[0][1]
+        B, _, H, dk = q.shape
+        dv = v.shape[-1]
+        import torch
+        shape = ops.ClrShape(B, L, H, dk, dv, ops._dtype_code(q))
+        nbytes = max(ops.workspace_bytes(shape, ops.OP_M2_FWD), ops.workspace_bytes(shape, ops.OP_M2_BWD))
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+        self.saved = [None] * N
+        self._fwd, self._bwd = ops.mamba2_fwd, ops.mamba2_bwd

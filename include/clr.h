@@ -30,7 +30,7 @@
  * ----------------------------------------------------------
  *     q, k, dq, dk      [B, T, H, dk]      element type = shape.dtype
  *     v, o, dO, dv      [B, T, H, dv]      element type = shape.dtype
- *     g, dg             GDN: [B, T, H]     GLA: [B, T, H, dk]   (shape.dtype)
+ *     g, dg             GDN, Mamba-2: [B, T, H]   GLA: [B, T, H, dk]   (shape.dtype)
  *     beta, dbeta       GDN: [B, T, H]     GLA: must be NULL     (shape.dtype)
  *     S_in, S_out, dS_out, dS_in   [B, H, dk, dv]  always float32
  * Supported head sizes: GDN (dk, dv) in {(32,32), (64,64), (128,128)};
@@ -89,7 +89,9 @@ typedef enum {
     CLR_OP_GDN_FWD = 0,
     CLR_OP_GDN_BWD = 1,
     CLR_OP_GLA_FWD = 2,
-    CLR_OP_GLA_BWD = 3
+    CLR_OP_GLA_BWD = 3,
+    CLR_OP_M2_FWD = 4,
+    CLR_OP_M2_BWD = 5
 } clr_op_t;
 
 typedef struct {
@@ -122,6 +124,25 @@ int gla_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* 
             const void* g, const void* beta, const float* S_in, const void* dO,
             const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
             float* dS_in, void* ws, size_t ws_bytes, void* stream);
+
+/* Mamba-2 member of the family (StateFlow paper, Sec. 2.1, Eq. 1: the
+ * transition F_t is a scalar times the identity), key-major:
+ *     S_t = alpha_t S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t,   alpha_t = exp(g_t)
+ * with one scalar gate per (token, head).  A Mamba-2 SSD layer maps onto it
+ * as q = C, k = B, v = dt * x, g = dt * A (the D skip term and the
+ * discretisation stay with the caller).  Same arguments and layouts as
+ * gla_fwd / gla_bwd except g and dg, which are [B, T, H] (shape.dtype);
+ * beta and dbeta must be NULL.  Head sizes as for GLA.  Runs on the GLA
+ * kernels with the gate broadcast over the key channels; dg is the channel
+ * sum of the per-channel gate gradient.  Workspace: CLR_OP_M2_FWD /
+ * CLR_OP_M2_BWD. */
+int mamba2_fwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+               const void* g, const void* beta, const float* S_in, void* o, float* S_out,
+               void* ws, size_t ws_bytes, void* stream);
+int mamba2_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+               const void* g, const void* beta, const float* S_in, const void* dO,
+               const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+               float* dS_in, void* ws, size_t ws_bytes, void* stream);
 
 /* Split-and-overlap forward (StateFlow paper, Sec. 3.4.2, "Split and
  * Overlap", forward wavefront).  gdn_fwd with o != NULL and at least 16

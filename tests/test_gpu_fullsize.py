@@ -5,7 +5,8 @@ times (the sequence-chunk driver):
     recurrence, so a head slice of the inputs is an exact sub-problem);
   * identities that hold for the exact layer at any size are checked on every
     head of the GPU result (q.dq = o.do per token; GDN k.dk + v.dv = 2 beta dbeta;
-    GLA k.dk = v.dv; joint linearity sum v.dv + <S_in, dS_in> = sum o.do + <S_out, dS_out>);
+    GLA and Mamba-2 k.dk = v.dv; joint linearity sum v.dv + <S_in, dS_in> =
+    sum o.do + <S_out, dS_out>; Mamba-2 dg as a suffix sum of q.dq - k.dk);
   * the chunked run equals the unchunked run bit for bit.
 """
 import concurrent.futures as cf
@@ -28,8 +29,10 @@ def _run(cfg, x, N):
     S_in, dS_out = to_dev(x["S_in"], "fp32"), to_dev(x["dS_out"], "fp32")
     if cfg["kind"] == "gdn":
         drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
-    else:
+    elif cfg["kind"] == "gla":
         drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
+    else:
+        drv = stateflow.Mamba2Chunked(d["q"], d["k"], d["v"], d["g"], N)
     o, S = drv.forward(S_in)
     gr = drv.backward(d["dO"], dS_out)
     torch.cuda.synchronize()
@@ -51,8 +54,9 @@ def _oracle_heads(cfg, x, pairs):
             o, S = oracle.gdn_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"])
             r = oracle.gdn_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], sl["dS_out"])
         else:
-            o, S = oracle.gla_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"])
-            r = oracle.gla_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], sl["dS_out"])
+            fwd, bwd = (oracle.gla_fwd, oracle.gla_bwd) if cfg["kind"] == "gla" else (oracle.mamba2_fwd, oracle.mamba2_bwd)
+            o, S = fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"])
+            r = bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], sl["dS_out"])
         r.update(o=o, S_out=S)
         return bh, r
 
@@ -85,6 +89,20 @@ def _check_identities(cfg, x, got):
     lhs = vdv.sum(1) + np.sum(x["S_in"] * f["dS_in"], (2, 3))
     rhs = odo.sum(1) + np.sum(f["S_out"] * x["dS_out"], (2, 3))
     assert rel_err(lhs, rhs) < 3e-2, rel_err(lhs, rhs)
+    if cfg["kind"] == "mamba2":
+        # scalar gate: dg_t = sum_{tau >= t} (q.dq - k.dk) + <S_out, dS_out>.
+        # The terms cancel over long suffixes and each carries the bf16
+        # rounding of dq and dk, so the residual is measured against the same
+        # sums over absolute values (the scale that rounding acts on); bf16
+        # rounds to 2^-9 relative, which leaves room for the kernel's own error.
+        def suffix(a):
+            return np.flip(np.cumsum(np.flip(a, 1), 1), 1)
+        sf = np.sum(f["S_out"] * x["dS_out"], (2, 3))[:, None, :]
+        gate = suffix(qdq - kdk) + sf
+        scale = suffix(np.sum(np.abs(q * f["dq"]), -1) + np.sum(np.abs(k * f["dk"]), -1)) + np.abs(sf)
+        e = float(np.max(np.abs(f["dg"] - gate)) / np.max(scale))
+        print(f"   scalar-gate identity residual {e:.2e} of the absolute-sum scale", flush=True)
+        assert e < 1e-2, e
 
 
 def _full(name, pairs, compare_unchunked):
@@ -114,6 +132,10 @@ def test_full_gdn_H16_T8192():
 
 def test_full_gla_B4_H16_T4096():
     _full("gla_bf16_B4_H16_T4096_dk128_dv256", [(1, 5), (3, 12)], False)
+
+
+def test_full_mamba2_B4_H16_T4096():
+    _full("mamba2_bf16_B4_H16_T4096_dk128_dv256", [(0, 2), (2, 15)], False)
 
 
 def test_full_gdn_H32_T65536():
