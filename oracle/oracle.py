@@ -46,6 +46,61 @@ def build(src: str = _SRC, out: str = _LIB_PATH, extra=()) -> str:
 
 
 _lib = None
+_conv_lib = None
+_CONV_SRC = os.path.join(_HERE, "conv_oracle.c")
+_CONV_LIB_PATH = os.path.join(_BUILD, "libconv_oracle.so")
+
+
+def build_conv(src: str = _CONV_SRC, out: str = _CONV_LIB_PATH) -> str:
+    """Compile the short-convolution oracle (conv_oracle.c)."""
+    return build(src=src, out=out)
+
+
+def load_conv(path: Optional[str] = None):
+    """Load (building first if absent) the short-convolution oracle."""
+    global _conv_lib
+    if path is None and _conv_lib is not None:
+        return _conv_lib
+    p = path or _CONV_LIB_PATH
+    if not os.path.exists(p):
+        build_conv(out=p)
+    lib = ctypes.CDLL(p)
+    i, dp = ctypes.c_int, _dp()
+    lib.ref_conv_fwd.argtypes = [i] * 5 + [dp] * 6
+    lib.ref_conv_bwd.argtypes = [i] * 5 + [dp] * 10
+    lib.ref_conv_fwd.restype = lib.ref_conv_bwd.restype = i
+    if path is None:
+        _conv_lib = lib
+    return lib
+
+
+def conv_fwd(x, w, bias=None, state_in=None, act=0, lib=None):
+    """Causal short convolution with boundary state (conv_oracle.c).
+    x [B,T,C], w [C,W], bias [C], state_in [B,W-1,C].  Returns (y, state_out)."""
+    lib = lib or load_conv()
+    x, w, bias, state_in = map(_c, (x, w, bias, state_in))
+    B, T, C = x.shape
+    W = w.shape[1]
+    y = np.zeros((B, T, C))
+    st = np.zeros((B, W - 1, C))
+    if lib.ref_conv_fwd(B, T, C, W, int(act), _p(x), _p(w), _p(bias), _p(state_in), _p(y), _p(st)) != 0:
+        raise RuntimeError("ref_conv_fwd failed")
+    return y, st
+
+
+def conv_bwd(x, w, bias, state_in, dy, dstate_out=None, act=0, lib=None):
+    """Gradients of the short convolution: dict dx, dw, dbias, dstate_in."""
+    lib = lib or load_conv()
+    x, w, bias, state_in, dy, dstate_out = map(_c, (x, w, bias, state_in, dy, dstate_out))
+    B, T, C = x.shape
+    W = w.shape[1]
+    r = dict(dx=np.zeros((B, T, C)), dw=np.zeros((C, W)), dbias=np.zeros(C),
+             dstate_in=np.zeros((B, W - 1, C)))
+    rc = lib.ref_conv_bwd(B, T, C, W, int(act), _p(x), _p(w), _p(bias), _p(state_in), _p(dy),
+                          _p(dstate_out), _p(r["dx"]), _p(r["dw"]), _p(r["dbias"]), _p(r["dstate_in"]))
+    if rc != 0:
+        raise RuntimeError("ref_conv_bwd failed")
+    return r
 
 
 def _dp():
