@@ -73,6 +73,29 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
     return W.get(name)
 
 
+def shortconv_work(name: str, B: int, Tc: int, C: int, W: int, es: int, P: int):
+    """Algorithmic (bytes, flops) of one short-convolution launch over a
+    sequence chunk of Tc tokens: every token row read or written once, the
+    carried rows, the fp32 weights, and (backward) the partial weight-gradient
+    table of P rows.  Flops are the taps' multiply-adds (vector ALU work)."""
+    rows, st, par = B * Tc * C * es, B * (W - 1) * C * es, C * (W + 1) * 4
+    if name == "shortconv_fwd":
+        return 2 * rows + 2 * st + par, 2 * W * B * Tc * C
+    if name == "shortconv_bwd":
+        return 3 * rows + 2 * st + par + P * par, 4 * W * B * Tc * C
+    if name == "shortconv_reduce":
+        return P * par + par, P * par // 4
+    return None
+
+
+def _conv_tile_groups(B: int, T: int, C: int, tt: int = 8, nv: int = 4) -> int:
+    """Tile groups per batch of the short-convolution backward grid (the
+    rule of the library's launcher: about 512 work-groups of 128 threads)."""
+    ntiles = (T + tt - 1) // tt
+    gx = (C // nv + 127) // 128
+    return max(1, min(ntiles, 512 // (gx * B)))
+
+
 def source_hash() -> str:
     """Hash of the HIP sources (ties stored counter data to a kernel build)."""
     h = hashlib.sha256()
@@ -110,10 +133,22 @@ def cpu_baseline(cfg: dict, x: dict, budget_chunks: int):
     L = T // N
     n = max(1, min(budget_chunks, N))
     Ts = L * n
-    sl = {k: (np.ascontiguousarray(v[:, :Ts]).astype(np.float64) if v.ndim >= 3 and k not in ("S_in", "dS_out")
-              else v.astype(np.float64)) for k, v in x.items()}
+    per_token = ("x", "dy") if cfg["kind"] == "shortconv" else ("q", "k", "v", "g", "beta", "dO")
+    sl = {k: (np.ascontiguousarray(v[:, :Ts]).astype(np.float64) if k in per_token else v.astype(np.float64))
+          for k, v in x.items()}
+
     def once():
-        if cfg["kind"] == "gdn":
+        if cfg["kind"] == "shortconv":
+            st = sl["state_in"]
+            states = []
+            for i in range(n):
+                states.append(st)
+                _, st = oracle.conv_fwd(sl["x"][:, i * L:(i + 1) * L], sl["w"], sl["bias"], st, cfg["act"])
+            ds = None
+            for i in reversed(range(n)):
+                ds = oracle.conv_bwd(sl["x"][:, i * L:(i + 1) * L], sl["w"], sl["bias"], states[i],
+                                     sl["dy"][:, i * L:(i + 1) * L], ds, cfg["act"])["dstate_in"]
+        elif cfg["kind"] == "gdn":
             oracle.gdn_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], None, n)
         elif cfg["kind"] == "gla":
             oracle.gla_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], None, n)
@@ -129,7 +164,8 @@ def cpu_baseline(cfg: dict, x: dict, budget_chunks: int):
         dt = time.perf_counter() - t0
     return {"value": cfg["B"] * Ts * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{'all' if n == N else f'first {n} of'} {N} sequence chunks ({cfg['B']}x{Ts} tokens, "
-                      f"all {cfg['H']} heads), fp64 fwd+bwd, {reps} run(s), {dt:.1f} s"}
+                      + (f"all {cfg['C']} channels" if cfg["kind"] == "shortconv" else f"all {cfg['H']} heads")
+                      + f"), fp64 fwd+bwd, {reps} run(s), {dt:.1f} s"}
 
 
 def main():
@@ -166,7 +202,7 @@ def main():
     ops.load()  # fail loudly if the HIP library is missing
 
     cfg = inputs.CONFIGS[args.workload]
-    B, T, H, dk, dv, N = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], cfg["N"]
+    B, T, N = cfg["B"], cfg["T"], cfg["N"]
     dtype = cfg["dtype"]
     x = inputs.make(cfg, seed=2)
 
@@ -176,22 +212,33 @@ def main():
             return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
-    keys = ("q", "k", "v", "g", "beta", "dO") if cfg["kind"] == "gdn" else ("q", "k", "v", "g", "dO")
-    d = {k: dev(x[k], dtype) for k in keys}
-    S_in = dev(x["S_in"], "fp32")
-    if cfg["kind"] == "gdn":
-        drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
-    elif cfg["kind"] == "gla":
-        drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
-    else:
-        drv = stateflow.Mamba2Chunked(d["q"], d["k"], d["v"], d["g"], N)
-    o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device="cuda")
-    grads = {k: torch.empty_like(d[k.replace("d", "", 1)] if k != "dbeta" else d["beta"])
-             for k in (("dq", "dk", "dv", "dg", "dbeta") if cfg["kind"] == "gdn" else ("dq", "dk", "dv", "dg"))}
+    if cfg["kind"] == "shortconv":
+        d = {k: dev(x[k], dtype) for k in ("x", "state_in", "dy")}
+        w, bias = dev(x["w"], "fp32"), dev(x["bias"], "fp32")
+        drv = stateflow.ShortConvChunked(d["x"], w, bias, N, act=cfg["act"])
+        y = torch.empty_like(d["x"])
 
-    def step():
-        drv.forward(S_in, o=o)
-        drv.backward(d["dO"], None, grads=grads)
+        def step():
+            drv.forward(d["state_in"], y=y)
+            drv.backward(d["dy"], None)
+    else:
+        H, dv = cfg["H"], cfg["dv"]
+        keys = ("q", "k", "v", "g", "beta", "dO") if cfg["kind"] == "gdn" else ("q", "k", "v", "g", "dO")
+        d = {k: dev(x[k], dtype) for k in keys}
+        S_in = dev(x["S_in"], "fp32")
+        if cfg["kind"] == "gdn":
+            drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
+        elif cfg["kind"] == "gla":
+            drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
+        else:
+            drv = stateflow.Mamba2Chunked(d["q"], d["k"], d["v"], d["g"], N)
+        o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device="cuda")
+        grads = {k: torch.empty_like(d[k.replace("d", "", 1)] if k != "dbeta" else d["beta"])
+                 for k in (("dq", "dk", "dv", "dg", "dbeta") if cfg["kind"] == "gdn" else ("dq", "dk", "dv", "dg"))}
+
+        def step():
+            drv.forward(S_in, o=o)
+            drv.backward(d["dO"], None, grads=grads)
 
     for _ in range(args.warmup):
         step()
@@ -214,19 +261,27 @@ def main():
     rep = ops.timing_report()
     ops.timing_enable(False)
     es = 2 if dtype == "bf16" else 4
-    NC = (T // N) // 64
-    blocks_per_launch = B * H * NC
+
+    def launch_work(name):
+        if cfg["kind"] == "shortconv":
+            P = B * _conv_tile_groups(B, T // N, cfg["C"])
+            return shortconv_work(name, B, T // N, cfg["C"], cfg["W"], es, P)
+        wk = kernel_work(name, cfg["dk"], cfg["dv"], es)
+        nb = B * cfg["H"] * ((T // N) // 64)
+        return None if wk is None else (wk[0] * nb, wk[1] * nb)
+
     kernels = {}
     tot_ms = sum(v[1] for v in rep.values())
     tot_flops = 0.0
     for name, (launches, total_ms) in rep.items():
         avg_us = total_ms / launches * 1e3
-        work = kernel_work(name, dk, dv, es)
+        work = launch_work(name)
         ent = {"launches_per_step": launches // args.steps, "avg_us": round(avg_us, 2),
                "share": round(total_ms / tot_ms, 3)}
         if work:
-            byts, flops = work[0] * blocks_per_launch, work[1] * blocks_per_launch
-            tot_flops += flops * launches / args.steps
+            byts, flops = work
+            if cfg["kind"] != "shortconv":  # short-convolution flops are vector ALU work, not MFMA
+                tot_flops += flops * launches / args.steps
             ent.update(alg_bytes=byts, alg_flops=flops,
                        gbs=round(byts / (avg_us * 1e-6) / 1e9, 1),
                        tflops=round(flops / (avg_us * 1e-6) / 1e12, 2))
@@ -250,8 +305,11 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
            "data": "synthetic",
-           "config": {"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "H": H, "dk": dk,
-                      "dv": dv, "seq_chunks": N, "block": 64},
+           "config": ({"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "C": cfg["C"], "W": cfg["W"],
+                       "act": "silu" if cfg["act"] else "identity", "seq_chunks": N}
+                      if cfg["kind"] == "shortconv" else
+                      {"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "H": cfg["H"], "dk": cfg["dk"],
+                       "dv": cfg["dv"], "seq_chunks": N, "block": 64}),
            "mfma_util": round(mfma_util, 4),
            "roofline": roofline, "kernels": kernels}
     if not args.no_cpu:

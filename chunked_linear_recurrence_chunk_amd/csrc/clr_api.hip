@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "clr.h"
+#include "clr_conv.h"
 #include "clr_kernels.h"
 
 using namespace clr;
@@ -126,6 +127,24 @@ int passthrough(const float* src, float* dst, size_t n, hipStream_t st) {
     hipError_t e = src ? hipMemcpyAsync(dst, src, n * 4, hipMemcpyDeviceToDevice, st)
                        : hipMemsetAsync(dst, 0, n * 4, st);
     return hip_status(e);
+}
+
+int conv_check_shape(const clr_conv_shape_t* s) {
+    if (!s) return CLR_EINVAL;
+    if (s->B < 1 || s->T < 0 || s->C < 8 || s->W < 1) return CLR_EINVAL;
+    if (s->dtype != CLR_F32 && s->dtype != CLR_BF16) return CLR_ENOTSUP;
+    if (s->C % 8 || s->W > 4 || (s->act != 0 && s->act != 1)) return CLR_ENOTSUP;
+    if ((double)s->B * s->T * s->C > 9.0e15) return CLR_EINVAL;
+    return CLR_OK;
+}
+
+template <typename E>
+ConvArgs<E> conv_args(const clr_conv_shape_t* s, const void* x, const float* w, const float* bias,
+                             const void* state_in) {
+    ConvArgs<E> a{};
+    a.B = s->B; a.T = s->T; a.C = s->C; a.W = s->W; a.act = s->act;
+    a.x = (const E*)x; a.w = w; a.bias = bias; a.state_in = (const E*)state_in;
+    return a;
 }
 
 }  // namespace
@@ -289,6 +308,74 @@ int mamba2_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v
                void* stream) {
     return bwd_common(K_M2, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
                       ws_bytes, stream);
+}
+
+size_t clr_shortconv_workspace_bytes(const clr_conv_shape_t* s) {
+    if (conv_check_shape(s) != CLR_OK) return 0;
+    const size_t P = (size_t)s->B * conv_bwd_tile_groups(s->B, s->T, s->C, CONV_BWD_TT);
+    return align_up(P * s->C * (s->W + 1) * 4 + 4);
+}
+
+int shortconv_fwd(const clr_conv_shape_t* s, const void* x, const float* w, const float* bias,
+                  const void* state_in, void* y, void* state_out, void* stream) {
+    int rc = conv_check_shape(s);
+    if (rc) return rc;
+    if (!x || !w || !y) return CLR_EINVAL;
+    const size_t es = esize(s->dtype), n = (size_t)s->B * s->T * s->C, ns = (size_t)s->B * (s->W - 1) * s->C;
+    Buf bufs[] = {{x, n * es, false}, {w, (size_t)s->C * s->W * 4, false}, {bias, (size_t)s->C * 4, false},
+                  {state_in, ns * es, false}, {y, n * es, true}, {state_out, ns * es, true}};
+    if ((rc = check_bufs(bufs, 6))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (s->T == 0) {
+        if (!state_out || ns == 0) return CLR_OK;
+        return hip_status(state_in ? hipMemcpyAsync(state_out, state_in, ns * es, hipMemcpyDeviceToDevice, st)
+                                   : hipMemsetAsync(state_out, 0, ns * es, st));
+    }
+    if (s->dtype == CLR_BF16) {
+        ConvArgs<bf16> a = conv_args<bf16>(s, x, w, bias, state_in);
+        a.y = (bf16*)y; a.state_out = (bf16*)state_out;
+        return hip_status(launch_shortconv_fwd(a, st));
+    }
+    ConvArgs<float> a = conv_args<float>(s, x, w, bias, state_in);
+    a.y = (float*)y; a.state_out = (float*)state_out;
+    return hip_status(launch_shortconv_fwd(a, st));
+}
+
+int shortconv_bwd(const clr_conv_shape_t* s, const void* x, const float* w, const float* bias,
+                  const void* state_in, const void* dy, const float* dstate_out, void* dx, float* dw,
+                  float* dbias, float* dstate_in, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+    int rc = conv_check_shape(s);
+    if (rc) return rc;
+    if (!x || !w || !dy || !dx || !dw || (s->W > 1 && !dstate_in)) return CLR_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return CLR_EINVAL;
+    const size_t es = esize(s->dtype), n = (size_t)s->B * s->T * s->C, ns = (size_t)s->B * (s->W - 1) * s->C;
+    const size_t nw = (size_t)s->C * s->W * 4, nb = (size_t)s->C * 4;
+    Buf bufs[] = {{x, n * es, false},          {w, nw, false},           {bias, nb, false},
+                  {state_in, ns * es, false},  {dy, n * es, false},      {dstate_out, ns * 4, false},
+                  {dx, n * es, true},          {dw, nw, true},           {dbias, nb, true},
+                  {dstate_in, ns * 4, true},   {ws, ws_bytes, true}};
+    if ((rc = check_bufs(bufs, 11))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (s->T == 0) {
+        hipError_t e = hipSuccess;
+        if (dstate_in && ns)
+            e = dstate_out ? hipMemcpyAsync(dstate_in, dstate_out, ns * 4, hipMemcpyDeviceToDevice, st)
+                           : hipMemsetAsync(dstate_in, 0, ns * 4, st);
+        if (e == hipSuccess && !accumulate) e = hipMemsetAsync(dw, 0, nw, st);
+        if (e == hipSuccess && !accumulate && dbias) e = hipMemsetAsync(dbias, 0, nb, st);
+        return hip_status(e);
+    }
+    if (!ws || ws_bytes < clr_shortconv_workspace_bytes(s) || ((uintptr_t)ws & (ALIGN - 1))) return CLR_EWORKSPACE;
+    if (s->dtype == CLR_BF16) {
+        ConvArgs<bf16> a = conv_args<bf16>(s, x, w, bias, state_in);
+        a.dy = (const bf16*)dy; a.dstate_out = dstate_out; a.dx = (bf16*)dx;
+        a.dstate_in = dstate_in; a.dw = dw; a.dbias = dbias; a.part = (float*)ws;
+        return hip_status(launch_shortconv_bwd(a, accumulate, st));
+    }
+    ConvArgs<float> a = conv_args<float>(s, x, w, bias, state_in);
+    a.dy = (const float*)dy; a.dstate_out = dstate_out; a.dx = (float*)dx;
+    a.dstate_in = dstate_in; a.dw = dw; a.dbias = dbias; a.part = (float*)ws;
+    return hip_status(launch_shortconv_bwd(a, accumulate, st));
 }
 
 int clr_probe_mma(int dtype, const void* A, const void* Bt, float* C, void* stream) {

@@ -1,0 +1,336 @@
+// shortconv.hip -- causal depthwise short convolution with a boundary state,
+// forward and backward (the local-convolution boundary state that the
+// StateFlow paper, Sec. 1 and Sec. 3.3, hands from one sequence chunk to the
+// next next to the recurrent state).
+//
+// Per batch b, channel c and token t of a chunk:
+//     xe = [state_in ; x]                      (W - 1 carried rows first)
+//     z_t = bias_c + sum_j w[c][j] xe[t + j],  y_t = act(z_t)
+//     state_out = the last W - 1 rows of xe.
+// The work is element-wise and HBM-bound: each thread owns a few channels
+// (8 in the forward, 4 in the backward, which keeps more rows per thread) over
+// a tile of TT tokens and issues every row load of its tile (plus the W - 1
+// halo rows) before computing; a wave reads or writes 256 - 1024 contiguous
+// bytes of a token row per instruction.
+#include <hip/hip_runtime.h>
+
+#include "clr_device.h"
+#include "clr_launch.h"
+#include "clr_conv.h"
+
+namespace clr {
+namespace {
+
+// NV consecutive elements of one token row, as loaded (NV * sizeof(E) bytes).
+template <typename E, int NV> struct RowV {
+    static constexpr int NW = NV * (int)sizeof(E) / 4;  // 32-bit words
+    unsigned u[NW];
+};
+template <typename E, int NV>
+__device__ __forceinline__ RowV<E, NV> ld_row(const E* p) {
+    RowV<E, NV> r;
+    if constexpr (RowV<E, NV>::NW == 2) {
+        const uint2 v = *(const uint2*)p;
+        r.u[0] = v.x, r.u[1] = v.y;
+    } else {
+#pragma unroll
+        for (int k = 0; k < RowV<E, NV>::NW / 4; ++k) {
+            const uint4 v = ((const uint4*)p)[k];
+            r.u[4 * k] = v.x, r.u[4 * k + 1] = v.y, r.u[4 * k + 2] = v.z, r.u[4 * k + 3] = v.w;
+        }
+    }
+    return r;
+}
+template <typename E, int NV>
+__device__ __forceinline__ RowV<E, NV> zero_row() {
+    RowV<E, NV> r;
+#pragma unroll
+    for (int k = 0; k < RowV<E, NV>::NW; ++k) r.u[k] = 0u;
+    return r;
+}
+template <typename E, int NV>
+__device__ __forceinline__ void st_row(E* p, const RowV<E, NV>& r) {
+    if constexpr (RowV<E, NV>::NW == 2) {
+        *(uint2*)p = uint2{r.u[0], r.u[1]};
+    } else {
+#pragma unroll
+        for (int k = 0; k < RowV<E, NV>::NW / 4; ++k)
+            ((uint4*)p)[k] = uint4{r.u[4 * k], r.u[4 * k + 1], r.u[4 * k + 2], r.u[4 * k + 3]};
+    }
+}
+template <int NV>
+__device__ __forceinline__ float elem(const RowV<bf16, NV>& r, int i) {
+    const unsigned w = r.u[i >> 1];
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+template <int NV>
+__device__ __forceinline__ float elem(const RowV<float, NV>& r, int i) {
+    return __uint_as_float(r.u[i]);
+}
+// store NV floats as E (bf16: round to nearest even)
+template <typename E, int NV>
+__device__ __forceinline__ void st_vals(E* p, const float* v) {
+    RowV<E, NV> r;
+    if constexpr (sizeof(E) == 2) {
+#pragma unroll
+        for (int k = 0; k < NV / 2; ++k) {
+            const bf16 lo = (bf16)v[2 * k], hi = (bf16)v[2 * k + 1];
+            r.u[k] = (unsigned)__builtin_bit_cast(unsigned short, lo) |
+                     ((unsigned)__builtin_bit_cast(unsigned short, hi) << 16);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) r.u[k] = __float_as_uint(v[k]);
+    }
+    st_row<E, NV>(p, r);
+}
+
+__device__ __forceinline__ float act_f(float z, int act) { return act ? z / (1.f + __expf(-z)) : z; }
+__device__ __forceinline__ float act_d(float z, int act) {
+    if (!act) return 1.f;
+    const float s = 1.f / (1.f + __expf(-z));
+    return s * (1.f + z * (1.f - s));
+}
+
+// Row of token t (channels c0 .. c0 + NV - 1) of xe: x for 0 <= t < T, the carried
+// state for -(W-1) <= t < 0 (zero when absent), zero past the chunk.
+template <typename E, int W, int NV>
+__device__ __forceinline__ RowV<E, NV> xe_row(const ConvArgs<E>& a, int b, int t, int c0) {
+    if (t >= 0 && t < a.T) return ld_row<E, NV>(a.x + ((size_t)b * a.T + t) * a.C + c0);
+    if (t < 0 && a.state_in) return ld_row<E, NV>(a.state_in + ((size_t)b * (W - 1) + (W - 1 + t)) * a.C + c0);
+    return zero_row<E, NV>();
+}
+
+template <typename E, int W, int TT>
+__global__ __launch_bounds__(128) void shortconv_fwd_kernel(ConvArgs<E> a) {
+    constexpr int NV = 8;  // channels per thread
+    const int cg = blockIdx.x * 128 + threadIdx.x;
+    if (cg * NV >= a.C) return;
+    const int c0 = cg * NV, b = blockIdx.z, t0 = blockIdx.y * TT, T = a.T, C = a.C;
+    constexpr int NR = TT + W - 1;  // rows: tokens t0 - W + 1 .. t0 + TT - 1
+    RowV<E, NV> raw[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) raw[r] = xe_row<E, W, NV>(a, b, t0 - W + 1 + r, c0);
+    float w[W][NV], bias[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        bias[i] = a.bias ? a.bias[c0 + i] : 0.f;
+#pragma unroll
+        for (int j = 0; j < W; ++j) w[j][i] = a.w[(size_t)(c0 + i) * W + j];
+    }
+#pragma unroll
+    for (int k = 0; k < TT; ++k) {
+        const int t = t0 + k;
+        if (t < T) {
+            float z[NV];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                float acc = bias[i];
+#pragma unroll
+                for (int j = 0; j < W; ++j) acc += w[j][i] * elem(raw[k + j], i);
+                z[i] = act_f(acc, a.act);
+            }
+            st_vals<E, NV>(a.y + ((size_t)b * T + t) * C + c0, z);
+        }
+    }
+    // state_out = xe rows of tokens T - W + 1 .. T - 1, written by the tile
+    // that holds the last token (row r of raw is token t0 - W + 1 + r)
+    if (W > 1 && a.state_out && t0 <= T - 1 && T - 1 < t0 + TT) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int k = r - (T - t0);  // state row of raw row r
+            if (k >= 0 && k < W - 1) st_row<E, NV>(a.state_out + ((size_t)b * (W - 1) + k) * C + c0, raw[r]);
+        }
+    }
+}
+
+// Backward.  Each thread walks the tiles blockIdx.y, blockIdx.y + gridDim.y,
+// ... of its batch and channels, and leaves its weight / bias gradient sums in
+// one row of the partial table (reduced in a fixed order afterwards).
+//   dz_t   = dy_t * act'(z_t)
+//   dx_s   = [dstate_out row s + W - 1 - T] + sum_j w[j] dz_{s + W - 1 - j}
+//            (j ascending, i.e. the latest token first, terms with
+//             0 <= token < T only), so that a chunk's dstate_in continues the
+//            same left fold in the previous chunk: chunked runs give the
+//            unchunked bits
+//   dstate_in rows r < W - 1 likewise with dz_{r - j}
+//   dw[j] += dz_t xe[t + j],  dbias += dz_t.
+template <typename E, int W, int TT>
+__global__ __launch_bounds__(128) void shortconv_bwd_kernel(ConvArgs<E> a) {
+    constexpr int NV = CONV_BWD_NV;  // channels per thread
+    const int cg = blockIdx.x * 128 + threadIdx.x;
+    if (cg * NV >= a.C) return;
+    const int c0 = cg * NV, b = blockIdx.z, T = a.T, C = a.C;
+    const int ntiles = (T + TT - 1) / TT;
+    float w[W][NV], bias[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        bias[i] = a.bias ? a.bias[c0 + i] : 0.f;
+#pragma unroll
+        for (int j = 0; j < W; ++j) w[j][i] = a.w[(size_t)(c0 + i) * W + j];
+    }
+    float dwp[W][NV], dbp[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        dbp[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < W; ++j) dwp[j][i] = 0.f;
+    }
+    constexpr int ND = TT + W - 1;       // dz of tokens t0 .. t0 + TT + W - 2
+    constexpr int NX = TT + 2 * W - 2;   // xe of tokens t0 - W + 1 .. t0 + TT + W - 2
+    for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
+        const int t0 = tile * TT;
+        RowV<E, NV> xr[NX], dyr[ND];
+#pragma unroll
+        for (int r = 0; r < NX; ++r) xr[r] = xe_row<E, W, NV>(a, b, t0 - W + 1 + r, c0);
+#pragma unroll
+        for (int m = 0; m < ND; ++m) {
+            const int t = t0 + m;
+            dyr[m] = t < T ? ld_row<E, NV>(a.dy + ((size_t)b * T + t) * C + c0) : zero_row<E, NV>();
+        }
+        float dz[ND][NV];
+#pragma unroll
+        for (int m = 0; m < ND; ++m)
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                float z = bias[i];
+#pragma unroll
+                for (int j = 0; j < W; ++j) z += w[j][i] * elem(xr[m + j], i);  // xe of token t0 + m - W + 1 + j
+                dz[m][i] = (t0 + m < T) ? elem(dyr[m], i) * act_d(z, a.act) : 0.f;
+            }
+        // weight and bias gradients over this tile's tokens
+#pragma unroll
+        for (int m = 0; m < TT; ++m)
+            if (t0 + m < T) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    dbp[i] += dz[m][i];
+#pragma unroll
+                    for (int j = 0; j < W; ++j) dwp[j][i] += dz[m][i] * elem(xr[m + j], i);
+                }
+            }
+        // dx of the tile's tokens
+#pragma unroll
+        for (int k = 0; k < TT; ++k) {
+            const int s = t0 + k;
+            if (s < T) {
+                float acc[NV];
+                const int so = s + W - 1 - T;  // state_out row fed by token s
+                if (so >= 0 && a.dstate_out) {
+                    const RowV<float, NV> d = ld_row<float, NV>(a.dstate_out + ((size_t)b * (W - 1) + so) * C + c0);
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) acc[i] = elem(d, i);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                    const int m = k + W - 1 - j;  // token s + W - 1 - j
+                    if (t0 + m < T) {
+#pragma unroll
+                        for (int i = 0; i < NV; ++i) acc[i] += w[j][i] * dz[m][i];
+                    }
+                }
+                st_vals<E, NV>(a.dx + ((size_t)b * T + s) * C + c0, acc);
+            }
+        }
+        // gradient of the carried state (xe rows 0 .. W - 2), from tile 0
+        if (W > 1 && tile == 0) {
+#pragma unroll
+            for (int r = 0; r < W - 1; ++r) {
+                float acc[NV];
+                if (r >= T && a.dstate_out) {
+                    const RowV<float, NV> d = ld_row<float, NV>(a.dstate_out + ((size_t)b * (W - 1) + (r - T)) * C + c0);
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) acc[i] = elem(d, i);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                    const int m = r - j;  // token r - j
+                    if (m >= 0 && m < T) {
+#pragma unroll
+                        for (int i = 0; i < NV; ++i) acc[i] += w[j][i] * dz[m][i];
+                    }
+                }
+                st_vals<float, NV>(a.dstate_in + ((size_t)b * (W - 1) + r) * C + c0, acc);
+            }
+        }
+    }
+    // partial row p = b * gridDim.y + blockIdx.y: [C][W + 1] (taps, then bias)
+    float* part = a.part + ((size_t)b * gridDim.y + blockIdx.y) * C * (W + 1) + (size_t)c0 * (W + 1);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+#pragma unroll
+        for (int j = 0; j < W; ++j) part[i * (W + 1) + j] = dwp[j][i];
+        part[i * (W + 1) + W] = dbp[i];
+    }
+}
+
+// dw[c][j] (= or +=) sum over the P partial rows in order; likewise dbias.
+__global__ __launch_bounds__(256) void shortconv_reduce_kernel(const float* part, int P, int C, int W, float* dw,
+                                                               float* dbias, int accumulate) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int n = C * (W + 1);
+    if (e >= n) return;
+    float s = 0.f;
+    for (int p = 0; p < P; ++p) s += part[(size_t)p * n + e];
+    const int c = e / (W + 1), j = e % (W + 1);
+    if (j < W) {
+        float* o = dw + (size_t)c * W + j;
+        *o = accumulate ? *o + s : s;
+    } else if (dbias) {
+        dbias[c] = accumulate ? dbias[c] + s : s;
+    }
+}
+
+template <typename E, int W>
+hipError_t fwd_t(const ConvArgs<E>& a, hipStream_t st) {
+    constexpr int TT = sizeof(E) == 2 ? 16 : 8;
+    const dim3 grid((a.C / 8 + 127) / 128, (a.T + TT - 1) / TT, a.B);
+    launch("shortconv_fwd", shortconv_fwd_kernel<E, W, TT>, grid, dim3(128), st, a);
+    return hipGetLastError();
+}
+
+template <typename E, int W>
+hipError_t bwd_t(const ConvArgs<E>& a, int accumulate, hipStream_t st) {
+    constexpr int TT = CONV_BWD_TT;
+    const dim3 grid((a.C / CONV_BWD_NV + 127) / 128, conv_bwd_tile_groups(a.B, a.T, a.C, TT), a.B);
+    launch("shortconv_bwd", shortconv_bwd_kernel<E, W, TT>, grid, dim3(128), st, a);
+    const int P = a.B * (int)grid.y, n = a.C * (W + 1);
+    launch("shortconv_reduce", shortconv_reduce_kernel, dim3((n + 255) / 256), dim3(256), st, (const float*)a.part, P,
+           a.C, W, a.dw, a.dbias, accumulate);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename E>
+hipError_t launch_shortconv_fwd(const ConvArgs<E>& a, hipStream_t st) {
+    switch (a.W) {
+        case 1: return fwd_t<E, 1>(a, st);
+        case 2: return fwd_t<E, 2>(a, st);
+        case 3: return fwd_t<E, 3>(a, st);
+        case 4: return fwd_t<E, 4>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+template <typename E>
+hipError_t launch_shortconv_bwd(const ConvArgs<E>& a, int accumulate, hipStream_t st) {
+    switch (a.W) {
+        case 1: return bwd_t<E, 1>(a, accumulate, st);
+        case 2: return bwd_t<E, 2>(a, accumulate, st);
+        case 3: return bwd_t<E, 3>(a, accumulate, st);
+        case 4: return bwd_t<E, 4>(a, accumulate, st);
+    }
+    return hipErrorInvalidValue;
+}
+template hipError_t launch_shortconv_fwd<bf16>(const ConvArgs<bf16>&, hipStream_t);
+template hipError_t launch_shortconv_fwd<float>(const ConvArgs<float>&, hipStream_t);
+template hipError_t launch_shortconv_bwd<bf16>(const ConvArgs<bf16>&, int, hipStream_t);
+template hipError_t launch_shortconv_bwd<float>(const ConvArgs<float>&, int, hipStream_t);
+
+}  // namespace clr

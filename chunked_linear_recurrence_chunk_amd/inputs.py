@@ -11,6 +11,11 @@ Distributions (per-token tensors are [B,T,H,d], states [B,H,dk,dv]):
   GLA:            q, k, v ~ N(0,1); g = logsigmoid(N(0,1)) / 16 per key channel;
                   S_in = 0.1 * N(0,1); dO ~ N(0,1); dS_out ~ N(0,1).
   Mamba-2:        as GLA, but one gate per (token, head): g [B,T,H].
+  Short conv:     x ~ N(0,1) [B,T,C]; w = 0.5 * N(0,1) [C,W]; bias = 0.1 * N(0,1);
+                  state_in ~ N(0,1) [B,W-1,C]; dy ~ N(0,1); dstate_out ~ N(0,1)
+                  (float32: state gradients are partial sums and stay fp32).
+                  The workload has C = H * (2 dk + dv) = 6144 channels, the q, k
+                  and v projections of the Gated DeltaNet workload, W = 4, SiLU.
 Draw order: q, k, v, g, beta (GDN only), S_in, dO, dS_out, all float32 from a
 numpy PCG64 generator.  For dtype "bf16" every per-token tensor (including dO)
 is rounded to bfloat16 (round-to-nearest-even) and returned as the exact
@@ -28,6 +33,8 @@ CONFIGS = {
     "gla_bf16_B4_H16_T4096_dk128_dv256": dict(kind="gla", dtype="bf16", B=4, H=16, T=4096, dk=128, dv=256, N=1),
     "gdn_bf16_H32_T65536_d128": dict(kind="gdn", dtype="bf16", B=1, H=32, T=65536, dk=128, dv=128, N=16),
     "gdn_bf16_H16_T262144_d128": dict(kind="gdn", dtype="bf16", B=1, H=16, T=262144, dk=128, dv=128, N=64),
+    # short convolution in front of the Gated DeltaNet workload (q, k, v channels)
+    "shortconv_bf16_T8192_C6144_W4": dict(kind="shortconv", dtype="bf16", B=1, T=8192, C=6144, W=4, act=1, N=4),
     # scalar-gate member at the GLA workload's shape
     "mamba2_bf16_B4_H16_T4096_dk128_dv256": dict(kind="mamba2", dtype="bf16", B=4, H=16, T=4096, dk=128, dv=256, N=1),
 }
@@ -138,6 +145,26 @@ def make_mamba2(B, T, H, dk, dv, dtype="bf16", seed=0, gate_scale=1.0 / 16.0):
     return d
 
 
+def make_shortconv(B, T, C, W, dtype="bf16", seed=0):
+    """Short-convolution inputs (x, w, bias, state_in, dy, dstate_out)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _normal(rng, (B, T, C))
+    w = (0.5 * _normal(rng, (C, W))).astype(np.float32)
+    bias = (0.1 * _normal(rng, (C,))).astype(np.float32)
+    state_in = _normal(rng, (B, W - 1, C))
+    dy = _normal(rng, (B, T, C))
+    dstate_out = _normal(rng, (B, W - 1, C))
+    d = dict(x=x, w=w, bias=bias, state_in=state_in, dy=dy, dstate_out=dstate_out)
+    if dtype == "bf16":
+        for key in ("x", "state_in", "dy"):
+            d[key] = bf16_round(d[key])
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return d
+
+
 def make(cfg: dict, seed: int, **kw):
+    if cfg["kind"] == "shortconv":
+        return make_shortconv(cfg["B"], cfg["T"], cfg["C"], cfg["W"], cfg["dtype"], seed)
     f = {"gdn": make_gdn, "gla": make_gla, "mamba2": make_mamba2}[cfg["kind"]]
     return f(cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], cfg["dtype"], seed, **kw)

@@ -26,6 +26,11 @@ class ClrShape(ctypes.Structure):
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class ClrConvShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("W", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
 class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
 
@@ -60,6 +65,13 @@ def load(path: Optional[str] = None):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 15 + [sz, vp]
         f.restype = i
+    cp = ctypes.POINTER(ClrConvShape)
+    lib.clr_shortconv_workspace_bytes.argtypes = [cp]
+    lib.clr_shortconv_workspace_bytes.restype = sz
+    lib.shortconv_fwd.argtypes = [cp] + [vp] * 7
+    lib.shortconv_fwd.restype = i
+    lib.shortconv_bwd.argtypes = [cp] + [vp] * 10 + [i, vp, sz, vp]
+    lib.shortconv_bwd.restype = i
     lib.clr_set_fwd_split.argtypes = [i]
     lib.clr_set_fwd_split.restype = i
     lib.clr_get_fwd_split.argtypes = []
@@ -242,6 +254,61 @@ def mamba2_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=No
 def mamba2_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None, out=None):
     """Scalar-gate (Mamba-2 member) chunk backward.  Returns dict dq, dk, dv, dg, dS_in."""
     return _bwd("mamba2_bwd", OP_M2_BWD, q, k, v, g, None, S_in, dO, dS_out, ws, out)
+
+
+def _conv_shape(x, w, act):
+    B, T, C = x.shape
+    return ClrConvShape(B, T, C, w.shape[1], _dtype_code(x), int(act))
+
+
+def shortconv_workspace_bytes(shape: ClrConvShape) -> int:
+    return int(load().clr_shortconv_workspace_bytes(ctypes.byref(shape)))
+
+
+def shortconv_fwd(x, w, bias=None, state_in=None, act=0, want_state=True, y=None, state_out=None):
+    """Causal short convolution with boundary state.  x [B,T,C] (bf16/fp32),
+    w [C,W] and bias [C] float32, state_in [B,W-1,C].  Returns (y, state_out)."""
+    import torch
+    _check_inputs(x, w, bias, state_in)
+    shape = _conv_shape(x, w, act)
+    B, T, C = x.shape
+    W = w.shape[1]
+    if w.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise TypeError("w and bias must be float32")
+    y = _out(y, (B, T, C), x.dtype, x.device)
+    if want_state or state_out is not None:
+        state_out = _out(state_out, (B, W - 1, C), x.dtype, x.device)
+    rc = load().shortconv_fwd(ctypes.byref(shape), _ptr(x), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(y),
+                              _ptr(state_out), _stream())
+    _check("shortconv_fwd", rc)
+    return y, state_out
+
+
+def shortconv_bwd(x, w, bias, state_in, dy, dstate_out=None, act=0, accumulate=False, out=None, ws=None):
+    """Gradients of shortconv_fwd: dict dx, dw, dbias (None without bias),
+    dstate_in (float32; dstate_out is float32 too).  With accumulate=True,
+    out["dw"] / out["dbias"] are added to."""
+    import torch
+    _check_inputs(x, w, bias, state_in, dy, dstate_out)
+    shape = _conv_shape(x, w, act)
+    B, T, C = x.shape
+    W = w.shape[1]
+    out = out or {}
+    dx = _out(out.get("dx"), (B, T, C), x.dtype, x.device)
+    dw = _out(out.get("dw"), (C, W), torch.float32, x.device)
+    dbias = _out(out.get("dbias"), (C,), torch.float32, x.device) if bias is not None else None
+    dstate_in = _out(out.get("dstate_in"), (B, W - 1, C), torch.float32, x.device)
+    if dstate_out is not None and dstate_out.dtype != torch.float32:
+        raise TypeError("dstate_out must be float32")
+    n = shortconv_workspace_bytes(shape)
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    rc = load().shortconv_bwd(ctypes.byref(shape), _ptr(x), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(dy),
+                              _ptr(dstate_out), _ptr(dx), _ptr(dw), _ptr(dbias),
+                              _ptr(dstate_in) if W > 1 else None, 1 if accumulate else 0, _ptr(ws),
+                              ws.numel(), _stream())
+    _check("shortconv_bwd", rc)
+    return dict(dx=dx, dw=dw, dbias=dbias, dstate_in=dstate_in)
 
 
 def probe_mma(A, Bt):

@@ -175,3 +175,56 @@ class Mamba2Chunked(GlaChunked):
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         self.saved = [None] * N
         self._fwd, self._bwd = ops.mamba2_fwd, ops.mamba2_bwd
+
+
+class ShortConvChunked:
+    """Causal short convolution over N sequence chunks: the forward hands the
+    last W - 1 input rows on as the next chunk's boundary state, the backward
+    hands dstate_in back and accumulates dw / dbias over the chunks (the
+    local-convolution boundary state of the StateFlow paper, Sec. 3.3)."""
+
+    def __init__(self, x, w, bias, N: int, act: int = 1):
+        from . import ops
+        self.ops = ops
+        self.x, self.w, self.bias, self.act, self.N = x, w, bias, act, N
+        self.bounds = _bounds(x.shape[1], N)
+        self.saved = [None] * N
+
+    def _chunk(self, t, i):
+        a, b = self.bounds[i]
+        return _sl(t, a, b)
+
+    def forward(self, state_in=None, y=None):
+        import torch
+        if y is None:
+            y = torch.empty_like(self.x)
+        st = state_in
+        for i in range(self.N):
+            a, b = self.bounds[i]
+            self.saved[i] = st
+            view = y[:, a:b]
+            yi, st = self.ops.shortconv_fwd(self._chunk(self.x, i), self.w, self.bias, st, self.act,
+                                            y=view if view.is_contiguous() else None)
+            if yi.data_ptr() != view.data_ptr():
+                view.copy_(yi)
+        return y, st
+
+    def backward(self, dy, dstate_out=None):
+        import torch
+        dx = torch.empty_like(self.x)
+        grads = dict(dw=torch.empty_like(self.w),
+                     dbias=torch.empty_like(self.bias) if self.bias is not None else None)
+        ds = dstate_out
+        for n, i in enumerate(reversed(range(self.N))):
+            a, b = self.bounds[i]
+            view = dx[:, a:b]
+            out = dict(dw=grads["dw"], dbias=grads["dbias"])
+            if view.is_contiguous():
+                out["dx"] = view
+            r = self.ops.shortconv_bwd(self._chunk(self.x, i), self.w, self.bias, self.saved[i],
+                                       self._chunk(dy, i), ds, self.act, accumulate=n > 0, out=out)
+            if r["dx"].data_ptr() != view.data_ptr():
+                view.copy_(r["dx"])
+            ds = r["dstate_in"]
+            self.saved[i] = None
+        return dict(dx=dx, dw=grads["dw"], dbias=grads["dbias"], dstate_in=ds)

@@ -144,6 +144,46 @@ int mamba2_bwd(const clr_shape_t* shape, const void* q, const void* k, const voi
                const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
                float* dS_in, void* ws, size_t ws_bytes, void* stream);
 
+/* Causal short convolution with a boundary state.
+ * The StateFlow paper (Sec. 1 and Sec. 3.3) hands the boundary state of a
+ * layer's local-convolution modules from one sequence chunk to the next,
+ * next to the recurrent state.  Here that convolution is the depthwise causal
+ * one of width W applied in front of such layers (the pages leave it
+ * unspecified; this is the plainest reading):
+ *     xe = [state_in ; x]                       (W - 1 carried rows first)
+ *     z_t = bias_c + sum_{j<W} w[c][j] xe[t + j],   y_t = act(z_t)
+ *     state_out = the last W - 1 rows of xe
+ * act: 0 = identity, 1 = SiLU (z * sigmoid(z)).  Chaining state_out ->
+ * state_in over sequence chunks reproduces the unchunked y, and chaining
+ * dstate_in -> dstate_out backward reproduces the unchunked dx, bit for bit;
+ * dw and dbias are sums over tokens (accumulate them over chunks with
+ * `accumulate` = 1).
+ * Layouts (contiguous, row-major, device memory):
+ *     x, y, dy, dx                    [B, T, C]    element type = dtype
+ *     state_in, state_out             [B, W-1, C]  element type = dtype
+ *                                                  (copies of input rows)
+ *     dstate_out, dstate_in           [B, W-1, C]  float32 (partial sums)
+ *     w, dw [C, W] and bias, dbias [C]             float32
+ * C must be a multiple of 8 and 1 <= W <= 4.  Nullable: bias (zero),
+ * state_in (zero), state_out (not wanted), dstate_out (zero), dbias (not
+ * wanted), dstate_in when W == 1.  All pointers 16-byte aligned.
+ * The backward needs a workspace of clr_shortconv_workspace_bytes() bytes.
+ * Errors as for the layer entry points (validated before any launch). */
+typedef struct {
+    int32_t B, T, C, W;
+    int32_t dtype; /* clr_dtype_t of x, y, the states and their gradients */
+    int32_t act;   /* 0 = identity, 1 = SiLU */
+} clr_conv_shape_t;
+
+size_t clr_shortconv_workspace_bytes(const clr_conv_shape_t* shape);
+int shortconv_fwd(const clr_conv_shape_t* shape, const void* x, const float* w, const float* bias,
+                  const void* state_in, void* y, void* state_out, void* stream);
+/* dw and dbias are overwritten (accumulate = 0) or added to (accumulate = 1). */
+int shortconv_bwd(const clr_conv_shape_t* shape, const void* x, const float* w, const float* bias,
+                  const void* state_in, const void* dy, const float* dstate_out, void* dx, float* dw,
+                  float* dbias, float* dstate_in, int accumulate, void* ws, size_t ws_bytes,
+                  void* stream);
+
 /* Split-and-overlap forward (StateFlow paper, Sec. 3.4.2, "Split and
  * Overlap", forward wavefront).  gdn_fwd with o != NULL and at least 16
  * 64-token blocks splits its blocks into two parts at `permille`/1000 of the

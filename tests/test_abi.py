@@ -131,6 +131,36 @@ def test_bwd_validation():
     assert lib.gdn_bwd(ctypes.byref(s64), *ptrs, 1 << 40, None) == ops.CLR_ENOTSUP
 
 
+def test_mamba2_and_shortconv_validation():
+    ops, lib = _lib()
+    s = _shape(ops, T=64, H=1, dk=32, dv=32)
+    assert _fwd(lib, ops, s, name="mamba2_fwd") == ops.CLR_EINVAL               # beta must be NULL
+    assert _fwd(lib, ops, _shape(ops, dk=96, dv=96), beta=None, name="mamba2_fwd") == ops.CLR_ENOTSUP
+    assert ops.workspace_bytes(_shape(ops, dk=128, dv=256), ops.OP_M2_BWD) == \
+        ops.workspace_bytes(_shape(ops, dk=128, dv=256), ops.OP_GLA_BWD)
+    cs = ops.ClrConvShape(2, 100, 64, 4, 1, 1)
+    assert ops.shortconv_workspace_bytes(cs) > 0
+    for bad in (ops.ClrConvShape(2, 100, 60, 4, 1, 1),   # C not a multiple of 8
+                ops.ClrConvShape(2, 100, 64, 5, 1, 1),   # W > 4
+                ops.ClrConvShape(2, 100, 64, 4, 1, 2),   # unknown activation
+                ops.ClrConvShape(2, 100, 64, 4, 7, 1)):  # dtype
+        assert ops.shortconv_workspace_bytes(bad) == 0
+        assert lib.shortconv_fwd(ctypes.byref(bad), *[_fake(0x10000 * (i + 1)) for i in range(6)], None) == \
+            ops.CLR_ENOTSUP
+    f = [_fake(0x100000 * (i + 1)) for i in range(6)]
+    assert lib.shortconv_fwd(ctypes.byref(cs), None, *f[1:], None) == ops.CLR_EINVAL     # x missing
+    al = list(f)
+    al[4] = al[0]                                                                   # y aliases x
+    assert lib.shortconv_fwd(ctypes.byref(cs), *al, None) == ops.CLR_EINVAL
+    b = [_fake(0x1000000 * (i + 1)) for i in range(10)]
+    nws = ops.shortconv_workspace_bytes(cs)
+    assert lib.shortconv_bwd(ctypes.byref(cs), *b, 0, _fake(0x20000000), nws - 256, None) == ops.CLR_EWORKSPACE
+    assert lib.shortconv_bwd(ctypes.byref(cs), *b, 2, _fake(0x20000000), nws, None) == ops.CLR_EINVAL
+    nb = list(b)
+    nb[9] = None                                                                    # dstate_in needed (W > 1)
+    assert lib.shortconv_bwd(ctypes.byref(cs), *nb, 0, _fake(0x20000000), nws, None) == ops.CLR_EINVAL
+
+
 def test_product_path_has_no_oracle_or_fallback():
     """The package never imports the oracle and the binding refuses to run
     without the built library."""
