@@ -19,7 +19,7 @@ template <typename E> struct ConvArgs {
     E* dx;
     float* dstate_in;
     float *dw, *dbias;
-    float* part;  // [B * tile groups][C][W + 1] partial weight / bias gradients
+    float* part;  // [B * tile groups][W + 1][C] partial weight / bias gradients
 };
 
 // Channels per thread and tokens per tile of the backward (the tile's rows

@@ -85,39 +85,93 @@ __device__ __forceinline__ void st_vals(E* p, const float* v) {
     st_row<E, NV>(p, r);
 }
 
-__device__ __forceinline__ float act_f(float z, int act) { return act ? z / (1.f + __expf(-z)) : z; }
-__device__ __forceinline__ float act_d(float z, int act) {
-    if (!act) return 1.f;
-    const float s = 1.f / (1.f + __expf(-z));
-    return s * (1.f + z * (1.f - s));
+// SiLU and its derivative with the hardware reciprocal (about 1 ulp) instead
+// of an IEEE division: the division sequence alone would make these
+// element-wise kernels VALU-bound.  exp(-z) = inf for very negative z gives
+// s = 0, the correct limit.
+template <int ACT> __device__ __forceinline__ float act_f(float z) {
+    if constexpr (ACT == 0) return z;
+    else return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
+template <int ACT> __device__ __forceinline__ float act_d(float z) {
+    if constexpr (ACT == 0) return 1.f;
+    else {
+        const float s = __builtin_amdgcn_rcpf(1.f + __expf(-z));
+        return s * (1.f + z * (1.f - s));
+    }
 }
 
 // Row of token t (channels c0 .. c0 + NV - 1) of xe: x for 0 <= t < T, the carried
 // state for -(W-1) <= t < 0 (zero when absent), zero past the chunk.
+// The load is unconditional (from a selected, always valid address) so that
+// a tile's row loads issue back to back without branches between them.
 template <typename E, int W, int NV>
 __device__ __forceinline__ RowV<E, NV> xe_row(const ConvArgs<E>& a, int b, int t, int c0) {
-    if (t >= 0 && t < a.T) return ld_row<E, NV>(a.x + ((size_t)b * a.T + t) * a.C + c0);
-    if (t < 0 && a.state_in) return ld_row<E, NV>(a.state_in + ((size_t)b * (W - 1) + (W - 1 + t)) * a.C + c0);
-    return zero_row<E, NV>();
+    const bool in_x = t >= 0 && t < a.T, in_s = t < 0 && a.state_in != nullptr;
+    const E* px = a.x + ((size_t)b * a.T + (in_x ? t : 0)) * a.C + c0;
+    const E* ps = in_s ? a.state_in + ((size_t)b * (W - 1) + (W - 1 + t)) * a.C + c0 : px;
+    RowV<E, NV> r = ld_row<E, NV>(in_x ? px : ps);
+    if (!in_x && !in_s) r = zero_row<E, NV>();
+    return r;
 }
 
-template <typename E, int W, int TT>
-__global__ __launch_bounds__(128) void shortconv_fwd_kernel(ConvArgs<E> a) {
-    constexpr int NV = 8;  // channels per thread
-    const int cg = blockIdx.x * 128 + threadIdx.x;
-    if (cg * NV >= a.C) return;
-    const int c0 = cg * NV, b = blockIdx.z, t0 = blockIdx.y * TT, T = a.T, C = a.C;
-    constexpr int NR = TT + W - 1;  // rows: tokens t0 - W + 1 .. t0 + TT - 1
-    RowV<E, NV> raw[NR];
+// The taps and bias of this work-group's channels [cb0, cb0 + 128 NV), staged
+// through LDS with coalesced loads (w is [C][W] row-major, so the block's taps
+// are one contiguous run), then read per thread into registers.
+template <int W, int NV>
+__device__ __forceinline__ void load_taps(const float* __restrict__ wg, const float* __restrict__ bg, int C,
+                                          float (&w)[W][NV], float (&bias)[NV]) {
+    __shared__ __align__(16) float sw[128 * NV * W], sb[128 * NV];
+    const int cb0 = blockIdx.x * 128 * NV, nch = min(128 * NV, C - cb0);  // nch: a multiple of 8
+    // float4 loads with compile-time trip counts, all issued before the first
+    // wait (a runtime-bounded loop would wait for each load in turn)
+    constexpr int NW4 = NV * W / 4, NB4 = NV / 4;
+    float4 tw[NW4], tb[NB4];
+    const float4* w4 = (const float4*)(wg + (size_t)cb0 * W);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) raw[r] = xe_row<E, W, NV>(a, b, t0 - W + 1 + r, c0);
-    float w[W][NV], bias[NV];
+    for (int k = 0; k < NW4; ++k) {
+        const int e = threadIdx.x + 128 * k;
+        tw[k] = e < nch * W / 4 ? w4[e] : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < NB4; ++k) {
+        const int e = threadIdx.x + 128 * k;
+        tb[k] = (bg && e < nch / 4) ? ((const float4*)(bg + cb0))[e] : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < NW4; ++k) ((float4*)sw)[threadIdx.x + 128 * k] = tw[k];
+#pragma unroll
+    for (int k = 0; k < NB4; ++k) ((float4*)sb)[threadIdx.x + 128 * k] = tb[k];
+    __syncthreads();
+    const int l0 = threadIdx.x * NV;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        bias[i] = a.bias ? a.bias[c0 + i] : 0.f;
+        bias[i] = l0 + i < nch ? sb[l0 + i] : 0.f;
 #pragma unroll
-        for (int j = 0; j < W; ++j) w[j][i] = a.w[(size_t)(c0 + i) * W + j];
+        for (int j = 0; j < W; ++j) w[j][i] = l0 + i < nch ? sw[(l0 + i) * W + j] : 0.f;
     }
+}
+
+template <typename E, int W, int TT, int ACT>
+__global__ __launch_bounds__(128) void shortconv_fwd_kernel(ConvArgs<E> a) {
+    constexpr int NV = 4;  // channels per thread
+    const int cg = blockIdx.x * 128 + threadIdx.x;
+    const bool active = cg * NV < a.C;
+    const int c0 = active ? cg * NV : 0, b = blockIdx.z, t0 = blockIdx.y * TT, T = a.T, C = a.C;
+    constexpr int NR = TT + W - 1;  // rows: tokens t0 - W + 1 .. t0 + TT - 1
+    // the tile's row loads go out first; the taps are staged meanwhile
+    RowV<E, NV> raw[NR];
+    if (t0 >= W - 1 && t0 + TT <= T) {  // interior tile: every row is in x
+        const E* xb = a.x + ((size_t)b * T + (t0 - W + 1)) * C + c0;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) raw[r] = ld_row<E, NV>(xb + (size_t)r * C);
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) raw[r] = xe_row<E, W, NV>(a, b, t0 - W + 1 + r, c0);
+    }
+    float w[W][NV], bias[NV];
+    load_taps<W, NV>(a.w, a.bias, a.C, w, bias);
+    if (!active) return;
 #pragma unroll
     for (int k = 0; k < TT; ++k) {
         const int t = t0 + k;
@@ -128,7 +182,7 @@ __global__ __launch_bounds__(128) void shortconv_fwd_kernel(ConvArgs<E> a) {
                 float acc = bias[i];
 #pragma unroll
                 for (int j = 0; j < W; ++j) acc += w[j][i] * elem(raw[k + j], i);
-                z[i] = act_f(acc, a.act);
+                z[i] = act_f<ACT>(acc);
             }
             st_vals<E, NV>(a.y + ((size_t)b * T + t) * C + c0, z);
         }
@@ -155,20 +209,16 @@ __global__ __launch_bounds__(128) void shortconv_fwd_kernel(ConvArgs<E> a) {
 //            unchunked bits
 //   dstate_in rows r < W - 1 likewise with dz_{r - j}
 //   dw[j] += dz_t xe[t + j],  dbias += dz_t.
-template <typename E, int W, int TT>
+template <typename E, int W, int TT, int ACT>
 __global__ __launch_bounds__(128) void shortconv_bwd_kernel(ConvArgs<E> a) {
     constexpr int NV = CONV_BWD_NV;  // channels per thread
+    static_assert(NV == 4, "partial rows are stored as one float4 per tap");
+    float w[W][NV], bias[NV];
+    load_taps<W, NV>(a.w, a.bias, a.C, w, bias);
     const int cg = blockIdx.x * 128 + threadIdx.x;
     if (cg * NV >= a.C) return;
     const int c0 = cg * NV, b = blockIdx.z, T = a.T, C = a.C;
     const int ntiles = (T + TT - 1) / TT;
-    float w[W][NV], bias[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        bias[i] = a.bias ? a.bias[c0 + i] : 0.f;
-#pragma unroll
-        for (int j = 0; j < W; ++j) w[j][i] = a.w[(size_t)(c0 + i) * W + j];
-    }
     float dwp[W][NV], dbp[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -181,12 +231,22 @@ __global__ __launch_bounds__(128) void shortconv_bwd_kernel(ConvArgs<E> a) {
     for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
         const int t0 = tile * TT;
         RowV<E, NV> xr[NX], dyr[ND];
+        if (t0 >= W - 1 && t0 + TT + W - 1 <= T) {  // interior tile: every row is in x and dy
+            const E* xb = a.x + ((size_t)b * T + (t0 - W + 1)) * C + c0;
+            const E* yb = a.dy + ((size_t)b * T + t0) * C + c0;
 #pragma unroll
-        for (int r = 0; r < NX; ++r) xr[r] = xe_row<E, W, NV>(a, b, t0 - W + 1 + r, c0);
+            for (int r = 0; r < NX; ++r) xr[r] = ld_row<E, NV>(xb + (size_t)r * C);
 #pragma unroll
-        for (int m = 0; m < ND; ++m) {
-            const int t = t0 + m;
-            dyr[m] = t < T ? ld_row<E, NV>(a.dy + ((size_t)b * T + t) * C + c0) : zero_row<E, NV>();
+            for (int m = 0; m < ND; ++m) dyr[m] = ld_row<E, NV>(yb + (size_t)m * C);
+        } else {
+#pragma unroll
+            for (int r = 0; r < NX; ++r) xr[r] = xe_row<E, W, NV>(a, b, t0 - W + 1 + r, c0);
+#pragma unroll
+            for (int m = 0; m < ND; ++m) {
+                const int t = t0 + m;
+                dyr[m] = ld_row<E, NV>(a.dy + ((size_t)b * T + (t < T ? t : T - 1)) * C + c0);
+                if (t >= T) dyr[m] = zero_row<E, NV>();
+            }
         }
         float dz[ND][NV];
 #pragma unroll
@@ -196,7 +256,7 @@ __global__ __launch_bounds__(128) void shortconv_bwd_kernel(ConvArgs<E> a) {
                 float z = bias[i];
 #pragma unroll
                 for (int j = 0; j < W; ++j) z += w[j][i] * elem(xr[m + j], i);  // xe of token t0 + m - W + 1 + j
-                dz[m][i] = (t0 + m < T) ? elem(dyr[m], i) * act_d(z, a.act) : 0.f;
+                dz[m][i] = (t0 + m < T) ? elem(dyr[m], i) * act_d<ACT>(z) : 0.f;
             }
         // weight and bias gradients over this tile's tokens
 #pragma unroll
@@ -260,25 +320,30 @@ __global__ __launch_bounds__(128) void shortconv_bwd_kernel(ConvArgs<E> a) {
             }
         }
     }
-    // partial row p = b * gridDim.y + blockIdx.y: [C][W + 1] (taps, then bias)
-    float* part = a.part + ((size_t)b * gridDim.y + blockIdx.y) * C * (W + 1) + (size_t)c0 * (W + 1);
+    // partial row p = b * gridDim.y + blockIdx.y: [W + 1][C] (taps, then
+    // bias), so that a wave stores contiguous runs of channels
+    float* part = a.part + ((size_t)b * gridDim.y + blockIdx.y) * C * (W + 1) + c0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-#pragma unroll
-        for (int j = 0; j < W; ++j) part[i * (W + 1) + j] = dwp[j][i];
-        part[i * (W + 1) + W] = dbp[i];
-    }
+    for (int j = 0; j < W; ++j) *(float4*)(part + (size_t)j * C) = float4{dwp[j][0], dwp[j][1], dwp[j][2], dwp[j][3]};
+    *(float4*)(part + (size_t)W * C) = float4{dbp[0], dbp[1], dbp[2], dbp[3]};
 }
 
-// dw[c][j] (= or +=) sum over the P partial rows in order; likewise dbias.
+// dw[c][j] (= or +=) the sum over the P partial rows, likewise dbias.  Four
+// lanes share one output: lane q sums rows q, q + 4, ... in order, then the
+// four sums are added in the order q = 0..3 (deterministic).
 __global__ __launch_bounds__(256) void shortconv_reduce_kernel(const float* part, int P, int C, int W, float* dw,
                                                                float* dbias, int accumulate) {
-    const int e = blockIdx.x * 256 + threadIdx.x;
+    __shared__ float red[4][64];
     const int n = C * (W + 1);
-    if (e >= n) return;
+    const int el = threadIdx.x & 63, q = threadIdx.x >> 6, e = blockIdx.x * 64 + el;
     float s = 0.f;
-    for (int p = 0; p < P; ++p) s += part[(size_t)p * n + e];
-    const int c = e / (W + 1), j = e % (W + 1);
+    if (e < n)
+        for (int p = q; p < P; p += 4) s += part[(size_t)p * n + e];
+    red[q][el] = s;
+    __syncthreads();
+    if (q != 0 || e >= n) return;
+    s = ((red[0][el] + red[1][el]) + red[2][el]) + red[3][el];
+    const int j = e / C, c = e % C;  // tap-major partial layout [W + 1][C]
     if (j < W) {
         float* o = dw + (size_t)c * W + j;
         *o = accumulate ? *o + s : s;
@@ -290,8 +355,11 @@ __global__ __launch_bounds__(256) void shortconv_reduce_kernel(const float* part
 template <typename E, int W>
 hipError_t fwd_t(const ConvArgs<E>& a, hipStream_t st) {
     constexpr int TT = sizeof(E) == 2 ? 16 : 8;
-    const dim3 grid((a.C / 8 + 127) / 128, (a.T + TT - 1) / TT, a.B);
-    launch("shortconv_fwd", shortconv_fwd_kernel<E, W, TT>, grid, dim3(128), st, a);
+    const dim3 grid((a.C / 4 + 127) / 128, (a.T + TT - 1) / TT, a.B);
+    if (a.act)
+        launch("shortconv_fwd", shortconv_fwd_kernel<E, W, TT, 1>, grid, dim3(128), st, a);
+    else
+        launch("shortconv_fwd", shortconv_fwd_kernel<E, W, TT, 0>, grid, dim3(128), st, a);
     return hipGetLastError();
 }
 
@@ -299,9 +367,12 @@ template <typename E, int W>
 hipError_t bwd_t(const ConvArgs<E>& a, int accumulate, hipStream_t st) {
     constexpr int TT = CONV_BWD_TT;
     const dim3 grid((a.C / CONV_BWD_NV + 127) / 128, conv_bwd_tile_groups(a.B, a.T, a.C, TT), a.B);
-    launch("shortconv_bwd", shortconv_bwd_kernel<E, W, TT>, grid, dim3(128), st, a);
+    if (a.act)
+        launch("shortconv_bwd", shortconv_bwd_kernel<E, W, TT, 1>, grid, dim3(128), st, a);
+    else
+        launch("shortconv_bwd", shortconv_bwd_kernel<E, W, TT, 0>, grid, dim3(128), st, a);
     const int P = a.B * (int)grid.y, n = a.C * (W + 1);
-    launch("shortconv_reduce", shortconv_reduce_kernel, dim3((n + 255) / 256), dim3(256), st, (const float*)a.part, P,
+    launch("shortconv_reduce", shortconv_reduce_kernel, dim3((n + 63) / 64), dim3(256), st, (const float*)a.part, P,
            a.C, W, a.dw, a.dbias, accumulate);
     return hipGetLastError();
 }
