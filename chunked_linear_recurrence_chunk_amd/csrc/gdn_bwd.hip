@@ -370,8 +370,8 @@ template <typename E, int DK, int DV> struct IntraLds {
     static constexpr size_t o_KKG = o_Ks + sizeof(E) * BLK * PK;       // f32[64][AP]   (K K^T * G), strictly lower
     static constexpr size_t o_TT = o_KKG + 4 * BLK * AP;               // E[64][PT]     TT[s][t] = T[t][s]
     static constexpr size_t o_Tr = o_TT + sizeof(E) * BLK * PT;        // E[64][PT]     T row-major
-    static constexpr size_t o_E = o_Tr + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms), + 256 spare
-    static constexpr size_t o_U = o_E + 4 * (BLK * 65 + 256);          // union starts here
+    static constexpr size_t o_E = o_Tr + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms), + 512 spare
+    static constexpr size_t o_U = o_E + 4 * (BLK * 65 + 512);          // union starts here
     // phase 0: Am f32[64][AP], Td f32[4][16][16]
     static constexpr size_t p0_Am = o_U, p0_Td = p0_Am + 4 * BLK * AP;
     static constexpr size_t p0_end = p0_Td + 4 * 4 * 256;
@@ -774,22 +774,23 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     //   dg_u = sum_{t>=u} y_t + sum_{t>=u>s} E[t][s] + sum_{r<u} z_r + Gam_C <h_n, dh_n>
     // with y_t the S0 -> token-t terms, E the pair terms (dP*P + dA*A) and
     // z_r = kh_r . (U dh^T)_r the Kh-path terms.
-    // F_u = sum_{t >= u} sum_{s < u} E[t][s]: waves 0..3 take rows t = 16w..16w+15,
+    // F_u = sum_{t >= u} sum_{s < u} E[t][s]: wave w8 takes rows t = 8 w8 .. 8 w8 + 7,
     // lane = column u; each row's exclusive prefix over s is a wave scan.
-    if (w8 < 4) {
+    {
         float Fp = 0.f;
 #pragma unroll 4
-        for (int i = 0; i < 16; ++i) {
-            const int t = 16 * w + i;
+        for (int i = 0; i < 8; ++i) {
+            const int t = 8 * w8 + i;
             const float e = Eb[t * 65 + l];
             const float ex = wave_prefix_sum(e) - e;
             if (t >= l) Fp += ex;
         }
-        Eb[64 * 65 + w * 64 + l] = Fp;  // spare row after E: the four wave partials
+        Eb[64 * 65 + w8 * 64 + l] = Fp;  // spare rows after E: the eight wave partials
     }
     __syncthreads();
     if (w8 == 0) {
-        const float F = Eb[64 * 65 + l] + Eb[64 * 65 + 64 + l] + Eb[64 * 65 + 128 + l] + Eb[64 * 65 + 192 + l];
+        const float* Fw = Eb + 64 * 65 + l;
+        const float F = ((Fw[0] + Fw[64]) + (Fw[128] + Fw[192])) + ((Fw[256] + Fw[320]) + (Fw[384] + Fw[448]));
         // reverse inclusive scan of y: lane l sums y over lanes >= l
         float x = s_y[l];
 #pragma unroll
