@@ -88,12 +88,16 @@ def shortconv_work(name: str, B: int, Tc: int, C: int, W: int, es: int, P: int):
     return None
 
 
-def _conv_tile_groups(B: int, T: int, C: int, tt: int = 8, nv: int = 4) -> int:
-    """Tile groups per batch of the short-convolution backward grid (the
-    rule of the library's launcher: about 512 work-groups of 128 threads)."""
+def _conv_tile_groups(B: int, T: int, C: int, tt: int = 4, nv: int = 4, tg: int = 4) -> int:
+    """Work-groups per batch along the tokens of the short-convolution
+    backward grid: the partial rows it writes (the rule of the library's
+    launcher: about 8 waves per CU, each thread a contiguous run of tiles,
+    tg token groups per work-group summed in LDS)."""
     ntiles = (T + tt - 1) // tt
-    gx = (C // nv + 127) // 128
-    return max(1, min(ntiles, 512 // (gx * B)))
+    want = max(1, min(ntiles, (256 * 8 * 64) // max(1, B * (C // nv))))
+    per = -(-ntiles // want)
+    groups = -(-ntiles // per)
+    return -(-groups // tg)
 
 
 def source_hash() -> str:

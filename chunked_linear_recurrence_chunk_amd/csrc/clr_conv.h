@@ -20,21 +20,26 @@ template <typename E> struct ConvArgs {
     float* dstate_in;
     float *dw, *dbias;
     float* part;  // [B * tile groups][W + 1][C] partial weight / bias gradients
+    int tpg;      // backward: tiles per group (each thread walks one run of tiles)
 };
 
-// Channels per thread and tokens per tile of the backward (the tile's rows
-// stay in registers).
-constexpr int CONV_BWD_NV = 4, CONV_BWD_TT = 8;
+// Backward geometry: 4 channels per thread, 4-token tiles, work-groups of
+// CONV_BWD_TG token groups x 128 threads.
+constexpr int CONV_BWD_NV = 4, CONV_BWD_TT = 4, CONV_BWD_TG = 4;
 
-// Tile groups per batch of the backward grid: about 512 work-groups of 128
-// threads in total, at most one per tile.
-inline int conv_bwd_tile_groups(int B, int T, int C, int tt) {
+// Work-groups per batch along the tokens (grid y) of the backward, and the
+// tiles each thread walks (*tpg).  Aims at about 8 waves per CU in total
+// (256 CUs); every thread's run of tiles is non-empty except at the very end.
+inline int conv_bwd_tile_groups(int B, int T, int C, int tt, int* tpg = nullptr) {
     const int ntiles = (T + tt - 1) / tt;
-    const int gx = (C / CONV_BWD_NV + 127) / 128;
-    int g = 512 / (gx * B);
-    if (g < 1) g = 1;
-    if (g > ntiles) g = ntiles;
-    return g;
+    const long threads_per_group = (long)B * (C / CONV_BWD_NV);  // one token group across every channel
+    long want = (256L * 8 * 64) / (threads_per_group > 0 ? threads_per_group : 1);  // token groups wanted
+    if (want < 1) want = 1;
+    if (want > ntiles) want = ntiles > 0 ? ntiles : 1;
+    const int per = ntiles > 0 ? (int)((ntiles + want - 1) / want) : 1;
+    if (tpg) *tpg = per;
+    const int groups = ntiles > 0 ? (ntiles + per - 1) / per : 1;  // token groups in total
+    return (groups + CONV_BWD_TG - 1) / CONV_BWD_TG;
 }
 
 template <typename E> hipError_t launch_shortconv_fwd(const ConvArgs<E>& a, hipStream_t st);

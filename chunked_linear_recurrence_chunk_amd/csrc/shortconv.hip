@@ -118,11 +118,15 @@ __device__ __forceinline__ RowV<E, NV> xe_row(const ConvArgs<E>& a, int b, int t
 // The taps and bias of this work-group's channels [cb0, cb0 + 128 NV), staged
 // through LDS with coalesced loads (w is [C][W] row-major, so the block's taps
 // are one contiguous run), then read per thread into registers.
+// Work-groups of more than 128 threads stage with the first 128; thread
+// threadIdx.x % 128 owns channels NV * (threadIdx.x % 128) of the block.
 template <int W, int NV>
 __device__ __forceinline__ void load_taps(const float* __restrict__ wg, const float* __restrict__ bg, int C,
                                           float (&w)[W][NV], float (&bias)[NV]) {
     __shared__ __align__(16) float sw[128 * NV * W], sb[128 * NV];
     const int cb0 = blockIdx.x * 128 * NV, nch = min(128 * NV, C - cb0);  // nch: a multiple of 8
+    const int tx = threadIdx.x & 127;
+    if (threadIdx.x < 128) {
     // float4 loads with compile-time trip counts, all issued before the first
     // wait (a runtime-bounded loop would wait for each load in turn)
     constexpr int NW4 = NV * W / 4, NB4 = NV / 4;
@@ -142,8 +146,9 @@ __device__ __forceinline__ void load_taps(const float* __restrict__ wg, const fl
     for (int k = 0; k < NW4; ++k) ((float4*)sw)[threadIdx.x + 128 * k] = tw[k];
 #pragma unroll
     for (int k = 0; k < NB4; ++k) ((float4*)sb)[threadIdx.x + 128 * k] = tb[k];
+    }
     __syncthreads();
-    const int l0 = threadIdx.x * NV;
+    const int l0 = tx * NV;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         bias[i] = l0 + i < nch ? sb[l0 + i] : 0.f;
@@ -198,9 +203,10 @@ __global__ __launch_bounds__(128) void shortconv_fwd_kernel(ConvArgs<E> a) {
     }
 }
 
-// Backward.  Each thread walks the tiles blockIdx.y, blockIdx.y + gridDim.y,
-// ... of its batch and channels, and leaves its weight / bias gradient sums in
-// one row of the partial table (reduced in a fixed order afterwards).
+// Backward.  A work-group is CONV_BWD_TG token groups x 128 threads; thread
+// (tg, x) owns NV channels and the contiguous run of tiles
+// [(CONV_BWD_TG blockIdx.y + tg) tpg, +tpg) of its batch, walked from the
+// top down:
 //   dz_t   = dy_t * act'(z_t)
 //   dx_s   = [dstate_out row s + W - 1 - T] + sum_j w[j] dz_{s + W - 1 - j}
 //            (j ascending, i.e. the latest token first, terms with
@@ -209,16 +215,25 @@ __global__ __launch_bounds__(128) void shortconv_fwd_kernel(ConvArgs<E> a) {
 //            unchunked bits
 //   dstate_in rows r < W - 1 likewise with dz_{r - j}
 //   dw[j] += dz_t xe[t + j],  dbias += dz_t.
+// Going down, the W - 1 lowest x rows of a tile's window are the top rows of
+// the next window and the dz of its W - 1 lowest tokens are the next tile's
+// look-ahead, so both are carried in registers; only the run's first tile
+// computes a look-ahead from halo rows.  The token groups' weight / bias sums
+// are added in LDS in group order and written as one row of the partial
+// table (reduced in a fixed order afterwards).
 template <typename E, int W, int TT, int ACT>
-__global__ __launch_bounds__(128) void shortconv_bwd_kernel(ConvArgs<E> a) {
-    constexpr int NV = CONV_BWD_NV;  // channels per thread
+__global__ __launch_bounds__(128 * CONV_BWD_TG) void shortconv_bwd_kernel(ConvArgs<E> a) {
+    constexpr int NV = CONV_BWD_NV, TG = CONV_BWD_TG;  // channels per thread, token groups
     static_assert(NV == 4, "partial rows are stored as one float4 per tap");
+    __shared__ __align__(16) float red[TG][W + 1][128 * NV];
     float w[W][NV], bias[NV];
     load_taps<W, NV>(a.w, a.bias, a.C, w, bias);
-    const int cg = blockIdx.x * 128 + threadIdx.x;
-    if (cg * NV >= a.C) return;
-    const int c0 = cg * NV, b = blockIdx.z, T = a.T, C = a.C;
+    const int tx = threadIdx.x & 127, tg = threadIdx.x >> 7;
+    const int cg = blockIdx.x * 128 + tx;
+    const bool active = cg * NV < a.C;
+    const int c0 = active ? cg * NV : 0, b = blockIdx.z, T = a.T, C = a.C;
     const int ntiles = (T + TT - 1) / TT;
+    const int k_lo = (TG * blockIdx.y + tg) * a.tpg, k_hi = min(k_lo + a.tpg, ntiles);
     float dwp[W][NV], dbp[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -226,106 +241,137 @@ __global__ __launch_bounds__(128) void shortconv_bwd_kernel(ConvArgs<E> a) {
 #pragma unroll
         for (int j = 0; j < W; ++j) dwp[j][i] = 0.f;
     }
-    constexpr int ND = TT + W - 1;       // dz of tokens t0 .. t0 + TT + W - 2
-    constexpr int NX = TT + 2 * W - 2;   // xe of tokens t0 - W + 1 .. t0 + TT + W - 2
-    for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
-        const int t0 = tile * TT;
-        RowV<E, NV> xr[NX], dyr[ND];
-        if (t0 >= W - 1 && t0 + TT + W - 1 <= T) {  // interior tile: every row is in x and dy
-            const E* xb = a.x + ((size_t)b * T + (t0 - W + 1)) * C + c0;
-            const E* yb = a.dy + ((size_t)b * T + t0) * C + c0;
+    // xw[r]: xe row of token t0 - W + 1 + r (window r < TT + W - 1; the last
+    // W - 1 slots are used only for the first tile's look-ahead)
+    constexpr int NXW = TT + W - 1, NX = NXW + W - 1;
+    RowV<E, NV> xw[NX], dyc[TT];
+    float dz[TT + W - 1][NV];  // dz of tokens t0 + m (m >= TT: look-ahead)
+    auto dy_row = [&](int t) {
+        RowV<E, NV> r = ld_row<E, NV>(a.dy + ((size_t)b * T + (t < T ? t : T - 1)) * C + c0);
+        if (t >= T) r = zero_row<E, NV>();
+        return r;
+    };
+    auto dz_of = [&](int t, int r0, float* out, const RowV<E, NV>& dyr) {
+        // z of token t from window rows r0 .. r0 + W - 1
 #pragma unroll
-            for (int r = 0; r < NX; ++r) xr[r] = ld_row<E, NV>(xb + (size_t)r * C);
+        for (int i = 0; i < NV; ++i) {
+            float z = bias[i];
 #pragma unroll
-            for (int m = 0; m < ND; ++m) dyr[m] = ld_row<E, NV>(yb + (size_t)m * C);
-        } else {
-#pragma unroll
-            for (int r = 0; r < NX; ++r) xr[r] = xe_row<E, W, NV>(a, b, t0 - W + 1 + r, c0);
-#pragma unroll
-            for (int m = 0; m < ND; ++m) {
-                const int t = t0 + m;
-                dyr[m] = ld_row<E, NV>(a.dy + ((size_t)b * T + (t < T ? t : T - 1)) * C + c0);
-                if (t >= T) dyr[m] = zero_row<E, NV>();
-            }
+            for (int j = 0; j < W; ++j) z += w[j][i] * elem(xw[r0 + j], i);
+            out[i] = t < T ? elem(dyr, i) * act_d<ACT>(z) : 0.f;
         }
-        float dz[ND][NV];
+    };
+    if (active && k_lo < k_hi) {
+        // first (top) tile of the run: its window, dy rows and the look-ahead
+        int t0 = (k_hi - 1) * TT;
 #pragma unroll
-        for (int m = 0; m < ND; ++m)
+        for (int r = 0; r < NX; ++r) xw[r] = xe_row<E, W, NV>(a, b, t0 - W + 1 + r, c0);
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                float z = bias[i];
+        for (int m = 0; m < TT; ++m) dyc[m] = dy_row(t0 + m);
+        {
+            RowV<E, NV> dya[W > 1 ? W - 1 : 1];
 #pragma unroll
-                for (int j = 0; j < W; ++j) z += w[j][i] * elem(xr[m + j], i);  // xe of token t0 + m - W + 1 + j
-                dz[m][i] = (t0 + m < T) ? elem(dyr[m], i) * act_d<ACT>(z) : 0.f;
-            }
-        // weight and bias gradients over this tile's tokens
+            for (int m = 0; m < W - 1; ++m) dya[m] = dy_row(t0 + TT + m);
 #pragma unroll
-        for (int m = 0; m < TT; ++m)
-            if (t0 + m < T) {
+            for (int m = 0; m < W - 1; ++m) dz_of(t0 + TT + m, TT + m, dz[TT + m], dya[m]);
+        }
+        for (int k = k_hi - 1; k >= k_lo; --k) {
+            t0 = k * TT;
 #pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    dbp[i] += dz[m][i];
+            for (int m = 0; m < TT; ++m) dz_of(t0 + m, m, dz[m], dyc[m]);
+            // weight and bias gradients over this tile's tokens
 #pragma unroll
-                    for (int j = 0; j < W; ++j) dwp[j][i] += dz[m][i] * elem(xr[m + j], i);
-                }
-            }
-        // dx of the tile's tokens
+            for (int m = 0; m < TT; ++m)
+                if (t0 + m < T) {
 #pragma unroll
-        for (int k = 0; k < TT; ++k) {
-            const int s = t0 + k;
-            if (s < T) {
-                float acc[NV];
-                const int so = s + W - 1 - T;  // state_out row fed by token s
-                if (so >= 0 && a.dstate_out) {
-                    const RowV<float, NV> d = ld_row<float, NV>(a.dstate_out + ((size_t)b * (W - 1) + so) * C + c0);
+                    for (int i = 0; i < NV; ++i) {
+                        dbp[i] += dz[m][i];
 #pragma unroll
-                    for (int i = 0; i < NV; ++i) acc[i] = elem(d, i);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-                }
-#pragma unroll
-                for (int j = 0; j < W; ++j) {
-                    const int m = k + W - 1 - j;  // token s + W - 1 - j
-                    if (t0 + m < T) {
-#pragma unroll
-                        for (int i = 0; i < NV; ++i) acc[i] += w[j][i] * dz[m][i];
+                        for (int j = 0; j < W; ++j) dwp[j][i] += dz[m][i] * elem(xw[m + j], i);
                     }
                 }
-                st_vals<E, NV>(a.dx + ((size_t)b * T + s) * C + c0, acc);
-            }
-        }
-        // gradient of the carried state (xe rows 0 .. W - 2), from tile 0
-        if (W > 1 && tile == 0) {
+            // dx of the tile's tokens
 #pragma unroll
-            for (int r = 0; r < W - 1; ++r) {
-                float acc[NV];
-                if (r >= T && a.dstate_out) {
-                    const RowV<float, NV> d = ld_row<float, NV>(a.dstate_out + ((size_t)b * (W - 1) + (r - T)) * C + c0);
+            for (int kk = 0; kk < TT; ++kk) {
+                const int s = t0 + kk;
+                if (s < T) {
+                    float acc[NV];
+                    const int so = s + W - 1 - T;  // state_out row fed by token s
+                    if (so >= 0 && a.dstate_out) {
+                        const RowV<float, NV> d = ld_row<float, NV>(a.dstate_out + ((size_t)b * (W - 1) + so) * C + c0);
 #pragma unroll
-                    for (int i = 0; i < NV; ++i) acc[i] = elem(d, i);
-                } else {
+                        for (int i = 0; i < NV; ++i) acc[i] = elem(d, i);
+                    } else {
 #pragma unroll
-                    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-                }
-#pragma unroll
-                for (int j = 0; j < W; ++j) {
-                    const int m = r - j;  // token r - j
-                    if (m >= 0 && m < T) {
-#pragma unroll
-                        for (int i = 0; i < NV; ++i) acc[i] += w[j][i] * dz[m][i];
+                        for (int i = 0; i < NV; ++i) acc[i] = 0.f;
                     }
+#pragma unroll
+                    for (int j = 0; j < W; ++j) {
+                        const int m = kk + W - 1 - j;  // token s + W - 1 - j
+                        if (t0 + m < T) {
+#pragma unroll
+                            for (int i = 0; i < NV; ++i) acc[i] += w[j][i] * dz[m][i];
+                        }
+                    }
+                    st_vals<E, NV>(a.dx + ((size_t)b * T + s) * C + c0, acc);
                 }
-                st_vals<float, NV>(a.dstate_in + ((size_t)b * (W - 1) + r) * C + c0, acc);
+            }
+            // gradient of the carried state (xe rows 0 .. W - 2), from tile 0
+            if (W > 1 && k == 0) {
+#pragma unroll
+                for (int r = 0; r < W - 1; ++r) {
+                    float acc[NV];
+                    if (r >= T && a.dstate_out) {
+                        const RowV<float, NV> d = ld_row<float, NV>(a.dstate_out + ((size_t)b * (W - 1) + (r - T)) * C + c0);
+#pragma unroll
+                        for (int i = 0; i < NV; ++i) acc[i] = elem(d, i);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+                    }
+#pragma unroll
+                    for (int j = 0; j < W; ++j) {
+                        const int m = r - j;  // token r - j
+                        if (m >= 0 && m < T) {
+#pragma unroll
+                            for (int i = 0; i < NV; ++i) acc[i] += w[j][i] * dz[m][i];
+                        }
+                    }
+                    st_vals<float, NV>(a.dstate_in + ((size_t)b * (W - 1) + r) * C + c0, acc);
+                }
+            }
+            if (k > k_lo) {  // slide down one tile: carry, then the next tile's new rows
+#pragma unroll
+                for (int r = 0; r < W - 1; ++r) xw[TT + r] = xw[r];
+#pragma unroll
+                for (int m = 0; m < W - 1; ++m)
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) dz[TT + m][i] = dz[m][i];
+#pragma unroll
+                for (int r = 0; r < TT; ++r) xw[r] = xe_row<E, W, NV>(a, b, t0 - TT - W + 1 + r, c0);
+#pragma unroll
+                for (int m = 0; m < TT; ++m) dyc[m] = dy_row(t0 - TT + m);
             }
         }
     }
-    // partial row p = b * gridDim.y + blockIdx.y: [W + 1][C] (taps, then
-    // bias), so that a wave stores contiguous runs of channels
+    // the token groups' sums, added in group order; partial row
+    // p = b * gridDim.y + blockIdx.y: [W + 1][C] (taps, then bias)
+#pragma unroll
+    for (int j = 0; j < W; ++j) *(float4*)&red[tg][j][tx * NV] = float4{dwp[j][0], dwp[j][1], dwp[j][2], dwp[j][3]};
+    *(float4*)&red[tg][W][tx * NV] = float4{dbp[0], dbp[1], dbp[2], dbp[3]};
+    __syncthreads();
+    if (tg != 0 || !active) return;
     float* part = a.part + ((size_t)b * gridDim.y + blockIdx.y) * C * (W + 1) + c0;
 #pragma unroll
-    for (int j = 0; j < W; ++j) *(float4*)(part + (size_t)j * C) = float4{dwp[j][0], dwp[j][1], dwp[j][2], dwp[j][3]};
-    *(float4*)(part + (size_t)W * C) = float4{dbp[0], dbp[1], dbp[2], dbp[3]};
+    for (int j = 0; j <= W; ++j) {
+        float4 v = *(const float4*)&red[0][j][tx * NV];
+#pragma unroll
+        for (int q = 1; q < TG; ++q) {
+            const float4 u = *(const float4*)&red[q][j][tx * NV];
+            v = float4{v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w};
+        }
+        *(float4*)(part + (size_t)j * C) = v;
+    }
 }
 
 // dw[c][j] (= or +=) the sum over the P partial rows, likewise dbias.  Four
@@ -366,11 +412,15 @@ hipError_t fwd_t(const ConvArgs<E>& a, hipStream_t st) {
 template <typename E, int W>
 hipError_t bwd_t(const ConvArgs<E>& a, int accumulate, hipStream_t st) {
     constexpr int TT = CONV_BWD_TT;
-    const dim3 grid((a.C / CONV_BWD_NV + 127) / 128, conv_bwd_tile_groups(a.B, a.T, a.C, TT), a.B);
+    int tpg;
+    const int groups = conv_bwd_tile_groups(a.B, a.T, a.C, TT, &tpg);
+    ConvArgs<E> ag = a;
+    ag.tpg = tpg;
+    const dim3 grid((a.C / CONV_BWD_NV + 127) / 128, groups, a.B);
     if (a.act)
-        launch("shortconv_bwd", shortconv_bwd_kernel<E, W, TT, 1>, grid, dim3(128), st, a);
+        launch("shortconv_bwd", shortconv_bwd_kernel<E, W, TT, 1>, grid, dim3(128 * CONV_BWD_TG), st, ag);
     else
-        launch("shortconv_bwd", shortconv_bwd_kernel<E, W, TT, 0>, grid, dim3(128), st, a);
+        launch("shortconv_bwd", shortconv_bwd_kernel<E, W, TT, 0>, grid, dim3(128 * CONV_BWD_TG), st, ag);
     const int P = a.B * (int)grid.y, n = a.C * (W + 1);
     launch("shortconv_reduce", shortconv_reduce_kernel, dim3((n + 63) / 64), dim3(256), st, (const float*)a.part, P,
            a.C, W, a.dw, a.dbias, accumulate);
