@@ -815,7 +815,7 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const GdnWs& ws = L.ws;
     GdnPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                       ws.gam, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
-    launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, gblk, dim3(256), st, pa);
+    launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
     GdnPrep2Args<E> p2{(const E*)L.q, (const E*)L.k, (const E*)L.dO, ws.gam, (const E*)ws.W,
                        ws.Rt, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dvlT, L.T, L.H, L.NC};
     launch("gdn_prep2", gdn_prep2_kernel<E, DK, DV>, gblk, dim3(256), st, p2);

@@ -15,7 +15,7 @@ struct GdnFwdStages {
         GdnPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                           L.ws.gam, (E*)L.ws.W, (E*)L.ws.KhT, (E*)L.ws.UtT};
         pa.n0 = n0;
-        launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, dim3(n1 - n0, L.H, L.B), dim3(256), st, pa);
+        launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, dim3(n1 - n0, L.H, L.B), dim3(512), st, pa);
     }
     void scan(int n0, int n1, const float* S_in, float* S_out, hipStream_t st) const {
         GdnScanArgs<E> sa{L.ws.gam, (const E*)L.ws.W, (const E*)L.ws.KhT, (const E*)L.ws.UtT, S_in, S_out,

@@ -158,9 +158,12 @@ __device__ __forceinline__ void st_fragT(float* base, int f, int l, const Frag<f
 // contract over the token index read them transposed (ldfrag_tr).
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
+__global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
+    constexpr int NT = 512;
     const int n = a.n0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    // wave w8: row block w = w8 & 3, half hf = w8 >> 2 (the halves split the
+    // Gram's column blocks and the output tiles)
+    const int tid = threadIdx.x, w8 = tid >> 6, w = w8 & 3, hf = w8 >> 2, l = tid & 63, r = l & 15, g = l >> 4;
     const int T = a.T, H = a.H, NC = a.NC;
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;  // first token (b, n*64)
     const size_t chunk = ((size_t)b * H + h) * NC + n;    // workspace block index
@@ -171,9 +174,9 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     __shared__ float Am[BLK * AP], Td[4 * 256];
     __shared__ __align__(16) E Ks[BLK * PK], Vs[BLK * PV], T1[BLK * PT], T2[BLK * PT];
 
-    const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * H * DK + (size_t)h * DK, (size_t)H * DK, nvalid);
-    const auto vx = load_rows<E, BLK, DV>(a.v + tok0 * H * DV + (size_t)h * DV, (size_t)H * DV, nvalid);
-    if (w == 0) {
+    const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * H * DK + (size_t)h * DK, (size_t)H * DK, nvalid);
+    const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * H * DV + (size_t)h * DV, (size_t)H * DV, nvalid);
+    if (w8 == 0) {
         // tokens past the end are identity steps: g = 0, beta = 0
         const size_t ig = (tok0 + l) * H + h;
         const float gv = l < nvalid ? to_f(a.g[ig]) : 0.f;
@@ -186,17 +189,19 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         s_bet[l] = bv;
         a.gam[chunk * BLK + l] = gam;
     }
-    store_rows<E, BLK, DK, PK>(kx, Ks);
-    store_rows<E, BLK, DV, PV>(vx, Vs);
+    store_rows<E, BLK, DK, PK, NT>(kx, Ks);
+    store_rows<E, BLK, DV, PV, NT>(vx, Vs);
     __syncthreads();
 
-    // Gram block row w: A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s), s < r.
+    // Gram block row w: A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s), s < r
+    // (column blocks j of this wave's half: j & 1 == hf)
     {
         Frag<E> fa[DK / 32];
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) fa[kk] = ldfrag(Ks + (16 * w + r) * PK + 32 * kk + 4 * g);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            if ((j & 1) != hf) continue;
             f32x4 acc = zero4();
             if (j <= w) {
 #pragma unroll
@@ -213,11 +218,11 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         }
     }
     __syncthreads();
-    {
-        // T = (I + A)^-1; wave w holds column block w.  T1 = T Diag(beta Gam),
-        // T2 = T Diag(beta), rounded to the element type.
+    if (hf == 0) {
+        // T = (I + A)^-1 on waves 0..3; wave w holds column block w.
+        // T1 = T Diag(beta Gam), T2 = T Diag(beta), rounded to the element type.
         f32x4 tc[4];
-        tri_inverse_cols(Am, Td, tc);
+        tri_inverse_cols(Am, Td, tc);  // one barrier inside
         const int s = 16 * w + r;
         const float b1 = s_bet[s] * s_Gam[s], b2 = s_bet[s];
 #pragma unroll
@@ -228,13 +233,15 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
                 T1[t * PT + s] = from_f<E>(tc[i][ii] * b1);
                 T2[t * PT + s] = from_f<E>(tc[i][ii] * b2);
             }
+    } else {
+        __syncthreads();  // matches the barrier inside tri_inverse_cols
     }
     __syncthreads();
 
     // W^T[d][t] = sum_s K^T[d][s] T1[t][s]  -> stored as W[t][d] (tiled)
     E* Wout = a.W + chunk * BLK * DK;
 #pragma unroll
-    for (int tile = w; tile < (DK / 16) * 4; tile += 4) {
+    for (int tile = w8; tile < (DK / 16) * 4; tile += 8) {
         const int db = tile >> 2, tb = tile & 3;
         f32x4 acc = zero4();
 #pragma unroll
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     // so that the scan forms -U = W S - Ut by accumulating onto it
     E* Uout = a.UtT + chunk * BLK * DV;
 #pragma unroll
-    for (int tile = w; tile < 4 * (DV / 16); tile += 4) {
+    for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
         const int tb = tile % 4, vb = tile / 4;
         f32x4 acc = zero4();
 #pragma unroll
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     // is the B fragment of Kh over tokens 32j.., columns 16db..
     E* Khout = a.KhT + chunk * BLK * DK;
 #pragma unroll
-    for (int f = w; f < 2 * (DK / 16); f += 4) {
+    for (int f = w8; f < 2 * (DK / 16); f += 8) {
         const int db = f >> 1, j = f & 1;
         Frag<E> x = ldfrag_tr(Ks, PK, 32 * j, 16 * db, l);
         frag_scale_k(x, s_ek, 32 * j, g);
