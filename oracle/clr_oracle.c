@@ -17,12 +17,15 @@
  *         F_t = alpha_t (I - beta_t k_t k_t^T),  write term beta_t v_t k_t^T;
  *     - Gated Linear Attention: per-key-channel (diagonal) decay alpha_t,
  *         write term v_t k_t^T;
- *     - Mamba-2: F_t is a scalar times the identity, write term v_t k_t^T.
+ *     - Mamba-2: F_t is a scalar times the identity, write term v_t k_t^T;
+ *     - Kimi Delta Attention (KDA): F_t is diagonal-plus-low-rank, the delta
+ *       rule's erase factor after a per-key-channel decay.
  *   Here the state is stored key-major, S in R^{dk x dv} (the transpose of the
  *   paper's value-major S), so the same maps read
  *     GDN:     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
  *     GLA:     S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T     (alpha_t in R^dk)
  *     Mamba-2: S_t = alpha_t S_{t-1} + k_t v_t^T            (alpha_t scalar)
+ *     KDA:     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
  *     all: o_t = S_t^T q_t,   alpha_t = exp(g_t)  (g = log alpha <= 0).
  *
  *   The chunk entry points take a boundary state S_in and return S_out (the
@@ -46,8 +49,8 @@
  * Layouts (all contiguous, row-major, fp64, host memory):
  *   q, k        [B, T, H, dk]
  *   v, o, dO    [B, T, H, dv]
- *   g           GDN, Mamba-2: [B, T, H]       GLA: [B, T, H, dk]
- *   beta        GDN: [B, T, H]       (GLA has none)
+ *   g           GDN, Mamba-2: [B, T, H]       GLA, KDA: [B, T, H, dk]
+ *   beta        GDN, KDA: [B, T, H]  (GLA and Mamba-2 have none)
  *   S_in, S_out, dS_in, dS_out   [B, H, dk, dv]
  * S_in / dS_out may be NULL (zero); S_out may be NULL (not wanted).
  * Return 0 on success, -1 on bad arguments or allocation failure.
@@ -573,6 +576,200 @@ int ref_m2_bwd(int B, int T, int H, int dk, int dv,
         }
         memcpy(dS_in + st(b, h, H, dk, dv), dS, ns * sizeof(double));
         free(ck); free(seg); free(dS);
+    }
+    return fail ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* KDA (per-channel decay, delta-rule erase and write)                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One KDA token, in delta form with the decayed state S' = Diag(alpha) S:
+ *   a     = S'^T k                (dv)
+ *   delta = v - a                 (dv)
+ *   S    <- S' + beta k delta^T
+ * which equals (I - beta k k^T) Diag(alpha) S + beta k v^T.
+ */
+static void kda_token_fwd(double *S, const double *kt, const double *vt,
+                          const double *gt, double beta, int dk, int dv,
+                          double *a_out)
+{
+    for (int i = 0; i < dk; ++i) {
+        const double al = exp(gt[i]);
+        double *Si = S + (size_t)i * dv;
+        for (int j = 0; j < dv; ++j) Si[j] *= al;
+    }
+    for (int j = 0; j < dv; ++j) a_out[j] = 0.0;
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) a_out[j] += S[(size_t)i * dv + j] * kt[i];
+    for (int i = 0; i < dk; ++i) {
+        const double bk = beta * kt[i];
+        double *Si = S + (size_t)i * dv;
+        for (int j = 0; j < dv; ++j) Si[j] += bk * (vt[j] - a_out[j]);
+    }
+}
+
+int ref_kda_fwd(int B, int T, int H, int dk, int dv,
+                const double *q, const double *k, const double *v,
+                const double *g, const double *beta, const double *S_in,
+                double *o, double *S_out)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
+    if (!q || !k || !v || !g || !beta || !o) return -1;
+    const size_t ns = (size_t)dk * dv;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(ref_get_max_threads()) reduction(|:fail)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        double *S = (double *)malloc(ns * sizeof(double));
+        double *a = (double *)malloc((size_t)dv * sizeof(double));
+        if (!S || !a) { free(S); free(a); fail |= 1; continue; }
+        load_state(S, S_in, st(b, h, H, dk, dv), ns);
+        for (int t = 0; t < T; ++t) {
+            kda_token_fwd(S, k + tok(b, t, h, T, H, dk), v + tok(b, t, h, T, H, dv),
+                          g + tok(b, t, h, T, H, dk), beta[hd(b, t, h, T, H)], dk, dv, a);
+            out_token(S, q + tok(b, t, h, T, H, dk), dk, dv, o + tok(b, t, h, T, H, dv));
+        }
+        if (S_out) memcpy(S_out + st(b, h, H, dk, dv), S, ns * sizeof(double));
+        free(S);
+        free(a);
+    }
+    return fail ? -1 : 0;
+}
+
+/*
+ * Reverse-mode step for one KDA token.  With S' = Diag(alpha) S_{t-1},
+ * a = S'^T k, delta = v - a, S_t = S' + beta k delta^T, o = S_t^T q:
+ *   dS_t      += q do^T ;  dq = S_t do
+ *   dbeta      = k^T dS_t delta
+ *   dk         = beta dS_t delta          (write term)
+ *   ddelta     = beta dS_t^T k ;  dv = ddelta ;  da = -ddelta
+ *   dS'        = dS_t + k da^T
+ *   dk        += S' da                    (erase term)
+ *   dalpha_i   = sum_j dS'[i,j] S_{t-1}[i,j],  dg_i = alpha_i dalpha_i
+ *   dS_{t-1}   = Diag(alpha) dS'
+ * Sp is S_{t-1}, St is S_t.
+ */
+static void kda_token_bwd(double *dS, const double *Sp, const double *St,
+                          const double *qt, const double *kt, const double *vt,
+                          const double *dot, const double *gt, double beta,
+                          int dk, int dv, double *dqt, double *dkt,
+                          double *dvt, double *dgt, double *dbt, double *wrk)
+{
+    double *Sd = wrk;             /* S' (dk x dv) */
+    double *dl = wrk + (size_t)dk * dv;  /* delta, then ddelta (dv) */
+    double *aa = dl + dv;                 /* a (dv) */
+    for (int i = 0; i < dk; ++i) {
+        const double al = exp(gt[i]);
+        for (int j = 0; j < dv; ++j) Sd[(size_t)i * dv + j] = al * Sp[(size_t)i * dv + j];
+    }
+    for (int j = 0; j < dv; ++j) {
+        double x = 0.0;
+        for (int i = 0; i < dk; ++i) x += Sd[(size_t)i * dv + j] * kt[i];
+        aa[j] = x;
+        dl[j] = vt[j] - x;
+    }
+    /* output */
+    for (int i = 0; i < dk; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dv; ++j) {
+            dS[(size_t)i * dv + j] += qt[i] * dot[j];
+            acc += St[(size_t)i * dv + j] * dot[j];
+        }
+        dqt[i] = acc;
+    }
+    /* write term */
+    double db = 0.0;
+    for (int i = 0; i < dk; ++i) {
+        double x = 0.0;
+        for (int j = 0; j < dv; ++j) x += dS[(size_t)i * dv + j] * dl[j];
+        dkt[i] = beta * x;
+        db += kt[i] * x;
+    }
+    *dbt = db;
+    /* ddelta = beta dS^T k, reusing dl */
+    for (int j = 0; j < dv; ++j) {
+        double y = 0.0;
+        for (int i = 0; i < dk; ++i) y += kt[i] * dS[(size_t)i * dv + j];
+        dl[j] = beta * y;
+        dvt[j] = dl[j];
+    }
+    /* erase term: dS' = dS - k ddelta^T, dk -= S' ddelta */
+    for (int i = 0; i < dk; ++i) {
+        double x = 0.0;
+        for (int j = 0; j < dv; ++j) {
+            x += Sd[(size_t)i * dv + j] * dl[j];
+            dS[(size_t)i * dv + j] -= kt[i] * dl[j];
+        }
+        dkt[i] -= x;
+    }
+    /* decay */
+    for (int i = 0; i < dk; ++i) {
+        const double al = exp(gt[i]);
+        double frob = 0.0;
+        for (int j = 0; j < dv; ++j) frob += dS[(size_t)i * dv + j] * Sp[(size_t)i * dv + j];
+        dgt[i] = frob * al;
+        for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] *= al;
+    }
+}
+
+int ref_kda_bwd(int B, int T, int H, int dk, int dv,
+                const double *q, const double *k, const double *v,
+                const double *g, const double *beta, const double *S_in,
+                const double *dO, const double *dS_out, double *dq, double *dk_,
+                double *dv_, double *dg, double *dbeta, double *dS_in)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
+    if (!q || !k || !v || !g || !beta || !dO) return -1;
+    if (!dq || !dk_ || !dv_ || !dg || !dbeta || !dS_in) return -1;
+    const size_t ns = (size_t)dk * dv;
+    const int nck = T / CKPT + 1;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(ref_get_max_threads()) reduction(|:fail)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        double *ck = (double *)malloc((size_t)nck * ns * sizeof(double));
+        double *seg = (double *)malloc((size_t)(CKPT + 1) * ns * sizeof(double));
+        double *dS = (double *)malloc(ns * sizeof(double));
+        double *wrk = (double *)malloc((ns + 2 * (size_t)dv) * sizeof(double));
+        if (!ck || !seg || !dS || !wrk) {
+            free(ck); free(seg); free(dS); free(wrk);
+            fail |= 1;
+            continue;
+        }
+        double *S = seg;
+        load_state(S, S_in, st(b, h, H, dk, dv), ns);
+        for (int t = 0; t < T; ++t) {
+            if (t % CKPT == 0) memcpy(ck + (size_t)(t / CKPT) * ns, S, ns * sizeof(double));
+            kda_token_fwd(S, k + tok(b, t, h, T, H, dk), v + tok(b, t, h, T, H, dv),
+                          g + tok(b, t, h, T, H, dk), beta[hd(b, t, h, T, H)], dk, dv, wrk);
+        }
+        if (dS_out) memcpy(dS, dS_out + st(b, h, H, dk, dv), ns * sizeof(double));
+        else memset(dS, 0, ns * sizeof(double));
+        const int nseg = (T + CKPT - 1) / CKPT;
+        for (int sgi = nseg - 1; sgi >= 0; --sgi) {
+            const int t0 = sgi * CKPT;
+            const int t1 = (t0 + CKPT < T) ? t0 + CKPT : T;
+            memcpy(seg, ck + (size_t)sgi * ns, ns * sizeof(double));
+            for (int t = t0; t < t1; ++t) {
+                double *nx = seg + (size_t)(t - t0 + 1) * ns;
+                memcpy(nx, seg + (size_t)(t - t0) * ns, ns * sizeof(double));
+                kda_token_fwd(nx, k + tok(b, t, h, T, H, dk), v + tok(b, t, h, T, H, dv),
+                              g + tok(b, t, h, T, H, dk), beta[hd(b, t, h, T, H)], dk, dv, wrk);
+            }
+            for (int t = t1 - 1; t >= t0; --t) {
+                kda_token_bwd(dS, seg + (size_t)(t - t0) * ns, seg + (size_t)(t - t0 + 1) * ns,
+                              q + tok(b, t, h, T, H, dk), k + tok(b, t, h, T, H, dk),
+                              v + tok(b, t, h, T, H, dv), dO + tok(b, t, h, T, H, dv),
+                              g + tok(b, t, h, T, H, dk), beta[hd(b, t, h, T, H)], dk, dv,
+                              dq + tok(b, t, h, T, H, dk), dk_ + tok(b, t, h, T, H, dk),
+                              dv_ + tok(b, t, h, T, H, dv), dg + tok(b, t, h, T, H, dk),
+                              dbeta + hd(b, t, h, T, H), wrk);
+            }
+        }
+        memcpy(dS_in + st(b, h, H, dk, dv), dS, ns * sizeof(double));
+        free(ck); free(seg); free(dS); free(wrk);
     }
     return fail ? -1 : 0;
 }

@@ -123,8 +123,10 @@ def load(path: Optional[str] = None):
     lib.ref_gla_bwd.argtypes = [i] * 5 + [dp] * 12
     lib.ref_m2_fwd.argtypes = [i] * 5 + [dp] * 7
     lib.ref_m2_bwd.argtypes = [i] * 5 + [dp] * 12
+    lib.ref_kda_fwd.argtypes = [i] * 5 + [dp] * 8
+    lib.ref_kda_bwd.argtypes = [i] * 5 + [dp] * 14
     for f in (lib.ref_gdn_fwd, lib.ref_gdn_bwd, lib.ref_gla_fwd, lib.ref_gla_bwd,
-              lib.ref_m2_fwd, lib.ref_m2_bwd):
+              lib.ref_m2_fwd, lib.ref_m2_bwd, lib.ref_kda_fwd, lib.ref_kda_bwd):
         f.restype = ctypes.c_int
     lib.ref_set_threads.argtypes = [i]
     lib.ref_set_threads.restype = None
@@ -247,6 +249,36 @@ def mamba2_bwd(q, k, v, g, S_in, dO, dS_out=None, lib=None):
                         _p(r["dg"]), _p(r["dS_in"]))
     if rc != 0:
         raise RuntimeError("ref_m2_bwd failed")
+    return r
+
+
+def kda_fwd(q, k, v, g, beta, S_in=None, lib=None):
+    """KDA chunk forward (per-channel gate g [B,T,H,dk], beta [B,T,H]):
+    returns (o, S_out)."""
+    lib = lib or load()
+    q, k, v, g, beta, S_in = map(_c, (q, k, v, g, beta, S_in))
+    B, T, H, dk, dv = _dims(q, v)
+    o = np.zeros((B, T, H, dv))
+    S_out = np.zeros((B, H, dk, dv))
+    rc = lib.ref_kda_fwd(B, T, H, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta),
+                         _p(S_in), _p(o), _p(S_out))
+    if rc != 0:
+        raise RuntimeError("ref_kda_fwd failed")
+    return o, S_out
+
+
+def kda_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, lib=None):
+    """KDA chunk backward: returns dict dq, dk, dv, dg, dbeta, dS_in."""
+    lib = lib or load()
+    q, k, v, g, beta, S_in, dO, dS_out = map(_c, (q, k, v, g, beta, S_in, dO, dS_out))
+    B, T, H, dk, dv = _dims(q, v)
+    r = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+             dg=np.zeros_like(g), dbeta=np.zeros((B, T, H)), dS_in=np.zeros((B, H, dk, dv)))
+    rc = lib.ref_kda_bwd(B, T, H, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta),
+                         _p(S_in), _p(dO), _p(dS_out), _p(r["dq"]), _p(r["dk"]),
+                         _p(r["dv"]), _p(r["dg"]), _p(r["dbeta"]), _p(r["dS_in"]))
+    if rc != 0:
+        raise RuntimeError("ref_kda_bwd failed")
     return r
 
 

@@ -36,6 +36,13 @@ MUTANTS = [
     ("m2: dS_{t-1} not decayed", "for (size_t e = 0; e < (size_t)dk * dv; ++e) dS[e] *= al;",
      "for (size_t e = 0; e < (size_t)dk * dv; ++e) dS[e] *= 1.0;"),
     ("m2: dk uses S_{t-1} adjoint before the q term", "dkt[i] = x;\n    }\n    /* dv_j", "dkt[i] = -x;\n    }\n    /* dv_j"),
+    ("kda: no decay before the erase", "for (int j = 0; j < dv; ++j) Si[j] *= al;\n    }\n    for (int j = 0; j < dv; ++j) a_out[j] = 0.0;",
+     "for (int j = 0; j < dv; ++j) Si[j] *= 1.0;\n    }\n    for (int j = 0; j < dv; ++j) a_out[j] = 0.0;"),
+    ("kda: dk misses the erase term", "dkt[i] -= x;", "dkt[i] -= 0.0 * x;"),
+    ("kda: dbeta sign", "*dbt = db;", "*dbt = -db;"),
+    ("kda: dS' without the erase", "dS[(size_t)i * dv + j] -= kt[i] * dl[j];", "dS[(size_t)i * dv + j] -= 0.0 * kt[i] * dl[j];"),
+    ("kda: dg from S_t", "frob += dS[(size_t)i * dv + j] * Sp[(size_t)i * dv + j];",
+     "frob += dS[(size_t)i * dv + j] * St[(size_t)i * dv + j];"),
     ("bwd: checkpoint off by one token", "if (t % CKPT == 0) memcpy(ck + (size_t)(t / CKPT) * ns, S, ns * sizeof(double));\n            gdn_token_fwd",
      "if (t % CKPT == 1 || t == 0) memcpy(ck + (size_t)(t / CKPT) * ns, S, ns * sizeof(double));\n            gdn_token_fwd"),
 ]
@@ -46,11 +53,13 @@ def _pins_pass(lib):
     from tests import test_oracle_fd as fd
     rng = np.random.default_rng(3)
     ok = True
-    for kind in ("gdn", "gla", "m2"):
+    for kind in ("gdn", "gla", "m2", "kda"):
         for shape in [(1, 6, 1, 3, 2), (1, 70, 1, 2, 2)]:
             B, T, H, dk, dv = shape
-            if kind == "gdn":
+            if kind in ("gdn", "kda"):
                 x = fd._rand_gdn(rng, *shape)
+                if kind == "kda":
+                    x["g"] = np.repeat(x["g"][..., None], shape[3], -1) * (0.5 + rng.random(shape[:3] + (shape[3],)))
             elif kind == "gla":
                 x = fd._rand_gla(rng, *shape)
             else:
@@ -58,11 +67,14 @@ def _pins_pass(lib):
                 x["g"] = x["g"][..., 0].copy()
             dO = rng.standard_normal((B, T, H, dv))
             dS = rng.standard_normal((B, H, dk, dv))
-            if kind == "gdn":
-                def loss(xx, a, b):
-                    o, S = oracle.gdn_fwd(xx["q"], xx["k"], xx["v"], xx["g"], xx["beta"], xx["S_in"], lib=lib)
+            if kind in ("gdn", "kda"):
+                fwd = oracle.gdn_fwd if kind == "gdn" else oracle.kda_fwd
+                bwd = oracle.gdn_bwd if kind == "gdn" else oracle.kda_bwd
+
+                def loss(xx, a, b, fwd=fwd):
+                    o, S = fwd(xx["q"], xx["k"], xx["v"], xx["g"], xx["beta"], xx["S_in"], lib=lib)
                     return float(np.sum(o * a) + np.sum(S * b))
-                r = oracle.gdn_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S_in"], dO, dS, lib=lib)
+                r = bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S_in"], dO, dS, lib=lib)
                 names = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", S_in="dS_in")
             else:
                 fwd = oracle.gla_fwd if kind == "gla" else oracle.mamba2_fwd
