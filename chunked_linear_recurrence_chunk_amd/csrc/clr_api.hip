@@ -75,6 +75,25 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     return w;
 }
 
+// The fp32 KDA forward is instantiated for d <= 64 only.
+bool kda_f32_unsupported(const clr_shape_t* s) { return s->dtype == CLR_F32 && s->dk > 64; }
+
+// KDA forward: the Gated DeltaNet forward layouts the scan reads, exp(b_C)
+// per key channel (padded to 256 floats) and U token-major for the output.
+GdnWs carve_kda(const clr_shape_t* s, char* base, size_t* total) {
+    Carver c{base};
+    const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
+    GdnWs w{};
+    w.W = c.take(nb * BLK * dk * es);
+    w.KhT = c.take(nb * BLK * dk * es);
+    w.UtT = c.take(nb * BLK * dv * es);
+    w.hT = c.take(nb * dk * dv * es);
+    w.eCk = (float*)c.take(nb * 256 * 4);
+    w.Utok = c.take((size_t)s->B * s->T * s->H * dv * es);
+    if (total) *total = c.off;
+    return w;
+}
+
 GlaWs carve_gla(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     Carver c{base};
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
@@ -165,6 +184,12 @@ const char* clr_status_string(int s) {
 }
 
 size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
+    if (op == CLR_OP_KDA_FWD) {
+        if (check_shape(s, false, false) != CLR_OK || kda_f32_unsupported(s)) return 0;
+        size_t total = 0;
+        carve_kda(s, nullptr, &total);
+        return total;
+    }
     if (op < CLR_OP_GDN_FWD || op > CLR_OP_M2_BWD) return 0;
     // the Mamba-2 member runs on the GLA kernels
     const bool gla = op != CLR_OP_GDN_FWD && op != CLR_OP_GDN_BWD;
@@ -177,31 +202,41 @@ size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
 }
 
 // Which member of the family an entry point computes.
-enum Kind { K_GDN, K_GLA, K_M2 };
+enum Kind { K_GDN, K_GLA, K_M2, K_KDA };
 
 static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void* k, const void* v,
                       const void* g, const void* beta, const float* S_in, void* o, float* S_out,
                       void* ws, size_t ws_bytes, void* stream) {
-    const bool gla = kind != K_GDN;
+    const bool gla = kind == K_GLA || kind == K_M2;  // GLA kernels and head sizes
+    const bool has_beta = kind == K_GDN || kind == K_KDA;
     int rc = check_shape(s, gla, false);
     if (rc) return rc;
+    if (kind == K_KDA && kda_f32_unsupported(s)) return CLR_ENOTSUP;
     if (!q || !k || !v || !g) return CLR_EINVAL;
-    if (gla ? beta != nullptr : beta == nullptr) return CLR_EINVAL;
+    if (has_beta ? beta == nullptr : beta != nullptr) return CLR_EINVAL;
     const size_t es = esize(s->dtype);
     const size_t ntok = (size_t)s->B * s->T * s->H, nst = (size_t)s->B * s->H * s->dk * s->dv;
     Buf bufs[] = {{q, ntok * s->dk * es, false}, {k, ntok * s->dk * es, false},
-                  {v, ntok * s->dv * es, false}, {g, ntok * (kind == K_GLA ? s->dk : 1) * es, false},
+                  {v, ntok * s->dv * es, false}, {g, ntok * ((kind == K_GLA || kind == K_KDA) ? s->dk : 1) * es, false},
                   {beta, ntok * es, false},      {S_in, nst * 4, false},
                   {o, ntok * s->dv * es, true},  {S_out, nst * 4, true},
                   {ws, ws_bytes, true}};
     // g and beta rows of GDN are only 2/4-byte aligned per token but the
     // tensors themselves must start 16-byte aligned.
     if ((rc = check_bufs(bufs, 9))) return rc;
-    const size_t need = clr_workspace_bytes(s, gla ? CLR_OP_GLA_FWD : CLR_OP_GDN_FWD);
+    const size_t need = clr_workspace_bytes(s, kind == K_KDA ? CLR_OP_KDA_FWD : gla ? CLR_OP_GLA_FWD : CLR_OP_GDN_FWD);
     hipStream_t st = (hipStream_t)stream;
     if (s->T == 0) return passthrough(S_in, S_out, nst, st);
     if (!ws || ws_bytes < need || ((uintptr_t)ws & (ALIGN - 1))) return CLR_EWORKSPACE;
     const int NC = (s->T + BLK - 1) / BLK;
+    if (kind == K_KDA) {
+        GdnLaunch L{};
+        L.B = s->B; L.T = s->T; L.H = s->H; L.NC = NC; L.dk = s->dk; L.dv = s->dv;
+        L.bf16 = s->dtype == CLR_BF16;
+        L.q = q; L.k = k; L.v = v; L.g = g; L.beta = beta; L.S_in = S_in; L.o = o; L.S_out = S_out;
+        L.ws = carve_kda(s, (char*)ws, nullptr);
+        return hip_status(launch_kda_fwd(L, st));
+    }
     if (!gla) {
         GdnLaunch L{};
         L.B = s->B; L.T = s->T; L.H = s->H; L.NC = NC; L.dk = s->dk; L.dv = s->dv;
@@ -230,6 +265,12 @@ int gla_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, c
             const void* beta, const float* S_in, void* o, float* S_out, void* ws, size_t ws_bytes,
             void* stream) {
     return fwd_common(K_GLA, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream);
+}
+
+int kda_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+            const void* beta, const float* S_in, void* o, float* S_out, void* ws, size_t ws_bytes,
+            void* stream) {
+    return fwd_common(K_KDA, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream);
 }
 
 int mamba2_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,

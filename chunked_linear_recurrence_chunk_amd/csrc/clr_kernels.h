@@ -16,6 +16,10 @@ namespace clr {
     CLR_CASE(E, 128, 128)
 // fp32 backward: the block-adjoint kernel's LDS tiles fit only for d = 32.
 #define CLR_FOR_GDN_BWD_SHAPES_F32(E) CLR_CASE(E, 32, 32)
+// fp32 KDA forward: the prep kernel's LDS tiles fit for d <= 64.
+#define CLR_FOR_KDA_SHAPES_F32(E) \
+    CLR_CASE(E, 32, 32)           \
+    CLR_CASE(E, 64, 64)
 
 // Workspace of the Gated DeltaNet path.  Block-major: index
 // ((b * H + h) * NC + n) selects the 64-token block n of head h in batch b.
@@ -27,6 +31,9 @@ struct GdnWs {
     void* hT;     // [.., dv, dk]   state entering the block, transposed
     void* UT;     // [.., dv, 64]   U^T (delta-rule new values)
     float* Smid;  // [B, H, dk, dv] state at the split point of a split forward
+    // KDA forward only
+    float* eCk;   // [.., 256]      exp(b_C) per key channel (padded)
+    void* Utok;   // [B, T, H, dv]  U, token-major
     // backward only
     float* Rt;    // [.., dv, dk]   R^T, R = (Diag(Gam) Q)^T dO - W^T dvloc  (fp32)
     void* WT;     // [.., dk, 64]   W^T
@@ -67,6 +74,11 @@ template <typename E> struct GdnScanArgs {
     E *hT, *UT;
     int H, NC, BH;
     int n0 = 0, n1 = 1 << 30;  // blocks [n0, min(n1, NC)) are scanned
+    // per-channel decay (KDA): exp(b_C) per block, padded to 256 floats, and
+    // U written token-major [B, T, H, dv] (rows of valid tokens only)
+    const float* eC = nullptr;
+    E* Utok = nullptr;
+    int T = 0;
 };
 
 template <typename E> struct GdnOutArgs {
@@ -79,6 +91,8 @@ template <typename E> struct GdnOutArgs {
 };
 
 hipError_t launch_gdn_fwd(const GdnLaunch& L, hipStream_t st);
+// KDA forward (g per key channel); kernels in gla.hip.
+hipError_t launch_kda_fwd(const GdnLaunch& L, hipStream_t st);
 hipError_t launch_gdn_bwd(const GdnLaunch& L, hipStream_t st);
 
 // ---------------------------------------------------------------------------

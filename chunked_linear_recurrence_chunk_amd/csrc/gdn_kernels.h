@@ -292,7 +292,7 @@ template <typename E, int DK> struct ScanFwdOps {
 // column c0 + r) into a row-major matrix with row stride ld, through LDS.
 template <typename E, int ROWS>
 __device__ __forceinline__ void store_rows16(E* dst, size_t ld, const f32x4 (&X)[ROWS / 16], E* tile, int c0, int r,
-                                             int g) {
+                                             int g, int nrows = ROWS) {
     const int l = 16 * g + r;
 #pragma unroll
     for (int rb = 0; rb < ROWS / 16; ++rb)
@@ -304,7 +304,7 @@ __device__ __forceinline__ void store_rows16(E* dst, size_t ld, const f32x4 (&X)
 #pragma unroll
     for (int c = l; c < ROWS * PER_ROW; c += 64) {
         const int d = c / PER_ROW, part = c % PER_ROW;
-        *(uint4*)(dst + (size_t)d * ld + c0 + part * VEC) = *(const uint4*)(tile + d * 16 + part * VEC);
+        if (d < nrows) *(uint4*)(dst + (size_t)d * ld + c0 + part * VEC) = *(const uint4*)(tile + d * 16 + part * VEC);
     }
     asm volatile("" ::: "memory");
 }
@@ -346,7 +346,7 @@ __device__ __forceinline__ void store_state_tiled(E* h, const f32x4 (&S)[DK / 16
 template <typename E, int DK, int NU>
 __device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK>& o, const char* slot, int l);
 
-template <typename E, int DK, int DV, bool HNAT, int NU>
+template <typename E, int DK, int DV, bool HNAT, int NU, bool PCD = false>
 __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[DK / 16],
                                               const GdnScanArgs<E>& a, size_t chunk, int vb, int l, E* tile,
                                               const char* slot) {
@@ -396,11 +396,23 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[D
 #pragma unroll
         for (int j = 0; j < 2; ++j) st8T(UT, 2 * vb + j, l, U[2 * j], U[2 * j + 1]);
     }
-    // S <- Gam_C S + Kh^T U
+    if constexpr (PCD) {
+        // U token-major for the output kernel (rows of valid tokens)
+        const size_t bh = chunk / a.NC;
+        const int n = (int)(chunk % a.NC), bb = (int)(bh / a.H), hh = (int)(bh % a.H);
+        const size_t ldv = (size_t)a.H * DV;
+        E* dst = a.Utok + ((size_t)bb * a.T + (size_t)n * BLK) * ldv + (size_t)hh * DV;
+        store_rows16<E, BLK>(dst, ldv, U, tile, 16 * vb, l & 15, l >> 4, min(BLK, a.T - n * BLK));
+    }
+    // S <- Diag(decay) S + Kh^T U: Gam_C (GDN), or exp(b_C) per key channel
+    // (KDA: row d of S scaled by its own channel's factor, from the slot's last unit)
     const float GC = __expf(o.gC);
+    const float* ecs = (const float*)(slot + (NU - 1) * RING_UNIT) + 4 * (l >> 4);
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
-        f32x4 acc = S[db] * GC;
+        f32x4 acc;
+        if constexpr (PCD) acc = S[db] * *(const f32x4*)(ecs + 16 * db);
+        else acc = S[db] * GC;
 #pragma unroll
         for (int j = 0; j < 2; ++j) mma(acc, o.kh[db][j], fu[j]);
         S[db] = acc;
@@ -433,12 +445,15 @@ __device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK>& o, cons
 // the next blocks into the LDS ring (clr_ring.h).  All operands are tiled, so
 // ring unit u of a block is the contiguous 1-KB run u of
 // [W | Kh^T | Ut^T fragments (vb, 0..1)].
-template <typename E, int DK, int DV, bool HNAT> struct ScanFwdGeom {
+// With PCD (per-channel decay, KDA) one more unit holds exp(b_C) for every key
+// channel, as fp32 (256 floats, padded), and the state-store tile also
+// stages U for its token-major store.
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFwdGeom {
     static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 1-KB units per fragment
     static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF;
-    static constexpr int NU = NWU + NKU + 2 * UPF;
+    static constexpr int NU = NWU + NKU + 2 * UPF + (PCD ? 1 : 0);
     static constexpr int SLOT = RingGeom<NU>::SLOT;
-    static constexpr int TILE = HNAT ? DK * 16 * (int)sizeof(E) : 16;
+    static constexpr int TILE = HNAT ? DK * 16 * (int)sizeof(E) : (PCD ? BLK * 16 * (int)sizeof(E) : 16);
     static constexpr int PF = (144 * 1024 - TILE) / SLOT;
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
     static constexpr int LDS = P * SLOT + TILE;  // ring, then the state-store tile
@@ -446,7 +461,7 @@ template <typename E, int DK, int DV, bool HNAT> struct ScanFwdGeom {
 
 // Scan body for work-group `wgi` of the scan grid; `smem` holds
 // ScanFwdGeom::LDS bytes (16-byte aligned).
-template <typename E, int DK, int DV, bool HNAT>
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false>
 __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int wgi, char* smem) {
     const int H = a.H, NC = a.NC;
     // blocks n0 .. n0 + NB - 1 of each head are scanned (ring index j = n - n0)
@@ -455,7 +470,7 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
     if (!scan_coords(wgi, DV / 16, a.BH, H, b, h, vb)) return;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
-    using SG = ScanFwdGeom<E, DK, DV, HNAT>;
+    using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD>;
     constexpr int ND = SG::ND, UPF = SG::UPF, NWU = SG::NWU, NKU = SG::NKU, NU = SG::NU, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
     using G = RingGeom<NU>;
@@ -473,9 +488,10 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
             auto src = [&](int u) -> const void* {
                 if (u < NWU) return W + u * UE;
                 if (u < NWU + NKU) return KhT + (u - NWU) * UE;
+                if (PCD && u == NU - 1) return a.eC + c * 256 + l * 4;
                 return UtT + (u - NWU - NKU) * UE;
             };
-            ring_issue<NU>(ring + (n % P) * G::SLOT, pid, src, a.gam + c * BLK + l);
+            ring_issue<NU>(ring + (n % P) * G::SLOT, pid, src, PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.gam + c * BLK + l));
         };
         const int pre = NB < P - 1 ? NB : P - 1;
         for (int n = 0; n < pre; ++n) issue(n);
@@ -501,7 +517,7 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
         ScanFwdOps<E, DK> o;
         const char* slot = ring + (n % P) * G::SLOT;
         scan_fwd_from_ring<E, DK, NU>(o, slot, l);
-        scan_fwd_step<E, DK, DV, HNAT, NU>(o, S, a, bh * NC + n0 + n, vb, l, tile, slot);
+        scan_fwd_step<E, DK, DV, HNAT, NU, PCD>(o, S, a, bh * NC + n0 + n, vb, l, tile, slot);
         ring_barrier();
     }
     if (a.S_out) {
@@ -513,10 +529,10 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
     }
 }
 
-template <typename E, int DK, int DV, bool HNAT>
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false>
 __global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
-    __shared__ __align__(16) char smem[ScanFwdGeom<E, DK, DV, HNAT>::LDS];
-    gdn_scan_fwd_body<E, DK, DV, HNAT>(a, blockIdx.x, smem);
+    __shared__ __align__(16) char smem[ScanFwdGeom<E, DK, DV, HNAT, PCD>::LDS];
+    gdn_scan_fwd_body<E, DK, DV, HNAT, PCD>(a, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------

@@ -909,6 +909,136 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 }
 
 // ---------------------------------------------------------------------------
+// KDA forward prep: per-key-channel decay with the delta rule's erase and
+// write (the diagonal-plus-low-rank transition of the StateFlow paper,
+// Sec. 2.1, Eq. 1).  With b = cumsum(g) per channel in the block,
+//   M[t][s] = sum_d k_t[d] k_s[d] e^{b_t[d] - b_s[d]}   (s < t)
+//   T = (I + Diag(beta) M)^-1,  W = T Diag(beta) (K * e^b),  Ut = T Diag(beta) V
+// and the scan forms U = Ut - W S, S <- Diag(e^{b_C}) S + (K * e^{b_C - b})^T U:
+// the delta-rule WY form with the channel-wise decay absorbed into the
+// factors.  M is formed per pair of 16-token tiles with the same references
+// as the GLA products (boundary before the row tile off the diagonal, the
+// tile's middle token on it).  Outputs use the Gated DeltaNet workspace
+// layouts (W, -Ut^T, Kh^T tiled), plus exp(b_C) padded to 256 floats.
+// ---------------------------------------------------------------------------
+template <typename E> struct KdaPrepArgs {
+    const E *k, *v, *g, *beta;
+    int T, H, NC;
+    float* eC;
+    E *W, *KhT, *UtT;
+};
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void kda_prep_kernel(KdaPrepArgs<E> a) {
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int T = a.T, H = a.H, NC = a.NC;
+    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
+    const size_t chunk = ((size_t)b * H + h) * NC + n;
+    const int nvalid = min(BLK, T - n * BLK);
+    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
+    constexpr int PK = RP<E, DK>, PV = RP<E, DV>, PB = DK + 4, ND = DK / 16, KK = DK / 32;
+
+    __shared__ __align__(16) E Ks[BLK * PK], Kd[BLK * PK], Vs[BLK * PV], T1[BLK * PT];
+    __shared__ __align__(16) float Bs[BLK * PB];
+    __shared__ __align__(16) float Am[BLK * AP], Td[4 * 256];
+    __shared__ __align__(16) float zrow[DK];
+    __shared__ float seg[256], s_bet[BLK];
+
+    {
+        const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto vx = load_rows<E, BLK, DV>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
+        const auto gx = load_gate<false, E, DK>(a.g, tok0, h, H, nvalid);
+        if (tid < BLK) s_bet[tid] = tid < nvalid ? to_f(a.beta[(tok0 + tid) * H + h]) : 0.f;
+        if (tid < DK) zrow[tid] = 0.f;
+        store_rows<E, BLK, DK, PK>(kx, Ks);
+        store_rows<E, BLK, DV, PV>(vx, Vs);
+        store_rows<E, BLK, DK, PK>(gx, Kd);  // g staged where K * e^b goes
+        __syncthreads();
+        gate_cumsum<E, DK, PK, PB>(Kd, Bs, seg, nvalid);
+        __syncthreads();
+    }
+    // K * e^b (factors <= 1), and exp(b_C) per channel
+    const float* bC = Bs + (BLK - 1) * PB;
+    for (int idx = tid; idx < BLK * DK; idx += 256) {
+        const int t = idx / DK, d = idx % DK;
+        Kd[t * PK + d] = from_f<E>(to_f(Ks[t * PK + d]) * __expf(Bs[t * PB + d]));
+    }
+    a.eC[chunk * 256 + tid] = tid < DK ? __expf(bC[tid]) : 0.f;
+
+    // Gram block row w: Am[t][s] = beta_t M[t][s] (s < t); column block j <= w
+    {
+        const int tl = 16 * w + r;
+        const float* refO = w > 0 ? Bs + (16 * w - 1) * PB : zrow;  // boundary before tile w
+        const float* refD = Bs + (16 * w + 7) * PB;                 // middle of tile w
+        Frag<E> fo[KK], fd[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            fo[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, Bs + tl * PB, refO, 1.f);
+            fd[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, Bs + tl * PB, refD, 1.f);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 acc = zero4();
+            if (j <= w) {
+                const int s = 16 * j + r;
+                const float* ref = j < w ? refO : refD;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    mma(acc, j < w ? fo[kk] : fd[kk], frag_row_decay(Ks, PK, s, 32 * kk, Bs + s * PB, ref, -1.f));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * w + 4 * g + i, col = 16 * j + r;
+                Am[row * AP + col] = col < row ? s_bet[row] * acc[i] : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+    {
+        // T = (I + A)^-1, wave w holds column block w; T1 = T Diag(beta)
+        f32x4 tc[4];
+        tri_inverse_cols(Am, Td, tc);
+        const int s = 16 * w + r;
+        const float bs = s_bet[s];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) T1[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii] * bs);
+    }
+    __syncthreads();
+    // W^T[d][t] = sum_s (K * e^b)^T[d][s] T1[t][s]  -> stored as W[t][d] (tiled)
+    E* Wout = a.W + chunk * BLK * DK;
+#pragma unroll
+    for (int tile = w; tile < ND * 4; tile += 4) {
+        const int db = tile >> 2, tb = tile & 3;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            mma(acc, ldfrag_tr(Kd, PK, 32 * j, 16 * db, l), ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g));
+        st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
+    }
+    // Ut = T1 V, stored negated as -Ut^T (tiled)
+    E* Uout = a.UtT + chunk * BLK * DV;
+#pragma unroll
+    for (int tile = w; tile < 4 * (DV / 16); tile += 4) {
+        const int tb = tile % 4, vb = tile / 4;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            mma(acc, ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g), ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
+        st4(Uout + toff<E>(16 * vb + r, 16 * tb + 4 * g, BLK), -acc);
+    }
+    // Kh^T[d][t] = K[t][d] e^{b_C[d] - b_t[d]} (tiled), fragment (db, j)
+    E* KhT = a.KhT + chunk * BLK * DK;
+#pragma unroll
+    for (int f = w; f < 2 * ND; f += 4) {
+        const int db = f >> 1, j = f & 1;
+        st_fragT(KhT, f, l, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, bC, -1.f, 0, BLK));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV, bool SG>
@@ -944,6 +1074,43 @@ hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
                        (const E*)ws.dh, (const E*)ws.dVs, (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, L.T, L.H, L.NC};
     launch(SG ? "m2_bwd_intra" : "gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV, SG>, gblk, dim3(512), st, ia);
     return hipGetLastError();
+}
+
+// KDA forward: prep here, the delta-rule scan with a per-channel decay, and
+// the GLA output kernel with U (token-major) in place of V:
+// O = (Q * e^b) S0 + (P * tril) U is the GLA output form.
+template <typename E, int DK, int DV>
+hipError_t launch_kda_fwd_t(const GdnLaunch& L, hipStream_t st) {
+    const dim3 gblk(L.NC, L.H, L.B);
+    const GdnWs& ws = L.ws;
+    KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
+                      ws.eCk, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
+    launch("kda_prep", kda_prep_kernel<E, DK, DV>, gblk, dim3(256), st, pa);
+    GdnScanArgs<E> sa{nullptr, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, L.S_out,
+                      (E*)ws.hT, nullptr, L.H, L.NC, L.B * L.H};
+    sa.eC = ws.eCk;
+    sa.Utok = (E*)ws.Utok;
+    sa.T = L.T;
+    launch("kda_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, true>, dim3(scan_grid(DV / 16, L.B * L.H)),
+           dim3(256), st, sa);
+    if (L.o) {
+        GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)ws.Utok, (const E*)L.g, (const E*)ws.hT,
+                         (E*)L.o, L.T, L.H, L.NC};
+        launch("kda_out", gla_out_kernel<E, DK, DV, false>, gblk, dim3(512), st, oa);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_kda_fwd(const GdnLaunch& L, hipStream_t st) {
+#define CLR_CASE(E, DK, DV) \
+    if (L.dk == DK && L.dv == DV) return launch_kda_fwd_t<E, DK, DV>(L, st);
+    if (L.bf16) {
+        CLR_FOR_GDN_SHAPES(bf16)
+    } else {
+        CLR_FOR_KDA_SHAPES_F32(float)
+    }
+#undef CLR_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gla_fwd(const GlaLaunch& L, hipStream_t st) {

@@ -11,6 +11,8 @@ Distributions (per-token tensors are [B,T,H,d], states [B,H,dk,dv]):
   GLA:            q, k, v ~ N(0,1); g = logsigmoid(N(0,1)) / 16 per key channel;
                   S_in = 0.1 * N(0,1); dO ~ N(0,1); dS_out ~ N(0,1).
   Mamba-2:        as GLA, but one gate per (token, head): g [B,T,H].
+  KDA:            q, k, v, beta, S_in as Gated DeltaNet; g = logsigmoid(N(0,1)) / 16
+                  per key channel [B,T,H,dk] as GLA.
   Short conv:     x ~ N(0,1) [B,T,C]; w = 0.5 * N(0,1) [C,W]; bias = 0.1 * N(0,1);
                   state_in ~ N(0,1) [B,W-1,C]; dy ~ N(0,1); dstate_out ~ N(0,1)
                   (float32: state gradients are partial sums and stay fp32).
@@ -35,6 +37,8 @@ CONFIGS = {
     "gdn_bf16_H16_T262144_d128": dict(kind="gdn", dtype="bf16", B=1, H=16, T=262144, dk=128, dv=128, N=64),
     # short convolution in front of the Gated DeltaNet workload (q, k, v channels)
     "shortconv_bf16_T8192_C6144_W4": dict(kind="shortconv", dtype="bf16", B=1, T=8192, C=6144, W=4, act=1, N=4),
+    # per-channel-decay delta rule at the Gated DeltaNet workload's shape (forward)
+    "kda_bf16_H16_T8192_d128": dict(kind="kda", dtype="bf16", B=1, H=16, T=8192, dk=128, dv=128, N=4),
     # scalar-gate member at the GLA workload's shape
     "mamba2_bf16_B4_H16_T4096_dk128_dv256": dict(kind="mamba2", dtype="bf16", B=4, H=16, T=4096, dk=128, dv=256, N=1),
 }
@@ -145,6 +149,29 @@ def make_mamba2(B, T, H, dk, dv, dtype="bf16", seed=0, gate_scale=1.0 / 16.0):
     return d
 
 
+def make_kda(B, T, H, dk, dv, dtype="bf16", seed=0, gate_scale=1.0 / 16.0):
+    """KDA inputs: q, k L2-normalised, v, beta, S_in as Gated DeltaNet; the
+    gate per key channel as GLA."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _l2n(_normal(rng, (B, T, H, dk)))
+    k = _l2n(_normal(rng, (B, T, H, dk)))
+    v = _normal(rng, (B, T, H, dv))
+    z = _normal(rng, (B, T, H, dk)).astype(np.float64)
+    logsig = -(np.maximum(-z, 0) + np.log1p(np.exp(-np.abs(z))))
+    g = (logsig * gate_scale).astype(np.float32)
+    beta = _sigmoid(_normal(rng, (B, T, H)))
+    S_in = (0.1 * _normal(rng, (B, H, dk, dv))).astype(np.float32)
+    dO = _normal(rng, (B, T, H, dv))
+    dS_out = _normal(rng, (B, H, dk, dv))
+    d = dict(q=q, k=k, v=v, g=g, beta=beta, S_in=S_in, dO=dO, dS_out=dS_out)
+    if dtype == "bf16":
+        for key in ("q", "k", "v", "g", "beta", "dO"):
+            d[key] = bf16_round(d[key])
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return d
+
+
 def make_shortconv(B, T, C, W, dtype="bf16", seed=0):
     """Short-convolution inputs (x, w, bias, state_in, dy, dstate_out)."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -166,5 +193,5 @@ def make_shortconv(B, T, C, W, dtype="bf16", seed=0):
 def make(cfg: dict, seed: int, **kw):
     if cfg["kind"] == "shortconv":
         return make_shortconv(cfg["B"], cfg["T"], cfg["C"], cfg["W"], cfg["dtype"], seed)
-    f = {"gdn": make_gdn, "gla": make_gla, "mamba2": make_mamba2}[cfg["kind"]]
+    f = {"gdn": make_gdn, "gla": make_gla, "mamba2": make_mamba2, "kda": make_kda}[cfg["kind"]]
     return f(cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], cfg["dtype"], seed, **kw)

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libclr.so")
 
 CLR_OK, CLR_EINVAL, CLR_ENOTSUP, CLR_EWORKSPACE, CLR_EHIP = range(5)
 CLR_F32, CLR_BF16 = 0, 1
-OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD, OP_M2_FWD, OP_M2_BWD = range(6)
+OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD, OP_M2_FWD, OP_M2_BWD, OP_KDA_FWD = range(7)
 
 
 class ClrShape(ctypes.Structure):
@@ -57,7 +57,7 @@ def load(path: Optional[str] = None):
     sp = ctypes.POINTER(ClrShape)
     lib.clr_workspace_bytes.argtypes = [sp, i]
     lib.clr_workspace_bytes.restype = sz
-    for name in ("gdn_fwd", "gla_fwd", "mamba2_fwd"):
+    for name in ("gdn_fwd", "gla_fwd", "mamba2_fwd", "kda_fwd"):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 9 + [sz, vp]
         f.restype = i
@@ -244,6 +244,12 @@ def gdn_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, ws=None, out=None):
 def gla_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None, out=None):
     """GLA chunk backward.  Returns dict dq, dk, dv, dg, dS_in."""
     return _bwd("gla_bwd", OP_GLA_BWD, q, k, v, g, None, S_in, dO, dS_out, ws, out)
+
+
+def kda_fwd(q, k, v, g, beta, S_in=None, want_state=True, ws=None, o=None, S_out=None):
+    """KDA chunk forward (per-key-channel gate g [B,T,H,dk], beta [B,T,H]).
+    Returns (o, S_out)."""
+    return _fwd("kda_fwd", OP_KDA_FWD, q, k, v, g, beta, S_in, want_state, ws, o, S_out)
 
 
 def mamba2_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None):

@@ -228,3 +228,38 @@ class ShortConvChunked:
             ds = r["dstate_in"]
             self.saved[i] = None
         return dict(dx=dx, dw=grads["dw"], dbias=grads["dbias"], dstate_in=ds)
+
+
+class KdaForwardChunked:
+    """Forward of one KDA layer (per-key-channel decay with the delta rule)
+    over N sequence chunks, handing S_out -> S_in.  The library has no KDA
+    backward."""
+
+    kind = "kda"
+
+    def __init__(self, q, k, v, g, beta, N: int):
+        from . import ops
+        self.ops = ops
+        self.q, self.k, self.v, self.g, self.beta = q, k, v, g, beta
+        self.N = N
+        self.bounds = _bounds(q.shape[1], N)
+        L = self.bounds[0][1]
+        B, _, H, dk = q.shape
+        import torch
+        shape = ops.ClrShape(B, L, H, dk, v.shape[-1], ops._dtype_code(q))
+        self.ws = torch.empty(max(ops.workspace_bytes(shape, ops.OP_KDA_FWD), 256), dtype=torch.uint8, device=q.device)
+
+    def forward(self, S_in=None, o=None):
+        import torch
+        B, T, H, dk = self.q.shape
+        if o is None:
+            o = torch.empty((B, T, H, self.v.shape[-1]), dtype=self.q.dtype, device=self.q.device)
+        S = S_in
+        for i in range(self.N):
+            a, b = self.bounds[i]
+            view = o[:, a:b]
+            args = tuple(_sl(t, a, b) for t in (self.q, self.k, self.v, self.g, self.beta))
+            oi, S = self.ops.kda_fwd(*args, S, ws=self.ws, o=view if view.is_contiguous() else None)
+            if oi.data_ptr() != view.data_ptr():
+                view.copy_(oi)
+        return o, S

@@ -91,7 +91,8 @@ typedef enum {
     CLR_OP_GLA_FWD = 2,
     CLR_OP_GLA_BWD = 3,
     CLR_OP_M2_FWD = 4,
-    CLR_OP_M2_BWD = 5
+    CLR_OP_M2_BWD = 5,
+    CLR_OP_KDA_FWD = 6
 } clr_op_t;
 
 typedef struct {
@@ -143,6 +144,20 @@ int mamba2_bwd(const clr_shape_t* shape, const void* q, const void* k, const voi
                const void* g, const void* beta, const float* S_in, const void* dO,
                const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
                float* dS_in, void* ws, size_t ws_bytes, void* stream);
+
+/* KDA member of the family (StateFlow paper, Sec. 2.1, Eq. 1: F_t
+ * diagonal-plus-low-rank), key-major:
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,   alpha_t = exp(g_t) in R^dk (per key channel).
+ * Forward only.  Same arguments as gdn_fwd except g, which is [B, T, H, dk]
+ * as for GLA; beta is required.  Head sizes as for GDN (fp32: d <= 64,
+ * CLR_ENOTSUP otherwise).  Workspace:
+ * CLR_OP_KDA_FWD.  The per-block decays use 16-token sub-tiles with the same
+ * e^80 bound as the GLA path (exact while the decay within half a tile stays
+ * within 80 nats per channel). */
+int kda_fwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+            const void* g, const void* beta, const float* S_in, void* o, float* S_out,
+            void* ws, size_t ws_bytes, void* stream);
 
 /* Causal short convolution with a boundary state.
  * The StateFlow paper (Sec. 1 and Sec. 3.3) hands the boundary state of a
