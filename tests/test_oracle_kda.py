@@ -145,3 +145,22 @@ def test_chunk_split_is_bit_exact(N):
     for key in ("dq", "dk", "dv", "dg", "dbeta"):
         assert np.array_equal(np.concatenate([p[key] for p in parts], 1), r1[key]), key
     assert np.array_equal(ds, r1["dS_in"])
+
+
+@pytest.mark.parametrize("C", [4, 16, 64])
+def test_chunk_form_backward_equals_the_oracle(C):
+    """The block adjoints the GPU backward implements (tests/kda_chunk_bwd.py)
+    against the oracle's per-token adjoints."""
+    from tests.kda_chunk_bwd import kda_chunk_bwd
+    rng = np.random.default_rng(50 + C)
+    T, dk, dv = 150, 6, 5
+    x = _rand(rng, 1, T, 1, dk, dv)
+    dO = rng.standard_normal((1, T, 1, dv))
+    dS = rng.standard_normal((1, 1, dk, dv))
+    ref = oracle.kda_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S_in"], dO, dS)
+    got = kda_chunk_bwd(x["q"][0, :, 0], x["k"][0, :, 0], x["v"][0, :, 0], x["g"][0, :, 0], x["beta"][0, :, 0],
+                        x["S_in"][0, 0], dO[0, :, 0], dS[0, 0], C)
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        r = ref[key][0, :, 0]
+        assert np.allclose(got[key], r, atol=1e-9 * max(1.0, np.max(np.abs(r)))), key
+    assert np.allclose(got["dS_in"], ref["dS_in"][0, 0], atol=1e-9)
