@@ -1,814 +1,9 @@
 // gdn_bwd.hip -- Gated DeltaNet chunk backward on gfx950.
-//
-// Given (q, k, v, g, beta, S_in) and upstream (dO, dS_out) the chunk backward
-// of the StateFlow paper (Sec. 3.1, "Backward Computation") returns the input
-// gradients and dS_in.  The forward is recomputed from S_in (full activation
-// recomputation, as in that paper's Sec. 4.1 setup), then:
-//
-//   prep   (as in the forward)        gamma, T, W, Ut, Kh^T
-//   prep2  (parallel over blocks)     W^T, Kh, dvloc = (Q K^T * G * tril)^T dO and
-//                                     R = (Diag(Gam) Q)^T dO - W^T dvloc (the dS-independent
-//                                     part of the reverse state step)
-//   scan   (forward recompute)        h_n (state entering block n, key-major), U_n
-//   dscan  (reverse, sequential)      dh_n = dL/dS_{n+1};  dU_n = dvloc_n + Kh_n dh_n;
-//                                     dS_n = Gam_C dh_n + (Diag(Gam) Q_n)^T dO_n - W_n^T dU_n
-//                                          = Gam_C dh_n + R_n - W_n^T (Kh_n dh_n)
-//   intra  (parallel over blocks)     dq, dk, dv, dbeta, dg of every block from
-//                                     (h_n, dh_n, U_n, dU_n) by the block adjoints:
-//     dQ  = Diag(Gam) dO h^T + dPm K,   dPm = (dO U^T) * G * tril
-//     dK  = dPm^T Q + Diag(exp(gamma_C - gamma)) U dh^T + Diag(beta Gam) T^T dW + (M + M^T) K
-//     dW  = -dU h^T,  dT = dU (Diag(beta) V)^T + dW (Diag(beta Gam) K)^T,
-//     dA  = -T^T dT T^T (strictly lower),  M = dA * beta_r * G,
-//     dV  = Diag(beta) T^T dU,
-//     dbeta_s = (T^T dU)_s . v_s + Gam_s (T^T dW)_s . k_s + sum_c dA[s,c] (K K^T * G)[s,c],
-//     dg_u = sum_{t >= u} y_t + sum_{t >= u > s} (dP*P + dA*A)[t][s] + sum_{r < u} z_r
-//            + Gam_C <h_n, dh_n>,   the chain rule through gamma = cumsum(g) with the
-//            within-suffix pair terms (which cancel exactly) left out:
-//            y_t = q_t . (Gam_t h_n do_t) + beta_t Gam_t (T^T dW)_t . k_t,
-//            z_r = exp(gamma_C - gamma_r) k_r . (U dh^T)_r.
-// Products run on the matrix cores (bf16 operands, fp32 accumulation; fp32
-// operands for fp32 inputs); each work-group computes transposed ([feature][token])
-// output tiles so that every lane stores four contiguous values.
-#include "gdn_kernels.h"
+// Kernels: gdn_bwd_kernels.h.  This file holds the launch sequence.
+#include "gdn_bwd_kernels.h"
 
 namespace clr {
 
-template <typename E> struct GdnPrep2Args {
-    const E *q, *k, *dO;
-    const float* gam;
-    const E* W;
-    float* Rt;
-    E *WT, *Kh, *dvlT;
-    int T, H, NC;
-};
-
-template <typename E> struct GdnScanBwdArgs {
-    const float* gam;
-    const E *Kh, *WT, *dvlT;
-    const float* Rt;
-    const float* dS_out;
-    float* dS_in;
-    E *dh, *dUT;
-    int H, NC, BH;
-};
-
-template <typename E> struct GdnIntraArgs {
-    const E *q, *k, *v, *beta, *dO;
-    const float* gam;
-    const E *h, *dh, *UT, *dUT;
-    E *dq, *dk, *dv, *dg, *dbeta;
-    int T, H, NC;
-};
-
-// ---------------------------------------------------------------------------
-// prep2: one work-group (4 waves) per (block, head, batch).  Q, dO and W are
-// staged row-major in LDS (all loads in flight at once) and read transposed
-// where a product contracts over tokens; wave w keeps K rows 16w.. in
-// registers (B operand of P and the rows of Kh it writes).
-// ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
-    const int T = a.T, H = a.H, NC = a.NC;
-    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
-    const size_t chunk = ((size_t)b * H + h) * NC + n;
-    const int nvalid = min(BLK, T - n * BLK);
-    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
-    const E* qb = a.q + tok0 * ldk + (size_t)h * DK;
-    const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
-    const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
-    constexpr int PQ = RP<E, DK>, PO = RP<E, DV>, KK = DK / 32, ND = DK / 16, NVB = DV / 16;
-
-    __shared__ float s_gam[BLK], s_Gam[BLK];
-    __shared__ __align__(16) E Qs[BLK * PQ], dOs[BLK * PO], Ws[BLK * PQ], dvlt[DV * PT];
-
-    const auto qx = load_rows<E, BLK, DK>(qb, ldk, nvalid);
-    const auto ox = load_rows<E, BLK, DV>(dob, ldv, nvalid);
-    const auto wx = load_tiled<E, BLK, DK>(a.W + chunk * BLK * DK);
-    Frag<E> fk[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) fk[kk] = ldfrag_row(kb, 16 * w + r, nvalid, ldk, 32 * kk + 4 * g);
-    if (tid < BLK) {
-        const float gm = a.gam[chunk * BLK + tid];
-        s_gam[tid] = gm;
-        s_Gam[tid] = __expf(gm);
-    }
-    store_rows<E, BLK, DK, PQ>(qx, Qs);
-    store_rows<E, BLK, DV, PO>(ox, dOs);
-    store_untiled<E, BLK, DK, PQ>(wx, Ws);
-    __syncthreads();
-
-    const float gC = s_gam[BLK - 1];
-    // W^T (tiled; A: m = d, k = t): fragment (db, j) is the B fragment of W
-    // over tokens 32j.., columns 16db..
-    E* WT = a.WT + chunk * BLK * DK;
-#pragma unroll
-    for (int f = w; f < 2 * ND; f += 4) st_fragT(WT, f, l, ldfrag_tr(Ws, PQ, 32 * (f & 1), 16 * (f >> 1), l));
-    // Kh[t][d] = exp(gamma_C - gamma_t) K[t][d] (tiled; A: m = t, k = d):
-    // fragments (w, kk) are this wave's K rows.
-    {
-        E* Kh = a.Kh + chunk * BLK * DK;
-        const float ek = __expf(gC - s_gam[16 * w + r]);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            Frag<E> x = fk[kk];
-            if constexpr (sizeof(E) == 2) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x.v[i] = (bf16)((float)x.v[i] * ek);
-            } else {
-                x.lo = x.lo * ek;
-                x.hi = x.hi * ek;
-            }
-            st_fragT(Kh, w * KK + kk, l, x);
-        }
-    }
-    // dvloc[s][v] = sum_t P[t][s] dO[t][v],  P[t][s] = (q_t . k_s) exp(gamma_t - gamma_s), s <= t.
-    // Wave w owns s-block w: P[tb][w] tiles (rows t, cols s) chain into A = P^T.
-    f32x4 P[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = zero4();
-        if (tb >= w) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) mma(acc, ldfrag(Qs + (16 * tb + r) * PQ + 32 * kk + 4 * g), fk[kk]);
-            const int s = 16 * w + r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * g + i;
-                acc[i] = (s <= t) ? acc[i] * __expf(s_gam[t] - s_gam[s]) : 0.f;
-            }
-        }
-        P[tb] = acc;
-    }
-    Frag<E> fp[2];
-    fp[0] = frag_from_acc<E>(P[0], P[1]);
-    fp[1] = frag_from_acc<E>(P[2], P[3]);
-    E* dvlT = a.dvlT + chunk * BLK * DV;
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
-        st4(dvlT + toff<E>(16 * vb + r, 16 * w + 4 * g, BLK), acc);
-        st4(dvlt + (16 * vb + r) * PT + 16 * w + 4 * g, acc);
-    }
-    __syncthreads();
-    // Qs <- Diag(Gam) Q in place
-#pragma unroll
-    for (int j = 0; j < RowsRegs<E, BLK, DK>::N; ++j) {
-        constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = DK / VEC;
-        const int idx = tid + 256 * j, t = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-        const float G = s_Gam[t];
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) Qs[t * PQ + c + i] = from_f<E>(to_f(Qs[t * PQ + c + i]) * G);
-    }
-    __syncthreads();
-    // R[d][v] = sum_t Qg^T[d][t] dO[t][v] - sum_t W^T[d][t] dvloc[t][v]   (fp32, accumulator-tiled)
-    float* Rt = a.Rt + chunk * DK * DV;
-    for (int tile = w; tile < ND * NVB; tile += 4) {
-        const int db = tile % ND, vb = tile / ND;
-        f32x4 acc = zero4(), acc2 = zero4();
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            mma(acc, ldfrag_tr(Qs, PQ, 32 * j, 16 * db, l), ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
-            mma(acc2, ldfrag_tr(Ws, PQ, 32 * j, 16 * db, l), ldfrag(dvlt + (16 * vb + r) * PT + 32 * j + 4 * g));
-        }
-        *(f32x4*)(Rt + atoff(db, vb, DK, l)) = acc - acc2;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// dscan: one work-group per (16-wide value slice, head, batch), blocks in
-// reverse.  Wave 0 runs the reverse recurrence with dS in accumulator tiles;
-// waves 1..3 stream the operands of the next blocks into the LDS ring
-// (clr_ring.h).  Ring unit u of a block is the contiguous 1-KB run u of
-// [Kh | W^T | R tiles (., vb) | dvloc^T fragments (vb, 0..1)], all tiled.
-// ---------------------------------------------------------------------------
-template <typename E, int DK> struct ScanBwdOps {
-    Frag<E> kh[4][DK / 32];   // Kh rows (A: m = t, k = d)
-    Frag<E> wt[DK / 16][2];   // W^T rows (A: m = d, k = t)
-    f32x4 rt[DK / 16];        // R accumulator tiles (rows d, column v0 + r)
-    Frag<E> dvl[2];           // dvloc^T[v0 + r][token tile pairs] (accumulator layout)
-    float gC;
-};
-
-template <typename E, int DK> struct ScanBwdRing {
-    static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;
-    static constexpr int KK = DK / 32, ND = DK / 16;
-    static constexpr int NKU = 4 * KK * UPF, NWU = 2 * ND * UPF, NRU = ND, NDU = 2 * UPF;
-    static constexpr int NU = NKU + NWU + NRU + NDU;
-};
-
-template <typename E, int DK, int NU>
-__device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK>& o, const char* slot, int l) {
-    using Rg = ScanBwdRing<E, DK>;
-    constexpr int KK = DK / 32, UPF = Rg::UPF;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) o.kh[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
-#pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) o.wt[db][j] = ring_frag(slot, Rg::NKU / UPF + 2 * db + j, l, (E*)nullptr);
-        o.rt[db] = *(const f32x4*)(slot + (Rg::NKU + Rg::NWU + db) * RING_UNIT + l * 16);
-    }
-    // dvloc fragments start at unit NKU + NWU + NRU, i.e. fragment index (that) / UPF
-    static_assert((Rg::NKU + Rg::NWU + Rg::NRU) % UPF == 0, "fragment alignment");
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        o.dvl[j] = ring_frag(slot, (Rg::NKU + Rg::NWU + Rg::NRU) / UPF + j, l, (E*)nullptr);
-    o.gC = ring_small<NU>(slot, BLK - 1);
-}
-
-// One reverse step: on entry dS = dL/dS_{n+1}; writes dh_n = dS and
-// dU_n = dvloc_n + Kh_n dS; leaves dS = dL/dS_n = Gam_C dS + R_n - W_n^T (Kh_n dS).
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 (&dS)[DK / 16],
-                                              const GdnScanBwdArgs<E>& a, size_t chunk, int vb, int l, E* tile) {
-    constexpr int ND = DK / 16;
-    store_state_tiled<E, DK, DV>(a.dh + chunk * DK * DV, dS, tile, 16 * vb, l);
-    Frag<E> fs[DK / 32];
-#pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
-    f32x4 dUp[4];
-    E* dUT = a.dUT + chunk * BLK * DV;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, o.kh[tb][kk], fs[kk]);
-        dUp[tb] = acc;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const Frag<E>& f = o.dvl[j];
-        f32x4 lo, hi;
-        if constexpr (sizeof(E) == 2) {
-            lo = f32x4{(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]};
-            hi = f32x4{(float)f.v[4], (float)f.v[5], (float)f.v[6], (float)f.v[7]};
-        } else {
-            lo = f.lo;
-            hi = f.hi;
-        }
-        st8T(dUT, 2 * vb + j, l, dUp[2 * j] + lo, dUp[2 * j + 1] + hi);
-    }
-    Frag<E> fu[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) fu[j] = frag_from_acc<E>(-dUp[2 * j], -dUp[2 * j + 1]);
-    const float GC = __expf(o.gC);
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-        f32x4 acc = dS[db] * GC + o.rt[db];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc, o.wt[db][j], fu[j]);
-        dS[db] = acc;
-    }
-}
-
-template <typename E, int DK> struct ScanBwdGeom {
-    static constexpr int NU = ScanBwdRing<E, DK>::NU;
-    static constexpr int SLOT = RingGeom<NU>::SLOT;
-    static constexpr int TILE = DK * 16 * (int)sizeof(E);
-    static constexpr int PF = (144 * 1024 - TILE) / SLOT;
-    static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
-    static constexpr int LDS = P * SLOT + TILE;
-};
-
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, int wgi, char* smem) {
-    const int H = a.H, NC = a.NC;
-    int b, h, vb;
-    if (!scan_coords(wgi, DV / 16, a.BH, H, b, h, vb)) return;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
-    const int v0 = 16 * vb;
-    constexpr int ND = DK / 16;
-    using Rg = ScanBwdRing<E, DK>;
-    using SG = ScanBwdGeom<E, DK>;
-    constexpr int NU = Rg::NU, UPF = Rg::UPF, P = SG::P;
-    constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
-    using G = RingGeom<NU>;
-    char* ring = smem;
-    E* tile = (E*)(smem + P * G::SLOT);
-    const size_t bh = (size_t)b * H + h;
-
-    // round m handles block NC - 1 - m
-    if (w > 0) {  // producers
-        const int pid = w - 1;
-        auto issue = [&](int m) {
-            const size_t c = bh * NC + (NC - 1 - m);
-            const E* Kh = a.Kh + c * BLK * DK + l * LE;
-            const E* WT = a.WT + c * BLK * DK + l * LE;
-            const float* Rt = a.Rt + c * DK * DV + (size_t)vb * ND * 256 + l * 4;
-            const E* dvl = a.dvlT + c * BLK * DV + (size_t)(2 * vb * UPF) * UE + l * LE;
-            auto src = [&](int u) -> const void* {
-                if (u < Rg::NKU) return Kh + u * UE;
-                if (u < Rg::NKU + Rg::NWU) return WT + (u - Rg::NKU) * UE;
-                if (u < Rg::NKU + Rg::NWU + Rg::NRU) return Rt + (u - Rg::NKU - Rg::NWU) * 256;
-                return dvl + (u - Rg::NKU - Rg::NWU - Rg::NRU) * UE;
-            };
-            ring_issue<NU>(ring + (m % P) * G::SLOT, pid, src, a.gam + c * BLK + l);
-        };
-        const int pre = NC < P - 1 ? NC : P - 1;
-        for (int m = 0; m < pre; ++m) issue(m);
-        ring_wait<G::NU_MIN>(pre - 1);  // round 0 has landed
-        ring_barrier();
-        for (int m = 0; m < NC; ++m) {
-            if (m + P - 1 < NC) issue(m + P - 1);
-            const int last = (m + P - 1 < NC ? m + P - 1 : NC - 1);
-            ring_wait<G::NU_MIN>(last - (m + 1));  // round m + 1 has landed
-            ring_barrier();
-        }
-        return;
-    }
-
-    f32x4 dS[ND];
-    const float* dSo = a.dS_out ? a.dS_out + bh * DK * DV : nullptr;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dS[db][i] = dSo ? dSo[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
-    ring_barrier();
-    for (int m = 0; m < NC; ++m) {
-        ScanBwdOps<E, DK> o;
-        scan_bwd_from_ring<E, DK, NU>(o, ring + (m % P) * G::SLOT, l);
-        scan_bwd_step<E, DK, DV>(o, dS, a, bh * NC + (NC - 1 - m), vb, l, tile);
-        ring_barrier();
-    }
-    float* dSi = a.dS_in + bh * DK * DV;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dSi[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = dS[db][i];
-}
-
-// The forward recompute (state entering every block) and the reverse scan are
-// independent given the prep outputs; one launch runs both, work-groups
-// [0, G) the former and [G, 2G) the latter, so together they fill the chip.
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_scan_pair_kernel(GdnScanArgs<E> fa, GdnScanBwdArgs<E> ba, int G) {
-    constexpr int LF = ScanFwdGeom<E, DK, DV, true>::LDS, LB = ScanBwdGeom<E, DK>::LDS;
-    __shared__ __align__(16) char smem[LF > LB ? LF : LB];
-    if ((int)blockIdx.x < G) gdn_scan_fwd_body<E, DK, DV, true>(fa, blockIdx.x, smem);
-    else gdn_scan_bwd_body<E, DK, DV>(ba, blockIdx.x - G, smem);
-}
-
-// ---------------------------------------------------------------------------
-// intra: one work-group (4 waves) per (block, head, batch).  Wave w owns the
-// 16 tokens 16w..16w+15 of the block, both as "t" (rows of dQ) and as "s"
-// (rows of dK, dV, dbeta).  K, Q, dO and V are staged row-major, U^T and dU^T
-// as [v][t]; every global load of a phase is issued at once, and products
-// that contract over the other index read the tiles transposed (ldfrag_tr).
-// The tiled h_n / dh_n fragments are read from global memory one 16-row
-// block ahead of their use.
-// ---------------------------------------------------------------------------
-template <typename E, int DK, int DV> struct IntraLds {
-    static constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
-    // persistent
-    static constexpr size_t o_Ks = 0;                                  // E[64][PK]     K
-    static constexpr size_t o_KKG = o_Ks + sizeof(E) * BLK * PK;       // f32[64][AP]   (K K^T * G), strictly lower
-    static constexpr size_t o_TT = o_KKG + 4 * BLK * AP;               // E[64][PT]     TT[s][t] = T[t][s]
-    static constexpr size_t o_Tr = o_TT + sizeof(E) * BLK * PT;        // E[64][PT]     T row-major
-    static constexpr size_t o_E = o_Tr + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms), + 512 spare
-    static constexpr size_t o_U = o_E + 4 * (BLK * 65 + 512);          // union starts here
-    // phase 0: Am f32[64][AP], Td f32[4][16][16]
-    static constexpr size_t p0_Am = o_U, p0_Td = p0_Am + 4 * BLK * AP;
-    static constexpr size_t p0_end = p0_Td + 4 * 4 * 256;
-    // phase A: Qs E[64][PK], dOs E[64][PV], UTs E[DV][PT]
-    static constexpr size_t pA_Q = o_U, pA_dO = pA_Q + sizeof(E) * BLK * PK;
-    static constexpr size_t pA_UT = pA_dO + sizeof(E) * BLK * PV;
-    static constexpr size_t pA_end = pA_UT + sizeof(E) * DV * PT;
-    // phase B: dUTs E[DV][PT], dWs E[64][PK], dTT E[64][PT], Ms E[64][PT], Vs E[64][PV]
-    static constexpr size_t pB_dUT = o_U, pB_dW = pB_dUT + sizeof(E) * DV * PT;
-    static constexpr size_t pB_dTT = pB_dW + sizeof(E) * BLK * PK;
-    static constexpr size_t pB_Ms = pB_dTT + sizeof(E) * BLK * PT;
-    static constexpr size_t pB_V = pB_Ms + sizeof(E) * BLK * PT;
-    static constexpr size_t pB_end = pB_V + sizeof(E) * BLK * PV;
-    static constexpr size_t m01 = p0_end > pA_end ? p0_end : pA_end;
-    static constexpr size_t total = m01 > pB_end ? m01 : pB_end;
-};
-
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
-    using Lay = IntraLds<E, DK, DV>;
-    constexpr int NT = 512;
-    constexpr int PK = Lay::PK, PV = Lay::PV, KK = DK / 32, KV = DV / 32, ND = DK / 16, NDH = ND / 2;
-    constexpr int NVH = DV / 32;  // value blocks per half
-    static_assert(Lay::total <= 150 * 1024, "LDS budget");
-    __shared__ __align__(16) char lds[Lay::total];
-    E* Ks = (E*)(lds + Lay::o_Ks);
-    float* KKG = (float*)(lds + Lay::o_KKG);
-    E* TT = (E*)(lds + Lay::o_TT);
-    E* Tr = (E*)(lds + Lay::o_Tr);
-    float* Eb = (float*)(lds + Lay::o_E);
-
-    // per-token partial sums of the two halves, combined in a fixed order
-    __shared__ float s_gam[BLK], s_bet[BLK], s_y[BLK], s_kdk[BLK], s_red[8];
-    __shared__ float s_q2[2][BLK], s_k2[2][BLK], s_g2[2][BLK], s_v2[2][BLK], s_b2[2][BLK];
-
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    // wave w8: token block w = w8 & 3, half hf = w8 >> 2 (halves split the
-    // feature / value / token-block loops of each phase)
-    const int tid = threadIdx.x, w8 = tid >> 6, w = w8 & 3, hf = w8 >> 2, l = tid & 63, r = l & 15, g = l >> 4;
-    const int T = a.T, H = a.H, NC = a.NC;
-    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
-    const size_t chunk = ((size_t)b * H + h) * NC + n;
-    const int nvalid = min(BLK, T - n * BLK);
-    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
-    const E* qb = a.q + tok0 * ldk + (size_t)h * DK;
-    const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
-    const E* vbase = a.v + tok0 * ldv + (size_t)h * DV;
-    const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
-    const E* S0 = a.h + chunk * DK * DV;   // h_n  [d][v], tiled
-    const E* dS1 = a.dh + chunk * DK * DV; // dh_n [d][v], tiled
-    const E* UT = a.UT + chunk * BLK * DV;
-    const E* dUT = a.dUT + chunk * BLK * DV;
-
-    // ---------------- phase 0: gates, K, Gram, T -----------------------------
-    const auto kx = load_rows<E, BLK, DK, NT>(kb, ldk, nvalid);
-    const auto qx = load_rows<E, BLK, DK, NT>(qb, ldk, nvalid);
-    const auto ox = load_rows<E, BLK, DV, NT>(dob, ldv, nvalid);
-    const auto ux = load_tiled<E, DV, BLK, NT>(UT);
-    if (tid < BLK) {
-        s_gam[tid] = a.gam[chunk * BLK + tid];
-        s_bet[tid] = tid < nvalid ? to_f(a.beta[(tok0 + tid) * H + h]) : 0.f;
-    }
-    store_rows<E, BLK, DK, PK, NT>(kx, Ks);
-    __syncthreads();
-    {
-        float* Am = (float*)(lds + Lay::p0_Am);
-        Frag<E> fa[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) fa[kk] = ldfrag(Ks + (16 * w + r) * PK + 32 * kk + 4 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if ((j & 1) != hf) continue;
-            f32x4 acc = zero4();
-            if (j <= w) {
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) mma(acc, fa[kk], ldfrag(Ks + (16 * j + r) * PK + 32 * kk + 4 * g));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * w + 4 * g + i, col = 16 * j + r;
-                const float kkg = col < row ? acc[i] * __expf(s_gam[row] - s_gam[col]) : 0.f;
-                KKG[row * AP + col] = kkg;
-                Am[row * AP + col] = s_bet[row] * kkg;
-            }
-        }
-        __syncthreads();
-        if (hf == 0) {
-            f32x4 tc[4];
-            tri_inverse_cols(Am, (float*)(lds + Lay::p0_Td), tc);  // waves 0..3; one barrier inside
-            // wave w holds column block w of T: write T row-major (Tr) and transposed (TT)
-            const int s = 16 * w + r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) Tr[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii]);
-                st4(TT + s * PT + 16 * i + 4 * g, tc[i]);
-            }
-        } else {
-            __syncthreads();  // matches the barrier inside tri_inverse_cols
-        }
-        __syncthreads();
-    }
-    // ---------------- phase A: dQ, and the output / state-update parts of dK ---
-    E* Qs = (E*)(lds + Lay::pA_Q);
-    E* dOs = (E*)(lds + Lay::pA_dO);
-    E* UTs = (E*)(lds + Lay::pA_UT);
-    // phase B operands: in flight during phase A
-    const auto vx = load_rows<E, BLK, DV, NT>(vbase, ldv, nvalid);
-    const auto dux = load_tiled<E, DV, BLK, NT>(dUT);
-    store_rows<E, BLK, DK, PK, NT>(qx, Qs);
-    store_rows<E, BLK, DV, PV, NT>(ox, dOs);
-    store_untiled<E, DV, BLK, PT, NT>(ux, UTs);
-    __syncthreads();
-
-    const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
-    const float gam_tw = s_gam[tw];
-    const float gC = s_gam[BLK - 1];
-    Frag<E> fdo[KV], fU[KV];
-#pragma unroll
-    for (int kk = 0; kk < KV; ++kk) {
-        fdo[kk] = ldfrag(dOs + tw * PV + 32 * kk + 4 * g);    // Bt = dO[t][v], rows of block w
-        fU[kk] = ldfrag_tr(UTs, PT, 32 * kk, 16 * w, l);     // Bt = U[s][v], rows of block w
-    }
-    // dPm^T[sb][w]: rows s, cols t = tw
-    f32x4 dPT[4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-        f32x4 acc = zero4();
-        if (sb <= w) {
-#pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag_tr(UTs, PT, 32 * kk, 16 * sb, l), fdo[kk]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s = 16 * sb + 4 * g + i;
-                acc[i] = (s <= tw) ? acc[i] * __expf(gam_tw - s_gam[s]) : 0.f;
-            }
-        }
-        dPT[sb] = acc;
-    }
-    // Gate cross terms of the output path: E[t][s] = dP[t][s] P[t][s]
-    // = dPm[t][s] (q_t . k_s)  (s <= t), with (Q K^T)^T tiles rows s, col t = tw.
-    {
-        Frag<E> fq[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) fq[kk] = ldfrag(Qs + tw * PK + 32 * kk + 4 * g);
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            if ((sb & 1) != hf) continue;
-            f32x4 qk = zero4();
-            if (sb <= w) {
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) mma(qk, ldfrag(Ks + (16 * sb + r) * PK + 32 * kk + 4 * g), fq[kk]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Eb[tw * 65 + 16 * sb + 4 * g + i] = dPT[sb][i] * qk[i];
-        }
-    }
-    // dPm[tb][w]: rows t, cols s = tw
-    f32x4 dP[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = zero4();
-        if (tb >= w) {
-#pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag(dOs + (16 * tb + r) * PV + 32 * kk + 4 * g), fU[kk]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * g + i;
-                acc[i] = (tw <= t) ? acc[i] * __expf(s_gam[t] - gam_tw) : 0.f;
-            }
-        }
-        dP[tb] = acc;
-    }
-    // One pass over this half's 16-row blocks of h_n and dh_n (fragments of the
-    // next block loaded while the current one is used):
-    //   dQ^T[db][w] = Gam_t (S0 dO^T) + K^T dPm^T,   y_t = q_t . (inter part of dq_t);
-    //   dK^T[db][w] = Q^T dPm + exp(gamma_C - gamma_s) (dh U^T),   z_s = kh_s . (U dh^T)_s;
-    //   <h_n, dh_n>, each wave summing one block in four.
-    f32x4 dKT[NDH];
-    {
-        Frag<E> fpt[2], fpm[2];
-        fpt[0] = frag_from_acc<E>(dPT[0], dPT[1]);
-        fpt[1] = frag_from_acc<E>(dPT[2], dPT[3]);
-        fpm[0] = frag_from_acc<E>(dP[0], dP[1]);
-        fpm[1] = frag_from_acc<E>(dP[2], dP[3]);
-        const float Gt = __expf(gam_tw), ek = __expf(gC - gam_tw);
-        float qdq = 0.f, kdk = 0.f, hdh = 0.f;
-        Frag<E> fh[KV], fd[KV];
-#pragma unroll
-        for (int kk = 0; kk < KV; ++kk) {
-            fh[kk] = ldfragT(S0, (hf * NDH) * KV + kk, l);
-            fd[kk] = ldfragT(dS1, (hf * NDH) * KV + kk, l);
-        }
-#pragma unroll
-        for (int jd = 0; jd < NDH; ++jd) {
-            const int db = hf * NDH + jd;
-            f32x4 acc = zero4(), accb = zero4();
-#pragma unroll
-            for (int kk = 0; kk < KV; ++kk) {
-                mma(acc, fh[kk], fdo[kk]);
-                mma(accb, fd[kk], fU[kk]);
-            }
-            if ((jd & 3) == w) {
-#pragma unroll
-                for (int kk = 0; kk < KV; ++kk) {
-                    if constexpr (sizeof(E) == 2) {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) hdh += (float)fh[kk].v[i] * (float)fd[kk].v[i];
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) hdh += fh[kk].lo[i] * fd[kk].lo[i] + fh[kk].hi[i] * fd[kk].hi[i];
-                    }
-                }
-            }
-            if (jd + 1 < NDH) {
-#pragma unroll
-                for (int kk = 0; kk < KV; ++kk) {
-                    fh[kk] = ldfragT(S0, (db + 1) * KV + kk, l);
-                    fd[kk] = ldfragT(dS1, (db + 1) * KV + kk, l);
-                }
-            }
-            acc = acc * Gt;
-            const f32x4 qv = ld4(Qs + tw * PK + 16 * db + 4 * g);
-            qdq += qv[0] * acc[0] + qv[1] * acc[1] + qv[2] * acc[2] + qv[3] * acc[3];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fpt[j]);
-            if (tw < nvalid) st4(a.dq + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, acc);
-            f32x4 acck = zero4();
-#pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acck, ldfrag_tr(Qs, PK, 32 * j, 16 * db, l), fpm[j]);
-            const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
-            kdk += kv[0] * accb[0] + kv[1] * accb[1] + kv[2] * accb[2] + kv[3] * accb[3];
-            dKT[jd] = acck + accb * ek;
-        }
-        qdq += __shfl_xor(qdq, 16, 64);
-        qdq += __shfl_xor(qdq, 32, 64);
-        kdk += __shfl_xor(kdk, 16, 64);
-        kdk += __shfl_xor(kdk, 32, 64);
-        if (g == 0) {
-            s_q2[hf][tw] = qdq;
-            s_k2[hf][tw] = kdk * ek;
-        }
-        hdh = wave_sum(hdh);
-        if (l == 0) s_red[w8] = hdh;
-    }
-    __syncthreads();  // phase A done: Qs, dOs, UTs free
-
-    // ---------------- phase B: WY-transform adjoints ------------------------
-    E* dUTs = (E*)(lds + Lay::pB_dUT);
-    E* dWs = (E*)(lds + Lay::pB_dW);
-    E* dTT = (E*)(lds + Lay::pB_dTT);
-    E* Ms = (E*)(lds + Lay::pB_Ms);
-    E* Vs = (E*)(lds + Lay::pB_V);
-    store_untiled<E, DV, BLK, PT, NT>(dux, dUTs);
-    store_rows<E, BLK, DV, PV, NT>(vx, Vs);
-    __syncthreads();
-    // dW^T[db][w] = -(S0 dU^T): rows d, cols t = tw;  stored as dW[t][d]
-    {
-        Frag<E> fdu[KV];
-#pragma unroll
-        for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr(dUTs, PT, 32 * kk, 16 * w, l);
-        Frag<E> fh[KV];
-#pragma unroll
-        for (int kk = 0; kk < KV; ++kk) fh[kk] = ldfragT(S0, (hf * NDH) * KV + kk, l);
-#pragma unroll
-        for (int jd = 0; jd < NDH; ++jd) {
-            const int db = hf * NDH + jd;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(acc, fh[kk], fdu[kk]);
-            if (jd + 1 < NDH) {
-#pragma unroll
-                for (int kk = 0; kk < KV; ++kk) fh[kk] = ldfragT(S0, (db + 1) * KV + kk, l);
-            }
-            st4(dWs + tw * PK + 16 * db + 4 * g, -acc);
-        }
-    }
-    __syncthreads();
-    // dT[w][sb] = beta_s (dU V^T) + beta_s Gam_s (dW K^T): rows t, cols s;  stored as dT^T[s][t]
-    {
-        Frag<E> fdu[KV], fdw[KK];
-#pragma unroll
-        for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr(dUTs, PT, 32 * kk, 16 * w, l);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) fdw[kk] = ldfrag(dWs + (16 * w + r) * PK + 32 * kk + 4 * g);
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            if ((sb & 1) != hf) continue;
-            f32x4 a1 = zero4(), a2 = zero4();
-#pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(a1, fdu[kk], ldfrag(Vs + (16 * sb + r) * PV + 32 * kk + 4 * g));
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) mma(a2, fdw[kk], ldfrag(Ks + (16 * sb + r) * PK + 32 * kk + 4 * g));
-            const int s = 16 * sb + r;
-            const float bs = s_bet[s];
-            const f32x4 dt = a1 * bs + a2 * (bs * __expf(s_gam[s]));
-            st4(dTT + s * PT + 16 * w + 4 * g, dt);
-        }
-    }
-    __syncthreads();
-    // X^T[sb][w] = dT^T T  (rows s, cols r' = tw);  dA[w][cb] = -X T^T (rows r', cols c)
-    {
-        f32x4 XT[4];
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                mma(acc, ldfrag(dTT + (16 * sb + r) * PT + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
-            XT[sb] = acc;
-        }
-        Frag<E> fx[2];
-        fx[0] = frag_from_acc<E>(XT[0], XT[1]);
-        fx[1] = frag_from_acc<E>(XT[2], XT[3]);
-        float gram[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            if ((cb & 1) != hf) continue;
-            f32x4 acc = zero4();
-            if (cb <= w) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) mma(acc, fx[j], ldfrag(Tr + (16 * cb + r) * PT + 32 * j + 4 * g));
-            }
-            const int c = 16 * cb + r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * w + 4 * g + i;
-                const float dA = (c < row) ? -acc[i] : 0.f;
-                gram[i] += dA * KKG[row * AP + c];
-                Eb[row * 65 + c] += dA * s_bet[row] * KKG[row * AP + c];  // gate cross term dA * A
-                const float m = dA * s_bet[row] * __expf(s_gam[row] - s_gam[c]);
-                if (c <= row) Ms[row * PT + c] = from_f<E>(c < row ? m : 0.f);
-                if (c < row) Ms[c * PT + row] = from_f<E>(m);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x = gram[i];
-            x += __shfl_xor(x, 1, 64);
-            x += __shfl_xor(x, 2, 64);
-            x += __shfl_xor(x, 4, 64);
-            x += __shfl_xor(x, 8, 64);
-            if (r == 0) s_g2[hf][16 * w + 4 * g + i] = x;
-        }
-    }
-    __syncthreads();
-    // dV^T[vb][w] = beta_s (dU^T T): rows v, cols s = tw;   dbeta V-term
-    const float bet_tw = s_bet[tw];
-    {
-        float dbv = 0.f;
-#pragma unroll
-        for (int jv = 0; jv < NVH; ++jv) {
-            const int vb = hf * NVH + jv;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                mma(acc, ldfrag(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
-            const f32x4 vv = ld4(Vs + tw * PV + 16 * vb + 4 * g);
-            dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
-            if (tw < nvalid) st4(a.dv + (tok0 + tw) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc * bet_tw);
-        }
-        dbv += __shfl_xor(dbv, 16, 64);
-        dbv += __shfl_xor(dbv, 32, 64);
-        if (g == 0) s_v2[hf][tw] = dbv;
-    }
-    // dK^T += beta_s Gam_s (dW^T T) + K^T Msym ;  dbeta K-term
-    const float Gs = __expf(gam_tw);
-    {
-        float dbk = 0.f;
-#pragma unroll
-        for (int jd = 0; jd < NDH; ++jd) {
-            const int db = hf * NDH + jd;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(dWs, PK, 32 * j, 16 * db, l), ldfrag(TT + tw * PT + 32 * j + 4 * g));
-            f32x4 accm = zero4();
-#pragma unroll
-            for (int j = 0; j < 2; ++j) mma(accm, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), ldfrag(Ms + tw * PT + 32 * j + 4 * g));
-            const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
-            dbk += kv[0] * acc[0] + kv[1] * acc[1] + kv[2] * acc[2] + kv[3] * acc[3];
-            const f32x4 res = dKT[jd] + acc * (bet_tw * Gs) + accm;
-            if (tw < nvalid) st4(a.dk + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, res);
-        }
-        dbk += __shfl_xor(dbk, 16, 64);
-        dbk += __shfl_xor(dbk, 32, 64);
-        if (g == 0) s_b2[hf][tw] = dbk;
-    }
-    __syncthreads();
-    if (tid < BLK) {  // combine the halves (fixed order)
-        const int t = tid;
-        const float Gt = __expf(s_gam[t]);
-        const float dbk = s_b2[0][t] + s_b2[1][t];
-        s_y[t] = (s_q2[0][t] + s_q2[1][t]) + s_bet[t] * Gt * dbk;  // W path: dgamma_t from Gam_t in W
-        s_kdk[t] = s_k2[0][t] + s_k2[1][t];
-        const float dbeta = (s_v2[0][t] + s_v2[1][t]) + Gt * dbk + (s_g2[0][t] + s_g2[1][t]);
-        if (t < nvalid) a.dbeta[(tok0 + t) * H + h] = from_f<E>(dbeta);
-    }
-    // Gate gradient, summing only contributions that cross the token boundary
-    // (exact, and free of the cancellation a suffix sum of per-token terms has):
-    //   dg_u = sum_{t>=u} y_t + sum_{t>=u>s} E[t][s] + sum_{r<u} z_r + Gam_C <h_n, dh_n>
-    // with y_t the S0 -> token-t terms, E the pair terms (dP*P + dA*A) and
-    // z_r = kh_r . (U dh^T)_r the Kh-path terms.
-    // F_u = sum_{t >= u} sum_{s < u} E[t][s]: wave w8 takes rows t = 8 w8 .. 8 w8 + 7,
-    // lane = column u; each row's exclusive prefix over s is a wave scan.
-    {
-        float Fp = 0.f;
-#pragma unroll 4
-        for (int i = 0; i < 8; ++i) {
-            const int t = 8 * w8 + i;
-            const float e = Eb[t * 65 + l];
-            const float ex = wave_prefix_sum(e) - e;
-            if (t >= l) Fp += ex;
-        }
-        Eb[64 * 65 + w8 * 64 + l] = Fp;  // spare rows after E: the eight wave partials
-    }
-    __syncthreads();
-    if (w8 == 0) {
-        const float* Fw = Eb + 64 * 65 + l;
-        const float F = ((Fw[0] + Fw[64]) + (Fw[128] + Fw[192])) + ((Fw[256] + Fw[320]) + (Fw[384] + Fw[448]));
-        // reverse inclusive scan of y: lane l sums y over lanes >= l
-        float x = s_y[l];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            float y = __shfl_down(x, off, 64);
-            if (l + off < 64) x += y;
-        }
-        const float z = s_kdk[l];
-        const float zex = wave_prefix_sum(z) - z;
-        const float hd = ((s_red[0] + s_red[1]) + (s_red[2] + s_red[3])) + ((s_red[4] + s_red[5]) + (s_red[6] + s_red[7]));
-        const float end = __expf(gC) * hd;
-        if (l < nvalid) a.dg[(tok0 + l) * H + h] = from_f<E>(x + F + zex + end);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Host-side launcher
-// ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);

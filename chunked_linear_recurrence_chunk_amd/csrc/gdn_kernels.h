@@ -396,7 +396,7 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[D
 #pragma unroll
         for (int j = 0; j < 2; ++j) st8T(UT, 2 * vb + j, l, U[2 * j], U[2 * j + 1]);
     }
-    if constexpr (PCD) {
+    if (PCD && a.Utok) {
         // U token-major for the output kernel (rows of valid tokens)
         const size_t bh = chunk / a.NC;
         const int n = (int)(chunk % a.NC), bb = (int)(bh / a.H), hh = (int)(bh % a.H);
@@ -453,7 +453,8 @@ template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFw
     static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF;
     static constexpr int NU = NWU + NKU + 2 * UPF + (PCD ? 1 : 0);
     static constexpr int SLOT = RingGeom<NU>::SLOT;
-    static constexpr int TILE = HNAT ? DK * 16 * (int)sizeof(E) : (PCD ? BLK * 16 * (int)sizeof(E) : 16);
+    static constexpr int TILE_H = HNAT ? DK * 16 * (int)sizeof(E) : 16, TILE_U = PCD ? BLK * 16 * (int)sizeof(E) : 16;
+    static constexpr int TILE = TILE_H > TILE_U ? TILE_H : TILE_U;
     static constexpr int PF = (144 * 1024 - TILE) / SLOT;
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
     static constexpr int LDS = P * SLOT + TILE;  // ring, then the state-store tile
