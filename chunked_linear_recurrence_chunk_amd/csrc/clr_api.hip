@@ -75,12 +75,15 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     return w;
 }
 
-// The fp32 KDA forward is instantiated for d <= 64 only.
-bool kda_f32_unsupported(const clr_shape_t* s) { return s->dtype == CLR_F32 && s->dk > 64; }
+// The fp32 KDA forward is instantiated for d <= 64 only, the backward for d = 32.
+bool kda_f32_unsupported(const clr_shape_t* s, bool bwd) {
+    return s->dtype == CLR_F32 && s->dk > (bwd ? 32 : 64);
+}
 
-// KDA forward: the Gated DeltaNet forward layouts the scan reads, exp(b_C)
-// per key channel (padded to 256 floats) and U token-major for the output.
-GdnWs carve_kda(const clr_shape_t* s, char* base, size_t* total) {
+// KDA: the Gated DeltaNet forward layouts the scan reads, exp(b_C) per key
+// channel (padded to 256 floats) and U token-major; the backward adds the
+// reverse-scan operands and the WY adjoints dM, dX.
+GdnWs carve_kda(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     Carver c{base};
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
     GdnWs w{};
@@ -90,6 +93,16 @@ GdnWs carve_kda(const clr_shape_t* s, char* base, size_t* total) {
     w.hT = c.take(nb * dk * dv * es);
     w.eCk = (float*)c.take(nb * 256 * 4);
     w.Utok = c.take((size_t)s->B * s->T * s->H * dv * es);
+    if (bwd) {
+        w.Rt = (float*)c.take(nb * dk * dv * 4);
+        w.WT = c.take(nb * BLK * dk * es);
+        w.Kh = c.take(nb * BLK * dk * es);
+        w.dvlT = c.take(nb * BLK * dv * es);
+        w.dhT = c.take(nb * dk * dv * es);
+        w.dUT = c.take(nb * BLK * dv * es);
+        w.dM = (float*)c.take(nb * BLK * BLK * 4);
+        w.dX = (float*)c.take(nb * BLK * dk * 4);
+    }
     if (total) *total = c.off;
     return w;
 }
@@ -184,10 +197,11 @@ const char* clr_status_string(int s) {
 }
 
 size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
-    if (op == CLR_OP_KDA_FWD) {
-        if (check_shape(s, false, false) != CLR_OK || kda_f32_unsupported(s)) return 0;
+    if (op == CLR_OP_KDA_FWD || op == CLR_OP_KDA_BWD) {
+        const bool bwd = op == CLR_OP_KDA_BWD;
+        if (check_shape(s, false, false) != CLR_OK || kda_f32_unsupported(s, bwd)) return 0;
         size_t total = 0;
-        carve_kda(s, nullptr, &total);
+        carve_kda(s, bwd, nullptr, &total);
         return total;
     }
     if (op < CLR_OP_GDN_FWD || op > CLR_OP_M2_BWD) return 0;
@@ -211,7 +225,7 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
     const bool has_beta = kind == K_GDN || kind == K_KDA;
     int rc = check_shape(s, gla, false);
     if (rc) return rc;
-    if (kind == K_KDA && kda_f32_unsupported(s)) return CLR_ENOTSUP;
+    if (kind == K_KDA && kda_f32_unsupported(s, false)) return CLR_ENOTSUP;
     if (!q || !k || !v || !g) return CLR_EINVAL;
     if (has_beta ? beta == nullptr : beta != nullptr) return CLR_EINVAL;
     const size_t es = esize(s->dtype);
@@ -234,7 +248,7 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
         L.B = s->B; L.T = s->T; L.H = s->H; L.NC = NC; L.dk = s->dk; L.dv = s->dv;
         L.bf16 = s->dtype == CLR_BF16;
         L.q = q; L.k = k; L.v = v; L.g = g; L.beta = beta; L.S_in = S_in; L.o = o; L.S_out = S_out;
-        L.ws = carve_kda(s, (char*)ws, nullptr);
+        L.ws = carve_kda(s, false, (char*)ws, nullptr);
         return hip_status(launch_kda_fwd(L, st));
     }
     if (!gla) {
@@ -283,15 +297,17 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
                       const void* g, const void* beta, const float* S_in, const void* dO,
                       const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
                       float* dS_in, void* ws, size_t ws_bytes, void* stream) {
-    const bool gla = kind != K_GDN;
-    int rc = check_shape(s, gla, true);
+    const bool gla = kind == K_GLA || kind == K_M2;  // GLA kernels and head sizes
+    const bool has_beta = kind == K_GDN || kind == K_KDA;
+    int rc = kind == K_KDA ? check_shape(s, false, false) : check_shape(s, gla, true);
     if (rc) return rc;
+    if (kind == K_KDA && kda_f32_unsupported(s, true)) return CLR_ENOTSUP;
     if (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg || !dS_in) return CLR_EINVAL;
-    if (gla ? (beta != nullptr || dbeta != nullptr) : (beta == nullptr || dbeta == nullptr))
+    if (has_beta ? (beta == nullptr || dbeta == nullptr) : (beta != nullptr || dbeta != nullptr))
         return CLR_EINVAL;
     const size_t es = esize(s->dtype);
     const size_t ntok = (size_t)s->B * s->T * s->H, nst = (size_t)s->B * s->H * s->dk * s->dv;
-    const size_t gn = ntok * (kind == K_GLA ? s->dk : 1) * es;
+    const size_t gn = ntok * ((kind == K_GLA || kind == K_KDA) ? s->dk : 1) * es;
     Buf bufs[] = {{q, ntok * s->dk * es, false},  {k, ntok * s->dk * es, false},
                   {v, ntok * s->dv * es, false},  {g, gn, false},
                   {beta, ntok * es, false},       {S_in, nst * 4, false},
@@ -301,7 +317,7 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
                   {dbeta, ntok * es, true},       {dS_in, nst * 4, true},
                   {ws, ws_bytes, true}};
     if ((rc = check_bufs(bufs, 15))) return rc;
-    const size_t need = clr_workspace_bytes(s, gla ? CLR_OP_GLA_BWD : CLR_OP_GDN_BWD);
+    const size_t need = clr_workspace_bytes(s, kind == K_KDA ? CLR_OP_KDA_BWD : gla ? CLR_OP_GLA_BWD : CLR_OP_GDN_BWD);
     hipStream_t st = (hipStream_t)stream;
     if (s->T == 0) return passthrough(dS_out, dS_in, nst, st);
     if (!ws || ws_bytes < need || ((uintptr_t)ws & (ALIGN - 1))) return CLR_EWORKSPACE;
@@ -313,6 +329,10 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
         L.q = q; L.k = k; L.v = v; L.g = g; L.beta = beta; L.S_in = S_in;
         L.dO = dO; L.dS_out = dS_out; L.dq = dq; L.dk_ = dk; L.dv_ = dv; L.dg = dg; L.dbeta = dbeta;
         L.dS_in = dS_in;
+        if (kind == K_KDA) {
+            L.ws = carve_kda(s, true, (char*)ws, nullptr);
+            return hip_status(launch_kda_bwd(L, st));
+        }
         L.ws = carve_gdn(s, true, (char*)ws, nullptr);
         return hip_status(launch_gdn_bwd(L, st));
     } else {
@@ -332,6 +352,14 @@ int gdn_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v, c
             void* dk, void* dv, void* dg, void* dbeta, float* dS_in, void* ws, size_t ws_bytes,
             void* stream) {
     return bwd_common(K_GDN, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
+                      ws_bytes, stream);
+}
+
+int kda_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+            const void* beta, const float* S_in, const void* dO, const float* dS_out, void* dq,
+            void* dk, void* dv, void* dg, void* dbeta, float* dS_in, void* ws, size_t ws_bytes,
+            void* stream) {
+    return bwd_common(K_KDA, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
                       ws_bytes, stream);
 }
 

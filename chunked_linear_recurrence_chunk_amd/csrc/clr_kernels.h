@@ -41,6 +41,9 @@ struct GdnWs {
     void* dvlT;   // [.., dv, 64]   dvloc^T, dvloc = (Q K^T * G * tril)^T dO
     void* dhT;    // [.., dv, dk]   gradient w.r.t. the state leaving the block, transposed
     void* dUT;    // [.., dv, 64]   dU^T
+    // KDA backward only
+    float* dM;    // [.., 64, 64]   Diag(beta) dA, the adjoint of the decayed Gram product (fp32)
+    float* dX;    // [.., 64, dk]   T^T dW (fp32)
 };
 
 struct GdnLaunch {
@@ -93,6 +96,7 @@ template <typename E> struct GdnOutArgs {
 hipError_t launch_gdn_fwd(const GdnLaunch& L, hipStream_t st);
 // KDA forward (g per key channel); kernels in gla.hip.
 hipError_t launch_kda_fwd(const GdnLaunch& L, hipStream_t st);
+hipError_t launch_kda_bwd(const GdnLaunch& L, hipStream_t st);
 hipError_t launch_gdn_bwd(const GdnLaunch& L, hipStream_t st);
 
 // ---------------------------------------------------------------------------

@@ -42,43 +42,6 @@ hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
     return hipGetLastError();
 }
 
-// KDA forward: prep here, the delta-rule scan with a per-channel decay, and
-// the GLA output kernel with U (token-major) in place of V:
-// O = (Q * e^b) S0 + (P * tril) U is the GLA output form.
-template <typename E, int DK, int DV>
-hipError_t launch_kda_fwd_t(const GdnLaunch& L, hipStream_t st) {
-    const dim3 gblk(L.NC, L.H, L.B);
-    const GdnWs& ws = L.ws;
-    KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
-                      ws.eCk, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
-    launch("kda_prep", kda_prep_kernel<E, DK, DV>, gblk, dim3(256), st, pa);
-    GdnScanArgs<E> sa{nullptr, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, L.S_out,
-                      (E*)ws.hT, nullptr, L.H, L.NC, L.B * L.H};
-    sa.eC = ws.eCk;
-    sa.Utok = (E*)ws.Utok;
-    sa.T = L.T;
-    launch("kda_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, true>, dim3(scan_grid(DV / 16, L.B * L.H)),
-           dim3(256), st, sa);
-    if (L.o) {
-        GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)ws.Utok, (const E*)L.g, (const E*)ws.hT,
-                         (E*)L.o, L.T, L.H, L.NC};
-        launch("kda_out", gla_out_kernel<E, DK, DV, false>, gblk, dim3(512), st, oa);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_kda_fwd(const GdnLaunch& L, hipStream_t st) {
-#define CLR_CASE(E, DK, DV) \
-    if (L.dk == DK && L.dv == DV) return launch_kda_fwd_t<E, DK, DV>(L, st);
-    if (L.bf16) {
-        CLR_FOR_GDN_SHAPES(bf16)
-    } else {
-        CLR_FOR_KDA_SHAPES_F32(float)
-    }
-#undef CLR_CASE
-    return hipErrorInvalidValue;
-}
-
 hipError_t launch_gla_fwd(const GlaLaunch& L, hipStream_t st) {
 #define CLR_CASE(E, DK, DV) \
     if (L.dk == DK && L.dv == DV) \

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libclr.so")
 
 CLR_OK, CLR_EINVAL, CLR_ENOTSUP, CLR_EWORKSPACE, CLR_EHIP = range(5)
 CLR_F32, CLR_BF16 = 0, 1
-OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD, OP_M2_FWD, OP_M2_BWD, OP_KDA_FWD = range(7)
+OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD, OP_M2_FWD, OP_M2_BWD, OP_KDA_FWD, OP_KDA_BWD = range(8)
 
 
 class ClrShape(ctypes.Structure):
@@ -61,7 +61,7 @@ def load(path: Optional[str] = None):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 9 + [sz, vp]
         f.restype = i
-    for name in ("gdn_bwd", "gla_bwd", "mamba2_bwd"):
+    for name in ("gdn_bwd", "gla_bwd", "mamba2_bwd", "kda_bwd"):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 15 + [sz, vp]
         f.restype = i
@@ -250,6 +250,11 @@ def kda_fwd(q, k, v, g, beta, S_in=None, want_state=True, ws=None, o=None, S_out
     """KDA chunk forward (per-key-channel gate g [B,T,H,dk], beta [B,T,H]).
     Returns (o, S_out)."""
     return _fwd("kda_fwd", OP_KDA_FWD, q, k, v, g, beta, S_in, want_state, ws, o, S_out)
+
+
+def kda_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, ws=None, out=None):
+    """KDA chunk backward.  Returns dict dq, dk, dv, dg, dbeta, dS_in."""
+    return _bwd("kda_bwd", OP_KDA_BWD, q, k, v, g, beta, S_in, dO, dS_out, ws, out)
 
 
 def mamba2_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None):

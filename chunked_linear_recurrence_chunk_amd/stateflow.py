@@ -34,6 +34,7 @@ class GdnChunked:
     """Forward/backward of one Gated DeltaNet layer over N sequence chunks."""
 
     kind = "gdn"
+    _names = ("gdn_fwd", "gdn_bwd", "OP_GDN_FWD", "OP_GDN_BWD")
 
     def __init__(self, q, k, v, g, beta, N: int):
         from . import ops
@@ -45,8 +46,10 @@ class GdnChunked:
         B, _, H, dk = q.shape
         dv = v.shape[-1]
         import torch
+        fwd, bwd, op_f, op_b = self._names
+        self._fwd, self._bwd = getattr(ops, fwd), getattr(ops, bwd)
         shape = ops.ClrShape(B, L, H, dk, dv, ops._dtype_code(q))
-        nbytes = max(ops.workspace_bytes(shape, ops.OP_GDN_FWD), ops.workspace_bytes(shape, ops.OP_GDN_BWD))
+        nbytes = max(ops.workspace_bytes(shape, getattr(ops, op_f)), ops.workspace_bytes(shape, getattr(ops, op_b)))
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         self.saved = [None] * N
 
@@ -66,7 +69,7 @@ class GdnChunked:
             a, b = self.bounds[i]
             self.saved[i] = S
             view = o[:, a:b]
-            oi, S = self.ops.gdn_fwd(*self._chunk(i), S, ws=self.ws, o=view if view.is_contiguous() else None)
+            oi, S = self._fwd(*self._chunk(i), S, ws=self.ws, o=view if view.is_contiguous() else None)
             if oi.data_ptr() != view.data_ptr():
                 view.copy_(oi)
         return o, S
@@ -83,7 +86,7 @@ class GdnChunked:
             a, b = self.bounds[i]
             views = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg", "dbeta")}
             out = {key: t for key, t in views.items() if t.is_contiguous()}
-            r = self.ops.gdn_bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
+            r = self._bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
             for key, t in views.items():
                 if r[key].data_ptr() != t.data_ptr():
                     t.copy_(r[key])
@@ -230,36 +233,9 @@ class ShortConvChunked:
         return dict(dx=dx, dw=grads["dw"], dbias=grads["dbias"], dstate_in=ds)
 
 
-class KdaForwardChunked:
-    """Forward of one KDA layer (per-key-channel decay with the delta rule)
-    over N sequence chunks, handing S_out -> S_in.  The library has no KDA
-    backward."""
+class KdaChunked(GdnChunked):
+    """Forward/backward of one KDA layer (per-key-channel decay with the delta
+    rule) over N sequence chunks; g is [B, T, H, dk]."""
 
     kind = "kda"
-
-    def __init__(self, q, k, v, g, beta, N: int):
-        from . import ops
-        self.ops = ops
-        self.q, self.k, self.v, self.g, self.beta = q, k, v, g, beta
-        self.N = N
-        self.bounds = _bounds(q.shape[1], N)
-        L = self.bounds[0][1]
-        B, _, H, dk = q.shape
-        import torch
-        shape = ops.ClrShape(B, L, H, dk, v.shape[-1], ops._dtype_code(q))
-        self.ws = torch.empty(max(ops.workspace_bytes(shape, ops.OP_KDA_FWD), 256), dtype=torch.uint8, device=q.device)
-
-    def forward(self, S_in=None, o=None):
-        import torch
-        B, T, H, dk = self.q.shape
-        if o is None:
-            o = torch.empty((B, T, H, self.v.shape[-1]), dtype=self.q.dtype, device=self.q.device)
-        S = S_in
-        for i in range(self.N):
-            a, b = self.bounds[i]
-            view = o[:, a:b]
-            args = tuple(_sl(t, a, b) for t in (self.q, self.k, self.v, self.g, self.beta))
-            oi, S = self.ops.kda_fwd(*args, S, ws=self.ws, o=view if view.is_contiguous() else None)
-            if oi.data_ptr() != view.data_ptr():
-                view.copy_(oi)
-        return o, S
+    _names = ("kda_fwd", "kda_bwd", "OP_KDA_FWD", "OP_KDA_BWD")

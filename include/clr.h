@@ -92,7 +92,8 @@ typedef enum {
     CLR_OP_GLA_BWD = 3,
     CLR_OP_M2_FWD = 4,
     CLR_OP_M2_BWD = 5,
-    CLR_OP_KDA_FWD = 6
+    CLR_OP_KDA_FWD = 6,
+    CLR_OP_KDA_BWD = 7
 } clr_op_t;
 
 typedef struct {
@@ -149,15 +150,21 @@ int mamba2_bwd(const clr_shape_t* shape, const void* q, const void* k, const voi
  * diagonal-plus-low-rank), key-major:
  *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
  *     o_t = S_t^T q_t,   alpha_t = exp(g_t) in R^dk (per key channel).
- * Forward only.  Same arguments as gdn_fwd except g, which is [B, T, H, dk]
- * as for GLA; beta is required.  Head sizes as for GDN (fp32: d <= 64,
- * CLR_ENOTSUP otherwise).  Workspace:
- * CLR_OP_KDA_FWD.  The per-block decays use 16-token sub-tiles with the same
- * e^80 bound as the GLA path (exact while the decay within half a tile stays
- * within 80 nats per channel). */
+ * Same arguments as gdn_fwd / gdn_bwd except g and dg, which are
+ * [B, T, H, dk] as for GLA; beta and dbeta are required.  Head sizes as for
+ * GDN (fp32: forward d <= 64, backward d = 32; CLR_ENOTSUP otherwise).
+ * Workspace: CLR_OP_KDA_FWD / CLR_OP_KDA_BWD.  The backward recomputes the
+ * forward from S_in (as gdn_bwd does); dS_out may be NULL (zero).  The
+ * per-block decays use 16-token sub-tiles with the same e^80 bound as the GLA
+ * path (exact while the decay within half a tile stays within 80 nats per
+ * channel). */
 int kda_fwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
             const void* g, const void* beta, const float* S_in, void* o, float* S_out,
             void* ws, size_t ws_bytes, void* stream);
+int kda_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+            const void* g, const void* beta, const float* S_in, const void* dO,
+            const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+            float* dS_in, void* ws, size_t ws_bytes, void* stream);
 
 /* Causal short convolution with a boundary state.
  * The StateFlow paper (Sec. 1 and Sec. 3.3) hands the boundary state of a

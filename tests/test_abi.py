@@ -129,6 +129,13 @@ def test_bwd_validation():
     # fp32 backward at d = 64 is not supported
     s64 = _shape(ops, T=64, H=1, dk=64, dv=64, dtype=0)
     assert lib.gdn_bwd(ctypes.byref(s64), *ptrs, 1 << 40, None) == ops.CLR_ENOTSUP
+    assert lib.kda_bwd(ctypes.byref(s64), *ptrs, 1 << 40, None) == ops.CLR_ENOTSUP
+    # KDA needs beta and dbeta; its workspace is larger than the forward's
+    bad = list(ptrs)
+    bad[4] = None
+    assert lib.kda_bwd(ctypes.byref(s), *bad, 1 << 40, None) == ops.CLR_EINVAL
+    assert ops.workspace_bytes(s, ops.OP_KDA_BWD) > ops.workspace_bytes(s, ops.OP_KDA_FWD) > 0
+    assert ops.workspace_bytes(s64, ops.OP_KDA_BWD) == 0 and ops.workspace_bytes(s64, ops.OP_KDA_FWD) > 0
 
 
 def test_mamba2_and_shortconv_validation():

@@ -4,7 +4,7 @@ times (the sequence-chunk driver):
   * the oracle recomputes whole sampled heads (every head is an independent
     recurrence, so a head slice of the inputs is an exact sub-problem);
   * identities that hold for the exact layer at any size are checked on every
-    head of the GPU result (q.dq = o.do per token; GDN k.dk + v.dv = 2 beta dbeta;
+    head of the GPU result (q.dq = o.do per token; GDN and KDA k.dk + v.dv = 2 beta dbeta;
     GLA and Mamba-2 k.dk = v.dv; joint linearity sum v.dv + <S_in, dS_in> =
     sum o.do + <S_out, dS_out>; Mamba-2 dg as a suffix sum of q.dq - k.dk);
   * the chunked run equals the unchunked run bit for bit.
@@ -24,11 +24,13 @@ def _run(cfg, x, N):
     import torch
     from chunked_linear_recurrence_chunk_amd import stateflow
     dt = cfg["dtype"]
-    keys = ("q", "k", "v", "g", "beta", "dO") if cfg["kind"] == "gdn" else ("q", "k", "v", "g", "dO")
+    delta = cfg["kind"] in ("gdn", "kda")
+    keys = ("q", "k", "v", "g", "beta", "dO") if delta else ("q", "k", "v", "g", "dO")
     d = {k: to_dev(x[k], dt) for k in keys}
     S_in, dS_out = to_dev(x["S_in"], "fp32"), to_dev(x["dS_out"], "fp32")
-    if cfg["kind"] == "gdn":
-        drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
+    if delta:
+        cls = stateflow.GdnChunked if cfg["kind"] == "gdn" else stateflow.KdaChunked
+        drv = cls(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
     elif cfg["kind"] == "gla":
         drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
     else:
@@ -50,9 +52,10 @@ def _oracle_heads(cfg, x, pairs):
         sl = {k: (v[b:b + 1, :, h:h + 1] if v.ndim >= 3 and k not in ("S_in", "dS_out") else v[b:b + 1, h:h + 1])
               for k, v in x.items()}
         sl = {k: np.ascontiguousarray(v, dtype=np.float64) for k, v in sl.items()}
-        if cfg["kind"] == "gdn":
-            o, S = oracle.gdn_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"])
-            r = oracle.gdn_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], sl["dS_out"])
+        if cfg["kind"] in ("gdn", "kda"):
+            fwd, bwd = (oracle.gdn_fwd, oracle.gdn_bwd) if cfg["kind"] == "gdn" else (oracle.kda_fwd, oracle.kda_bwd)
+            o, S = fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"])
+            r = bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], sl["dS_out"])
         else:
             fwd, bwd = (oracle.gla_fwd, oracle.gla_bwd) if cfg["kind"] == "gla" else (oracle.mamba2_fwd, oracle.mamba2_bwd)
             o, S = fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"])
@@ -81,7 +84,8 @@ def _check_identities(cfg, x, got):
     odo = np.sum(f["o"] * dO, -1)
     assert rel_err(qdq, odo) < 3e-2, rel_err(qdq, odo)
     kdk, vdv = np.sum(k * f["dk"], -1), np.sum(v * f["dv"], -1)
-    if cfg["kind"] == "gdn":
+    if cfg["kind"] in ("gdn", "kda"):
+        # (k, v, beta) -> (c k, c v, beta / c^2) leaves the layer unchanged
         e = rel_err(kdk + vdv, 2 * x["beta"] * f["dbeta"])
     else:
         e = rel_err(kdk, vdv)
@@ -128,6 +132,10 @@ def _full(name, pairs, compare_unchunked):
 
 def test_full_gdn_H16_T8192():
     _full("gdn_bf16_H16_T8192_d128", [(0, 0), (0, 9)], True)
+
+
+def test_full_kda_H16_T8192():
+    _full("kda_bf16_H16_T8192_d128", [(0, 0), (0, 11)], True)
 
 
 def test_full_gla_B4_H16_T4096():

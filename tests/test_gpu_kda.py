@@ -1,7 +1,6 @@
-"""GPU parity of the KDA forward (per-key-channel decay with the delta rule,
-kda_fwd) against the fp64 oracle, through the C ABI; sequence-chunk
-exactness; the full workload on sampled heads."""
-import numpy as np
+"""GPU parity of the KDA forward and backward (per-key-channel decay with
+the delta rule, kda_fwd / kda_bwd) against the fp64 oracle, through the C
+ABI, and sequence-chunk exactness (the full workload: test_gpu_fullsize)."""
 import pytest
 
 from tests.conftest import gpu_available
@@ -46,34 +45,48 @@ def test_kda_fwd_matches_oracle(case):
     assert eo < tol(dtype, "o") and es < tol(dtype, "S_out"), (eo, es)
 
 
-def test_kda_fwd_chunked_equals_unchunked():
+def test_kda_chunked_equals_unchunked():
     import torch
     from chunked_linear_recurrence_chunk_amd import inputs, stateflow
     x = inputs.make_kda(1, 1024, 2, 128, 128, "bf16", 78)
     d, S_in = _dev(x, "bf16")
+    dO, dS_out = to_dev(x["dO"], "bf16"), to_dev(x["dS_out"], "fp32")
     res = []
     for N in (1, 4):
-        drv = stateflow.KdaForwardChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
+        drv = stateflow.KdaChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
         o, S = drv.forward(S_in)
+        gr = drv.backward(dO, dS_out)
         torch.cuda.synchronize()
-        res.append((o, S))
-    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+        res.append(dict(o=o, S_out=S, **gr))
+    for key in res[0]:
+        assert torch.equal(res[0][key], res[1][key]), key
 
 
-def test_kda_fwd_full_workload_sampled_heads():
+BWD_CASES = [
+    (1, 256, 1, 32, 32, "fp32", 81, 1 / 16),
+    (2, 200, 2, 32, 32, "fp32", 82, 1.0),        # ragged tail, strong gates
+    (1, 192, 2, 32, 32, "bf16", 83, 1 / 16),
+    (2, 320, 2, 64, 64, "bf16", 84, 1 / 16),
+    (1, 512, 2, 128, 128, "bf16", 85, 1 / 16),
+    (1, 100, 3, 128, 128, "bf16", 86, 1 / 16),   # ragged, < 2 blocks
+    (1, 256, 2, 128, 128, "bf16", 87, 1.0),      # strong gates
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[_ids(c) for c in BWD_CASES])
+def test_kda_bwd_matches_oracle(case):
     import torch
-    from chunked_linear_recurrence_chunk_amd import inputs, stateflow
+    from chunked_linear_recurrence_chunk_amd import inputs, ops
     from oracle import oracle
-    cfg = inputs.CONFIGS["kda_bf16_H16_T8192_d128"]
-    x = inputs.make(cfg, seed=100)
-    d, S_in = _dev(x, "bf16")
-    drv = stateflow.KdaForwardChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], cfg["N"])
-    o, S = drv.forward(S_in)
+    B, T, H, dk, dv, dtype, seed, gs = case
+    print(f"[kda bwd] case {case}", flush=True)
+    x = inputs.make_kda(B, T, H, dk, dv, dtype, seed, gate_scale=gs)
+    d, S_in = _dev(x, dtype)
+    dO, dS_out = to_dev(x["dO"], dtype), to_dev(x["dS_out"], "fp32")
+    gr = ops.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S_in, dO, dS_out)
     torch.cuda.synchronize()
-    for h in (0, 11):
-        sl = {k: np.ascontiguousarray(x[k][:, :, h:h + 1]) for k in ("q", "k", "v", "g", "beta")}
-        o_ref, S_ref = oracle.kda_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], x["S_in"][:, h:h + 1])
-        eo = rel_err(to_np(o[:, :, h:h + 1]), o_ref)
-        es = rel_err(to_np(S[:, h:h + 1]), S_ref)
-        print(f"   head {h}: o {eo:.2e} S_out {es:.2e}", flush=True)
-        assert eo < tol("bf16", "o") and es < tol("bf16", "S_out"), (h, eo, es)
+    ref = oracle.kda_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S_in"], x["dO"], x["dS_out"])
+    errs = {k: rel_err(to_np(gr[k]), ref[k]) for k in ref}
+    print("  errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, e in errs.items():
+        assert e < tol(dtype, k), (k, e)
