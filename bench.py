@@ -68,6 +68,22 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
                                  2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv)
         W[pre + "_scan_fwd_rec"] = W[pre + "_scan_fwd"]
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
+    # KDA (per-channel gate, dk == dv): the Gated DeltaNet data flow with
+    # per-channel decays (exp(b_C) per channel in place of the per-token
+    # gate), U token-major, and the WY adjoints dM, dX handed to the GLA intra
+    # kernel in fp32
+    W["kda_prep"] = (2 * Ck * es + Cv * es + C * es + dk * f4 + 2 * Ck * es + Cv * es,
+                     2 * CC * dk + 2 * CC * dk + 2 * CC * dv + C ** 3 // 3)
+    W["kda_prep2"] = (5 * Ck * es + 3 * Ck * es + kv * f4, 2 * CC * dk + 2 * CC * dv + 2 * (2 * C * kv))
+    W["kda_scan_fwd"] = (dk * f4 + 3 * Ck * es + kv * es + Cv * es, 2 * (2 * C * kv))
+    W["kda_out"] = W["gla_out"]
+    kda_scan_bwd = (dk * f4 + 2 * Ck * es + kv * f4 + Cv * es + kv * es + Cv * es, 2 * (2 * C * kv))
+    W["kda_scan_pair"] = tuple(x + y for x, y in zip(W["kda_scan_fwd"], kda_scan_bwd))
+    W["kda_bwd_wy"] = (2 * Ck * es + Cv * es + C * es + kv * es + Cv * es + Cv * es + C * es + CC * f4 + Ck * f4,
+                       2 * CC * dk + C ** 3 // 3 + 2 * C * kv + 2 * CC * dv + 2 * CC * dk + 2 * (2 * C ** 3)
+                       + 2 * CC * dv + 2 * CC * dk)
+    W["kda_bwd_intra"] = (5 * Ck * es + 2 * kv * es + CC * f4 + Ck * f4 + C * es + 3 * Ck * es,
+                          2 * (2 * CC * dv) + 2 * (2 * C * kv) + 4 * (2 * CC * dk))
     # one launch running the forward recompute and the reverse scan side by side
     W["gdn_scan_pair"] = tuple(x + y for x, y in zip(W["gdn_scan_fwd"], W["gdn_scan_bwd"]))
     return W.get(name)
@@ -154,6 +170,8 @@ def cpu_baseline(cfg: dict, x: dict, budget_chunks: int):
                                      sl["dy"][:, i * L:(i + 1) * L], ds, cfg["act"])["dstate_in"]
         elif cfg["kind"] == "gdn":
             oracle.gdn_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], None, n)
+        elif cfg["kind"] == "kda":
+            oracle.kda_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["S_in"], sl["dO"], None, n)
         elif cfg["kind"] == "gla":
             oracle.gla_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], None, n)
         else:
@@ -227,18 +245,20 @@ def main():
             drv.backward(d["dy"], None)
     else:
         H, dv = cfg["H"], cfg["dv"]
-        keys = ("q", "k", "v", "g", "beta", "dO") if cfg["kind"] == "gdn" else ("q", "k", "v", "g", "dO")
+        delta = cfg["kind"] in ("gdn", "kda")
+        keys = ("q", "k", "v", "g", "beta", "dO") if delta else ("q", "k", "v", "g", "dO")
         d = {k: dev(x[k], dtype) for k in keys}
         S_in = dev(x["S_in"], "fp32")
-        if cfg["kind"] == "gdn":
-            drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
+        if delta:
+            cls = stateflow.GdnChunked if cfg["kind"] == "gdn" else stateflow.KdaChunked
+            drv = cls(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
         elif cfg["kind"] == "gla":
             drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
         else:
             drv = stateflow.Mamba2Chunked(d["q"], d["k"], d["v"], d["g"], N)
         o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device="cuda")
         grads = {k: torch.empty_like(d[k.replace("d", "", 1)] if k != "dbeta" else d["beta"])
-                 for k in (("dq", "dk", "dv", "dg", "dbeta") if cfg["kind"] == "gdn" else ("dq", "dk", "dv", "dg"))}
+                 for k in (("dq", "dk", "dv", "dg", "dbeta") if delta else ("dq", "dk", "dv", "dg"))}
 
         def step():
             drv.forward(S_in, o=o)

@@ -37,7 +37,7 @@ CONFIGS = {
     "gdn_bf16_H16_T262144_d128": dict(kind="gdn", dtype="bf16", B=1, H=16, T=262144, dk=128, dv=128, N=64),
     # short convolution in front of the Gated DeltaNet workload (q, k, v channels)
     "shortconv_bf16_T8192_C6144_W4": dict(kind="shortconv", dtype="bf16", B=1, T=8192, C=6144, W=4, act=1, N=4),
-    # per-channel-decay delta rule at the Gated DeltaNet workload's shape (forward)
+    # per-channel-decay delta rule at the Gated DeltaNet workload's shape
     "kda_bf16_H16_T8192_d128": dict(kind="kda", dtype="bf16", B=1, H=16, T=8192, dk=128, dv=128, N=4),
     # scalar-gate member at the GLA workload's shape
     "mamba2_bf16_B4_H16_T4096_dk128_dv256": dict(kind="mamba2", dtype="bf16", B=4, H=16, T=4096, dk=128, dv=256, N=1),

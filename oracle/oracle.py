@@ -364,3 +364,29 @@ def mamba2_chunked(q, k, v, g, S_in, dO, dS_out, N, lib=None):
              for key in ("dq", "dk", "dv", "dg")}
     grads["dS_in"] = dS
     return np.concatenate(outs, axis=1), S_out, grads
+
+
+def kda_chunked(q, k, v, g, beta, S_in, dO, dS_out, N, lib=None):
+    """KDA over N sequence chunks: forward in order, backward in reverse,
+    with the boundary state and its gradient handed over (as gdn_chunked)."""
+    B, T, H, dk, dv = _dims(q, v)
+    bounds = _split_bounds(T, N)
+    S = S_in
+    states, outs = [], []
+    for a, b in bounds:
+        states.append(S)
+        o_i, S = kda_fwd(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b], beta[:, a:b], S, lib=lib)
+        outs.append(o_i)
+    S_out = S
+    dS = dS_out
+    parts = [None] * N
+    for i in reversed(range(N)):
+        a, b = bounds[i]
+        r = kda_bwd(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b], beta[:, a:b], states[i],
+                    dO[:, a:b], dS, lib=lib)
+        parts[i] = r
+        dS = r["dS_in"]
+    grads = {key: np.concatenate([p[key] for p in parts], axis=1)
+             for key in ("dq", "dk", "dv", "dg", "dbeta")}
+    grads["dS_in"] = dS
+    return np.concatenate(outs, axis=1), S_out, grads
