@@ -998,16 +998,83 @@ template <typename E> struct KdaPrepArgs {
     E *W, *KhT, *UtT;
 };
 
+// dst[t][d] = src[t][d] e^{b_t[d]} over a 64 x DK tile (row pitch PX, b row
+// pitch PB), 16-byte vectors, all NT threads.
+template <typename E, int DK, int PX, int PB, int NT>
+__device__ __forceinline__ void scale_exp_rows(const E* src, const float* Bs, E* dst) {
+    constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = DK / VEC, UNITS = BLK * PER_ROW;
+#pragma unroll
+    for (int j = 0; j < (UNITS + NT - 1) / NT; ++j) {
+        const int u = (int)threadIdx.x + NT * j;
+        if (UNITS % NT == 0 || u < UNITS) {
+            const int t = u / PER_ROW, c = (u % PER_ROW) * VEC;
+            union {
+                uint4 u;
+                E e[VEC];
+            } x;
+            x.u = *(const uint4*)(src + t * PX + c);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) x.e[i] = from_f<E>(to_f(x.e[i]) * __expf(Bs[t * PB + c + i]));
+            *(uint4*)(dst + t * PX + c) = x.u;
+        }
+    }
+}
+
+// Block row w of the per-channel decayed Gram product of K,
+//   M[t][s] = sum_d k_t[d] k_s[d] e^{b_t[d] - b_s[d]}   (s < t),
+// column blocks j <= w with (j & 1) == half when halves split them (all j
+// when half < 0).  Each 16 x 16 tile is one dense product of rescaled rows
+// against a reference row of b between the tiles: the boundary before tile w
+// off the diagonal (both factors <= 1), the middle of tile w on it.
+// emit(row, col, value) receives every element of the visited tiles (0 on
+// and above the diagonal).
+template <typename E, int DK, int PK, int PB, typename F>
+__device__ __forceinline__ void kda_gram_row(const E* Ks, const float* Bs, const float* zrow, int w, int half,
+                                             F&& emit) {
+    constexpr int KK = DK / 32;
+    const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+    const int tl = 16 * w + r;
+    const float* refO = w > 0 ? Bs + (16 * w - 1) * PB : zrow;
+    const float* refD = Bs + (16 * w + 7) * PB;
+    Frag<E> fo[KK], fd[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        fo[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, Bs + tl * PB, refO, 1.f);
+        fd[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, Bs + tl * PB, refD, 1.f);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (half >= 0 && (j & 1) != half) continue;
+        f32x4 acc = zero4();
+        if (j <= w) {
+            const int s = 16 * j + r;
+            const float* ref = j < w ? refO : refD;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                mma(acc, j < w ? fo[kk] : fd[kk], frag_row_decay(Ks, PK, s, 32 * kk, Bs + s * PB, ref, -1.f));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * j + r;
+            emit(row, col, col < row ? acc[i] : 0.f);
+        }
+    }
+}
+
+// KDA prep: one work-group (8 waves) per (block, head, batch).  Wave w8: row
+// block w = w8 & 3, half hf = w8 >> 2 (the halves split the Gram's column
+// blocks and the output tiles).
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void kda_prep_kernel(KdaPrepArgs<E> a) {
+__global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
+    constexpr int NT = 512;
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, w8 = tid >> 6, w = w8 & 3, hf = w8 >> 2, l = tid & 63, r = l & 15, g = l >> 4;
     const int T = a.T, H = a.H, NC = a.NC;
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
     const size_t chunk = ((size_t)b * H + h) * NC + n;
     const int nvalid = min(BLK, T - n * BLK);
     const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
-    constexpr int PK = RP<E, DK>, PV = RP<E, DV>, PB = DK + 4, ND = DK / 16, KK = DK / 32;
+    constexpr int PK = RP<E, DK>, PV = RP<E, DV>, PB = DK + 4, ND = DK / 16;
 
     __shared__ __align__(16) E Ks[BLK * PK], Kd[BLK * PK], Vs[BLK * PV], T1[BLK * PT];
     __shared__ __align__(16) float Bs[BLK * PB];
@@ -1016,71 +1083,44 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaPrepArgs<E> a) {
     __shared__ float seg[256], s_bet[BLK];
 
     {
-        const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        const auto vx = load_rows<E, BLK, DV>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
-        const auto gx = load_gate<false, E, DK>(a.g, tok0, h, H, nvalid);
+        const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
+        const auto gx = load_gate<false, E, DK, NT>(a.g, tok0, h, H, nvalid);
         if (tid < BLK) s_bet[tid] = tid < nvalid ? to_f(a.beta[(tok0 + tid) * H + h]) : 0.f;
         if (tid < DK) zrow[tid] = 0.f;
-        store_rows<E, BLK, DK, PK>(kx, Ks);
-        store_rows<E, BLK, DV, PV>(vx, Vs);
-        store_rows<E, BLK, DK, PK>(gx, Kd);  // g staged where K * e^b goes
+        store_rows<E, BLK, DK, PK, NT>(kx, Ks);
+        store_rows<E, BLK, DV, PV, NT>(vx, Vs);
+        store_rows<E, BLK, DK, PK, NT>(gx, Kd);  // g staged where K * e^b goes
         __syncthreads();
         gate_cumsum<E, DK, PK, PB>(Kd, Bs, seg, nvalid);
         __syncthreads();
     }
     // K * e^b (factors <= 1), and exp(b_C) per channel
     const float* bC = Bs + (BLK - 1) * PB;
-    for (int idx = tid; idx < BLK * DK; idx += 256) {
-        const int t = idx / DK, d = idx % DK;
-        Kd[t * PK + d] = from_f<E>(to_f(Ks[t * PK + d]) * __expf(Bs[t * PB + d]));
-    }
-    a.eC[chunk * 256 + tid] = tid < DK ? __expf(bC[tid]) : 0.f;
-
-    // Gram block row w: Am[t][s] = beta_t M[t][s] (s < t); column block j <= w
-    {
-        const int tl = 16 * w + r;
-        const float* refO = w > 0 ? Bs + (16 * w - 1) * PB : zrow;  // boundary before tile w
-        const float* refD = Bs + (16 * w + 7) * PB;                 // middle of tile w
-        Frag<E> fo[KK], fd[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            fo[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, Bs + tl * PB, refO, 1.f);
-            fd[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, Bs + tl * PB, refD, 1.f);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f32x4 acc = zero4();
-            if (j <= w) {
-                const int s = 16 * j + r;
-                const float* ref = j < w ? refO : refD;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    mma(acc, j < w ? fo[kk] : fd[kk], frag_row_decay(Ks, PK, s, 32 * kk, Bs + s * PB, ref, -1.f));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * w + 4 * g + i, col = 16 * j + r;
-                Am[row * AP + col] = col < row ? s_bet[row] * acc[i] : 0.f;
-            }
-        }
-    }
+    scale_exp_rows<E, DK, PK, PB, NT>(Ks, Bs, Kd);
+    if (tid < 256) a.eC[chunk * 256 + tid] = tid < DK ? __expf(bC[tid]) : 0.f;
+    // Am[t][s] = beta_t M[t][s] (s < t)
+    kda_gram_row<E, DK, PK, PB>(Ks, Bs, zrow, w, hf,
+                                [&](int row, int col, float m) { Am[row * AP + col] = s_bet[row] * m; });
     __syncthreads();
-    {
+    if (hf == 0) {
         // T = (I + A)^-1, wave w holds column block w; T1 = T Diag(beta)
         f32x4 tc[4];
-        tri_inverse_cols(Am, Td, tc);
+        tri_inverse_cols(Am, Td, tc);  // one barrier inside
         const int s = 16 * w + r;
         const float bs = s_bet[s];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) T1[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii] * bs);
+    } else {
+        __syncthreads();  // matches the barrier inside tri_inverse_cols
     }
     __syncthreads();
     // W^T[d][t] = sum_s (K * e^b)^T[d][s] T1[t][s]  -> stored as W[t][d] (tiled)
     E* Wout = a.W + chunk * BLK * DK;
 #pragma unroll
-    for (int tile = w; tile < ND * 4; tile += 4) {
+    for (int tile = w8; tile < ND * 4; tile += 8) {
         const int db = tile >> 2, tb = tile & 3;
         f32x4 acc = zero4();
 #pragma unroll
@@ -1091,7 +1131,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaPrepArgs<E> a) {
     // Ut = T1 V, stored negated as -Ut^T (tiled)
     E* Uout = a.UtT + chunk * BLK * DV;
 #pragma unroll
-    for (int tile = w; tile < 4 * (DV / 16); tile += 4) {
+    for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
         const int tb = tile % 4, vb = tile / 4;
         f32x4 acc = zero4();
 #pragma unroll
@@ -1102,7 +1142,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaPrepArgs<E> a) {
     // Kh^T[d][t] = K[t][d] e^{b_C[d] - b_t[d]} (tiled), fragment (db, j)
     E* KhT = a.KhT + chunk * BLK * DK;
 #pragma unroll
-    for (int f = w; f < 2 * ND; f += 4) {
+    for (int f = w8; f < 2 * ND; f += 8) {
         const int db = f >> 1, j = f & 1;
         st_fragT(KhT, f, l, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, bC, -1.f, 0, BLK));
     }

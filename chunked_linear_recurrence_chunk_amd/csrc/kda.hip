@@ -34,15 +34,17 @@ template <typename E> struct KdaPrep2Args {
 };
 
 // ---------------------------------------------------------------------------
-// prep2: one work-group (4 waves) per (block, head, batch); wave w owns the
-// 16 tokens 16w.. as s (columns of P, rows of Kh and dvloc).  P is formed per
+// prep2: one work-group (8 waves) per (block, head, batch); wave w8 owns the
+// 16 tokens 16w.. (w = w8 & 3) as s (columns of P, rows of Kh and dvloc) and
+// half hf = w8 >> 2 of the output tiles.  Both halves form the same P tiles.  P is formed per
 // pair of 16-token tiles against a reference row of b between the two tiles
 // (the end of tile w off the diagonal, its middle on it), as in the GLA kernels.
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void kda_prep2_kernel(KdaPrep2Args<E> a) {
+__global__ __launch_bounds__(512) void kda_prep2_kernel(KdaPrep2Args<E> a) {
+    constexpr int NT = 512;
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, w8 = tid >> 6, w = w8 & 3, hf = w8 >> 2, l = tid & 63, r = l & 15, g = l >> 4;
     const int T = a.T, H = a.H, NC = a.NC;
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
     const size_t chunk = ((size_t)b * H + h) * NC + n;
@@ -55,32 +57,32 @@ __global__ __launch_bounds__(256) void kda_prep2_kernel(KdaPrep2Args<E> a) {
     __shared__ float seg[256];
 
     {
-        const auto kx = load_rows<E, BLK, DK>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        const auto gx = load_gate<false, E, DK>(a.g, tok0, h, H, nvalid);
-        const auto qx = load_rows<E, BLK, DK>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        const auto ox = load_rows<E, BLK, DV>(a.dO + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
-        const auto wx = load_tiled<E, BLK, DK>(a.W + chunk * BLK * DK);
-        store_rows<E, BLK, DK, PQ>(kx, Ks);
-        store_rows<E, BLK, DK, PQ>(gx, Qs);  // g staged where Q goes
-        store_rows<E, BLK, DV, PO>(ox, dOs);
-        store_untiled<E, BLK, DK, PQ>(wx, Ws);
+        const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto gx = load_gate<false, E, DK, NT>(a.g, tok0, h, H, nvalid);
+        const auto qx = load_rows<E, BLK, DK, NT>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        const auto ox = load_rows<E, BLK, DV, NT>(a.dO + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
+        const auto wx = load_tiled<E, BLK, DK, NT>(a.W + chunk * BLK * DK);
+        store_rows<E, BLK, DK, PQ, NT>(kx, Ks);
+        store_rows<E, BLK, DK, PQ, NT>(gx, Qs);  // g staged where Q goes
+        store_rows<E, BLK, DV, PO, NT>(ox, dOs);
+        store_untiled<E, BLK, DK, PQ, NT>(wx, Ws);
         __syncthreads();
         gate_cumsum<E, DK, PQ, PB>(Qs, Bs, seg, nvalid);
         __syncthreads();
-        store_rows<E, BLK, DK, PQ>(qx, Qs);
+        store_rows<E, BLK, DK, PQ, NT>(qx, Qs);
         __syncthreads();
     }
     const float* bC = Bs + (BLK - 1) * PB;
     // W^T (tiled; A: m = d, k = t)
     E* WT = a.WT + chunk * BLK * DK;
 #pragma unroll
-    for (int f = w; f < 2 * ND; f += 4) st_fragT(WT, f, l, ldfrag_tr(Ws, PQ, 32 * (f & 1), 16 * (f >> 1), l));
+    for (int f = w8; f < 2 * ND; f += 8) st_fragT(WT, f, l, ldfrag_tr(Ws, PQ, 32 * (f & 1), 16 * (f >> 1), l));
     // Kh[t][d] = K[t][d] e^{b_C[d] - b_t[d]} (tiled; A: m = t, k = d): fragments (w, kk)
     const int s = 16 * w + r;
     {
         E* Kh = a.Kh + chunk * BLK * DK;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) st_fragT(Kh, w * KK + kk, l, frag_row_decay(Ks, PQ, s, 32 * kk, Bs + s * PB, bC, -1.f));
+        for (int kk = hf; kk < KK; kk += 2) st_fragT(Kh, w * KK + kk, l, frag_row_decay(Ks, PQ, s, 32 * kk, Bs + s * PB, bC, -1.f));
     }
     // P[tb][w] (rows t, cols s), s <= t
     f32x4 P[4];
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(256) void kda_prep2_kernel(KdaPrep2Args<E> a) {
     fp[1] = frag_from_acc<E>(P[2], P[3]);
     E* dvlT = a.dvlT + chunk * BLK * DV;
 #pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
+    for (int vb = hf; vb < NVB; vb += 2) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
@@ -124,14 +126,11 @@ __global__ __launch_bounds__(256) void kda_prep2_kernel(KdaPrep2Args<E> a) {
     }
     __syncthreads();
     // Qs <- Q e^b (factors <= 1)
-    for (int idx = tid; idx < BLK * DK; idx += 256) {
-        const int t = idx / DK, d = idx % DK;
-        Qs[t * PQ + d] = from_f<E>(to_f(Qs[t * PQ + d]) * __expf(Bs[t * PB + d]));
-    }
+    scale_exp_rows<E, DK, PQ, PB, NT>(Qs, Bs, Qs);
     __syncthreads();
     // R[d][v] = sum_t (Q e^b)^T[d][t] dO[t][v] - sum_t W^T[d][t] dvloc[t][v]   (fp32, accumulator-tiled)
     float* Rt = a.Rt + chunk * DK * DV;
-    for (int tile = w; tile < ND * NVB; tile += 4) {
+    for (int tile = w8; tile < ND * NVB; tile += 8) {
         const int db = tile % ND, vb = tile / ND;
         f32x4 acc = zero4(), acc2 = zero4();
 #pragma unroll
@@ -220,42 +219,12 @@ __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
         gate_cumsum<E, DK, PK, PB>((const E*)Am, Bs, seg, nvalid);
         __syncthreads();
     }
-    for (int idx = tid; idx < BLK * DK; idx += NT) {
-        const int t = idx / DK, d = idx % DK;
-        Kd[t * PK + d] = from_f<E>(to_f(Ks[t * PK + d]) * __expf(Bs[t * PB + d]));
-    }
-    // Gram block row w, column blocks j <= w of this half:
-    // M[t][s] (s < t) and Am = Diag(beta) M
-    {
-        const int tl = 16 * w + r;
-        const float* refO = w > 0 ? Bs + (16 * w - 1) * PB : zrow;  // boundary before tile w
-        const float* refD = Bs + (16 * w + 7) * PB;                 // middle of tile w
-        Frag<E> fo[KK], fd[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            fo[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, Bs + tl * PB, refO, 1.f);
-            fd[kk] = frag_row_decay(Ks, PK, tl, 32 * kk, Bs + tl * PB, refD, 1.f);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if ((j & 1) != hf) continue;
-            f32x4 acc = zero4();
-            if (j <= w) {
-                const int s = 16 * j + r;
-                const float* ref = j < w ? refO : refD;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    mma(acc, j < w ? fo[kk] : fd[kk], frag_row_decay(Ks, PK, s, 32 * kk, Bs + s * PB, ref, -1.f));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * w + 4 * g + i, col = 16 * j + r;
-                const float m = col < row ? acc[i] : 0.f;
-                Mf[row * AP + col] = m;
-                Am[row * AP + col] = s_bet[row] * m;
-            }
-        }
-    }
+    scale_exp_rows<E, DK, PK, PB, NT>(Ks, Bs, Kd);
+    // Gram block row w, column blocks of this half: M[t][s] (s < t) and Am = Diag(beta) M
+    kda_gram_row<E, DK, PK, PB>(Ks, Bs, zrow, w, hf, [&](int row, int col, float m) {
+        Mf[row * AP + col] = m;
+        Am[row * AP + col] = s_bet[row] * m;
+    });
     __syncthreads();
     if (hf == 0) {
         // T = (I + A)^-1; wave w holds column block w: T row-major (Tr) and transposed (TT)
@@ -420,7 +389,7 @@ hipError_t launch_kda_fwd_t(const GdnLaunch& L, hipStream_t st) {
     const GdnWs& ws = L.ws;
     KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                       ws.eCk, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
-    launch("kda_prep", kda_prep_kernel<E, DK, DV>, gblk, dim3(256), st, pa);
+    launch("kda_prep", kda_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
     GdnScanArgs<E> sa{nullptr, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, L.S_out,
                       (E*)ws.hT, nullptr, L.H, L.NC, L.B * L.H};
     sa.eC = ws.eCk;
@@ -442,10 +411,10 @@ hipError_t launch_kda_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const GdnWs& ws = L.ws;
     KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                       ws.eCk, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
-    launch("kda_prep", kda_prep_kernel<E, DK, DV>, gblk, dim3(256), st, pa);
+    launch("kda_prep", kda_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
     KdaPrep2Args<E> p2{(const E*)L.q, (const E*)L.k, (const E*)L.dO, (const E*)L.g, (const E*)ws.W,
                        ws.Rt, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dvlT, L.T, L.H, L.NC};
-    launch("kda_prep2", kda_prep2_kernel<E, DK, DV>, gblk, dim3(256), st, p2);
+    launch("kda_prep2", kda_prep2_kernel<E, DK, DV>, gblk, dim3(512), st, p2);
     GdnScanArgs<E> sa{nullptr, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, nullptr, L.H, L.NC, L.B * L.H};
     sa.eC = ws.eCk;
