@@ -50,8 +50,10 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
         "gdn_out": (2 * Ck * es + C * f4 + kv * es + Cv * es + Cv * es,
                     2 * CC * dk + 2 * C * kv + 2 * CC * dv),
         "gdn_scan_bwd": (C * f4 + 2 * Ck * es + kv * f4 + Cv * es + kv * es + Cv * es, 2 * (2 * C * kv)),
-        "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 2 * kv * es + 2 * Cv * es + 3 * Ck * es + 2 * C * es,
-                          3 * (2 * C * kv) + 11 * (2 * CC * dk) + 2 * (2 * C ** 3) + 2 * CC * dk),
+        # reads T^T and the decayed Gram tiles that the backward's prep wrote
+        "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 2 * kv * es + 2 * Cv * es + 3 * Ck * es + 2 * C * es
+                          + CC * es + CC * f4,
+                          3 * (2 * C * kv) + 11 * (2 * CC * dk) + 2 * (2 * C ** 3)),
     }
     # GLA (per-channel gate, gk = dk gate values per token) and its scalar-gate
     # Mamba-2 member on the same kernels (gk = 1)
@@ -68,6 +70,8 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
                                  2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv)
         W[pre + "_scan_fwd_rec"] = W[pre + "_scan_fwd"]
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
+    # the backward's prep also writes T^T and K K^T * G for the block adjoints
+    W["gdn_prep_bwd"] = (W["gdn_prep"][0] + CC * es + CC * f4, W["gdn_prep"][1])
     # KDA (per-channel gate, dk == dv): the Gated DeltaNet data flow with
     # per-channel decays (exp(b_C) per channel in place of the per-token
     # gate), U token-major, and the WY adjoints dM, dX handed to the GLA intra

@@ -70,6 +70,8 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
         w.dvlT = c.take(nb * BLK * dv * es);
         w.dhT = c.take(nb * dk * dv * es);
         w.dUT = c.take(nb * BLK * dv * es);
+        w.TT = c.take(nb * BLK * BLK * es);
+        w.KKG = (float*)c.take(nb * BLK * BLK * 4);
     }
     if (total) *total = c.off;
     return w;

@@ -41,6 +41,8 @@ struct GdnWs {
     void* dvlT;   // [.., dv, 64]   dvloc^T, dvloc = (Q K^T * G * tril)^T dO
     void* dhT;    // [.., dv, dk]   gradient w.r.t. the state leaving the block, transposed
     void* dUT;    // [.., dv, 64]   dU^T
+    void* TT;     // [.., 64, 64]   T^T (tiled), T = (I + A)^-1
+    float* KKG;   // [.., 16, 256]  K K^T * G, strictly lower, accumulator tiles (rb, cb) at (4 rb + cb) * 256
     // KDA backward only
     float* dM;    // [.., 64, 64]   Diag(beta) dA, the adjoint of the decayed Gram product (fp32)
     float* dX;    // [.., 64, dk]   T^T dW (fp32)
@@ -67,6 +69,10 @@ template <typename E> struct GdnPrepArgs {
     float* gam;
     E *W, *KhT, *UtT;
     int n0 = 0;  // first block of the launch (grid x covers blocks n0 ..)
+    // backward only (nullable): T^T (tiled [s][t]) and the decayed Gram
+    // product K K^T * G (strictly lower, fp32, 16 accumulator tiles)
+    E* TT = nullptr;
+    float* KKG = nullptr;
 };
 
 template <typename E> struct GdnScanArgs {

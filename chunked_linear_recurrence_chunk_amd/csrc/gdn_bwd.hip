@@ -10,7 +10,9 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const GdnWs& ws = L.ws;
     GdnPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                       ws.gam, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
-    launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
+    pa.TT = (E*)ws.TT;
+    pa.KKG = ws.KKG;
+    launch("gdn_prep_bwd", gdn_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
     GdnPrep2Args<E> p2{(const E*)L.q, (const E*)L.k, (const E*)L.dO, ws.gam, (const E*)ws.W,
                        ws.Rt, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dvlT, L.T, L.H, L.NC};
     launch("gdn_prep2", gdn_prep2_kernel<E, DK, DV>, gblk, dim3(256), st, p2);
@@ -22,6 +24,7 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV>, dim3(2 * G), dim3(256), st, sa, sb, G);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const E*)ws.dUT,
+                       (const E*)ws.TT, ws.KKG,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};
     launch("gdn_bwd_intra", gdn_bwd_intra_kernel<E, DK, DV>, gblk, dim3(512), st, ia);
     return hipGetLastError();

@@ -61,6 +61,8 @@ template <typename E> struct GdnIntraArgs {
     const E *q, *k, *v, *beta, *dO;
     const float* gam;
     const E *h, *dh, *UT, *dUT;
+    const E* TT;        // T^T per block (tiled), from the prep
+    const float* KKG;   // K K^T * G per block (accumulator tiles), from the prep
     E *dq, *dk, *dv, *dg, *dbeta;
     int T, H, NC;
 };
@@ -382,14 +384,10 @@ template <typename E, int DK, int DV> struct IntraLds {
     static constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
     // persistent
     static constexpr size_t o_Ks = 0;                                  // E[64][PK]     K
-    static constexpr size_t o_KKG = o_Ks + sizeof(E) * BLK * PK;       // f32[64][AP]   (K K^T * G), strictly lower
-    static constexpr size_t o_TT = o_KKG + 4 * BLK * AP;               // E[64][PT]     TT[s][t] = T[t][s]
-    static constexpr size_t o_Tr = o_TT + sizeof(E) * BLK * PT;        // E[64][PT]     T row-major
-    static constexpr size_t o_E = o_Tr + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms), + 512 spare
+    static constexpr size_t o_TT = o_Ks + sizeof(E) * BLK * PK;        // E[64][PT]     TT[s][t] = T[t][s]
+    static constexpr size_t o_E = o_TT + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms), + 512 spare
     static constexpr size_t o_U = o_E + 4 * (BLK * 65 + 512);          // union starts here
-    // phase 0: Am f32[64][AP], Td f32[4][16][16]
-    static constexpr size_t p0_Am = o_U, p0_Td = p0_Am + 4 * BLK * AP;
-    static constexpr size_t p0_end = p0_Td + 4 * 4 * 256;
+    static constexpr size_t p0_end = o_U;
     // phase A: Qs E[64][PK], dOs E[64][PV], UTs E[DV][PT]
     static constexpr size_t pA_Q = o_U, pA_dO = pA_Q + sizeof(E) * BLK * PK;
     static constexpr size_t pA_UT = pA_dO + sizeof(E) * BLK * PV;
@@ -413,9 +411,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     static_assert(Lay::total <= 150 * 1024, "LDS budget");
     __shared__ __align__(16) char lds[Lay::total];
     E* Ks = (E*)(lds + Lay::o_Ks);
-    float* KKG = (float*)(lds + Lay::o_KKG);
     E* TT = (E*)(lds + Lay::o_TT);
-    E* Tr = (E*)(lds + Lay::o_Tr);
     float* Eb = (float*)(lds + Lay::o_E);
 
     // per-token partial sums of the two halves, combined in a fixed order
@@ -440,55 +436,19 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     const E* UT = a.UT + chunk * BLK * DV;
     const E* dUT = a.dUT + chunk * BLK * DV;
 
-    // ---------------- phase 0: gates, K, Gram, T -----------------------------
+    // ---------------- phase 0: gates, K, T (from the prep) -------------------
     const auto kx = load_rows<E, BLK, DK, NT>(kb, ldk, nvalid);
     const auto qx = load_rows<E, BLK, DK, NT>(qb, ldk, nvalid);
     const auto ox = load_rows<E, BLK, DV, NT>(dob, ldv, nvalid);
     const auto ux = load_tiled<E, DV, BLK, NT>(UT);
+    const auto tx = load_tiled<E, BLK, BLK, NT>(a.TT + chunk * BLK * BLK);
     if (tid < BLK) {
         s_gam[tid] = a.gam[chunk * BLK + tid];
         s_bet[tid] = tid < nvalid ? to_f(a.beta[(tok0 + tid) * H + h]) : 0.f;
     }
     store_rows<E, BLK, DK, PK, NT>(kx, Ks);
+    store_untiled<E, BLK, BLK, PT, NT>(tx, TT);
     __syncthreads();
-    {
-        float* Am = (float*)(lds + Lay::p0_Am);
-        Frag<E> fa[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) fa[kk] = ldfrag(Ks + (16 * w + r) * PK + 32 * kk + 4 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if ((j & 1) != hf) continue;
-            f32x4 acc = zero4();
-            if (j <= w) {
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) mma(acc, fa[kk], ldfrag(Ks + (16 * j + r) * PK + 32 * kk + 4 * g));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * w + 4 * g + i, col = 16 * j + r;
-                const float kkg = col < row ? acc[i] * __expf(s_gam[row] - s_gam[col]) : 0.f;
-                KKG[row * AP + col] = kkg;
-                Am[row * AP + col] = s_bet[row] * kkg;
-            }
-        }
-        __syncthreads();
-        if (hf == 0) {
-            f32x4 tc[4];
-            tri_inverse_cols(Am, (float*)(lds + Lay::p0_Td), tc);  // waves 0..3; one barrier inside
-            // wave w holds column block w of T: write T row-major (Tr) and transposed (TT)
-            const int s = 16 * w + r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) Tr[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii]);
-                st4(TT + s * PT + 16 * i + 4 * g, tc[i]);
-            }
-        } else {
-            __syncthreads();  // matches the barrier inside tri_inverse_cols
-        }
-        __syncthreads();
-    }
     // ---------------- phase A: dQ, and the output / state-update parts of dK ---
     E* Qs = (E*)(lds + Lay::pA_Q);
     E* dOs = (E*)(lds + Lay::pA_dO);
@@ -706,17 +666,19 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         for (int cb = 0; cb < 4; ++cb) {
             if ((cb & 1) != hf) continue;
             f32x4 acc = zero4();
+            // K K^T * G tile (w, cb): this lane's rows 16w + 4g + i, column 16cb + r
+            const f32x4 kkg = *(const f32x4*)(a.KKG + chunk * BLK * BLK + (4 * w + cb) * 256 + l * 4);
             if (cb <= w) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) mma(acc, fx[j], ldfrag(Tr + (16 * cb + r) * PT + 32 * j + 4 * g));
+                for (int j = 0; j < 2; ++j) mma(acc, fx[j], ldfrag_tr(TT, PT, 32 * j, 16 * cb, l));  // T rows 16cb + r
             }
             const int c = 16 * cb + r;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * w + 4 * g + i;
                 const float dA = (c < row) ? -acc[i] : 0.f;
-                gram[i] += dA * KKG[row * AP + c];
-                Eb[row * 65 + c] += dA * s_bet[row] * KKG[row * AP + c];  // gate cross term dA * A
+                gram[i] += dA * kkg[i];
+                Eb[row * 65 + c] += dA * s_bet[row] * kkg[i];  // gate cross term dA * A
                 const float m = dA * s_bet[row] * __expf(s_gam[row] - s_gam[c]);
                 if (c <= row) Ms[row * PT + c] = from_f<E>(c < row ? m : 0.f);
                 if (c < row) Ms[c * PT + row] = from_f<E>(m);

@@ -208,13 +208,14 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
                 for (int kk = 0; kk < DK / 32; ++kk) mma(acc, fa[kk], ldfrag(Ks + (16 * j + r) * PK + 32 * kk + 4 * g));
             }
             // D tile rows = 16w + 4g + i (r index "row"), cols = 16j + r (s index)
+            f32x4 kkg;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * w + 4 * g + i, col = 16 * j + r;
-                float val = 0.f;
-                if (col < row) val = s_bet[row] * __expf(s_gam[row] - s_gam[col]) * acc[i];
-                Am[row * AP + col] = val;
+                kkg[i] = col < row ? acc[i] * __expf(s_gam[row] - s_gam[col]) : 0.f;
+                Am[row * AP + col] = s_bet[row] * kkg[i];
             }
+            if (a.KKG) *(f32x4*)(a.KKG + chunk * BLK * BLK + (4 * w + j) * 256 + l * 4) = kkg;
         }
     }
     __syncthreads();
@@ -233,6 +234,11 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
                 T1[t * PT + s] = from_f<E>(tc[i][ii] * b1);
                 T2[t * PT + s] = from_f<E>(tc[i][ii] * b2);
             }
+        // T^T[s][t] (tiled) for the backward's block adjoints
+        if (a.TT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st4(a.TT + chunk * BLK * BLK + toff<E>(s, 16 * i + 4 * g, BLK), tc[i]);
+        }
     } else {
         __syncthreads();  // matches the barrier inside tri_inverse_cols
     }
