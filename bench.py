@@ -83,9 +83,11 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
     W["kda_out"] = W["gla_out"]
     kda_scan_bwd = (dk * f4 + 2 * Ck * es + kv * f4 + Cv * es + kv * es + Cv * es, 2 * (2 * C * kv))
     W["kda_scan_pair"] = tuple(x + y for x, y in zip(W["kda_scan_fwd"], kda_scan_bwd))
-    W["kda_bwd_wy"] = (2 * Ck * es + Cv * es + C * es + kv * es + Cv * es + Cv * es + C * es + CC * f4 + Ck * f4,
-                       2 * CC * dk + C ** 3 // 3 + 2 * C * kv + 2 * CC * dv + 2 * CC * dk + 2 * (2 * C ** 3)
-                       + 2 * CC * dv + 2 * CC * dk)
+    # the backward's prep also writes T^T, M and K e^b for the WY adjoint kernel
+    W["kda_prep_bwd"] = (W["kda_prep"][0] + CC * es + CC * f4 + Ck * es, W["kda_prep"][1])
+    W["kda_bwd_wy"] = (Ck * es + CC * es + CC * f4 + Cv * es + C * es + kv * es + Cv * es
+                       + Cv * es + C * es + CC * f4 + Ck * f4,
+                       2 * C * kv + 2 * CC * dv + 2 * CC * dk + 2 * (2 * C ** 3) + 2 * CC * dv + 2 * CC * dk)
     W["kda_bwd_intra"] = (5 * Ck * es + 2 * kv * es + CC * f4 + Ck * f4 + C * es + 3 * Ck * es,
                           2 * (2 * CC * dv) + 2 * (2 * C * kv) + 4 * (2 * CC * dk))
     # one launch running the forward recompute and the reverse scan side by side

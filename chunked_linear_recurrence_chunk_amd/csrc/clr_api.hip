@@ -104,6 +104,9 @@ GdnWs carve_kda(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
         w.dUT = c.take(nb * BLK * dv * es);
         w.dM = (float*)c.take(nb * BLK * BLK * 4);
         w.dX = (float*)c.take(nb * BLK * dk * 4);
+        w.TT = c.take(nb * BLK * BLK * es);
+        w.KKG = (float*)c.take(nb * BLK * BLK * 4);  // M, the decayed Gram product
+        w.Kd = c.take(nb * BLK * dk * es);
     }
     if (total) *total = c.off;
     return w;

@@ -44,6 +44,7 @@ struct GdnWs {
     void* TT;     // [.., 64, 64]   T^T (tiled), T = (I + A)^-1
     float* KKG;   // [.., 16, 256]  K K^T * G, strictly lower, accumulator tiles (rb, cb) at (4 rb + cb) * 256
     // KDA backward only
+    void* Kd;     // [.., 64, dk]   K e^b (row-major)
     float* dM;    // [.., 64, 64]   Diag(beta) dA, the adjoint of the decayed Gram product (fp32)
     float* dX;    // [.., 64, dk]   T^T dW (fp32)
 };

@@ -996,6 +996,11 @@ template <typename E> struct KdaPrepArgs {
     int T, H, NC;
     float* eC;
     E *W, *KhT, *UtT;
+    // backward only (nullable): T^T (tiled [s][t]), the decayed Gram product M
+    // (strictly lower, fp32, 16 accumulator tiles) and K e^b (row-major [64][dk])
+    E* TT = nullptr;
+    float* M = nullptr;
+    E* Kd = nullptr;
 };
 
 // dst[t][d] = src[t][d] e^{b_t[d]} over a 64 x DK tile (row pitch PX, b row
@@ -1099,10 +1104,21 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
     const float* bC = Bs + (BLK - 1) * PB;
     scale_exp_rows<E, DK, PK, PB, NT>(Ks, Bs, Kd);
     if (tid < 256) a.eC[chunk * 256 + tid] = tid < DK ? __expf(bC[tid]) : 0.f;
-    // Am[t][s] = beta_t M[t][s] (s < t)
-    kda_gram_row<E, DK, PK, PB>(Ks, Bs, zrow, w, hf,
-                                [&](int row, int col, float m) { Am[row * AP + col] = s_bet[row] * m; });
+    // Am[t][s] = beta_t M[t][s] (s < t); M as accumulator tiles for the backward
+    float* Mg = a.M ? a.M + chunk * BLK * BLK : nullptr;
+    kda_gram_row<E, DK, PK, PB>(Ks, Bs, zrow, w, hf, [&](int row, int col, float m) {
+        Am[row * AP + col] = s_bet[row] * m;
+        if (Mg) Mg[(4 * (row >> 4) + (col >> 4)) * 256 + l * 4 + (row & 3)] = m;
+    });
     __syncthreads();
+    if (a.Kd) {  // K e^b, row-major, for the backward
+        constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = DK / VEC;
+        E* dst = a.Kd + chunk * BLK * DK;
+        for (int u = tid; u < BLK * PER_ROW; u += NT) {
+            const int t = u / PER_ROW, c = (u % PER_ROW) * VEC;
+            *(uint4*)(dst + t * DK + c) = *(const uint4*)(Kd + t * PK + c);
+        }
+    }
     if (hf == 0) {
         // T = (I + A)^-1, wave w holds column block w; T1 = T Diag(beta)
         f32x4 tc[4];
@@ -1113,6 +1129,10 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) T1[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii] * bs);
+        if (a.TT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st4(a.TT + chunk * BLK * BLK + toff<E>(s, 16 * i + 4 * g, BLK), tc[i]);
+        }
     } else {
         __syncthreads();  // matches the barrier inside tri_inverse_cols
     }

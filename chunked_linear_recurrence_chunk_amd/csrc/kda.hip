@@ -143,52 +143,44 @@ __global__ __launch_bounds__(512) void kda_prep2_kernel(KdaPrep2Args<E> a) {
 }
 
 template <typename E> struct KdaWyArgs {
-    const E *k, *v, *g, *beta;
+    const E *v, *beta;
     const E *h, *dUT;  // S0 per block (tiled [d][v]), dU^T per block (tiled [v][t])
+    const E* TT;       // per block, from the prep: T^T (tiled)
+    const float* M;    //   the decayed Gram product (accumulator tiles)
+    const E* Kd;       //   K e^b (row-major [64][dk])
     E *dv, *dbeta;
     float *dM, *dX;    // per block: [64][64] and [64][dk], fp32
     int T, H, NC;
 };
 
 template <typename E, int DK, int DV> struct KdaWyLds {
-    static constexpr int PK = RP<E, DK>, PV = RP<E, DV>, PB = DK + 4;
+    static constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
     // persistent
     static constexpr size_t o_Kd = 0;                               // E[64][PK]    K e^b
-    static constexpr size_t o_M = o_Kd + sizeof(E) * BLK * PK;      // f32[64][AP]  M (strictly lower)
-    static constexpr size_t o_Tr = o_M + 4 * BLK * AP;              // E[64][PT]    T row-major
-    static constexpr size_t o_TT = o_Tr + sizeof(E) * BLK * PT;     // E[64][PT]    TT[s][t] = T[t][s]
+    static constexpr size_t o_TT = o_Kd + sizeof(E) * BLK * PK;     // E[64][PT]    TT[s][t] = T[t][s]
     static constexpr size_t o_V = o_TT + sizeof(E) * BLK * PT;      // E[64][PV]
-    static constexpr size_t o_U = o_V + sizeof(E) * BLK * PV;       // union
-    // phase 0: Ks E[64][PK], Bs f32[64][PB], Am f32[64][AP] (g staged there first), Td f32[1024]
-    static constexpr size_t p0_K = o_U, p0_B = p0_K + sizeof(E) * BLK * PK;
-    static constexpr size_t p0_Am = p0_B + 4 * BLK * PB, p0_Td = p0_Am + 4 * BLK * AP;
-    static constexpr size_t p0_end = p0_Td + 4 * 1024;
-    static_assert(sizeof(E) * PK <= 4 * AP, "g staging fits the Am rows");
     // phase B: dUTs E[DV][PT], dWs E[64][PK], dTT E[64][PT]
-    static constexpr size_t pB_dUT = o_U, pB_dW = pB_dUT + sizeof(E) * DV * PT;
+    static constexpr size_t pB_dUT = o_V + sizeof(E) * BLK * PV, pB_dW = pB_dUT + sizeof(E) * DV * PT;
     static constexpr size_t pB_dTT = pB_dW + sizeof(E) * BLK * PK;
-    static constexpr size_t pB_end = pB_dTT + sizeof(E) * BLK * PT;
-    static constexpr size_t total = p0_end > pB_end ? p0_end : pB_end;
+    static constexpr size_t total = pB_dTT + sizeof(E) * BLK * PT;
 };
 
 // ---------------------------------------------------------------------------
 // WY adjoints: one work-group (8 waves) per (block, head, batch).  Wave w8:
 // token block w = w8 & 3, half hf = w8 >> 2 (the halves split the column
-// blocks of the Gram and adjoint tiles and the feature / value loops).
+// blocks of the adjoint tiles and the feature / value loops).  T, M and
+// K e^b come from the prep of the same call.
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
     using Lay = KdaWyLds<E, DK, DV>;
     constexpr int NT = 512;
-    constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, KK = DK / 32, KV = DV / 32, ND = DK / 16;
+    constexpr int PK = Lay::PK, PV = Lay::PV, KK = DK / 32, KV = DV / 32, ND = DK / 16;
     constexpr int NDH = ND / 2, NVH = DV / 32;
     static_assert(Lay::total <= 150 * 1024, "LDS budget");
     __shared__ __align__(16) char lds[Lay::total];
-    __shared__ float s_bet[BLK], seg[256], s_g2[2][BLK], s_v2[2][BLK], s_k2[2][BLK];
-    __shared__ __align__(16) float zrow[DK];
+    __shared__ float s_bet[BLK], s_g2[2][BLK], s_v2[2][BLK], s_k2[2][BLK];
     E* Kd = (E*)(lds + Lay::o_Kd);
-    float* Mf = (float*)(lds + Lay::o_M);
-    E* Tr = (E*)(lds + Lay::o_Tr);
     E* TT = (E*)(lds + Lay::o_TT);
     E* Vs = (E*)(lds + Lay::o_V);
 
@@ -198,56 +190,27 @@ __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
     const size_t chunk = ((size_t)b * H + h) * NC + n;
     const int nvalid = min(BLK, T - n * BLK);
-    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
+    const size_t ldv = (size_t)H * DV;
     const E* S0 = a.h + chunk * DK * DV;
 
-    // ---------------- phase 0: b, K e^b, decayed Gram, T ---------------------
-    E* Ks = (E*)(lds + Lay::p0_K);
-    float* Bs = (float*)(lds + Lay::p0_B);
-    float* Am = (float*)(lds + Lay::p0_Am);
-    const auto dux = load_tiled<E, DV, BLK, NT>(a.dUT + chunk * BLK * DV);  // in flight during phase 0
+    // ---------------- phase 0: operands -------------------------------------
+    E* dUTs = (E*)(lds + Lay::pB_dUT);
+    E* dWs = (E*)(lds + Lay::pB_dW);
+    E* dTT = (E*)(lds + Lay::pB_dTT);
     {
-        const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        const auto gx = load_gate<false, E, DK, NT>(a.g, tok0, h, H, nvalid);
+        const auto dux = load_tiled<E, DV, BLK, NT>(a.dUT + chunk * BLK * DV);
+        const auto kx = load_rows<E, BLK, DK, NT>(a.Kd + chunk * BLK * DK, DK, BLK);
+        const auto tx = load_tiled<E, BLK, BLK, NT>(a.TT + chunk * BLK * BLK);
         const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
         if (tid < BLK) s_bet[tid] = tid < nvalid ? to_f(a.beta[(tok0 + tid) * H + h]) : 0.f;
-        if (tid < DK) zrow[tid] = 0.f;
-        store_rows<E, BLK, DK, PK, NT>(kx, Ks);
-        store_rows<E, BLK, DK, PK, NT>(gx, (E*)Am);  // g staged where Am goes
+        store_rows<E, BLK, DK, PK, NT>(kx, Kd);
+        store_untiled<E, BLK, BLK, PT, NT>(tx, TT);
         store_rows<E, BLK, DV, PV, NT>(vx, Vs);
-        __syncthreads();
-        gate_cumsum<E, DK, PK, PB>((const E*)Am, Bs, seg, nvalid);
-        __syncthreads();
-    }
-    scale_exp_rows<E, DK, PK, PB, NT>(Ks, Bs, Kd);
-    // Gram block row w, column blocks of this half: M[t][s] (s < t) and Am = Diag(beta) M
-    kda_gram_row<E, DK, PK, PB>(Ks, Bs, zrow, w, hf, [&](int row, int col, float m) {
-        Mf[row * AP + col] = m;
-        Am[row * AP + col] = s_bet[row] * m;
-    });
-    __syncthreads();
-    if (hf == 0) {
-        // T = (I + A)^-1; wave w holds column block w: T row-major (Tr) and transposed (TT)
-        f32x4 tc[4];
-        tri_inverse_cols(Am, (float*)(lds + Lay::p0_Td), tc);  // one barrier inside
-        const int s = 16 * w + r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) Tr[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii]);
-            st4(TT + s * PT + 16 * i + 4 * g, tc[i]);
-        }
-    } else {
-        __syncthreads();  // matches the barrier inside tri_inverse_cols
+        store_untiled<E, DV, BLK, PT, NT>(dux, dUTs);
     }
     __syncthreads();
 
     // ---------------- phase B: WY adjoints ------------------------------------
-    E* dUTs = (E*)(lds + Lay::pB_dUT);
-    E* dWs = (E*)(lds + Lay::pB_dW);
-    E* dTT = (E*)(lds + Lay::pB_dTT);
-    store_untiled<E, DV, BLK, PT, NT>(dux, dUTs);
-    __syncthreads();
     const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
     // dW^T[db][w] = -(S0 dU^T): rows d, cols t = tw; stored as dW[t][d]
     {
@@ -312,16 +275,18 @@ __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
         for (int cb = 0; cb < 4; ++cb) {
             if ((cb & 1) != hf) continue;
             f32x4 acc = zero4();
+            // M tile (w, cb): this lane's rows 16w + 4g + i, column 16cb + r
+            const f32x4 mt = *(const f32x4*)(a.M + chunk * BLK * BLK + (4 * w + cb) * 256 + l * 4);
             if (cb <= w) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) mma(acc, fx[j], ldfrag(Tr + (16 * cb + r) * PT + 32 * j + 4 * g));
+                for (int j = 0; j < 2; ++j) mma(acc, fx[j], ldfrag_tr(TT, PT, 32 * j, 16 * cb, l));  // T rows 16cb + r
             }
             const int c = 16 * cb + r;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * w + 4 * g + i;
                 const float dA = c < row ? -acc[i] : 0.f;
-                gram[i] += dA * Mf[row * AP + c];
+                gram[i] += dA * mt[i];
                 dMb[row * BLK + c] = dA * s_bet[row];
             }
         }
@@ -411,7 +376,10 @@ hipError_t launch_kda_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const GdnWs& ws = L.ws;
     KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                       ws.eCk, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
-    launch("kda_prep", kda_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
+    pa.TT = (E*)ws.TT;
+    pa.M = ws.KKG;
+    pa.Kd = (E*)ws.Kd;
+    launch("kda_prep_bwd", kda_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
     KdaPrep2Args<E> p2{(const E*)L.q, (const E*)L.k, (const E*)L.dO, (const E*)L.g, (const E*)ws.W,
                        ws.Rt, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dvlT, L.T, L.H, L.NC};
     launch("kda_prep2", kda_prep2_kernel<E, DK, DV>, gblk, dim3(512), st, p2);
@@ -425,8 +393,8 @@ hipError_t launch_kda_bwd_t(const GdnLaunch& L, hipStream_t st) {
     sb.eC = ws.eCk;
     const int G = (int)scan_grid(DV / 16, L.B * L.H);
     launch("kda_scan_pair", gdn_scan_pair_kernel<E, DK, DV, true>, dim3(2 * G), dim3(256), st, sa, sb, G);
-    KdaWyArgs<E> wa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, (const E*)ws.hT,
-                    (const E*)ws.dUT, (E*)L.dv_, (E*)L.dbeta, ws.dM, ws.dX, L.T, L.H, L.NC};
+    KdaWyArgs<E> wa{(const E*)L.v, (const E*)L.beta, (const E*)ws.hT, (const E*)ws.dUT, (const E*)ws.TT, ws.KKG,
+                    (const E*)ws.Kd, (E*)L.dv_, (E*)L.dbeta, ws.dM, ws.dX, L.T, L.H, L.NC};
     launch("kda_bwd_wy", kda_bwd_wy_kernel<E, DK, DV>, gblk, dim3(512), st, wa);
     GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)ws.Utok, (const E*)L.dO, (const E*)L.g,
                        (const E*)ws.hT, (const E*)ws.dhT, nullptr, (E*)L.dq, (E*)L.dk_, nullptr, (E*)L.dg,
