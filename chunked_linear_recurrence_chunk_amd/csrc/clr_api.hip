@@ -231,8 +231,10 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
     int rc = check_shape(s, gla, false);
     if (rc) return rc;
     if (kind == K_KDA && kda_f32_unsupported(s, false)) return CLR_ENOTSUP;
-    if (!q || !k || !v || !g) return CLR_EINVAL;
-    if (has_beta ? beta == nullptr : beta != nullptr) return CLR_EINVAL;
+    // per-token tensors are empty when T == 0 and may then be NULL
+    const bool tok = s->T > 0;
+    if (tok && (!q || !k || !v || !g)) return CLR_EINVAL;
+    if (has_beta ? (tok && beta == nullptr) : beta != nullptr) return CLR_EINVAL;
     const size_t es = esize(s->dtype);
     const size_t ntok = (size_t)s->B * s->T * s->H, nst = (size_t)s->B * s->H * s->dk * s->dv;
     Buf bufs[] = {{q, ntok * s->dk * es, false}, {k, ntok * s->dk * es, false},
@@ -307,8 +309,10 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
     int rc = kind == K_KDA ? check_shape(s, false, false) : check_shape(s, gla, true);
     if (rc) return rc;
     if (kind == K_KDA && kda_f32_unsupported(s, true)) return CLR_ENOTSUP;
-    if (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg || !dS_in) return CLR_EINVAL;
-    if (has_beta ? (beta == nullptr || dbeta == nullptr) : (beta != nullptr || dbeta != nullptr))
+    // per-token tensors are empty when T == 0 and may then be NULL
+    const bool tok = s->T > 0;
+    if (!dS_in || (tok && (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg))) return CLR_EINVAL;
+    if (has_beta ? (tok && (beta == nullptr || dbeta == nullptr)) : (beta != nullptr || dbeta != nullptr))
         return CLR_EINVAL;
     const size_t es = esize(s->dtype);
     const size_t ntok = (size_t)s->B * s->T * s->H, nst = (size_t)s->B * s->H * s->dk * s->dv;
@@ -394,7 +398,7 @@ int shortconv_fwd(const clr_conv_shape_t* s, const void* x, const float* w, cons
                   const void* state_in, void* y, void* state_out, void* stream) {
     int rc = conv_check_shape(s);
     if (rc) return rc;
-    if (!x || !w || !y) return CLR_EINVAL;
+    if (!w || (s->T > 0 && (!x || !y))) return CLR_EINVAL;  // x, y are empty (may be NULL) when T == 0
     const size_t es = esize(s->dtype), n = (size_t)s->B * s->T * s->C, ns = (size_t)s->B * (s->W - 1) * s->C;
     Buf bufs[] = {{x, n * es, false}, {w, (size_t)s->C * s->W * 4, false}, {bias, (size_t)s->C * 4, false},
                   {state_in, ns * es, false}, {y, n * es, true}, {state_out, ns * es, true}};
@@ -420,7 +424,7 @@ int shortconv_bwd(const clr_conv_shape_t* s, const void* x, const float* w, cons
                   float* dbias, float* dstate_in, int accumulate, void* ws, size_t ws_bytes, void* stream) {
     int rc = conv_check_shape(s);
     if (rc) return rc;
-    if (!x || !w || !dy || !dx || !dw || (s->W > 1 && !dstate_in)) return CLR_EINVAL;
+    if (!w || !dw || (s->W > 1 && !dstate_in) || (s->T > 0 && (!x || !dy || !dx))) return CLR_EINVAL;
     if (accumulate != 0 && accumulate != 1) return CLR_EINVAL;
     const size_t es = esize(s->dtype), n = (size_t)s->B * s->T * s->C, ns = (size_t)s->B * (s->W - 1) * s->C;
     const size_t nw = (size_t)s->C * s->W * 4, nb = (size_t)s->C * 4;

@@ -36,7 +36,9 @@
  * Supported head sizes: GDN (dk, dv) in {(32,32), (64,64), (128,128)};
  * GLA additionally (128, 256).  The float32 backward supports (32, 32) only
  * (CLR_ENOTSUP otherwise).  Any T >= 0 (a ragged last 64-token block is
- * handled by treating the missing tokens as identity steps).
+ * handled by treating the missing tokens as identity steps; with T == 0 the
+ * per-token tensors are empty and may be NULL, and the state passes through:
+ * S_out = S_in, dS_in = dS_out).
  *
  * Ownership and execution
  * -----------------------
