@@ -418,6 +418,15 @@ __device__ __forceinline__ f32x4 cvt4(Raw4<bf16> x) {
 __device__ __forceinline__ f32x4 cvt4(Raw4<float> x) { return x.v; }
 
 // Inclusive prefix sum over the 64 lanes of a wave (lane order).
+// Four consecutive floats (16-byte aligned, LDS or global) read together and
+// kept ahead of any per-element condition: the empty asm stops the compiler
+// from sinking each read under its own branch and waiting on it separately.
+__device__ __forceinline__ f32x4 ld4_now(const float* p) {
+    f32x4 v = *(const f32x4*)p;
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 __device__ __forceinline__ float wave_prefix_sum(float x) {
     const int l = lane_id();
 #pragma unroll

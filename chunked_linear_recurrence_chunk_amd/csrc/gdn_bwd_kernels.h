@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
     const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
     constexpr int PQ = RP<E, DK>, PO = RP<E, DV>, KK = DK / 32, ND = DK / 16, NVB = DV / 16;
 
-    __shared__ float s_gam[BLK], s_Gam[BLK];
+    __shared__ __align__(16) float s_gam[BLK], s_Gam[BLK];
     __shared__ __align__(16) E Qs[BLK * PQ], dOs[BLK * PO], Ws[BLK * PQ], dvlt[DV * PT];
 
     const auto qx = load_rows<E, BLK, DK>(qb, ldk, nvalid);
@@ -140,10 +140,12 @@ __global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) mma(acc, ldfrag(Qs + (16 * tb + r) * PQ + 32 * kk + 4 * g), fk[kk]);
             const int s = 16 * w + r;
+            const f32x4 gt = ld4_now(s_gam + 16 * tb + 4 * g);
+            const float gs = s_gam[s];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * g + i;
-                acc[i] = (s <= t) ? acc[i] * __expf(s_gam[t] - s_gam[s]) : 0.f;
+                acc[i] = (s <= t) ? acc[i] * __expf(gt[i] - gs) : 0.f;
             }
         }
         P[tb] = acc;
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     float* Eb = (float*)(lds + Lay::o_E);
 
     // per-token partial sums of the two halves, combined in a fixed order
-    __shared__ float s_gam[BLK], s_bet[BLK], s_y[BLK], s_kdk[BLK], s_red[8];
+    __shared__ __align__(16) float s_gam[BLK], s_bet[BLK], s_y[BLK], s_kdk[BLK], s_red[8];
     __shared__ float s_q2[2][BLK], s_k2[2][BLK], s_g2[2][BLK], s_v2[2][BLK], s_b2[2][BLK];
 
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -478,10 +480,11 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         if (sb <= w) {
 #pragma unroll
             for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag_tr(UTs, PT, 32 * kk, 16 * sb, l), fdo[kk]);
+            const f32x4 gs = ld4_now(s_gam + 16 * sb + 4 * g);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = 16 * sb + 4 * g + i;
-                acc[i] = (s <= tw) ? acc[i] * __expf(gam_tw - s_gam[s]) : 0.f;
+                acc[i] = (s <= tw) ? acc[i] * __expf(gam_tw - gs[i]) : 0.f;
             }
         }
         dPT[sb] = acc;
@@ -512,10 +515,11 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         if (tb >= w) {
 #pragma unroll
             for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag(dOs + (16 * tb + r) * PV + 32 * kk + 4 * g), fU[kk]);
+            const f32x4 gt = ld4_now(s_gam + 16 * tb + 4 * g);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * g + i;
-                acc[i] = (tw <= t) ? acc[i] * __expf(s_gam[t] - gam_tw) : 0.f;
+                acc[i] = (tw <= t) ? acc[i] * __expf(gt[i] - gam_tw) : 0.f;
             }
         }
         dP[tb] = acc;
@@ -673,13 +677,15 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
                 for (int j = 0; j < 2; ++j) mma(acc, fx[j], ldfrag_tr(TT, PT, 32 * j, 16 * cb, l));  // T rows 16cb + r
             }
             const int c = 16 * cb + r;
+            const f32x4 gr = ld4_now(s_gam + 16 * w + 4 * g), br = ld4_now(s_bet + 16 * w + 4 * g);
+            const float gc = s_gam[c];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * w + 4 * g + i;
                 const float dA = (c < row) ? -acc[i] : 0.f;
                 gram[i] += dA * kkg[i];
-                Eb[row * 65 + c] += dA * s_bet[row] * kkg[i];  // gate cross term dA * A
-                const float m = dA * s_bet[row] * __expf(s_gam[row] - s_gam[c]);
+                Eb[row * 65 + c] += dA * br[i] * kkg[i];  // gate cross term dA * A
+                const float m = dA * br[i] * __expf(gr[i] - gc);
                 if (c <= row) Ms[row * PT + c] = from_f<E>(c < row ? m : 0.f);
                 if (c < row) Ms[c * PT + row] = from_f<E>(m);
             }

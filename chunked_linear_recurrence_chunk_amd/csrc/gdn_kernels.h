@@ -170,7 +170,7 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     const int nvalid = min(BLK, T - n * BLK);             // tokens of this block inside the sequence
     constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
 
-    __shared__ float s_gam[BLK], s_bet[BLK], s_Gam[BLK], s_ek[BLK];
+    __shared__ __align__(16) float s_gam[BLK], s_bet[BLK], s_Gam[BLK], s_ek[BLK];
     __shared__ float Am[BLK * AP], Td[4 * 256];
     __shared__ __align__(16) E Ks[BLK * PK], Vs[BLK * PV], T1[BLK * PT], T2[BLK * PT];
 
@@ -209,11 +209,13 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
             }
             // D tile rows = 16w + 4g + i (r index "row"), cols = 16j + r (s index)
             f32x4 kkg;
+            const f32x4 gr = ld4_now(s_gam + 16 * w + 4 * g), br = ld4_now(s_bet + 16 * w + 4 * g);
+            const float gc = s_gam[16 * j + r];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * w + 4 * g + i, col = 16 * j + r;
-                kkg[i] = col < row ? acc[i] * __expf(s_gam[row] - s_gam[col]) : 0.f;
-                Am[row * AP + col] = s_bet[row] * kkg[i];
+                kkg[i] = col < row ? acc[i] * __expf(gr[i] - gc) : 0.f;
+                Am[row * AP + col] = br[i] * kkg[i];
             }
             if (a.KKG) *(f32x4*)(a.KKG + chunk * BLK * BLK + (4 * w + j) * 256 + l * 4) = kkg;
         }
@@ -585,6 +587,10 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) fq[kk] = ldfrag(Qs + t_lane * PK + 32 * kk + 4 * g);
     const float gt = gam[t_lane];
+    // gamma at rows 16 sb + 4g + i, all read before use
+    f32x4 gs[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) gs[sb] = ld4_now(gam + 16 * sb + 4 * g);
     // P^T[s][t] = (k_s . q_t) exp(gamma_t - gamma_s) for s <= t
     f32x4 P[4];
 #pragma unroll
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s2 = 16 * sb + 4 * g + i;
-                acc[i] = (s2 <= t_lane) ? acc[i] * __expf(gt - gam[s2]) : 0.f;
+                acc[i] = (s2 <= t_lane) ? acc[i] * __expf(gt - gs[sb][i]) : 0.f;
             }
         }
         P[sb] = acc;
