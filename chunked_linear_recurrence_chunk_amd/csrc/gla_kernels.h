@@ -91,8 +91,9 @@ __device__ __forceinline__ Frag<E> ldfrag_tokcol(const E* base, size_t ld, int j
 
 // ---------------------------------------------------------------------------
 // Block gate cumsum b[t][d] = sum_{s <= t} g[s][d] (tokens past the end of
-// the sequence contribute 0), from a row-major g tile in LDS (pitch PG) into
-// fp32 LDS (pitch PB).  256 threads take 256 / DK token segments per channel:
+// the sequence contribute 0: every caller stages those rows of g as zeros,
+// so the reads need no test and go out together), from a row-major g tile in
+// LDS (pitch PG) into fp32 LDS (pitch PB).  256 threads take 256 / DK token segments per channel:
 // each sums its segment in token order, then adds the totals of the earlier
 // segments in order.  The split does not depend on the work-group size, so
 // every kernel that forms b gets bit-identical values.  `seg` is 256 floats
@@ -102,12 +103,16 @@ template <typename E, int DK, int PG, int PB>
 __device__ __forceinline__ void gate_cumsum(const E* gs, float* bs, float* seg, int nvalid) {
     constexpr int S = 256 / DK, L = BLK / S;  // segments per channel, tokens per segment
     const int tid = threadIdx.x, d = tid % DK, sg = tid / DK;
+    (void)nvalid;  // rows at or past nvalid are zero in gs
     if (tid < 256) {
+        float gv[L];
+#pragma unroll
+        for (int i = 0; i < L; ++i) gv[i] = to_f(gs[(sg * L + i) * PG + d]);
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const int t = sg * L + i;
-            run += t < nvalid ? to_f(gs[t * PG + d]) : 0.f;
+            run += gv[i];
             bs[t * PB + d] = run;
         }
         seg[tid] = run;
