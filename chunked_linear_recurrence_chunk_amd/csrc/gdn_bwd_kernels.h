@@ -599,6 +599,12 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     __syncthreads();  // phase A done: Qs, dOs, UTs free
 
     // ---------------- phase B: WY-transform adjoints ------------------------
+    // K K^T * G tiles (w, cb) of this half, cb = hf and hf + 2 (rows 16w + 4g + i,
+    // column 16cb + r), in flight during the dW and dT products
+    f32x4 kkgt[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+        kkgt[u] = *(const f32x4*)(a.KKG + chunk * BLK * BLK + (4 * w + hf + 2 * u) * 256 + l * 4);
     E* dUTs = (E*)(lds + Lay::pB_dUT);
     E* dWs = (E*)(lds + Lay::pB_dW);
     E* dTT = (E*)(lds + Lay::pB_dTT);
@@ -670,8 +676,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         for (int cb = 0; cb < 4; ++cb) {
             if ((cb & 1) != hf) continue;
             f32x4 acc = zero4();
-            // K K^T * G tile (w, cb): this lane's rows 16w + 4g + i, column 16cb + r
-            const f32x4 kkg = *(const f32x4*)(a.KKG + chunk * BLK * BLK + (4 * w + cb) * 256 + l * 4);
+            const f32x4 kkg = kkgt[cb >> 1];  // K K^T * G tile (w, cb)
             if (cb <= w) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) mma(acc, fx[j], ldfrag_tr(TT, PT, 32 * j, 16 * cb, l));  // T rows 16cb + r

@@ -211,6 +211,10 @@ __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
     __syncthreads();
 
     // ---------------- phase B: WY adjoints ------------------------------------
+    // M tiles (w, cb) of this half, cb = hf and hf + 2, in flight during the dW and dT products
+    f32x4 mtt[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) mtt[u] = *(const f32x4*)(a.M + chunk * BLK * BLK + (4 * w + hf + 2 * u) * 256 + l * 4);
     const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
     // dW^T[db][w] = -(S0 dU^T): rows d, cols t = tw; stored as dW[t][d]
     {
@@ -275,8 +279,7 @@ __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
         for (int cb = 0; cb < 4; ++cb) {
             if ((cb & 1) != hf) continue;
             f32x4 acc = zero4();
-            // M tile (w, cb): this lane's rows 16w + 4g + i, column 16cb + r
-            const f32x4 mt = *(const f32x4*)(a.M + chunk * BLK * BLK + (4 * w + cb) * 256 + l * 4);
+            const f32x4 mt = mtt[cb >> 1];  // M tile (w, cb): rows 16w + 4g + i, column 16cb + r
             if (cb <= w) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) mma(acc, fx[j], ldfrag_tr(TT, PT, 32 * j, 16 * cb, l));  // T rows 16cb + r
