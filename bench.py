@@ -44,8 +44,6 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
         # Gated DeltaNet (dk == dv)
         "gdn_prep": (2 * Ck * es + 2 * C * es + C * f4 + 3 * Ck * es,
                      2 * CC * dk + 2 * (2 * CC * dk) + C ** 3 // 3),
-        "gdn_prep2": (4 * Ck * es + C * f4 + 3 * Ck * es + kv * f4,
-                      2 * (2 * CC * dk) + 2 * (2 * C * kv)),
         "gdn_scan_fwd": (C * f4 + 3 * Ck * es + kv * es + Cv * es, 2 * (2 * C * kv)),
         "gdn_out": (2 * Ck * es + C * f4 + kv * es + Cv * es + Cv * es,
                     2 * CC * dk + 2 * C * kv + 2 * CC * dv),
@@ -70,8 +68,11 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
                                  2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv)
         W[pre + "_scan_fwd_rec"] = W[pre + "_scan_fwd"]
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
-    # the backward's prep also writes T^T and K K^T * G for the block adjoints
-    W["gdn_prep_bwd"] = (W["gdn_prep"][0] + CC * es + CC * f4, W["gdn_prep"][1])
+    # the backward's prep also reads Q and dO and writes the reverse scan's
+    # operands W^T, Kh, dvloc^T, R (fp32) and T^T, K K^T * G for the block
+    # adjoints; products P = Q K^T, P^T dO, Z = Gam Q - P W, R = Z^T dO
+    W["gdn_prep_bwd"] = (W["gdn_prep"][0] + 2 * Ck * es + 3 * Ck * es + kv * f4 + CC * es + CC * f4,
+                         W["gdn_prep"][1] + 2 * CC * dk + 2 * CC * dv + 2 * CC * dk + 2 * C * kv)
     # KDA (per-channel gate, dk == dv): the Gated DeltaNet data flow with
     # per-channel decays (exp(b_C) per channel in place of the per-token
     # gate), U token-major, and the WY adjoints dM, dX handed to the GLA intra

@@ -74,6 +74,10 @@ template <typename E> struct GdnPrepArgs {
     // product K K^T * G (strictly lower, fp32, 16 accumulator tiles)
     E* TT = nullptr;
     float* KKG = nullptr;
+    // backward only: the reverse scan's operands (q, dO in; W^T, Kh, dvloc^T, R out)
+    const E *q = nullptr, *dO = nullptr;
+    E *WT = nullptr, *Kh = nullptr, *dvlT = nullptr;
+    float* Rt = nullptr;
 };
 
 template <typename E> struct GdnScanArgs {

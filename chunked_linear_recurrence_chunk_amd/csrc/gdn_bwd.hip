@@ -12,10 +12,13 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
                       ws.gam, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
     pa.TT = (E*)ws.TT;
     pa.KKG = ws.KKG;
-    launch("gdn_prep_bwd", gdn_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
-    GdnPrep2Args<E> p2{(const E*)L.q, (const E*)L.k, (const E*)L.dO, ws.gam, (const E*)ws.W,
-                       ws.Rt, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dvlT, L.T, L.H, L.NC};
-    launch("gdn_prep2", gdn_prep2_kernel<E, DK, DV>, gblk, dim3(256), st, p2);
+    pa.q = (const E*)L.q;
+    pa.dO = (const E*)L.dO;
+    pa.WT = (E*)ws.WT;
+    pa.Kh = (E*)ws.Kh;
+    pa.dvlT = (E*)ws.dvlT;
+    pa.Rt = ws.Rt;
+    launch("gdn_prep_bwd", gdn_prep_kernel<E, DK, DV, true>, gblk, dim3(512), st, pa);
     GdnScanArgs<E> sa{ws.gam, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, (E*)ws.UT, L.H, L.NC, L.B * L.H};
     GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,

@@ -7,10 +7,11 @@
 // gradients and dS_in.  The forward is recomputed from S_in (full activation
 // recomputation, as in that paper's Sec. 4.1 setup), then:
 //
-//   prep   (as in the forward)        gamma, T, W, Ut, Kh^T
-//   prep2  (parallel over blocks)     W^T, Kh, dvloc = (Q K^T * G * tril)^T dO and
-//                                     R = (Diag(Gam) Q)^T dO - W^T dvloc (the dS-independent
-//                                     part of the reverse state step)
+//   prep   (parallel over blocks)     as in the forward: gamma, T, W, Ut, Kh^T; and from the
+//                                     same staged tiles W^T, Kh, dvloc = (Q K^T * G * tril)^T dO,
+//                                     R = (Diag(Gam) Q)^T dO - W^T dvloc (the dS-independent part
+//                                     of the reverse state step), T^T and K K^T * G
+//                                     (gdn_kernels.h, gdn_prep_kernel with BWD)
 //   scan   (forward recompute)        h_n (state entering block n, key-major), U_n
 //   dscan  (reverse, sequential)      dh_n = dL/dS_{n+1};  dU_n = dvloc_n + Kh_n dh_n;
 //                                     dS_n = Gam_C dh_n + (Diag(Gam) Q_n)^T dO_n - W_n^T dU_n
@@ -37,15 +38,6 @@
 
 namespace clr {
 
-template <typename E> struct GdnPrep2Args {
-    const E *q, *k, *dO;
-    const float* gam;
-    const E* W;
-    float* Rt;
-    E *WT, *Kh, *dvlT;
-    int T, H, NC;
-};
-
 template <typename E> struct GdnScanBwdArgs {
     const float* gam;
     const E *Kh, *WT, *dvlT;
@@ -66,126 +58,6 @@ template <typename E> struct GdnIntraArgs {
     E *dq, *dk, *dv, *dg, *dbeta;
     int T, H, NC;
 };
-
-// ---------------------------------------------------------------------------
-// prep2: one work-group (4 waves) per (block, head, batch).  Q, dO and W are
-// staged row-major in LDS (all loads in flight at once) and read transposed
-// where a product contracts over tokens; wave w keeps K rows 16w.. in
-// registers (B operand of P and the rows of Kh it writes).
-// ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_prep2_kernel(GdnPrep2Args<E> a) {
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
-    const int T = a.T, H = a.H, NC = a.NC;
-    const size_t tok0 = (size_t)b * T + (size_t)n * BLK;
-    const size_t chunk = ((size_t)b * H + h) * NC + n;
-    const int nvalid = min(BLK, T - n * BLK);
-    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
-    const E* qb = a.q + tok0 * ldk + (size_t)h * DK;
-    const E* kb = a.k + tok0 * ldk + (size_t)h * DK;
-    const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
-    constexpr int PQ = RP<E, DK>, PO = RP<E, DV>, KK = DK / 32, ND = DK / 16, NVB = DV / 16;
-
-    __shared__ __align__(16) float s_gam[BLK], s_Gam[BLK];
-    __shared__ __align__(16) E Qs[BLK * PQ], dOs[BLK * PO], Ws[BLK * PQ], dvlt[DV * PT];
-
-    const auto qx = load_rows<E, BLK, DK>(qb, ldk, nvalid);
-    const auto ox = load_rows<E, BLK, DV>(dob, ldv, nvalid);
-    const auto wx = load_tiled<E, BLK, DK>(a.W + chunk * BLK * DK);
-    Frag<E> fk[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) fk[kk] = ldfrag_row(kb, 16 * w + r, nvalid, ldk, 32 * kk + 4 * g);
-    if (tid < BLK) {
-        const float gm = a.gam[chunk * BLK + tid];
-        s_gam[tid] = gm;
-        s_Gam[tid] = __expf(gm);
-    }
-    store_rows<E, BLK, DK, PQ>(qx, Qs);
-    store_rows<E, BLK, DV, PO>(ox, dOs);
-    store_untiled<E, BLK, DK, PQ>(wx, Ws);
-    __syncthreads();
-
-    const float gC = s_gam[BLK - 1];
-    // W^T (tiled; A: m = d, k = t): fragment (db, j) is the B fragment of W
-    // over tokens 32j.., columns 16db..
-    E* WT = a.WT + chunk * BLK * DK;
-#pragma unroll
-    for (int f = w; f < 2 * ND; f += 4) st_fragT(WT, f, l, ldfrag_tr(Ws, PQ, 32 * (f & 1), 16 * (f >> 1), l));
-    // Kh[t][d] = exp(gamma_C - gamma_t) K[t][d] (tiled; A: m = t, k = d):
-    // fragments (w, kk) are this wave's K rows.
-    {
-        E* Kh = a.Kh + chunk * BLK * DK;
-        const float ek = __expf(gC - s_gam[16 * w + r]);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            Frag<E> x = fk[kk];
-            if constexpr (sizeof(E) == 2) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x.v[i] = (bf16)((float)x.v[i] * ek);
-            } else {
-                x.lo = x.lo * ek;
-                x.hi = x.hi * ek;
-            }
-            st_fragT(Kh, w * KK + kk, l, x);
-        }
-    }
-    // dvloc[s][v] = sum_t P[t][s] dO[t][v],  P[t][s] = (q_t . k_s) exp(gamma_t - gamma_s), s <= t.
-    // Wave w owns s-block w: P[tb][w] tiles (rows t, cols s) chain into A = P^T.
-    f32x4 P[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = zero4();
-        if (tb >= w) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) mma(acc, ldfrag(Qs + (16 * tb + r) * PQ + 32 * kk + 4 * g), fk[kk]);
-            const int s = 16 * w + r;
-            const f32x4 gt = ld4_now(s_gam + 16 * tb + 4 * g);
-            const float gs = s_gam[s];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * g + i;
-                acc[i] = (s <= t) ? acc[i] * __expf(gt[i] - gs) : 0.f;
-            }
-        }
-        P[tb] = acc;
-    }
-    Frag<E> fp[2];
-    fp[0] = frag_from_acc<E>(P[0], P[1]);
-    fp[1] = frag_from_acc<E>(P[2], P[3]);
-    E* dvlT = a.dvlT + chunk * BLK * DV;
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
-        st4(dvlT + toff<E>(16 * vb + r, 16 * w + 4 * g, BLK), acc);
-        st4(dvlt + (16 * vb + r) * PT + 16 * w + 4 * g, acc);
-    }
-    __syncthreads();
-    // Qs <- Diag(Gam) Q in place
-#pragma unroll
-    for (int j = 0; j < RowsRegs<E, BLK, DK>::N; ++j) {
-        constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = DK / VEC;
-        const int idx = tid + 256 * j, t = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-        const float G = s_Gam[t];
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) Qs[t * PQ + c + i] = from_f<E>(to_f(Qs[t * PQ + c + i]) * G);
-    }
-    __syncthreads();
-    // R[d][v] = sum_t Qg^T[d][t] dO[t][v] - sum_t W^T[d][t] dvloc[t][v]   (fp32, accumulator-tiled)
-    float* Rt = a.Rt + chunk * DK * DV;
-    for (int tile = w; tile < ND * NVB; tile += 4) {
-        const int db = tile % ND, vb = tile / ND;
-        f32x4 acc = zero4(), acc2 = zero4();
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            mma(acc, ldfrag_tr(Qs, PQ, 32 * j, 16 * db, l), ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
-            mma(acc2, ldfrag_tr(Ws, PQ, 32 * j, 16 * db, l), ldfrag(dvlt + (16 * vb + r) * PT + 32 * j + 4 * g));
-        }
-        *(f32x4*)(Rt + atoff(db, vb, DK, l)) = acc - acc2;
-    }
-}
 
 // ---------------------------------------------------------------------------
 // dscan: one work-group per (16-wide value slice, head, batch), blocks in

@@ -153,11 +153,35 @@ __device__ __forceinline__ void st_fragT(float* base, int f, int l, const Frag<f
 }
 
 // ---------------------------------------------------------------------------
-// prep: one work-group (4 waves) per (block n, head h, batch b).  K and V are
+// prep: one work-group (8 waves) per (block n, head h, batch b).  K and V are
 // staged row-major in LDS with all loads in flight at once; products that
 // contract over the token index read them transposed (ldfrag_tr).
+//
+// With BWD it also does the dS-independent part of the backward for the
+// block (the reverse scan's operands) from the same staged tiles:
+//   W^T and Kh = Diag(exp(gamma_C - gamma)) K (tiled),
+//   dvloc = P^T dO,  P[t][s] = (q_t . k_s) exp(gamma_t - gamma_s)  (s <= t),
+//   R = (Diag(Gam) Q)^T dO - W^T dvloc = Z^T dO,  Z = Diag(Gam) Q - P W,
+// and writes T^T and K K^T * G for the block adjoints.  The LDS regions of
+// the first part are reused by the second:
+//   [Ks | Vs -> Qs | Am -> Ws | Td | T1, T2 -> dOs],  P^T over Ks (or after
+//   the last region when it does not fit there).
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV> struct PrepLds {
+    static constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
+    static constexpr size_t o_K = 0, o_V = o_K + sizeof(E) * BLK * PK;
+    static constexpr size_t o_A = o_V + sizeof(E) * BLK * PV, o_Td = o_A + 4 * BLK * AP;
+    static constexpr size_t o_T1 = o_Td + 4 * 1024, o_T2 = o_T1 + sizeof(E) * BLK * PT;
+    static constexpr size_t end1 = o_T2 + sizeof(E) * BLK * PT;
+    static constexpr bool P_OVER_K = sizeof(E) * BLK * PT <= sizeof(E) * BLK * PK;
+    static constexpr size_t o_P = P_OVER_K ? o_K : end1;
+    static constexpr size_t total = P_OVER_K ? end1 : end1 + sizeof(E) * BLK * PT;
+    // the backward's second part fits the regions of the first
+    static constexpr bool BWD_FITS = DK == DV && sizeof(E) * BLK * PK <= 4 * BLK * AP &&
+                                     sizeof(E) * BLK * PV <= 2 * sizeof(E) * BLK * PT;
+};
+
+template <typename E, int DK, int DV, bool BWD = false>
 __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     constexpr int NT = 512;
     const int n = a.n0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -168,14 +192,21 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     const size_t tok0 = (size_t)b * T + (size_t)n * BLK;  // first token (b, n*64)
     const size_t chunk = ((size_t)b * H + h) * NC + n;    // workspace block index
     const int nvalid = min(BLK, T - n * BLK);             // tokens of this block inside the sequence
-    constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
+    using Lay = PrepLds<E, DK, DV>;
+    constexpr int PK = Lay::PK, PV = Lay::PV, ND = DK / 16, KK = DK / 32;
 
     __shared__ __align__(16) float s_gam[BLK], s_bet[BLK], s_Gam[BLK], s_ek[BLK];
-    __shared__ float Am[BLK * AP], Td[4 * 256];
-    __shared__ __align__(16) E Ks[BLK * PK], Vs[BLK * PV], T1[BLK * PT], T2[BLK * PT];
+    __shared__ __align__(16) char lds[Lay::total];
+    E* Ks = (E*)(lds + Lay::o_K);
+    E* Vs = (E*)(lds + Lay::o_V);
+    float* Am = (float*)(lds + Lay::o_A);
+    float* Td = (float*)(lds + Lay::o_Td);
+    E* T1 = (E*)(lds + Lay::o_T1);
+    E* T2 = (E*)(lds + Lay::o_T2);
 
-    const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * H * DK + (size_t)h * DK, (size_t)H * DK, nvalid);
-    const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * H * DV + (size_t)h * DV, (size_t)H * DV, nvalid);
+    const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
+    const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+    const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
     if (w8 == 0) {
         // tokens past the end are identity steps: g = 0, beta = 0
         const size_t ig = (tok0 + l) * H + h;
@@ -196,16 +227,16 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     // Gram block row w: A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s), s < r
     // (column blocks j of this wave's half: j & 1 == hf)
     {
-        Frag<E> fa[DK / 32];
+        Frag<E> fa[KK];
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) fa[kk] = ldfrag(Ks + (16 * w + r) * PK + 32 * kk + 4 * g);
+        for (int kk = 0; kk < KK; ++kk) fa[kk] = ldfrag(Ks + (16 * w + r) * PK + 32 * kk + 4 * g);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if ((j & 1) != hf) continue;
             f32x4 acc = zero4();
             if (j <= w) {
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) mma(acc, fa[kk], ldfrag(Ks + (16 * j + r) * PK + 32 * kk + 4 * g));
+                for (int kk = 0; kk < KK; ++kk) mma(acc, fa[kk], ldfrag(Ks + (16 * j + r) * PK + 32 * kk + 4 * g));
             }
             // D tile rows = 16w + 4g + i (r index "row"), cols = 16j + r (s index)
             f32x4 kkg;
@@ -246,16 +277,26 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     }
     __syncthreads();
 
-    // W^T[d][t] = sum_s K^T[d][s] T1[t][s]  -> stored as W[t][d] (tiled)
+    // backward: Q and dO in flight while the outputs below are formed
+    RowsRegs<E, BLK, DK, NT> qx;
+    RowsRegs<E, BLK, DV, NT> ox;
+    if constexpr (BWD) {
+        qx = load_rows<E, BLK, DK, NT>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        ox = load_rows<E, BLK, DV, NT>(a.dO + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
+    }
+    // W^T[d][t] = sum_s K^T[d][s] T1[t][s]  -> stored as W[t][d] (tiled); backward
+    // also row-major in LDS (Ws, where Am was)
     E* Wout = a.W + chunk * BLK * DK;
+    E* Ws = (E*)(lds + Lay::o_A);
 #pragma unroll
-    for (int tile = w8; tile < (DK / 16) * 4; tile += 8) {
+    for (int tile = w8; tile < ND * 4; tile += 8) {
         const int db = tile >> 2, tb = tile & 3;
         f32x4 acc = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             mma(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g));
         st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
+        if constexpr (BWD) st4(Ws + (16 * tb + r) * PK + 16 * db + 4 * g, acc);
     }
     // Ut[t][v] = sum_s T2[t][s] V[s][v]  -> stored negated as -Ut^T[v][t] (tiled),
     // so that the scan forms -U = W S - Ut by accumulating onto it
@@ -273,11 +314,109 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     // is the B fragment of Kh over tokens 32j.., columns 16db..
     E* Khout = a.KhT + chunk * BLK * DK;
 #pragma unroll
-    for (int f = w8; f < 2 * (DK / 16); f += 8) {
+    for (int f = w8; f < 2 * ND; f += 8) {
         const int db = f >> 1, j = f & 1;
         Frag<E> x = ldfrag_tr(Ks, PK, 32 * j, 16 * db, l);
         frag_scale_k(x, s_ek, 32 * j, g);
         st_fragT(Khout, f, l, x);
+    }
+    if constexpr (BWD) {
+        static_assert(Lay::BWD_FITS, "Q where V was, W where Am was, dO where T1, T2 were");
+        constexpr int PQ = PK, PO = PV, NVB = DV / 16;
+        E* Qs = (E*)(lds + Lay::o_V);
+        E* dOs = (E*)(lds + Lay::o_T1);
+        E* PsT = (E*)(lds + Lay::o_P);
+        __syncthreads();  // V, T1, T2 no longer read: Q and dO take their places
+        store_rows<E, BLK, DK, PQ, NT>(qx, Qs);
+        store_rows<E, BLK, DV, PO, NT>(ox, dOs);
+        __syncthreads();
+        // W^T (tiled; A: m = d, k = t) and Kh (tiled; A: m = t, k = d): fragments (w, kk)
+        E* WT = a.WT + chunk * BLK * DK;
+#pragma unroll
+        for (int f = w8; f < 2 * ND; f += 8) st_fragT(WT, f, l, ldfrag_tr(Ws, PQ, 32 * (f & 1), 16 * (f >> 1), l));
+        const int s = 16 * w + r;
+        Frag<E> fk[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) fk[kk] = ldfrag(Ks + s * PK + 32 * kk + 4 * g);
+        {
+            E* Kh = a.Kh + chunk * BLK * DK;
+            const float ek = s_ek[s];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                if ((kk & 1) != hf) continue;  // static indices: fk stays in registers
+                Frag<E> x = fk[kk];
+                if constexpr (sizeof(E) == 2) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) x.v[i] = (bf16)((float)x.v[i] * ek);
+                } else {
+                    x.lo = x.lo * ek;
+                    x.hi = x.hi * ek;
+                }
+                st_fragT(Kh, w * KK + kk, l, x);
+            }
+        }
+        // P[tb][w] (rows t, cols s = 16w + r), s <= t; both halves form the same tiles
+        f32x4 P[4];
+        const float gs = s_gam[s];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 acc = zero4();
+            if (tb >= w) {
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) mma(acc, ldfrag(Qs + (16 * tb + r) * PQ + 32 * kk + 4 * g), fk[kk]);
+                const f32x4 gt = ld4_now(s_gam + 16 * tb + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tb + 4 * g + i;
+                    acc[i] = (s <= t) ? acc[i] * __expf(gt[i] - gs) : 0.f;
+                }
+            }
+            P[tb] = acc;
+        }
+        // dvloc^T[v][s] = sum_t P[t][s] dO[t][v] (this half's value blocks)
+        Frag<E> fp[2];
+        fp[0] = frag_from_acc<E>(P[0], P[1]);
+        fp[1] = frag_from_acc<E>(P[2], P[3]);
+        E* dvlT = a.dvlT + chunk * BLK * DV;
+#pragma unroll
+        for (int vb = hf; vb < NVB; vb += 2) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
+            st4(dvlT + toff<E>(16 * vb + r, 16 * w + 4 * g, BLK), acc);
+        }
+        __syncthreads();  // K no longer read: P^T may take its place
+        if (hf == 0) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) st4(PsT + s * PT + 16 * tb + 4 * g, P[tb]);
+        }
+        __syncthreads();
+        // Z = Diag(Gam) Q - P W in place of Q: tiles (tb, db), rows t = 16tb + 4g + i, column d = 16db + r
+#pragma unroll
+        for (int tile = w8; tile < 4 * ND; tile += 8) {
+            const int tb = tile & 3, db = tile >> 2;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                mma(acc, ldfrag_tr(PsT, PT, 32 * j, 16 * tb, l), ldfrag_tr(Ws, PQ, 32 * j, 16 * db, l));
+            const f32x4 Gt = ld4_now(s_Gam + 16 * tb + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                E& q = Qs[(16 * tb + 4 * g + i) * PQ + 16 * db + r];
+                q = from_f<E>(Gt[i] * to_f(q) - acc[i]);
+            }
+        }
+        __syncthreads();
+        // R[d][v] = sum_t Z[t][d] dO[t][v]   (fp32, accumulator-tiled)
+        float* Rt = a.Rt + chunk * DK * DV;
+        for (int tile = w8; tile < ND * NVB; tile += 8) {
+            const int db = tile % ND, vb = tile / ND;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                mma(acc, ldfrag_tr(Qs, PQ, 32 * j, 16 * db, l), ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
+            *(f32x4*)(Rt + atoff(db, vb, DK, l)) = acc;
+        }
     }
 }
 
