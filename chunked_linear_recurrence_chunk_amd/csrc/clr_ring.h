@@ -66,10 +66,10 @@ __device__ __forceinline__ void ring_issue_units(char* slot, int pid, F unit_src
     }
 }
 
-template <int NU, typename F>
+template <int NU, typename F, int NP = NPROD>
 __device__ __forceinline__ void ring_issue(char* slot, int pid, F unit_src, const void* small_src) {
-    ring_issue_units<NU, NPROD>(slot, pid, unit_src);
-    if (__builtin_amdgcn_readfirstlane(pid) == NPROD - 1)
+    ring_issue_units<NU, NP>(slot, pid, unit_src);
+    if (__builtin_amdgcn_readfirstlane(pid) == NP - 1)
         __builtin_amdgcn_global_load_lds(small_src, CLR_LDS(slot + NU * RING_UNIT), 4, 0, 0);
 }
 

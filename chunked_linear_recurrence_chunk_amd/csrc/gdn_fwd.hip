@@ -22,8 +22,8 @@ struct GdnFwdStages {
                           (E*)L.ws.hT, (E*)L.ws.UT, L.H, L.NC, L.B * L.H};
         sa.n0 = n0;
         sa.n1 = n1;
-        launch("gdn_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(DV / 16, L.B * L.H)), dim3(256),
-               st, sa);
+        launch("gdn_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, false, SCAN_NP_FAST>,
+               dim3(scan_grid(DV / 16, L.B * L.H)), dim3(scan_threads<SCAN_NP_FAST>), st, sa);
     }
     void out(int n0, int n1, hipStream_t st) const {
         GdnOutArgs<E> oa{(const E*)L.q, (const E*)L.k, L.ws.gam, (const E*)L.ws.hT, (const E*)L.ws.UT, (E*)L.o,

@@ -595,6 +595,14 @@ __device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK>& o, cons
 // With PCD (per-channel decay, KDA) one more unit holds exp(b_C) for every key
 // channel, as fp32 (256 floats, padded), and the state-store tile also
 // stages U for its token-major store.
+// Scan work-groups: one consumer wave and NP producer waves.  The Gated
+// DeltaNet forward scan's consumer is light enough for the operand stream to
+// bound it, and seven producers stream faster than three (27 -> 20.5 us per
+// 2048-token chunk at H = 16); the scans whose consumer does more per block
+// (KDA's token-major U, the reverse scan) measured no gain or a loss.
+constexpr int SCAN_NP_FAST = 7;
+template <int NP> constexpr int scan_threads = 64 * (NP + 1);
+
 template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFwdGeom {
     static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 1-KB units per fragment
     static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF;
@@ -609,7 +617,7 @@ template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFw
 
 // Scan body for work-group `wgi` of the scan grid; `smem` holds
 // ScanFwdGeom::LDS bytes (16-byte aligned).
-template <typename E, int DK, int DV, bool HNAT, bool PCD = false>
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NP = NPROD>
 __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int wgi, char* smem) {
     const int H = a.H, NC = a.NC;
     // blocks n0 .. n0 + NB - 1 of each head are scanned (ring index j = n - n0)
@@ -621,7 +629,7 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
     using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD>;
     constexpr int ND = SG::ND, UPF = SG::UPF, NWU = SG::NWU, NKU = SG::NKU, NU = SG::NU, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
-    using G = RingGeom<NU>;
+    using G = RingGeom<NU, NP>;
     char* ring = smem;
     E* tile = (E*)(smem + P * G::SLOT);
     const size_t bh = (size_t)b * H + h;
@@ -639,7 +647,8 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
                 if (PCD && u == NU - 1) return a.eC + c * 256 + l * 4;
                 return UtT + (u - NWU - NKU) * UE;
             };
-            ring_issue<NU>(ring + (n % P) * G::SLOT, pid, src, PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.gam + c * BLK + l));
+            ring_issue<NU, decltype(src), NP>(ring + (n % P) * G::SLOT, pid, src,
+                                                     PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.gam + c * BLK + l));
         };
         const int pre = NB < P - 1 ? NB : P - 1;
         for (int n = 0; n < pre; ++n) issue(n);
@@ -677,10 +686,10 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
     }
 }
 
-template <typename E, int DK, int DV, bool HNAT, bool PCD = false>
-__global__ __launch_bounds__(256) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NP = NPROD>
+__global__ __launch_bounds__(scan_threads<NP>) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
     __shared__ __align__(16) char smem[ScanFwdGeom<E, DK, DV, HNAT, PCD>::LDS];
-    gdn_scan_fwd_body<E, DK, DV, HNAT, PCD>(a, blockIdx.x, smem);
+    gdn_scan_fwd_body<E, DK, DV, HNAT, PCD, NP>(a, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
