@@ -112,10 +112,10 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 
                                               const GdnScanBwdArgs<E>& a, size_t chunk, int vb, int l, E* tile,
                                               const char* slot = nullptr) {
     constexpr int ND = DK / 16;
-    store_state_tiled<E, DK, DV>(a.dh + chunk * DK * DV, dS, tile, 16 * vb, l);
     Frag<E> fs[DK / 32];
 #pragma unroll
     for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+    store_state_sel<E, DK, DV>(a.dh + chunk * DK * DV, fs, 16 * vb, l);
     f32x4 dUp[4];
     E* dUT = a.dUT + chunk * BLK * DV;
 #pragma unroll

@@ -487,6 +487,50 @@ __device__ __forceinline__ void store_state_tiled(E* h, const f32x4 (&S)[DK / 16
     asm volatile("" ::: "memory");
 }
 
+// The same store without the LDS round trip.  fs[kk] (the state's B fragment
+// over rows 32kk.., from frag_from_acc) is also the A fragment of the state's
+// transpose; its product with the 32 x 16 selector [I; 0] (half 0) or [0; I]
+// (half 1) is the transposed tile of rows 32kk + 16 half.., in which lane
+// (r, g) holds S[32kk + 16 half + r][v0 + 4g + i], i < 4: exactly this lane's
+// four elements of the tiled h fragment.  Each product has one nonzero term,
+// so the stored values are the rounded state, as above.
+template <typename E> __device__ __forceinline__ Frag<E> state_sel(int half, int l);
+template <> __device__ __forceinline__ Frag<bf16> state_sel<bf16>(int half, int l) {
+    const int r = l & 15, g = l >> 4;
+    Frag<bf16> f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int k = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);
+        f.v[i] = (bf16)(k == r + 16 * half ? 1.f : 0.f);
+    }
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> state_sel<float>(int half, int l) {
+    const int r = l & 15, g = l >> 4;
+    Frag<float> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.lo[i] = (half == 0 && 4 * g + i == r) ? 1.f : 0.f;
+        f.hi[i] = (half == 1 && 4 * g + i == r) ? 1.f : 0.f;
+    }
+    return f;
+}
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void store_state_sel(E* h, const Frag<E> (&fs)[DK / 32], int v0, int l) {
+    const int r = l & 15, g = l >> 4;
+    const Frag<E> sel[2] = {state_sel<E>(0, l), state_sel<E>(1, l)};
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            f32x4 c = zero4();
+            mma(c, fs[kk], sel[half]);
+            E* dst = h + toff<E>(32 * kk + 16 * half + r, v0 + 4 * g, DV);
+            if constexpr (sizeof(E) == 2) *(bf16x4*)dst = bf16x4{(bf16)c[0], (bf16)c[1], (bf16)c[2], (bf16)c[3]};
+            else *(f32x4*)dst = c;
+        }
+}
+
 // One block of the recurrence.  HNAT selects the layout of the saved states:
 // false -> tiled h^T[v][d] (read by the forward's out kernel), true -> tiled
 // h[d][v] (read by the backward).
@@ -505,7 +549,7 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[D
     if (a.hT) {
         E* hT = a.hT + chunk * DK * DV;
         if constexpr (HNAT) {
-            store_state_tiled<E, DK, DV>(hT, S, tile, 16 * vb, l);
+            store_state_sel<E, DK, DV>(hT, fs, 16 * vb, l);
         } else {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) st8T(hT, vb * KK + kk, l, S[2 * kk], S[2 * kk + 1]);
