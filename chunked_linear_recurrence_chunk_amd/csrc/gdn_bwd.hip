@@ -24,7 +24,8 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
                          L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC, L.B * L.H};
     const int G = (int)scan_grid(DV / 16, L.B * L.H);
-    launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV>, dim3(2 * G), dim3(256), st, sa, sb, G);
+    launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV, false, SCAN_NP_FAST>, dim3(2 * G),
+           dim3(scan_threads<SCAN_NP_FAST>), st, sa, sb, G);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const E*)ws.dUT,
                        (const E*)ws.TT, ws.KKG,

@@ -164,7 +164,7 @@ template <typename E, int DK, bool PCD = false> struct ScanBwdGeom {
     static constexpr int LDS = P * SLOT + TILE;
 };
 
-template <typename E, int DK, int DV, bool PCD = false>
+template <typename E, int DK, int DV, bool PCD = false, int NP = NPROD>
 __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, int wgi, char* smem) {
     const int H = a.H, NC = a.NC;
     int b, h, vb;
@@ -176,7 +176,7 @@ __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, in
     using SG = ScanBwdGeom<E, DK, PCD>;
     constexpr int NU = Rg::NU, UPF = Rg::UPF, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
-    using G = RingGeom<NU>;
+    using G = RingGeom<NU, NP>;
     char* ring = smem;
     E* tile = (E*)(smem + P * G::SLOT);
     const size_t bh = (size_t)b * H + h;
@@ -197,8 +197,8 @@ __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, in
                 if (PCD && u == NU - 1) return a.eC + c * 256 + l * 4;
                 return dvl + (u - Rg::NKU - Rg::NWU - Rg::NRU) * UE;
             };
-            ring_issue<NU>(ring + (m % P) * G::SLOT, pid, src,
-                           PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.gam + c * BLK + l));
+            ring_issue<NU, decltype(src), NP>(ring + (m % P) * G::SLOT, pid, src,
+                                              PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.gam + c * BLK + l));
         };
         const int pre = NC < P - 1 ? NC : P - 1;
         for (int m = 0; m < pre; ++m) issue(m);
@@ -237,12 +237,12 @@ __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, in
 // The forward recompute (state entering every block) and the reverse scan are
 // independent given the prep outputs; one launch runs both, work-groups
 // [0, G) the former and [G, 2G) the latter, so together they fill the chip.
-template <typename E, int DK, int DV, bool PCD = false>
-__global__ __launch_bounds__(256) void gdn_scan_pair_kernel(GdnScanArgs<E> fa, GdnScanBwdArgs<E> ba, int G) {
+template <typename E, int DK, int DV, bool PCD = false, int NP = NPROD>
+__global__ __launch_bounds__(scan_threads<NP>) void gdn_scan_pair_kernel(GdnScanArgs<E> fa, GdnScanBwdArgs<E> ba, int G) {
     constexpr int LF = ScanFwdGeom<E, DK, DV, true, PCD>::LDS, LB = ScanBwdGeom<E, DK, PCD>::LDS;
     __shared__ __align__(16) char smem[LF > LB ? LF : LB];
-    if ((int)blockIdx.x < G) gdn_scan_fwd_body<E, DK, DV, true, PCD>(fa, blockIdx.x, smem);
-    else gdn_scan_bwd_body<E, DK, DV, PCD>(ba, blockIdx.x - G, smem);
+    if ((int)blockIdx.x < G) gdn_scan_fwd_body<E, DK, DV, true, PCD, NP>(fa, blockIdx.x, smem);
+    else gdn_scan_bwd_body<E, DK, DV, PCD, NP>(ba, blockIdx.x - G, smem);
 }
 
 // ---------------------------------------------------------------------------
