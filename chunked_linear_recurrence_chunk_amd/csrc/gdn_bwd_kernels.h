@@ -115,7 +115,7 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 
     Frag<E> fs[DK / 32];
 #pragma unroll
     for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
-    store_state_sel<E, DK, DV>(a.dh + chunk * DK * DV, fs, 16 * vb, l);
+    state_store<E, DK, DV, PCD>(a.dh + chunk * DK * DV, fs, tile, 16 * vb, l);
     f32x4 dUp[4];
     E* dUT = a.dUT + chunk * BLK * DV;
 #pragma unroll
@@ -158,7 +158,7 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 
 template <typename E, int DK, bool PCD = false> struct ScanBwdGeom {
     static constexpr int NU = ScanBwdRing<E, DK, PCD>::NU;
     static constexpr int SLOT = RingGeom<NU>::SLOT;
-    static constexpr int TILE = DK * 16 * (int)sizeof(E);
+    static constexpr int TILE = state_tile_bytes(DK, sizeof(E));
     static constexpr int PF = (144 * 1024 - TILE) / SLOT;
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
     static constexpr int LDS = P * SLOT + TILE;

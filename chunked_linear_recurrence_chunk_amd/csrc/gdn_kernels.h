@@ -531,6 +531,49 @@ __device__ __forceinline__ void store_state_sel(E* h, const Frag<E> (&fs)[DK / 3
         }
 }
 
+// The same store for bf16 through a wave-private LDS tile T[16 v][DK + 8]:
+// each lane writes the two bf16x4 halves of fs[kk] (four consecutive rows d
+// of its column v0 + r) as 8-byte runs of row r, and reads back with the
+// transposing LDS read, which hands lane (r, g) T[4g + i][16 db + r] =
+// S[16 db + r][v0 + 4g + i]: its four elements of the tiled h fragment.  Eight
+// 8-byte writes and eight transposing reads per block, no matrix-core work on
+// the recurrence's chain; fp32 states take the selector path.  Measured per
+// 2048-token chunk: with three producer waves (KDA's scans) this path is the
+// faster one (pair scan 42.2 -> 39.2 us), with seven (the Gated DeltaNet
+// scans, whose producers keep LDS busier) the selector products are (28.8
+// against 31.5 us).  state_store() picks accordingly.
+constexpr int state_tile_bytes(int dk, int es) { return 16 * (dk + 8) * es; }
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void store_state_tr(E* h, const Frag<E> (&fs)[DK / 32], E* tile, int v0, int l) {
+    if constexpr (sizeof(E) == 2) {
+        constexpr int PS = DK + 8;
+        const int r = l & 15, g = l >> 4, j = (l >> 2) & 3, q = l & 3;
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            const bf16x8 v = fs[kk].v;
+            *(bf16x4*)(tile + r * PS + 32 * kk + 4 * g) = bf16x4{v[0], v[1], v[2], v[3]};
+            *(bf16x4*)(tile + r * PS + 32 * kk + 16 + 4 * g) = bf16x4{v[4], v[5], v[6], v[7]};
+        }
+        // LDS operations of one wave complete in order
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int db = 0; db < DK / 16; ++db) {
+            const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(tile + (4 * g + j) * PS + 16 * db + 4 * q));
+            *(bf16x4*)(h + toff<E>(16 * db + r, v0 + 4 * g, DV)) = x;
+        }
+        asm volatile("" ::: "memory");
+    } else {
+        store_state_sel<E, DK, DV>(h, fs, v0, l);
+    }
+}
+
+template <typename E, int DK, int DV, bool VIA_LDS>
+__device__ __forceinline__ void state_store(E* h, const Frag<E> (&fs)[DK / 32], E* tile, int v0, int l) {
+    if constexpr (VIA_LDS) store_state_tr<E, DK, DV>(h, fs, tile, v0, l);
+    else store_state_sel<E, DK, DV>(h, fs, v0, l);
+}
+
 // One block of the recurrence.  HNAT selects the layout of the saved states:
 // false -> tiled h^T[v][d] (read by the forward's out kernel), true -> tiled
 // h[d][v] (read by the backward).
@@ -549,7 +592,7 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[D
     if (a.hT) {
         E* hT = a.hT + chunk * DK * DV;
         if constexpr (HNAT) {
-            store_state_sel<E, DK, DV>(hT, fs, 16 * vb, l);
+            state_store<E, DK, DV, PCD>(hT, fs, tile, 16 * vb, l);
         } else {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) st8T(hT, vb * KK + kk, l, S[2 * kk], S[2 * kk + 1]);
@@ -652,7 +695,7 @@ template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFw
     static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF;
     static constexpr int NU = NWU + NKU + 2 * UPF + (PCD ? 1 : 0);
     static constexpr int SLOT = RingGeom<NU>::SLOT;
-    static constexpr int TILE_H = HNAT ? DK * 16 * (int)sizeof(E) : 16, TILE_U = PCD ? BLK * 16 * (int)sizeof(E) : 16;
+    static constexpr int TILE_H = HNAT ? state_tile_bytes(DK, sizeof(E)) : 16, TILE_U = PCD ? BLK * 16 * (int)sizeof(E) : 16;
     static constexpr int TILE = TILE_H > TILE_U ? TILE_H : TILE_U;
     static constexpr int PF = (144 * 1024 - TILE) / SLOT;
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
