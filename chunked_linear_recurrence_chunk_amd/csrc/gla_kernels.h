@@ -314,7 +314,7 @@ template <typename E, int DK, int DV, bool HNAT> struct GlaScanGeom : GlaSlices<
     static constexpr int ND = DK / 16, NKU = 2 * ND * SL::UPF;
     static constexpr int NU = NKU + SL::NS * SL::NVU + 1;  // Kh^T | V slices | exp(b_C)
     static constexpr int SLOT = RingGeom<NU, SL::NPW>::SLOT;
-    static constexpr int TILE = HNAT ? DK * 16 * (int)sizeof(E) : 16;  // per consumer wave
+    static constexpr int TILE = HNAT ? state_tile_bytes(DK, sizeof(E)) : 16;  // per consumer wave
     static constexpr int PF = (144 * 1024 - SL::NS * TILE) / SLOT;
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
 };
@@ -379,7 +379,10 @@ __global__ __launch_bounds__((GlaSlices<E, DK, DV>::THREADS)) void gla_scan_fwd_
         if (a.hT) {
             E* hT = a.hT + (bh * NC + n) * DK * DV;
             if constexpr (HNAT) {
-                store_state_tiled<E, DK, DV>(hT, S, tile, v0, l);
+                Frag<E> fs[KK];
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
+                store_state_tr<E, DK, DV>(hT, fs, tile, v0, l);
             } else {
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) st8T(hT, vb * KK + kk, l, S[2 * kk], S[2 * kk + 1]);
@@ -535,7 +538,9 @@ template <typename E, int DK, int DV> struct GlaDscanGeom : GlaSlices<E, DK, DV>
     static constexpr int NHU = 4 * KK * SL::UPF, NQU = 2 * ND * SL::UPF;
     static constexpr int NU = NHU + NQU + SL::NS * SL::NVU + 1;
     static constexpr int SLOT = RingGeom<NU, SL::NPW>::SLOT;
-    static constexpr int TILE = (DK > BLK ? DK : BLK) * 16 * (int)sizeof(E);
+    // per consumer wave: the state store's tile, or the dV rows' staging
+    static constexpr int TILE = state_tile_bytes(DK, sizeof(E)) > BLK * 16 * (int)sizeof(E)
+                                    ? state_tile_bytes(DK, sizeof(E)) : BLK * 16 * (int)sizeof(E);
     static constexpr int PF = (144 * 1024 - SL::NS * TILE) / SLOT;
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
 };
@@ -601,10 +606,10 @@ __global__ __launch_bounds__((GlaSlices<E, DK, DV>::THREADS)) void gla_scan_bwd_
     for (int m = 0; m < NC; ++m) {
         const size_t c = bh * NC + (NC - 1 - m);
         const char* slot = ring + (m % P) * G::SLOT;
-        store_state_tiled<E, DK, DV>(a.dh + c * DK * DV, dS, tile, v0, l);
         Frag<E> fs[KK];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+        store_state_tr<E, DK, DV>(a.dh + c * DK * DV, fs, tile, v0, l);
         f32x4 dVs[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
