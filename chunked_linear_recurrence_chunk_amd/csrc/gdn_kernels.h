@@ -432,11 +432,10 @@ template <typename E, int DK> struct ScanFwdOps {
     float gC;                 // gamma at the last token of the block
 };
 
-// Store the fp32 state slice (accumulator tiles, rows d, column v0 + r) in
-// key-major h[d][v] layout: staged through LDS (tile[d][16 v]) so that each
-// lane writes whole 16-byte rows instead of scattered elements.
-// More generally: store ROWS x 16 accumulator tiles (rows 16 rb + 4 g + i,
-// column c0 + r) into a row-major matrix with row stride ld, through LDS.
+// Store ROWS x 16 accumulator tiles (rows 16 rb + 4 g + i, column c0 + r)
+// into a row-major matrix with row stride ld, staged through LDS
+// (tile[ROWS][16]) so that each lane writes whole 16-byte row pieces instead
+// of scattered elements.
 template <typename E, int ROWS>
 __device__ __forceinline__ void store_rows16(E* dst, size_t ld, const f32x4 (&X)[ROWS / 16], E* tile, int c0, int r,
                                              int g, int nrows = ROWS) {
@@ -456,44 +455,17 @@ __device__ __forceinline__ void store_rows16(E* dst, size_t ld, const f32x4 (&X)
     asm volatile("" ::: "memory");
 }
 
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void store_state_kmajor(E* h, const f32x4 (&S)[DK / 16], E* tile, int v0, int r, int g) {
-    store_rows16<E, DK>(h, DV, S, tile, v0, r, g);
-}
-
 // Store a state slice (accumulator tiles: rows d = 16 db + 4g + i, column
 // v0 + r) into the tiled key-major h[d][v] (R = DK, C = DV).  A lane's values
-// belong to four different lane units of that layout, so the slice is
-// transposed through LDS (tile[d][16], used by the calling wave only); lane
-// l then writes columns v0 + 4 (l >> 4) .. +3 of row 16 db + (l & 15), which
-// is one contiguous half of a lane unit.
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void store_state_tiled(E* h, const f32x4 (&S)[DK / 16], E* tile, int v0, int l) {
-    const int r = l & 15, g = l >> 4;
-#pragma unroll
-    for (int db = 0; db < DK / 16; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tile[(16 * db + 4 * g + i) * 16 + r] = from_f<E>(S[db][i]);
-    // LDS operations of one wave complete in order
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
-        const int d = 16 * db + r;
-        E* dst = h + toff<E>(d, v0 + 4 * g, DV);
-        const E* src = tile + d * 16 + 4 * g;
-        if constexpr (sizeof(E) == 2) *(bf16x4*)dst = *(const bf16x4*)src;
-        else *(f32x4*)dst = *(const f32x4*)src;
-    }
-    asm volatile("" ::: "memory");
-}
-
-// The same store without the LDS round trip.  fs[kk] (the state's B fragment
-// over rows 32kk.., from frag_from_acc) is also the A fragment of the state's
-// transpose; its product with the 32 x 16 selector [I; 0] (half 0) or [0; I]
-// (half 1) is the transposed tile of rows 32kk + 16 half.., in which lane
-// (r, g) holds S[32kk + 16 half + r][v0 + 4g + i], i < 4: exactly this lane's
-// four elements of the tiled h fragment.  Each product has one nonzero term,
-// so the stored values are the rounded state, as above.
+// belong to four different lane units of that layout, so the slice has to be
+// transposed; two ways follow.
+// Without LDS: fs[kk] (the state's B fragment over rows 32kk.., from
+// frag_from_acc) is also the A fragment of the state's transpose; its product
+// with the 32 x 16 selector [I; 0] (half 0) or [0; I] (half 1) is the
+// transposed tile of rows 32kk + 16 half.., in which lane (r, g) holds
+// S[32kk + 16 half + r][v0 + 4g + i], i < 4: exactly this lane's four elements
+// of the tiled h fragment.  Each product has one nonzero term, so the stored
+// values are the bf16-rounded state.
 template <typename E> __device__ __forceinline__ Frag<E> state_sel(int half, int l);
 template <> __device__ __forceinline__ Frag<bf16> state_sel<bf16>(int half, int l) {
     const int r = l & 15, g = l >> 4;
@@ -531,7 +503,7 @@ __device__ __forceinline__ void store_state_sel(E* h, const Frag<E> (&fs)[DK / 3
         }
 }
 
-// The same store for bf16 through a wave-private LDS tile T[16 v][DK + 8]:
+// Through LDS (bf16), a wave-private tile T[16 v][DK + 8]:
 // each lane writes the two bf16x4 halves of fs[kk] (four consecutive rows d
 // of its column v0 + r) as 8-byte runs of row r, and reads back with the
 // transposing LDS read, which hands lane (r, g) T[4g + i][16 db + r] =
