@@ -3,12 +3,13 @@
 // A sequential scan is latency-bound: each 64-token block needs tens of KB of
 // operands, and one wave can only keep ~63 memory operations in flight.  The
 // scan work-groups therefore run one consumer wave (the recurrence, state in
-// registers) and three producer waves that stream the operands of the next
-// blocks into a ring of P LDS slots with direct global->LDS loads
+// registers) and NP producer waves (three, or seven where the consumer is
+// light enough for the stream to bound it) that stream the operands of the
+// next blocks into a ring of P LDS slots with direct global->LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at slot + unit*1024 +
 // lane*16, exactly where the consumer lane reads its fragment back).
 //
-// Round n (all four waves, separated by s_barrier):
+// Round n (all waves, separated by s_barrier):
 //   consumer  computes block n from slot n % P;
 //   producers issue block n + P - 1 into slot (n - 1) % P (read in round n-1),
 //             then wait until their loads for block n + 1 have landed.

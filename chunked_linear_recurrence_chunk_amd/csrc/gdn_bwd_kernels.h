@@ -62,7 +62,7 @@ template <typename E> struct GdnIntraArgs {
 // ---------------------------------------------------------------------------
 // dscan: one work-group per (16-wide value slice, head, batch), blocks in
 // reverse.  Wave 0 runs the reverse recurrence with dS in accumulator tiles;
-// waves 1..3 stream the operands of the next blocks into the LDS ring
+// the other waves stream the operands of the next blocks into the LDS ring
 // (clr_ring.h).  Ring unit u of a block is the contiguous 1-KB run u of
 // [Kh | W^T | R tiles (., vb) | dvloc^T fragments (vb, 0..1)], all tiled.
 // ---------------------------------------------------------------------------
@@ -246,9 +246,10 @@ __global__ __launch_bounds__(scan_threads<NP>) void gdn_scan_pair_kernel(GdnScan
 }
 
 // ---------------------------------------------------------------------------
-// intra: one work-group (4 waves) per (block, head, batch).  Wave w owns the
-// 16 tokens 16w..16w+15 of the block, both as "t" (rows of dQ) and as "s"
-// (rows of dK, dV, dbeta).  K, Q, dO and V are staged row-major, U^T and dU^T
+// intra: one work-group (8 waves) per (block, head, batch).  Waves w and
+// w + 4 own the 16 tokens 16w..16w+15 of the block, both as "t" (rows of dQ)
+// and as "s" (rows of dK, dV, dbeta), and split each phase's feature, value or
+// token-block loop between them.  K, Q, dO and V are staged row-major, U^T and dU^T
 // as [v][t]; every global load of a phase is issued at once, and products
 // that contract over the other index read the tiles transposed (ldfrag_tr).
 // The tiled h_n / dh_n fragments are read from global memory one 16-row

@@ -647,8 +647,8 @@ __device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK>& o, cons
         for (int j = 0; j < 2; ++j) o.kh[db][j] = ring_frag(slot, NWF + 2 * db + j, l, (E*)nullptr);
 }
 
-// Work-group: wave 0 runs the recurrence, waves 1..3 stream the operands of
-// the next blocks into the LDS ring (clr_ring.h).  All operands are tiled, so
+// Work-group: wave 0 runs the recurrence, the other waves stream the operands
+// of the next blocks into the LDS ring (clr_ring.h).  All operands are tiled, so
 // ring unit u of a block is the contiguous 1-KB run u of
 // [W | Kh^T | Ut^T fragments (vb, 0..1)].
 // With PCD (per-channel decay, KDA) one more unit holds exp(b_C) for every key

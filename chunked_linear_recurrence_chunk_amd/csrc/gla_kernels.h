@@ -412,8 +412,8 @@ __global__ __launch_bounds__((GlaSlices<E, DK, DV>::THREADS)) void gla_scan_fwd_
 }
 
 // ---------------------------------------------------------------------------
-// out: one work-group (4 waves) per (block, head, batch); wave R owns tokens
-// 16R..16R+15.  O^T tiles: inter part (h^T (Q*exp(b))^T) plus P V.  Q, K,
+// out: one work-group (8 waves) per (block, head, batch); waves R and R + 4
+// own tokens 16R..16R+15 and split the value slices.  O^T tiles: inter part (h^T (Q*exp(b))^T) plus P V.  Q, K,
 // V and the gate are staged row-major in LDS (V read transposed; when V does
 // not fit, its fragments are gathered from global memory).
 // ---------------------------------------------------------------------------
@@ -641,8 +641,9 @@ __global__ __launch_bounds__((GlaSlices<E, DK, DV>::THREADS)) void gla_scan_bwd_
 }
 
 // ---------------------------------------------------------------------------
-// intra: one work-group (4 waves) per (block, head, batch); wave R owns tokens
-// 16R..16R+15 (as t for dq, as s for dk and dv).  All output tiles are
+// intra: one work-group (8 waves) per (block, head, batch); waves R and R + 4
+// own tokens 16R..16R+15 (as t for dq, as s for dk and dv) and split each
+// phase's loops.  All output tiles are
 // transposed ([feature][token]) so each lane stores four contiguous values.
 // K, Q, V, dO and the gate tile are staged row-major in LDS with every load
 // of a stage in flight at once; the block gate cumsum is formed in LDS.
