@@ -115,7 +115,7 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 
     Frag<E> fs[DK / 32];
 #pragma unroll
     for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
-    state_store<E, DK, DV, PCD>(a.dh + chunk * DK * DV, fs, tile, 16 * vb, l);
+    state_store<E, DK, DV, PCD>(a.dh + chunk * DK * DV, fs, tile, 16 * vb, l);  // selector with seven producers
     f32x4 dUp[4];
     E* dUT = a.dUT + chunk * BLK * DV;
 #pragma unroll

@@ -511,9 +511,11 @@ __device__ __forceinline__ void store_state_sel(E* h, const Frag<E> (&fs)[DK / 3
 // 8-byte writes and eight transposing reads per block, no matrix-core work on
 // the recurrence's chain; fp32 states take the selector path.  Measured per
 // 2048-token chunk: with three producer waves (KDA's scans) this path is the
-// faster one (pair scan 42.2 -> 39.2 us), with seven (the Gated DeltaNet
-// scans, whose producers keep LDS busier) the selector products are (28.8
-// against 31.5 us).  state_store() picks accordingly.
+// faster one for both halves of the pair scan (42.2 -> 39.2 us); with seven
+// (the Gated DeltaNet pair, whose producers keep LDS busier) it is for the
+// recompute's h (29.1 -> 28.1 us) but not for the reverse scan's dh, where
+// the selector products are (both halves through LDS: 31.5 us).
+// state_store() picks accordingly.
 constexpr int state_tile_bytes(int dk, int es) { return 16 * (dk + 8) * es; }
 template <typename E, int DK, int DV>
 __device__ __forceinline__ void store_state_tr(E* h, const Frag<E> (&fs)[DK / 32], E* tile, int v0, int l) {
@@ -564,7 +566,7 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[D
     if (a.hT) {
         E* hT = a.hT + chunk * DK * DV;
         if constexpr (HNAT) {
-            state_store<E, DK, DV, PCD>(hT, fs, tile, 16 * vb, l);
+            state_store<E, DK, DV, true>(hT, fs, tile, 16 * vb, l);  // through LDS in either scan
         } else {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) st8T(hT, vb * KK + kk, l, S[2 * kk], S[2 * kk + 1]);
