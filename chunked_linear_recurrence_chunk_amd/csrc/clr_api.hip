@@ -56,20 +56,22 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     Carver c{base};
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
     GdnWs w{};
+    // Ut, U, dvloc and dU are fp32 (split operands; gdn_kernels.h, "Precision")
     w.gam = (float*)c.take(nb * BLK * 4);
     w.W = c.take(nb * BLK * dk * es);
     w.KhT = c.take(nb * BLK * dk * es);
-    w.UtT = c.take(nb * BLK * dv * es);
+    w.UtT = c.take(nb * BLK * dv * 4);
     w.hT = c.take(nb * dk * dv * es);
-    w.UT = c.take(nb * BLK * dv * es);
+    w.UT = c.take(nb * BLK * dv * 4);
     w.Smid = (float*)c.take((size_t)s->B * s->H * dk * dv * 4);
     if (bwd) {
         w.Rt = (float*)c.take(nb * dk * dv * 4);
         w.WT = c.take(nb * BLK * dk * es);
         w.Kh = c.take(nb * BLK * dk * es);
-        w.dvlT = c.take(nb * BLK * dv * es);
+        w.dvlT = c.take(nb * BLK * dv * 4);
         w.dhT = c.take(nb * dk * dv * es);
-        w.dUT = c.take(nb * BLK * dv * es);
+        if (es == 2) w.dhT_lo = c.take(nb * dk * dv * es);  // the lo part of dh (bf16 pair)
+        w.dUT = c.take(nb * BLK * dv * 4);
         w.TT = c.take(nb * BLK * BLK * es);
         w.KKG = (float*)c.take(nb * BLK * BLK * 4);
     }

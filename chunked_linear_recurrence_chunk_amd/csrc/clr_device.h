@@ -158,6 +158,64 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // ---------------------------------------------------------------------------
+// Split operands.  An fp32 value x is carried into a bf16 product as the pair
+// hi = bf16(x), lo = bf16(x - hi): hi + lo holds about 16 significant bits,
+// and a product with a bf16 operand b is hi*b + lo*b (two matrix-core
+// instructions, fp32 accumulation).  With two split operands the lo*lo term,
+// below 2^-16 relative, is left out.  Used where the block form of the delta
+// rule cancels: with repeated keys and beta near 1, the new values U of one
+// key telescope within a block, so a rounding of U (or of T, or of the
+// adjoints that T multiplies) of one bf16 ulp is amplified in the sums over
+// tokens.  fp32 elements are not split (Frag2<float> is one fragment).
+// ---------------------------------------------------------------------------
+template <typename E> struct Frag2;
+template <> struct Frag2<bf16> { Frag<bf16> hi, lo; };
+template <> struct Frag2<float> { Frag<float> hi; };
+
+// From eight fp32 elements in fragment order (i = 0..3 in a, 4..7 in b).
+template <typename E> __device__ __forceinline__ Frag2<E> split8(f32x4 a, f32x4 b);
+template <> __device__ __forceinline__ Frag2<bf16> split8<bf16>(f32x4 a, f32x4 b) {
+    Frag2<bf16> x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16 ha = (bf16)a[i], hb = (bf16)b[i];
+        x.hi.v[i] = ha;
+        x.hi.v[4 + i] = hb;
+        x.lo.v[i] = (bf16)(a[i] - (float)ha);
+        x.lo.v[4 + i] = (bf16)(b[i] - (float)hb);
+    }
+    return x;
+}
+template <> __device__ __forceinline__ Frag2<float> split8<float>(f32x4 a, f32x4 b) {
+    Frag2<float> x;
+    x.hi.lo = a;
+    x.hi.hi = b;
+    return x;
+}
+// Split B fragment (or transposed A fragment) from two vertically adjacent
+// fp32 accumulator tiles, as frag_from_acc.
+template <typename E> __device__ __forceinline__ Frag2<E> split_acc(f32x4 lo, f32x4 hi) { return split8<E>(lo, hi); }
+// Split fragment from an fp32 fragment (e.g. read from tiled fp32 storage).
+template <typename E> __device__ __forceinline__ Frag2<E> split_frag(const Frag<float>& f) { return split8<E>(f.lo, f.hi); }
+
+__device__ __forceinline__ void mma2(f32x4& acc, const Frag2<bf16>& a, const Frag<bf16>& b) {
+    mma(acc, a.hi, b);
+    mma(acc, a.lo, b);
+}
+__device__ __forceinline__ void mma2(f32x4& acc, const Frag<bf16>& a, const Frag2<bf16>& b) {
+    mma(acc, a, b.hi);
+    mma(acc, a, b.lo);
+}
+__device__ __forceinline__ void mma2(f32x4& acc, const Frag2<bf16>& a, const Frag2<bf16>& b) {
+    mma(acc, a.hi, b.hi);
+    mma(acc, a.hi, b.lo);
+    mma(acc, a.lo, b.hi);
+}
+__device__ __forceinline__ void mma2(f32x4& acc, const Frag2<float>& a, const Frag<float>& b) { mma(acc, a.hi, b); }
+__device__ __forceinline__ void mma2(f32x4& acc, const Frag<float>& a, const Frag2<float>& b) { mma(acc, a, b.hi); }
+__device__ __forceinline__ void mma2(f32x4& acc, const Frag2<float>& a, const Frag2<float>& b) { mma(acc, a.hi, b.hi); }
+
+// ---------------------------------------------------------------------------
 // Fragment-packed ("kmap-32") order.  Within every aligned group of 32
 // indices, index kmap(g, i) is stored at position 8g + i, so the eight
 // elements of one lane's fragment are contiguous (one 16-byte load for bf16).
@@ -396,6 +454,49 @@ __device__ __forceinline__ void store_untiled(const TiledRegs<E, R, C, NT>& x, E
         }
     }
 }
+
+// Tiled fp32 global X[R][C] (loaded with load_tiled<float, ...>) -> row-major
+// LDS in the element type E, split: hi[r * P + c] = E(X[r][c]) and, for bf16,
+// lo[r * P + c] = bf16(X[r][c] - hi).  For E = float only hi is written.
+template <typename E, int R, int C, int P, int NT = 256>
+__device__ __forceinline__ void store_untiled_split(const TiledRegs<float, R, C, NT>& x, E* hi, E* lo) {
+#pragma unroll
+    for (int j = 0; j < x.N; ++j) {
+        const int u = threadIdx.x + NT * j;
+        if (u >= x.UNITS) continue;
+        const int f = u >> 7, half = (u >> 6) & 1, lane = u & 63;
+        const int row = 16 * (f / (C / 32)) + (lane & 15), c = 32 * (f % (C / 32)) + 16 * half + 4 * (lane >> 4);
+        const f32x4 v = *(const f32x4*)&x.u[j];
+        if constexpr (sizeof(E) == 2) {
+            bf16x4 h, o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                h[i] = (bf16)v[i];
+                o[i] = (bf16)(v[i] - (float)h[i]);
+            }
+            *(bf16x4*)(hi + row * P + c) = h;
+            *(bf16x4*)(lo + row * P + c) = o;
+        } else {
+            *(f32x4*)(hi + row * P + c) = v;
+        }
+    }
+}
+
+// Split fragments of a matrix staged as a (hi, lo) pair of LDS tiles: the
+// row-major read of ldfrag and the transposing read of ldfrag_tr.
+__device__ __forceinline__ Frag2<bf16> ldfrag2(const bf16* hi, const bf16* lo) { return Frag2<bf16>{ldfrag(hi), ldfrag(lo)}; }
+__device__ __forceinline__ Frag2<float> ldfrag2(const float* hi, const float*) { return Frag2<float>{ldfrag(hi)}; }
+__device__ __forceinline__ Frag2<bf16> ldfrag_tr2(const bf16* hi, const bf16* lo, int P, int k0, int n0, int l) {
+    return Frag2<bf16>{ldfrag_tr(hi, P, k0, n0, l), ldfrag_tr(lo, P, k0, n0, l)};
+}
+__device__ __forceinline__ Frag2<float> ldfrag_tr2(const float* hi, const float*, int P, int k0, int n0, int l) {
+    return Frag2<float>{ldfrag_tr(hi, P, k0, n0, l)};
+}
+// Split fragment f of a matrix stored tiled as a (hi, lo) pair (lo unused for fp32).
+__device__ __forceinline__ Frag2<bf16> ldfragT2(const bf16* hi, const bf16* lo, int f, int l) {
+    return Frag2<bf16>{ldfragT(hi, f, l), ldfragT(lo, f, l)};
+}
+__device__ __forceinline__ Frag2<float> ldfragT2(const float* hi, const float*, int f, int l) { return Frag2<float>{ldfragT(hi, f, l)}; }
 
 // Accumulator-tiled fp32 storage of an [M][N] matrix: the 16 x 16 tile
 // (mb, nb) is 1 KB in lane order, lane l = 16g + r holding rows 16 mb + 4g + i

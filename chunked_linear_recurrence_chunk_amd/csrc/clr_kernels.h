@@ -23,11 +23,14 @@ namespace clr {
 
 // Workspace of the Gated DeltaNet path.  Block-major: index
 // ((b * H + h) * NC + n) selects the 64-token block n of head h in batch b.
+// Gated DeltaNet: UtT, UT, dvlT and dUT are fp32 (see gdn_kernels.h,
+// "Precision"); KhT / Kh hold the keys themselves.  KDA: the input type, and
+// KhT / Kh the per-channel decayed keys.
 struct GdnWs {
     float* gam;   // [.., 64]       in-block cumulative log gate
     void* W;      // [.., 64, dk]   W = T Diag(beta Gam) K           (token-major)
-    void* KhT;    // [.., dk, 64]   (Diag(exp(gamma_C - gamma)) K)^T
-    void* UtT;    // [.., dv, 64]   (T Diag(beta) V)^T
+    void* KhT;    // [.., dk, 64]   K^T (GDN), (K * exp(b_C - b))^T (KDA)
+    void* UtT;    // [.., dv, 64]   -(T Diag(beta) V)^T
     void* hT;     // [.., dv, dk]   state entering the block, transposed
     void* UT;     // [.., dv, 64]   U^T (delta-rule new values)
     float* Smid;  // [B, H, dk, dv] state at the split point of a split forward
@@ -37,9 +40,10 @@ struct GdnWs {
     // backward only
     float* Rt;    // [.., dv, dk]   R^T, R = (Diag(Gam) Q)^T dO - W^T dvloc  (fp32)
     void* WT;     // [.., dk, 64]   W^T
-    void* Kh;     // [.., 64, dk]   Diag(exp(gamma_C - gamma)) K      (token-major)
+    void* Kh;     // [.., 64, dk]   K (GDN), K * exp(b_C - b) (KDA)   (token-major)
     void* dvlT;   // [.., dv, 64]   dvloc^T, dvloc = (Q K^T * G * tril)^T dO
-    void* dhT;    // [.., dv, dk]   gradient w.r.t. the state leaving the block, transposed
+    void* dhT;    // [.., dk, dv]   gradient w.r.t. the state leaving the block (GDN: bf16 hi part)
+    void* dhT_lo; // [.., dk, dv]   GDN, bf16 inputs: the lo part of that gradient
     void* dUT;    // [.., dv, 64]   dU^T
     void* TT;     // [.., 64, 64]   T^T (tiled), T = (I + A)^-1
     float* KKG;   // [.., 16, 256]  K K^T * G, strictly lower, accumulator tiles (rb, cb) at (4 rb + cb) * 256
@@ -68,7 +72,8 @@ template <typename E> struct GdnPrepArgs {
     const E *k, *v, *g, *beta;
     int T, H, NC;
     float* gam;
-    E *W, *KhT, *UtT;
+    E *W, *KhT;
+    float* UtT;
     int n0 = 0;  // first block of the launch (grid x covers blocks n0 ..)
     // backward only (nullable): T^T (tiled [s][t]) and the decayed Gram
     // product K K^T * G (strictly lower, fp32, 16 accumulator tiles)
@@ -76,16 +81,20 @@ template <typename E> struct GdnPrepArgs {
     float* KKG = nullptr;
     // backward only: the reverse scan's operands (q, dO in; W^T, Kh, dvloc^T, R out)
     const E *q = nullptr, *dO = nullptr;
-    E *WT = nullptr, *Kh = nullptr, *dvlT = nullptr;
+    E *WT = nullptr, *Kh = nullptr;
+    float* dvlT = nullptr;
     float* Rt = nullptr;
 };
 
+// UtT and UT are fp32 for the Gated DeltaNet scans and of type E for KDA's.
 template <typename E> struct GdnScanArgs {
     const float* gam;
-    const E *W, *KhT, *UtT;
+    const E *W, *KhT;
+    const void* UtT;
     const float* S_in;
     float* S_out;
-    E *hT, *UT;
+    E* hT;
+    void* UT;
     int H, NC, BH;
     int n0 = 0, n1 = 1 << 30;  // blocks [n0, min(n1, NC)) are scanned
     // per-channel decay (KDA): exp(b_C) per block, padded to 256 floats, and
@@ -98,7 +107,8 @@ template <typename E> struct GdnScanArgs {
 template <typename E> struct GdnOutArgs {
     const E *q, *k;
     const float* gam;
-    const E *hT, *UT;
+    const E* hT;
+    const float* UT;
     E* o;
     int T, H, NC;
     int n0 = 0;  // first block of the launch

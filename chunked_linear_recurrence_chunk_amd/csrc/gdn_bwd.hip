@@ -9,27 +9,29 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GdnWs& ws = L.ws;
     GdnPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
-                      ws.gam, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
+                      ws.gam, (E*)ws.W, (E*)ws.KhT, (float*)ws.UtT};
     pa.TT = (E*)ws.TT;
     pa.KKG = ws.KKG;
     pa.q = (const E*)L.q;
     pa.dO = (const E*)L.dO;
     pa.WT = (E*)ws.WT;
     pa.Kh = (E*)ws.Kh;
-    pa.dvlT = (E*)ws.dvlT;
+    pa.dvlT = (float*)ws.dvlT;
     pa.Rt = ws.Rt;
     launch("gdn_prep_bwd", gdn_prep_kernel<E, DK, DV, true>, gblk, dim3(512), st, pa);
     GdnScanArgs<E> sa{ws.gam, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, (E*)ws.UT, L.H, L.NC, L.B * L.H};
     GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
-                         L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC, L.B * L.H};
+                         L.dS_out, L.dS_in, (E*)ws.dhT, ws.dUT, L.H, L.NC, L.B * L.H};
+    sb.dh_lo = (E*)ws.dhT_lo;
     const int G = (int)scan_grid(DV / 16, L.B * L.H);
     launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV, false, SCAN_NP_FAST>, dim3(2 * G),
            dim3(scan_threads<SCAN_NP_FAST>), st, sa, sb, G);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
-                       ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const E*)ws.dUT,
+                       ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const float*)ws.UT, (const float*)ws.dUT,
                        (const E*)ws.TT, ws.KKG,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};
+    ia.dh_lo = (const E*)ws.dhT_lo;
     launch("gdn_bwd_intra", gdn_bwd_intra_kernel<E, DK, DV>, gblk, dim3(512), st, ia);
     return hipGetLastError();
 }

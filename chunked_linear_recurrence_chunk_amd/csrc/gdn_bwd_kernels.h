@@ -38,25 +38,32 @@
 
 namespace clr {
 
+// dvlT and dUT are fp32 for the Gated DeltaNet scan (of type E for KDA's), and
+// its dh is stored as a bf16 hi/lo pair (dh, dh_lo) for bf16 inputs.
 template <typename E> struct GdnScanBwdArgs {
     const float* gam;
-    const E *Kh, *WT, *dvlT;
+    const E *Kh, *WT;
+    const void* dvlT;
     const float* Rt;
     const float* dS_out;
     float* dS_in;
-    E *dh, *dUT;
+    E* dh;
+    void* dUT;
     int H, NC, BH;
     const float* eC = nullptr;  // per-channel decay (KDA): exp(b_C) per block, padded to 256 floats
+    E* dh_lo = nullptr;
 };
 
 template <typename E> struct GdnIntraArgs {
     const E *q, *k, *v, *beta, *dO;
     const float* gam;
-    const E *h, *dh, *UT, *dUT;
+    const E *h, *dh;
+    const float *UT, *dUT;
     const E* TT;        // T^T per block (tiled), from the prep
     const float* KKG;   // K K^T * G per block (accumulator tiles), from the prep
     E *dq, *dk, *dv, *dg, *dbeta;
     int T, H, NC;
+    const E* dh_lo = nullptr;  // bf16 inputs: lo part of dh
 };
 
 // ---------------------------------------------------------------------------
@@ -64,29 +71,33 @@ template <typename E> struct GdnIntraArgs {
 // reverse.  Wave 0 runs the reverse recurrence with dS in accumulator tiles;
 // the other waves stream the operands of the next blocks into the LDS ring
 // (clr_ring.h).  Ring unit u of a block is the contiguous 1-KB run u of
-// [Kh | W^T | R tiles (., vb) | dvloc^T fragments (vb, 0..1)], all tiled.
+// [K (Kh) | W^T | R tiles (., vb) | dvloc^T fragments (vb, 0..1)], all tiled;
+// the small unit holds gamma (exp(b_C) per channel in a last unit for KDA).
 // ---------------------------------------------------------------------------
-template <typename E, int DK> struct ScanBwdOps {
-    Frag<E> kh[4][DK / 32];   // Kh rows (A: m = t, k = d)
+template <typename E, int DK, typename UE = E> struct ScanBwdOps {
+    Frag<E> kh[4][DK / 32];   // K (GDN) or Kh (KDA) rows (A: m = t, k = d)
     Frag<E> wt[DK / 16][2];   // W^T rows (A: m = d, k = t)
     f32x4 rt[DK / 16];        // R accumulator tiles (rows d, column v0 + r)
-    Frag<E> dvl[2];           // dvloc^T[v0 + r][token tile pairs] (accumulator layout)
+    Frag<UE> dvl[2];          // dvloc^T[v0 + r][token tile pairs] (accumulator layout)
     float gC;
 };
 
 // With PCD (per-channel decay, KDA) a last unit holds exp(b_C) for every key
-// channel (fp32, 256 floats).
+// channel (fp32, 256 floats).  dvloc is fp32 (two units per fragment) for the
+// Gated DeltaNet scan.
 template <typename E, int DK, bool PCD = false> struct ScanBwdRing {
     static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;
+    static constexpr int UPFU = sizeof(ScanWsT<PCD, E>) == 2 ? 1 : 2;
     static constexpr int KK = DK / 32, ND = DK / 16;
-    static constexpr int NKU = 4 * KK * UPF, NWU = 2 * ND * UPF, NRU = ND, NDU = 2 * UPF;
+    static constexpr int NKU = 4 * KK * UPF, NWU = 2 * ND * UPF, NRU = ND, NDU = 2 * UPFU;
     static constexpr int NU = NKU + NWU + NRU + NDU + (PCD ? 1 : 0);
 };
 
-template <typename E, int DK, int NU>
-__device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK>& o, const char* slot, int l) {
-    using Rg = ScanBwdRing<E, DK>;
-    constexpr int KK = DK / 32, UPF = Rg::UPF;
+template <typename E, int DK, int NU, bool PCD>
+__device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK, ScanWsT<PCD, E>>& o, const char* slot, int l) {
+    using Rg = ScanBwdRing<E, DK, PCD>;
+    using UE = ScanWsT<PCD, E>;
+    constexpr int KK = DK / 32, UPF = Rg::UPF, UPFU = Rg::UPFU;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -97,39 +108,72 @@ __device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK>& o, const c
         for (int j = 0; j < 2; ++j) o.wt[db][j] = ring_frag(slot, Rg::NKU / UPF + 2 * db + j, l, (E*)nullptr);
         o.rt[db] = *(const f32x4*)(slot + (Rg::NKU + Rg::NWU + db) * RING_UNIT + l * 16);
     }
-    // dvloc fragments start at unit NKU + NWU + NRU, i.e. fragment index (that) / UPF
-    static_assert((Rg::NKU + Rg::NWU + Rg::NRU) % UPF == 0, "fragment alignment");
+    // dvloc fragments start at unit NKU + NWU + NRU, i.e. fragment index (that) / UPFU
+    static_assert((Rg::NKU + Rg::NWU + Rg::NRU) % UPFU == 0, "fragment alignment");
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-        o.dvl[j] = ring_frag(slot, (Rg::NKU + Rg::NWU + Rg::NRU) / UPF + j, l, (E*)nullptr);
+        o.dvl[j] = ring_frag(slot, (Rg::NKU + Rg::NWU + Rg::NRU) / UPFU + j, l, (UE*)nullptr);
     o.gC = ring_small<NU>(slot, BLK - 1);
 }
 
 // One reverse step: on entry dS = dL/dS_{n+1}; writes dh_n = dS and
 // dU_n = dvloc_n + Kh_n dS; leaves dS = dL/dS_n = Gam_C dS + R_n - W_n^T (Kh_n dS).
+// Gated DeltaNet: Kh_n dS = Diag(e) (K_n dS) with e_t = exp(gamma_C - gamma_t)
+// and dS split (the operand of a product whose rows telescope over repeated
+// keys), dU fp32, dh stored as a bf16 hi/lo pair.
 template <typename E, int DK, int DV, int NU = 0, bool PCD = false>
-__device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK>& o, f32x4 (&dS)[DK / 16],
+__device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PCD, E>>& o, f32x4 (&dS)[DK / 16],
                                               const GdnScanBwdArgs<E>& a, size_t chunk, int vb, int l, E* tile,
                                               const char* slot = nullptr) {
-    constexpr int ND = DK / 16;
-    Frag<E> fs[DK / 32];
-#pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
-    state_store<E, DK, DV, PCD>(a.dh + chunk * DK * DV, fs, tile, 16 * vb, l);  // selector with seven producers
+    constexpr int ND = DK / 16, KK = DK / 32;
+    using UE = ScanWsT<PCD, E>;
     f32x4 dUp[4];
-    E* dUT = a.dUT + chunk * BLK * DV;
+    if constexpr (PCD) {
+        Frag<E> fs[KK];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = zero4();
+        for (int kk = 0; kk < KK; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+        state_store<E, DK, DV, PCD>(a.dh + chunk * DK * DV, fs, tile, 16 * vb, l);
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) mma(acc, o.kh[tb][kk], fs[kk]);
-        dUp[tb] = acc;
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) mma(acc, o.kh[tb][kk], fs[kk]);
+            dUp[tb] = acc;
+        }
+    } else {
+        Frag2<E> fs[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) fs[kk] = split_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+        {
+            Frag<E> fh[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) fh[kk] = fs[kk].hi;
+            state_store<E, DK, DV, false>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);  // selector products
+        }
+        if constexpr (sizeof(E) == 2) {
+            Frag<E> fl[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) fl[kk] = fs[kk].lo;
+            state_store<E, DK, DV, false>(a.dh_lo + chunk * DK * DV, fl, tile, 16 * vb, l);
+        }
+        const float* gsm = (const float*)(slot + NU * RING_UNIT) + 4 * (l >> 4);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) mma2(acc, o.kh[tb][kk], fs[kk]);
+            const f32x4 gt = *(const f32x4*)(gsm + 16 * tb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= __expf(o.gC - gt[i]);
+            dUp[tb] = acc;
+        }
     }
+    UE* dUT = (UE*)a.dUT + chunk * BLK * DV;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const Frag<E>& f = o.dvl[j];
+        const Frag<UE>& f = o.dvl[j];
         f32x4 lo, hi;
-        if constexpr (sizeof(E) == 2) {
+        if constexpr (sizeof(UE) == 2) {
             lo = f32x4{(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]};
             hi = f32x4{(float)f.v[4], (float)f.v[5], (float)f.v[6], (float)f.v[7]};
         } else {
@@ -174,7 +218,8 @@ __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, in
     constexpr int ND = DK / 16;
     using Rg = ScanBwdRing<E, DK, PCD>;
     using SG = ScanBwdGeom<E, DK, PCD>;
-    constexpr int NU = Rg::NU, UPF = Rg::UPF, P = SG::P;
+    using UT_ = ScanWsT<PCD, E>;
+    constexpr int NU = Rg::NU, UPFU = Rg::UPFU, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
     using G = RingGeom<NU, NP>;
     char* ring = smem;
@@ -189,13 +234,14 @@ __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, in
             const E* Kh = a.Kh + c * BLK * DK + l * LE;
             const E* WT = a.WT + c * BLK * DK + l * LE;
             const float* Rt = a.Rt + c * DK * DV + (size_t)vb * ND * 256 + l * 4;
-            const E* dvl = a.dvlT + c * BLK * DV + (size_t)(2 * vb * UPF) * UE + l * LE;
+            const UT_* dvl = (const UT_*)a.dvlT + c * BLK * DV + (size_t)(2 * vb * UPFU) * UNIT_ELEMS<UT_> +
+                             l * LANE_ELEMS<UT_>;
             auto src = [&](int u) -> const void* {
                 if (u < Rg::NKU) return Kh + u * UE;
                 if (u < Rg::NKU + Rg::NWU) return WT + (u - Rg::NKU) * UE;
                 if (u < Rg::NKU + Rg::NWU + Rg::NRU) return Rt + (u - Rg::NKU - Rg::NWU) * 256;
                 if (PCD && u == NU - 1) return a.eC + c * 256 + l * 4;
-                return dvl + (u - Rg::NKU - Rg::NWU - Rg::NRU) * UE;
+                return dvl + (u - Rg::NKU - Rg::NWU - Rg::NRU) * UNIT_ELEMS<UT_>;
             };
             ring_issue<NU, decltype(src), NP>(ring + (m % P) * G::SLOT, pid, src,
                                               PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.gam + c * BLK + l));
@@ -221,9 +267,9 @@ __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, in
         for (int i = 0; i < 4; ++i) dS[db][i] = dSo ? dSo[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
     ring_barrier();
     for (int m = 0; m < NC; ++m) {
-        ScanBwdOps<E, DK> o;
+        ScanBwdOps<E, DK, UT_> o;
         const char* slot = ring + (m % P) * G::SLOT;
-        scan_bwd_from_ring<E, DK, NU>(o, slot, l);
+        scan_bwd_from_ring<E, DK, NU, PCD>(o, slot, l);
         scan_bwd_step<E, DK, DV, NU, PCD>(o, dS, a, bh * NC + (NC - 1 - m), vb, l, tile, slot);
         ring_barrier();
     }
@@ -254,21 +300,26 @@ __global__ __launch_bounds__(scan_threads<NP>) void gdn_scan_pair_kernel(GdnScan
 // that contract over the other index read the tiles transposed (ldfrag_tr).
 // The tiled h_n / dh_n fragments are read from global memory one 16-row
 // block ahead of their use.
+// U and dU (fp32 in the workspace) are staged as bf16 hi/lo pairs, dh_n is read
+// as its stored pair, and dPm is split: the products that carry them sum over
+// tokens whose terms telescope with repeated keys (gdn_kernels.h, "Precision").
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV> struct IntraLds {
     static constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
+    static constexpr size_t LO = sizeof(E) == 2 ? 1 : 0;  // lo parts (bf16 only)
     // persistent
     static constexpr size_t o_Ks = 0;                                  // E[64][PK]     K
     static constexpr size_t o_TT = o_Ks + sizeof(E) * BLK * PK;        // E[64][PT]     TT[s][t] = T[t][s]
     static constexpr size_t o_E = o_TT + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms), + 512 spare
     static constexpr size_t o_U = o_E + 4 * (BLK * 65 + 512);          // union starts here
     static constexpr size_t p0_end = o_U;
-    // phase A: Qs E[64][PK], dOs E[64][PV], UTs E[DV][PT]
+    // phase A: Qs E[64][PK], dOs E[64][PV], UTs E[DV][PT] (hi, lo)
     static constexpr size_t pA_Q = o_U, pA_dO = pA_Q + sizeof(E) * BLK * PK;
-    static constexpr size_t pA_UT = pA_dO + sizeof(E) * BLK * PV;
-    static constexpr size_t pA_end = pA_UT + sizeof(E) * DV * PT;
-    // phase B: dUTs E[DV][PT], dWs E[64][PK], dTT E[64][PT], Ms E[64][PT], Vs E[64][PV]
-    static constexpr size_t pB_dUT = o_U, pB_dW = pB_dUT + sizeof(E) * DV * PT;
+    static constexpr size_t pA_UT = pA_dO + sizeof(E) * BLK * PV, pA_UTl = pA_UT + sizeof(E) * DV * PT;
+    static constexpr size_t pA_end = pA_UTl + LO * sizeof(E) * DV * PT;
+    // phase B: dUTs E[DV][PT] (hi, lo), dWs E[64][PK], dTT E[64][PT], Ms E[64][PT], Vs E[64][PV]
+    static constexpr size_t pB_dUT = o_U, pB_dUTl = pB_dUT + sizeof(E) * DV * PT;
+    static constexpr size_t pB_dW = pB_dUTl + LO * sizeof(E) * DV * PT;
     static constexpr size_t pB_dTT = pB_dW + sizeof(E) * BLK * PK;
     static constexpr size_t pB_Ms = pB_dTT + sizeof(E) * BLK * PT;
     static constexpr size_t pB_V = pB_Ms + sizeof(E) * BLK * PT;
@@ -283,7 +334,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     constexpr int NT = 512;
     constexpr int PK = Lay::PK, PV = Lay::PV, KK = DK / 32, KV = DV / 32, ND = DK / 16, NDH = ND / 2;
     constexpr int NVH = DV / 32;  // value blocks per half
-    static_assert(Lay::total <= 150 * 1024, "LDS budget");
+    static_assert(Lay::total <= 154 * 1024, "LDS budget");
     __shared__ __align__(16) char lds[Lay::total];
     E* Ks = (E*)(lds + Lay::o_Ks);
     E* TT = (E*)(lds + Lay::o_TT);
@@ -307,15 +358,16 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     const E* vbase = a.v + tok0 * ldv + (size_t)h * DV;
     const E* dob = a.dO + tok0 * ldv + (size_t)h * DV;
     const E* S0 = a.h + chunk * DK * DV;   // h_n  [d][v], tiled
-    const E* dS1 = a.dh + chunk * DK * DV; // dh_n [d][v], tiled
-    const E* UT = a.UT + chunk * BLK * DV;
-    const E* dUT = a.dUT + chunk * BLK * DV;
+    const E* dS1 = a.dh + chunk * DK * DV; // dh_n [d][v], tiled (bf16: hi part)
+    const E* dS1l = a.dh_lo ? a.dh_lo + chunk * DK * DV : nullptr;  // lo part
+    const float* UT = a.UT + chunk * BLK * DV;
+    const float* dUT = a.dUT + chunk * BLK * DV;
 
     // ---------------- phase 0: gates, K, T (from the prep) -------------------
     const auto kx = load_rows<E, BLK, DK, NT>(kb, ldk, nvalid);
     const auto qx = load_rows<E, BLK, DK, NT>(qb, ldk, nvalid);
     const auto ox = load_rows<E, BLK, DV, NT>(dob, ldv, nvalid);
-    const auto ux = load_tiled<E, DV, BLK, NT>(UT);
+    const auto ux = load_tiled<float, DV, BLK, NT>(UT);
     const auto tx = load_tiled<E, BLK, BLK, NT>(a.TT + chunk * BLK * BLK);
     if (tid < BLK) {
         s_gam[tid] = a.gam[chunk * BLK + tid];
@@ -328,22 +380,24 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     E* Qs = (E*)(lds + Lay::pA_Q);
     E* dOs = (E*)(lds + Lay::pA_dO);
     E* UTs = (E*)(lds + Lay::pA_UT);
+    E* UTl = (E*)(lds + Lay::pA_UTl);
     // phase B operands: in flight during phase A
     const auto vx = load_rows<E, BLK, DV, NT>(vbase, ldv, nvalid);
-    const auto dux = load_tiled<E, DV, BLK, NT>(dUT);
+    const auto dux = load_tiled<float, DV, BLK, NT>(dUT);
     store_rows<E, BLK, DK, PK, NT>(qx, Qs);
     store_rows<E, BLK, DV, PV, NT>(ox, dOs);
-    store_untiled<E, DV, BLK, PT, NT>(ux, UTs);
+    store_untiled_split<E, DV, BLK, PT, NT>(ux, UTs, UTl);
     __syncthreads();
 
     const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
     const float gam_tw = s_gam[tw];
     const float gC = s_gam[BLK - 1];
-    Frag<E> fdo[KV], fU[KV];
+    Frag<E> fdo[KV];
+    Frag2<E> fU[KV];
 #pragma unroll
     for (int kk = 0; kk < KV; ++kk) {
-        fdo[kk] = ldfrag(dOs + tw * PV + 32 * kk + 4 * g);    // Bt = dO[t][v], rows of block w
-        fU[kk] = ldfrag_tr(UTs, PT, 32 * kk, 16 * w, l);     // Bt = U[s][v], rows of block w
+        fdo[kk] = ldfrag(dOs + tw * PV + 32 * kk + 4 * g);       // Bt = dO[t][v], rows of block w
+        fU[kk] = ldfrag_tr2(UTs, UTl, PT, 32 * kk, 16 * w, l);  // Bt = U[s][v], rows of block w
     }
     // dPm^T[sb][w]: rows s, cols t = tw
     f32x4 dPT[4];
@@ -352,7 +406,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         f32x4 acc = zero4();
         if (sb <= w) {
 #pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag_tr(UTs, PT, 32 * kk, 16 * sb, l), fdo[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma2(acc, ldfrag_tr2(UTs, UTl, PT, 32 * kk, 16 * sb, l), fdo[kk]);
             const f32x4 gs = ld4_now(s_gam + 16 * sb + 4 * g);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -387,7 +441,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         f32x4 acc = zero4();
         if (tb >= w) {
 #pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag(dOs + (16 * tb + r) * PV + 32 * kk + 4 * g), fU[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma2(acc, ldfrag(dOs + (16 * tb + r) * PV + 32 * kk + 4 * g), fU[kk]);
             const f32x4 gt = ld4_now(s_gam + 16 * tb + 4 * g);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -404,18 +458,19 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     //   <h_n, dh_n>, each wave summing one block in four.
     f32x4 dKT[NDH];
     {
-        Frag<E> fpt[2], fpm[2];
-        fpt[0] = frag_from_acc<E>(dPT[0], dPT[1]);
-        fpt[1] = frag_from_acc<E>(dPT[2], dPT[3]);
-        fpm[0] = frag_from_acc<E>(dP[0], dP[1]);
-        fpm[1] = frag_from_acc<E>(dP[2], dP[3]);
+        Frag2<E> fpt[2], fpm[2];
+        fpt[0] = split_acc<E>(dPT[0], dPT[1]);
+        fpt[1] = split_acc<E>(dPT[2], dPT[3]);
+        fpm[0] = split_acc<E>(dP[0], dP[1]);
+        fpm[1] = split_acc<E>(dP[2], dP[3]);
         const float Gt = __expf(gam_tw), ek = __expf(gC - gam_tw);
         float qdq = 0.f, kdk = 0.f, hdh = 0.f;
-        Frag<E> fh[KV], fd[KV];
+        Frag<E> fh[KV];
+        Frag2<E> fd[KV];
 #pragma unroll
         for (int kk = 0; kk < KV; ++kk) {
             fh[kk] = ldfragT(S0, (hf * NDH) * KV + kk, l);
-            fd[kk] = ldfragT(dS1, (hf * NDH) * KV + kk, l);
+            fd[kk] = ldfragT2(dS1, dS1l, (hf * NDH) * KV + kk, l);
         }
 #pragma unroll
         for (int jd = 0; jd < NDH; ++jd) {
@@ -424,17 +479,19 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
 #pragma unroll
             for (int kk = 0; kk < KV; ++kk) {
                 mma(acc, fh[kk], fdo[kk]);
-                mma(accb, fd[kk], fU[kk]);
+                mma2(accb, fd[kk], fU[kk]);
             }
             if ((jd & 3) == w) {
 #pragma unroll
                 for (int kk = 0; kk < KV; ++kk) {
                     if constexpr (sizeof(E) == 2) {
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) hdh += (float)fh[kk].v[i] * (float)fd[kk].v[i];
+                        for (int i = 0; i < 8; ++i)
+                            hdh += (float)fh[kk].v[i] * ((float)fd[kk].hi.v[i] + (float)fd[kk].lo.v[i]);
                     } else {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) hdh += fh[kk].lo[i] * fd[kk].lo[i] + fh[kk].hi[i] * fd[kk].hi[i];
+                        for (int i = 0; i < 4; ++i)
+                            hdh += fh[kk].lo[i] * fd[kk].hi.lo[i] + fh[kk].hi[i] * fd[kk].hi.hi[i];
                     }
                 }
             }
@@ -442,18 +499,18 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
 #pragma unroll
                 for (int kk = 0; kk < KV; ++kk) {
                     fh[kk] = ldfragT(S0, (db + 1) * KV + kk, l);
-                    fd[kk] = ldfragT(dS1, (db + 1) * KV + kk, l);
+                    fd[kk] = ldfragT2(dS1, dS1l, (db + 1) * KV + kk, l);
                 }
             }
             acc = acc * Gt;
             const f32x4 qv = ld4(Qs + tw * PK + 16 * db + 4 * g);
             qdq += qv[0] * acc[0] + qv[1] * acc[1] + qv[2] * acc[2] + qv[3] * acc[3];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fpt[j]);
+            for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fpt[j]);
             if (tw < nvalid) st4(a.dq + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, acc);
             f32x4 acck = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acck, ldfrag_tr(Qs, PK, 32 * j, 16 * db, l), fpm[j]);
+            for (int j = 0; j < 2; ++j) mma2(acck, ldfrag_tr(Qs, PK, 32 * j, 16 * db, l), fpm[j]);
             const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
             kdk += kv[0] * accb[0] + kv[1] * accb[1] + kv[2] * accb[2] + kv[3] * accb[3];
             dKT[jd] = acck + accb * ek;
@@ -479,18 +536,19 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     for (int u = 0; u < 2; ++u)
         kkgt[u] = *(const f32x4*)(a.KKG + chunk * BLK * BLK + (4 * w + hf + 2 * u) * 256 + l * 4);
     E* dUTs = (E*)(lds + Lay::pB_dUT);
+    E* dUTl = (E*)(lds + Lay::pB_dUTl);
     E* dWs = (E*)(lds + Lay::pB_dW);
     E* dTT = (E*)(lds + Lay::pB_dTT);
     E* Ms = (E*)(lds + Lay::pB_Ms);
     E* Vs = (E*)(lds + Lay::pB_V);
-    store_untiled<E, DV, BLK, PT, NT>(dux, dUTs);
+    store_untiled_split<E, DV, BLK, PT, NT>(dux, dUTs, dUTl);
     store_rows<E, BLK, DV, PV, NT>(vx, Vs);
     __syncthreads();
     // dW^T[db][w] = -(S0 dU^T): rows d, cols t = tw;  stored as dW[t][d]
     {
-        Frag<E> fdu[KV];
+        Frag2<E> fdu[KV];
 #pragma unroll
-        for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr(dUTs, PT, 32 * kk, 16 * w, l);
+        for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr2(dUTs, dUTl, PT, 32 * kk, 16 * w, l);
         Frag<E> fh[KV];
 #pragma unroll
         for (int kk = 0; kk < KV; ++kk) fh[kk] = ldfragT(S0, (hf * NDH) * KV + kk, l);
@@ -499,7 +557,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             const int db = hf * NDH + jd;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(acc, fh[kk], fdu[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma2(acc, fh[kk], fdu[kk]);
             if (jd + 1 < NDH) {
 #pragma unroll
                 for (int kk = 0; kk < KV; ++kk) fh[kk] = ldfragT(S0, (db + 1) * KV + kk, l);
@@ -510,9 +568,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     __syncthreads();
     // dT[w][sb] = beta_s (dU V^T) + beta_s Gam_s (dW K^T): rows t, cols s;  stored as dT^T[s][t]
     {
-        Frag<E> fdu[KV], fdw[KK];
+        Frag2<E> fdu[KV];
+        Frag<E> fdw[KK];
 #pragma unroll
-        for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr(dUTs, PT, 32 * kk, 16 * w, l);
+        for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr2(dUTs, dUTl, PT, 32 * kk, 16 * w, l);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) fdw[kk] = ldfrag(dWs + (16 * w + r) * PK + 32 * kk + 4 * g);
 #pragma unroll
@@ -520,7 +579,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             if ((sb & 1) != hf) continue;
             f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma(a1, fdu[kk], ldfrag(Vs + (16 * sb + r) * PV + 32 * kk + 4 * g));
+            for (int kk = 0; kk < KV; ++kk) mma2(a1, fdu[kk], ldfrag(Vs + (16 * sb + r) * PV + 32 * kk + 4 * g));
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) mma(a2, fdw[kk], ldfrag(Ks + (16 * sb + r) * PK + 32 * kk + 4 * g));
             const int s = 16 * sb + r;
@@ -589,7 +648,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                mma(acc, ldfrag(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
+                mma2(acc, ldfrag2(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g, dUTl + (16 * vb + r) * PT + 32 * j + 4 * g),
+                     ldfrag(TT + tw * PT + 32 * j + 4 * g));
             const f32x4 vv = ld4(Vs + tw * PV + 16 * vb + 4 * g);
             dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
             if (tw < nvalid) st4(a.dv + (tok0 + tw) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc * bet_tw);

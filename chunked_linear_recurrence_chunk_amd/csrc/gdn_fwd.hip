@@ -13,7 +13,7 @@ struct GdnFwdStages {
     const GdnLaunch& L;
     void prep(int n0, int n1, hipStream_t st) const {
         GdnPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
-                          L.ws.gam, (E*)L.ws.W, (E*)L.ws.KhT, (E*)L.ws.UtT};
+                          L.ws.gam, (E*)L.ws.W, (E*)L.ws.KhT, (float*)L.ws.UtT};
         pa.n0 = n0;
         launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, dim3(n1 - n0, L.H, L.B), dim3(512), st, pa);
     }
@@ -26,7 +26,7 @@ struct GdnFwdStages {
                dim3(scan_grid(DV / 16, L.B * L.H)), dim3(scan_threads<SCAN_NP_FAST>), st, sa);
     }
     void out(int n0, int n1, hipStream_t st) const {
-        GdnOutArgs<E> oa{(const E*)L.q, (const E*)L.k, L.ws.gam, (const E*)L.ws.hT, (const E*)L.ws.UT, (E*)L.o,
+        GdnOutArgs<E> oa{(const E*)L.q, (const E*)L.k, L.ws.gam, (const E*)L.ws.hT, (const float*)L.ws.UT, (E*)L.o,
                          L.T, L.H, L.NC};
         oa.n0 = n0;
         launch("gdn_out", gdn_out_kernel<E, DK, DV>, dim3(n1 - n0, L.H, L.B), dim3(256), st, oa);

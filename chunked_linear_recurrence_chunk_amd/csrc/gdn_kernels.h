@@ -11,16 +11,28 @@
 //   prep  (Pre, parallel over blocks):  gamma = cumsum(g), the UT transform
 //         T = (I + Diag(beta) strict_lower(K K^T * G))^-1 and the WY pair
 //         W = T Diag(beta Gam) K, Ut = T Diag(beta) V   (Gam = exp(gamma),
-//         G[r,s] = exp(gamma_r - gamma_s)); also Kh^T = (Diag(exp(gamma_C - gamma)) K)^T.
+//         G[r,s] = exp(gamma_r - gamma_s)); also K^T.
 //   scan  (ST, sequential over blocks, parallel over heads x 16-wide value
-//         slices): h_n = S;  U_n = Ut_n - W_n S;  S <- Gam_C S + Kh_n^T U_n.
+//         slices): h_n = S;  U_n = Ut_n - W_n S;  S <- Gam_C S + K_n^T (e * U_n),
+//         e_t = exp(gamma_C - gamma_t)  (so S_C gains Kh^T U, Kh = Diag(e) K).
 //   out   (Out, parallel over blocks):  O = Diag(Gam) Q h_n + (Q K^T * G * tril) U_n.
 //
 // U_n is the delta rule's "new value" V^new of Eq. 2.  Every per-block matrix
-// in the workspace (W, Kh^T, Ut^T, the saved states, U^T) is kept in the tiled
+// in the workspace (W, K^T, Ut^T, the saved states, U^T) is kept in the tiled
 // fragment-major layout of clr_device.h, so that each wave moves whole 1-KB
 // runs straight into (or out of) matrix-core fragments.
+//
+// Precision.  Inputs, W, K^T and the saved states h_n are in the input type;
+// T, Ut and U are fp32, and enter bf16 products as hi/lo pairs (split
+// operands, clr_device.h).  With repeated keys and beta near 1 the writes of
+// one key within a block nearly cancel (U telescopes), so one bf16 rounding of
+// T, Ut or U per token grows in the sums over tokens; and a rounded decayed key
+// Diag(e) K would add components outside the span of the keys, which a state
+// that hardly decays keeps.  The scan therefore multiplies the exact keys by
+// the fp32 e * U, and rounds nothing that T multiplies to a single bf16.
 #pragma once
+
+#include <type_traits>
 
 #include "clr_kernels.h"
 #include "clr_ring.h"
@@ -159,12 +171,12 @@ __device__ __forceinline__ void st_fragT(float* base, int f, int l, const Frag<f
 //
 // With BWD it also does the dS-independent part of the backward for the
 // block (the reverse scan's operands) from the same staged tiles:
-//   W^T and Kh = Diag(exp(gamma_C - gamma)) K (tiled),
+//   W^T and K (tiled),
 //   dvloc = P^T dO,  P[t][s] = (q_t . k_s) exp(gamma_t - gamma_s)  (s <= t),
 //   R = (Diag(Gam) Q)^T dO - W^T dvloc = Z^T dO,  Z = Diag(Gam) Q - P W,
 // and writes T^T and K K^T * G for the block adjoints.  The LDS regions of
 // the first part are reused by the second:
-//   [Ks | Vs -> Qs | Am -> Ws | Td | T1, T2 -> dOs],  P^T over Ks (or after
+//   [Ks | Vs -> Qs | Am -> Ws | Td | T (fp32) -> dOs],  P^T over Ks (or after
 //   the last region when it does not fit there).
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV> struct PrepLds {
@@ -176,6 +188,8 @@ template <typename E, int DK, int DV> struct PrepLds {
     static constexpr bool P_OVER_K = sizeof(E) * BLK * PT <= sizeof(E) * BLK * PK;
     static constexpr size_t o_P = P_OVER_K ? o_K : end1;
     static constexpr size_t total = P_OVER_K ? end1 : end1 + sizeof(E) * BLK * PT;
+    // T (fp32, row pitch AP) is kept where T1 and T2 were
+    static_assert((size_t)4 * BLK * AP <= end1 - o_T1, "fp32 T fits the T1, T2 regions");
     // the backward's second part fits the regions of the first
     static constexpr bool BWD_FITS = DK == DV && sizeof(E) * BLK * PK <= 4 * BLK * AP &&
                                      sizeof(E) * BLK * PV <= 2 * sizeof(E) * BLK * PT;
@@ -195,14 +209,12 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     using Lay = PrepLds<E, DK, DV>;
     constexpr int PK = Lay::PK, PV = Lay::PV, ND = DK / 16, KK = DK / 32;
 
-    __shared__ __align__(16) float s_gam[BLK], s_bet[BLK], s_Gam[BLK], s_ek[BLK];
+    __shared__ __align__(16) float s_gam[BLK], s_bet[BLK], s_Gam[BLK], s_bG[BLK];
     __shared__ __align__(16) char lds[Lay::total];
     E* Ks = (E*)(lds + Lay::o_K);
     E* Vs = (E*)(lds + Lay::o_V);
     float* Am = (float*)(lds + Lay::o_A);
     float* Td = (float*)(lds + Lay::o_Td);
-    E* T1 = (E*)(lds + Lay::o_T1);
-    E* T2 = (E*)(lds + Lay::o_T2);
 
     const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
     const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
@@ -213,10 +225,8 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         const float gv = l < nvalid ? to_f(a.g[ig]) : 0.f;
         const float bv = l < nvalid ? to_f(a.beta[ig]) : 0.f;
         const float gam = wave_prefix_sum(gv);
-        const float gC = __shfl(gam, BLK - 1, 64);
         s_gam[l] = gam;
         s_Gam[l] = __expf(gam);
-        s_ek[l] = __expf(gC - gam);
         s_bet[l] = bv;
         a.gam[chunk * BLK + l] = gam;
     }
@@ -252,26 +262,22 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         }
     }
     __syncthreads();
+    float* Tm = (float*)(lds + Lay::o_T1);  // T, fp32, row pitch AP
     if (hf == 0) {
-        // T = (I + A)^-1 on waves 0..3; wave w holds column block w.
-        // T1 = T Diag(beta Gam), T2 = T Diag(beta), rounded to the element type.
+        // T = (I + A)^-1 on waves 0..3; wave w holds column block w
         f32x4 tc[4];
         tri_inverse_cols(Am, Td, tc);  // one barrier inside
         const int s = 16 * w + r;
-        const float b1 = s_bet[s] * s_Gam[s], b2 = s_bet[s];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int t = 16 * i + 4 * g + ii;
-                T1[t * PT + s] = from_f<E>(tc[i][ii] * b1);
-                T2[t * PT + s] = from_f<E>(tc[i][ii] * b2);
-            }
+            for (int ii = 0; ii < 4; ++ii) Tm[(16 * i + 4 * g + ii) * AP + s] = tc[i][ii];
         // T^T[s][t] (tiled) for the backward's block adjoints
         if (a.TT) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) st4(a.TT + chunk * BLK * BLK + toff<E>(s, 16 * i + 4 * g, BLK), tc[i]);
         }
+        if (w8 == 0) s_bG[l] = s_bet[l] * s_Gam[l];
     } else {
         __syncthreads();  // matches the barrier inside tri_inverse_cols
     }
@@ -284,8 +290,13 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         qx = load_rows<E, BLK, DK, NT>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
         ox = load_rows<E, BLK, DV, NT>(a.dO + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
     }
-    // W^T[d][t] = sum_s K^T[d][s] T1[t][s]  -> stored as W[t][d] (tiled); backward
-    // also row-major in LDS (Ws, where Am was)
+    // Row fragment (m = t, k = s) of T Diag(c): fp32, scaled, split
+    auto tfrag = [&](int t, int k0, const float* c) {
+        const float* p = Tm + t * AP + k0 + 4 * g;
+        return split8<E>(ld4(p) * ld4_now(c + k0 + 4 * g), ld4(p + 16) * ld4_now(c + k0 + 16 + 4 * g));
+    };
+    // W^T[d][t] = sum_s K^T[d][s] (T Diag(beta Gam))[t][s]  -> stored as W[t][d] (tiled);
+    // backward also row-major in LDS (Ws, where Am was)
     E* Wout = a.W + chunk * BLK * DK;
     E* Ws = (E*)(lds + Lay::o_A);
 #pragma unroll
@@ -293,33 +304,27 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         const int db = tile >> 2, tb = tile & 3;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            mma(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g));
+        for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), tfrag(16 * tb + r, 32 * j, s_bG));
         st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
         if constexpr (BWD) st4(Ws + (16 * tb + r) * PK + 16 * db + 4 * g, acc);
     }
-    // Ut[t][v] = sum_s T2[t][s] V[s][v]  -> stored negated as -Ut^T[v][t] (tiled),
-    // so that the scan forms -U = W S - Ut by accumulating onto it
-    E* Uout = a.UtT + chunk * BLK * DV;
+    // Ut[t][v] = sum_s (T Diag(beta))[t][s] V[s][v]  -> stored negated as fp32 -Ut^T[v][t]
+    // (tiled), so that the scan forms -U = W S - Ut by accumulating onto it
+    float* Uout = a.UtT + chunk * BLK * DV;
 #pragma unroll
     for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
         const int tb = tile % 4, vb = tile / 4;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            mma(acc, ldfrag(T2 + (16 * tb + r) * PT + 32 * j + 4 * g), ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
-        st4(Uout + toff<E>(16 * vb + r, 16 * tb + 4 * g, BLK), -acc);
+        for (int j = 0; j < 2; ++j) mma2(acc, tfrag(16 * tb + r, 32 * j, s_bet), ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
+        *(f32x4*)(Uout + toff<float>(16 * vb + r, 16 * tb + 4 * g, BLK)) = -acc;
     }
-    // Kh^T[d][t] = exp(gamma_C - gamma_t) K[t][d] (tiled): its fragment (db, j)
-    // is the B fragment of Kh over tokens 32j.., columns 16db..
-    E* Khout = a.KhT + chunk * BLK * DK;
+    // K^T[d][t] (tiled): its fragment (db, j) is the B fragment of K over tokens
+    // 32j.., columns 16db..  (the decay exp(gamma_C - gamma_t) is applied to U
+    // in the scan, so the keys are stored exactly)
+    E* KTout = a.KhT + chunk * BLK * DK;
 #pragma unroll
-    for (int f = w8; f < 2 * ND; f += 8) {
-        const int db = f >> 1, j = f & 1;
-        Frag<E> x = ldfrag_tr(Ks, PK, 32 * j, 16 * db, l);
-        frag_scale_k(x, s_ek, 32 * j, g);
-        st_fragT(Khout, f, l, x);
-    }
+    for (int f = w8; f < 2 * ND; f += 8) st_fragT(KTout, f, l, ldfrag_tr(Ks, PK, 32 * (f & 1), 16 * (f >> 1), l));
     if constexpr (BWD) {
         static_assert(Lay::BWD_FITS, "Q where V was, W where Am was, dO where T1, T2 were");
         constexpr int PQ = PK, PO = PV, NVB = DV / 16;
@@ -339,20 +344,12 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) fk[kk] = ldfrag(Ks + s * PK + 32 * kk + 4 * g);
         {
-            E* Kh = a.Kh + chunk * BLK * DK;
-            const float ek = s_ek[s];
+            // K, exact (the reverse scan applies exp(gamma_C - gamma_t) to K dS)
+            E* Kt = a.Kh + chunk * BLK * DK;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 if ((kk & 1) != hf) continue;  // static indices: fk stays in registers
-                Frag<E> x = fk[kk];
-                if constexpr (sizeof(E) == 2) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x.v[i] = (bf16)((float)x.v[i] * ek);
-                } else {
-                    x.lo = x.lo * ek;
-                    x.hi = x.hi * ek;
-                }
-                st_fragT(Kh, w * KK + kk, l, x);
+                st_fragT(Kt, w * KK + kk, l, fk[kk]);
             }
         }
         // P[tb][w] (rows t, cols s = 16w + r), s <= t; both halves form the same tiles
@@ -377,13 +374,13 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         Frag<E> fp[2];
         fp[0] = frag_from_acc<E>(P[0], P[1]);
         fp[1] = frag_from_acc<E>(P[2], P[3]);
-        E* dvlT = a.dvlT + chunk * BLK * DV;
+        float* dvlT = a.dvlT + chunk * BLK * DV;  // fp32: the reverse scan adds it to K dS
 #pragma unroll
         for (int vb = hf; vb < NVB; vb += 2) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
-            st4(dvlT + toff<E>(16 * vb + r, 16 * w + 4 * g, BLK), acc);
+            *(f32x4*)(dvlT + toff<float>(16 * vb + r, 16 * w + 4 * g, BLK)) = acc;
         }
         __syncthreads();  // K no longer read: P^T may take its place
         if (hf == 0) {
@@ -425,10 +422,15 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
 // the blocks.  The fp32 state slice S[0:DK][v0:v0+16] lives in accumulator
 // tiles of the consumer wave.  Writes the state entering each block and U_n^T.
 // ---------------------------------------------------------------------------
-template <typename E, int DK> struct ScanFwdOps {
+// The scans of the Gated DeltaNet path keep Ut and U in fp32 and multiply the
+// exact keys (HP, see "Precision" above); KDA's (per-channel decay, PCD) keep
+// them in the input type with the decayed keys.
+template <bool PCD, typename E> using ScanWsT = typename std::conditional<PCD, E, float>::type;
+
+template <typename E, int DK, typename UE = E> struct ScanFwdOps {
     Frag<E> w[4][DK / 32];    // W rows (A: m = t, k = d)
-    Frag<E> kh[DK / 16][2];   // Kh^T rows (A: m = d, k = t)
-    Frag<E> ut[2];            // -Ut^T[v0 + r][token pair-tiles 2j, 2j+1] (accumulator layout)
+    Frag<E> kh[DK / 16][2];   // K^T (GDN) or Kh^T (KDA) rows (A: m = d, k = t)
+    Frag<UE> ut[2];           // -Ut^T[v0 + r][token pair-tiles 2j, 2j+1] (accumulator layout)
     float gC;                 // gamma at the last token of the block
 };
 
@@ -551,14 +553,15 @@ __device__ __forceinline__ void state_store(E* h, const Frag<E> (&fs)[DK / 32], 
 // One block of the recurrence.  HNAT selects the layout of the saved states:
 // false -> tiled h^T[v][d] (read by the forward's out kernel), true -> tiled
 // h[d][v] (read by the backward).
-template <typename E, int DK, int NU>
-__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK>& o, const char* slot, int l);
+template <typename E, int DK, int NU, typename UE>
+__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK, UE>& o, const char* slot, int l);
 
 template <typename E, int DK, int DV, bool HNAT, int NU, bool PCD = false>
-__device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[DK / 16],
+__device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>& o, f32x4 (&S)[DK / 16],
                                               const GdnScanArgs<E>& a, size_t chunk, int vb, int l, E* tile,
                                               const char* slot) {
     constexpr int ND = DK / 16, KK = DK / 32;
+    using UE = ScanWsT<PCD, E>;
     Frag<E> fs[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
@@ -576,8 +579,8 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[D
     f32x4 U[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const Frag<E>& f = o.ut[j];
-        if constexpr (sizeof(E) == 2) {
+        const Frag<UE>& f = o.ut[j];
+        if constexpr (sizeof(UE) == 2) {
             U[2 * j] = f32x4{(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]};
             U[2 * j + 1] = f32x4{(float)f.v[4], (float)f.v[5], (float)f.v[6], (float)f.v[7]};
         } else {
@@ -592,15 +595,12 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[D
     }
     // the Kh^T reads go out while the products above run
     asm volatile("" ::: "memory");
-    scan_fwd_from_ring_kh<E, DK, NU>(o, slot, l);
+    scan_fwd_from_ring_kh<E, DK, NU, UE>(o, slot, l);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) U[tb] = -U[tb];
     // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles
-    Frag<E> fu[2];
-    fu[0] = frag_from_acc<E>(U[0], U[1]);
-    fu[1] = frag_from_acc<E>(U[2], U[3]);
     if (a.UT) {
-        E* UT = a.UT + chunk * BLK * DV;
+        UE* UT = (UE*)a.UT + chunk * BLK * DV;
 #pragma unroll
         for (int j = 0; j < 2; ++j) st8T(UT, 2 * vb + j, l, U[2 * j], U[2 * j + 1]);
     }
@@ -612,36 +612,62 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK>& o, f32x4 (&S)[D
         E* dst = a.Utok + ((size_t)bb * a.T + (size_t)n * BLK) * ldv + (size_t)hh * DV;
         store_rows16<E, BLK>(dst, ldv, U, tile, 16 * vb, l & 15, l >> 4, min(BLK, a.T - n * BLK));
     }
-    // S <- Diag(decay) S + Kh^T U: Gam_C (GDN), or exp(b_C) per key channel
-    // (KDA: row d of S scaled by its own channel's factor, from the slot's last unit)
-    const float GC = __expf(o.gC);
-    const float* ecs = (const float*)(slot + (NU - 1) * RING_UNIT) + 4 * (l >> 4);
+    if constexpr (PCD) {
+        // S <- Diag(exp(b_C)) S + Kh^T U (KDA: row d of S scaled by its own
+        // channel's factor, from the slot's last unit)
+        Frag<E> fu[2];
+        fu[0] = frag_from_acc<E>(U[0], U[1]);
+        fu[1] = frag_from_acc<E>(U[2], U[3]);
+        const float* ecs = (const float*)(slot + (NU - 1) * RING_UNIT) + 4 * (l >> 4);
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-        f32x4 acc;
-        if constexpr (PCD) acc = S[db] * *(const f32x4*)(ecs + 16 * db);
-        else acc = S[db] * GC;
+        for (int db = 0; db < ND; ++db) {
+            f32x4 acc = S[db] * *(const f32x4*)(ecs + 16 * db);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc, o.kh[db][j], fu[j]);
-        S[db] = acc;
+            for (int j = 0; j < 2; ++j) mma(acc, o.kh[db][j], fu[j]);
+            S[db] = acc;
+        }
+    } else {
+        // S <- Gam_C S + K^T (e * U), e_t = exp(gamma_C - gamma_t) on the rows
+        // of the U tiles (gamma from the slot's small unit), e * U split
+        const float* gsm = (const float*)(slot + NU * RING_UNIT) + 4 * (l >> 4);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const f32x4 gt = *(const f32x4*)(gsm + 16 * tb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) U[tb][i] *= __expf(o.gC - gt[i]);
+        }
+        Frag2<E> fu[2];
+        fu[0] = split_acc<E>(U[0], U[1]);
+        fu[1] = split_acc<E>(U[2], U[3]);
+        const float GC = __expf(o.gC);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            f32x4 acc = S[db] * GC;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mma2(acc, o.kh[db][j], fu[j]);
+            S[db] = acc;
+        }
     }
 }
 
 // Operands of one block from a ring slot (see clr_ring.h for the layout).
-template <typename E, int DK, int NU>
-__device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK>& o, const char* slot, int l) {
+template <typename E, int DK, int NU, typename UE>
+__device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK, UE>& o, const char* slot, int l) {
     constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * (DK / 16);
+    // units per fragment of W / K and of Ut; Ut starts after the W and K units
+    constexpr int UPF = sizeof(E) == 2 ? 1 : 2, UPFU = sizeof(UE) == 2 ? 1 : 2;
+    static_assert((NWF + NKF) * UPF % UPFU == 0, "fragment alignment");
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) o.w[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, NWF + NKF + j, l, (E*)nullptr);
+    for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, (NWF + NKF) * UPF / UPFU + j, l, (UE*)nullptr);
     o.gC = ring_small<NU>(slot, BLK - 1);
 }
-// Kh^T operands of a block (read after the W S products have been issued).
-template <typename E, int DK, int NU>
-__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK>& o, const char* slot, int l) {
+// K^T (Kh^T) operands of a block (read after the W S products have been issued).
+template <typename E, int DK, int NU, typename UE>
+__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK, UE>& o, const char* slot, int l) {
     constexpr int KK = DK / 32, NWF = 4 * KK;
 #pragma unroll
     for (int db = 0; db < DK / 16; ++db)
@@ -652,7 +678,8 @@ __device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK>& o, cons
 // Work-group: wave 0 runs the recurrence, the other waves stream the operands
 // of the next blocks into the LDS ring (clr_ring.h).  All operands are tiled, so
 // ring unit u of a block is the contiguous 1-KB run u of
-// [W | Kh^T | Ut^T fragments (vb, 0..1)].
+// [W | K^T (Kh^T) | Ut^T fragments (vb, 0..1)]  (Ut fp32 for the Gated
+// DeltaNet scans: two units per fragment); the small unit holds gamma.
 // With PCD (per-channel decay, KDA) one more unit holds exp(b_C) for every key
 // channel, as fp32 (256 floats, padded), and the state-store tile also
 // stages U for its token-major store.
@@ -666,8 +693,9 @@ template <int NP> constexpr int scan_threads = 64 * (NP + 1);
 
 template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFwdGeom {
     static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 1-KB units per fragment
+    static constexpr int UPFU = sizeof(ScanWsT<PCD, E>) == 2 ? 1 : 2;  // ... of Ut
     static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF;
-    static constexpr int NU = NWU + NKU + 2 * UPF + (PCD ? 1 : 0);
+    static constexpr int NU = NWU + NKU + 2 * UPFU + (PCD ? 1 : 0);
     static constexpr int SLOT = RingGeom<NU>::SLOT;
     static constexpr int TILE_H = HNAT ? state_tile_bytes(DK, sizeof(E)) : 16, TILE_U = PCD ? BLK * 16 * (int)sizeof(E) : 16;
     static constexpr int TILE = TILE_H > TILE_U ? TILE_H : TILE_U;
@@ -688,7 +716,8 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
     const int v0 = 16 * vb;
     using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD>;
-    constexpr int ND = SG::ND, UPF = SG::UPF, NWU = SG::NWU, NKU = SG::NKU, NU = SG::NU, P = SG::P;
+    using UT_ = ScanWsT<PCD, E>;
+    constexpr int ND = SG::ND, UPFU = SG::UPFU, NWU = SG::NWU, NKU = SG::NKU, NU = SG::NU, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
     using G = RingGeom<NU, NP>;
     char* ring = smem;
@@ -701,12 +730,13 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
             const size_t c = bh * NC + n0 + n;
             const E* W = a.W + c * BLK * DK + l * LE;
             const E* KhT = a.KhT + c * BLK * DK + l * LE;
-            const E* UtT = a.UtT + c * BLK * DV + (size_t)(2 * vb * UPF) * UE + l * LE;
+            const UT_* UtT = (const UT_*)a.UtT + c * BLK * DV + (size_t)(2 * vb * UPFU) * UNIT_ELEMS<UT_> +
+                             l * LANE_ELEMS<UT_>;
             auto src = [&](int u) -> const void* {
                 if (u < NWU) return W + u * UE;
                 if (u < NWU + NKU) return KhT + (u - NWU) * UE;
                 if (PCD && u == NU - 1) return a.eC + c * 256 + l * 4;
-                return UtT + (u - NWU - NKU) * UE;
+                return UtT + (u - NWU - NKU) * UNIT_ELEMS<UT_>;
             };
             ring_issue<NU, decltype(src), NP>(ring + (n % P) * G::SLOT, pid, src,
                                                      PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.gam + c * BLK + l));
@@ -732,9 +762,9 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
         for (int i = 0; i < 4; ++i) S[db][i] = Sin ? Sin[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
     ring_barrier();
     for (int n = 0; n < NB; ++n) {
-        ScanFwdOps<E, DK> o;
+        ScanFwdOps<E, DK, UT_> o;
         const char* slot = ring + (n % P) * G::SLOT;
-        scan_fwd_from_ring<E, DK, NU>(o, slot, l);
+        scan_fwd_from_ring<E, DK, NU, UT_>(o, slot, l);
         scan_fwd_step<E, DK, DV, HNAT, NU, PCD>(o, S, a, bh * NC + n0 + n, vb, l, tile, slot);
         ring_barrier();
     }
@@ -775,8 +805,9 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
     __shared__ __align__(16) E Qs[BLK * PK], Ks[BLK * PK];
 
     const E* hT = a.hT + chunk * DK * DV;
-    const E* UT = a.UT + chunk * BLK * DV;
-    Frag<E> fh[2][KK], fu[2][2];
+    const float* UT = a.UT + chunk * BLK * DV;
+    Frag<E> fh[2][KK];
+    Frag<float> fu[2][2];  // U^T fp32, split when used
     auto load_slice = [&](int buf, int vb) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) fh[buf][kk] = ldfragT(hT, vb * KK + kk, l);
@@ -816,9 +847,10 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
         }
         P[sb] = acc;
     }
-    Frag<E> fp[2];
-    fp[0] = frag_from_acc<E>(P[0], P[1]);
-    fp[1] = frag_from_acc<E>(P[2], P[3]);
+    // P U: both factors split (U telescopes over repeated keys)
+    Frag2<E> fp[2];
+    fp[0] = split_acc<E>(P[0], P[1]);
+    fp[1] = split_acc<E>(P[2], P[3]);
     const float Gt = __expf(gt);
     E* ob = a.o + tok0 * H * DV + (size_t)h * DV;
     auto compute_slice = [&](int buf, int vb) {
@@ -828,7 +860,7 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
         acc = acc * Gt;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            if (2 * j <= w) mma(acc, fu[buf][j], fp[j]);
+            if (2 * j <= w) mma2(acc, split_frag<E>(fu[buf][j]), fp[j]);
         if (t_lane < nvalid) st4(ob + (size_t)t_lane * H * DV + 16 * vb + 4 * g, acc);
     };
 #pragma unroll

@@ -13,6 +13,8 @@ Distributions (per-token tensors are [B,T,H,d], states [B,H,dk,dv]):
   Mamba-2:        as GLA, but one gate per (token, head): g [B,T,H].
   KDA:            q, k, v, beta, S_in as Gated DeltaNet; g = logsigmoid(N(0,1)) / 16
                   per key channel [B,T,H,dk] as GLA.
+  Delta-rule stress (make_delta_stress): keys repeated from 8 L2-normalised
+                  vectors per head, beta = 0.99, g = -softplus(N(0,1))/1024 or 0.
   Short conv:     x ~ N(0,1) [B,T,C]; w = 0.5 * N(0,1) [C,W]; bias = 0.1 * N(0,1);
                   state_in ~ N(0,1) [B,W-1,C]; dy ~ N(0,1); dstate_out ~ N(0,1)
                   (float32: state gradients are partial sums and stay fp32).
@@ -164,6 +166,48 @@ def make_kda(B, T, H, dk, dv, dtype="bf16", seed=0, gate_scale=1.0 / 16.0):
     dO = _normal(rng, (B, T, H, dv))
     dS_out = _normal(rng, (B, H, dk, dv))
     d = dict(q=q, k=k, v=v, g=g, beta=beta, S_in=S_in, dO=dO, dS_out=dS_out)
+    if dtype == "bf16":
+        for key in ("q", "k", "v", "g", "beta", "dO"):
+            d[key] = bf16_round(d[key])
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return d
+
+
+def make_delta_stress(kind, B, T, H, dk, dv, dtype="bf16", seed=0, gate="slow", beta=0.99, n_keys=8):
+    """Stress inputs for the delta-rule members (kind "gdn" or "kda"): almost
+    no decay, an almost complete erase, and keys repeated from a small set, so
+    that the state is carried over the whole sequence and each block's writes
+    nearly cancel one another.
+
+      keys:   a pool of n_keys L2-normalised N(0,1) vectors per (batch, head);
+              token t uses pool[b, h, j] with j uniform in [0, n_keys);
+      gate:   "slow": g = -softplus(N(0,1)) / 1024; "zero": g = 0
+              (per (token, head) for "gdn", per key channel for "kda");
+      beta:   the constant `beta` (0.99);
+      q, v, S_in, dO, dS_out as make_gdn.
+    Draw order: q, key pool, key index, v, gate normals, S_in, dO, dS_out."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _l2n(_normal(rng, (B, T, H, dk)))
+    pool = _l2n(_normal(rng, (B, H, n_keys, dk)))
+    idx = rng.integers(0, n_keys, size=(B, T, H))
+    bi = np.arange(B)[:, None, None]
+    hi = np.arange(H)[None, None, :]
+    k = np.ascontiguousarray(pool[bi, hi, idx])  # [B, T, H, dk]
+    v = _normal(rng, (B, T, H, dv))
+    gshape = (B, T, H) if kind == "gdn" else (B, T, H, dk)
+    z = _normal(rng, gshape)
+    if gate == "slow":
+        g = (-_softplus(z) / 1024.0).astype(np.float32)
+    elif gate == "zero":
+        g = np.zeros(gshape, np.float32)
+    else:
+        raise ValueError(gate)
+    b = np.full((B, T, H), beta, np.float32)
+    S_in = (0.1 * _normal(rng, (B, H, dk, dv))).astype(np.float32)
+    dO = _normal(rng, (B, T, H, dv))
+    dS_out = _normal(rng, (B, H, dk, dv))
+    d = dict(q=q, k=k, v=v, g=g, beta=b, S_in=S_in, dO=dO, dS_out=dS_out)
     if dtype == "bf16":
         for key in ("q", "k", "v", "g", "beta", "dO"):
             d[key] = bf16_round(d[key])
