@@ -58,6 +58,7 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     GdnWs w{};
     // Ut, U, dvloc and dU are fp32 (split operands; gdn_kernels.h, "Precision")
     w.gam = (float*)c.take(nb * BLK * 4);
+    w.eg = (float*)c.take(nb * BLK * 4);
     w.W = c.take(nb * BLK * dk * es);
     w.KhT = c.take(nb * BLK * dk * es);
     w.UtT = c.take(nb * BLK * dv * 4);

@@ -28,6 +28,7 @@ namespace clr {
 // KhT / Kh the per-channel decayed keys.
 struct GdnWs {
     float* gam;   // [.., 64]       in-block cumulative log gate
+    float* eg;    // [.., 64]       exp(gamma_C - gamma_t) for t < 63, exp(gamma_C) at t = 63 (GDN scans)
     void* W;      // [.., 64, dk]   W = T Diag(beta Gam) K           (token-major)
     void* KhT;    // [.., dk, 64]   K^T (GDN), (K * exp(b_C - b))^T (KDA)
     void* UtT;    // [.., dv, 64]   -(T Diag(beta) V)^T
@@ -74,6 +75,7 @@ template <typename E> struct GdnPrepArgs {
     float* gam;
     E *W, *KhT;
     float* UtT;
+    float* eg;
     int n0 = 0;  // first block of the launch (grid x covers blocks n0 ..)
     // backward only (nullable): T^T (tiled [s][t]) and the decayed Gram
     // product K K^T * G (strictly lower, fp32, 16 accumulator tiles)
@@ -88,7 +90,7 @@ template <typename E> struct GdnPrepArgs {
 
 // UtT and UT are fp32 for the Gated DeltaNet scans and of type E for KDA's.
 template <typename E> struct GdnScanArgs {
-    const float* gam;
+    const float* eg;  // GDN: per block exp(gamma_C - gamma_t), t < 63, and exp(gamma_C) at 63
     const E *W, *KhT;
     const void* UtT;
     const float* S_in;

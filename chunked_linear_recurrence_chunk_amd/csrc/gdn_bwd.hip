@@ -9,7 +9,7 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GdnWs& ws = L.ws;
     GdnPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
-                      ws.gam, (E*)ws.W, (E*)ws.KhT, (float*)ws.UtT};
+                      ws.gam, (E*)ws.W, (E*)ws.KhT, (float*)ws.UtT, ws.eg};
     pa.TT = (E*)ws.TT;
     pa.KKG = ws.KKG;
     pa.q = (const E*)L.q;
@@ -19,9 +19,9 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     pa.dvlT = (float*)ws.dvlT;
     pa.Rt = ws.Rt;
     launch("gdn_prep_bwd", gdn_prep_kernel<E, DK, DV, true>, gblk, dim3(512), st, pa);
-    GdnScanArgs<E> sa{ws.gam, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
+    GdnScanArgs<E> sa{ws.eg, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, (E*)ws.UT, L.H, L.NC, L.B * L.H};
-    GdnScanBwdArgs<E> sb{ws.gam, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
+    GdnScanBwdArgs<E> sb{ws.eg, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
                          L.dS_out, L.dS_in, (E*)ws.dhT, ws.dUT, L.H, L.NC, L.B * L.H};
     sb.dh_lo = (E*)ws.dhT_lo;
     const int G = (int)scan_grid(DV / 16, L.B * L.H);

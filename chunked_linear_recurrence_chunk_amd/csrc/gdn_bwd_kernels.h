@@ -41,7 +41,7 @@ namespace clr {
 // dvlT and dUT are fp32 for the Gated DeltaNet scan (of type E for KDA's), and
 // its dh is stored as a bf16 hi/lo pair (dh, dh_lo) for bf16 inputs.
 template <typename E> struct GdnScanBwdArgs {
-    const float* gam;
+    const float* eg;  // GDN: as GdnScanArgs::eg
     const E *Kh, *WT;
     const void* dvlT;
     const float* Rt;
@@ -74,12 +74,12 @@ template <typename E> struct GdnIntraArgs {
 // [K (Kh) | W^T | R tiles (., vb) | dvloc^T fragments (vb, 0..1)], all tiled;
 // the small unit holds gamma (exp(b_C) per channel in a last unit for KDA).
 // ---------------------------------------------------------------------------
+// (W^T and R are read from the slot by the step itself, after the K dS
+// products have been issued, so that their registers are not live at once.)
 template <typename E, int DK, typename UE = E> struct ScanBwdOps {
     Frag<E> kh[4][DK / 32];   // K (GDN) or Kh (KDA) rows (A: m = t, k = d)
-    Frag<E> wt[DK / 16][2];   // W^T rows (A: m = d, k = t)
-    f32x4 rt[DK / 16];        // R accumulator tiles (rows d, column v0 + r)
     Frag<UE> dvl[2];          // dvloc^T[v0 + r][token tile pairs] (accumulator layout)
-    float gC;
+    float GC;                 // GDN: Gam_C, from the small unit
 };
 
 // With PCD (per-channel decay, KDA) a last unit holds exp(b_C) for every key
@@ -97,23 +97,17 @@ template <typename E, int DK, int NU, bool PCD>
 __device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK, ScanWsT<PCD, E>>& o, const char* slot, int l) {
     using Rg = ScanBwdRing<E, DK, PCD>;
     using UE = ScanWsT<PCD, E>;
-    constexpr int KK = DK / 32, UPF = Rg::UPF, UPFU = Rg::UPFU;
+    constexpr int KK = DK / 32, UPFU = Rg::UPFU;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) o.kh[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
-#pragma unroll
-    for (int db = 0; db < DK / 16; ++db) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) o.wt[db][j] = ring_frag(slot, Rg::NKU / UPF + 2 * db + j, l, (E*)nullptr);
-        o.rt[db] = *(const f32x4*)(slot + (Rg::NKU + Rg::NWU + db) * RING_UNIT + l * 16);
-    }
     // dvloc fragments start at unit NKU + NWU + NRU, i.e. fragment index (that) / UPFU
     static_assert((Rg::NKU + Rg::NWU + Rg::NRU) % UPFU == 0, "fragment alignment");
 #pragma unroll
     for (int j = 0; j < 2; ++j)
         o.dvl[j] = ring_frag(slot, (Rg::NKU + Rg::NWU + Rg::NRU) / UPFU + j, l, (UE*)nullptr);
-    o.gC = ring_small<NU>(slot, BLK - 1);
+    o.GC = ring_small<NU>(slot, BLK - 1);
 }
 
 // One reverse step: on entry dS = dL/dS_{n+1}; writes dh_n = dS and
@@ -144,29 +138,44 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
         Frag2<E> fs[KK];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) fs[kk] = split_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
-        {
-            Frag<E> fh[KK];
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) fh[kk] = fs[kk].hi;
-            state_store<E, DK, DV, false>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);  // selector products
-        }
-        if constexpr (sizeof(E) == 2) {
-            Frag<E> fl[KK];
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) fl[kk] = fs[kk].lo;
-            state_store<E, DK, DV, false>(a.dh_lo + chunk * DK * DV, fl, tile, 16 * vb, l);
-        }
-        const float* gsm = (const float*)(slot + NU * RING_UNIT) + 4 * (l >> 4);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) mma2(acc, o.kh[tb][kk], fs[kk]);
-            const f32x4 gt = *(const f32x4*)(gsm + 16 * tb);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= __expf(o.gC - gt[i]);
             dUp[tb] = acc;
         }
+        // the state's hi part through the selector products, the lo part
+        // through the wave's LDS tile (no matrix-core work)
+        {
+            Frag<E> fh[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) fh[kk] = fs[kk].hi;
+            state_store<E, DK, DV, false>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
+        }
+        if constexpr (sizeof(E) == 2) {
+            Frag<E> fl[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) fl[kk] = fs[kk].lo;
+            state_store<E, DK, DV, true>(a.dh_lo + chunk * DK * DV, fl, tile, 16 * vb, l);
+        }
+        // e_t = exp(gamma_C - gamma_t) from the small unit (its last slot holds Gam_C: e_63 = 1)
+        const f32x4* es = (const f32x4*)(slot + NU * RING_UNIT) + (l >> 4);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 et = es[4 * tb];
+            if (tb == 3) et[3] = (l >> 4) == 3 ? 1.f : et[3];
+            dUp[tb] = dUp[tb] * et;
+        }
+    }
+    using Rg = ScanBwdRing<E, DK, PCD>;
+    Frag<E> wt[ND][2];  // W^T rows (A: m = d, k = t)
+    f32x4 rt[ND];       // R accumulator tiles (rows d, column v0 + r)
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) wt[db][j] = ring_frag(slot, Rg::NKU / Rg::UPF + 2 * db + j, l, (E*)nullptr);
+        rt[db] = *(const f32x4*)(slot + (Rg::NKU + Rg::NWU + db) * RING_UNIT + l * 16);
     }
     UE* dUT = (UE*)a.dUT + chunk * BLK * DV;
 #pragma unroll
@@ -185,16 +194,15 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
     Frag<E> fu[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) fu[j] = frag_from_acc<E>(-dUp[2 * j], -dUp[2 * j + 1]);
-    const float GC = __expf(o.gC);
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
         f32x4 acc;
         if constexpr (PCD)  // row d scaled by exp(b_C[d]) from the slot's last unit
-            acc = dS[db] * *(const f32x4*)((const float*)(slot + (NU - 1) * RING_UNIT) + 4 * (l >> 4) + 16 * db) + o.rt[db];
+            acc = dS[db] * *(const f32x4*)((const float*)(slot + (NU - 1) * RING_UNIT) + 4 * (l >> 4) + 16 * db) + rt[db];
         else
-            acc = dS[db] * GC + o.rt[db];
+            acc = dS[db] * o.GC + rt[db];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc, o.wt[db][j], fu[j]);
+        for (int j = 0; j < 2; ++j) mma(acc, wt[db][j], fu[j]);
         dS[db] = acc;
     }
 }
@@ -203,7 +211,7 @@ template <typename E, int DK, bool PCD = false> struct ScanBwdGeom {
     static constexpr int NU = ScanBwdRing<E, DK, PCD>::NU;
     static constexpr int SLOT = RingGeom<NU>::SLOT;
     static constexpr int TILE = state_tile_bytes(DK, sizeof(E));
-    static constexpr int PF = (144 * 1024 - TILE) / SLOT;
+    static constexpr int PF = (160 * 1024 - 512 - TILE) / SLOT;  // ring + tile within the CU's LDS
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
     static constexpr int LDS = P * SLOT + TILE;
 };
@@ -244,7 +252,7 @@ __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, in
                 return dvl + (u - Rg::NKU - Rg::NWU - Rg::NRU) * UNIT_ELEMS<UT_>;
             };
             ring_issue<NU, decltype(src), NP>(ring + (m % P) * G::SLOT, pid, src,
-                                              PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.gam + c * BLK + l));
+                                              PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.eg + c * BLK + l));
         };
         const int pre = NC < P - 1 ? NC : P - 1;
         for (int m = 0; m < pre; ++m) issue(m);

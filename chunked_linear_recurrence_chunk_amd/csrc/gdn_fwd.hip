@@ -13,12 +13,12 @@ struct GdnFwdStages {
     const GdnLaunch& L;
     void prep(int n0, int n1, hipStream_t st) const {
         GdnPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
-                          L.ws.gam, (E*)L.ws.W, (E*)L.ws.KhT, (float*)L.ws.UtT};
+                          L.ws.gam, (E*)L.ws.W, (E*)L.ws.KhT, (float*)L.ws.UtT, L.ws.eg};
         pa.n0 = n0;
         launch("gdn_prep", gdn_prep_kernel<E, DK, DV>, dim3(n1 - n0, L.H, L.B), dim3(512), st, pa);
     }
     void scan(int n0, int n1, const float* S_in, float* S_out, hipStream_t st) const {
-        GdnScanArgs<E> sa{L.ws.gam, (const E*)L.ws.W, (const E*)L.ws.KhT, (const E*)L.ws.UtT, S_in, S_out,
+        GdnScanArgs<E> sa{L.ws.eg, (const E*)L.ws.W, (const E*)L.ws.KhT, (const E*)L.ws.UtT, S_in, S_out,
                           (E*)L.ws.hT, (E*)L.ws.UT, L.H, L.NC, L.B * L.H};
         sa.n0 = n0;
         sa.n1 = n1;

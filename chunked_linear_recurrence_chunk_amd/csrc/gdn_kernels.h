@@ -225,10 +225,13 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         const float gv = l < nvalid ? to_f(a.g[ig]) : 0.f;
         const float bv = l < nvalid ? to_f(a.beta[ig]) : 0.f;
         const float gam = wave_prefix_sum(gv);
+        const float gC = __shfl(gam, BLK - 1, 64);
         s_gam[l] = gam;
         s_Gam[l] = __expf(gam);
         s_bet[l] = bv;
         a.gam[chunk * BLK + l] = gam;
+        // the scans' per-token decay to the block end, and Gam_C in the last slot
+        a.eg[chunk * BLK + l] = l < BLK - 1 ? __expf(gC - gam) : __expf(gC);
     }
     store_rows<E, BLK, DK, PK, NT>(kx, Ks);
     store_rows<E, BLK, DV, PV, NT>(vx, Vs);
@@ -431,7 +434,7 @@ template <typename E, int DK, typename UE = E> struct ScanFwdOps {
     Frag<E> w[4][DK / 32];    // W rows (A: m = t, k = d)
     Frag<E> kh[DK / 16][2];   // K^T (GDN) or Kh^T (KDA) rows (A: m = d, k = t)
     Frag<UE> ut[2];           // -Ut^T[v0 + r][token pair-tiles 2j, 2j+1] (accumulator layout)
-    float gC;                 // gamma at the last token of the block
+    float GC;                 // GDN: Gam_C = exp(gamma_C), from the small unit
 };
 
 // Store ROWS x 16 accumulator tiles (rows 16 rb + 4 g + i, column c0 + r)
@@ -628,21 +631,21 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>
         }
     } else {
         // S <- Gam_C S + K^T (e * U), e_t = exp(gamma_C - gamma_t) on the rows
-        // of the U tiles (gamma from the slot's small unit), e * U split
-        const float* gsm = (const float*)(slot + NU * RING_UNIT) + 4 * (l >> 4);
+        // of the U tiles (from the slot's small unit, whose last slot holds
+        // Gam_C: e_63 = 1), e * U split
+        const f32x4* es = (const f32x4*)(slot + NU * RING_UNIT) + (l >> 4);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            const f32x4 gt = *(const f32x4*)(gsm + 16 * tb);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) U[tb][i] *= __expf(o.gC - gt[i]);
+            f32x4 et = es[4 * tb];
+            if (tb == 3) et[3] = (l >> 4) == 3 ? 1.f : et[3];
+            U[tb] = U[tb] * et;
         }
         Frag2<E> fu[2];
         fu[0] = split_acc<E>(U[0], U[1]);
         fu[1] = split_acc<E>(U[2], U[3]);
-        const float GC = __expf(o.gC);
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-            f32x4 acc = S[db] * GC;
+            f32x4 acc = S[db] * o.GC;
 #pragma unroll
             for (int j = 0; j < 2; ++j) mma2(acc, o.kh[db][j], fu[j]);
             S[db] = acc;
@@ -663,7 +666,7 @@ __device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK, UE>& o, con
         for (int kk = 0; kk < KK; ++kk) o.w[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
 #pragma unroll
     for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, (NWF + NKF) * UPF / UPFU + j, l, (UE*)nullptr);
-    o.gC = ring_small<NU>(slot, BLK - 1);
+    o.GC = ring_small<NU>(slot, BLK - 1);
 }
 // K^T (Kh^T) operands of a block (read after the W S products have been issued).
 template <typename E, int DK, int NU, typename UE>
@@ -699,7 +702,7 @@ template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFw
     static constexpr int SLOT = RingGeom<NU>::SLOT;
     static constexpr int TILE_H = HNAT ? state_tile_bytes(DK, sizeof(E)) : 16, TILE_U = PCD ? BLK * 16 * (int)sizeof(E) : 16;
     static constexpr int TILE = TILE_H > TILE_U ? TILE_H : TILE_U;
-    static constexpr int PF = (144 * 1024 - TILE) / SLOT;
+    static constexpr int PF = (160 * 1024 - 512 - TILE) / SLOT;  // ring + tile within the CU's LDS
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
     static constexpr int LDS = P * SLOT + TILE;  // ring, then the state-store tile
 };
@@ -739,7 +742,7 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
                 return UtT + (u - NWU - NKU) * UNIT_ELEMS<UT_>;
             };
             ring_issue<NU, decltype(src), NP>(ring + (n % P) * G::SLOT, pid, src,
-                                                     PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.gam + c * BLK + l));
+                                                     PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.eg + c * BLK + l));
         };
         const int pre = NB < P - 1 ? NB : P - 1;
         for (int n = 0; n < pre; ++n) issue(n);
