@@ -135,6 +135,46 @@ def _workspace(shape, op, device):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
 
 
+# gate layout per member: one value per (token, head), or one per key channel
+_GATE_PER_CHANNEL = {"gdn": False, "mamba2": False, "gla": True, "kda": True}
+_HAS_BETA = {"gdn": True, "kda": True, "gla": False, "mamba2": False}
+
+
+def _validate(kind, q, k, v, g, beta, S_in, dO=None, dS_out=None):
+    """Shapes and dtypes of a layer call against (B, T, H, dk, dv) from q and v
+    (ValueError for a shape, TypeError for a dtype), before anything reaches
+    the library: the C ABI takes bare pointers and cannot see a wrong size."""
+    import torch
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    want = {"k": (k, (B, T, H, dk)), "v": (v, (B, T, H, dv)),
+            "g": (g, (B, T, H, dk) if _GATE_PER_CHANNEL[kind] else (B, T, H))}
+    if _HAS_BETA[kind]:
+        want["beta"] = (beta, (B, T, H))
+    elif beta is not None:
+        raise ValueError(f"{kind} takes no beta")
+    if dO is not None:
+        want["dO"] = (dO, (B, T, H, dv))
+    for name, (t, shp) in want.items():
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} must have shape {shp}, got {tuple(t.shape)}")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must be {q.dtype} like q, got {t.dtype}")
+    for name, t in (("S_in", S_in), ("dS_out", dS_out)):
+        if t is None:
+            continue
+        if tuple(t.shape) != (B, H, dk, dv):
+            raise ValueError(f"{name} must have shape {(B, H, dk, dv)}, got {tuple(t.shape)}")
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32 (states are fp32), got {t.dtype}")
+
+
 def _check_inputs(*ts):
     for t in ts:
         if t is None:
@@ -180,6 +220,7 @@ def _out(t, shape, dtype, device):
 
 def _fwd(name, op, q, k, v, g, beta, S_in, want_state, ws, o=None, S_out=None):
     import torch
+    _validate(name.split("_")[0], q, k, v, g, beta, S_in)
     _check_inputs(q, k, v, g, beta, S_in)
     shape = make_shape(q, v)
     B, T, H, dk = q.shape
@@ -210,6 +251,7 @@ def gla_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None)
 
 def _bwd(name, op, q, k, v, g, beta, S_in, dO, dS_out, ws, out=None):
     import torch
+    _validate(name.split("_")[0], q, k, v, g, beta, S_in, dO, dS_out)
     _check_inputs(q, k, v, g, beta, S_in, dO, dS_out)
     shape = make_shape(q, v)
     B, T, H, dk = q.shape

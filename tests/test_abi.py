@@ -180,3 +180,53 @@ def test_product_path_has_no_oracle_or_fallback():
     from chunked_linear_recurrence_chunk_amd import ops
     with pytest.raises(OSError):
         ops.load(os.path.join(ROOT, "does_not_exist.so"))
+
+
+def test_binding_checks_shapes_and_dtypes_before_the_library():
+    """ops.py compares every tensor with (B, T, H, dk, dv) taken from q and v,
+    per member, so a wrong gate layout or a bf16 state never reaches the
+    kernels as a short buffer (CPU tensors: the checks run before the device
+    check)."""
+    import torch
+    ops, _ = _lib()
+    B, T, H, dk, dv = 1, 64, 2, 32, 32
+    bf = torch.bfloat16
+    q = torch.zeros(B, T, H, dk, dtype=bf)
+    k = torch.zeros(B, T, H, dk, dtype=bf)
+    v = torch.zeros(B, T, H, dv, dtype=bf)
+    g_tok = torch.zeros(B, T, H, dtype=bf)
+    g_ch = torch.zeros(B, T, H, dk, dtype=bf)
+    beta = torch.zeros(B, T, H, dtype=bf)
+    S = torch.zeros(B, H, dk, dv)
+    dO = torch.zeros(B, T, H, dv, dtype=bf)
+    on_gpu = "must be on the GPU"
+
+    def raises(exc, text, fn, *a):
+        with pytest.raises(exc) as e:
+            fn(*a)
+        assert text in str(e.value), str(e.value)
+
+    # well-formed calls get as far as the device check
+    raises(ValueError, on_gpu, ops.gdn_fwd, q, k, v, g_tok, beta, S)
+    raises(ValueError, on_gpu, ops.gla_fwd, q, k, v, g_ch, S)
+    raises(ValueError, on_gpu, ops.kda_bwd, q, k, v, g_ch, beta, S, dO, S)
+    raises(ValueError, on_gpu, ops.mamba2_bwd, q, k, v, g_tok, S, dO, None)
+    # gate layouts: per (token, head) for GDN and Mamba-2, per key channel for GLA and KDA
+    raises(ValueError, "g must have shape", ops.gla_fwd, q, k, v, g_tok, S)
+    raises(ValueError, "g must have shape", ops.kda_fwd, q, k, v, g_tok, beta, S)
+    raises(ValueError, "g must have shape", ops.gdn_bwd, q, k, v, g_ch, beta, S, dO, None)
+    raises(ValueError, "g must have shape", ops.mamba2_fwd, q, k, v, g_ch, S)
+    # beta: required for the delta rule, refused otherwise; [B, T, H]
+    raises(ValueError, "beta is required", ops.gdn_fwd, q, k, v, g_tok, None, S)
+    raises(ValueError, "beta must have shape", ops.kda_fwd, q, k, v, g_ch, g_ch, S)
+    # k, v, dO shapes
+    raises(ValueError, "k must have shape", ops.gdn_fwd, q, k[:, :32], v, g_tok, beta, S)
+    raises(ValueError, "dO must have shape", ops.gdn_bwd, q, k, v, g_tok, beta, S, dO[..., :16], None)
+    # dtypes: per-token tensors like q, states fp32
+    raises(TypeError, "must be", ops.gdn_fwd, q, k.float(), v, g_tok, beta, S)
+    raises(TypeError, "S_in must be float32", ops.gdn_fwd, q, k, v, g_tok, beta, S.to(bf))
+    raises(TypeError, "dS_out must be float32", ops.gdn_bwd, q, k, v, g_tok, beta, S, dO, S.to(bf))
+    raises(ValueError, "S_in must have shape", ops.gla_fwd, q, k, v, g_ch, S[:, :, :16])
+    raises(ValueError, "dS_out must have shape", ops.gdn_bwd, q, k, v, g_tok, beta, S, dO, S[:1, :1])
+    raises(TypeError, "unsupported dtype", ops.gdn_fwd, q.half(), k.half(), v.half(), g_tok.half(), beta.half(), S)
+    raises(ValueError, "gla takes no beta", ops._fwd, "gla_fwd", ops.OP_GLA_FWD, q, k, v, g_ch, beta, S, True, None)
