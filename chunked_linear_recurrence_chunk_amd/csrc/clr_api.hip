@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "clr.h"
 #include "clr_conv.h"
 #include "clr_kernels.h"
@@ -200,6 +202,7 @@ const char* clr_status_string(int s) {
         case CLR_ENOTSUP: return "unsupported dtype or head size";
         case CLR_EWORKSPACE: return "workspace missing or too small";
         case CLR_EHIP: return "HIP error";
+        case CLR_ESCRATCH: return "needs more scratch than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }
@@ -223,12 +226,41 @@ size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
     return total;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free Gated DeltaNet forward: gdn_fwd with its workspace in the
+// library's own device array.  The array's host-side name is not a device
+// address; each device's address is taken once, with that device current,
+// by hipGetSymbolAddress and kept, and only that address reaches a kernel.
+// Nothing in it has to start at zero: the forward writes every workspace
+// element before reading it.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[CLR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];  // device address of `scratch`, per device (null until taken)
+
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return CLR_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CLR_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CLR_OK;
+}
+}  // namespace
+
 // Which member of the family an entry point computes.
 enum Kind { K_GDN, K_GLA, K_M2, K_KDA };
 
 static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void* k, const void* v,
                       const void* g, const void* beta, const float* S_in, void* o, float* S_out,
-                      void* ws, size_t ws_bytes, void* stream) {
+                      void* ws, size_t ws_bytes, void* stream, bool noalloc = false) {
     const bool gla = kind == K_GLA || kind == K_M2;  // GLA kernels and head sizes
     const bool has_beta = kind == K_GDN || kind == K_KDA;
     int rc = check_shape(s, gla, false);
@@ -249,8 +281,13 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
     // tensors themselves must start 16-byte aligned.
     if ((rc = check_bufs(bufs, 9))) return rc;
     const size_t need = clr_workspace_bytes(s, kind == K_KDA ? CLR_OP_KDA_FWD : gla ? CLR_OP_GLA_FWD : CLR_OP_GDN_FWD);
+    if (noalloc && need > (size_t)CLR_NOALLOC_SCRATCH_BYTES) return CLR_ESCRATCH;
     hipStream_t st = (hipStream_t)stream;
     if (s->T == 0) return passthrough(S_in, S_out, nst, st);
+    if (noalloc) {  // the static scratch in place of a workspace (all arguments checked above)
+        if ((rc = scratch_address(&ws))) return rc;
+        ws_bytes = CLR_NOALLOC_SCRATCH_BYTES;
+    }
     if (!ws || ws_bytes < need || ((uintptr_t)ws & (ALIGN - 1))) return CLR_EWORKSPACE;
     const int NC = (s->T + BLK - 1) / BLK;
     if (kind == K_KDA) {
@@ -267,6 +304,7 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
         L.bf16 = s->dtype == CLR_BF16;
         L.q = q; L.k = k; L.v = v; L.g = g; L.beta = beta; L.S_in = S_in; L.o = o; L.S_out = S_out;
         L.ws = carve_gdn(s, false, (char*)ws, nullptr);
+        L.no_split = noalloc;
         return hip_status(launch_gdn_fwd(L, st));
     } else {
         GlaLaunch L{};
@@ -283,6 +321,12 @@ int gdn_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, c
             const void* beta, const float* S_in, void* o, float* S_out, void* ws, size_t ws_bytes,
             void* stream) {
     return fwd_common(K_GDN, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream);
+}
+
+// gdn_fwd with the static scratch as its workspace (validated first; no split schedule)
+int gdn_fwd_noalloc(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, const float* S_in, void* o, float* S_out, void* stream) {
+    return fwd_common(K_GDN, s, q, k, v, g, beta, S_in, o, S_out, nullptr, 0, stream, /*noalloc=*/true);
 }
 
 int gla_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,

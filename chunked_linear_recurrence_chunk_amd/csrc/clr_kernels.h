@@ -67,6 +67,7 @@ struct GdnLaunch {
     void *dq, *dk_, *dv_, *dg, *dbeta;
     float* dS_in;
     GdnWs ws;
+    bool no_split = false;  // never take the two-stream split forward
 };
 
 template <typename E> struct GdnPrepArgs {

@@ -41,7 +41,7 @@ struct GdnFwdStages {
 // keeps at least 8 blocks.
 inline int fwd_split_block(const GdnLaunch& L) {
     const int pm = fwd_split_permille();
-    if (pm <= 0 || !L.o || L.NC < 16) return 0;
+    if (pm <= 0 || L.no_split || !L.o || L.NC < 16) return 0;
     int n1 = (int)(((long long)L.NC * pm + 500) / 1000);
     if (n1 < 8) n1 = 8;
     if (n1 > L.NC - 8) n1 = L.NC - 8;

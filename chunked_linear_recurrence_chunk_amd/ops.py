@@ -16,7 +16,8 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libclr.so")
 
-CLR_OK, CLR_EINVAL, CLR_ENOTSUP, CLR_EWORKSPACE, CLR_EHIP = range(5)
+CLR_OK, CLR_EINVAL, CLR_ENOTSUP, CLR_EWORKSPACE, CLR_EHIP, CLR_ESCRATCH = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CLR_NOALLOC_SCRATCH_BYTES
 CLR_F32, CLR_BF16 = 0, 1
 OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD, OP_M2_FWD, OP_M2_BWD, OP_KDA_FWD, OP_KDA_BWD = range(8)
 
@@ -61,6 +62,8 @@ def load(path: Optional[str] = None):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 9 + [sz, vp]
         f.restype = i
+    lib.gdn_fwd_noalloc.argtypes = [sp] + [vp] * 9
+    lib.gdn_fwd_noalloc.restype = i
     for name in ("gdn_bwd", "gla_bwd", "mamba2_bwd", "kda_bwd"):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 15 + [sz, vp]
@@ -242,6 +245,26 @@ def gdn_fwd(q, k, v, g, beta, S_in=None, want_state=True, ws=None, o=None, S_out
     """Gated DeltaNet chunk forward.  Returns (o, S_out).  ``o`` / ``S_out``
     may be preallocated contiguous outputs (e.g. views of a larger tensor)."""
     return _fwd("gdn_fwd", OP_GDN_FWD, q, k, v, g, beta, S_in, want_state, ws, o, S_out)
+
+
+def gdn_fwd_noalloc(q, k, v, g, beta, S_in=None, o=None, S_out=None):
+    """gdn_fwd through the allocation-free entry point: the library's static
+    scratch replaces the workspace, so the call itself allocates nothing on
+    the device once ``o`` and ``S_out`` are given (they are allocated here
+    otherwise).  Returns (o, S_out); raises ClrError with CLR_ESCRATCH when the
+    shape needs more than NOALLOC_SCRATCH_BYTES of workspace."""
+    import torch
+    _validate("gdn", q, k, v, g, beta, S_in)
+    _check_inputs(q, k, v, g, beta, S_in)
+    shape = make_shape(q, v)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = _out(o, (B, T, H, dv), q.dtype, q.device)
+    S_out = _out(S_out, (B, H, dk, dv), torch.float32, q.device)
+    rc = load().gdn_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(S_in), _ptr(o), _ptr(S_out), _stream())
+    _check("gdn_fwd_noalloc", rc)
+    return o, S_out
 
 
 def gla_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None):

@@ -44,7 +44,8 @@
  * -----------------------
  * The caller allocates every buffer, including the workspace `ws` of at least
  * clr_workspace_bytes() bytes (256-byte aligned).  The library allocates no
- * device memory and is re-entrant; calls are enqueued asynchronously on
+ * device memory (its one static device array, the scratch of gdn_fwd_noalloc,
+ * is part of its code object) and is re-entrant; calls are enqueued asynchronously on
  * `stream` (a hipStream_t of the current device; NULL = the default stream).
  * Inputs are never modified; outputs are overwritten.  Calls that share a
  * workspace must be ordered on one stream.  The only state kept between calls
@@ -65,6 +66,8 @@
  *     CLR_ENOTSUP     unsupported dtype or head size
  *     CLR_EWORKSPACE  ws is NULL or smaller than clr_workspace_bytes()
  *     CLR_EHIP        a HIP launch error (reported after enqueueing)
+ *     CLR_ESCRATCH    gdn_fwd_noalloc only: the call needs more workspace
+ *                     than the library's static scratch holds
  * No exception or abort crosses the ABI.  Loading the library needs no GPU.
  */
 #ifndef CLR_H
@@ -82,7 +85,8 @@ typedef enum {
     CLR_EINVAL = 1,
     CLR_ENOTSUP = 2,
     CLR_EWORKSPACE = 3,
-    CLR_EHIP = 4
+    CLR_EHIP = 4,
+    CLR_ESCRATCH = 5
 } clr_status_t;
 
 typedef enum { CLR_F32 = 0, CLR_BF16 = 1 } clr_dtype_t;
@@ -117,6 +121,25 @@ int gdn_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* 
             const void* g, const void* beta, const float* S_in, const void* dO,
             const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
             float* dS_in, void* ws, size_t ws_bytes, void* stream);
+
+/* Allocation-free Gated DeltaNet forward, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same operation, arguments, layouts and results as
+ * gdn_fwd (bit for bit), without the workspace: the library keeps one static
+ * device array of CLR_NOALLOC_SCRATCH_BYTES per GPU for it (taken when the
+ * library's code is loaded on that GPU, held until the process ends) and
+ * allocates nothing per call.  Calls whose workspace, clr_workspace_bytes(
+ * shape, CLR_OP_GDN_FWD), exceeds CLR_NOALLOC_SCRATCH_BYTES return
+ * CLR_ESCRATCH before launching anything (at dk = dv = 128, bf16, the limit
+ * is about 500 64-token blocks x heads, e.g. 16 heads x 1984 tokens).  All
+ * calls on one GPU share its array and each call leaves it dirty: calls on
+ * one GPU must be ordered (one stream, or synchronised); calls that overlap
+ * on one GPU race.  The split-and-overlap schedule (clr_set_fwd_split) is
+ * never used here. */
+#define CLR_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gdn_fwd_noalloc(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+                    const void* g, const void* beta, const float* S_in, void* o, float* S_out,
+                    void* stream);
 
 /* GLA chunk forward; `beta` must be NULL (no delta term, no write scale). */
 int gla_fwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,

@@ -37,8 +37,9 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     ops, lib = _lib()
     assert lib.clr_version() >= 100
-    for s in range(5):
-        assert ops.status_string(s)
+    for s in range(6):
+        assert ops.status_string(s) != "unknown status"
+    assert ops.status_string(6) == "unknown status"
 
 
 def _shape(ops, B=1, T=128, H=2, dk=128, dv=128, dtype=1):
@@ -182,6 +183,23 @@ def test_product_path_has_no_oracle_or_fallback():
         ops.load(os.path.join(ROOT, "does_not_exist.so"))
 
 
+def test_noalloc_forward_rejects_on_the_host():
+    """The allocation-free forward validates like gdn_fwd and refuses shapes
+    whose workspace exceeds its static scratch, before touching the GPU."""
+    ops, lib = _lib()
+    big = _shape(ops, T=2048, H=16)
+    assert ops.workspace_bytes(big, ops.OP_GDN_FWD) > ops.NOALLOC_SCRATCH_BYTES
+    # distinct, aligned, never dereferenced addresses: validation stops at the size
+    fake = [ctypes.c_void_p((i + 1) << 30) for i in range(8)]
+    assert lib.gdn_fwd_noalloc(ctypes.byref(big), *fake, None) == ops.CLR_ESCRATCH
+    assert lib.gdn_fwd_noalloc(ctypes.byref(big), *([None] * 9)) == ops.CLR_EINVAL  # null tensors first
+    fits = _shape(ops, T=1984, H=16)
+    assert ops.workspace_bytes(fits, ops.OP_GDN_FWD) <= ops.NOALLOC_SCRATCH_BYTES
+    assert lib.gdn_fwd_noalloc(ctypes.byref(fits), *([None] * 9)) == ops.CLR_EINVAL
+    assert lib.gdn_fwd_noalloc(ctypes.byref(_shape(ops, dk=96, dv=96)), *([None] * 9)) == ops.CLR_ENOTSUP
+    assert lib.gdn_fwd_noalloc(None, *([None] * 9)) == ops.CLR_EINVAL
+
+
 def test_binding_checks_shapes_and_dtypes_before_the_library():
     """ops.py compares every tensor with (B, T, H, dk, dv) taken from q and v,
     per member, so a wrong gate layout or a bf16 state never reaches the
@@ -230,3 +248,4 @@ def test_binding_checks_shapes_and_dtypes_before_the_library():
     raises(ValueError, "dS_out must have shape", ops.gdn_bwd, q, k, v, g_tok, beta, S, dO, S[:1, :1])
     raises(TypeError, "unsupported dtype", ops.gdn_fwd, q.half(), k.half(), v.half(), g_tok.half(), beta.half(), S)
     raises(ValueError, "gla takes no beta", ops._fwd, "gla_fwd", ops.OP_GLA_FWD, q, k, v, g_ch, beta, S, True, None)
+    raises(ValueError, "g must have shape", ops.gdn_fwd_noalloc, q, k, v, g_ch, beta, S)
