@@ -9,7 +9,15 @@ in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Prints one JSON line (see README of the JSON fields in the design doc).
+Prints one JSON line (the fields are described in DESIGN.md, "Measured").
+
+    python bench.py --workload NAME --profile-summary DIR
+
+writes profiles/NAME.md and the NAME entries of profiles/traffic.json from
+the rocprofv3 output under DIR (kt/: --kernel-trace --stats; fetch/, write/:
+--pmc FETCH_SIZE / WRITE_SIZE; mfma/: --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE; copy/fetch/ and
+copy/write/: the same FETCH/WRITE counters on --calibrate-copy 1 GiB).
 """
 from __future__ import annotations
 
@@ -31,27 +39,68 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/byte
+CLOCK_GHZ, SIMDS = 2.4, 1024  # matrix-core busy cycles are summed over the 1024 SIMDs
+
+# The layer's own tensors each kernel reads or writes (the algorithmic I/O of
+# the pages' Fwd / Bwd, one touch each); the scans touch none of them, only
+# the boundary states.  Sizes per token-head in bytes, see layer_io().
+KERNEL_IO = {
+    "gdn_prep": "k v g beta", "gdn_out": "q k o", "gdn_prep_bwd": "q k v g beta dO",
+    "gdn_bwd_intra": "q k v g beta dO dq dk dv dg dbeta",
+    "kda_prep": "k v g beta", "kda_out": "q k g o", "kda_prep_bwd": "k v g beta", "kda_prep2": "q k g dO",
+    "kda_bwd_wy": "v beta dv dbeta", "kda_bwd_intra": "q k g beta dO dq dk dg",
+}
+for _p in ("gla", "m2"):
+    KERNEL_IO.update({_p + "_prep": "k g", _p + "_out": "q k g o", _p + "_prep_bwd": "q k g",
+                      _p + "_scan_fwd": "v", _p + "_scan_fwd_rec": "v", _p + "_scan_bwd": "dO",
+                      _p + "_bwd_intra": "q k v g dO dq dk dv dg"})
+# boundary states each scan reads or writes (fp32 [B, H, dk, dv])
+SCAN_STATES = {"gdn_scan_fwd": 2, "gdn_scan_pair": 3, "kda_scan_fwd": 2, "kda_scan_pair": 3,
+               "gla_scan_fwd": 2, "gla_scan_fwd_rec": 1, "gla_scan_bwd": 2,
+               "m2_scan_fwd": 2, "m2_scan_fwd_rec": 1, "m2_scan_bwd": 2}
+
+
+def layer_io(name: str, kind: str, dk: int, dv: int, es: int) -> int:
+    """Algorithmic bytes per token-head of one kernel: the layer tensors it
+    touches (q, k, dq, dk: dk elements; v, o, dO, dv: dv; g, dg: dk for the
+    per-channel gates, 1 otherwise; beta, dbeta: 1), each once."""
+    gk = dk if kind in ("gla", "kda") else 1
+    size = {"q": dk, "k": dk, "dq": dk, "dk": dk, "v": dv, "o": dv, "dO": dv, "dv": dv,
+            "g": gk, "dg": gk, "beta": 1, "dbeta": 1}
+    return sum(size[t] for t in KERNEL_IO.get(name, "").split()) * es
+
+
+def scan_phase_bytes(name: str, dk: int, dv: int, es: int) -> int:
+    """The state-scan phase's per-unit traffic of the survey's section 8(d):
+    per token-head, one direction of the scan reads its operands (W, K, U~:
+    2 dk + dv elements) and writes the new values (dv elements) and the state
+    entering each 64-token block in fp32 (dk dv / 64 floats): about 2 KB at
+    dk = dv = 128.  The backward's pair launch runs two directions."""
+    one = (2 * dk + 2 * dv) * es + dk * dv * 4 // 64
+    return 2 * one if name.endswith("_pair") else one
 
 
 def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
-    """Algorithmic (bytes, flops) of one kernel per 64-token block and head
-    (element size es; fp32 for gates and states kept in fp32).  Bytes count
-    every tensor the kernel reads or writes once; flops count its dense
-    products as executed (2 m n k each).  The definitions are listed per
-    kernel in DESIGN.md."""
+    """The design's model of one kernel per 64-token block and head: (bytes,
+    flops), bytes counting every tensor it reads or writes once, workspace
+    included (element size es; fp32 where the design keeps fp32), flops its
+    dense products as executed (2 m n k each; a split operand executes a
+    product twice, two split operands three times).  This is the traffic the
+    design has to move, not the algorithmic I/O (layer_io)."""
     Ck, Cv, kv, CC, f4 = C * dk, C * dv, dk * dv, C * C, 4
     W = {
-        # Gated DeltaNet (dk == dv)
-        "gdn_prep": (2 * Ck * es + 2 * C * es + C * f4 + 3 * Ck * es,
-                     2 * CC * dk + 2 * (2 * CC * dk) + C ** 3 // 3),
-        "gdn_scan_fwd": (C * f4 + 3 * Ck * es + kv * es + Cv * es, 2 * (2 * C * kv)),
-        "gdn_out": (2 * Ck * es + C * f4 + kv * es + Cv * es + Cv * es,
-                    2 * CC * dk + 2 * C * kv + 2 * CC * dv),
-        "gdn_scan_bwd": (C * f4 + 2 * Ck * es + kv * f4 + Cv * es + kv * es + Cv * es, 2 * (2 * C * kv)),
+        # Gated DeltaNet (dk == dv): Ut, U, dvloc, dU fp32; dh a bf16 pair
+        "gdn_prep": (2 * Ck * es + 2 * C * es + 2 * C * f4 + 2 * Ck * es + Cv * f4,
+                     2 * CC * dk + 2 * (2 * (2 * CC * dk)) + C ** 3 // 3),
+        "gdn_scan_fwd": (C * f4 + 2 * Ck * es + Cv * f4 + kv * es + Cv * f4, 3 * (2 * C * kv)),
+        "gdn_out": (2 * Ck * es + C * f4 + kv * es + Cv * f4 + Cv * es,
+                    2 * CC * dk + 2 * C * kv + 3 * (2 * CC * dv)),
+        "gdn_scan_bwd": (C * f4 + 2 * Ck * es + kv * f4 + Cv * f4 + 2 * kv * es + Cv * f4,
+                         3 * (2 * C * kv) + 2 * C * kv // 2),
         # reads T^T and the decayed Gram tiles that the backward's prep wrote
-        "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 2 * kv * es + 2 * Cv * es + 3 * Ck * es + 2 * C * es
+        "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 3 * kv * es + 2 * Cv * f4 + 3 * Ck * es + 2 * C * es
                           + CC * es + CC * f4,
-                          3 * (2 * C * kv) + 11 * (2 * CC * dk) + 2 * (2 * C ** 3)),
+                          6 * (2 * C * kv) + 16 * (2 * CC * dk) + 2 * (2 * C ** 3)),
     }
     # GLA (per-channel gate, gk = dk gate values per token) and its scalar-gate
     # Mamba-2 member on the same kernels (gk = 1)
@@ -71,7 +120,7 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
     # the backward's prep also reads Q and dO and writes the reverse scan's
     # operands W^T, Kh, dvloc^T, R (fp32) and T^T, K K^T * G for the block
     # adjoints; products P = Q K^T, P^T dO, Z = Gam Q - P W, R = Z^T dO
-    W["gdn_prep_bwd"] = (W["gdn_prep"][0] + 2 * Ck * es + 3 * Ck * es + kv * f4 + CC * es + CC * f4,
+    W["gdn_prep_bwd"] = (W["gdn_prep"][0] + 2 * Ck * es + 2 * Ck * es + Cv * f4 + kv * f4 + CC * es + CC * f4,
                          W["gdn_prep"][1] + 2 * CC * dk + 2 * CC * dv + 2 * CC * dk + 2 * C * kv)
     # KDA (per-channel gate, dk == dv): the Gated DeltaNet data flow with
     # per-channel decays (exp(b_C) per channel in place of the per-token
@@ -134,9 +183,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if absent or taken on different kernel sources."""
+def load_counters(workload: str, kernel: str):
+    """The committed rocprofv3 counter summary of one kernel (HBM bytes per
+    launch, matrix-core busy cycles and flops per launch), or None if absent
+    or taken on different kernel sources."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         d = json.load(open(p))
@@ -145,20 +195,177 @@ def load_traffic(workload: str, kernel: str):
     e = d.get(workload, {}).get(kernel)
     if not e or e.get("source_hash") != source_hash():
         return None
-    return e.get("bytes_per_launch")
+    return e
 
 
-def cpu_baseline(cfg: dict, x: dict, budget_chunks: int):
+def load_traffic(workload: str, kernel: str):
+    e = load_counters(workload, kernel)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def launch_name(mangled: str, kind: str) -> str:
+    """The library's launch name of a kernel symbol in a rocprofv3 trace
+    (the symbol is a template instantiation; the flags that tell launches of
+    one kernel apart are its bool template arguments, in order)."""
+    import re
+    m = re.match(r"_ZN3clr(\d+)", mangled)
+    if not m:
+        return mangled
+    n = int(m.group(1))
+    base = mangled[m.end():m.end() + n]
+    base = base[:-len("_kernel")] if base.endswith("_kernel") else base
+    flags = re.findall(r"Lb([01])E", mangled[m.end() + n:])
+    if base == "gdn_prep":
+        return "gdn_prep_bwd" if flags[0] == "1" else "gdn_prep"
+    if base == "gdn_scan_fwd":  # <E, DK, DV, HNAT, PCD, NP>
+        return "kda_scan_fwd" if flags[1] == "1" else "gdn_scan_fwd"
+    if base == "gdn_scan_pair":  # <E, DK, DV, PCD, NP>
+        return "kda_scan_pair" if flags[0] == "1" else "gdn_scan_pair"
+    if base.startswith("gla_"):
+        pre = {"gla": "gla_", "mamba2": "m2_", "kda": "kda_"}.get(kind, "gla_")
+        rest = base[4:]
+        if rest == "prep":  # <E, DK, BWD, SG>
+            rest = "prep_bwd" if flags[0] == "1" else "prep"
+        elif rest == "scan_fwd":  # <E, DK, DV, HNAT>
+            rest = "scan_fwd_rec" if flags[0] == "1" else "scan_fwd"
+        return pre + rest
+    return base  # kda_prep serves both the forward and the backward's prep
+
+
+def profile_summary(workload: str, d: str) -> None:
+    """Summarise the rocprofv3 passes under d (see the module docstring) into
+    profiles/<workload>.md and the workload's entries of profiles/traffic.json."""
+    import csv
+    import glob
+    from collections import defaultdict
+    from chunked_linear_recurrence_chunk_amd import inputs
+    cfg = inputs.CONFIGS[workload]
+    kind = cfg["kind"]
+
+    def one(pattern):
+        f = glob.glob(os.path.join(d, pattern))
+        if not f:
+            raise SystemExit(f"no {pattern} under {d}")
+        return list(csv.DictReader(open(f[0])))
+
+    def counters(sub):
+        per = defaultdict(lambda: defaultdict(list))
+        for r in one(sub + "/*counter_collection.csv"):
+            per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+
+    copy_dir = os.path.join(d, "..", "copy")
+    cf = counters_copy = {}
+    for sub in ("fetch", "write"):
+        rows = [r for r in csv.DictReader(open(glob.glob(os.path.join(copy_dir, sub, "*counter_collection.csv"))[0]))
+                if "copyBuffer" in r["Kernel_Name"]]
+        cf[sub] = sum(float(r["Counter_Value"]) for r in rows) / len(rows)
+    gib_kib = (1 << 30) / 1024
+    f_scale, w_scale = gib_kib / cf["fetch"], gib_kib / cf["write"]
+    stats = {}
+    for r in one("kt/*kernel_stats.csv"):
+        name = launch_name(r["Name"], kind)
+        st = stats.setdefault(name, {"calls": 0, "ns": 0.0, "pct": 0.0})
+        st["calls"] += int(r["Calls"])
+        st["ns"] += float(r["TotalDurationNs"])
+        st["pct"] += float(r["Percentage"])
+    fetch, write, mfma = counters("fetch"), counters("write"), counters("mfma")
+
+    def by_name(c):
+        out = defaultdict(list)
+        for k, v in c.items():
+            out[launch_name(k, kind)].append(v)
+        return {k: {c2: sum(x[c2] for x in vs) / len(vs) for c2 in vs[0]} for k, vs in out.items()}
+    fetch, write, mfma = by_name(fetch), by_name(write), by_name(mfma)
+    h = source_hash()
+    tp = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        allt = json.load(open(tp))
+    except (OSError, ValueError):
+        allt = {}
+    ent = {}
+    rows = []
+    for name, st in sorted(stats.items(), key=lambda kv: -kv[1]["ns"]):
+        if name not in fetch or name not in write:
+            continue
+        fk, wk = fetch[name]["FETCH_SIZE"], write[name]["WRITE_SIZE"]
+        byts = int(round(fk * 1024 * f_scale + wk * 1024 * w_scale))
+        e = {"bytes_per_launch": byts, "source_hash": h, "fetch_kib": fk, "write_kib": wk}
+        mf = mfma.get(name)
+        if mf:
+            e.update(mfma_flops=mf["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512, mfma_busy_cycles=mf["SQ_VALU_MFMA_BUSY_CYCLES"],
+                     sq_busy_cycles=mf["SQ_BUSY_CYCLES"], grbm_gui_active=mf["GRBM_GUI_ACTIVE"])
+        ent[name] = e
+        avg_us = st["ns"] / st["calls"] / 1e3
+        busy = e.get("mfma_busy_cycles")
+        rows.append(f"| {name} | {st['calls']} | {avg_us:.2f} | {st['pct']:.1f} | {fk:.1f} | {wk:.1f} | "
+                    f"{byts / 1e6:.1f} | {byts / (avg_us * 1e-6) / 1e9:.0f} | "
+                    + (f"{e['mfma_flops'] / 1e9:.2f} | {busy:.3g} | {busy / (SIMDS * CLOCK_GHZ * 1e3 * avg_us):.3f} | "
+                       f"{e['mfma_flops'] / (avg_us * 1e-6) / 1e12:.0f} |" if busy is not None else "- | - | - | - |"))
+    allt[workload] = ent
+    with open(tp, "w") as f:
+        json.dump(allt, f, indent=1, sort_keys=True)
+    args = f"--workload {workload}"
+    md = [f"# rocprofv3 summary: {workload}", "",
+          f"Workload: {cfg}; one launch processes one sequence chunk.", "",
+          "Commands (run from /tmp with TMPDIR=/tmp; R = repository root on the GPU box; "
+          "D = $R/gpurun_out/prof/" + workload + "):", "", "```",
+          f"rocprofv3 --kernel-trace --stats -T -f csv -d $D/kt -o run -- python3 $R/bench.py {args} --steps 5 --warmup 2 --no-cpu",
+          f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d $D/fetch -o run -- python3 $R/bench.py {args} --steps 1 --warmup 1 --no-cpu",
+          f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d $D/write -o run -- python3 $R/bench.py {args} --steps 1 --warmup 1 --no-cpu",
+          "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -T -f csv "
+          f"-d $D/mfma -o run -- python3 $R/bench.py {args} --steps 1 --warmup 1 --no-cpu",
+          "rocprofv3 --pmc FETCH_SIZE -T -f csv -d $R/gpurun_out/prof/copy/fetch -o run -- python3 $R/bench.py --calibrate-copy 1073741824",
+          "rocprofv3 --pmc WRITE_SIZE -T -f csv -d $R/gpurun_out/prof/copy/write -o run -- python3 $R/bench.py --calibrate-copy 1073741824",
+          f"python3 bench.py {args} --profile-summary gpurun_out/prof/{workload}", "```", "",
+          f"Counter calibration (1 GiB device copy): FETCH_SIZE reads {cf['fetch']:.0f} KiB, WRITE_SIZE "
+          f"{cf['write']:.0f} KiB per dispatch -> scale factors fetch x{f_scale:.3f}, write x{w_scale:.3f}.", "",
+          "Matrix cores: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 is the bf16 matrix flops a launch executed; "
+          "SQ_VALU_MFMA_BUSY_CYCLES counts matrix-core busy cycles summed over the 1024 SIMDs (16 per "
+          "16x16x32 bf16 instruction), so busy / (1024 x 2.4 GHz x duration) is the fraction of the "
+          "chip's matrix-core time in use, equal to (flops / duration) / 2.5 PFLOP/s.", "",
+          f"Kernel sources hash: {h}", ""]
+    if kind == "kda":
+        md += ["`kda_prep` runs in the forward and, writing a few more outputs, in the backward: the trace "
+               "merges both (one kernel symbol).", ""]
+    md += ["| kernel | calls | avg us | share % | FETCH KiB/disp | WRITE KiB/disp | HBM MB/launch (scaled) | HBM GB/s | "
+           "MFMA GFLOP/launch | MFMA busy cycles | MFMA busy frac | MFMA TFLOP/s |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"] + rows
+    open(os.path.join(ROOT, "profiles", workload + ".md"), "w").write("\n".join(md) + "\n")
+    print("wrote", os.path.join("profiles", workload + ".md"))
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _compiler() -> str:
+    import subprocess
+    try:
+        return subprocess.run(["gcc", "--version"], capture_output=True, text=True).stdout.splitlines()[0]
+    except (OSError, IndexError):
+        return "unknown"
+
+
+def cpu_baseline(cfg: dict, x: dict, budget_chunks: int, reps: int = 20, reps1: int = 5):
     """The fp64 oracle (as it stands) on the host cores over a bounded sample:
-    the first `budget_chunks` sequence chunks of the workload, forward then
-    backward with boundary-state hand-off."""
+    the first `budget_chunks` sequence chunks of the workload (at most 4096
+    tokens), forward then backward with boundary-state hand-off.  The median
+    of `reps` runs on all cores, and of `reps1` runs on one core."""
+    import statistics
+
     import numpy as np
     from oracle import oracle
     threads = len(os.sched_getaffinity(0))
-    oracle.set_threads(threads)
     T, N = cfg["T"], cfg["N"]
     L = T // N
-    n = max(1, min(budget_chunks, N))
+    n = max(1, min(budget_chunks, N, max(1, 4096 // L)))
     Ts = L * n
     per_token = ("x", "dy") if cfg["kind"] == "shortconv" else ("q", "k", "v", "g", "beta", "dO")
     sl = {k: (np.ascontiguousarray(v[:, :Ts]).astype(np.float64) if k in per_token else v.astype(np.float64))
@@ -183,18 +390,28 @@ def cpu_baseline(cfg: dict, x: dict, budget_chunks: int):
             oracle.gla_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], None, n)
         else:
             oracle.mamba2_chunked(sl["q"], sl["k"], sl["v"], sl["g"], sl["S_in"], sl["dO"], None, n)
-    t0 = time.perf_counter()
-    once()
-    reps, dt = 1, time.perf_counter() - t0
-    # repeat a cheap sample until about 10 s of oracle work has been timed
-    while dt < 10.0 and reps < 40:
-        once()
-        reps += 1
-        dt = time.perf_counter() - t0
-    return {"value": cfg["B"] * Ts * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+
+    def median_time(k, nthreads):
+        oracle.set_threads(nthreads)
+        ts = []
+        for _ in range(k):
+            t0 = time.perf_counter()
+            once()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts), sum(ts)
+
+    once()  # page the sample in
+    med, tot = median_time(reps, threads)
+    med1, tot1 = median_time(reps1, 1)
+    oracle.set_threads(threads)
+    tok = cfg["B"] * Ts
+    return {"value": tok / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "single_thread": tok / med1, "cpu_model": _cpu_model(), "compiler": _compiler(),
+            "build": "gcc -O3 -march=x86-64-v3 -fopenmp, fp64; OpenMP over (batch, head)",
             "sample": f"{'all' if n == N else f'first {n} of'} {N} sequence chunks ({cfg['B']}x{Ts} tokens, "
                       + (f"all {cfg['C']} channels" if cfg["kind"] == "shortconv" else f"all {cfg['H']} heads")
-                      + f"), fp64 fwd+bwd, {reps} run(s), {dt:.1f} s"}
+                      + f"), fp64 fwd+bwd; median of {reps} runs on {threads} threads ({tot:.1f} s) "
+                      + f"and of {reps1} on one ({tot1:.1f} s)"}
 
 
 def main():
@@ -205,9 +422,13 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-chunks", type=int, default=64, help="sequence chunks in the CPU-baseline sample")
+    ap.add_argument("--profile-summary", metavar="DIR", help="summarise rocprofv3 output under DIR into profiles/")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
+    if args.profile_summary:
+        profile_summary(args.workload, args.profile_summary)
+        return
     if args.calibrate_copy:
         import torch
         src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda")
@@ -303,34 +524,93 @@ def main():
 
     kernels = {}
     tot_ms = sum(v[1] for v in rep.values())
-    tot_flops = 0.0
+    conv = cfg["kind"] == "shortconv"
+    th = 0 if conv else B * cfg["H"] * (T // N)  # token-heads per launch (one sequence chunk)
+    nst = 0 if conv else B * cfg["H"] * cfg["dk"] * cfg["dv"] * 4  # bytes of one fp32 boundary state
     for name, (launches, total_ms) in rep.items():
         avg_us = total_ms / launches * 1e3
-        work = launch_work(name)
         ent = {"launches_per_step": launches // args.steps, "avg_us": round(avg_us, 2),
                "share": round(total_ms / tot_ms, 3)}
+        work = launch_work(name)
+        if conv:
+            alg = work[0] if work else None
+        elif "scan" in name:
+            alg = scan_phase_bytes(name, cfg["dk"], cfg["dv"], es) * th + SCAN_STATES.get(name, 0) * nst
+        else:
+            alg = layer_io(name, cfg["kind"], cfg["dk"], cfg["dv"], es) * th
+        if alg:
+            ent.update(alg_bytes=alg, alg_gbs=round(alg / (avg_us * 1e-6) / 1e9, 1))
         if work:
-            byts, flops = work
-            if cfg["kind"] != "shortconv":  # short-convolution flops are vector ALU work, not MFMA
-                tot_flops += flops * launches / args.steps
-            ent.update(alg_bytes=byts, alg_flops=flops,
-                       gbs=round(byts / (avg_us * 1e-6) / 1e9, 1),
-                       tflops=round(flops / (avg_us * 1e-6) / 1e12, 2))
+            ent.update(model_bytes=work[0], model_flops=work[1],
+                       model_tflops=round(work[1] / (avg_us * 1e-6) / 1e12, 2))
+        ctr = load_counters(args.workload, name)
+        if ctr:
+            ent.update(hbm_bytes=ctr["bytes_per_launch"],
+                       hbm_gbs=round(ctr["bytes_per_launch"] / (avg_us * 1e-6) / 1e9, 1))
+            if alg:
+                ent["hbm_over_alg"] = round(ctr["bytes_per_launch"] / alg, 2)
+            if ctr.get("mfma_busy_cycles") is not None:
+                ent["mfma_busy"] = round(ctr["mfma_busy_cycles"] / (SIMDS * CLOCK_GHZ * 1e3 * avg_us), 4)
+                ent["mfma_tflops"] = round(ctr["mfma_flops"] / (avg_us * 1e-6) / 1e12, 2)
         kernels[name] = ent
         print(f"[bench]   {name:18s} {ent}", file=sys.stderr, flush=True)
     dom = max(rep, key=lambda k: rep[k][1])
-    dk_ent = kernels[dom]
-    bound = "hbm" if dk_ent["alg_flops"] / dk_ent["alg_bytes"] < RIDGE else "mfma"
+    de = kernels[dom]
+    flops = de.get("model_flops", 0)
+    bound = "hbm" if (conv or flops / de["alg_bytes"] < RIDGE) else "mfma"
     peak_flops = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
     if bound == "hbm":
-        achieved, peak, unit = dk_ent["gbs"], PEAK_HBM_GBS, "GB/s"
+        achieved, peak, unit = de["alg_gbs"], PEAK_HBM_GBS, "GB/s"
     else:
-        achieved, peak, unit = dk_ent["tflops"], peak_flops, "TFLOP/s"
+        achieved, peak, unit = round(flops / (de["avg_us"] * 1e-6) / 1e12, 2), peak_flops, "TFLOP/s"
+    traffic = load_traffic(args.workload, dom)
     roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": load_traffic(args.workload, dom),
-                "kernel": dom, "avg_us": dk_ent["avg_us"], "alg_bytes_per_launch": dk_ent["alg_bytes"],
-                "alg_flops_per_launch": dk_ent["alg_flops"]}
-    mfma_util = tot_flops / (ms * 1e-3) / (peak_flops * 1e12)
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "traffic_over_alg": round(traffic / de["alg_bytes"], 2) if traffic else None,
+                "kernel": dom, "avg_us": de["avg_us"], "alg_bytes_per_launch": de["alg_bytes"]}
+
+    # the two phases the targets name: intra-chunk (every block-parallel
+    # kernel) against the bf16 matrix-core peak, state scan against HBM
+    phases = None
+    if not conv:
+        per_step = {k: rep[k][1] / args.steps for k in rep}  # ms
+        intra = [k for k in rep if "scan" not in k]
+        scan = [k for k in rep if "scan" in k]
+        t_in = sum(per_step[k] for k in intra) * 1e-3
+        t_sc = sum(per_step[k] for k in scan) * 1e-3
+        dk, dv, C = cfg["dk"], cfg["dv"], 64
+        if cfg["kind"] == "gdn":
+            # section 8(d): fwd 2C(3dk+2dv) + 6 dk dv + C^2/3, bwd C(18dk+10dv) + 16 dk dv + 4.3 C^2
+            # per token-head, less the scans' 12 dk dv
+            f_th = (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv + C * C / 3 + C * (18 * dk + 10 * dv)
+                    + 16 * dk * dv + 4.3 * C * C - 12 * dk * dv)
+            f_in, f_src = f_th * B * cfg["H"] * T, "algorithmic, section 8(d)"
+        else:
+            f_in = sum(kernels[k].get("model_flops", 0) * rep[k][0] / args.steps for k in intra)
+            f_src = "products as executed"
+        ph_in = {"kernels": intra, "us_per_step": round(t_in * 1e6, 1), "flops_per_step": f_in, "flops": f_src,
+                 "tflops": round(f_in / t_in / 1e12, 1), "frac_of_mfma_peak": round(f_in / t_in / 1e12 / peak_flops, 4),
+                 "target": 0.5}
+        busy = [(load_counters(args.workload, k), k) for k in intra]
+        if all(c and c.get("mfma_busy_cycles") is not None for c, _ in busy):
+            cyc = sum(c["mfma_busy_cycles"] * rep[k][0] / args.steps for c, k in busy)
+            ph_in["mfma_busy_counter"] = round(cyc / (SIMDS * CLOCK_GHZ * 1e9 * t_in), 4)
+        tr = [load_traffic(args.workload, k) for k in scan]
+        ph_sc = {"kernels": scan, "us_per_step": round(t_sc * 1e6, 1), "target": 0.6}
+        if scan and all(tr):
+            byts = sum(t * rep[k][0] / args.steps for t, k in zip(tr, scan))
+            ph_sc.update(bytes_per_step=byts, bytes="rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated",
+                         gbs=round(byts / t_sc / 1e9, 1), frac_of_hbm_peak=round(byts / t_sc / 1e9 / PEAK_HBM_GBS, 4))
+        elif scan:
+            byts = sum(kernels[k]["alg_bytes"] * rep[k][0] / args.steps for k in scan)
+            ph_sc.update(bytes_per_step=byts, bytes="section 8(d) per-unit figure (no counters at these sources)",
+                         gbs=round(byts / t_sc / 1e9, 1), frac_of_hbm_peak=round(byts / t_sc / 1e9 / PEAK_HBM_GBS, 4))
+        phases = {"intra": ph_in, "scan": ph_sc}
+    mfma_util = None
+    cs = [(load_counters(args.workload, k), k) for k in rep]
+    if not conv and all(c and c.get("mfma_flops") is not None for c, _ in cs):
+        mfma_util = round(sum(c["mfma_flops"] * rep[k][0] / args.steps for c, k in cs) / (ms * 1e-3)
+                          / (peak_flops * 1e12), 4)
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -338,11 +618,12 @@ def main():
            "data": "synthetic",
            "config": ({"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "C": cfg["C"], "W": cfg["W"],
                        "act": "silu" if cfg["act"] else "identity", "seq_chunks": N}
-                      if cfg["kind"] == "shortconv" else
+                      if conv else
                       {"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "H": cfg["H"], "dk": cfg["dk"],
                        "dv": cfg["dv"], "seq_chunks": N, "block": 64}),
-           "mfma_util": round(mfma_util, 4),
-           "roofline": roofline, "kernels": kernels}
+           "mfma_util": mfma_util,
+           "peak_mem_gb": round(torch.cuda.max_memory_allocated() / 1e9, 3),
+           "roofline": roofline, "phases": phases, "kernels": kernels}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_chunks)
     print(json.dumps(out), flush=True)
