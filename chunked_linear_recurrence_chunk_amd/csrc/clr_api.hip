@@ -30,6 +30,7 @@ int check_shape(const clr_shape_t* s, bool gla, bool bwd) {
     if (!s) return CLR_EINVAL;
     if (s->B < 1 || s->H < 1 || s->T < 0 || s->dk < 1 || s->dv < 1) return CLR_EINVAL;
     if (s->dtype != CLR_F32 && s->dtype != CLR_BF16) return CLR_ENOTSUP;
+    if (s->chunk != 0 && s->chunk != BLK) return CLR_ENOTSUP;  // the kernels' block size
     if (gla ? !gla_shape_ok(s->dk, s->dv) : !gdn_shape_ok(s->dk, s->dv)) return CLR_ENOTSUP;
     if (bwd && s->dtype == CLR_F32 && !(s->dk == 32 && s->dv == 32)) return CLR_ENOTSUP;
     // 64-bit element counts must stay addressable

@@ -23,8 +23,10 @@ OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD, OP_M2_FWD, OP_M2_BWD, OP_KDA_FWD
 
 
 class ClrShape(ctypes.Structure):
+    # chunk: the kernel-level block (0 = the library's 64 tokens)
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
-                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("chunk", ctypes.c_int32)]
 
 
 class ClrConvShape(ctypes.Structure):

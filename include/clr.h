@@ -34,8 +34,10 @@
  *     beta, dbeta       GDN: [B, T, H]     GLA: must be NULL     (shape.dtype)
  *     S_in, S_out, dS_out, dS_in   [B, H, dk, dv]  always float32
  * Supported head sizes: GDN (dk, dv) in {(32,32), (64,64), (128,128)};
- * GLA additionally (128, 256).  The float32 backward supports (32, 32) only
- * (CLR_ENOTSUP otherwise).  Any T >= 0 (a ragged last 64-token block is
+ * GLA additionally (128, 256).  The float32 backward supports (32, 32) only.
+ * Others, among them GDN and KDA at dk = dv = 256 (the block kernels' LDS
+ * tiles and the scans' per-block operands would not fit a CU at that size),
+ * return CLR_ENOTSUP.  Any T >= 0 (a ragged last 64-token block is
  * handled by treating the missing tokens as identity steps; with T == 0 the
  * per-token tensors are empty and may be NULL, and the state passes through:
  * S_out = S_in, dS_in = dS_out).
@@ -102,9 +104,14 @@ typedef enum {
     CLR_OP_KDA_BWD = 7
 } clr_op_t;
 
+/* Shape of a call.  `chunk` is the kernel-level block of the chunkwise form
+ * (the "kernel-level chunks" of the StateFlow paper, Sec. 3.1), in tokens:
+ * 0 or 64, the only block size the kernels are built for (any other value
+ * returns CLR_ENOTSUP).  Being last, it is 0 when an initialiser omits it. */
 typedef struct {
     int32_t B, T, H, dk, dv;
     int32_t dtype; /* clr_dtype_t */
+    int32_t chunk; /* 0 or 64 */
 } clr_shape_t;
 
 /* Workspace bytes needed by `op` (clr_op_t) at `shape`; 0 on invalid input. */

@@ -249,3 +249,25 @@ def test_binding_checks_shapes_and_dtypes_before_the_library():
     raises(TypeError, "unsupported dtype", ops.gdn_fwd, q.half(), k.half(), v.half(), g_tok.half(), beta.half(), S)
     raises(ValueError, "gla takes no beta", ops._fwd, "gla_fwd", ops.OP_GLA_FWD, q, k, v, g_ch, beta, S, True, None)
     raises(ValueError, "g must have shape", ops.gdn_fwd_noalloc, q, k, v, g_ch, beta, S)
+
+
+def test_shape_chunk_field_and_unsupported_sizes():
+    """The kernel-level block is 64 tokens (chunk 0 or 64); Gated DeltaNet at
+    dk = dv = 256 and the fp32 backward beyond d = 32 are not built."""
+    ops, lib = _lib()
+    base = ops.workspace_bytes(_shape(ops), ops.OP_GDN_FWD)
+    s64 = _shape(ops)
+    s64.chunk = 64
+    assert ops.workspace_bytes(s64, ops.OP_GDN_FWD) == base
+    for bad in (16, 32, 128, -1):
+        s = _shape(ops)
+        s.chunk = bad
+        assert ops.workspace_bytes(s, ops.OP_GDN_FWD) == 0
+        assert lib.gdn_fwd(ctypes.byref(s), *([None] * 9), 0, None) == ops.CLR_ENOTSUP
+    for op in (ops.OP_GDN_FWD, ops.OP_GDN_BWD, ops.OP_KDA_FWD, ops.OP_KDA_BWD):
+        assert ops.workspace_bytes(_shape(ops, dk=256, dv=256), op) == 0
+    s256 = _shape(ops, dk=256, dv=256)
+    assert lib.gdn_fwd(ctypes.byref(s256), *([None] * 9), 0, None) == ops.CLR_ENOTSUP
+    assert lib.gdn_bwd(ctypes.byref(s256), *([None] * 15), 0, None) == ops.CLR_ENOTSUP
+    for d in (64, 128):
+        assert ops.workspace_bytes(_shape(ops, dk=d, dv=d, dtype=0), ops.OP_GDN_BWD) == 0
