@@ -2,7 +2,9 @@
 times (the sequence-chunk driver):
 
   * the oracle recomputes whole sampled heads (every head is an independent
-    recurrence, so a head slice of the inputs is an exact sub-problem);
+    recurrence, so a head slice of the inputs is an exact sub-problem): eight
+    heads per Gated DeltaNet workload, one per residue h mod 8 (the XCD its
+    scan work-groups run on), in parallel on the host cores;
   * identities that hold for the exact layer at any size are checked on every
     head of the GPU result (q.dq = o.do per token; GDN and KDA k.dk + v.dv = 2 beta dbeta;
     GLA and Mamba-2 k.dk = v.dv; joint linearity sum v.dv + <S_in, dS_in> =
@@ -130,8 +132,17 @@ def _full(name, pairs, compare_unchunked):
     _check_sampled(cfg, got, refs)
 
 
+def _residue_heads(H, n=8):
+    """n heads covering every residue h mod 8: the scans place all value
+    slices of head h on XCD h mod 8, so this samples every XCD."""
+    step = H // n
+    return [(0, (i * step + i) % H) for i in range(n)] if H >= 2 * n else [(0, i) for i in range(min(n, H))]
+
+
 def test_full_gdn_H16_T8192():
-    _full("gdn_bf16_H16_T8192_d128", [(0, 0), (0, 9)], True)
+    pairs = _residue_heads(16)
+    assert sorted(h % 8 for _, h in pairs) == list(range(8))
+    _full("gdn_bf16_H16_T8192_d128", pairs, True)
 
 
 def test_full_kda_H16_T8192():
@@ -147,8 +158,12 @@ def test_full_mamba2_B4_H16_T4096():
 
 
 def test_full_gdn_H32_T65536():
-    _full("gdn_bf16_H32_T65536_d128", [(0, 17)], True)
+    pairs = _residue_heads(32)
+    assert sorted(h % 8 for _, h in pairs) == list(range(8))
+    _full("gdn_bf16_H32_T65536_d128", pairs, True)
 
 
 def test_full_gdn_H16_T262144():
-    _full("gdn_bf16_H16_T262144_d128", [(0, 3)], True)
+    pairs = _residue_heads(16)
+    assert sorted(h % 8 for _, h in pairs) == list(range(8))
+    _full("gdn_bf16_H16_T262144_d128", pairs, True)
