@@ -95,9 +95,11 @@ GdnWs carve_kda(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     Carver c{base};
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
     GdnWs w{};
+    // Ut, dvloc and dU fp32; the decayed keys as a bf16 hi/lo pair (gdn_kernels.h, "Precision")
     w.W = c.take(nb * BLK * dk * es);
     w.KhT = c.take(nb * BLK * dk * es);
-    w.UtT = c.take(nb * BLK * dv * es);
+    if (es == 2) w.KhT_lo = c.take(nb * BLK * dk * es);
+    w.UtT = c.take(nb * BLK * dv * 4);
     w.hT = c.take(nb * dk * dv * es);
     w.eCk = (float*)c.take(nb * 256 * 4);
     w.Utok = c.take((size_t)s->B * s->T * s->H * dv * es);
@@ -105,9 +107,10 @@ GdnWs carve_kda(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
         w.Rt = (float*)c.take(nb * dk * dv * 4);
         w.WT = c.take(nb * BLK * dk * es);
         w.Kh = c.take(nb * BLK * dk * es);
-        w.dvlT = c.take(nb * BLK * dv * es);
+        if (es == 2) w.Kh_lo = c.take(nb * BLK * dk * es);
+        w.dvlT = c.take(nb * BLK * dv * 4);
         w.dhT = c.take(nb * dk * dv * es);
-        w.dUT = c.take(nb * BLK * dv * es);
+        w.dUT = c.take(nb * BLK * dv * 4);
         w.dM = (float*)c.take(nb * BLK * BLK * 4);
         w.dX = (float*)c.take(nb * BLK * dk * 4);
         w.TT = c.take(nb * BLK * BLK * es);

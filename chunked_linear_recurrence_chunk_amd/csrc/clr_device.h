@@ -186,6 +186,9 @@ template <> __device__ __forceinline__ Frag2<bf16> split8<bf16>(f32x4 a, f32x4 b
     }
     return x;
 }
+// A split pair from its two stored halves (fp32: the value itself).
+__device__ __forceinline__ Frag2<bf16> pair_of(const Frag<bf16>& hi, const Frag<bf16>& lo) { return Frag2<bf16>{hi, lo}; }
+__device__ __forceinline__ Frag2<float> pair_of(const Frag<float>& hi, const Frag<float>&) { return Frag2<float>{hi}; }
 template <> __device__ __forceinline__ Frag2<float> split8<float>(f32x4 a, f32x4 b) {
     Frag2<float> x;
     x.hi.lo = a;
@@ -479,6 +482,19 @@ __device__ __forceinline__ void store_untiled_split(const TiledRegs<float, R, C,
         } else {
             *(f32x4*)(hi + row * P + c) = v;
         }
+    }
+}
+
+// Tiled fp32 global X[R][C] -> row-major LDS in the element type (rounded).
+template <typename E, int R, int C, int P, int NT = 256>
+__device__ __forceinline__ void store_untiled_round(const TiledRegs<float, R, C, NT>& x, E* dst) {
+#pragma unroll
+    for (int j = 0; j < x.N; ++j) {
+        const int u = threadIdx.x + NT * j;
+        if (u >= x.UNITS) continue;
+        const int f = u >> 7, half = (u >> 6) & 1, lane = u & 63;
+        const int row = 16 * (f / (C / 32)) + (lane & 15), c = 32 * (f % (C / 32)) + 16 * half + 4 * (lane >> 4);
+        st4(dst + row * P + c, *(const f32x4*)&x.u[j]);
     }
 }
 

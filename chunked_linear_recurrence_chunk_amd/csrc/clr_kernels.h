@@ -23,15 +23,16 @@ namespace clr {
 
 // Workspace of the Gated DeltaNet path.  Block-major: index
 // ((b * H + h) * NC + n) selects the 64-token block n of head h in batch b.
-// Gated DeltaNet: UtT, UT, dvlT and dUT are fp32 (see gdn_kernels.h,
-// "Precision"); KhT / Kh hold the keys themselves.  KDA: the input type, and
-// KhT / Kh the per-channel decayed keys.
+// UtT, UT, dvlT and dUT are fp32 (see gdn_kernels.h, "Precision").  Gated
+// DeltaNet: KhT / Kh hold the keys themselves; KDA: the per-channel decayed
+// keys, as a bf16 hi/lo pair for bf16 inputs.
 struct GdnWs {
     float* gam;   // [.., 64]       in-block cumulative log gate
     float* eg;    // [.., 64]       exp(gamma_C - gamma_t) for t < 63, exp(gamma_C) at t = 63 (GDN scans)
     void* W;      // [.., 64, dk]   W = T Diag(beta Gam) K           (token-major)
     void* KhT;    // [.., dk, 64]   K^T (GDN), (K * exp(b_C - b))^T (KDA)
     void* UtT;    // [.., dv, 64]   -(T Diag(beta) V)^T
+    void* KhT_lo; // [.., dk, 64]   KDA, bf16 inputs: lo half of the decayed keys Kh^T
     void* hT;     // [.., dv, dk]   state entering the block, transposed
     void* UT;     // [.., dv, 64]   U^T (delta-rule new values)
     float* Smid;  // [B, H, dk, dv] state at the split point of a split forward
@@ -42,6 +43,7 @@ struct GdnWs {
     float* Rt;    // [.., dv, dk]   R^T, R = (Diag(Gam) Q)^T dO - W^T dvloc  (fp32)
     void* WT;     // [.., dk, 64]   W^T
     void* Kh;     // [.., 64, dk]   K (GDN), K * exp(b_C - b) (KDA)   (token-major)
+    void* Kh_lo;  // [.., 64, dk]   KDA, bf16 inputs: lo half of Kh
     void* dvlT;   // [.., dv, 64]   dvloc^T, dvloc = (Q K^T * G * tril)^T dO
     void* dhT;    // [.., dk, dv]   gradient w.r.t. the state leaving the block (GDN: bf16 hi part)
     void* dhT_lo; // [.., dk, dv]   GDN, bf16 inputs: the lo part of that gradient
@@ -89,7 +91,8 @@ template <typename E> struct GdnPrepArgs {
     float* Rt = nullptr;
 };
 
-// UtT and UT are fp32 for the Gated DeltaNet scans and of type E for KDA's.
+// UtT and UT are fp32.  KDA (eC set): KhT is the hi half of the decayed keys
+// and KhT_lo their lo half (bf16 inputs).
 template <typename E> struct GdnScanArgs {
     const float* eg;  // GDN: per block exp(gamma_C - gamma_t), t < 63, and exp(gamma_C) at 63
     const E *W, *KhT;
@@ -105,6 +108,7 @@ template <typename E> struct GdnScanArgs {
     const float* eC = nullptr;
     E* Utok = nullptr;
     int T = 0;
+    const E* KhT_lo = nullptr;
 };
 
 template <typename E> struct GdnOutArgs {

@@ -38,8 +38,9 @@
 
 namespace clr {
 
-// dvlT and dUT are fp32 for the Gated DeltaNet scan (of type E for KDA's), and
-// its dh is stored as a bf16 hi/lo pair (dh, dh_lo) for bf16 inputs.
+// dvlT and dUT are fp32.  The Gated DeltaNet scan stores dh as a bf16 hi/lo
+// pair (dh, dh_lo) for bf16 inputs; KDA's reads the decayed keys as a pair
+// (Kh, Kh_lo) and stores dh once.
 template <typename E> struct GdnScanBwdArgs {
     const float* eg;  // GDN: as GdnScanArgs::eg
     const E *Kh, *WT;
@@ -52,6 +53,7 @@ template <typename E> struct GdnScanBwdArgs {
     int H, NC, BH;
     const float* eC = nullptr;  // per-channel decay (KDA): exp(b_C) per block, padded to 256 floats
     E* dh_lo = nullptr;
+    const E* Kh_lo = nullptr;
 };
 
 template <typename E> struct GdnIntraArgs {
@@ -77,7 +79,8 @@ template <typename E> struct GdnIntraArgs {
 // (W^T and R are read from the slot by the step itself, after the K dS
 // products have been issued, so that their registers are not live at once.)
 template <typename E, int DK, typename UE = E> struct ScanBwdOps {
-    Frag<E> kh[4][DK / 32];   // K (GDN) or Kh (KDA) rows (A: m = t, k = d)
+    Frag<E> kh[4][DK / 32];   // K (GDN) or Kh (KDA, hi half) rows (A: m = t, k = d)
+    Frag<E> kl[4][DK / 32];   // KDA: lo half of Kh
     Frag<UE> dvl[2];          // dvloc^T[v0 + r][token tile pairs] (accumulator layout)
     float GC;                 // GDN: Gam_C, from the small unit
 };
@@ -89,7 +92,8 @@ template <typename E, int DK, bool PCD = false> struct ScanBwdRing {
     static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;
     static constexpr int UPFU = sizeof(ScanWsT<PCD, E>) == 2 ? 1 : 2;
     static constexpr int KK = DK / 32, ND = DK / 16;
-    static constexpr int NKU = 4 * KK * UPF, NWU = 2 * ND * UPF, NRU = ND, NDU = 2 * UPFU;
+    static constexpr int KP = key_parts<PCD, E>();  // KDA: Kh as a hi/lo pair
+    static constexpr int NKU = 4 * KK * UPF * KP, NWU = 2 * ND * UPF, NRU = ND, NDU = 2 * UPFU;
     static constexpr int NU = NKU + NWU + NRU + NDU + (PCD ? 1 : 0);
 };
 
@@ -101,7 +105,10 @@ __device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK, ScanWsT<PCD
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) o.kh[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
+        for (int kk = 0; kk < KK; ++kk) {
+            o.kh[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
+            if constexpr (Rg::KP == 2) o.kl[tb][kk] = ring_frag(slot, 4 * KK + tb * KK + kk, l, (E*)nullptr);
+        }
     // dvloc fragments start at unit NKU + NWU + NRU, i.e. fragment index (that) / UPFU
     static_assert((Rg::NKU + Rg::NWU + Rg::NRU) % UPFU == 0, "fragment alignment");
 #pragma unroll
@@ -123,15 +130,21 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
     using UE = ScanWsT<PCD, E>;
     f32x4 dUp[4];
     if constexpr (PCD) {
-        Frag<E> fs[KK];
+        // KDA: Kh (a pair) times the split dS; dh stored once
+        Frag2<E> fs[KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) fs[kk] = frag_from_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
-        state_store<E, DK, DV, PCD>(a.dh + chunk * DK * DV, fs, tile, 16 * vb, l);
+        for (int kk = 0; kk < KK; ++kk) fs[kk] = split_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+        {
+            Frag<E> fh[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) fh[kk] = fs[kk].hi;
+            state_store<E, DK, DV, true>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
+        }
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) mma(acc, o.kh[tb][kk], fs[kk]);
+            for (int kk = 0; kk < KK; ++kk) mma2(acc, pair_of(o.kh[tb][kk], o.kl[tb][kk]), fs[kk]);
             dUp[tb] = acc;
         }
     } else {
@@ -145,13 +158,12 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
             for (int kk = 0; kk < KK; ++kk) mma2(acc, o.kh[tb][kk], fs[kk]);
             dUp[tb] = acc;
         }
-        // the state's hi part through the selector products, the lo part
-        // through the wave's LDS tile (no matrix-core work)
+        // both parts of the state through the wave's LDS tile (no matrix-core work)
         {
             Frag<E> fh[KK];
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) fh[kk] = fs[kk].hi;
-            state_store<E, DK, DV, false>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
+            state_store<E, DK, DV, true>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
         }
         if constexpr (sizeof(E) == 2) {
             Frag<E> fl[KK];
@@ -180,16 +192,7 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
     UE* dUT = (UE*)a.dUT + chunk * BLK * DV;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const Frag<UE>& f = o.dvl[j];
-        f32x4 lo, hi;
-        if constexpr (sizeof(UE) == 2) {
-            lo = f32x4{(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]};
-            hi = f32x4{(float)f.v[4], (float)f.v[5], (float)f.v[6], (float)f.v[7]};
-        } else {
-            lo = f.lo;
-            hi = f.hi;
-        }
-        st8T(dUT, 2 * vb + j, l, dUp[2 * j] + lo, dUp[2 * j + 1] + hi);
+        st8T(dUT, 2 * vb + j, l, dUp[2 * j] + o.dvl[j].lo, dUp[2 * j + 1] + o.dvl[j].hi);
     }
     Frag<E> fu[2];
 #pragma unroll
@@ -240,12 +243,16 @@ __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, in
         auto issue = [&](int m) {
             const size_t c = bh * NC + (NC - 1 - m);
             const E* Kh = a.Kh + c * BLK * DK + l * LE;
+            const E* Khl = PCD ? a.Kh_lo + c * BLK * DK + l * LE : nullptr;
             const E* WT = a.WT + c * BLK * DK + l * LE;
             const float* Rt = a.Rt + c * DK * DV + (size_t)vb * ND * 256 + l * 4;
             const UT_* dvl = (const UT_*)a.dvlT + c * BLK * DV + (size_t)(2 * vb * UPFU) * UNIT_ELEMS<UT_> +
                              l * LANE_ELEMS<UT_>;
             auto src = [&](int u) -> const void* {
-                if (u < Rg::NKU) return Kh + u * UE;
+                if (u < Rg::NKU) {  // KDA: the lo half follows the hi half
+                    if (Rg::KP == 2 && u >= Rg::NKU / 2) return Khl + (u - Rg::NKU / 2) * UE;
+                    return Kh + u * UE;
+                }
                 if (u < Rg::NKU + Rg::NWU) return WT + (u - Rg::NKU) * UE;
                 if (u < Rg::NKU + Rg::NWU + Rg::NRU) return Rt + (u - Rg::NKU - Rg::NWU) * 256;
                 if (PCD && u == NU - 1) return a.eC + c * 256 + l * 4;

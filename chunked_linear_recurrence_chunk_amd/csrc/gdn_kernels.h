@@ -425,14 +425,17 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
 // the blocks.  The fp32 state slice S[0:DK][v0:v0+16] lives in accumulator
 // tiles of the consumer wave.  Writes the state entering each block and U_n^T.
 // ---------------------------------------------------------------------------
-// The scans of the Gated DeltaNet path keep Ut and U in fp32 and multiply the
-// exact keys (HP, see "Precision" above); KDA's (per-channel decay, PCD) keep
-// them in the input type with the decayed keys.
-template <bool PCD, typename E> using ScanWsT = typename std::conditional<PCD, E, float>::type;
+// The scans keep Ut, U, dvloc and dU in fp32 (see "Precision" above).  The
+// Gated DeltaNet scans multiply the exact keys by e * U; KDA's (per-channel
+// decay, PCD) multiply the decayed keys, streamed as a bf16 hi/lo pair.
+template <bool PCD, typename E> using ScanWsT = float;
+// Factor of the key units in a ring slot: two for the KDA pair (bf16 only).
+template <bool PCD, typename E> constexpr int key_parts() { return PCD && sizeof(E) == 2 ? 2 : 1; }
 
 template <typename E, int DK, typename UE = E> struct ScanFwdOps {
     Frag<E> w[4][DK / 32];    // W rows (A: m = t, k = d)
-    Frag<E> kh[DK / 16][2];   // K^T (GDN) or Kh^T (KDA) rows (A: m = d, k = t)
+    Frag<E> kh[DK / 16][2];   // K^T (GDN) or Kh^T (KDA, hi half) rows (A: m = d, k = t)
+    Frag<E> kl[DK / 16][2];   // KDA: lo half of Kh^T
     Frag<UE> ut[2];           // -Ut^T[v0 + r][token pair-tiles 2j, 2j+1] (accumulator layout)
     float GC;                 // GDN: Gam_C = exp(gamma_C), from the small unit
 };
@@ -556,7 +559,7 @@ __device__ __forceinline__ void state_store(E* h, const Frag<E> (&fs)[DK / 32], 
 // One block of the recurrence.  HNAT selects the layout of the saved states:
 // false -> tiled h^T[v][d] (read by the forward's out kernel), true -> tiled
 // h[d][v] (read by the backward).
-template <typename E, int DK, int NU, typename UE>
+template <typename E, int DK, int NU, typename UE, int KP = 1>
 __device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK, UE>& o, const char* slot, int l);
 
 template <typename E, int DK, int DV, bool HNAT, int NU, bool PCD = false>
@@ -582,14 +585,8 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>
     f32x4 U[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const Frag<UE>& f = o.ut[j];
-        if constexpr (sizeof(UE) == 2) {
-            U[2 * j] = f32x4{(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]};
-            U[2 * j + 1] = f32x4{(float)f.v[4], (float)f.v[5], (float)f.v[6], (float)f.v[7]};
-        } else {
-            U[2 * j] = f.lo;
-            U[2 * j + 1] = f.hi;
-        }
+        U[2 * j] = o.ut[j].lo;
+        U[2 * j + 1] = o.ut[j].hi;
     }
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -598,7 +595,7 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>
     }
     // the Kh^T reads go out while the products above run
     asm volatile("" ::: "memory");
-    scan_fwd_from_ring_kh<E, DK, NU, UE>(o, slot, l);
+    scan_fwd_from_ring_kh<E, DK, NU, UE, key_parts<PCD, E>()>(o, slot, l);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) U[tb] = -U[tb];
     // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles
@@ -617,16 +614,16 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>
     }
     if constexpr (PCD) {
         // S <- Diag(exp(b_C)) S + Kh^T U (KDA: row d of S scaled by its own
-        // channel's factor, from the slot's last unit)
-        Frag<E> fu[2];
-        fu[0] = frag_from_acc<E>(U[0], U[1]);
-        fu[1] = frag_from_acc<E>(U[2], U[3]);
+        // channel's factor, from the slot's last unit); Kh and U both split
+        Frag2<E> fu[2];
+        fu[0] = split_acc<E>(U[0], U[1]);
+        fu[1] = split_acc<E>(U[2], U[3]);
         const float* ecs = (const float*)(slot + (NU - 1) * RING_UNIT) + 4 * (l >> 4);
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
             f32x4 acc = S[db] * *(const f32x4*)(ecs + 16 * db);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, o.kh[db][j], fu[j]);
+            for (int j = 0; j < 2; ++j) mma2(acc, pair_of(o.kh[db][j], o.kl[db][j]), fu[j]);
             S[db] = acc;
         }
     } else {
@@ -654,9 +651,9 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>
 }
 
 // Operands of one block from a ring slot (see clr_ring.h for the layout).
-template <typename E, int DK, int NU, typename UE>
+template <typename E, int DK, int NU, typename UE, int KP = 1>
 __device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK, UE>& o, const char* slot, int l) {
-    constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * (DK / 16);
+    constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * (DK / 16) * KP;
     // units per fragment of W / K and of Ut; Ut starts after the W and K units
     constexpr int UPF = sizeof(E) == 2 ? 1 : 2, UPFU = sizeof(UE) == 2 ? 1 : 2;
     static_assert((NWF + NKF) * UPF % UPFU == 0, "fragment alignment");
@@ -669,13 +666,16 @@ __device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK, UE>& o, con
     o.GC = ring_small<NU>(slot, BLK - 1);
 }
 // K^T (Kh^T) operands of a block (read after the W S products have been issued).
-template <typename E, int DK, int NU, typename UE>
+template <typename E, int DK, int NU, typename UE, int KP>
 __device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK, UE>& o, const char* slot, int l) {
-    constexpr int KK = DK / 32, NWF = 4 * KK;
+    constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * (DK / 16);
 #pragma unroll
     for (int db = 0; db < DK / 16; ++db)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) o.kh[db][j] = ring_frag(slot, NWF + 2 * db + j, l, (E*)nullptr);
+        for (int j = 0; j < 2; ++j) {
+            o.kh[db][j] = ring_frag(slot, NWF + 2 * db + j, l, (E*)nullptr);
+            if constexpr (KP == 2) o.kl[db][j] = ring_frag(slot, NWF + NKF + 2 * db + j, l, (E*)nullptr);
+        }
 }
 
 // Work-group: wave 0 runs the recurrence, the other waves stream the operands
@@ -697,7 +697,7 @@ template <int NP> constexpr int scan_threads = 64 * (NP + 1);
 template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFwdGeom {
     static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 1-KB units per fragment
     static constexpr int UPFU = sizeof(ScanWsT<PCD, E>) == 2 ? 1 : 2;  // ... of Ut
-    static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF;
+    static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF * key_parts<PCD, E>();
     static constexpr int NU = NWU + NKU + 2 * UPFU + (PCD ? 1 : 0);
     static constexpr int SLOT = RingGeom<NU>::SLOT;
     static constexpr int TILE_H = HNAT ? state_tile_bytes(DK, sizeof(E)) : 16, TILE_U = PCD ? BLK * 16 * (int)sizeof(E) : 16;
@@ -733,11 +733,16 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
             const size_t c = bh * NC + n0 + n;
             const E* W = a.W + c * BLK * DK + l * LE;
             const E* KhT = a.KhT + c * BLK * DK + l * LE;
+            const E* KhTl = PCD ? a.KhT_lo + c * BLK * DK + l * LE : nullptr;
             const UT_* UtT = (const UT_*)a.UtT + c * BLK * DV + (size_t)(2 * vb * UPFU) * UNIT_ELEMS<UT_> +
                              l * LANE_ELEMS<UT_>;
             auto src = [&](int u) -> const void* {
                 if (u < NWU) return W + u * UE;
-                if (u < NWU + NKU) return KhT + (u - NWU) * UE;
+                if (u < NWU + NKU) {
+                    const int k = u - NWU;  // KDA: the lo half follows the hi half
+                    if (PCD && k >= NKU / 2 && key_parts<PCD, E>() == 2) return KhTl + (k - NKU / 2) * UE;
+                    return KhT + k * UE;
+                }
                 if (PCD && u == NU - 1) return a.eC + c * 256 + l * 4;
                 return UtT + (u - NWU - NKU) * UNIT_ELEMS<UT_>;
             };
@@ -767,7 +772,7 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
     for (int n = 0; n < NB; ++n) {
         ScanFwdOps<E, DK, UT_> o;
         const char* slot = ring + (n % P) * G::SLOT;
-        scan_fwd_from_ring<E, DK, NU, UT_>(o, slot, l);
+        scan_fwd_from_ring<E, DK, NU, UT_, key_parts<PCD, E>()>(o, slot, l);
         scan_fwd_step<E, DK, DV, HNAT, NU, PCD>(o, S, a, bh * NC + n0 + n, vb, l, tile, slot);
         ring_barrier();
     }

@@ -171,6 +171,23 @@ __device__ __forceinline__ Frag<E> frag_row_decay(const E* X, int PX, int row, i
     }
     return ldfrag_scaled(X + row * PX + col + 4 * g, s0, s1);
 }
+// The same fragment as a split pair (the decayed keys of the KDA scans, whose
+// rounding would add components to a state that decays slowly).
+template <typename E>
+__device__ __forceinline__ Frag2<E> frag_row_decay2(const E* X, int PX, int row, int col, const float* brow,
+                                                    const float* ref, float sgn) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const int c0 = col + 4 * g, c1 = col + 16 + 4 * g;
+    const f32x4 d0 = ld4f(brow + c0) - ld4f(ref + c0), d1 = ld4f(brow + c1) - ld4f(ref + c1);
+    f32x4 s0, s1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s0[i] = expu(sgn * d0[i]);
+        s1[i] = expu(sgn * d1[i]);
+    }
+    const E* p = X + row * PX + col + 4 * g;
+    return split8<E>(ld4(p) * s0, ld4(p + 16) * s1);
+}
 
 // A fragment of X^T (m = feature m0 + r, k = token s = k0 + kmap(g, i)) from
 // a row-major LDS tile X[s][feature], element scaled by
@@ -181,13 +198,10 @@ __device__ __forceinline__ Frag<E> frag_row_decay(const E* X, int PX, int row, i
 // outside [klo, khi) the exponent is -inf, so the factor is exactly 0.  It
 // needs a few more registers: kernels already at the register limit pass false.
 template <bool BATCH = true, typename E>
-__device__ __forceinline__ Frag<E> frag_col_decay(const E* X, int PX, const float* bs, int PB, int m0, int k0,
-                                                  const float* ref, float sgn, int klo, int khi) {
-    const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
-    const int m = m0 + r;
+__device__ __forceinline__ void col_decay_scales(const float* bs, int PB, int m, int k0, const float* ref, float sgn,
+                                                 int klo, int khi, float (&sc)[8]) {
+    const int g = (threadIdx.x & 63) >> 4;
     const float rm = ref[m];
-    Frag<E> x = ldfrag_tr(X, PX, k0, m0, l);
-    float sc[8];
     if constexpr (BATCH) {
 #pragma unroll
         for (int hbl = 0; hbl < 2; ++hbl) {
@@ -209,6 +223,14 @@ __device__ __forceinline__ Frag<E> frag_col_decay(const E* X, int PX, const floa
             sc[i] = (k >= klo && k < khi) ? expu(sgn * (bs[k * PB + m] - rm)) : 0.f;
         }
     }
+}
+template <bool BATCH = true, typename E>
+__device__ __forceinline__ Frag<E> frag_col_decay(const E* X, int PX, const float* bs, int PB, int m0, int k0,
+                                                  const float* ref, float sgn, int klo, int khi) {
+    const int l = threadIdx.x & 63, r = l & 15;
+    Frag<E> x = ldfrag_tr(X, PX, k0, m0, l);
+    float sc[8];
+    col_decay_scales<BATCH, E>(bs, PB, m0 + r, k0, ref, sgn, klo, khi, sc);
     if constexpr (sizeof(E) == 2) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) x.v[i] = (bf16)((float)x.v[i] * sc[i]);
@@ -220,6 +242,27 @@ __device__ __forceinline__ Frag<E> frag_col_decay(const E* X, int PX, const floa
         }
     }
     return x;
+}
+// The same fragment as a split pair.
+template <bool BATCH = true, typename E>
+__device__ __forceinline__ Frag2<E> frag_col_decay2(const E* X, int PX, const float* bs, int PB, int m0, int k0,
+                                                    const float* ref, float sgn, int klo, int khi) {
+    const int l = threadIdx.x & 63, r = l & 15;
+    const Frag<E> x = ldfrag_tr(X, PX, k0, m0, l);
+    float sc[8];
+    col_decay_scales<BATCH, E>(bs, PB, m0 + r, k0, ref, sgn, klo, khi, sc);
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (sizeof(E) == 2) {
+            a[i] = (float)x.v[i] * sc[i];
+            b[i] = (float)x.v[4 + i] * sc[4 + i];
+        } else {
+            a[i] = x.lo[i] * sc[i];
+            b[i] = x.hi[i] * sc[4 + i];
+        }
+    }
+    return split8<E>(a, b);
 }
 
 // ---------------------------------------------------------------------------
@@ -1023,11 +1066,19 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 // tile's middle token on it).  Outputs use the Gated DeltaNet workspace
 // layouts (W, -Ut^T, Kh^T tiled), plus exp(b_C) padded to 256 floats.
 // ---------------------------------------------------------------------------
+// Precision as for the Gated DeltaNet prep (gdn_kernels.h, "Precision"): T is
+// kept in fp32 and W, Ut are formed from its hi/lo split; Ut is stored fp32;
+// the decayed keys Kh^T = (K e^{b_C - b})^T are stored as a bf16 hi/lo pair
+// (KhT, KhT_lo): with a per-channel decay the scan cannot multiply the exact
+// keys, and a rounded decayed key adds components that a slowly decaying
+// state keeps.
 template <typename E> struct KdaPrepArgs {
     const E *k, *v, *g, *beta;
     int T, H, NC;
     float* eC;
-    E *W, *KhT, *UtT;
+    E *W, *KhT;
+    float* UtT;
+    E* KhT_lo;
     // backward only (nullable): T^T (tiled [s][t]), the decayed Gram product M
     // (strictly lower, fp32, 16 accumulator tiles) and K e^b (row-major [64][dk])
     E* TT = nullptr;
@@ -1113,11 +1164,12 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
     const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
     constexpr int PK = RP<E, DK>, PV = RP<E, DV>, PB = DK + 4, ND = DK / 16;
 
-    __shared__ __align__(16) E Ks[BLK * PK], Kd[BLK * PK], Vs[BLK * PV], T1[BLK * PT];
+    __shared__ __align__(16) E Ks[BLK * PK], Kd[BLK * PK], Vs[BLK * PV];
     __shared__ __align__(16) float Bs[BLK * PB];
-    __shared__ __align__(16) float Am[BLK * AP], Td[4 * 256];
+    __shared__ __align__(16) float Am[BLK * AP], Td[4 * 256];  // A, then T (fp32)
     __shared__ __align__(16) float zrow[DK];
-    __shared__ float seg[256], s_bet[BLK];
+    __shared__ float seg[256];
+    __shared__ __align__(16) float s_bet[BLK];
 
     {
         const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
@@ -1151,16 +1203,11 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
             *(uint4*)(dst + t * DK + c) = *(const uint4*)(Kd + t * PK + c);
         }
     }
+    f32x4 tc[4];
     if (hf == 0) {
-        // T = (I + A)^-1, wave w holds column block w; T1 = T Diag(beta)
-        f32x4 tc[4];
+        // T = (I + A)^-1, wave w holds column block w
         tri_inverse_cols(Am, Td, tc);  // one barrier inside
         const int s = 16 * w + r;
-        const float bs = s_bet[s];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) T1[(16 * i + 4 * g + ii) * PT + s] = from_f<E>(tc[i][ii] * bs);
         if (a.TT) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) st4(a.TT + chunk * BLK * BLK + toff<E>(s, 16 * i + 4 * g, BLK), tc[i]);
@@ -1168,7 +1215,20 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
     } else {
         __syncthreads();  // matches the barrier inside tri_inverse_cols
     }
+    __syncthreads();  // A no longer read: T (fp32) takes its place
+    if (hf == 0) {
+        const int s = 16 * w + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) Am[(16 * i + 4 * g + ii) * AP + s] = tc[i][ii];
+    }
     __syncthreads();
+    // Row fragment (m = t, k = s) of T1 = T Diag(beta): fp32, scaled, split
+    auto tfrag = [&](int t, int k0) {
+        const float* p = Am + t * AP + k0 + 4 * g;
+        return split8<E>(ld4(p) * ld4f(s_bet + k0 + 4 * g), ld4(p + 16) * ld4f(s_bet + k0 + 16 + 4 * g));
+    };
     // W^T[d][t] = sum_s (K * e^b)^T[d][s] T1[t][s]  -> stored as W[t][d] (tiled)
     E* Wout = a.W + chunk * BLK * DK;
 #pragma unroll
@@ -1176,27 +1236,28 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
         const int db = tile >> 2, tb = tile & 3;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            mma(acc, ldfrag_tr(Kd, PK, 32 * j, 16 * db, l), ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g));
+        for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Kd, PK, 32 * j, 16 * db, l), tfrag(16 * tb + r, 32 * j));
         st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
     }
-    // Ut = T1 V, stored negated as -Ut^T (tiled)
-    E* Uout = a.UtT + chunk * BLK * DV;
+    // Ut = T1 V, stored negated as fp32 -Ut^T (tiled)
+    float* Uout = a.UtT + chunk * BLK * DV;
 #pragma unroll
     for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
         const int tb = tile % 4, vb = tile / 4;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            mma(acc, ldfrag(T1 + (16 * tb + r) * PT + 32 * j + 4 * g), ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
-        st4(Uout + toff<E>(16 * vb + r, 16 * tb + 4 * g, BLK), -acc);
+        for (int j = 0; j < 2; ++j) mma2(acc, tfrag(16 * tb + r, 32 * j), ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
+        *(f32x4*)(Uout + toff<float>(16 * vb + r, 16 * tb + 4 * g, BLK)) = -acc;
     }
-    // Kh^T[d][t] = K[t][d] e^{b_C[d] - b_t[d]} (tiled), fragment (db, j)
+    // Kh^T[d][t] = K[t][d] e^{b_C[d] - b_t[d]} (tiled, hi/lo pair), fragment (db, j)
     E* KhT = a.KhT + chunk * BLK * DK;
+    E* KhTl = a.KhT_lo + chunk * BLK * DK;
 #pragma unroll
     for (int f = w8; f < 2 * ND; f += 8) {
         const int db = f >> 1, j = f & 1;
-        st_fragT(KhT, f, l, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, bC, -1.f, 0, BLK));
+        const Frag2<E> x = frag_col_decay2(Ks, PK, Bs, PB, 16 * db, 32 * j, bC, -1.f, 0, BLK);
+        st_fragT(KhT, f, l, x.hi);
+        if constexpr (sizeof(E) == 2) st_fragT(KhTl, f, l, x.lo);
     }
 }
 

@@ -29,8 +29,10 @@ template <typename E> struct KdaPrep2Args {
     const E *q, *k, *dO, *g;
     const E* W;
     float* Rt;
-    E *WT, *Kh, *dvlT;
+    E *WT, *Kh;
+    float* dvlT;  // fp32 (the reverse scan adds it to Kh dS)
     int T, H, NC;
+    E* Kh_lo = nullptr;  // lo half of the decayed keys (bf16 inputs)
 };
 
 // ---------------------------------------------------------------------------
@@ -80,9 +82,15 @@ __global__ __launch_bounds__(512) void kda_prep2_kernel(KdaPrep2Args<E> a) {
     // Kh[t][d] = K[t][d] e^{b_C[d] - b_t[d]} (tiled; A: m = t, k = d): fragments (w, kk)
     const int s = 16 * w + r;
     {
+        // as a hi/lo pair: the reverse scan multiplies it by the split dS
         E* Kh = a.Kh + chunk * BLK * DK;
+        E* Khl = a.Kh_lo + chunk * BLK * DK;
 #pragma unroll
-        for (int kk = hf; kk < KK; kk += 2) st_fragT(Kh, w * KK + kk, l, frag_row_decay(Ks, PQ, s, 32 * kk, Bs + s * PB, bC, -1.f));
+        for (int kk = hf; kk < KK; kk += 2) {
+            const Frag2<E> x = frag_row_decay2(Ks, PQ, s, 32 * kk, Bs + s * PB, bC, -1.f);
+            st_fragT(Kh, w * KK + kk, l, x.hi);
+            if constexpr (sizeof(E) == 2) st_fragT(Khl, w * KK + kk, l, x.lo);
+        }
     }
     // P[tb][w] (rows t, cols s), s <= t
     f32x4 P[4];
@@ -115,13 +123,13 @@ __global__ __launch_bounds__(512) void kda_prep2_kernel(KdaPrep2Args<E> a) {
     Frag<E> fp[2];
     fp[0] = frag_from_acc<E>(P[0], P[1]);
     fp[1] = frag_from_acc<E>(P[2], P[3]);
-    E* dvlT = a.dvlT + chunk * BLK * DV;
+    float* dvlT = a.dvlT + chunk * BLK * DV;
 #pragma unroll
     for (int vb = hf; vb < NVB; vb += 2) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
-        st4(dvlT + toff<E>(16 * vb + r, 16 * w + 4 * g, BLK), acc);
+        *(f32x4*)(dvlT + toff<float>(16 * vb + r, 16 * w + 4 * g, BLK)) = acc;
         st4(dvlt + (16 * vb + r) * PT + 16 * w + 4 * g, acc);
     }
     __syncthreads();
@@ -144,7 +152,8 @@ __global__ __launch_bounds__(512) void kda_prep2_kernel(KdaPrep2Args<E> a) {
 
 template <typename E> struct KdaWyArgs {
     const E *v, *beta;
-    const E *h, *dUT;  // S0 per block (tiled [d][v]), dU^T per block (tiled [v][t])
+    const E* h;        // S0 per block (tiled [d][v])
+    const float* dUT;  // dU^T per block (tiled [v][t], fp32)
     const E* TT;       // per block, from the prep: T^T (tiled)
     const float* M;    //   the decayed Gram product (accumulator tiles)
     const E* Kd;       //   K e^b (row-major [64][dk])
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
     E* dWs = (E*)(lds + Lay::pB_dW);
     E* dTT = (E*)(lds + Lay::pB_dTT);
     {
-        const auto dux = load_tiled<E, DV, BLK, NT>(a.dUT + chunk * BLK * DV);
+        const auto dux = load_tiled<float, DV, BLK, NT>(a.dUT + chunk * BLK * DV);
         const auto kx = load_rows<E, BLK, DK, NT>(a.Kd + chunk * BLK * DK, DK, BLK);
         const auto tx = load_tiled<E, BLK, BLK, NT>(a.TT + chunk * BLK * BLK);
         const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
         store_rows<E, BLK, DK, PK, NT>(kx, Kd);
         store_untiled<E, BLK, BLK, PT, NT>(tx, TT);
         store_rows<E, BLK, DV, PV, NT>(vx, Vs);
-        store_untiled<E, DV, BLK, PT, NT>(dux, dUTs);
+        store_untiled_round<E, DV, BLK, PT, NT>(dux, dUTs);
     }
     __syncthreads();
 
@@ -356,13 +365,14 @@ hipError_t launch_kda_fwd_t(const GdnLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GdnWs& ws = L.ws;
     KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
-                      ws.eCk, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
+                      ws.eCk, (E*)ws.W, (E*)ws.KhT, (float*)ws.UtT, (E*)ws.KhT_lo};
     launch("kda_prep", kda_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
     GdnScanArgs<E> sa{nullptr, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, L.S_out,
                       (E*)ws.hT, nullptr, L.H, L.NC, L.B * L.H};
     sa.eC = ws.eCk;
     sa.Utok = (E*)ws.Utok;
     sa.T = L.T;
+    sa.KhT_lo = (const E*)ws.KhT_lo;
     launch("kda_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, true>, dim3(scan_grid(DV / 16, L.B * L.H)),
            dim3(256), st, sa);
     if (L.o) {
@@ -378,25 +388,28 @@ hipError_t launch_kda_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GdnWs& ws = L.ws;
     KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
-                      ws.eCk, (E*)ws.W, (E*)ws.KhT, (E*)ws.UtT};
+                      ws.eCk, (E*)ws.W, (E*)ws.KhT, (float*)ws.UtT, (E*)ws.KhT_lo};
     pa.TT = (E*)ws.TT;
     pa.M = ws.KKG;
     pa.Kd = (E*)ws.Kd;
     launch("kda_prep_bwd", kda_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
     KdaPrep2Args<E> p2{(const E*)L.q, (const E*)L.k, (const E*)L.dO, (const E*)L.g, (const E*)ws.W,
-                       ws.Rt, (E*)ws.WT, (E*)ws.Kh, (E*)ws.dvlT, L.T, L.H, L.NC};
+                       ws.Rt, (E*)ws.WT, (E*)ws.Kh, (float*)ws.dvlT, L.T, L.H, L.NC};
+    p2.Kh_lo = (E*)ws.Kh_lo;
     launch("kda_prep2", kda_prep2_kernel<E, DK, DV>, gblk, dim3(512), st, p2);
     GdnScanArgs<E> sa{nullptr, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, nullptr, L.H, L.NC, L.B * L.H};
     sa.eC = ws.eCk;
     sa.Utok = (E*)ws.Utok;
     sa.T = L.T;
+    sa.KhT_lo = (const E*)ws.KhT_lo;
     GdnScanBwdArgs<E> sb{nullptr, (const E*)ws.Kh, (const E*)ws.WT, (const E*)ws.dvlT, ws.Rt,
                          L.dS_out, L.dS_in, (E*)ws.dhT, (E*)ws.dUT, L.H, L.NC, L.B * L.H};
     sb.eC = ws.eCk;
+    sb.Kh_lo = (const E*)ws.Kh_lo;
     const int G = (int)scan_grid(DV / 16, L.B * L.H);
     launch("kda_scan_pair", gdn_scan_pair_kernel<E, DK, DV, true>, dim3(2 * G), dim3(256), st, sa, sb, G);
-    KdaWyArgs<E> wa{(const E*)L.v, (const E*)L.beta, (const E*)ws.hT, (const E*)ws.dUT, (const E*)ws.TT, ws.KKG,
+    KdaWyArgs<E> wa{(const E*)L.v, (const E*)L.beta, (const E*)ws.hT, (const float*)ws.dUT, (const E*)ws.TT, ws.KKG,
                     (const E*)ws.Kd, (E*)L.dv_, (E*)L.dbeta, ws.dM, ws.dX, L.T, L.H, L.NC};
     launch("kda_bwd_wy", kda_bwd_wy_kernel<E, DK, DV>, gblk, dim3(512), st, wa);
     GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)ws.Utok, (const E*)L.dO, (const E*)L.g,

@@ -28,24 +28,13 @@ CASES = [
     ("kda", 1, 8192, 4, 128, "bf16", 4, "slow", 315),
     ("kda", 1, 8192, 4, 128, "bf16", 4, "zero", 316),
 ]
-# KDA's block form still rounds T, Ut, U and the decayed keys to bf16: on this
-# input S_out measures 2.2e-2 and dbeta 2.6e-2 (slow gates; zero gates at 8192
-# tokens dv 2.1e-2, dbeta 2.6e-2).  Expected to fail until that path carries
-# the split operands the Gated DeltaNet path has.
-KDA_BF16_OPEN = {313, 315, 316}
 
 
 def _ids(c):
     return f"{c[0]}-T{c[2]}H{c[3]}d{c[4]}-{c[5]}-N{c[6]}-{c[7]}"
 
 
-def _param(c):
-    if c[-1] in KDA_BF16_OPEN:
-        return pytest.param(c, marks=pytest.mark.xfail(strict=True, reason="KDA bf16 block form without split operands"))
-    return c
-
-
-@pytest.mark.parametrize("case", [_param(c) for c in CASES], ids=[_ids(c) for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
 def test_delta_stress_matches_oracle(case):
     import torch
     from chunked_linear_recurrence_chunk_amd import inputs, stateflow
