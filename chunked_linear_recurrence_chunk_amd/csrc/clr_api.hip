@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "clr.h"
 #include "clr_conv.h"
@@ -95,6 +96,7 @@ GdnWs carve_kda(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     Carver c{base};
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
     GdnWs w{};
+    w.range = (int*)c.take(nb * 4);  // first, where clr_range_status finds it
     // Ut, dvloc and dU fp32; the decayed keys as a bf16 hi/lo pair (gdn_kernels.h, "Precision")
     w.W = c.take(nb * BLK * dk * es);
     w.KhT = c.take(nb * BLK * dk * es);
@@ -125,6 +127,7 @@ GlaWs carve_gla(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     Carver c{base};
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
     GlaWs w{};
+    w.range = (int*)c.take(nb * 4);  // first, where clr_range_status finds it
     w.eC = (float*)c.take(nb * dk * 4);
     w.KhT = c.take(nb * BLK * dk * es);
     w.hT = c.take(nb * dk * dv * es);
@@ -207,6 +210,7 @@ const char* clr_status_string(int s) {
         case CLR_EWORKSPACE: return "workspace missing or too small";
         case CLR_EHIP: return "HIP error";
         case CLR_ESCRATCH: return "needs more scratch than the allocation-free entry point holds";
+        case CLR_ERANGE: return "gates beyond the diagonal tiles' decay bound";
         default: return "unknown status";
     }
 }
@@ -228,6 +232,29 @@ size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
     if (gla) carve_gla(s, bwd, nullptr, &total);
     else carve_gdn(s, bwd, nullptr, &total);
     return total;
+}
+
+// The per-block range records sit at the start of the GLA, KDA and Mamba-2
+// workspaces (carve_gla, carve_kda); the prep kernels rewrite them every call.
+int clr_range_status(const clr_shape_t* s, int op, const void* ws, void* stream) {
+    if (op < CLR_OP_GDN_FWD || op > CLR_OP_KDA_BWD) return CLR_EINVAL;
+    const bool kda = op == CLR_OP_KDA_FWD || op == CLR_OP_KDA_BWD;
+    const bool gla = !kda && op != CLR_OP_GDN_FWD && op != CLR_OP_GDN_BWD;
+    const bool bwd = op == CLR_OP_GDN_BWD || op == CLR_OP_GLA_BWD || op == CLR_OP_M2_BWD || op == CLR_OP_KDA_BWD;
+    if (const int rc = check_shape(s, gla, kda ? false : bwd)) return rc;
+    if (kda && kda_f32_unsupported(s, bwd)) return CLR_ENOTSUP;
+    if (!kda && !gla) return CLR_OK;
+    if (!ws || ((uintptr_t)ws & (ALIGN - 1))) return CLR_EWORKSPACE;
+    const size_t nb = nblocks(s);
+    if (nb == 0) return CLR_OK;
+    std::vector<int> flags(nb);
+    hipStream_t st = (hipStream_t)stream;
+    if (hipMemcpyAsync(flags.data(), ws, nb * sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return CLR_EHIP;
+    for (const int f : flags)
+        if (f) return CLR_ERANGE;
+    return CLR_OK;
 }
 
 // ---------------------------------------------------------------------------

@@ -38,6 +38,7 @@ struct GdnWs {
     float* Smid;  // [B, H, dk, dv] state at the split point of a split forward
     // KDA forward only
     float* eCk;   // [.., 256]      exp(b_C) per key channel (padded)
+    int* range;   // [..]           per block: 1 if the gates leave the diagonal tiles' bound
     void* Utok;   // [B, T, H, dv]  U, token-major
     // backward only
     float* Rt;    // [.., dv, dk]   R^T, R = (Diag(Gam) Q)^T dO - W^T dvloc  (fp32)
@@ -137,6 +138,7 @@ hipError_t launch_gdn_bwd(const GdnLaunch& L, hipStream_t st);
     CLR_CASE(E, 128, 256)
 
 struct GlaWs {
+    int* range;   // [..]          per block: 1 if the gates leave the diagonal tiles' bound
     float* eC;    // [.., dk]      exp(b_C): the block's total decay per channel (fp32)
     void* KhT;    // [.., dk, 64]  (K * exp(b_C - b))^T, tiled
     void* hT;     // fwd: [.., dv, dk] state entering the block as h^T, tiled;

@@ -13,6 +13,7 @@ hipError_t launch_gla_fwd_t(const GlaLaunch& L, hipStream_t st) {
     const GlaWs& ws = L.ws;
     using SL = GlaSlices<E, DK, DV>;
     GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC, ws.eC, (E*)ws.KhT, nullptr, nullptr};
+    pa.range = ws.range;
     launch(SG ? "m2_prep" : "gla_prep", gla_prep_kernel<E, DK, false, SG>, gblk, dim3(256), st, pa);
     GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, L.S_out, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
     launch(SG ? "m2_scan_fwd" : "gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
@@ -30,6 +31,7 @@ hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
     using SL = GlaSlices<E, DK, DV>;
     GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC,
                       ws.eC, (E*)ws.KhT, (E*)ws.QgT, (E*)ws.Kh};
+    pa.range = ws.range;
     launch(SG ? "m2_prep_bwd" : "gla_prep_bwd", gla_prep_kernel<E, DK, true, SG>, gblk, dim3(256), st, pa);
     GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, nullptr, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
     launch(SG ? "m2_scan_fwd_rec" : "gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);

@@ -34,13 +34,32 @@
 namespace clr {
 
 // exp clamped at e^80 (the rescaling bound of the diagonal tiles)
-__device__ __forceinline__ float expu(float x) { return __expf(fminf(x, 80.f)); }
+constexpr float DIAG_RANGE = 80.f;
+__device__ __forceinline__ float expu(float x) { return __expf(fminf(x, DIAG_RANGE)); }
+
+// Whether the block's gates leave the diagonal tiles' bound: some channel d
+// decays by more than DIAG_RANGE nats between a 16-token tile's first token
+// and its middle (token 7), or between the middle and its last token, so that
+// a rescaling factor of the diagonal pair terms would be clamped.  All
+// threads call it (a block-wide OR); bs is the cumulative gate b[t][d] in LDS
+// (row pitch PB).
+template <int DK, int PB>
+__device__ __forceinline__ bool diag_out_of_range(const float* bs) {
+    bool out = false;
+    for (int i = threadIdx.x; i < 4 * DK; i += blockDim.x) {
+        const int R = i / DK, d = i % DK;
+        const float b0 = bs[(16 * R) * PB + d], bm = bs[(16 * R + 7) * PB + d], b1 = bs[(16 * R + 15) * PB + d];
+        out |= (b0 - bm > DIAG_RANGE) || (bm - b1 > DIAG_RANGE);
+    }
+    return __syncthreads_or(out);
+}
 
 template <typename E> struct GlaPrepArgs {
     const E *q, *k, *g;
     int T, H, NC;
     float* eC;
     E *KhT, *QgT, *Kh;
+    int* range = nullptr;  // per block: 1 if the gates leave the diagonal tiles' bound
 };
 template <typename E> struct GlaScanArgs {
     const float* eC;
@@ -298,6 +317,8 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
         __syncthreads();
         gate_cumsum<E, DK, PK, PB>(Qs, Bs, seg, nvalid);
         __syncthreads();
+        const bool over = diag_out_of_range<DK, PB>(Bs);
+        if (a.range && tid == 0) a.range[chunk] = over ? 1 : 0;
         if constexpr (BWD) {
             store_rows<E, BLK, DK, PK>(qx, Qs);
             __syncthreads();
@@ -1079,6 +1100,7 @@ template <typename E> struct KdaPrepArgs {
     E *W, *KhT;
     float* UtT;
     E* KhT_lo;
+    int* range = nullptr;  // per block: 1 if the gates leave the diagonal tiles' bound
     // backward only (nullable): T^T (tiled [s][t]), the decayed Gram product M
     // (strictly lower, fp32, 16 accumulator tiles) and K e^b (row-major [64][dk])
     E* TT = nullptr;
@@ -1183,6 +1205,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
         __syncthreads();
         gate_cumsum<E, DK, PK, PB>(Kd, Bs, seg, nvalid);
         __syncthreads();
+        const bool over = diag_out_of_range<DK, PB>(Bs);
+        if (a.range && tid == 0) a.range[chunk] = over ? 1 : 0;
     }
     // K * e^b (factors <= 1), and exp(b_C) per channel
     const float* bC = Bs + (BLK - 1) * PB;

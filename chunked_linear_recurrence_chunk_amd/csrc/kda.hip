@@ -366,6 +366,7 @@ hipError_t launch_kda_fwd_t(const GdnLaunch& L, hipStream_t st) {
     const GdnWs& ws = L.ws;
     KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                       ws.eCk, (E*)ws.W, (E*)ws.KhT, (float*)ws.UtT, (E*)ws.KhT_lo};
+    pa.range = ws.range;
     launch("kda_prep", kda_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
     GdnScanArgs<E> sa{nullptr, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, L.S_out,
                       (E*)ws.hT, nullptr, L.H, L.NC, L.B * L.H};
@@ -389,6 +390,7 @@ hipError_t launch_kda_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const GdnWs& ws = L.ws;
     KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                       ws.eCk, (E*)ws.W, (E*)ws.KhT, (float*)ws.UtT, (E*)ws.KhT_lo};
+    pa.range = ws.range;
     pa.TT = (E*)ws.TT;
     pa.M = ws.KKG;
     pa.Kd = (E*)ws.Kd;

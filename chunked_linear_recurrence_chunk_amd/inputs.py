@@ -15,6 +15,8 @@ Distributions (per-token tensors are [B,T,H,d], states [B,H,dk,dv]):
                   per key channel [B,T,H,dk] as GLA.
   Delta-rule stress (make_delta_stress): keys repeated from 8 L2-normalised
                   vectors per head, beta = 0.99, g = -softplus(N(0,1))/1024 or 0.
+  Strong decay (make_strong_decay): the GLA / KDA / Mamba-2 recipe, then
+                  g = -U(lo, hi) on key channels d = 0 mod 4 (scalar gate: even heads).
   Short conv:     x ~ N(0,1) [B,T,C]; w = 0.5 * N(0,1) [C,W]; bias = 0.1 * N(0,1);
                   state_in ~ N(0,1) [B,W-1,C]; dy ~ N(0,1); dstate_out ~ N(0,1)
                   (float32: state gradients are partial sums and stay fp32).
@@ -211,6 +213,32 @@ def make_delta_stress(kind, B, T, H, dk, dv, dtype="bf16", seed=0, gate="slow", 
     if dtype == "bf16":
         for key in ("q", "k", "v", "g", "beta", "dO"):
             d[key] = bf16_round(d[key])
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return d
+
+
+def make_strong_decay(kind, B, T, H, dk, dv, dtype="bf16", seed=0, lo=9.0, hi=9.75):
+    """Inputs of the per-channel and scalar-gate members (kind "gla", "kda",
+    "mamba2") with some gates near the diagonal tiles' decay bound: the
+    member's own recipe (make_gla / make_kda / make_mamba2 with `seed`), then,
+    from a second generator (seed + 7919), g = -U(lo, hi) on every token for
+    the key channels d = 0 mod 4 (per-channel members) or the even heads
+    (scalar gate).  With hi <= 10 no 8 consecutive gates sum below -80; with
+    lo > 80 / 7 some 16-token sub-tile leaves that bound."""
+    f = {"gla": make_gla, "kda": make_kda, "mamba2": make_mamba2}[kind]
+    d = f(B, T, H, dk, dv, "fp32", seed)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    g = d["g"].copy()
+    if kind == "mamba2":
+        g[:, :, 0::2] = -rng.uniform(lo, hi, size=g[:, :, 0::2].shape)
+    else:
+        g[..., 0::4] = -rng.uniform(lo, hi, size=g[..., 0::4].shape)
+    d["g"] = g.astype(np.float32)
+    if dtype == "bf16":
+        for key in ("q", "k", "v", "g", "beta", "dO"):
+            if key in d:
+                d[key] = bf16_round(d[key])
     elif dtype != "fp32":
         raise ValueError(dtype)
     return d

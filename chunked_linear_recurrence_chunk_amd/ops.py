@@ -16,7 +16,7 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libclr.so")
 
-CLR_OK, CLR_EINVAL, CLR_ENOTSUP, CLR_EWORKSPACE, CLR_EHIP, CLR_ESCRATCH = range(6)
+CLR_OK, CLR_EINVAL, CLR_ENOTSUP, CLR_EWORKSPACE, CLR_EHIP, CLR_ESCRATCH, CLR_ERANGE = range(7)
 NOALLOC_SCRATCH_BYTES = 64 << 20  # CLR_NOALLOC_SCRATCH_BYTES
 CLR_F32, CLR_BF16 = 0, 1
 OP_GDN_FWD, OP_GDN_BWD, OP_GLA_FWD, OP_GLA_BWD, OP_M2_FWD, OP_M2_BWD, OP_KDA_FWD, OP_KDA_BWD = range(8)
@@ -71,6 +71,8 @@ def load(path: Optional[str] = None):
         f.argtypes = [sp] + [vp] * 15 + [sz, vp]
         f.restype = i
     cp = ctypes.POINTER(ClrConvShape)
+    lib.clr_range_status.argtypes = [sp, i, vp, vp]
+    lib.clr_range_status.restype = i
     lib.clr_shortconv_workspace_bytes.argtypes = [cp]
     lib.clr_shortconv_workspace_bytes.restype = sz
     lib.shortconv_fwd.argtypes = [cp] + [vp] * 7
@@ -223,7 +225,21 @@ def _out(t, shape, dtype, device):
     return t
 
 
-def _fwd(name, op, q, k, v, g, beta, S_in, want_state, ws, o=None, S_out=None):
+def range_status(shape: ClrShape, op: int, ws) -> int:
+    """clr_range_status: CLR_OK if the gates of the last GLA / KDA / Mamba-2
+    call of ``op`` at ``shape`` on workspace ``ws`` stayed within the diagonal
+    tiles' decay bound, CLR_ERANGE if not (waits for the current stream).
+    The GLA, KDA and Mamba-2 wrappers take ``check_range=True`` to raise
+    ClrError with CLR_ERANGE after the call in that case."""
+    return int(load().clr_range_status(ctypes.byref(shape), op, _ptr(ws), _stream()))
+
+
+def _range_check(name, shape, op, ws, check_range):
+    if check_range:
+        _check(name, range_status(shape, op, ws))
+
+
+def _fwd(name, op, q, k, v, g, beta, S_in, want_state, ws, o=None, S_out=None, check_range=False):
     import torch
     _validate(name.split("_")[0], q, k, v, g, beta, S_in)
     _check_inputs(q, k, v, g, beta, S_in)
@@ -240,6 +256,7 @@ def _fwd(name, op, q, k, v, g, beta, S_in, want_state, ws, o=None, S_out=None):
     rc = getattr(load(), name)(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(S_in), _ptr(o), _ptr(S_out), _ptr(ws), n, _stream())
     _check(name, rc)
+    _range_check(name, shape, op, ws, check_range)
     return o, S_out
 
 
@@ -269,12 +286,12 @@ def gdn_fwd_noalloc(q, k, v, g, beta, S_in=None, o=None, S_out=None):
     return o, S_out
 
 
-def gla_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None):
+def gla_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None, check_range=False):
     """GLA chunk forward (per-key-channel gate g).  Returns (o, S_out)."""
-    return _fwd("gla_fwd", OP_GLA_FWD, q, k, v, g, None, S_in, want_state, ws, o, S_out)
+    return _fwd("gla_fwd", OP_GLA_FWD, q, k, v, g, None, S_in, want_state, ws, o, S_out, check_range)
 
 
-def _bwd(name, op, q, k, v, g, beta, S_in, dO, dS_out, ws, out=None):
+def _bwd(name, op, q, k, v, g, beta, S_in, dO, dS_out, ws, out=None, check_range=False):
     import torch
     _validate(name.split("_")[0], q, k, v, g, beta, S_in, dO, dS_out)
     _check_inputs(q, k, v, g, beta, S_in, dO, dS_out)
@@ -296,6 +313,7 @@ def _bwd(name, op, q, k, v, g, beta, S_in, dO, dS_out, ws, out=None):
                                _ptr(S_in), _ptr(dO), _ptr(dS_out), _ptr(dq), _ptr(dk_), _ptr(dv_),
                                _ptr(dg), _ptr(dbeta), _ptr(dS_in), _ptr(ws), n, _stream())
     _check(name, rc)
+    _range_check(name, shape, op, ws, check_range)
     r = dict(dq=dq, dk=dk_, dv=dv_, dg=dg, dS_in=dS_in)
     if dbeta is not None:
         r["dbeta"] = dbeta
@@ -308,30 +326,30 @@ def gdn_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, ws=None, out=None):
     return _bwd("gdn_bwd", OP_GDN_BWD, q, k, v, g, beta, S_in, dO, dS_out, ws, out)
 
 
-def gla_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None, out=None):
+def gla_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None, out=None, check_range=False):
     """GLA chunk backward.  Returns dict dq, dk, dv, dg, dS_in."""
-    return _bwd("gla_bwd", OP_GLA_BWD, q, k, v, g, None, S_in, dO, dS_out, ws, out)
+    return _bwd("gla_bwd", OP_GLA_BWD, q, k, v, g, None, S_in, dO, dS_out, ws, out, check_range)
 
 
-def kda_fwd(q, k, v, g, beta, S_in=None, want_state=True, ws=None, o=None, S_out=None):
+def kda_fwd(q, k, v, g, beta, S_in=None, want_state=True, ws=None, o=None, S_out=None, check_range=False):
     """KDA chunk forward (per-key-channel gate g [B,T,H,dk], beta [B,T,H]).
     Returns (o, S_out)."""
-    return _fwd("kda_fwd", OP_KDA_FWD, q, k, v, g, beta, S_in, want_state, ws, o, S_out)
+    return _fwd("kda_fwd", OP_KDA_FWD, q, k, v, g, beta, S_in, want_state, ws, o, S_out, check_range)
 
 
-def kda_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, ws=None, out=None):
+def kda_bwd(q, k, v, g, beta, S_in, dO, dS_out=None, ws=None, out=None, check_range=False):
     """KDA chunk backward.  Returns dict dq, dk, dv, dg, dbeta, dS_in."""
-    return _bwd("kda_bwd", OP_KDA_BWD, q, k, v, g, beta, S_in, dO, dS_out, ws, out)
+    return _bwd("kda_bwd", OP_KDA_BWD, q, k, v, g, beta, S_in, dO, dS_out, ws, out, check_range)
 
 
-def mamba2_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None):
+def mamba2_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None, check_range=False):
     """Scalar-gate (Mamba-2 member) chunk forward, g [B,T,H].  Returns (o, S_out)."""
-    return _fwd("mamba2_fwd", OP_M2_FWD, q, k, v, g, None, S_in, want_state, ws, o, S_out)
+    return _fwd("mamba2_fwd", OP_M2_FWD, q, k, v, g, None, S_in, want_state, ws, o, S_out, check_range)
 
 
-def mamba2_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None, out=None):
+def mamba2_bwd(q, k, v, g, S_in, dO, dS_out=None, ws=None, out=None, check_range=False):
     """Scalar-gate (Mamba-2 member) chunk backward.  Returns dict dq, dk, dv, dg, dS_in."""
-    return _bwd("mamba2_bwd", OP_M2_BWD, q, k, v, g, None, S_in, dO, dS_out, ws, out)
+    return _bwd("mamba2_bwd", OP_M2_BWD, q, k, v, g, None, S_in, dO, dS_out, ws, out, check_range)
 
 
 def _conv_shape(x, w, act):

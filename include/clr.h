@@ -70,6 +70,8 @@
  *     CLR_EHIP        a HIP launch error (reported after enqueueing)
  *     CLR_ESCRATCH    gdn_fwd_noalloc only: the call needs more workspace
  *                     than the library's static scratch holds
+ *     CLR_ERANGE      clr_range_status only: the gates of the last GLA, KDA
+ *                     or Mamba-2 call left the diagonal tiles' bound
  * No exception or abort crosses the ABI.  Loading the library needs no GPU.
  */
 #ifndef CLR_H
@@ -88,7 +90,8 @@ typedef enum {
     CLR_ENOTSUP = 2,
     CLR_EWORKSPACE = 3,
     CLR_EHIP = 4,
-    CLR_ESCRATCH = 5
+    CLR_ESCRATCH = 5,
+    CLR_ERANGE = 6
 } clr_status_t;
 
 typedef enum { CLR_F32 = 0, CLR_BF16 = 1 } clr_dtype_t;
@@ -148,7 +151,8 @@ int gdn_fwd_noalloc(const clr_shape_t* shape, const void* q, const void* k, cons
                     const void* g, const void* beta, const float* S_in, void* o, float* S_out,
                     void* stream);
 
-/* GLA chunk forward; `beta` must be NULL (no delta term, no write scale). */
+/* GLA chunk forward; `beta` must be NULL (no delta term, no write scale).
+ * Exact within the decay bound that clr_range_status reports on. */
 int gla_fwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
             const void* g, const void* beta, const float* S_in, void* o, float* S_out,
             void* ws, size_t ws_bytes, void* stream);
@@ -169,7 +173,7 @@ int gla_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* 
  * beta and dbeta must be NULL.  Head sizes as for GLA.  Runs on the GLA
  * kernels with the gate broadcast over the key channels; dg is the channel
  * sum of the per-channel gate gradient.  Workspace: CLR_OP_M2_FWD /
- * CLR_OP_M2_BWD. */
+ * CLR_OP_M2_BWD.  Decay bound as for GLA (clr_range_status). */
 int mamba2_fwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
                const void* g, const void* beta, const float* S_in, void* o, float* S_out,
                void* ws, size_t ws_bytes, void* stream);
@@ -188,8 +192,7 @@ int mamba2_bwd(const clr_shape_t* shape, const void* q, const void* k, const voi
  * Workspace: CLR_OP_KDA_FWD / CLR_OP_KDA_BWD.  The backward recomputes the
  * forward from S_in (as gdn_bwd does); dS_out may be NULL (zero).  The
  * per-block decays use 16-token sub-tiles with the same e^80 bound as the GLA
- * path (exact while the decay within half a tile stays within 80 nats per
- * channel). */
+ * path (see clr_range_status). */
 int kda_fwd(const clr_shape_t* shape, const void* q, const void* k, const void* v,
             const void* g, const void* beta, const float* S_in, void* o, float* S_out,
             void* ws, size_t ws_bytes, void* stream);
@@ -197,6 +200,27 @@ int kda_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* 
             const void* g, const void* beta, const float* S_in, const void* dO,
             const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
             float* dS_in, void* ws, size_t ws_bytes, void* stream);
+
+/* Range check of the per-channel and scalar-gate members (GLA, KDA, Mamba-2).
+ * Their kernels apply the decay between two tokens of one 16-token diagonal
+ * sub-tile as a factor on each operand, both taken relative to the sub-tile's
+ * 8th token (StateFlow paper, Sec. 2.1, Eq. 1: the products of the gates
+ * between two steps); each factor is clamped at e^80 so that it stays finite
+ * in float32 and bfloat16.  The results are exact while, for every key
+ * channel, the summed -g from a sub-tile's first token to its 8th, and from
+ * its 8th to its last, stays within 80 (for example -g <= 10 on every token);
+ * beyond it the affected within-sub-tile terms are too small, but every
+ * output stays finite.  Every GLA, KDA and Mamba-2 forward and backward
+ * records, per 64-token block, in its workspace whether that bound held (no
+ * extra launch).  clr_range_status waits for `stream`, reads those records
+ * from `ws` as the last such call of `op` at `shape` left them, and returns
+ * CLR_OK if the bound held in every block and CLR_ERANGE if not.  Call it
+ * after that call, on the same stream, before `ws` is used again.  For the
+ * Gated DeltaNet ops it returns CLR_OK without reading `ws` (the scalar gate
+ * enters through exact exponentials of non-positive arguments).  Errors:
+ * CLR_EINVAL / CLR_ENOTSUP for a bad shape or op, CLR_EWORKSPACE for a NULL
+ * or misaligned ws, CLR_EHIP if the copy fails. */
+int clr_range_status(const clr_shape_t* shape, int op, const void* ws, void* stream);
 
 /* Causal short convolution with a boundary state.
  * The StateFlow paper (Sec. 1 and Sec. 3.3) hands the boundary state of a

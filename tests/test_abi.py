@@ -37,9 +37,9 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     ops, lib = _lib()
     assert lib.clr_version() >= 100
-    for s in range(6):
+    for s in range(7):
         assert ops.status_string(s) != "unknown status"
-    assert ops.status_string(6) == "unknown status"
+    assert ops.status_string(7) == "unknown status"
 
 
 def _shape(ops, B=1, T=128, H=2, dk=128, dv=128, dtype=1):
@@ -198,6 +198,29 @@ def test_noalloc_forward_rejects_on_the_host():
     assert lib.gdn_fwd_noalloc(ctypes.byref(fits), *([None] * 9)) == ops.CLR_EINVAL
     assert lib.gdn_fwd_noalloc(ctypes.byref(_shape(ops, dk=96, dv=96)), *([None] * 9)) == ops.CLR_ENOTSUP
     assert lib.gdn_fwd_noalloc(None, *([None] * 9)) == ops.CLR_EINVAL
+
+
+def test_range_status_rejects_on_the_host():
+    """clr_range_status validates shape, op and workspace before reading, and
+    answers CLR_OK for the Gated DeltaNet ops without touching the workspace
+    (no device call on any of these paths)."""
+    ops, lib = _lib()
+    sh = _shape(ops)
+    fake = ctypes.c_void_p(1 << 30)
+    for op in (ops.OP_GDN_FWD, ops.OP_GDN_BWD):
+        assert lib.clr_range_status(ctypes.byref(sh), op, None, None) == ops.CLR_OK
+    for op in (ops.OP_GLA_FWD, ops.OP_GLA_BWD, ops.OP_M2_FWD, ops.OP_M2_BWD, ops.OP_KDA_FWD, ops.OP_KDA_BWD):
+        assert lib.clr_range_status(ctypes.byref(sh), op, None, None) == ops.CLR_EWORKSPACE
+        assert lib.clr_range_status(ctypes.byref(sh), op, ctypes.c_void_p((1 << 30) + 8), None) == \
+            ops.CLR_EWORKSPACE
+        assert lib.clr_range_status(None, op, fake, None) == ops.CLR_EINVAL
+        assert lib.clr_range_status(ctypes.byref(_shape(ops, dk=96, dv=96)), op, fake, None) == ops.CLR_ENOTSUP
+        assert lib.clr_range_status(ctypes.byref(_shape(ops, T=0)), op, fake, None) == ops.CLR_OK  # no blocks
+    for op in (-1, 8):
+        assert lib.clr_range_status(ctypes.byref(sh), op, fake, None) == ops.CLR_EINVAL
+    # the fp32 KDA backward exists for d = 32 only
+    f32 = _shape(ops, dk=64, dv=64, dtype=0)
+    assert lib.clr_range_status(ctypes.byref(f32), ops.OP_KDA_BWD, fake, None) == ops.CLR_ENOTSUP
 
 
 def test_binding_checks_shapes_and_dtypes_before_the_library():
