@@ -97,10 +97,10 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
                     2 * CC * dk + 2 * C * kv + 3 * (2 * CC * dv)),
         "gdn_scan_bwd": (C * f4 + 2 * Ck * es + kv * f4 + Cv * f4 + 2 * kv * es + Cv * f4,
                          3 * (2 * C * kv) + 2 * C * kv // 2),
-        # reads T^T and the decayed Gram tiles that the backward's prep wrote
+        # reads T^T that the backward's prep wrote and forms the decayed Gram tiles again
         "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 3 * kv * es + 2 * Cv * f4 + 3 * Ck * es + 2 * C * es
-                          + CC * es + CC * f4,
-                          6 * (2 * C * kv) + 16 * (2 * CC * dk) + 2 * (2 * C ** 3)),
+                          + CC * es,
+                          6 * (2 * C * kv) + 16 * (2 * CC * dk) + 2 * (2 * C ** 3) + CC * dk),
     }
     # GLA (per-channel gate, gk = dk gate values per token) and its scalar-gate
     # Mamba-2 member on the same kernels (gk = 1)
@@ -118,9 +118,9 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
         W[pre + "_scan_fwd_rec"] = W[pre + "_scan_fwd"]
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
     # the backward's prep also reads Q and dO and writes the reverse scan's
-    # operands W^T, Kh, dvloc^T, R (fp32) and T^T, K K^T * G for the block
-    # adjoints; products P = Q K^T, P^T dO, Z = Gam Q - P W, R = Z^T dO
-    W["gdn_prep_bwd"] = (W["gdn_prep"][0] + 2 * Ck * es + 2 * Ck * es + Cv * f4 + kv * f4 + CC * es + CC * f4,
+    # operands W^T, Kh, dvloc^T, R (fp32) and T^T for the block adjoints;
+    # products P = Q K^T, P^T dO, Z = Gam Q - P W, R = Z^T dO
+    W["gdn_prep_bwd"] = (W["gdn_prep"][0] + 2 * Ck * es + 2 * Ck * es + Cv * f4 + kv * f4 + CC * es,
                          W["gdn_prep"][1] + 2 * CC * dk + 2 * CC * dv + 2 * CC * dk + 2 * C * kv)
     # KDA (per-channel gate, dk == dv): the Gated DeltaNet data flow with
     # per-channel decays (exp(b_C) per channel in place of the per-token

@@ -78,7 +78,6 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
         if (es == 2) w.dhT_lo = c.take(nb * dk * dv * es);  // the lo part of dh (bf16 pair)
         w.dUT = c.take(nb * BLK * dv * 4);
         w.TT = c.take(nb * BLK * BLK * es);
-        w.KKG = (float*)c.take(nb * BLK * BLK * 4);
     }
     if (total) *total = c.off;
     return w;

@@ -50,7 +50,7 @@ struct GdnWs {
     void* dhT_lo; // [.., dk, dv]   GDN, bf16 inputs: the lo part of that gradient
     void* dUT;    // [.., dv, 64]   dU^T
     void* TT;     // [.., 64, 64]   T^T (tiled), T = (I + A)^-1
-    float* KKG;   // [.., 16, 256]  K K^T * G, strictly lower, accumulator tiles (rb, cb) at (4 rb + cb) * 256
+    float* KKG;   // [.., 16, 256]  KDA: M, the decayed Gram product, accumulator tiles (rb, cb) at (4 rb + cb) * 256
     // KDA backward only
     void* Kd;     // [.., 64, dk]   K e^b (row-major)
     float* dM;    // [.., 64, 64]   Diag(beta) dA, the adjoint of the decayed Gram product (fp32)
@@ -81,10 +81,8 @@ template <typename E> struct GdnPrepArgs {
     float* UtT;
     float* eg;
     int n0 = 0;  // first block of the launch (grid x covers blocks n0 ..)
-    // backward only (nullable): T^T (tiled [s][t]) and the decayed Gram
-    // product K K^T * G (strictly lower, fp32, 16 accumulator tiles)
+    // backward only (nullable): T^T (tiled [s][t])
     E* TT = nullptr;
-    float* KKG = nullptr;
     // backward only: the reverse scan's operands (q, dO in; W^T, Kh, dvloc^T, R out)
     const E *q = nullptr, *dO = nullptr;
     E *WT = nullptr, *Kh = nullptr;

@@ -11,7 +11,6 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     GdnPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
                       ws.gam, (E*)ws.W, (E*)ws.KhT, (float*)ws.UtT, ws.eg};
     pa.TT = (E*)ws.TT;
-    pa.KKG = ws.KKG;
     pa.q = (const E*)L.q;
     pa.dO = (const E*)L.dO;
     pa.WT = (E*)ws.WT;
@@ -29,7 +28,7 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
            dim3(scan_threads<SCAN_NP_FAST>), st, sa, sb, G);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const float*)ws.UT, (const float*)ws.dUT,
-                       (const E*)ws.TT, ws.KKG,
+                       (const E*)ws.TT,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};
     ia.dh_lo = (const E*)ws.dhT_lo;
     launch("gdn_bwd_intra", gdn_bwd_intra_kernel<E, DK, DV>, gblk, dim3(512), st, ia);

@@ -62,7 +62,6 @@ template <typename E> struct GdnIntraArgs {
     const E *h, *dh;
     const float *UT, *dUT;
     const E* TT;        // T^T per block (tiled), from the prep
-    const float* KKG;   // K K^T * G per block (accumulator tiles), from the prep
     E *dq, *dk, *dv, *dg, *dbeta;
     int T, H, NC;
     const E* dh_lo = nullptr;  // bf16 inputs: lo part of dh
@@ -545,11 +544,25 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
 
     // ---------------- phase B: WY-transform adjoints ------------------------
     // K K^T * G tiles (w, cb) of this half, cb = hf and hf + 2 (rows 16w + 4g + i,
-    // column 16cb + r), in flight during the dW and dT products
+    // column 16cb + r), strictly lower: the prep's Gram products (same operands,
+    // same order, so the same values), formed again from the staged K
     f32x4 kkgt[2];
+    {
+        const f32x4 gr = ld4_now(s_gam + 16 * w + 4 * g);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-        kkgt[u] = *(const f32x4*)(a.KKG + chunk * BLK * BLK + (4 * w + hf + 2 * u) * 256 + l * 4);
+        for (int u = 0; u < 2; ++u) {
+            const int cb = hf + 2 * u;
+            f32x4 acc = zero4();
+            if (cb <= w) {
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    mma(acc, ldfrag(Ks + (16 * w + r) * PK + 32 * kk + 4 * g), ldfrag(Ks + (16 * cb + r) * PK + 32 * kk + 4 * g));
+            }
+            const float gc = s_gam[16 * cb + r];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kkgt[u][i] = 16 * cb + r < 16 * w + 4 * g + i ? acc[i] * __expf(gr[i] - gc) : 0.f;
+        }
+    }
     E* dUTs = (E*)(lds + Lay::pB_dUT);
     E* dUTl = (E*)(lds + Lay::pB_dUTl);
     E* dWs = (E*)(lds + Lay::pB_dW);

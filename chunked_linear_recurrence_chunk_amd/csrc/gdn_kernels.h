@@ -174,7 +174,7 @@ __device__ __forceinline__ void st_fragT(float* base, int f, int l, const Frag<f
 //   W^T and K (tiled),
 //   dvloc = P^T dO,  P[t][s] = (q_t . k_s) exp(gamma_t - gamma_s)  (s <= t),
 //   R = (Diag(Gam) Q)^T dO - W^T dvloc = Z^T dO,  Z = Diag(Gam) Q - P W,
-// and writes T^T and K K^T * G for the block adjoints.  The LDS regions of
+// and writes T^T for the block adjoints.  The LDS regions of
 // the first part are reused by the second:
 //   [Ks | Vs -> Qs | Am -> Ws | Td | T (fp32) -> dOs],  P^T over Ks (or after
 //   the last region when it does not fit there).
@@ -261,7 +261,6 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
                 kkg[i] = col < row ? acc[i] * __expf(gr[i] - gc) : 0.f;
                 Am[row * AP + col] = br[i] * kkg[i];
             }
-            if (a.KKG) *(f32x4*)(a.KKG + chunk * BLK * BLK + (4 * w + j) * 256 + l * 4) = kkg;
         }
     }
     __syncthreads();
