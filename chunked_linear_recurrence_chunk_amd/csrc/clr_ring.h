@@ -29,6 +29,9 @@ constexpr int NPROD = 3;         // producer waves
 
 // s_waitcnt immediate for vmcnt(n), other counters unconstrained (gfx9 encoding).
 constexpr unsigned vmcnt_imm(int n) { return (unsigned)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8)); }
+// s_waitcnt immediate for lgkmcnt(0) (this wave's LDS operations done), the
+// other counters unconstrained.
+constexpr unsigned lgkmcnt0_imm() { return (unsigned)(15 | (3 << 14) | (7 << 4)); }
 
 template <int NU, int NP = NPROD>
 struct RingGeom {
@@ -44,6 +47,7 @@ __device__ __forceinline__ void ring_wait(int k) {
     else if (k == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NU_MIN));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NU_MIN));
 }
+
 
 __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");

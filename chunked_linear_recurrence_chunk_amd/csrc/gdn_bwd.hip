@@ -24,8 +24,9 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
                          L.dS_out, L.dS_in, (E*)ws.dhT, ws.dUT, L.H, L.NC, L.B * L.H};
     sb.dh_lo = (E*)ws.dhT_lo;
     const int G = (int)scan_grid(DV / 16, L.B * L.H);
-    launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV, false, SCAN_NP_FAST>, dim3(2 * G),
-           dim3(scan_threads<SCAN_NP_FAST>), st, sa, sb, G);
+    constexpr int NCW = scan_can_split<E, DK>() ? 2 : 1, NP = scan_np_fast<NCW>;
+    launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV, false, NP, NCW>, dim3(2 * G),
+           dim3(scan_threads<NP, NCW>), st, sa, sb, G);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
                        ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const float*)ws.UT, (const float*)ws.dUT,
                        (const E*)ws.TT,

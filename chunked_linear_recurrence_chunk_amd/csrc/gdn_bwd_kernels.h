@@ -77,9 +77,9 @@ template <typename E> struct GdnIntraArgs {
 // ---------------------------------------------------------------------------
 // (W^T and R are read from the slot by the step itself, after the K dS
 // products have been issued, so that their registers are not live at once.)
-template <typename E, int DK, typename UE = E> struct ScanBwdOps {
-    Frag<E> kh[4][DK / 32];   // K (GDN) or Kh (KDA, hi half) rows (A: m = t, k = d)
-    Frag<E> kl[4][DK / 32];   // KDA: lo half of Kh
+template <typename E, int DK, typename UE = E, int NCW = 1> struct ScanBwdOps {
+    Frag<E> kh[4][DK / 32 / NCW];   // K (GDN) or Kh (KDA, hi half) rows (A: m = t, k = d), this consumer's key range
+    Frag<E> kl[4][DK / 32 / NCW];   // KDA: lo half of Kh
     Frag<UE> dvl[2];          // dvloc^T[v0 + r][token tile pairs] (accumulator layout)
     float GC;                 // GDN: Gam_C, from the small unit
 };
@@ -96,23 +96,24 @@ template <typename E, int DK, bool PCD = false> struct ScanBwdRing {
     static constexpr int NU = NKU + NWU + NRU + NDU + (PCD ? 1 : 0);
 };
 
-template <typename E, int DK, int NU, bool PCD>
-__device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK, ScanWsT<PCD, E>>& o, const char* slot, int l) {
+template <typename E, int DK, int NU, bool PCD, int C = 0, int NCW = 1>
+__device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK, ScanWsT<PCD, E>, NCW>& o, const char* slot, int l) {
     using Rg = ScanBwdRing<E, DK, PCD>;
     using UE = ScanWsT<PCD, E>;
-    constexpr int KK = DK / 32, UPFU = Rg::UPFU;
+    constexpr int KK = DK / 32, KKC = KK / NCW, UPFU = Rg::UPFU;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            o.kh[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
-            if constexpr (Rg::KP == 2) o.kl[tb][kk] = ring_frag(slot, 4 * KK + tb * KK + kk, l, (E*)nullptr);
+        for (int kk = 0; kk < KKC; ++kk) {
+            o.kh[tb][kk] = ring_frag(slot, tb * KK + C * KKC + kk, l, (E*)nullptr);
+            if constexpr (Rg::KP == 2) o.kl[tb][kk] = ring_frag(slot, 4 * KK + tb * KK + C * KKC + kk, l, (E*)nullptr);
         }
-    // dvloc fragments start at unit NKU + NWU + NRU, i.e. fragment index (that) / UPFU
+    // dvloc fragments start at unit NKU + NWU + NRU, i.e. fragment index (that) / UPFU;
+    // with two consumers, consumer j stores fragment j of dU
     static_assert((Rg::NKU + Rg::NWU + Rg::NRU) % UPFU == 0, "fragment alignment");
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-        o.dvl[j] = ring_frag(slot, (Rg::NKU + Rg::NWU + Rg::NRU) / UPFU + j, l, (UE*)nullptr);
+        if (NCW == 1 || j == C) o.dvl[j] = ring_frag(slot, (Rg::NKU + Rg::NWU + Rg::NRU) / UPFU + j, l, (UE*)nullptr);
     o.GC = ring_small<NU>(slot, BLK - 1);
 }
 
@@ -120,56 +121,59 @@ __device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK, ScanWsT<PCD
 // dU_n = dvloc_n + Kh_n dS; leaves dS = dL/dS_n = Gam_C dS + R_n - W_n^T (Kh_n dS).
 // Gated DeltaNet: Kh_n dS = Diag(e) (K_n dS) with e_t = exp(gamma_C - gamma_t)
 // and dS split (the operand of a product whose rows telescope over repeated
-// keys), dU fp32, dh stored as a bf16 hi/lo pair.
-template <typename E, int DK, int DV, int NU = 0, bool PCD = false>
-__device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PCD, E>>& o, f32x4 (&dS)[DK / 16],
-                                              const GdnScanBwdArgs<E>& a, size_t chunk, int vb, int l, E* tile,
-                                              const char* slot = nullptr) {
-    constexpr int ND = DK / 16, KK = DK / 32;
+// keys), dU fp32, dh stored as a bf16 hi/lo pair.  Consumer C of NCW holds
+// the rows of its key range; K_n dS is the sum of the consumers' parts.
+template <typename E, int DK, int DV, int NU = 0, bool PCD = false, int C = 0, int NCW = 1>
+__device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PCD, E>, NCW>& o,
+                                              f32x4 (&dS)[DK / 16 / NCW], const GdnScanBwdArgs<E>& a, size_t chunk,
+                                              int vb, int l, E* tile, const char* slot, f32x4* xch) {
+    constexpr int KKC = DK / 32 / NCW, NDC = DK / 16 / NCW;
     using UE = ScanWsT<PCD, E>;
     f32x4 dUp[4];
     if constexpr (PCD) {
         // KDA: Kh (a pair) times the split dS; dh stored once
-        Frag2<E> fs[KK];
+        Frag2<E> fs[KKC];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) fs[kk] = split_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+        for (int kk = 0; kk < KKC; ++kk) fs[kk] = split_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
         {
-            Frag<E> fh[KK];
+            Frag<E> fh[KKC];
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) fh[kk] = fs[kk].hi;
-            state_store<E, DK, DV, true>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
+            for (int kk = 0; kk < KKC; ++kk) fh[kk] = fs[kk].hi;
+            state_store<E, DK, DV, true, C, NCW>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
         }
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) mma2(acc, pair_of(o.kh[tb][kk], o.kl[tb][kk]), fs[kk]);
+            for (int kk = 0; kk < KKC; ++kk) mma2(acc, pair_of(o.kh[tb][kk], o.kl[tb][kk]), fs[kk]);
             dUp[tb] = acc;
         }
+        if constexpr (NCW == 2) consumers_exchange<C>(dUp, xch, l);
     } else {
-        Frag2<E> fs[KK];
+        Frag2<E> fs[KKC];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) fs[kk] = split_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
+        for (int kk = 0; kk < KKC; ++kk) fs[kk] = split_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) mma2(acc, o.kh[tb][kk], fs[kk]);
+            for (int kk = 0; kk < KKC; ++kk) mma2(acc, o.kh[tb][kk], fs[kk]);
             dUp[tb] = acc;
         }
-        // both parts of the state through the wave's LDS tile (no matrix-core work)
+        // both parts of the state through the LDS tile (no matrix-core work)
         {
-            Frag<E> fh[KK];
+            Frag<E> fh[KKC];
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) fh[kk] = fs[kk].hi;
-            state_store<E, DK, DV, true>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
+            for (int kk = 0; kk < KKC; ++kk) fh[kk] = fs[kk].hi;
+            state_store<E, DK, DV, true, C, NCW>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
         }
         if constexpr (sizeof(E) == 2) {
-            Frag<E> fl[KK];
+            Frag<E> fl[KKC];
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) fl[kk] = fs[kk].lo;
-            state_store<E, DK, DV, true>(a.dh_lo + chunk * DK * DV, fl, tile, 16 * vb, l);
+            for (int kk = 0; kk < KKC; ++kk) fl[kk] = fs[kk].lo;
+            state_store<E, DK, DV, true, C, NCW>(a.dh_lo + chunk * DK * DV, fl, tile, 16 * vb, l);
         }
+        if constexpr (NCW == 2) consumers_exchange<C>(dUp, xch, l);
         // e_t = exp(gamma_C - gamma_t) from the small unit (its last slot holds Gam_C: e_63 = 1)
         const f32x4* es = (const f32x4*)(slot + NU * RING_UNIT) + (l >> 4);
 #pragma unroll
@@ -180,27 +184,26 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
         }
     }
     using Rg = ScanBwdRing<E, DK, PCD>;
-    Frag<E> wt[ND][2];  // W^T rows (A: m = d, k = t)
-    f32x4 rt[ND];       // R accumulator tiles (rows d, column v0 + r)
+    Frag<E> wt[NDC][2];  // W^T rows (A: m = d, k = t)
+    f32x4 rt[NDC];       // R accumulator tiles (rows d, column v0 + r)
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
+    for (int db = 0; db < NDC; ++db) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) wt[db][j] = ring_frag(slot, Rg::NKU / Rg::UPF + 2 * db + j, l, (E*)nullptr);
-        rt[db] = *(const f32x4*)(slot + (Rg::NKU + Rg::NWU + db) * RING_UNIT + l * 16);
+        for (int j = 0; j < 2; ++j) wt[db][j] = ring_frag(slot, Rg::NKU / Rg::UPF + 2 * (C * NDC + db) + j, l, (E*)nullptr);
+        rt[db] = *(const f32x4*)(slot + (Rg::NKU + Rg::NWU + C * NDC + db) * RING_UNIT + l * 16);
     }
     UE* dUT = (UE*)a.dUT + chunk * BLK * DV;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        st8T(dUT, 2 * vb + j, l, dUp[2 * j] + o.dvl[j].lo, dUp[2 * j + 1] + o.dvl[j].hi);
-    }
+    for (int j = 0; j < 2; ++j)
+        if (NCW == 1 || j == C) st8T(dUT, 2 * vb + j, l, dUp[2 * j] + o.dvl[j].lo, dUp[2 * j + 1] + o.dvl[j].hi);
     Frag<E> fu[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) fu[j] = frag_from_acc<E>(-dUp[2 * j], -dUp[2 * j + 1]);
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
+    for (int db = 0; db < NDC; ++db) {
         f32x4 acc;
         if constexpr (PCD)  // row d scaled by exp(b_C[d]) from the slot's last unit
-            acc = dS[db] * *(const f32x4*)((const float*)(slot + (NU - 1) * RING_UNIT) + 4 * (l >> 4) + 16 * db) + rt[db];
+            acc = dS[db] * *(const f32x4*)((const float*)(slot + (NU - 1) * RING_UNIT) + 4 * (l >> 4) + 16 * (C * NDC + db)) + rt[db];
         else
             acc = dS[db] * o.GC + rt[db];
 #pragma unroll
@@ -209,100 +212,118 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
     }
 }
 
-template <typename E, int DK, bool PCD = false> struct ScanBwdGeom {
+template <typename E, int DK, bool PCD = false, int NCW_ = 1> struct ScanBwdGeom {
     static constexpr int NU = ScanBwdRing<E, DK, PCD>::NU;
     static constexpr int SLOT = RingGeom<NU>::SLOT;
     static constexpr int TILE = state_tile_bytes(DK, sizeof(E));
-    static constexpr int PF = (160 * 1024 - 512 - TILE) / SLOT;  // ring + tile within the CU's LDS
+    static constexpr int NCW = NCW_;
+    static_assert(NCW == 1 || (NCW == 2 && scan_can_split<E, DK>()), "consumer split");
+    static constexpr int XCH = NCW == 2 ? 2 * 4 * 64 * 16 : 0;  // the consumers' exchange
+    static constexpr int PF = (160 * 1024 - 512 - TILE - XCH) / SLOT;  // ring, tile, exchange within the CU's LDS
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
-    static constexpr int LDS = P * SLOT + TILE;
+    static constexpr int LDS = P * SLOT + TILE + XCH;
 };
 
-template <typename E, int DK, int DV, bool PCD = false, int NP = NPROD>
+// Consumer C of the reverse scan body.
+template <typename E, int DK, int DV, bool PCD, int NP, int NCW, int C>
+__device__ __forceinline__ void gdn_scan_bwd_consume(const GdnScanBwdArgs<E>& a, const char* ring, E* tile, f32x4* xch,
+                                                     size_t bh, int vb, int l) {
+    using SG = ScanBwdGeom<E, DK, PCD, NCW>;
+    using UT_ = ScanWsT<PCD, E>;
+    constexpr int NDC = DK / 16 / NCW, NU = SG::NU, P = SG::P;
+    using G = RingGeom<NU, NP>;
+    const int NC = a.NC, r = l & 15, g = l >> 4, v0 = 16 * vb;
+    f32x4 dS[NDC];
+    const float* dSo = a.dS_out ? a.dS_out + bh * DK * DV : nullptr;
+#pragma unroll
+    for (int db = 0; db < NDC; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dS[db][i] = dSo ? dSo[(size_t)(16 * (C * NDC + db) + 4 * g + i) * DV + v0 + r] : 0.f;
+    ring_barrier();
+    for (int m = 0; m < NC; ++m) {
+        ScanBwdOps<E, DK, UT_, NCW> o;
+        const char* slot = ring + (m % P) * G::SLOT;
+        scan_bwd_from_ring<E, DK, NU, PCD, C, NCW>(o, slot, l);
+        scan_bwd_step<E, DK, DV, NU, PCD, C, NCW>(o, dS, a, bh * NC + (NC - 1 - m), vb, l, tile, slot, xch);
+        ring_barrier();
+    }
+    float* dSi = a.dS_in + bh * DK * DV;
+#pragma unroll
+    for (int db = 0; db < NDC; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dSi[(size_t)(16 * (C * NDC + db) + 4 * g + i) * DV + v0 + r] = dS[db][i];
+}
+
+template <typename E, int DK, int DV, bool PCD = false, int NP = NPROD, int NCW = 1>
 __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, int wgi, char* smem) {
     const int H = a.H, NC = a.NC;
     int b, h, vb;
     if (!scan_coords(wgi, DV / 16, a.BH, H, b, h, vb)) return;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
-    const int v0 = 16 * vb;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     constexpr int ND = DK / 16;
     using Rg = ScanBwdRing<E, DK, PCD>;
-    using SG = ScanBwdGeom<E, DK, PCD>;
+    using SG = ScanBwdGeom<E, DK, PCD, NCW>;
     using UT_ = ScanWsT<PCD, E>;
     constexpr int NU = Rg::NU, UPFU = Rg::UPFU, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
     using G = RingGeom<NU, NP>;
     char* ring = smem;
     E* tile = (E*)(smem + P * G::SLOT);
+    f32x4* xch = (f32x4*)(smem + P * G::SLOT + SG::TILE);
     const size_t bh = (size_t)b * H + h;
 
     // round m handles block NC - 1 - m
-    if (w > 0) {  // producers
-        const int pid = w - 1;
+    // lane 0's address of unit u of workspace block c (lane l reads 16 l bytes further)
+    auto unit_ptr = [&](size_t c, int u) -> const char* {
+        if (u < Rg::NKU) {  // KDA: the lo half follows the hi half
+            if (Rg::KP == 2 && u >= Rg::NKU / 2) return (const char*)(a.Kh_lo + c * BLK * DK + (u - Rg::NKU / 2) * UE);
+            return (const char*)(a.Kh + c * BLK * DK + u * UE);
+        }
+        if (u < Rg::NKU + Rg::NWU) return (const char*)(a.WT + c * BLK * DK + (u - Rg::NKU) * UE);
+        if (u < Rg::NKU + Rg::NWU + Rg::NRU)
+            return (const char*)(a.Rt + c * DK * DV + (size_t)vb * ND * 256 + (size_t)(u - Rg::NKU - Rg::NWU) * 256);
+        if (PCD && u == NU - 1) return (const char*)(a.eC + c * 256);
+        return (const char*)((const UT_*)a.dvlT + c * BLK * DV + (size_t)(2 * vb * UPFU) * UNIT_ELEMS<UT_> +
+                             (size_t)(u - Rg::NKU - Rg::NWU - Rg::NRU) * UNIT_ELEMS<UT_>);
+    };
+    auto small_ptr = [&](size_t c) -> const char* {
+        return PCD ? (const char*)(a.eC + c * 256) : (const char*)(a.eg + c * BLK);
+    };
+    const int pre = NC < P - 1 ? NC : P - 1;
+    if (w >= NCW) {  // producers
+        const int pid = w - NCW;
         auto issue = [&](int m) {
             const size_t c = bh * NC + (NC - 1 - m);
-            const E* Kh = a.Kh + c * BLK * DK + l * LE;
-            const E* Khl = PCD ? a.Kh_lo + c * BLK * DK + l * LE : nullptr;
-            const E* WT = a.WT + c * BLK * DK + l * LE;
-            const float* Rt = a.Rt + c * DK * DV + (size_t)vb * ND * 256 + l * 4;
-            const UT_* dvl = (const UT_*)a.dvlT + c * BLK * DV + (size_t)(2 * vb * UPFU) * UNIT_ELEMS<UT_> +
-                             l * LANE_ELEMS<UT_>;
-            auto src = [&](int u) -> const void* {
-                if (u < Rg::NKU) {  // KDA: the lo half follows the hi half
-                    if (Rg::KP == 2 && u >= Rg::NKU / 2) return Khl + (u - Rg::NKU / 2) * UE;
-                    return Kh + u * UE;
-                }
-                if (u < Rg::NKU + Rg::NWU) return WT + (u - Rg::NKU) * UE;
-                if (u < Rg::NKU + Rg::NWU + Rg::NRU) return Rt + (u - Rg::NKU - Rg::NWU) * 256;
-                if (PCD && u == NU - 1) return a.eC + c * 256 + l * 4;
-                return dvl + (u - Rg::NKU - Rg::NWU - Rg::NRU) * UNIT_ELEMS<UT_>;
-            };
-            ring_issue<NU, decltype(src), NP>(ring + (m % P) * G::SLOT, pid, src,
-                                              PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.eg + c * BLK + l));
+            auto src = [&](int u) -> const void* { return unit_ptr(c, u) + 16 * l; };
+            ring_issue<NU, decltype(src), NP>(ring + (m % P) * G::SLOT, pid, src, small_ptr(c) + 4 * l);
         };
-        const int pre = NC < P - 1 ? NC : P - 1;
         for (int m = 0; m < pre; ++m) issue(m);
         ring_wait<G::NU_MIN>(pre - 1);  // round 0 has landed
         ring_barrier();
         for (int m = 0; m < NC; ++m) {
             if (m + P - 1 < NC) issue(m + P - 1);
+            if constexpr (NCW == 2) ring_barrier();  // the consumers' exchange within round m
             const int last = (m + P - 1 < NC ? m + P - 1 : NC - 1);
             ring_wait<G::NU_MIN>(last - (m + 1));  // round m + 1 has landed
             ring_barrier();
         }
         return;
     }
-
-    f32x4 dS[ND];
-    const float* dSo = a.dS_out ? a.dS_out + bh * DK * DV : nullptr;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dS[db][i] = dSo ? dSo[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
-    ring_barrier();
-    for (int m = 0; m < NC; ++m) {
-        ScanBwdOps<E, DK, UT_> o;
-        const char* slot = ring + (m % P) * G::SLOT;
-        scan_bwd_from_ring<E, DK, NU, PCD>(o, slot, l);
-        scan_bwd_step<E, DK, DV, NU, PCD>(o, dS, a, bh * NC + (NC - 1 - m), vb, l, tile, slot);
-        ring_barrier();
-    }
-    float* dSi = a.dS_in + bh * DK * DV;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dSi[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = dS[db][i];
+    if (w == 0) gdn_scan_bwd_consume<E, DK, DV, PCD, NP, NCW, 0>(a, ring, tile, xch, bh, vb, l);
+    if constexpr (NCW == 2)
+        if (w == 1) gdn_scan_bwd_consume<E, DK, DV, PCD, NP, NCW, 1>(a, ring, tile, xch, bh, vb, l);
 }
 
 // The forward recompute (state entering every block) and the reverse scan are
 // independent given the prep outputs; one launch runs both, work-groups
 // [0, G) the former and [G, 2G) the latter, so together they fill the chip.
-template <typename E, int DK, int DV, bool PCD = false, int NP = NPROD>
-__global__ __launch_bounds__(scan_threads<NP>) void gdn_scan_pair_kernel(GdnScanArgs<E> fa, GdnScanBwdArgs<E> ba, int G) {
-    constexpr int LF = ScanFwdGeom<E, DK, DV, true, PCD>::LDS, LB = ScanBwdGeom<E, DK, PCD>::LDS;
+template <typename E, int DK, int DV, bool PCD = false, int NP = NPROD, int NCW = 1>
+__global__ __launch_bounds__((scan_threads<NP, NCW>)) void gdn_scan_pair_kernel(GdnScanArgs<E> fa, GdnScanBwdArgs<E> ba, int G) {
+    constexpr int LF = ScanFwdGeom<E, DK, DV, true, PCD, NCW>::LDS, LB = ScanBwdGeom<E, DK, PCD, NCW>::LDS;
     __shared__ __align__(16) char smem[LF > LB ? LF : LB];
-    if ((int)blockIdx.x < G) gdn_scan_fwd_body<E, DK, DV, true, PCD, NP>(fa, blockIdx.x, smem);
-    else gdn_scan_bwd_body<E, DK, DV, PCD, NP>(ba, blockIdx.x - G, smem);
+    if ((int)blockIdx.x < G) gdn_scan_fwd_body<E, DK, DV, true, PCD, NP, NCW>(fa, blockIdx.x, smem);
+    else gdn_scan_bwd_body<E, DK, DV, PCD, NP, NCW>(ba, blockIdx.x - G, smem);
 }
 
 // ---------------------------------------------------------------------------

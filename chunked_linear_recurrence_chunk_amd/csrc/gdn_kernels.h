@@ -431,10 +431,22 @@ template <bool PCD, typename E> using ScanWsT = float;
 // Factor of the key units in a ring slot: two for the KDA pair (bf16 only).
 template <bool PCD, typename E> constexpr int key_parts() { return PCD && sizeof(E) == 2 ? 2 : 1; }
 
-template <typename E, int DK, typename UE = E> struct ScanFwdOps {
-    Frag<E> w[4][DK / 32];    // W rows (A: m = t, k = d)
-    Frag<E> kh[DK / 16][2];   // K^T (GDN) or Kh^T (KDA, hi half) rows (A: m = d, k = t)
-    Frag<E> kl[DK / 16][2];   // KDA: lo half of Kh^T
+// Consumer waves per scan work-group (NCW).  With two (bf16, dk >= 64, where
+// each takes whole 32-row fragments of the key dimension) consumer c keeps
+// the state rows [c dk/2, (c+1) dk/2) of the slice and forms its half of each
+// contraction over d; the two partial sums meet in LDS (one more work-group
+// barrier per block), so a block's matrix-core chain runs on two SIMDs
+// instead of one.  Where that chain bounds the scan (the Gated DeltaNet pair
+// scan: 42.2 -> 35.4 us per 2048-token chunk at H = 16) two are used; where
+// the operand stream does (the Gated DeltaNet forward scan: 28.5 -> 30.2 us
+// with two), or the extra barrier costs more than it saves (KDA's scans:
+// 51 -> 66 us and 64 -> 69 us), one.
+template <typename E, int DK> constexpr bool scan_can_split() { return sizeof(E) == 2 && DK >= 64; }
+
+template <typename E, int DK, typename UE = E, int NCW = 1> struct ScanFwdOps {
+    Frag<E> w[4][DK / 32 / NCW];   // W rows (A: m = t, k = d), this consumer's key range
+    Frag<E> kh[DK / 16 / NCW][2];  // K^T (GDN) or Kh^T (KDA, hi half) rows (A: m = d, k = t), same range
+    Frag<E> kl[DK / 16 / NCW][2];  // KDA: lo half of Kh^T
     Frag<UE> ut[2];           // -Ut^T[v0 + r][token pair-tiles 2j, 2j+1] (accumulator layout)
     float GC;                 // GDN: Gam_C = exp(gamma_C), from the small unit
 };
@@ -524,86 +536,116 @@ __device__ __forceinline__ void store_state_sel(E* h, const Frag<E> (&fs)[DK / 3
 // the selector products are (both halves through LDS: 31.5 us).
 // state_store() picks accordingly.
 constexpr int state_tile_bytes(int dk, int es) { return 16 * (dk + 8) * es; }
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void store_state_tr(E* h, const Frag<E> (&fs)[DK / 32], E* tile, int v0, int l) {
+// With two consumers (C, NCW = 2) each writes and reads back the columns of
+// its own key range of the shared tile.
+template <typename E, int DK, int DV, int C = 0, int NCW = 1>
+__device__ __forceinline__ void store_state_tr(E* h, const Frag<E> (&fs)[DK / 32 / NCW], E* tile, int v0, int l) {
     if constexpr (sizeof(E) == 2) {
-        constexpr int PS = DK + 8;
+        constexpr int PS = DK + 8, KKC = DK / 32 / NCW, NDC = DK / 16 / NCW;
         const int r = l & 15, g = l >> 4, j = (l >> 2) & 3, q = l & 3;
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
+        for (int kk = 0; kk < KKC; ++kk) {
             const bf16x8 v = fs[kk].v;
-            *(bf16x4*)(tile + r * PS + 32 * kk + 4 * g) = bf16x4{v[0], v[1], v[2], v[3]};
-            *(bf16x4*)(tile + r * PS + 32 * kk + 16 + 4 * g) = bf16x4{v[4], v[5], v[6], v[7]};
+            const int c0 = 32 * (C * KKC + kk);
+            *(bf16x4*)(tile + r * PS + c0 + 4 * g) = bf16x4{v[0], v[1], v[2], v[3]};
+            *(bf16x4*)(tile + r * PS + c0 + 16 + 4 * g) = bf16x4{v[4], v[5], v[6], v[7]};
         }
         // LDS operations of one wave complete in order
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int db = 0; db < DK / 16; ++db) {
+        for (int db = 0; db < NDC; ++db) {
+            const int d0 = 16 * (C * NDC + db);
             const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(tile + (4 * g + j) * PS + 16 * db + 4 * q));
-            *(bf16x4*)(h + toff<E>(16 * db + r, v0 + 4 * g, DV)) = x;
+                (lds_bf16x4*)(tile + (4 * g + j) * PS + d0 + 4 * q));
+            *(bf16x4*)(h + toff<E>(d0 + r, v0 + 4 * g, DV)) = x;
         }
         asm volatile("" ::: "memory");
     } else {
+        static_assert(NCW == 1, "fp32 states run with one consumer");
         store_state_sel<E, DK, DV>(h, fs, v0, l);
     }
 }
 
-template <typename E, int DK, int DV, bool VIA_LDS>
-__device__ __forceinline__ void state_store(E* h, const Frag<E> (&fs)[DK / 32], E* tile, int v0, int l) {
-    if constexpr (VIA_LDS) store_state_tr<E, DK, DV>(h, fs, tile, v0, l);
-    else store_state_sel<E, DK, DV>(h, fs, v0, l);
+template <typename E, int DK, int DV, bool VIA_LDS, int C = 0, int NCW = 1>
+__device__ __forceinline__ void state_store(E* h, const Frag<E> (&fs)[DK / 32 / NCW], E* tile, int v0, int l) {
+    if constexpr (VIA_LDS) {
+        store_state_tr<E, DK, DV, C, NCW>(h, fs, tile, v0, l);
+    } else {
+        static_assert(NCW == 1, "the selector path runs with one consumer");
+        store_state_sel<E, DK, DV>(h, fs, v0, l);
+    }
 }
 
 // One block of the recurrence.  HNAT selects the layout of the saved states:
 // false -> tiled h^T[v][d] (read by the forward's out kernel), true -> tiled
-// h[d][v] (read by the backward).
-template <typename E, int DK, int NU, typename UE, int KP = 1>
-__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK, UE>& o, const char* slot, int l);
+// h[d][v] (read by the backward).  Consumer C of NCW holds the state rows
+// 16 db of its key range (db = C ND/NCW ..), and the operands of that range.
+template <typename E, int DK, int NU, typename UE, int KP = 1, int C = 0, int NCW = 1>
+__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK, UE, NCW>& o, const char* slot, int l);
 
-template <typename E, int DK, int DV, bool HNAT, int NU, bool PCD = false>
-__device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>& o, f32x4 (&S)[DK / 16],
-                                              const GdnScanArgs<E>& a, size_t chunk, int vb, int l, E* tile,
-                                              const char* slot) {
-    constexpr int ND = DK / 16, KK = DK / 32;
-    using UE = ScanWsT<PCD, E>;
-    Frag<E> fs[KK];
+// The two consumers' partial sums X[4] (accumulator tiles over the 64 tokens)
+// of a contraction over their key halves, added in one fixed order so that
+// both hold the same values.  Both write, wait for their LDS writes, meet at
+// the work-group barrier (the producers take part in it), and read.
+template <int C>
+__device__ __forceinline__ void consumers_exchange(f32x4 (&X)[4], f32x4* xch, int l) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
-    // state entering block n
+    for (int tb = 0; tb < 4; ++tb) xch[(4 * C + tb) * 64 + l] = X[tb];
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    ring_barrier();
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const f32x4 other = xch[(4 * (1 - C) + tb) * 64 + l];
+        X[tb] = C == 0 ? X[tb] + other : other + X[tb];
+    }
+}
+
+template <typename E, int DK, int DV, bool HNAT, int NU, bool PCD = false, int C = 0, int NCW = 1>
+__device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>, NCW>& o, f32x4 (&S)[DK / 16 / NCW],
+                                              const GdnScanArgs<E>& a, size_t chunk, int vb, int l, E* tile,
+                                              const char* slot, f32x4* xch) {
+    constexpr int KK = DK / 32, NDC = DK / 16 / NCW, KKC = KK / NCW;
+    using UE = ScanWsT<PCD, E>;
+    Frag<E> fs[KKC];
+#pragma unroll
+    for (int kk = 0; kk < KKC; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
+    // state entering block n (this consumer's rows)
     if (a.hT) {
         E* hT = a.hT + chunk * DK * DV;
         if constexpr (HNAT) {
-            state_store<E, DK, DV, true>(hT, fs, tile, 16 * vb, l);  // through LDS in either scan
+            state_store<E, DK, DV, true, C, NCW>(hT, fs, tile, 16 * vb, l);  // through LDS in either scan
         } else {
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) st8T(hT, vb * KK + kk, l, S[2 * kk], S[2 * kk + 1]);
+            for (int kk = 0; kk < KKC; ++kk) st8T(hT, vb * KK + C * KKC + kk, l, S[2 * kk], S[2 * kk + 1]);
         }
     }
-    // -U = W S - Ut, accumulated onto the stored -Ut  (tiles: rows t = 16tb + 4g + i, col v0 + r)
+    // -U = W S - Ut, accumulated onto the stored -Ut  (tiles: rows t = 16tb + 4g + i, col v0 + r);
+    // with two consumers each forms W S over its key half, the first onto -Ut
     f32x4 U[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        U[2 * j] = o.ut[j].lo;
-        U[2 * j + 1] = o.ut[j].hi;
+        U[2 * j] = C == 0 ? o.ut[j].lo : zero4();
+        U[2 * j + 1] = C == 0 ? o.ut[j].hi : zero4();
     }
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) mma(U[tb], o.w[tb][kk], fs[kk]);
+        for (int kk = 0; kk < KKC; ++kk) mma(U[tb], o.w[tb][kk], fs[kk]);
     }
     // the Kh^T reads go out while the products above run
     asm volatile("" ::: "memory");
-    scan_fwd_from_ring_kh<E, DK, NU, UE, key_parts<PCD, E>()>(o, slot, l);
+    scan_fwd_from_ring_kh<E, DK, NU, UE, key_parts<PCD, E>(), C, NCW>(o, slot, l);
+    if constexpr (NCW == 2) consumers_exchange<C>(U, xch, l);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) U[tb] = -U[tb];
-    // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles
+    // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles (consumer j stores it)
     if (a.UT) {
         UE* UT = (UE*)a.UT + chunk * BLK * DV;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) st8T(UT, 2 * vb + j, l, U[2 * j], U[2 * j + 1]);
+        for (int j = 0; j < 2; ++j)
+            if (NCW == 1 || j == C) st8T(UT, 2 * vb + j, l, U[2 * j], U[2 * j + 1]);
     }
-    if (PCD && a.Utok) {
+    if (PCD && C == 0 && a.Utok) {
         // U token-major for the output kernel (rows of valid tokens)
         const size_t bh = chunk / a.NC;
         const int n = (int)(chunk % a.NC), bb = (int)(bh / a.H), hh = (int)(bh % a.H);
@@ -619,8 +661,8 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>
         fu[1] = split_acc<E>(U[2], U[3]);
         const float* ecs = (const float*)(slot + (NU - 1) * RING_UNIT) + 4 * (l >> 4);
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            f32x4 acc = S[db] * *(const f32x4*)(ecs + 16 * db);
+        for (int db = 0; db < NDC; ++db) {
+            f32x4 acc = S[db] * *(const f32x4*)(ecs + 16 * (C * NDC + db));
 #pragma unroll
             for (int j = 0; j < 2; ++j) mma2(acc, pair_of(o.kh[db][j], o.kl[db][j]), fu[j]);
             S[db] = acc;
@@ -640,7 +682,7 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>
         fu[0] = split_acc<E>(U[0], U[1]);
         fu[1] = split_acc<E>(U[2], U[3]);
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
+        for (int db = 0; db < NDC; ++db) {
             f32x4 acc = S[db] * o.GC;
 #pragma unroll
             for (int j = 0; j < 2; ++j) mma2(acc, o.kh[db][j], fu[j]);
@@ -650,50 +692,52 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>>
 }
 
 // Operands of one block from a ring slot (see clr_ring.h for the layout).
-template <typename E, int DK, int NU, typename UE, int KP = 1>
-__device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK, UE>& o, const char* slot, int l) {
-    constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * (DK / 16) * KP;
+template <typename E, int DK, int NU, typename UE, int KP = 1, int C = 0, int NCW = 1>
+__device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK, UE, NCW>& o, const char* slot, int l) {
+    constexpr int KK = DK / 32, KKC = KK / NCW, NWF = 4 * KK, NKF = 2 * (DK / 16) * KP;
     // units per fragment of W / K and of Ut; Ut starts after the W and K units
     constexpr int UPF = sizeof(E) == 2 ? 1 : 2, UPFU = sizeof(UE) == 2 ? 1 : 2;
     static_assert((NWF + NKF) * UPF % UPFU == 0, "fragment alignment");
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) o.w[tb][kk] = ring_frag(slot, tb * KK + kk, l, (E*)nullptr);
+        for (int kk = 0; kk < KKC; ++kk) o.w[tb][kk] = ring_frag(slot, tb * KK + C * KKC + kk, l, (E*)nullptr);
+    if constexpr (C == 0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, (NWF + NKF) * UPF / UPFU + j, l, (UE*)nullptr);
+        for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, (NWF + NKF) * UPF / UPFU + j, l, (UE*)nullptr);
+    }
     o.GC = ring_small<NU>(slot, BLK - 1);
 }
 // K^T (Kh^T) operands of a block (read after the W S products have been issued).
-template <typename E, int DK, int NU, typename UE, int KP>
-__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK, UE>& o, const char* slot, int l) {
-    constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * (DK / 16);
+template <typename E, int DK, int NU, typename UE, int KP, int C, int NCW>
+__device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK, UE, NCW>& o, const char* slot, int l) {
+    constexpr int KK = DK / 32, NWF = 4 * KK, NKF = 2 * (DK / 16), NDC = DK / 16 / NCW;
 #pragma unroll
-    for (int db = 0; db < DK / 16; ++db)
+    for (int db = 0; db < NDC; ++db)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            o.kh[db][j] = ring_frag(slot, NWF + 2 * db + j, l, (E*)nullptr);
-            if constexpr (KP == 2) o.kl[db][j] = ring_frag(slot, NWF + NKF + 2 * db + j, l, (E*)nullptr);
+            o.kh[db][j] = ring_frag(slot, NWF + 2 * (C * NDC + db) + j, l, (E*)nullptr);
+            if constexpr (KP == 2) o.kl[db][j] = ring_frag(slot, NWF + NKF + 2 * (C * NDC + db) + j, l, (E*)nullptr);
         }
 }
 
-// Work-group: wave 0 runs the recurrence, the other waves stream the operands
-// of the next blocks into the LDS ring (clr_ring.h).  All operands are tiled, so
-// ring unit u of a block is the contiguous 1-KB run u of
+// Work-group: the consumer waves (NCW) run the recurrence, the
+// other waves stream the operands of the next blocks into the LDS ring
+// (clr_ring.h).  All operands are tiled, so ring unit u of a block is the
+// contiguous 1-KB run u of
 // [W | K^T (Kh^T) | Ut^T fragments (vb, 0..1)]  (Ut fp32 for the Gated
 // DeltaNet scans: two units per fragment); the small unit holds gamma.
 // With PCD (per-channel decay, KDA) one more unit holds exp(b_C) for every key
 // channel, as fp32 (256 floats, padded), and the state-store tile also
 // stages U for its token-major store.
-// Scan work-groups: one consumer wave and NP producer waves.  The Gated
-// DeltaNet forward scan's consumer is light enough for the operand stream to
-// bound it, and seven producers stream faster than three (27 -> 20.5 us per
-// 2048-token chunk at H = 16); the scans whose consumer does more per block
-// (KDA's token-major U, the reverse scan) measured no gain or a loss.
-constexpr int SCAN_NP_FAST = 7;
-template <int NP> constexpr int scan_threads = 64 * (NP + 1);
+// Producer waves: the Gated DeltaNet scans stream faster with more of them
+// (three -> seven with one consumer: 27 -> 20.5 us per 2048-token chunk at
+// H = 16), so their work-groups fill eight waves; KDA's scans, whose
+// consumer does more per block (the token-major U), keep three.
+template <int NCW> constexpr int scan_np_fast = 8 - NCW;
+template <int NP, int NCW> constexpr int scan_threads = 64 * (NP + NCW);
 
-template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFwdGeom {
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NCW_ = 1> struct ScanFwdGeom {
     static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 1-KB units per fragment
     static constexpr int UPFU = sizeof(ScanWsT<PCD, E>) == 2 ? 1 : 2;  // ... of Ut
     static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF * key_parts<PCD, E>();
@@ -701,95 +745,115 @@ template <typename E, int DK, int DV, bool HNAT, bool PCD = false> struct ScanFw
     static constexpr int SLOT = RingGeom<NU>::SLOT;
     static constexpr int TILE_H = HNAT ? state_tile_bytes(DK, sizeof(E)) : 16, TILE_U = PCD ? BLK * 16 * (int)sizeof(E) : 16;
     static constexpr int TILE = TILE_H > TILE_U ? TILE_H : TILE_U;
-    static constexpr int PF = (160 * 1024 - 512 - TILE) / SLOT;  // ring + tile within the CU's LDS
+    static constexpr int NCW = NCW_;
+    static_assert(NCW == 1 || (NCW == 2 && scan_can_split<E, DK>()), "consumer split");
+    static constexpr int XCH = NCW == 2 ? 2 * 4 * 64 * 16 : 0;  // the consumers' exchange
+    static constexpr int PF = (160 * 1024 - 512 - TILE - XCH) / SLOT;  // ring, tile, exchange within the CU's LDS
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
-    static constexpr int LDS = P * SLOT + TILE;  // ring, then the state-store tile
+    static constexpr int LDS = P * SLOT + TILE + XCH;  // ring, then the state-store tile, then the exchange
 };
+
+// Consumer C of the forward scan body.
+template <typename E, int DK, int DV, bool HNAT, bool PCD, int NP, int NCW, int C>
+__device__ __forceinline__ void gdn_scan_fwd_consume(const GdnScanArgs<E>& a, const char* ring, E* tile, f32x4* xch,
+                                                     size_t bh, int vb, int l) {
+    using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD, NCW>;
+    using UT_ = ScanWsT<PCD, E>;
+    constexpr int NDC = DK / 16 / NCW, NU = SG::NU, P = SG::P;
+    using G = RingGeom<NU, NP>;
+    const int n0 = a.n0, NB = (a.n1 < a.NC ? a.n1 : a.NC) - a.n0;
+    const int r = l & 15, g = l >> 4, v0 = 16 * vb;
+    f32x4 S[NDC];
+    const float* Sin = a.S_in ? a.S_in + bh * DK * DV : nullptr;
+#pragma unroll
+    for (int db = 0; db < NDC; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[db][i] = Sin ? Sin[(size_t)(16 * (C * NDC + db) + 4 * g + i) * DV + v0 + r] : 0.f;
+    ring_barrier();
+    for (int n = 0; n < NB; ++n) {
+        ScanFwdOps<E, DK, UT_, NCW> o;
+        const char* slot = ring + (n % P) * G::SLOT;
+        scan_fwd_from_ring<E, DK, NU, UT_, key_parts<PCD, E>(), C, NCW>(o, slot, l);
+        scan_fwd_step<E, DK, DV, HNAT, NU, PCD, C, NCW>(o, S, a, bh * a.NC + n0 + n, vb, l, tile, slot, xch);
+        ring_barrier();
+    }
+    if (a.S_out) {
+        float* So = a.S_out + bh * DK * DV;
+#pragma unroll
+        for (int db = 0; db < NDC; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) So[(size_t)(16 * (C * NDC + db) + 4 * g + i) * DV + v0 + r] = S[db][i];
+    }
+}
 
 // Scan body for work-group `wgi` of the scan grid; `smem` holds
 // ScanFwdGeom::LDS bytes (16-byte aligned).
-template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NP = NPROD>
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NP = NPROD, int NCW = 1>
 __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int wgi, char* smem) {
     const int H = a.H, NC = a.NC;
     // blocks n0 .. n0 + NB - 1 of each head are scanned (ring index j = n - n0)
     const int n0 = a.n0, NB = (a.n1 < NC ? a.n1 : NC) - a.n0;
     int b, h, vb;
     if (!scan_coords(wgi, DV / 16, a.BH, H, b, h, vb)) return;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
-    const int v0 = 16 * vb;
-    using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD>;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD, NCW>;
     using UT_ = ScanWsT<PCD, E>;
-    constexpr int ND = SG::ND, UPFU = SG::UPFU, NWU = SG::NWU, NKU = SG::NKU, NU = SG::NU, P = SG::P;
+    constexpr int UPFU = SG::UPFU, NWU = SG::NWU, NKU = SG::NKU, NU = SG::NU, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
     using G = RingGeom<NU, NP>;
     char* ring = smem;
     E* tile = (E*)(smem + P * G::SLOT);
+    f32x4* xch = (f32x4*)(smem + P * G::SLOT + SG::TILE);
     const size_t bh = (size_t)b * H + h;
 
-    if (w > 0) {  // producers
-        const int pid = w - 1;
+    // lane 0's address of unit u of workspace block c (lane l reads 16 l bytes further)
+    auto unit_ptr = [&](size_t c, int u) -> const char* {
+        if (u < NWU) return (const char*)(a.W + c * BLK * DK + u * UE);
+        if (u < NWU + NKU) {
+            const int k = u - NWU;  // KDA: the lo half follows the hi half
+            if (PCD && k >= NKU / 2 && key_parts<PCD, E>() == 2)
+                return (const char*)(a.KhT_lo + c * BLK * DK + (k - NKU / 2) * UE);
+            return (const char*)(a.KhT + c * BLK * DK + k * UE);
+        }
+        if (PCD && u == NU - 1) return (const char*)(a.eC + c * 256);
+        return (const char*)((const UT_*)a.UtT + c * BLK * DV + (size_t)(2 * vb * UPFU) * UNIT_ELEMS<UT_> +
+                             (size_t)(u - NWU - NKU) * UNIT_ELEMS<UT_>);
+    };
+    // lane 0's address of the small unit (4 bytes per lane)
+    auto small_ptr = [&](size_t c) -> const char* {
+        return PCD ? (const char*)(a.eC + c * 256) : (const char*)(a.eg + c * BLK);
+    };
+    const int pre = NB < P - 1 ? NB : P - 1;
+    if (w >= NCW) {  // producers
+        const int pid = w - NCW;
         auto issue = [&](int n) {
             const size_t c = bh * NC + n0 + n;
-            const E* W = a.W + c * BLK * DK + l * LE;
-            const E* KhT = a.KhT + c * BLK * DK + l * LE;
-            const E* KhTl = PCD ? a.KhT_lo + c * BLK * DK + l * LE : nullptr;
-            const UT_* UtT = (const UT_*)a.UtT + c * BLK * DV + (size_t)(2 * vb * UPFU) * UNIT_ELEMS<UT_> +
-                             l * LANE_ELEMS<UT_>;
-            auto src = [&](int u) -> const void* {
-                if (u < NWU) return W + u * UE;
-                if (u < NWU + NKU) {
-                    const int k = u - NWU;  // KDA: the lo half follows the hi half
-                    if (PCD && k >= NKU / 2 && key_parts<PCD, E>() == 2) return KhTl + (k - NKU / 2) * UE;
-                    return KhT + k * UE;
-                }
-                if (PCD && u == NU - 1) return a.eC + c * 256 + l * 4;
-                return UtT + (u - NWU - NKU) * UNIT_ELEMS<UT_>;
-            };
-            ring_issue<NU, decltype(src), NP>(ring + (n % P) * G::SLOT, pid, src,
-                                                     PCD ? (const void*)(a.eC + c * 256 + l) : (const void*)(a.eg + c * BLK + l));
+            auto src = [&](int u) -> const void* { return unit_ptr(c, u) + 16 * l; };
+            ring_issue<NU, decltype(src), NP>(ring + (n % P) * G::SLOT, pid, src, small_ptr(c) + 4 * l);
         };
-        const int pre = NB < P - 1 ? NB : P - 1;
         for (int n = 0; n < pre; ++n) issue(n);
         ring_wait<G::NU_MIN>(pre - 1);  // block 0 has landed
         ring_barrier();
         for (int n = 0; n < NB; ++n) {
             if (n + P - 1 < NB) issue(n + P - 1);
+            if constexpr (NCW == 2) ring_barrier();  // the consumers' exchange within block n
             const int last = (n + P - 1 < NB ? n + P - 1 : NB - 1);
             ring_wait<G::NU_MIN>(last - (n + 1));  // block n + 1 has landed
             ring_barrier();
         }
         return;
     }
-
-    f32x4 S[ND];
-    const float* Sin = a.S_in ? a.S_in + bh * DK * DV : nullptr;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[db][i] = Sin ? Sin[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] : 0.f;
-    ring_barrier();
-    for (int n = 0; n < NB; ++n) {
-        ScanFwdOps<E, DK, UT_> o;
-        const char* slot = ring + (n % P) * G::SLOT;
-        scan_fwd_from_ring<E, DK, NU, UT_, key_parts<PCD, E>()>(o, slot, l);
-        scan_fwd_step<E, DK, DV, HNAT, NU, PCD>(o, S, a, bh * NC + n0 + n, vb, l, tile, slot);
-        ring_barrier();
-    }
-    if (a.S_out) {
-        float* So = a.S_out + bh * DK * DV;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) So[(size_t)(16 * db + 4 * g + i) * DV + v0 + r] = S[db][i];
-    }
+    if (w == 0) gdn_scan_fwd_consume<E, DK, DV, HNAT, PCD, NP, NCW, 0>(a, ring, tile, xch, bh, vb, l);
+    if constexpr (NCW == 2)
+        if (w == 1) gdn_scan_fwd_consume<E, DK, DV, HNAT, PCD, NP, NCW, 1>(a, ring, tile, xch, bh, vb, l);
 }
 
 template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NP = NPROD>
-__global__ __launch_bounds__(scan_threads<NP>) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
+__global__ __launch_bounds__((scan_threads<NP, 1>)) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
     __shared__ __align__(16) char smem[ScanFwdGeom<E, DK, DV, HNAT, PCD>::LDS];
     gdn_scan_fwd_body<E, DK, DV, HNAT, PCD, NP>(a, blockIdx.x, smem);
 }
-
 // ---------------------------------------------------------------------------
 // out: one work-group (4 waves) per (block, head, batch); wave w owns tokens
 // 16w..16w+15 of the block.  Computes O^T tiles so that each lane writes four
