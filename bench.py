@@ -423,6 +423,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-chunks", type=int, default=64, help="sequence chunks in the CPU-baseline sample")
     ap.add_argument("--profile-summary", metavar="DIR", help="summarise rocprofv3 output under DIR into profiles/")
+    ap.add_argument("--scan-bv", type=int, choices=(16, 32), default=None,
+                    help="value columns per work-group of the Gated DeltaNet forward scan (default: the library's, 16)")
+    ap.add_argument("--fwd-split", type=int, default=None, metavar="PERMILLE",
+                    help="split-and-overlap forward at PERMILLE/1000 of the blocks (0 = off, the default)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -450,6 +454,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ops.load()  # fail loudly if the HIP library is missing
+    if args.scan_bv is not None:
+        ops.set_scan_bv(args.scan_bv)
+    if args.fwd_split is not None:
+        ops.set_fwd_split(args.fwd_split)
 
     cfg = inputs.CONFIGS[args.workload]
     B, T, N = cfg["B"], cfg["T"], cfg["N"]
@@ -620,7 +628,8 @@ def main():
                        "act": "silu" if cfg["act"] else "identity", "seq_chunks": N}
                       if conv else
                       {"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "H": cfg["H"], "dk": cfg["dk"],
-                       "dv": cfg["dv"], "seq_chunks": N, "block": 64}),
+                       "dv": cfg["dv"], "seq_chunks": N, "block": 64,
+                       "scan_bv": ops.get_scan_bv(), "fwd_split_permille": ops.get_fwd_split()}),
            "mfma_util": mfma_util,
            "peak_mem_gb": round(torch.cuda.max_memory_allocated() / 1e9, 3),
            "roofline": roofline, "phases": phases, "kernels": kernels}

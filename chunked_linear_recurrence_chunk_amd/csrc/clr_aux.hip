@@ -25,6 +25,8 @@ std::mutex g_aux_mu;
 AuxDev g_aux[MAX_DEV];
 // Share of the blocks (per mille) that go into the first part; 0 = no split.
 std::atomic<int> g_split{FWD_SPLIT_DEFAULT};
+// Value columns per forward-scan work-group (16 or 32).
+std::atomic<int> g_scan_bv{16};
 
 void aux_release(AuxDev& a) {
     for (auto& e : a.ev)
@@ -34,6 +36,7 @@ void aux_release(AuxDev& a) {
 }  // namespace
 
 int fwd_split_permille() { return g_split.load(std::memory_order_relaxed); }
+int scan_bv() { return g_scan_bv.load(std::memory_order_relaxed); }
 
 AuxGuard::AuxGuard(hipStream_t main) : lk_(g_aux_mu) {
     int dev = -1;
@@ -64,3 +67,11 @@ extern "C" int clr_set_fwd_split(int permille) {
 }
 
 extern "C" int clr_get_fwd_split(void) { return clr::fwd_split_permille(); }
+
+extern "C" int clr_set_scan_bv(int bv) {
+    if (bv != 16 && bv != 32) return CLR_EINVAL;
+    clr::g_scan_bv.store(bv, std::memory_order_relaxed);
+    return CLR_OK;
+}
+
+extern "C" int clr_get_scan_bv(void) { return clr::scan_bv(); }

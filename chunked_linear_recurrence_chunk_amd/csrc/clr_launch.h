@@ -19,6 +19,9 @@ namespace clr {
 // MI355X (measured), more than the overlap can hide.
 constexpr int FWD_SPLIT_DEFAULT = 0;
 int fwd_split_permille();
+// Value columns per work-group of the Gated DeltaNet forward scan (16 or 32);
+// set through clr_set_scan_bv.
+int scan_bv();
 
 // The auxiliary stream of the current device and its events, held under a
 // process-wide lock for the lifetime of the guard.  `stream` stays null when

@@ -22,9 +22,16 @@ struct GdnFwdStages {
                           (E*)L.ws.hT, (E*)L.ws.UT, L.H, L.NC, L.B * L.H};
         sa.n0 = n0;
         sa.n1 = n1;
-        constexpr int NP = scan_np_fast<1>;
-        launch("gdn_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, false, NP>,
-               dim3(scan_grid(DV / 16, L.B * L.H)), dim3(scan_threads<NP, 1>), st, sa);
+        if (scan_bv() == 32 && DV % 32 == 0) {
+            // two value slices per work-group, sharing their W and K^T stream
+            constexpr int NP = scan_np_fast<2>;
+            launch("gdn_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, false, NP, 2>,
+                   dim3(scan_grid(DV / 32, L.B * L.H)), dim3(scan_threads<NP, 2>), st, sa);
+        } else {
+            constexpr int NP = scan_np_fast<1>;
+            launch("gdn_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, false, NP>,
+                   dim3(scan_grid(DV / 16, L.B * L.H)), dim3(scan_threads<NP, 1>), st, sa);
+        }
     }
     void out(int n0, int n1, hipStream_t st) const {
         GdnOutArgs<E> oa{(const E*)L.q, (const E*)L.k, L.ws.gam, (const E*)L.ws.hT, (const float*)L.ws.UT, (E*)L.o,

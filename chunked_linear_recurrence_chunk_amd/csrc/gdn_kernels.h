@@ -693,7 +693,7 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>,
 
 // Operands of one block from a ring slot (see clr_ring.h for the layout).
 template <typename E, int DK, int NU, typename UE, int KP = 1, int C = 0, int NCW = 1>
-__device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK, UE, NCW>& o, const char* slot, int l) {
+__device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK, UE, NCW>& o, const char* slot, int l, int s = 0) {
     constexpr int KK = DK / 32, KKC = KK / NCW, NWF = 4 * KK, NKF = 2 * (DK / 16) * KP;
     // units per fragment of W / K and of Ut; Ut starts after the W and K units
     constexpr int UPF = sizeof(E) == 2 ? 1 : 2, UPFU = sizeof(UE) == 2 ? 1 : 2;
@@ -704,7 +704,7 @@ __device__ __forceinline__ void scan_fwd_from_ring(ScanFwdOps<E, DK, UE, NCW>& o
         for (int kk = 0; kk < KKC; ++kk) o.w[tb][kk] = ring_frag(slot, tb * KK + C * KKC + kk, l, (E*)nullptr);
     if constexpr (C == 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, (NWF + NKF) * UPF / UPFU + j, l, (UE*)nullptr);
+        for (int j = 0; j < 2; ++j) o.ut[j] = ring_frag(slot, (NWF + NKF) * UPF / UPFU + 2 * s + j, l, (UE*)nullptr);
     }
     o.GC = ring_small<NU>(slot, BLK - 1);
 }
@@ -737,11 +737,14 @@ __device__ __forceinline__ void scan_fwd_from_ring_kh(ScanFwdOps<E, DK, UE, NCW>
 template <int NCW> constexpr int scan_np_fast = 8 - NCW;
 template <int NP, int NCW> constexpr int scan_threads = 64 * (NP + NCW);
 
-template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NCW_ = 1> struct ScanFwdGeom {
+// NVS value slices per work-group (B_V = 16 NVS): the slices share the W and
+// K^T units of a slot and each has its own Ut units and consumer wave.
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NCW_ = 1, int NVS = 1> struct ScanFwdGeom {
+    static_assert(NVS == 1 || (NCW_ == 1 && !HNAT && !PCD && DV % (16 * NVS) == 0), "value-slice groups");
     static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;  // 1-KB units per fragment
     static constexpr int UPFU = sizeof(ScanWsT<PCD, E>) == 2 ? 1 : 2;  // ... of Ut
     static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF * key_parts<PCD, E>();
-    static constexpr int NU = NWU + NKU + 2 * UPFU + (PCD ? 1 : 0);
+    static constexpr int NU = NWU + NKU + 2 * UPFU * NVS + (PCD ? 1 : 0);
     static constexpr int SLOT = RingGeom<NU>::SLOT;
     static constexpr int TILE_H = HNAT ? state_tile_bytes(DK, sizeof(E)) : 16, TILE_U = PCD ? BLK * 16 * (int)sizeof(E) : 16;
     static constexpr int TILE = TILE_H > TILE_U ? TILE_H : TILE_U;
@@ -754,10 +757,10 @@ template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NCW_ = 1>
 };
 
 // Consumer C of the forward scan body.
-template <typename E, int DK, int DV, bool HNAT, bool PCD, int NP, int NCW, int C>
+template <typename E, int DK, int DV, bool HNAT, bool PCD, int NP, int NCW, int C, int NVS = 1>
 __device__ __forceinline__ void gdn_scan_fwd_consume(const GdnScanArgs<E>& a, const char* ring, E* tile, f32x4* xch,
-                                                     size_t bh, int vb, int l) {
-    using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD, NCW>;
+                                                     size_t bh, int vb, int l, int s = 0) {
+    using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD, NCW, NVS>;
     using UT_ = ScanWsT<PCD, E>;
     constexpr int NDC = DK / 16 / NCW, NU = SG::NU, P = SG::P;
     using G = RingGeom<NU, NP>;
@@ -774,7 +777,7 @@ __device__ __forceinline__ void gdn_scan_fwd_consume(const GdnScanArgs<E>& a, co
     for (int n = 0; n < NB; ++n) {
         ScanFwdOps<E, DK, UT_, NCW> o;
         const char* slot = ring + (n % P) * G::SLOT;
-        scan_fwd_from_ring<E, DK, NU, UT_, key_parts<PCD, E>(), C, NCW>(o, slot, l);
+        scan_fwd_from_ring<E, DK, NU, UT_, key_parts<PCD, E>(), C, NCW>(o, slot, l, s);
         scan_fwd_step<E, DK, DV, HNAT, NU, PCD, C, NCW>(o, S, a, bh * a.NC + n0 + n, vb, l, tile, slot, xch);
         ring_barrier();
     }
@@ -789,15 +792,16 @@ __device__ __forceinline__ void gdn_scan_fwd_consume(const GdnScanArgs<E>& a, co
 
 // Scan body for work-group `wgi` of the scan grid; `smem` holds
 // ScanFwdGeom::LDS bytes (16-byte aligned).
-template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NP = NPROD, int NCW = 1>
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NP = NPROD, int NCW = 1, int NVS = 1>
 __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int wgi, char* smem) {
     const int H = a.H, NC = a.NC;
     // blocks n0 .. n0 + NB - 1 of each head are scanned (ring index j = n - n0)
     const int n0 = a.n0, NB = (a.n1 < NC ? a.n1 : NC) - a.n0;
-    int b, h, vb;
-    if (!scan_coords(wgi, DV / 16, a.BH, H, b, h, vb)) return;
+    int b, h, vg;  // value-slice group vg: slices NVS vg .. NVS vg + NVS - 1
+    if (!scan_coords(wgi, DV / 16 / NVS, a.BH, H, b, h, vg)) return;
+    const int vb = NVS * vg;  // the group's first slice
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD, NCW>;
+    using SG = ScanFwdGeom<E, DK, DV, HNAT, PCD, NCW, NVS>;
     using UT_ = ScanWsT<PCD, E>;
     constexpr int UPFU = SG::UPFU, NWU = SG::NWU, NKU = SG::NKU, NU = SG::NU, P = SG::P;
     constexpr int UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
@@ -825,8 +829,8 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
         return PCD ? (const char*)(a.eC + c * 256) : (const char*)(a.eg + c * BLK);
     };
     const int pre = NB < P - 1 ? NB : P - 1;
-    if (w >= NCW) {  // producers
-        const int pid = w - NCW;
+    if (w >= NCW * NVS) {  // producers
+        const int pid = w - NCW * NVS;
         auto issue = [&](int n) {
             const size_t c = bh * NC + n0 + n;
             auto src = [&](int u) -> const void* { return unit_ptr(c, u) + 16 * l; };
@@ -844,15 +848,19 @@ __device__ __forceinline__ void gdn_scan_fwd_body(const GdnScanArgs<E>& a, int w
         }
         return;
     }
-    if (w == 0) gdn_scan_fwd_consume<E, DK, DV, HNAT, PCD, NP, NCW, 0>(a, ring, tile, xch, bh, vb, l);
-    if constexpr (NCW == 2)
-        if (w == 1) gdn_scan_fwd_consume<E, DK, DV, HNAT, PCD, NP, NCW, 1>(a, ring, tile, xch, bh, vb, l);
+    if constexpr (NVS > 1) {  // one consumer per slice of the group
+        gdn_scan_fwd_consume<E, DK, DV, HNAT, PCD, NP, NCW, 0, NVS>(a, ring, tile, xch, bh, vb + w, l, w);
+    } else {
+        if (w == 0) gdn_scan_fwd_consume<E, DK, DV, HNAT, PCD, NP, NCW, 0>(a, ring, tile, xch, bh, vb, l);
+        if constexpr (NCW == 2)
+            if (w == 1) gdn_scan_fwd_consume<E, DK, DV, HNAT, PCD, NP, NCW, 1>(a, ring, tile, xch, bh, vb, l);
+    }
 }
 
-template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NP = NPROD>
-__global__ __launch_bounds__((scan_threads<NP, 1>)) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
-    __shared__ __align__(16) char smem[ScanFwdGeom<E, DK, DV, HNAT, PCD>::LDS];
-    gdn_scan_fwd_body<E, DK, DV, HNAT, PCD, NP>(a, blockIdx.x, smem);
+template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NP = NPROD, int NVS = 1>
+__global__ __launch_bounds__((scan_threads<NP, NVS>)) void gdn_scan_fwd_kernel(GdnScanArgs<E> a) {
+    __shared__ __align__(16) char smem[ScanFwdGeom<E, DK, DV, HNAT, PCD, 1, NVS>::LDS];
+    gdn_scan_fwd_body<E, DK, DV, HNAT, PCD, NP, 1, NVS>(a, blockIdx.x, smem);
 }
 // ---------------------------------------------------------------------------
 // out: one work-group (4 waves) per (block, head, batch); wave w owns tokens

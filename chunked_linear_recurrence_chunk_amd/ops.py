@@ -83,6 +83,10 @@ def load(path: Optional[str] = None):
     lib.clr_set_fwd_split.restype = i
     lib.clr_get_fwd_split.argtypes = []
     lib.clr_get_fwd_split.restype = i
+    lib.clr_set_scan_bv.argtypes = [i]
+    lib.clr_set_scan_bv.restype = i
+    lib.clr_get_scan_bv.argtypes = []
+    lib.clr_get_scan_bv.restype = i
     lib.clr_status_string.argtypes = [i]
     lib.clr_status_string.restype = ctypes.c_char_p
     lib.clr_version.argtypes = []
@@ -200,6 +204,16 @@ def set_fwd_split(permille: int) -> None:
 
 def get_fwd_split() -> int:
     return int(load().clr_get_fwd_split())
+
+
+def set_scan_bv(bv: int) -> None:
+    """Value-tile width of the Gated DeltaNet forward state scan: 16 or 32
+    (clr_set_scan_bv)."""
+    _check("clr_set_scan_bv", load().clr_set_scan_bv(int(bv)))
+
+
+def get_scan_bv() -> int:
+    return int(load().clr_get_scan_bv())
 
 
 def timing_enable(on: bool = True) -> None:

@@ -276,6 +276,18 @@ int shortconv_bwd(const clr_conv_shape_t* shape, const void* x, const float* w, 
 int clr_set_fwd_split(int permille);
 int clr_get_fwd_split(void);
 
+/* Value-tile width B_V of the Gated DeltaNet forward state scan (StateFlow
+ * paper, Sec. 3.4.1: the ST kernel's grid is B x heads x dv / B_V, and B_V is
+ * chosen by profiling).  16 (the default): one work-group per 16 value
+ * columns of a head, one consumer wave.  32: one work-group per 32 columns,
+ * two consumer waves sharing the stream of the block operands W and K^T
+ * (half the work-groups, each slot 40 instead of 36 KB, three slots instead
+ * of four).  The results are bit-identical.  Process-global; returns
+ * CLR_EINVAL for any other value.  clr_get_scan_bv returns the current
+ * value. */
+int clr_set_scan_bv(int bv);
+int clr_get_scan_bv(void);
+
 /* Human-readable text of a status code (static storage). */
 const char* clr_status_string(int status);
 

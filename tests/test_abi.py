@@ -62,6 +62,22 @@ def test_fwd_split_setting():
         ops.set_fwd_split(old)
 
 
+def test_scan_bv_setting():
+    ops, lib = _lib()
+    old = ops.get_scan_bv()
+    assert old in (16, 32)
+    for bad in (0, 8, 24, 64, -16):
+        assert lib.clr_set_scan_bv(bad) == ops.CLR_EINVAL
+    assert ops.get_scan_bv() == old
+    try:
+        ops.set_scan_bv(32)
+        assert ops.get_scan_bv() == 32
+        ops.set_scan_bv(16)
+        assert ops.get_scan_bv() == 16
+    finally:
+        ops.set_scan_bv(old)
+
+
 def test_workspace_sizes():
     ops, lib = _lib()
     s = _shape(ops)

@@ -108,6 +108,42 @@ def test_gdn_fwd_split_is_bit_identical(case):
     assert np.array_equal(o0, o2) and np.array_equal(S0, S2)
 
 
+BV_CASES = [
+    # (B, T, H, dk, dv, dtype, seed)
+    (1, 2048, 16, 128, 128, "bf16", 26),
+    (2, 1500, 3, 64, 64, "bf16", 27),     # ragged last block, H not a multiple of 8
+    (1, 200, 2, 32, 32, "fp32", 28),
+]
+
+
+@pytest.mark.parametrize("case", BV_CASES, ids=[f"B{c[0]}T{c[1]}H{c[2]}d{c[3]}-{c[5]}" for c in BV_CASES])
+def test_gdn_fwd_scan_bv32_is_bit_identical(case):
+    """The forward scan with 32 value columns per work-group (two slices
+    sharing the W / K^T stream) gives the 16-column scan's bits, alone and
+    under the split-and-overlap schedule."""
+    import torch
+    from chunked_linear_recurrence_chunk_amd import inputs
+    ops = _ops()
+    B, T, H, dk, dv, dtype, seed = case
+    print(f"[gdn fwd bv32] case {case}", flush=True)
+    x = inputs.make_gdn(B, T, H, dk, dv, dtype, seed)
+    old_bv, old_split = ops.get_scan_bv(), ops.get_fwd_split()
+    try:
+        ops.set_fwd_split(0)
+        ops.set_scan_bv(16)
+        o0, S0 = _run_fwd(x, dtype)
+        ops.set_scan_bv(32)
+        o1, S1 = _run_fwd(x, dtype)
+        ops.set_fwd_split(500)
+        o2, S2 = _run_fwd(x, dtype)
+    finally:
+        ops.set_scan_bv(old_bv)
+        ops.set_fwd_split(old_split)
+    torch.cuda.synchronize()
+    assert np.array_equal(o0, o1) and np.array_equal(S0, S1)
+    assert np.array_equal(o0, o2) and np.array_equal(S0, S2)
+
+
 def test_gdn_fwd_split_matches_oracle():
     from chunked_linear_recurrence_chunk_amd import inputs
     from oracle import oracle
