@@ -136,10 +136,11 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
 #pragma unroll
         for (int kk = 0; kk < KKC; ++kk) fs[kk] = split_acc<E>(dS[2 * kk], dS[2 * kk + 1]);
         {
+            // by selector products: the KDA slots need all of the LDS
             Frag<E> fh[KKC];
 #pragma unroll
             for (int kk = 0; kk < KKC; ++kk) fh[kk] = fs[kk].hi;
-            state_store<E, DK, DV, true, C, NCW>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
+            state_store<E, DK, DV, false, C, NCW>(a.dh + chunk * DK * DV, fh, tile, 16 * vb, l);
         }
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -215,11 +216,11 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
 template <typename E, int DK, bool PCD = false, int NCW_ = 1> struct ScanBwdGeom {
     static constexpr int NU = ScanBwdRing<E, DK, PCD>::NU;
     static constexpr int SLOT = RingGeom<NU>::SLOT;
-    static constexpr int TILE = state_tile_bytes(DK, sizeof(E));
+    static constexpr int TILE = PCD ? 16 : state_tile_bytes(DK, sizeof(E));  // KDA: no state-store tile
     static constexpr int NCW = NCW_;
     static_assert(NCW == 1 || (NCW == 2 && scan_can_split<E, DK>()), "consumer split");
     static constexpr int XCH = NCW == 2 ? 2 * 4 * 64 * 16 : 0;  // the consumers' exchange
-    static constexpr int PF = (160 * 1024 - 512 - TILE - XCH) / SLOT;  // ring, tile, exchange within the CU's LDS
+    static constexpr int PF = (160 * 1024 - TILE - XCH) / SLOT;  // ring, tile, exchange within the CU's LDS
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
     static constexpr int LDS = P * SLOT + TILE + XCH;
 };

@@ -613,7 +613,9 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>,
     if (a.hT) {
         E* hT = a.hT + chunk * DK * DV;
         if constexpr (HNAT) {
-            state_store<E, DK, DV, true, C, NCW>(hT, fs, tile, 16 * vb, l);  // through LDS in either scan
+            // through LDS (Gated DeltaNet), by selector products (KDA, whose
+            // slots need all of the LDS)
+            state_store<E, DK, DV, !PCD, C, NCW>(hT, fs, tile, 16 * vb, l);
         } else {
 #pragma unroll
             for (int kk = 0; kk < KKC; ++kk) st8T(hT, vb * KK + C * KKC + kk, l, S[2 * kk], S[2 * kk + 1]);
@@ -646,12 +648,14 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>,
             if (NCW == 1 || j == C) st8T(UT, 2 * vb + j, l, U[2 * j], U[2 * j + 1]);
     }
     if (PCD && C == 0 && a.Utok) {
-        // U token-major for the output kernel (rows of valid tokens)
+        // U token-major for the output kernel (rows of valid tokens), staged
+        // in the slot's W units: the W S products above have read them, and
+        // the producers refill this slot only in a later round
         const size_t bh = chunk / a.NC;
         const int n = (int)(chunk % a.NC), bb = (int)(bh / a.H), hh = (int)(bh % a.H);
         const size_t ldv = (size_t)a.H * DV;
         E* dst = a.Utok + ((size_t)bb * a.T + (size_t)n * BLK) * ldv + (size_t)hh * DV;
-        store_rows16<E, BLK>(dst, ldv, U, tile, 16 * vb, l & 15, l >> 4, min(BLK, a.T - n * BLK));
+        store_rows16<E, BLK>(dst, ldv, U, (E*)slot, 16 * vb, l & 15, l >> 4, min(BLK, a.T - n * BLK));
     }
     if constexpr (PCD) {
         // S <- Diag(exp(b_C)) S + Kh^T U (KDA: row d of S scaled by its own
@@ -746,12 +750,14 @@ template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NCW_ = 1,
     static constexpr int ND = DK / 16, KK = DK / 32, NWU = 4 * KK * UPF, NKU = 2 * ND * UPF * key_parts<PCD, E>();
     static constexpr int NU = NWU + NKU + 2 * UPFU * NVS + (PCD ? 1 : 0);
     static constexpr int SLOT = RingGeom<NU>::SLOT;
-    static constexpr int TILE_H = HNAT ? state_tile_bytes(DK, sizeof(E)) : 16, TILE_U = PCD ? BLK * 16 * (int)sizeof(E) : 16;
-    static constexpr int TILE = TILE_H > TILE_U ? TILE_H : TILE_U;
+    // the state-store tile (KDA stores the state without one, and stages its
+    // token-major U in the slot: its slots need all of the LDS)
+    static constexpr int TILE = HNAT && !PCD ? state_tile_bytes(DK, sizeof(E)) : 16;
+    static_assert(BLK * 16 * (int)sizeof(E) <= NWU * RING_UNIT, "U staging fits the W units");
     static constexpr int NCW = NCW_;
     static_assert(NCW == 1 || (NCW == 2 && scan_can_split<E, DK>()), "consumer split");
     static constexpr int XCH = NCW == 2 ? 2 * 4 * 64 * 16 : 0;  // the consumers' exchange
-    static constexpr int PF = (160 * 1024 - 512 - TILE - XCH) / SLOT;  // ring, tile, exchange within the CU's LDS
+    static constexpr int PF = (160 * 1024 - TILE - XCH) / SLOT;  // ring, tile, exchange within the CU's LDS
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
     static constexpr int LDS = P * SLOT + TILE + XCH;  // ring, then the state-store tile, then the exchange
 };
