@@ -301,25 +301,32 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     // backward also row-major in LDS (Ws, where Am was)
     E* Wout = a.W + chunk * BLK * DK;
     E* Ws = (E*)(lds + Lay::o_A);
+    // a wave's tiles below all lie in token block w8 & 3 (tile & 3 and tile % 4
+    // with tile = w8 + 8i), so its split T rows are formed once per loop
+    const int tbw = w8 & 3;
+    const Frag2<E> tw[2] = {tfrag(16 * tbw + r, 0, s_bG), tfrag(16 * tbw + r, 32, s_bG)};
 #pragma unroll
     for (int tile = w8; tile < ND * 4; tile += 8) {
-        const int db = tile >> 2, tb = tile & 3;
+        const int db = tile >> 2, tb = tbw;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), tfrag(16 * tb + r, 32 * j, s_bG));
+        for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), tw[j]);
         st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
         if constexpr (BWD) st4(Ws + (16 * tb + r) * PK + 16 * db + 4 * g, acc);
     }
     // Ut[t][v] = sum_s (T Diag(beta))[t][s] V[s][v]  -> stored negated as fp32 -Ut^T[v][t]
     // (tiled), so that the scan forms -U = W S - Ut by accumulating onto it
     float* Uout = a.UtT + chunk * BLK * DV;
+    {
+        const Frag2<E> tu[2] = {tfrag(16 * tbw + r, 0, s_bet), tfrag(16 * tbw + r, 32, s_bet)};
 #pragma unroll
-    for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
-        const int tb = tile % 4, vb = tile / 4;
-        f32x4 acc = zero4();
+        for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
+            const int tb = tbw, vb = tile / 4;
+            f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma2(acc, tfrag(16 * tb + r, 32 * j, s_bet), ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
-        *(f32x4*)(Uout + toff<float>(16 * vb + r, 16 * tb + 4 * g, BLK)) = -acc;
+            for (int j = 0; j < 2; ++j) mma2(acc, tu[j], ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
+            *(f32x4*)(Uout + toff<float>(16 * vb + r, 16 * tb + 4 * g, BLK)) = -acc;
+        }
     }
     // K^T[d][t] (tiled): its fragment (db, j) is the B fragment of K over tokens
     // 32j.., columns 16db..  (the decay exp(gamma_C - gamma_t) is applied to U

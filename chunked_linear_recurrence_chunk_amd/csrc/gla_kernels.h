@@ -1255,22 +1255,26 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
     };
     // W^T[d][t] = sum_s (K * e^b)^T[d][s] T1[t][s]  -> stored as W[t][d] (tiled)
     E* Wout = a.W + chunk * BLK * DK;
+    // a wave's tiles below all lie in token block w8 & 3, so its split T1 rows
+    // are formed once
+    const int tbw = w8 & 3;
+    const Frag2<E> t1[2] = {tfrag(16 * tbw + r, 0), tfrag(16 * tbw + r, 32)};
 #pragma unroll
     for (int tile = w8; tile < ND * 4; tile += 8) {
-        const int db = tile >> 2, tb = tile & 3;
+        const int db = tile >> 2, tb = tbw;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Kd, PK, 32 * j, 16 * db, l), tfrag(16 * tb + r, 32 * j));
+        for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Kd, PK, 32 * j, 16 * db, l), t1[j]);
         st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
     }
     // Ut = T1 V, stored negated as fp32 -Ut^T (tiled)
     float* Uout = a.UtT + chunk * BLK * DV;
 #pragma unroll
     for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
-        const int tb = tile % 4, vb = tile / 4;
+        const int tb = tbw, vb = tile / 4;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma2(acc, tfrag(16 * tb + r, 32 * j), ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
+        for (int j = 0; j < 2; ++j) mma2(acc, t1[j], ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
         *(f32x4*)(Uout + toff<float>(16 * vb + r, 16 * tb + 4 * g, BLK)) = -acc;
     }
     // Kh^T[d][t] = K[t][d] e^{b_C[d] - b_t[d]} (tiled, hi/lo pair), fragment (db, j)
