@@ -639,6 +639,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         }
     }
     __syncthreads();
+    // row tw of T^T (B operand over the token index): read once for X^T, dV and dK below
+    const Frag<E> ftt[2] = {ldfrag(TT + tw * PT + 4 * g), ldfrag(TT + tw * PT + 32 + 4 * g)};
     // X^T[sb][w] = dT^T T  (rows s, cols r' = tw);  dA[w][cb] = -X T^T (rows r', cols c)
     {
         f32x4 XT[4];
@@ -646,8 +648,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         for (int sb = 0; sb < 4; ++sb) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                mma(acc, ldfrag(dTT + (16 * sb + r) * PT + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
+            for (int j = 0; j < 2; ++j) mma(acc, ldfrag(dTT + (16 * sb + r) * PT + 32 * j + 4 * g), ftt[j]);
             XT[sb] = acc;
         }
         Frag<E> fx[2];
@@ -699,7 +700,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 mma2(acc, ldfrag2(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g, dUTl + (16 * vb + r) * PT + 32 * j + 4 * g),
-                     ldfrag(TT + tw * PT + 32 * j + 4 * g));
+                     ftt[j]);
             const f32x4 vv = ld4(Vs + tw * PV + 16 * vb + 4 * g);
             dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
             if (tw < nvalid) st4(a.dv + (tok0 + tw) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc * bet_tw);
@@ -712,15 +713,16 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     const float Gs = __expf(gam_tw);
     {
         float dbk = 0.f;
+        const Frag<E> fms[2] = {ldfrag(Ms + tw * PT + 4 * g), ldfrag(Ms + tw * PT + 32 + 4 * g)};
 #pragma unroll
         for (int jd = 0; jd < NDH; ++jd) {
             const int db = hf * NDH + jd;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(dWs, PK, 32 * j, 16 * db, l), ldfrag(TT + tw * PT + 32 * j + 4 * g));
+            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(dWs, PK, 32 * j, 16 * db, l), ftt[j]);
             f32x4 accm = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(accm, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), ldfrag(Ms + tw * PT + 32 * j + 4 * g));
+            for (int j = 0; j < 2; ++j) mma(accm, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fms[j]);
             const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
             dbk += kv[0] * acc[0] + kv[1] * acc[1] + kv[2] * acc[2] + kv[3] * acc[3];
             const f32x4 res = dKT[jd] + acc * (bet_tw * Gs) + accm;

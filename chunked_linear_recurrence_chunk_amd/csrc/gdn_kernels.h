@@ -398,13 +398,14 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         }
         __syncthreads();
         // Z = Diag(Gam) Q - P W in place of Q: tiles (tb, db), rows t = 16tb + 4g + i, column d = 16db + r
+        // (a wave's tiles share token block w8 & 3: its P^T operands are read once)
+        const Frag<E> pz[2] = {ldfrag_tr(PsT, PT, 0, 16 * tbw, l), ldfrag_tr(PsT, PT, 32, 16 * tbw, l)};
 #pragma unroll
         for (int tile = w8; tile < 4 * ND; tile += 8) {
-            const int tb = tile & 3, db = tile >> 2;
+            const int tb = tbw, db = tile >> 2;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                mma(acc, ldfrag_tr(PsT, PT, 32 * j, 16 * tb, l), ldfrag_tr(Ws, PQ, 32 * j, 16 * db, l));
+            for (int j = 0; j < 2; ++j) mma(acc, pz[j], ldfrag_tr(Ws, PQ, 32 * j, 16 * db, l));
             const f32x4 Gt = ld4_now(s_Gam + 16 * tb + 4 * g);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -415,12 +416,15 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         __syncthreads();
         // R[d][v] = sum_t Z[t][d] dO[t][v]   (fp32, accumulator-tiled)
         float* Rt = a.Rt + chunk * DK * DV;
+        // (a wave's tiles share d-block w8 % ND, ND dividing 8: its Z^T operands are read once)
+        static_assert(8 % ND == 0, "d-block per wave");
+        const int dbw = w8 % ND;
+        const Frag<E> zq[2] = {ldfrag_tr(Qs, PQ, 0, 16 * dbw, l), ldfrag_tr(Qs, PQ, 32, 16 * dbw, l)};
         for (int tile = w8; tile < ND * NVB; tile += 8) {
-            const int db = tile % ND, vb = tile / ND;
+            const int db = dbw, vb = tile / ND;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                mma(acc, ldfrag_tr(Qs, PQ, 32 * j, 16 * db, l), ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
+            for (int j = 0; j < 2; ++j) mma(acc, zq[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
             *(f32x4*)(Rt + atoff(db, vb, DK, l)) = acc;
         }
     }
