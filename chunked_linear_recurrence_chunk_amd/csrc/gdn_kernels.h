@@ -517,17 +517,17 @@ template <> __device__ __forceinline__ Frag<float> state_sel<float>(int half, in
     }
     return f;
 }
-template <typename E, int DK, int DV>
-__device__ __forceinline__ void store_state_sel(E* h, const Frag<E> (&fs)[DK / 32], int v0, int l) {
+template <typename E, int DK, int DV, int C = 0, int NCW = 1>
+__device__ __forceinline__ void store_state_sel(E* h, const Frag<E> (&fs)[DK / 32 / NCW], int v0, int l) {
     const int r = l & 15, g = l >> 4;
     const Frag<E> sel[2] = {state_sel<E>(0, l), state_sel<E>(1, l)};
 #pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk)
+    for (int kk = 0; kk < DK / 32 / NCW; ++kk)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             f32x4 c = zero4();
             mma(c, fs[kk], sel[half]);
-            E* dst = h + toff<E>(32 * kk + 16 * half + r, v0 + 4 * g, DV);
+            E* dst = h + toff<E>(32 * (C * (DK / 32 / NCW) + kk) + 16 * half + r, v0 + 4 * g, DV);
             if constexpr (sizeof(E) == 2) *(bf16x4*)dst = bf16x4{(bf16)c[0], (bf16)c[1], (bf16)c[2], (bf16)c[3]};
             else *(f32x4*)dst = c;
         }
@@ -579,12 +579,8 @@ __device__ __forceinline__ void store_state_tr(E* h, const Frag<E> (&fs)[DK / 32
 
 template <typename E, int DK, int DV, bool VIA_LDS, int C = 0, int NCW = 1>
 __device__ __forceinline__ void state_store(E* h, const Frag<E> (&fs)[DK / 32 / NCW], E* tile, int v0, int l) {
-    if constexpr (VIA_LDS) {
-        store_state_tr<E, DK, DV, C, NCW>(h, fs, tile, v0, l);
-    } else {
-        static_assert(NCW == 1, "the selector path runs with one consumer");
-        store_state_sel<E, DK, DV>(h, fs, v0, l);
-    }
+    if constexpr (VIA_LDS) store_state_tr<E, DK, DV, C, NCW>(h, fs, tile, v0, l);
+    else store_state_sel<E, DK, DV, C, NCW>(h, fs, v0, l);
 }
 
 // One block of the recurrence.  HNAT selects the layout of the saved states:
