@@ -217,9 +217,9 @@ def launch_name(mangled: str, kind: str) -> str:
     flags = re.findall(r"Lb([01])E", mangled[m.end() + n:])
     if base == "gdn_prep":
         return "gdn_prep_bwd" if flags[0] == "1" else "gdn_prep"
-    if base == "gdn_scan_fwd":  # <E, DK, DV, HNAT, PCD, NP>
+    if base == "gdn_scan_fwd":  # <E, DK, DV, HNAT, PCD, NP, NVS>
         return "kda_scan_fwd" if flags[1] == "1" else "gdn_scan_fwd"
-    if base == "gdn_scan_pair":  # <E, DK, DV, PCD, NP>
+    if base == "gdn_scan_pair":  # <E, DK, DV, PCD, NP, NCW>
         return "kda_scan_pair" if flags[0] == "1" else "gdn_scan_pair"
     if base.startswith("gla_"):
         pre = {"gla": "gla_", "mamba2": "m2_", "kda": "kda_"}.get(kind, "gla_")
