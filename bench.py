@@ -208,9 +208,9 @@ def launch_name(mangled: str, kind: str) -> str:
     (the symbol is a template instantiation; the flags that tell launches of
     one kernel apart are its bool template arguments, in order)."""
     import re
-    m = re.match(r"_ZN3clr(\d+)", mangled)
-    if not m:
-        return mangled
+    m = re.match(r"_ZN3clr(?:12_GLOBAL__N_1)?(\d+)", mangled)  # (kernels of a file-local namespace)
+    if not m:  # an unmangled symbol
+        return mangled[:-len("_kernel")] if mangled.endswith("_kernel") else mangled
     n = int(m.group(1))
     base = mangled[m.end():m.end() + n]
     base = base[:-len("_kernel")] if base.endswith("_kernel") else base
