@@ -173,13 +173,20 @@ def _conv_tile_groups(B: int, T: int, C: int, tt: int = 4, nv: int = 4, tg: int 
 
 
 def source_hash() -> str:
-    """Hash of the HIP sources (ties stored counter data to a kernel build)."""
+    """Hash of the HIP sources' code (ties stored counter data to a kernel
+    build): comments and whitespace are left out, so that editing a comment
+    does not detach the counters of an unchanged kernel."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunked_linear_recurrence_chunk_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
         if fn.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, fn), "rb") as f:
-                h.update(fn.encode() + f.read())
+            with open(os.path.join(csrc, fn), encoding="utf-8") as f:
+                code = f.read()
+            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
+            code = " ".join(code.split())
+            h.update(fn.encode() + code.encode())
     return h.hexdigest()[:16]
 
 

@@ -2,15 +2,17 @@
 //
 // A sequential scan is latency-bound: each 64-token block needs tens of KB of
 // operands, and one wave can only keep ~63 memory operations in flight.  The
-// scan work-groups therefore run one consumer wave (the recurrence, state in
-// registers) and NP producer waves (three, or seven where the consumer is
-// light enough for the stream to bound it) that stream the operands of the
-// next blocks into a ring of P LDS slots with direct global->LDS loads
-// (global_load_lds_dwordx4: each lane's 16 bytes land at slot + unit*1024 +
-// lane*16, exactly where the consumer lane reads its fragment back).
+// scan work-groups therefore run consumer waves (the recurrence, state in
+// registers: one, or two that each hold half of the state's key rows) and NP
+// producer waves (three, or enough to fill eight waves where the stream
+// bounds the scan) that stream the operands of the next blocks into a ring
+// of P LDS slots with direct global->LDS loads (global_load_lds_dwordx4: each
+// lane's 16 bytes land at slot + unit*1024 + lane*16, exactly where the
+// consumer lane reads its fragment back).
 //
 // Round n (all waves, separated by s_barrier):
-//   consumer  computes block n from slot n % P;
+//   consumers compute block n from slot n % P (two consumers meet once more
+//             within the round, at a barrier the producers also pass);
 //   producers issue block n + P - 1 into slot (n - 1) % P (read in round n-1),
 //             then wait until their loads for block n + 1 have landed.
 // The waits are explicit vmcnt immediates; s_barrier is used without a fence
