@@ -69,8 +69,9 @@ template <typename E> struct GdnIntraArgs {
 
 // ---------------------------------------------------------------------------
 // dscan: one work-group per (16-wide value slice, head, batch), blocks in
-// reverse.  Wave 0 runs the reverse recurrence with dS in accumulator tiles;
-// the other waves stream the operands of the next blocks into the LDS ring
+// reverse.  The consumer wave(s) run the reverse recurrence with dS in
+// accumulator tiles (two consumers: half of dS's key rows each, as in the
+// forward scan); the other waves stream the operands of the next blocks into the LDS ring
 // (clr_ring.h).  Ring unit u of a block is the contiguous 1-KB run u of
 // [K (Kh) | W^T | R tiles (., vb) | dvloc^T fragments (vb, 0..1)], all tiled;
 // the small unit holds gamma (exp(b_C) per channel in a last unit for KDA).
