@@ -198,8 +198,6 @@ template <> __device__ __forceinline__ Frag2<float> split8<float>(f32x4 a, f32x4
 // Split B fragment (or transposed A fragment) from two vertically adjacent
 // fp32 accumulator tiles, as frag_from_acc.
 template <typename E> __device__ __forceinline__ Frag2<E> split_acc(f32x4 lo, f32x4 hi) { return split8<E>(lo, hi); }
-// Split fragment from an fp32 fragment (e.g. read from tiled fp32 storage).
-template <typename E> __device__ __forceinline__ Frag2<E> split_frag(const Frag<float>& f) { return split8<E>(f.lo, f.hi); }
 
 __device__ __forceinline__ void mma2(f32x4& acc, const Frag2<bf16>& a, const Frag<bf16>& b) {
     mma(acc, a.hi, b);

@@ -114,7 +114,7 @@ template <typename E> struct GdnOutArgs {
     const E *q, *k;
     const float* gam;
     const E* hT;
-    const float* UT;
+    const E* UT;  // U^T in the element type (the forward scan's store)
     E* o;
     int T, H, NC;
     int n0 = 0;  // first block of the launch

@@ -34,7 +34,7 @@ struct GdnFwdStages {
         }
     }
     void out(int n0, int n1, hipStream_t st) const {
-        GdnOutArgs<E> oa{(const E*)L.q, (const E*)L.k, L.ws.gam, (const E*)L.ws.hT, (const float*)L.ws.UT, (E*)L.o,
+        GdnOutArgs<E> oa{(const E*)L.q, (const E*)L.k, L.ws.gam, (const E*)L.ws.hT, (const E*)L.ws.UT, (E*)L.o,
                          L.T, L.H, L.NC};
         oa.n0 = n0;
         launch("gdn_out", gdn_out_kernel<E, DK, DV>, dim3(n1 - n0, L.H, L.B), dim3(256), st, oa);

@@ -29,7 +29,9 @@
 // T, Ut or U per token grows in the sums over tokens; and a rounded decayed key
 // Diag(e) K would add components outside the span of the keys, which a state
 // that hardly decays keeps.  The scan therefore multiplies the exact keys by
-// the fp32 e * U, and rounds nothing that T multiplies to a single bf16.
+// the fp32 e * U, and rounds nothing that T multiplies to a single bf16.  The
+// one U the forward's output kernel reads (P U, which does not feed the
+// state) is stored in the input type.
 #pragma once
 
 #include <type_traits>
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
 // the blocks.  The fp32 state slice S[0:DK][v0:v0+16] lives in accumulator
 // tiles of the consumer wave.  Writes the state entering each block and U_n^T.
 // ---------------------------------------------------------------------------
-// The scans keep Ut, U, dvloc and dU in fp32 (see "Precision" above).  The
+// The scans keep Ut, U (backward), dvloc and dU in fp32 (see "Precision" above).  The
 // Gated DeltaNet scans multiply the exact keys by e * U; KDA's (per-channel
 // decay, PCD) multiply the decayed keys, streamed as a bf16 hi/lo pair.
 template <bool PCD, typename E> using ScanWsT = float;
@@ -647,9 +649,11 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>,
     if constexpr (NCW == 2) consumers_exchange<C>(U, xch, l);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) U[tb] = -U[tb];
-    // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles (consumer j stores it)
+    // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles (consumer j stores it);
+    // in the element type for the forward's output kernel, fp32 for the backward's block adjoints
     if (a.UT) {
-        UE* UT = (UE*)a.UT + chunk * BLK * DV;
+        using UTE = std::conditional_t<HNAT, UE, E>;
+        UTE* UT = (UTE*)a.UT + chunk * BLK * DV;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             if (NCW == 1 || j == C) st8T(UT, 2 * vb + j, l, U[2 * j], U[2 * j + 1]);
@@ -897,9 +901,9 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
     __shared__ __align__(16) E Qs[BLK * PK], Ks[BLK * PK];
 
     const E* hT = a.hT + chunk * DK * DV;
-    const float* UT = a.UT + chunk * BLK * DV;
+    const E* UT = a.UT + chunk * BLK * DV;
     Frag<E> fh[2][KK];
-    Frag<float> fu[2][2];  // U^T fp32, split when used
+    Frag<E> fu[2][2];
     auto load_slice = [&](int buf, int vb) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) fh[buf][kk] = ldfragT(hT, vb * KK + kk, l);
@@ -939,7 +943,10 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
         }
         P[sb] = acc;
     }
-    // P U: both factors split (U telescopes over repeated keys)
+    // P U: P split, U in the element type (U telescopes over repeated keys;
+    // an fp64 emulation of the block algorithm on the stress input puts o at
+    // 7e-3 with U rounded here against 2e-3 with U kept split: the products
+    // that carry U into the state stay split)
     Frag2<E> fp[2];
     fp[0] = split_acc<E>(P[0], P[1]);
     fp[1] = split_acc<E>(P[2], P[3]);
@@ -952,7 +959,7 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnOutArgs<E> a) {
         acc = acc * Gt;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            if (2 * j <= w) mma2(acc, split_frag<E>(fu[buf][j]), fp[j]);
+            if (2 * j <= w) mma2(acc, fu[buf][j], fp[j]);
         if (t_lane < nvalid) st4(ob + (size_t)t_lane * H * DV + 16 * vb + 4 * g, acc);
     };
 #pragma unroll

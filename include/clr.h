@@ -141,7 +141,7 @@ int gdn_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* 
  * allocates nothing per call.  Calls whose workspace, clr_workspace_bytes(
  * shape, CLR_OP_GDN_FWD), exceeds CLR_NOALLOC_SCRATCH_BYTES return
  * CLR_ESCRATCH before launching anything (at dk = dv = 128, bf16, the limit
- * is about 500 64-token blocks x heads, e.g. 16 heads x 1984 tokens).  All
+ * is about 570 64-token blocks x heads, e.g. 16 heads x 2240 tokens).  All
  * calls on one GPU share its array and each call leaves it dirty: calls on
  * one GPU must be ordered (one stream, or synchronised); calls that overlap
  * on one GPU race.  The split-and-overlap schedule (clr_set_fwd_split) is

@@ -203,13 +203,13 @@ def test_noalloc_forward_rejects_on_the_host():
     """The allocation-free forward validates like gdn_fwd and refuses shapes
     whose workspace exceeds its static scratch, before touching the GPU."""
     ops, lib = _lib()
-    big = _shape(ops, T=2048, H=16)
+    big = _shape(ops, T=2304, H=16)
     assert ops.workspace_bytes(big, ops.OP_GDN_FWD) > ops.NOALLOC_SCRATCH_BYTES
     # distinct, aligned, never dereferenced addresses: validation stops at the size
     fake = [ctypes.c_void_p((i + 1) << 30) for i in range(8)]
     assert lib.gdn_fwd_noalloc(ctypes.byref(big), *fake, None) == ops.CLR_ESCRATCH
     assert lib.gdn_fwd_noalloc(ctypes.byref(big), *([None] * 9)) == ops.CLR_EINVAL  # null tensors first
-    fits = _shape(ops, T=1984, H=16)
+    fits = _shape(ops, T=2240, H=16)
     assert ops.workspace_bytes(fits, ops.OP_GDN_FWD) <= ops.NOALLOC_SCRATCH_BYTES
     assert lib.gdn_fwd_noalloc(ctypes.byref(fits), *([None] * 9)) == ops.CLR_EINVAL
     assert lib.gdn_fwd_noalloc(ctypes.byref(_shape(ops, dk=96, dv=96)), *([None] * 9)) == ops.CLR_ENOTSUP
