@@ -92,16 +92,17 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
         # Gated DeltaNet (dk == dv): Ut, U, dvloc, dU fp32; dh a bf16 pair
         "gdn_prep": (2 * Ck * es + 2 * C * es + 2 * C * f4 + 2 * Ck * es + Cv * f4,
                      2 * CC * dk + 2 * (2 * (2 * CC * dk)) + C ** 3 // 3),
-        # the forward's U (read by the output kernel only) in the element type
+        # U (read by the output kernel and the block adjoints) in the element type
         "gdn_scan_fwd": (C * f4 + 2 * Ck * es + Cv * f4 + kv * es + Cv * es, 3 * (2 * C * kv)),
         "gdn_out": (2 * Ck * es + C * f4 + kv * es + Cv * es + Cv * es,
                     2 * CC * dk + 2 * C * kv + 2 * (2 * CC * dv)),
         "gdn_scan_bwd": (C * f4 + 2 * Ck * es + kv * f4 + Cv * f4 + 2 * kv * es + Cv * f4,
                          3 * (2 * C * kv) + 2 * C * kv // 2),
-        # reads T^T that the backward's prep wrote and forms the decayed Gram tiles again
-        "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 3 * kv * es + 2 * Cv * f4 + 3 * Ck * es + 2 * C * es
-                          + CC * es,
-                          6 * (2 * C * kv) + 16 * (2 * CC * dk) + 2 * (2 * C ** 3) + CC * dk),
+        # reads T^T that the backward's prep wrote and forms the decayed Gram tiles
+        # again; U in the element type, dU fp32 (split when used)
+        "gdn_bwd_intra": (4 * Ck * es + 2 * C * es + C * f4 + 3 * kv * es + Cv * es + Cv * f4 + 3 * Ck * es
+                          + 2 * C * es + CC * es,
+                          5 * (2 * C * kv) + 14 * (2 * CC * dk) + 2 * (2 * C ** 3) + CC * dk),
     }
     # GLA (per-channel gate, gk = dk gate values per token) and its scalar-gate
     # Mamba-2 member on the same kernels (gk = 1)
@@ -117,8 +118,7 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
                                  + Cv * es + Cg * es,
                                  2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv)
         W[pre + "_scan_fwd_rec"] = W[pre + "_scan_fwd"]
-    # the backward's recompute stores U in fp32 (read by the block adjoints)
-    W["gdn_scan_fwd_rec"] = (W["gdn_scan_fwd"][0] + Cv * (f4 - es), W["gdn_scan_fwd"][1])
+    W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
     # the backward's prep also reads Q and dO and writes the reverse scan's
     # operands W^T, Kh, dvloc^T, R (fp32) and T^T for the block adjoints;
     # products P = Q K^T, P^T dO, Z = Gam Q - P W, R = Z^T dO

@@ -60,15 +60,14 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     Carver c{base};
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
     GdnWs w{};
-    // Ut, dvloc and dU are fp32, U fp32 in the backward (split operands;
-    // gdn_kernels.h, "Precision")
+    // Ut, dvloc and dU are fp32 (split operands; gdn_kernels.h, "Precision")
     w.gam = (float*)c.take(nb * BLK * 4);
     w.eg = (float*)c.take(nb * BLK * 4);
     w.W = c.take(nb * BLK * dk * es);
     w.KhT = c.take(nb * BLK * dk * es);
     w.UtT = c.take(nb * BLK * dv * 4);
     w.hT = c.take(nb * dk * dv * es);
-    w.UT = c.take(nb * BLK * dv * (bwd ? 4 : es));  // forward: element type; backward: fp32
+    w.UT = c.take(nb * BLK * dv * es);
     w.Smid = (float*)c.take((size_t)s->B * s->H * dk * dv * 4);
     if (bwd) {
         w.Rt = (float*)c.take(nb * dk * dv * 4);

@@ -28,7 +28,7 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV, false, NP, NCW>, dim3(2 * G),
            dim3(scan_threads<NP, NCW>), st, sa, sb, G);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
-                       ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const float*)ws.UT, (const float*)ws.dUT,
+                       ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const float*)ws.dUT,
                        (const E*)ws.TT,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};
     ia.dh_lo = (const E*)ws.dhT_lo;

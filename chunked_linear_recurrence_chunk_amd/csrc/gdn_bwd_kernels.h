@@ -60,7 +60,8 @@ template <typename E> struct GdnIntraArgs {
     const E *q, *k, *v, *beta, *dO;
     const float* gam;
     const E *h, *dh;
-    const float *UT, *dUT;
+    const E* UT;       // U^T in the element type
+    const float* dUT;
     const E* TT;        // T^T per block (tiled), from the prep
     E *dq, *dk, *dv, *dg, *dbeta;
     int T, H, NC;
@@ -337,9 +338,13 @@ __global__ __launch_bounds__((scan_threads<NP, NCW>)) void gdn_scan_pair_kernel(
 // that contract over the other index read the tiles transposed (ldfrag_tr).
 // The tiled h_n / dh_n fragments are read from global memory one 16-row
 // block ahead of their use.
-// U and dU (fp32 in the workspace) are staged as bf16 hi/lo pairs, dh_n is read
-// as its stored pair, and dPm is split: the products that carry them sum over
-// tokens whose terms telescope with repeated keys (gdn_kernels.h, "Precision").
+// U (stored in the element type by the recompute) is staged as is; dU (fp32 in
+// the workspace) is staged as a bf16 hi/lo pair, dh_n is read as its stored
+// pair, and dPm is split: the products that carry them sum over tokens whose
+// terms telescope with repeated keys (gdn_kernels.h, "Precision").  An fp64
+// emulation of the block algorithm on that stress input puts dq at 7.5e-3 and
+// dg at 1.0e-2 with U in bf16 (1.7e-3 and 9.8e-3 with U split), dv at 8.5e-3
+// and dg at 1.3e-2 were dU in bf16 as well: dU stays a pair.
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV> struct IntraLds {
     static constexpr int PK = RP<E, DK>, PV = RP<E, DV>;
@@ -350,10 +355,10 @@ template <typename E, int DK, int DV> struct IntraLds {
     static constexpr size_t o_E = o_TT + sizeof(E) * BLK * PT;         // f32[64][65]   dP*P + dA*A (gate cross terms), + 512 spare
     static constexpr size_t o_U = o_E + 4 * (BLK * 65 + 512);          // union starts here
     static constexpr size_t p0_end = o_U;
-    // phase A: Qs E[64][PK], dOs E[64][PV], UTs E[DV][PT] (hi, lo)
+    // phase A: Qs E[64][PK], dOs E[64][PV], UTs E[DV][PT]
     static constexpr size_t pA_Q = o_U, pA_dO = pA_Q + sizeof(E) * BLK * PK;
-    static constexpr size_t pA_UT = pA_dO + sizeof(E) * BLK * PV, pA_UTl = pA_UT + sizeof(E) * DV * PT;
-    static constexpr size_t pA_end = pA_UTl + LO * sizeof(E) * DV * PT;
+    static constexpr size_t pA_UT = pA_dO + sizeof(E) * BLK * PV;
+    static constexpr size_t pA_end = pA_UT + sizeof(E) * DV * PT;
     // phase B: dUTs E[DV][PT] (hi, lo), dWs E[64][PK], dTT E[64][PT], Ms E[64][PT], Vs E[64][PV]
     static constexpr size_t pB_dUT = o_U, pB_dUTl = pB_dUT + sizeof(E) * DV * PT;
     static constexpr size_t pB_dW = pB_dUTl + LO * sizeof(E) * DV * PT;
@@ -397,14 +402,14 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     const E* S0 = a.h + chunk * DK * DV;   // h_n  [d][v], tiled
     const E* dS1 = a.dh + chunk * DK * DV; // dh_n [d][v], tiled (bf16: hi part)
     const E* dS1l = a.dh_lo ? a.dh_lo + chunk * DK * DV : nullptr;  // lo part
-    const float* UT = a.UT + chunk * BLK * DV;
+    const E* UT = a.UT + chunk * BLK * DV;
     const float* dUT = a.dUT + chunk * BLK * DV;
 
     // ---------------- phase 0: gates, K, T (from the prep) -------------------
     const auto kx = load_rows<E, BLK, DK, NT>(kb, ldk, nvalid);
     const auto qx = load_rows<E, BLK, DK, NT>(qb, ldk, nvalid);
     const auto ox = load_rows<E, BLK, DV, NT>(dob, ldv, nvalid);
-    const auto ux = load_tiled<float, DV, BLK, NT>(UT);
+    const auto ux = load_tiled<E, DV, BLK, NT>(UT);
     const auto tx = load_tiled<E, BLK, BLK, NT>(a.TT + chunk * BLK * BLK);
     if (tid < BLK) {
         s_gam[tid] = a.gam[chunk * BLK + tid];
@@ -417,24 +422,23 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
     E* Qs = (E*)(lds + Lay::pA_Q);
     E* dOs = (E*)(lds + Lay::pA_dO);
     E* UTs = (E*)(lds + Lay::pA_UT);
-    E* UTl = (E*)(lds + Lay::pA_UTl);
     // phase B operands: in flight during phase A
     const auto vx = load_rows<E, BLK, DV, NT>(vbase, ldv, nvalid);
     const auto dux = load_tiled<float, DV, BLK, NT>(dUT);
     store_rows<E, BLK, DK, PK, NT>(qx, Qs);
     store_rows<E, BLK, DV, PV, NT>(ox, dOs);
-    store_untiled_split<E, DV, BLK, PT, NT>(ux, UTs, UTl);
+    store_untiled<E, DV, BLK, PT, NT>(ux, UTs);
     __syncthreads();
 
     const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
     const float gam_tw = s_gam[tw];
     const float gC = s_gam[BLK - 1];
     Frag<E> fdo[KV];
-    Frag2<E> fU[KV];
+    Frag<E> fU[KV];
 #pragma unroll
     for (int kk = 0; kk < KV; ++kk) {
-        fdo[kk] = ldfrag(dOs + tw * PV + 32 * kk + 4 * g);       // Bt = dO[t][v], rows of block w
-        fU[kk] = ldfrag_tr2(UTs, UTl, PT, 32 * kk, 16 * w, l);  // Bt = U[s][v], rows of block w
+        fdo[kk] = ldfrag(dOs + tw * PV + 32 * kk + 4 * g);  // Bt = dO[t][v], rows of block w
+        fU[kk] = ldfrag_tr(UTs, PT, 32 * kk, 16 * w, l);    // Bt = U[s][v], rows of block w
     }
     // dPm^T[sb][w]: rows s, cols t = tw
     f32x4 dPT[4];
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         f32x4 acc = zero4();
         if (sb <= w) {
 #pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma2(acc, ldfrag_tr2(UTs, UTl, PT, 32 * kk, 16 * sb, l), fdo[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag_tr(UTs, PT, 32 * kk, 16 * sb, l), fdo[kk]);
             const f32x4 gs = ld4_now(s_gam + 16 * sb + 4 * g);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         f32x4 acc = zero4();
         if (tb >= w) {
 #pragma unroll
-            for (int kk = 0; kk < KV; ++kk) mma2(acc, ldfrag(dOs + (16 * tb + r) * PV + 32 * kk + 4 * g), fU[kk]);
+            for (int kk = 0; kk < KV; ++kk) mma(acc, ldfrag(dOs + (16 * tb + r) * PV + 32 * kk + 4 * g), fU[kk]);
             const f32x4 gt = ld4_now(s_gam + 16 * tb + 4 * g);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

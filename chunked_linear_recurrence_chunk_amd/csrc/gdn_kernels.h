@@ -30,8 +30,8 @@
 // Diag(e) K would add components outside the span of the keys, which a state
 // that hardly decays keeps.  The scan therefore multiplies the exact keys by
 // the fp32 e * U, and rounds nothing that T multiplies to a single bf16.  The
-// one U the forward's output kernel reads (P U, which does not feed the
-// state) is stored in the input type.
+// U that the output kernel and the block adjoints read (products that do not
+// feed the state) is stored in the input type.
 #pragma once
 
 #include <type_traits>
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
 // the blocks.  The fp32 state slice S[0:DK][v0:v0+16] lives in accumulator
 // tiles of the consumer wave.  Writes the state entering each block and U_n^T.
 // ---------------------------------------------------------------------------
-// The scans keep Ut, U (backward), dvloc and dU in fp32 (see "Precision" above).  The
+// The scans keep Ut, dvloc and dU in fp32 (see "Precision" above).  The
 // Gated DeltaNet scans multiply the exact keys by e * U; KDA's (per-channel
 // decay, PCD) multiply the decayed keys, streamed as a bf16 hi/lo pair.
 template <bool PCD, typename E> using ScanWsT = float;
@@ -649,11 +649,10 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>,
     if constexpr (NCW == 2) consumers_exchange<C>(U, xch, l);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) U[tb] = -U[tb];
-    // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles (consumer j stores it);
-    // in the element type for the forward's output kernel, fp32 for the backward's block adjoints
+    // U^T tiled (R = DV, C = BLK): fragment (vb, j) is this pair of tiles (consumer j stores it),
+    // in the element type (read by the output kernel and the block adjoints, not by the state)
     if (a.UT) {
-        using UTE = std::conditional_t<HNAT, UE, E>;
-        UTE* UT = (UTE*)a.UT + chunk * BLK * DV;
+        E* UT = (E*)a.UT + chunk * BLK * DV;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             if (NCW == 1 || j == C) st8T(UT, 2 * vb + j, l, U[2 * j], U[2 * j + 1]);
