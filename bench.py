@@ -89,14 +89,15 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
     design has to move, not the algorithmic I/O (layer_io)."""
     Ck, Cv, kv, CC, f4 = C * dk, C * dv, dk * dv, C * C, 4
     W = {
-        # Gated DeltaNet (dk == dv): Ut, U, dvloc, dU fp32; dh a bf16 pair
+        # Gated DeltaNet (dk == dv): Ut and dU fp32; dh a bf16 pair
         "gdn_prep": (2 * Ck * es + 2 * C * es + 2 * C * f4 + 2 * Ck * es + Cv * f4,
                      2 * CC * dk + 2 * (2 * (2 * CC * dk)) + C ** 3 // 3),
         # U (read by the output kernel and the block adjoints) in the element type
         "gdn_scan_fwd": (C * f4 + 2 * Ck * es + Cv * f4 + kv * es + Cv * es, 3 * (2 * C * kv)),
         "gdn_out": (2 * Ck * es + C * f4 + kv * es + Cv * es + Cv * es,
                     2 * CC * dk + 2 * C * kv + 2 * (2 * CC * dv)),
-        "gdn_scan_bwd": (C * f4 + 2 * Ck * es + kv * f4 + Cv * f4 + 2 * kv * es + Cv * f4,
+        # R and dvloc in the element type
+        "gdn_scan_bwd": (C * f4 + 2 * Ck * es + kv * es + Cv * es + 2 * kv * es + Cv * f4,
                          3 * (2 * C * kv) + 2 * C * kv // 2),
         # reads T^T that the backward's prep wrote and forms the decayed Gram tiles
         # again; U in the element type, dU fp32 (split when used)
@@ -120,9 +121,9 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
         W[pre + "_scan_fwd_rec"] = W[pre + "_scan_fwd"]
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
     # the backward's prep also reads Q and dO and writes the reverse scan's
-    # operands W^T, Kh, dvloc^T, R (fp32) and T^T for the block adjoints;
+    # operands W^T, Kh, dvloc^T, R (element type) and T^T for the block adjoints;
     # products P = Q K^T, P^T dO, Z = Gam Q - P W, R = Z^T dO
-    W["gdn_prep_bwd"] = (W["gdn_prep"][0] + 2 * Ck * es + 2 * Ck * es + Cv * f4 + kv * f4 + CC * es,
+    W["gdn_prep_bwd"] = (W["gdn_prep"][0] + 2 * Ck * es + 2 * Ck * es + Cv * es + kv * es + CC * es,
                          W["gdn_prep"][1] + 2 * CC * dk + 2 * CC * dv + 2 * CC * dk + 2 * C * kv)
     # KDA (per-channel gate, dk == dv): the Gated DeltaNet data flow with
     # per-channel decays (exp(b_C) per channel in place of the per-token
@@ -133,7 +134,8 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
     W["kda_prep2"] = (5 * Ck * es + 3 * Ck * es + kv * f4, 2 * CC * dk + 2 * CC * dv + 2 * (2 * C * kv))
     W["kda_scan_fwd"] = (dk * f4 + 3 * Ck * es + kv * es + Cv * es, 2 * (2 * C * kv))
     W["kda_out"] = W["gla_out"]
-    kda_scan_bwd = (dk * f4 + 2 * Ck * es + kv * f4 + Cv * es + kv * es + Cv * es, 2 * (2 * C * kv))
+    # reverse scan: Kh as a hi/lo pair and W^T in, R and dvloc fp32, dh and dU out
+    kda_scan_bwd = (dk * f4 + 3 * Ck * es + kv * f4 + Cv * f4 + kv * es + Cv * es, 2 * (2 * C * kv))
     W["kda_scan_pair"] = tuple(x + y for x, y in zip(W["kda_scan_fwd"], kda_scan_bwd))
     # the backward's prep also writes T^T, M and K e^b for the WY adjoint kernel
     W["kda_prep_bwd"] = (W["kda_prep"][0] + CC * es + CC * f4 + Ck * es, W["kda_prep"][1])

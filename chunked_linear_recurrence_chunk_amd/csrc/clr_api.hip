@@ -60,7 +60,7 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     Carver c{base};
     const size_t nb = nblocks(s), es = esize(s->dtype), dk = s->dk, dv = s->dv;
     GdnWs w{};
-    // Ut, dvloc and dU are fp32 (split operands; gdn_kernels.h, "Precision")
+    // Ut and dU are fp32 (split operands); U, R and dvloc in the element type (gdn_kernels.h, "Precision")
     w.gam = (float*)c.take(nb * BLK * 4);
     w.eg = (float*)c.take(nb * BLK * 4);
     w.W = c.take(nb * BLK * dk * es);
@@ -70,10 +70,10 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     w.UT = c.take(nb * BLK * dv * es);
     w.Smid = (float*)c.take((size_t)s->B * s->H * dk * dv * 4);
     if (bwd) {
-        w.Rt = (float*)c.take(nb * dk * dv * 4);
+        w.Rt = c.take(nb * dk * dv * es);  // R in the element type
         w.WT = c.take(nb * BLK * dk * es);
         w.Kh = c.take(nb * BLK * dk * es);
-        w.dvlT = c.take(nb * BLK * dv * 4);
+        w.dvlT = c.take(nb * BLK * dv * es);  // dvloc in the element type
         w.dhT = c.take(nb * dk * dv * es);
         if (es == 2) w.dhT_lo = c.take(nb * dk * dv * es);  // the lo part of dh (bf16 pair)
         w.dUT = c.take(nb * BLK * dv * 4);
@@ -105,7 +105,7 @@ GdnWs carve_kda(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     w.eCk = (float*)c.take(nb * 256 * 4);
     w.Utok = c.take((size_t)s->B * s->T * s->H * dv * es);
     if (bwd) {
-        w.Rt = (float*)c.take(nb * dk * dv * 4);
+        w.Rt = c.take(nb * dk * dv * 4);
         w.WT = c.take(nb * BLK * dk * es);
         w.Kh = c.take(nb * BLK * dk * es);
         if (es == 2) w.Kh_lo = c.take(nb * BLK * dk * es);

@@ -66,6 +66,17 @@ inline unsigned scan_grid(int NV, int BH) { return (unsigned)(((BH + NXCD - 1) /
 template <typename E> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
 template <> struct Frag<float> { f32x4 lo, hi; };
+// A fragment's eight elements as fp32 (lo: elements 0..3, hi: 4..7).
+__device__ __forceinline__ Frag<float> widen(const Frag<float>& x) { return x; }
+__device__ __forceinline__ Frag<float> widen(const Frag<bf16>& x) {
+    Frag<float> y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        y.lo[i] = (float)x.v[i];
+        y.hi[i] = (float)x.v[4 + i];
+    }
+    return y;
+}
 
 // Four contiguous elements <-> f32x4.
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }

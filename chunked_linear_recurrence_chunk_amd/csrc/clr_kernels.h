@@ -23,7 +23,8 @@ namespace clr {
 
 // Workspace of the Gated DeltaNet path.  Block-major: index
 // ((b * H + h) * NC + n) selects the 64-token block n of head h in batch b.
-// UtT, UT, dvlT and dUT are fp32 (see gdn_kernels.h, "Precision").  Gated
+// UtT and dUT are fp32; UT is in the element type, and so are Rt and dvlT for
+// Gated DeltaNet (fp32 for KDA) (see gdn_kernels.h, "Precision").  Gated
 // DeltaNet: KhT / Kh hold the keys themselves; KDA: the per-channel decayed
 // keys, as a bf16 hi/lo pair for bf16 inputs.
 struct GdnWs {
@@ -41,7 +42,7 @@ struct GdnWs {
     int* range;   // [..]           per block: 1 if the gates leave the diagonal tiles' bound
     void* Utok;   // [B, T, H, dv]  U, token-major
     // backward only
-    float* Rt;    // [.., dv, dk]   R^T, R = (Diag(Gam) Q)^T dO - W^T dvloc  (fp32)
+    void* Rt;     // [.., dv, dk]   R^T, R = (Diag(Gam) Q)^T dO - W^T dvloc  (GDN: element type; KDA: fp32)
     void* WT;     // [.., dk, 64]   W^T
     void* Kh;     // [.., 64, dk]   K (GDN), K * exp(b_C - b) (KDA)   (token-major)
     void* Kh_lo;  // [.., 64, dk]   KDA, bf16 inputs: lo half of Kh
@@ -86,8 +87,8 @@ template <typename E> struct GdnPrepArgs {
     // backward only: the reverse scan's operands (q, dO in; W^T, Kh, dvloc^T, R out)
     const E *q = nullptr, *dO = nullptr;
     E *WT = nullptr, *Kh = nullptr;
-    float* dvlT = nullptr;
-    float* Rt = nullptr;
+    E* dvlT = nullptr;  // in the element type
+    E* Rt = nullptr;  // in the element type (accumulator-tiled, 256 elements per 16 x 16 tile)
 };
 
 // UtT and UT are fp32.  KDA (eC set): KhT is the hi half of the decayed keys

@@ -15,8 +15,8 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     pa.dO = (const E*)L.dO;
     pa.WT = (E*)ws.WT;
     pa.Kh = (E*)ws.Kh;
-    pa.dvlT = (float*)ws.dvlT;
-    pa.Rt = ws.Rt;
+    pa.dvlT = (E*)ws.dvlT;
+    pa.Rt = (E*)ws.Rt;
     launch("gdn_prep_bwd", gdn_prep_kernel<E, DK, DV, true>, gblk, dim3(512), st, pa);
     GdnScanArgs<E> sa{ws.eg, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, (E*)ws.UT, L.H, L.NC, L.B * L.H};

@@ -38,14 +38,14 @@
 
 namespace clr {
 
-// dvlT and dUT are fp32.  The Gated DeltaNet scan stores dh as a bf16 hi/lo
+// dUT is fp32; dvlT and Rt are DvlT / RtT (below).  The Gated DeltaNet scan stores dh as a bf16 hi/lo
 // pair (dh, dh_lo) for bf16 inputs; KDA's reads the decayed keys as a pair
 // (Kh, Kh_lo) and stores dh once.
 template <typename E> struct GdnScanBwdArgs {
     const float* eg;  // GDN: as GdnScanArgs::eg
     const E *Kh, *WT;
-    const void* dvlT;
-    const float* Rt;
+    const void* dvlT;  // DvlT<PCD, E>, tiled as fragments of dvloc^T
+    const void* Rt;  // RtT<PCD, E> (accumulator-tiled, 256 elements per 16 x 16 tile)
     const float* dS_out;
     float* dS_in;
     E* dh;
@@ -87,14 +87,25 @@ template <typename E, int DK, typename UE = E, int NCW = 1> struct ScanBwdOps {
 };
 
 // With PCD (per-channel decay, KDA) a last unit holds exp(b_C) for every key
-// channel (fp32, 256 floats).  dvloc is fp32 (two units per fragment) for the
-// Gated DeltaNet scan.
+// channel (fp32, 256 floats).
+// R's and dvloc's element types: the Gated DeltaNet backward prep stores both
+// in the input type (by an fp64 emulation with these rounding points, the
+// stress input's dS_in moves from 1.9e-3 to 2.4e-3 and dv from 2.5e-3 to
+// 5.7e-3); KDA's stay fp32.  Neither feeds the state's own recurrence: R is
+// added to dS once per block and dvloc to dU.
+template <bool PCD, typename E> using RtT = std::conditional_t<PCD, float, E>;
+template <bool PCD, typename E> using DvlT = std::conditional_t<PCD, float, E>;
+
 template <typename E, int DK, bool PCD = false> struct ScanBwdRing {
     static constexpr int UPF = sizeof(E) == 2 ? 1 : 2;
-    static constexpr int UPFU = sizeof(ScanWsT<PCD, E>) == 2 ? 1 : 2;
+    static constexpr int UPFU = sizeof(ScanWsT<PCD, E>) == 2 ? 1 : 2;   // units per dU fragment
+    static constexpr int UPFD = sizeof(DvlT<PCD, E>) == 2 ? 1 : 2;      // ... per dvloc fragment
     static constexpr int KK = DK / 32, ND = DK / 16;
     static constexpr int KP = key_parts<PCD, E>();  // KDA: Kh as a hi/lo pair
-    static constexpr int NKU = 4 * KK * UPF * KP, NWU = 2 * ND * UPF, NRU = ND, NDU = 2 * UPFU;
+    // R: ND 16 x 16 tiles of 256 elements per slice, ND units in fp32
+    static constexpr int NRU = ND * (int)sizeof(RtT<PCD, E>) / 4;
+    static_assert(ND * (int)sizeof(RtT<PCD, E>) % 4 == 0, "whole R units");
+    static constexpr int NKU = 4 * KK * UPF * KP, NWU = 2 * ND * UPF, NDU = 2 * UPFD;
     static constexpr int NU = NKU + NWU + NRU + NDU + (PCD ? 1 : 0);
 };
 
@@ -102,7 +113,7 @@ template <typename E, int DK, int NU, bool PCD, int C = 0, int NCW = 1>
 __device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK, ScanWsT<PCD, E>, NCW>& o, const char* slot, int l) {
     using Rg = ScanBwdRing<E, DK, PCD>;
     using UE = ScanWsT<PCD, E>;
-    constexpr int KK = DK / 32, KKC = KK / NCW, UPFU = Rg::UPFU;
+    constexpr int KK = DK / 32, KKC = KK / NCW;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -110,12 +121,12 @@ __device__ __forceinline__ void scan_bwd_from_ring(ScanBwdOps<E, DK, ScanWsT<PCD
             o.kh[tb][kk] = ring_frag(slot, tb * KK + C * KKC + kk, l, (E*)nullptr);
             if constexpr (Rg::KP == 2) o.kl[tb][kk] = ring_frag(slot, 4 * KK + tb * KK + C * KKC + kk, l, (E*)nullptr);
         }
-    // dvloc fragments start at unit NKU + NWU + NRU, i.e. fragment index (that) / UPFU;
-    // with two consumers, consumer j stores fragment j of dU
-    static_assert((Rg::NKU + Rg::NWU + Rg::NRU) % UPFU == 0, "fragment alignment");
+    // dvloc fragments start at unit NKU + NWU + NRU; with two consumers,
+    // consumer j stores fragment j of dU
+    const char* dvs = slot + (Rg::NKU + Rg::NWU + Rg::NRU) * RING_UNIT;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-        if (NCW == 1 || j == C) o.dvl[j] = ring_frag(slot, (Rg::NKU + Rg::NWU + Rg::NRU) / UPFU + j, l, (UE*)nullptr);
+        if (NCW == 1 || j == C) o.dvl[j] = widen(ring_frag(dvs, j, l, (DvlT<PCD, E>*)nullptr));
     o.GC = ring_small<NU>(slot, BLK - 1);
 }
 
@@ -193,7 +204,7 @@ __device__ __forceinline__ void scan_bwd_step(const ScanBwdOps<E, DK, ScanWsT<PC
     for (int db = 0; db < NDC; ++db) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) wt[db][j] = ring_frag(slot, Rg::NKU / Rg::UPF + 2 * (C * NDC + db) + j, l, (E*)nullptr);
-        rt[db] = *(const f32x4*)(slot + (Rg::NKU + Rg::NWU + C * NDC + db) * RING_UNIT + l * 16);
+        rt[db] = ld4((const RtT<PCD, E>*)(slot + (Rg::NKU + Rg::NWU) * RING_UNIT) + (C * NDC + db) * 256 + l * 4);
     }
     UE* dUT = (UE*)a.dUT + chunk * BLK * DV;
 #pragma unroll
@@ -285,10 +296,13 @@ __device__ __forceinline__ void gdn_scan_bwd_body(const GdnScanBwdArgs<E>& a, in
         }
         if (u < Rg::NKU + Rg::NWU) return (const char*)(a.WT + c * BLK * DK + (u - Rg::NKU) * UE);
         if (u < Rg::NKU + Rg::NWU + Rg::NRU)
-            return (const char*)(a.Rt + c * DK * DV + (size_t)vb * ND * 256 + (size_t)(u - Rg::NKU - Rg::NWU) * 256);
+            return (const char*)((const RtT<PCD, E>*)a.Rt + c * DK * DV + (size_t)vb * ND * 256 +
+                                 (size_t)(u - Rg::NKU - Rg::NWU) * UNIT_ELEMS<RtT<PCD, E>>);
         if (PCD && u == NU - 1) return (const char*)(a.eC + c * 256);
-        return (const char*)((const UT_*)a.dvlT + c * BLK * DV + (size_t)(2 * vb * UPFU) * UNIT_ELEMS<UT_> +
-                             (size_t)(u - Rg::NKU - Rg::NWU - Rg::NRU) * UNIT_ELEMS<UT_>);
+        // slice vb: fragments 2 vb, 2 vb + 1 of 512 elements each
+        using DT = DvlT<PCD, E>;
+        return (const char*)((const DT*)a.dvlT + c * BLK * DV + (size_t)vb * 1024 +
+                             (size_t)(u - Rg::NKU - Rg::NWU - Rg::NRU) * UNIT_ELEMS<DT>);
     };
     auto small_ptr = [&](size_t c) -> const char* {
         return PCD ? (const char*)(a.eC + c * 256) : (const char*)(a.eg + c * BLK);

@@ -31,7 +31,8 @@
 // that hardly decays keeps.  The scan therefore multiplies the exact keys by
 // the fp32 e * U, and rounds nothing that T multiplies to a single bf16.  The
 // U that the output kernel and the block adjoints read (products that do not
-// feed the state) is stored in the input type.
+// feed the state) is stored in the input type, and so are the backward's
+// dS-independent terms R and dvloc, each added once per block.
 #pragma once
 
 #include <type_traits>
@@ -385,13 +386,13 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         Frag<E> fp[2];
         fp[0] = frag_from_acc<E>(P[0], P[1]);
         fp[1] = frag_from_acc<E>(P[2], P[3]);
-        float* dvlT = a.dvlT + chunk * BLK * DV;  // fp32: the reverse scan adds it to K dS
+        E* dvlT = a.dvlT + chunk * BLK * DV;  // the reverse scan adds it to dU in fp32
 #pragma unroll
         for (int vb = hf; vb < NVB; vb += 2) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int j = 0; j < 2; ++j) mma(acc, fp[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
-            *(f32x4*)(dvlT + toff<float>(16 * vb + r, 16 * w + 4 * g, BLK)) = acc;
+            st4(dvlT + toff<E>(16 * vb + r, 16 * w + 4 * g, BLK), acc);
         }
         __syncthreads();  // K no longer read: P^T may take its place
         if (hf == 0) {
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         }
         __syncthreads();
         // R[d][v] = sum_t Z[t][d] dO[t][v]   (fp32, accumulator-tiled)
-        float* Rt = a.Rt + chunk * DK * DV;
+        E* Rt = a.Rt + chunk * DK * DV;
         // (a wave's tiles share d-block w8 % ND, ND dividing 8: its Z^T operands are read once)
         static_assert(8 % ND == 0, "d-block per wave");
         const int dbw = w8 % ND;
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int j = 0; j < 2; ++j) mma(acc, zq[j], ldfrag_tr(dOs, PO, 32 * j, 16 * vb, l));
-            *(f32x4*)(Rt + atoff(db, vb, DK, l)) = acc;
+            st4(Rt + atoff(db, vb, DK, l), acc);
         }
     }
 }
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
 // the blocks.  The fp32 state slice S[0:DK][v0:v0+16] lives in accumulator
 // tiles of the consumer wave.  Writes the state entering each block and U_n^T.
 // ---------------------------------------------------------------------------
-// The scans keep Ut, dvloc and dU in fp32 (see "Precision" above).  The
+// The scans keep Ut and dU in fp32 (see "Precision" above).  The
 // Gated DeltaNet scans multiply the exact keys by e * U; KDA's (per-channel
 // decay, PCD) multiply the decayed keys, streamed as a bf16 hi/lo pair.
 template <bool PCD, typename E> using ScanWsT = float;

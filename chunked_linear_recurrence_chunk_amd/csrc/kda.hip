@@ -396,7 +396,7 @@ hipError_t launch_kda_bwd_t(const GdnLaunch& L, hipStream_t st) {
     pa.Kd = (E*)ws.Kd;
     launch("kda_prep_bwd", kda_prep_kernel<E, DK, DV>, gblk, dim3(512), st, pa);
     KdaPrep2Args<E> p2{(const E*)L.q, (const E*)L.k, (const E*)L.dO, (const E*)L.g, (const E*)ws.W,
-                       ws.Rt, (E*)ws.WT, (E*)ws.Kh, (float*)ws.dvlT, L.T, L.H, L.NC};
+                       (float*)ws.Rt, (E*)ws.WT, (E*)ws.Kh, (float*)ws.dvlT, L.T, L.H, L.NC};
     p2.Kh_lo = (E*)ws.Kh_lo;
     launch("kda_prep2", kda_prep2_kernel<E, DK, DV>, gblk, dim3(512), st, p2);
     GdnScanArgs<E> sa{nullptr, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
