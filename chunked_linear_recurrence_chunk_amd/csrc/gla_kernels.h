@@ -737,7 +737,7 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, PD = Lay::PD, KV = DV / 32, KK = DK / 32;
     static_assert(Lay::total <= 150 * 1024, "LDS budget");
     __shared__ __align__(16) char lds[Lay::total];
-    __shared__ float rsum[4][DK], rowhd[DK], seg[256];
+    __shared__ float rsum[4][DK], rowhd[DK], seg[256], segt[SG ? 1 : NT];
     __shared__ __align__(16) float zrow[DK];
     E* Ks = (E*)(lds + Lay::o_K);
     E* Qs = (E*)(lds + Lay::o_Q);
@@ -906,7 +906,6 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     __syncthreads();  // dO, V no longer read from LDS: the union becomes dgb
     float* dgb = (float*)(lds + Lay::u_dg);
     constexpr int NDH = DK / 32;  // feature blocks per half
-    float rpart[NDH][4];
     // (4) dQ^T and (5) dK^T, per 16-row block of features d (this half's
     // blocks).  The state fragments of the next block are loaded while the
     // current block's decay terms run.
@@ -1006,7 +1005,16 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             qk[i] = qv[i] * dq[i] - kv[i] * dk[i] + 2.f * kv[i] * ex[i];
-            rpart[jd][i] = kv[i] * __expf(bCv[i] - btv[i]) * ks[i];
+        }
+        // sum_s Kh[s][d] X[d][s] over this wave's 16 tokens (rows d0 + i)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x = kv[i] * __expf(bCv[i] - btv[i]) * ks[i];
+            x += __shfl_xor(x, 1, 64);
+            x += __shfl_xor(x, 2, 64);
+            x += __shfl_xor(x, 4, 64);
+            x += __shfl_xor(x, 8, 64);
+            if (r == 0) rsum[R][d0 + i] = x;
         }
         if (tl < nvalid) {
             st4(a.dq + (tok0 + tl) * ldk + (size_t)h * DK + d0, dq);
@@ -1015,27 +1023,30 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dgb[tl * PD + d0 + i] = qk[i];
     }
-    // sum_s Kh[s][d] X[d][s] over this wave's 16 tokens
-#pragma unroll
-    for (int jd = 0; jd < NDH; ++jd)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int db = hf * NDH + jd;
-            float x = rpart[jd][i];
-            x += __shfl_xor(x, 1, 64);
-            x += __shfl_xor(x, 2, 64);
-            x += __shfl_xor(x, 4, 64);
-            x += __shfl_xor(x, 8, 64);
-            if (r == 0) rsum[R][16 * db + 4 * g + i] = x;
-        }
     __syncthreads();
     if constexpr (!SG) {
-        // (7) dg[t][d] = sum_{tau >= t} dgb[tau][d] + rowsum(S1 * dh)[d]
-        for (int d = tid; d < DK; d += 256) {
+        // (7) dg[t][d] = sum_{tau >= t} dgb[tau][d] + rowsum(S1 * dh)[d]: thread
+        // (sg, d) takes the L-token segment sg of channel d; segment totals
+        // first, then each thread adds the later segments' totals (in order)
+        // and runs its own segment backwards.
+        constexpr int NSEG = NT / DK, L = BLK / NSEG;
+        static_assert(NT % DK == 0 && BLK % NSEG == 0, "token segments");
+        const int d = tid % DK, sg = tid / DK;
+        {
+            float x = 0.f;
+#pragma unroll 4
+            for (int i = L - 1; i >= 0; --i) x += dgb[(sg * L + i) * PD + d];
+            segt[sg * DK + d] = x;
+        }
+        __syncthreads();
+        {
             float acc = __expf(bC[d]) * rowhd[d] + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
-            for (int t = BLK - 1; t >= 0; --t) {
-                acc += dgb[t * PD + d];
-                if (t < nvalid) a.dg[(tok0 + t) * ldk + (size_t)h * DK + d] = from_f<E>(acc);
+            for (int s2 = NSEG - 1; s2 > sg; --s2) acc += segt[s2 * DK + d];
+            E* dgp = a.dg + (tok0 + (size_t)sg * L) * ldk + (size_t)h * DK + d;
+#pragma unroll 4
+            for (int i = L - 1; i >= 0; --i) {
+                acc += dgb[(sg * L + i) * PD + d];
+                if (sg * L + i < nvalid) dgp[(size_t)i * ldk] = from_f<E>(acc);
             }
         }
     } else {
