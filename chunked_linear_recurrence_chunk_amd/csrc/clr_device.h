@@ -542,6 +542,12 @@ __device__ __forceinline__ f32x4 cvt4(Raw4<bf16> x) {
     return f32x4{(float)x.v[0], (float)x.v[1], (float)x.v[2], (float)x.v[3]};
 }
 __device__ __forceinline__ f32x4 cvt4(Raw4<float> x) { return x.v; }
+// Four fp32 values rounded to E (as a product operand would take them).
+template <typename E> __device__ __forceinline__ Raw4<E> to_raw4(f32x4 v);
+template <> __device__ __forceinline__ Raw4<bf16> to_raw4<bf16>(f32x4 v) {
+    return Raw4<bf16>{bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]}};
+}
+template <> __device__ __forceinline__ Raw4<float> to_raw4<float>(f32x4 v) { return Raw4<float>{v}; }
 
 // Inclusive prefix sum over the 64 lanes of a wave (lane order).
 // Four consecutive floats (16-byte aligned, LDS or global) read together and

@@ -498,6 +498,8 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     __shared__ __align__(16) char lds[Lay::total];
     __shared__ __align__(16) float zrow[DK];
     __shared__ float seg[256];
+    // the P^T tiles (sb, R) in accumulator layout, one writer each
+    __shared__ __align__(16) Raw4<E> Px[4][4][64];
     E* Qs = (E*)(lds + Lay::o_Q);
     E* Ks = (E*)(lds + Lay::o_K);
     float* Bs = (float*)(lds + Lay::o_B);
@@ -551,12 +553,15 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
         qo[kk] = frag_row_decay(Qs, PK, tl, 32 * kk, bt, refO, 1.f);
         qd[kk] = frag_row_decay(Qs, PK, tl, 32 * kk, bt, refD, 1.f);
     }
-    // P^T[sb][R]: rows s, column t = tl
-    f32x4 P[4];
+    // P^T[sb][R]: rows s, column t = tl.  Both waves of token tile R need
+    // all of its tiles; wave (R, hf) forms the tiles sb = hf, hf + 2 (when
+    // sb <= R), rounded to E as the product below takes them, and the two
+    // exchange them through LDS.
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-        f32x4 acc = zero4();
+    for (int u = 0; u < 2; ++u) {
+        const int sb = hf + 2 * u;
         if (sb <= R) {
+            f32x4 acc = zero4();
             const int s = 16 * sb + r;
             const float* ref = sb < R ? refO : refD;
 #pragma unroll
@@ -565,9 +570,13 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (16 * sb + 4 * g + i > tl) acc[i] = 0.f;
+            Px[sb][R][l] = to_raw4<E>(acc);
         }
-        P[sb] = acc;
     }
+    __syncthreads();
+    f32x4 P[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) P[sb] = sb <= R ? cvt4(Px[sb][R][l]) : zero4();
     Frag<E> fp[2];
     fp[0] = frag_from_acc<E>(P[0], P[1]);
     fp[1] = frag_from_acc<E>(P[2], P[3]);
@@ -737,7 +746,7 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, PD = Lay::PD, KV = DV / 32, KK = DK / 32;
     static_assert(Lay::total <= 150 * 1024, "LDS budget");
     __shared__ __align__(16) char lds[Lay::total];
-    __shared__ float rsum[4][DK], rowhd[DK], seg[256], segt[SG ? 1 : NT];
+    __shared__ float rsum[4][DK], rowhd[4][DK], seg[256], segt[SG ? 1 : NT];
     __shared__ __align__(16) float zrow[DK];
     E* Ks = (E*)(lds + Lay::o_K);
     E* Qs = (E*)(lds + Lay::o_Q);
@@ -918,15 +927,15 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 #pragma unroll
     for (int jd = 0; jd < NDH; ++jd) {
         const int db = hf * NDH + jd;
-        // dQ inter exp(b_t) (S0 dO^T), the state part of dK, and (wave 0) the
-        // row sums of S0 * dh for rows 16 db + r
+        // dQ inter exp(b_t) (S0 dO^T), the state part of dK, and the row sums
+        // of S0 * dh for rows 16 db + r (wave R sums the value blocks kk = R mod 4)
         f32x4 qi = zero4(), ks = zero4();
         float hd = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KV; ++kk) {
             mma(qi, fh[kk], fdo[kk]);
             mma(ks, fd[kk], fv[kk]);
-            if (R == 0) {
+            if ((kk & 3) == R) {
                 if constexpr (sizeof(E) == 2) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) hd += (float)fh[kk].v[i] * (float)fd[kk].v[i];
@@ -936,11 +945,9 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
                 }
             }
         }
-        if (R == 0) {
-            hd += __shfl_xor(hd, 16, 64);
-            hd += __shfl_xor(hd, 32, 64);
-            if (g == 0) rowhd[16 * db + r] = hd;
-        }
+        hd += __shfl_xor(hd, 16, 64);
+        hd += __shfl_xor(hd, 32, 64);
+        if (g == 0) rowhd[R][16 * db + r] = hd;
         if (jd + 1 < NDH) {
 #pragma unroll
             for (int kk = 0; kk < KV; ++kk) {
@@ -1040,7 +1047,8 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
         }
         __syncthreads();
         {
-            float acc = __expf(bC[d]) * rowhd[d] + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
+            const float hdd = (rowhd[0][d] + rowhd[1][d]) + (rowhd[2][d] + rowhd[3][d]);
+            float acc = __expf(bC[d]) * hdd + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
             for (int s2 = NSEG - 1; s2 > sg; --s2) acc += segt[s2 * DK + d];
             E* dgp = a.dg + (tok0 + (size_t)sg * L) * ldk + (size_t)h * DK + d;
 #pragma unroll 4
@@ -1067,7 +1075,8 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
         if (w8 == 1) {
             float c = 0.f;
             for (int d = l; d < DK; d += 64)
-                c += __expf(bC[d]) * rowhd[d] + rsum[0][d] + rsum[1][d] + rsum[2][d] + rsum[3][d];
+                c += __expf(bC[d]) * ((rowhd[0][d] + rowhd[1][d]) + (rowhd[2][d] + rowhd[3][d])) + rsum[0][d] + rsum[1][d] +
+                     rsum[2][d] + rsum[3][d];
 #pragma unroll
             for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
             if (l == 0) seg[BLK] = c;
