@@ -211,45 +211,36 @@ __device__ __forceinline__ Frag2<E> frag_row_decay2(const E* X, int PX, int row,
 // A fragment of X^T (m = feature m0 + r, k = token s = k0 + kmap(g, i)) from
 // a row-major LDS tile X[s][feature], element scaled by
 // exp(sgn * (b[s][m] - ref[m])) and zero for tokens outside [klo, khi).
-// With BATCH the b values are read four at a time (k is always inside the
-// 64-token tile, so every read is in bounds); the empty asm keeps the compiler
-// from moving each read under its range test, which serialises them, and
-// outside [klo, khi) the exponent is -inf, so the factor is exactly 0.  It
-// needs a few more registers: kernels already at the register limit pass false.
-template <bool BATCH = true, typename E>
+// The b values are read four at a time (k is always inside the 64-token
+// tile, so every read is in bounds); the empty asm keeps the compiler from
+// moving each read under its range test, which serialises them, and outside
+// [klo, khi) the exponent is -inf, so the factor is exactly 0.
+template <typename E>
 __device__ __forceinline__ void col_decay_scales(const float* bs, int PB, int m, int k0, const float* ref, float sgn,
                                                  int klo, int khi, float (&sc)[8]) {
     const int g = (threadIdx.x & 63) >> 4;
     const float rm = ref[m];
-    if constexpr (BATCH) {
 #pragma unroll
-        for (int hbl = 0; hbl < 2; ++hbl) {
-            float bv[4];
+    for (int hbl = 0; hbl < 2; ++hbl) {
+        float bv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = bs[(k0 + 16 * hbl + 4 * g + i) * PB + m];
-            asm volatile("" : "+v"(bv[0]), "+v"(bv[1]), "+v"(bv[2]), "+v"(bv[3]));
+        for (int i = 0; i < 4; ++i) bv[i] = bs[(k0 + 16 * hbl + 4 * g + i) * PB + m];
+        asm volatile("" : "+v"(bv[0]), "+v"(bv[1]), "+v"(bv[2]), "+v"(bv[3]));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int k = k0 + 16 * hbl + 4 * g + i;
-                const float y = sgn * (bv[i] - rm);
-                sc[4 * hbl + i] = expu((k >= klo && k < khi) ? y : -__builtin_inff());
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int k = k0 + (i < 4 ? 4 * g + i : 12 + 4 * g + i);
-            sc[i] = (k >= klo && k < khi) ? expu(sgn * (bs[k * PB + m] - rm)) : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int k = k0 + 16 * hbl + 4 * g + i;
+            const float y = sgn * (bv[i] - rm);
+            sc[4 * hbl + i] = expu((k >= klo && k < khi) ? y : -__builtin_inff());
         }
     }
 }
-template <bool BATCH = true, typename E>
+template <typename E>
 __device__ __forceinline__ Frag<E> frag_col_decay(const E* X, int PX, const float* bs, int PB, int m0, int k0,
                                                   const float* ref, float sgn, int klo, int khi) {
     const int l = threadIdx.x & 63, r = l & 15;
     Frag<E> x = ldfrag_tr(X, PX, k0, m0, l);
     float sc[8];
-    col_decay_scales<BATCH, E>(bs, PB, m0 + r, k0, ref, sgn, klo, khi, sc);
+    col_decay_scales<E>(bs, PB, m0 + r, k0, ref, sgn, klo, khi, sc);
     if constexpr (sizeof(E) == 2) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) x.v[i] = (bf16)((float)x.v[i] * sc[i]);
@@ -263,13 +254,13 @@ __device__ __forceinline__ Frag<E> frag_col_decay(const E* X, int PX, const floa
     return x;
 }
 // The same fragment as a split pair.
-template <bool BATCH = true, typename E>
+template <typename E>
 __device__ __forceinline__ Frag2<E> frag_col_decay2(const E* X, int PX, const float* bs, int PB, int m0, int k0,
                                                     const float* ref, float sgn, int klo, int khi) {
     const int l = threadIdx.x & 63, r = l & 15;
     const Frag<E> x = ldfrag_tr(X, PX, k0, m0, l);
     float sc[8];
-    col_decay_scales<BATCH, E>(bs, PB, m0 + r, k0, ref, sgn, klo, khi, sc);
+    col_decay_scales<E>(bs, PB, m0 + r, k0, ref, sgn, klo, khi, sc);
     f32x4 a, b;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -731,6 +722,8 @@ template <typename E, int DK, int DV> struct GlaIntraLds {
     static constexpr size_t u_dO = o_U, u_V = u_dO + sizeof(E) * BLK * PV;  //   dO, V  E[64][PV]
     static constexpr size_t u_dg = o_U;                                //   dgb f32[64][PD]
     static constexpr size_t end1 = u_V + sizeof(E) * BLK * PV, end2 = u_dg + 4 * BLK * PD;
+    // dgb fits in the dO rows: V stays readable while dgb is written
+    static constexpr bool VKEEP = 4 * BLK * PD <= sizeof(E) * BLK * PV;
     static constexpr size_t total = end1 > end2 ? end1 : end2;
 };
 
@@ -934,7 +927,8 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 #pragma unroll
         for (int kk = 0; kk < KV; ++kk) {
             mma(qi, fh[kk], fdo[kk]);
-            mma(ks, fd[kk], fv[kk]);
+            if constexpr (Lay::VKEEP) mma(ks, fd[kk], ldfrag(Vs + tl * PV + 32 * kk + 4 * g));
+            else mma(ks, fd[kk], fv[kk]);
             if ((kk & 3) == R) {
                 if constexpr (sizeof(E) == 2) {
 #pragma unroll
@@ -961,12 +955,12 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             if (32 * j < 16 * R) {
-                const Frag<E> x = frag_col_decay<(DV <= 128)>(Ks, PK, Bs, PB, 16 * db, 32 * j, refO, -1.f, 0, 16 * R);
+                const Frag<E> x = frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, refO, -1.f, 0, 16 * R);
                 mma(qo, x, fptO[j]);
                 if constexpr (KDA) mma(eo, x, fmtO[j]);
             }
             if (32 * j <= 16 * R && 16 * R < 32 * j + 32) {
-                const Frag<E> x = frag_col_decay<(DV <= 128)>(Ks, PK, Bs, PB, 16 * db, 32 * j, refD, -1.f, 16 * R, 16 * R + 16);
+                const Frag<E> x = frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, refD, -1.f, 16 * R, 16 * R + 16);
                 mma(qd, x, fptD[j]);
                 if constexpr (KDA) mma(ed, x, fmtD[j]);
             }
@@ -977,12 +971,12 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             if (32 * j + 32 > 16 * R + 16) {
-                mma(kl, frag_col_decay<(DV <= 128)>(Qs, PK, Bs, PB, 16 * db, 32 * j, refE, 1.f, 16 * R + 16, BLK), fpL[j]);
-                if constexpr (KDA) mma(fo, frag_col_decay<(DV <= 128)>(Ks, PK, Bs, PB, 16 * db, 32 * j, refE, 1.f, 16 * R + 16, BLK), fmL[j]);
+                mma(kl, frag_col_decay(Qs, PK, Bs, PB, 16 * db, 32 * j, refE, 1.f, 16 * R + 16, BLK), fpL[j]);
+                if constexpr (KDA) mma(fo, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, refE, 1.f, 16 * R + 16, BLK), fmL[j]);
             }
             if (32 * j <= 16 * R && 16 * R < 32 * j + 32) {
-                mma(kd, frag_col_decay<(DV <= 128)>(Qs, PK, Bs, PB, 16 * db, 32 * j, refD, 1.f, 16 * R, 16 * R + 16), fpD[j]);
-                if constexpr (KDA) mma(fd2, frag_col_decay<(DV <= 128)>(Ks, PK, Bs, PB, 16 * db, 32 * j, refD, 1.f, 16 * R, 16 * R + 16), fmD[j]);
+                mma(kd, frag_col_decay(Qs, PK, Bs, PB, 16 * db, 32 * j, refD, 1.f, 16 * R, 16 * R + 16), fpD[j]);
+                if constexpr (KDA) mma(fd2, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, refD, 1.f, 16 * R, 16 * R + 16), fmD[j]);
             }
         }
         // element-wise factors: rows d = 16 db + 4 g + i, column token tl
