@@ -20,6 +20,8 @@
 // slot g of each).  Accumulation is fp32 in both cases.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -566,6 +568,22 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
         float y = __shfl_up(x, off, 64);
         if (l >= off) x += y;
     }
+    return x;
+}
+
+// Sum over the 16 lanes of each row (lanes 16 k .. 16 k + 15); every lane of
+// the row gets it.  DPP lane moves (quad_perm [1,0,3,2], [2,3,0,1], then
+// row_half_mirror and row_mirror) instead of LDS permutes; each step adds a
+// partner that holds an equal partial, the same sums as xor 1, 2, 4, 8.
+__device__ __forceinline__ float row16_sum(float x) {
+    auto step = [](float v, auto ctrl) {
+        const int m = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), decltype(ctrl)::value, 0xF, 0xF, false);
+        return v + __builtin_bit_cast(float, m);
+    };
+    x = step(x, std::integral_constant<int, 0xB1>{});
+    x = step(x, std::integral_constant<int, 0x4E>{});
+    x = step(x, std::integral_constant<int, 0x141>{});
+    x = step(x, std::integral_constant<int, 0x140>{});
     return x;
 }
 

@@ -699,11 +699,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float x = gram[i];
-            x += __shfl_xor(x, 1, 64);
-            x += __shfl_xor(x, 2, 64);
-            x += __shfl_xor(x, 4, 64);
-            x += __shfl_xor(x, 8, 64);
+            const float x = row16_sum(gram[i]);
             if (r == 0) s_g2[hf][16 * w + 4 * g + i] = x;
         }
     }

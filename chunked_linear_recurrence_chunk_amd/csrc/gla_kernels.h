@@ -1010,11 +1010,7 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
         // sum_s Kh[s][d] X[d][s] over this wave's 16 tokens (rows d0 + i)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float x = kv[i] * __expf(bCv[i] - btv[i]) * ks[i];
-            x += __shfl_xor(x, 1, 64);
-            x += __shfl_xor(x, 2, 64);
-            x += __shfl_xor(x, 4, 64);
-            x += __shfl_xor(x, 8, 64);
+            const float x = row16_sum(kv[i] * __expf(bCv[i] - btv[i]) * ks[i]);
             if (r == 0) rsum[R][d0 + i] = x;
         }
         if (tl < nvalid) {
