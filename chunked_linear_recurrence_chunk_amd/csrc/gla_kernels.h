@@ -507,7 +507,9 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     const E* vbase = a.v + tok0 * ldv + (size_t)h * DV;
     const E* hT = a.hT + chunk * DK * DV;
 
-    Frag<E> fh[2][KK];
+    // h^T slices of this half, loaded PD slices ahead of their use
+    constexpr int PD = NVH > 2 ? 2 : 1, NB = PD + 1;
+    Frag<E> fh[NB][KK];
     auto load_slice = [&](int buf, int vb) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) fh[buf][kk] = ldfragT(hT, vb * KK + kk, l);
@@ -516,7 +518,8 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
         const auto qx = load_rows<E, BLK, DK, NT>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
         const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
         const auto gx = load_gate<SG, E, DK, NT>(a.g, tok0, h, H, nvalid);
-        load_slice(0, hf * NVH);
+#pragma unroll
+        for (int j = 0; j < PD; ++j) load_slice(j, hf * NVH + j);
         store_rows<E, BLK, DK, PK, NT>(qx, Qs);
         store_rows<E, BLK, DK, PK, NT>(kx, Ks);
         store_rows<E, BLK, DK, PK, NT>(gx, Vs);
@@ -586,8 +589,8 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     };
 #pragma unroll
     for (int jv = 0; jv < NVH; ++jv) {
-        if (jv + 1 < NVH) load_slice((jv + 1) & 1, hf * NVH + jv + 1);
-        compute_slice(jv & 1, hf * NVH + jv);
+        if (jv + PD < NVH) load_slice((jv + PD) % NB, hf * NVH + jv + PD);
+        compute_slice(jv % NB, hf * NVH + jv);
     }
 }
 
