@@ -222,6 +222,13 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
     const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
     const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
+    // backward: Q and dO in flight through the Gram and inverse phases
+    RowsRegs<E, BLK, DK, NT> qx;
+    RowsRegs<E, BLK, DV, NT> ox;
+    if constexpr (BWD) {
+        qx = load_rows<E, BLK, DK, NT>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
+        ox = load_rows<E, BLK, DV, NT>(a.dO + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
+    }
     if (w8 == 0) {
         // tokens past the end are identity steps: g = 0, beta = 0
         const size_t ig = (tok0 + l) * H + h;
@@ -288,13 +295,6 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     }
     __syncthreads();
 
-    // backward: Q and dO in flight while the outputs below are formed
-    RowsRegs<E, BLK, DK, NT> qx;
-    RowsRegs<E, BLK, DV, NT> ox;
-    if constexpr (BWD) {
-        qx = load_rows<E, BLK, DK, NT>(a.q + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        ox = load_rows<E, BLK, DV, NT>(a.dO + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
-    }
     // Row fragment (m = t, k = s) of T Diag(c): fp32, scaled, split
     auto tfrag = [&](int t, int k0, const float* c) {
         const float* p = Tm + t * AP + k0 + 4 * g;
