@@ -370,8 +370,8 @@ hipError_t launch_kda_fwd_t(const GdnLaunch& L, hipStream_t st) {
     sa.Utok = (E*)ws.Utok;
     sa.T = L.T;
     sa.KhT_lo = (const E*)ws.KhT_lo;
-    launch("kda_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, true>, dim3(scan_grid(DV / 16, L.B * L.H)),
-           dim3(scan_threads<NPROD, 1>), st, sa);
+    launch("kda_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, true, scan_np_fast<1>>,
+           dim3(scan_grid(DV / 16, L.B * L.H)), dim3(scan_threads<scan_np_fast<1>, 1>), st, sa);
     if (L.o) {
         GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)ws.Utok, (const E*)L.g, (const E*)ws.hT,
                          (E*)L.o, L.T, L.H, L.NC};
@@ -406,8 +406,8 @@ hipError_t launch_kda_bwd_t(const GdnLaunch& L, hipStream_t st) {
     sb.eC = ws.eCk;
     sb.Kh_lo = (const E*)ws.Kh_lo;
     const int G = (int)scan_grid(DV / 16, L.B * L.H);
-    launch("kda_scan_pair", gdn_scan_pair_kernel<E, DK, DV, true>, dim3(2 * G), dim3(scan_threads<NPROD, 1>), st,
-           sa, sb, G);
+    launch("kda_scan_pair", gdn_scan_pair_kernel<E, DK, DV, true, scan_np_fast<1>, 1>, dim3(2 * G),
+           dim3(scan_threads<scan_np_fast<1>, 1>), st, sa, sb, G);
     KdaWyArgs<E> wa{(const E*)L.v, (const E*)L.beta, (const E*)ws.hT, (const float*)ws.dUT, (const E*)ws.TT, ws.KKG,
                     (const E*)ws.Kd, (E*)L.dv_, (E*)L.dbeta, ws.dM, ws.dX, L.T, L.H, L.NC};
     launch("kda_bwd_wy", kda_bwd_wy_kernel<E, DK, DV>, gblk, dim3(512), st, wa);
