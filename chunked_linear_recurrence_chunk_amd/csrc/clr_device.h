@@ -561,13 +561,23 @@ __device__ __forceinline__ f32x4 ld4_now(const float* p) {
     return v;
 }
 
+// The value of lane src(l) by a DPP move (CTRL), for the rows in ROW_MASK;
+// 0 where the source lane lies outside the row or the row is masked off.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes: within each 16-lane row by
+// row_shr 1, 2, 4, 8, then the row totals by row_bcast 15 (into rows 1 and 3)
+// and row_bcast 31 (into rows 2 and 3).
 __device__ __forceinline__ float wave_prefix_sum(float x) {
-    const int l = lane_id();
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float y = __shfl_up(x, off, 64);
-        if (l >= off) x += y;
-    }
+    x += dpp_move<0x111>(x);
+    x += dpp_move<0x112>(x);
+    x += dpp_move<0x114>(x);
+    x += dpp_move<0x118>(x);
+    x += dpp_move<0x142, 0xA>(x);
+    x += dpp_move<0x143, 0xC>(x);
     return x;
 }
 
@@ -576,14 +586,10 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // row_half_mirror and row_mirror) instead of LDS permutes; each step adds a
 // partner that holds an equal partial, the same sums as xor 1, 2, 4, 8.
 __device__ __forceinline__ float row16_sum(float x) {
-    auto step = [](float v, auto ctrl) {
-        const int m = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), decltype(ctrl)::value, 0xF, 0xF, false);
-        return v + __builtin_bit_cast(float, m);
-    };
-    x = step(x, std::integral_constant<int, 0xB1>{});
-    x = step(x, std::integral_constant<int, 0x4E>{});
-    x = step(x, std::integral_constant<int, 0x141>{});
-    x = step(x, std::integral_constant<int, 0x140>{});
+    x += dpp_move<0xB1>(x);
+    x += dpp_move<0x4E>(x);
+    x += dpp_move<0x141>(x);
+    x += dpp_move<0x140>(x);
     return x;
 }
 
