@@ -167,11 +167,13 @@ template <typename E, int DK, int DV> struct KdaWyLds {
     // persistent
     static constexpr size_t o_Kd = 0;                               // E[64][PK]    K e^b
     static constexpr size_t o_TT = o_Kd + sizeof(E) * BLK * PK;     // E[64][PT]    TT[s][t] = T[t][s]
-    static constexpr size_t o_V = o_TT + sizeof(E) * BLK * PT;      // E[64][PV]
-    // phase B: dUTs E[DV][PT], dWs E[64][PK], dTT E[64][PT]
+    static constexpr size_t o_V = o_TT + sizeof(E) * BLK * PT;      // E[64][PV]; then dTT E[64][PT]
+    // phase B: dUTs E[DV][PT], dWs E[64][PK]; dT^T takes V's place once the dT
+    // products have read V (the total stays within 80 KB: two work-groups per CU)
     static constexpr size_t pB_dUT = o_V + sizeof(E) * BLK * PV, pB_dW = pB_dUT + sizeof(E) * DV * PT;
-    static constexpr size_t pB_dTT = pB_dW + sizeof(E) * BLK * PK;
-    static constexpr size_t total = pB_dTT + sizeof(E) * BLK * PT;
+    static constexpr bool ALIAS = PT <= PV;  // else (small dv) a region of its own
+    static constexpr size_t pB_dTT = ALIAS ? o_V : pB_dW + sizeof(E) * BLK * PK;
+    static constexpr size_t total = pB_dW + sizeof(E) * BLK * PK + (ALIAS ? 0 : sizeof(E) * BLK * PT);
 };
 
 // ---------------------------------------------------------------------------
@@ -248,24 +250,33 @@ __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
     }
     __syncthreads();
     // dT[w][sb] = beta_s (dU V^T + dW (K e^b)^T): rows t, cols s; stored as dT^T[s][t]
+    // (where V was, after every wave's V reads)
     {
         Frag<E> fdu[KV], fdw[KK];
 #pragma unroll
         for (int kk = 0; kk < KV; ++kk) fdu[kk] = ldfrag_tr(dUTs, PT, 32 * kk, 16 * w, l);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) fdw[kk] = ldfrag(dWs + (16 * w + r) * PK + 32 * kk + 4 * g);
+        f32x4 dts[2];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            if ((sb & 1) != hf) continue;
+        for (int u = 0; u < 2; ++u) {
+            const int sb = hf + 2 * u;
             f32x4 acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < KV; ++kk) mma(acc, fdu[kk], ldfrag(Vs + (16 * sb + r) * PV + 32 * kk + 4 * g));
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) mma(acc, fdw[kk], ldfrag(Kd + (16 * sb + r) * PK + 32 * kk + 4 * g));
-            const int s = 16 * sb + r;
-            st4(dTT + s * PT + 16 * w + 4 * g, acc * s_bet[s]);
+            dts[u] = acc * s_bet[16 * sb + r];
         }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) st4(dTT + (16 * (hf + 2 * u) + r) * PT + 16 * w + 4 * g, dts[u]);
     }
+    // V rows of this lane's token for the V term of dbeta (V is no longer in LDS)
+    Raw4<E> vrow[NVH];
+    const E* vtok = a.v + (tok0 + min(tw, nvalid - 1)) * ldv + (size_t)h * DV;
+#pragma unroll
+    for (int jv = 0; jv < NVH; ++jv) vrow[jv] = ldraw4(vtok + 16 * (hf * NVH + jv) + 4 * g);
     __syncthreads();
     // X^T[sb][w] = dT^T T (rows s, cols t = tw);  dA[w][cb] = -X T^T (rows t, cols c),
     // strictly lower;  dM = beta_t dA;  the Gram term of dbeta, sum_c dA[t][c] M[t][c]
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(512) void kda_bwd_wy_kernel(KdaWyArgs<E> a) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 mma(acc, ldfrag(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g), ldfrag(TT + tw * PT + 32 * j + 4 * g));
-            const f32x4 vv = ld4(Vs + tw * PV + 16 * vb + 4 * g);
+            const f32x4 vv = cvt4(vrow[jv]);
             dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
             if (tw < nvalid) st4(a.dv + (tok0 + tw) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc * bet_tw);
         }
