@@ -1121,10 +1121,10 @@ template <typename E> struct KdaPrepArgs {
     E* Kd = nullptr;
 };
 
-// dst[t][d] = src[t][d] e^{b_t[d]} over a 64 x DK tile (row pitch PX, b row
-// pitch PB), 16-byte vectors, all NT threads.
+// dst[t][d] = src[t][d] e^{b_t[d]} over a 64 x DK tile (row pitch PX; dst row
+// pitch PD, PX when not given; b row pitch PB), 16-byte vectors, all NT threads.
 template <typename E, int DK, int PX, int PB, int NT>
-__device__ __forceinline__ void scale_exp_rows(const E* src, const float* Bs, E* dst) {
+__device__ __forceinline__ void scale_exp_rows(const E* src, const float* Bs, E* dst, int PD = PX) {
     constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = DK / VEC, UNITS = BLK * PER_ROW;
 #pragma unroll
     for (int j = 0; j < (UNITS + NT - 1) / NT; ++j) {
@@ -1138,7 +1138,7 @@ __device__ __forceinline__ void scale_exp_rows(const E* src, const float* Bs, E*
             x.u = *(const uint4*)(src + t * PX + c);
 #pragma unroll
             for (int i = 0; i < VEC; ++i) x.e[i] = from_f<E>(to_f(x.e[i]) * __expf(Bs[t * PB + c + i]));
-            *(uint4*)(dst + t * PX + c) = x.u;
+            *(uint4*)(dst + t * PD + c) = x.u;
         }
     }
 }
@@ -1199,31 +1199,37 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
     const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
     constexpr int PK = RP<E, DK>, PV = RP<E, DV>, PB = DK + 4, ND = DK / 16;
 
-    __shared__ __align__(16) E Ks[BLK * PK], Kd[BLK * PK], Vs[BLK * PV];
+    // LDS: K, the cumulative gate b (fp32) and one fp32 64 x 64 region that
+    // holds g (for the cumsum), then A, then T, then V; K * e^b is formed
+    // where it is read.  About 73 KB with dk = dv = 128: two work-groups per CU.
+    __shared__ __align__(16) E Ks[BLK * PK];
     __shared__ __align__(16) float Bs[BLK * PB];
-    __shared__ __align__(16) float Am[BLK * AP], Td[4 * 256];  // A, then T (fp32)
+    __shared__ __align__(16) float Am[BLK * AP], Td[4 * 256];  // g, A, T (fp32), V
     __shared__ __align__(16) float zrow[DK];
     __shared__ float seg[256];
     __shared__ __align__(16) float s_bet[BLK];
+    static_assert(sizeof(E) * BLK * PK <= sizeof(float) * BLK * AP && sizeof(E) * BLK * PV <= sizeof(float) * BLK * AP,
+                  "g and V fit the A region");
+    E* Gs = (E*)Am;  // g, staged for the cumsum
+    E* Vs = (E*)Am;  // V, once T has been read into registers
 
+    // V waits in registers until its rows are staged (after T)
+    const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
     {
         const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
-        const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
         const auto gx = load_gate<false, E, DK, NT>(a.g, tok0, h, H, nvalid);
         if (tid < BLK) s_bet[tid] = tid < nvalid ? to_f(a.beta[(tok0 + tid) * H + h]) : 0.f;
         if (tid < DK) zrow[tid] = 0.f;
         store_rows<E, BLK, DK, PK, NT>(kx, Ks);
-        store_rows<E, BLK, DV, PV, NT>(vx, Vs);
-        store_rows<E, BLK, DK, PK, NT>(gx, Kd);  // g staged where K * e^b goes
+        store_rows<E, BLK, DK, PK, NT>(gx, Gs);
         __syncthreads();
-        gate_cumsum<E, DK, PK, PB>(Kd, Bs, seg, nvalid);
+        gate_cumsum<E, DK, PK, PB>(Gs, Bs, seg, nvalid);
         __syncthreads();
         const bool over = diag_out_of_range<DK, PB>(Bs);
         if (a.range && tid == 0) a.range[chunk] = over ? 1 : 0;
     }
-    // K * e^b (factors <= 1), and exp(b_C) per channel
+    // exp(b_C) per channel
     const float* bC = Bs + (BLK - 1) * PB;
-    scale_exp_rows<E, DK, PK, PB, NT>(Ks, Bs, Kd);
     if (tid < 256) a.eC[chunk * 256 + tid] = tid < DK ? __expf(bC[tid]) : 0.f;
     // Am[t][s] = beta_t M[t][s] (s < t); M as accumulator tiles for the backward
     float* Mg = a.M ? a.M + chunk * BLK * BLK : nullptr;
@@ -1232,14 +1238,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
         if (Mg) Mg[(4 * (row >> 4) + (col >> 4)) * 256 + l * 4 + (row & 3)] = m;
     });
     __syncthreads();
-    if (a.Kd) {  // K e^b, row-major, for the backward
-        constexpr int VEC = 16 / (int)sizeof(E), PER_ROW = DK / VEC;
-        E* dst = a.Kd + chunk * BLK * DK;
-        for (int u = tid; u < BLK * PER_ROW; u += NT) {
-            const int t = u / PER_ROW, c = (u % PER_ROW) * VEC;
-            *(uint4*)(dst + t * DK + c) = *(const uint4*)(Kd + t * PK + c);
-        }
-    }
+    if (a.Kd)  // K e^b (factors <= 1), row-major, for the backward
+        scale_exp_rows<E, DK, PK, PB, NT>(Ks, Bs, a.Kd + chunk * BLK * DK, DK);
     f32x4 tc[4];
     if (hf == 0) {
         // T = (I + A)^-1, wave w holds column block w
@@ -1277,9 +1277,13 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
         const int db = tile >> 2, tb = tbw;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Kd, PK, 32 * j, 16 * db, l), t1[j]);
+        for (int j = 0; j < 2; ++j)  // (K e^b)^T fragment, scaled as it is read
+            mma2(acc, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, zrow, 1.f, 0, BLK), t1[j]);
         st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
     }
+    __syncthreads();  // every wave has its T1 rows: V takes T's place
+    store_rows<E, BLK, DV, PV, NT>(vx, Vs);
+    __syncthreads();
     // Ut = T1 V, stored negated as fp32 -Ut^T (tiled)
     float* Uout = a.UtT + chunk * BLK * DV;
 #pragma unroll
