@@ -507,8 +507,8 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     const E* vbase = a.v + tok0 * ldv + (size_t)h * DV;
     const E* hT = a.hT + chunk * DK * DV;
 
-    // h^T slices of this half, loaded PD slices ahead of their use
-    constexpr int PD = NVH > 2 ? 2 : 1, NB = PD + 1;
+    // h^T slices of this half, loaded AHEAD slices before their use
+    constexpr int AHEAD = NVH > 2 ? 2 : 1, NB = AHEAD + 1;
     Frag<E> fh[NB][KK];
     auto load_slice = [&](int buf, int vb) {
 #pragma unroll
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
         const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
         const auto gx = load_gate<SG, E, DK, NT>(a.g, tok0, h, H, nvalid);
 #pragma unroll
-        for (int j = 0; j < PD; ++j) load_slice(j, hf * NVH + j);
+        for (int j = 0; j < AHEAD; ++j) load_slice(j, hf * NVH + j);
         store_rows<E, BLK, DK, PK, NT>(qx, Qs);
         store_rows<E, BLK, DK, PK, NT>(kx, Ks);
         store_rows<E, BLK, DK, PK, NT>(gx, Vs);
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     };
 #pragma unroll
     for (int jv = 0; jv < NVH; ++jv) {
-        if (jv + PD < NVH) load_slice((jv + PD) % NB, hf * NVH + jv + PD);
+        if (jv + AHEAD < NVH) load_slice((jv + AHEAD) % NB, hf * NVH + jv + AHEAD);
         compute_slice(jv % NB, hf * NVH + jv);
     }
 }
