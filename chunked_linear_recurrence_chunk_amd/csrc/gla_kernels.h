@@ -892,16 +892,17 @@ __global__ __launch_bounds__(512) void gla_bwd_intra_kernel(GlaIntraArgs<E> a) {
     const float bet_tl = KDA && tl < nvalid ? to_f(a.beta[(tok0 + tl) * H + h]) : 0.f;
     // (6) dV^T[vb][R] = dO^T P + (Kh dh)^T   (rows v, col s = tl)
     if constexpr (!KDA) {
-        const E* dVs = a.dVs + chunk * BLK * DV;
+        // the state part of dV, all loads issued before use (rows past the
+        // sequence end read the last valid row and are dropped)
         constexpr int NVH = DV / 32;  // value blocks per half
-        f32x4 ds[NVH];
+        Raw4<E> dsr[NVH];
+        const E* dVrow = a.dVs + chunk * BLK * DV + (size_t)min(tl, nvalid - 1) * DV;
 #pragma unroll
-        for (int jv = 0; jv < NVH; ++jv)
-            ds[jv] = tl < nvalid ? ld4(dVs + (size_t)tl * DV + 16 * (hf * NVH + jv) + 4 * g) : zero4();
+        for (int jv = 0; jv < NVH; ++jv) dsr[jv] = ldraw4(dVrow + 16 * (hf * NVH + jv) + 4 * g);
 #pragma unroll
         for (int jv = 0; jv < NVH; ++jv) {
             const int vb = hf * NVH + jv;
-            f32x4 acc = ds[jv];
+            f32x4 acc = tl < nvalid ? cvt4(dsr[jv]) : zero4();
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 if (32 * j + 32 > 16 * R) mma(acc, ldfrag_tr(dOs, PV, 32 * j, 16 * vb, l), fP[j]);
