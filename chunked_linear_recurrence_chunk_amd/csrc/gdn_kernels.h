@@ -220,6 +220,14 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     float* Td = (float*)(lds + Lay::o_Td);
 
     const size_t ldk = (size_t)H * DK, ldv = (size_t)H * DV;
+    // wave 0's gate and beta loads go out first, so that the cumsum waits for
+    // them alone (rows past the end read the last valid token; selected below)
+    E graw = from_f<E>(0.f), braw = from_f<E>(0.f);
+    if (w8 == 0) {
+        const size_t ig = (tok0 + min(l, nvalid - 1)) * H + h;
+        graw = a.g[ig];
+        braw = a.beta[ig];
+    }
     const auto kx = load_rows<E, BLK, DK, NT>(a.k + tok0 * ldk + (size_t)h * DK, ldk, nvalid);
     const auto vx = load_rows<E, BLK, DV, NT>(a.v + tok0 * ldv + (size_t)h * DV, ldv, nvalid);
     // backward: Q and dO in flight through the Gram and inverse phases
@@ -231,9 +239,8 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     }
     if (w8 == 0) {
         // tokens past the end are identity steps: g = 0, beta = 0
-        const size_t ig = (tok0 + l) * H + h;
-        const float gv = l < nvalid ? to_f(a.g[ig]) : 0.f;
-        const float bv = l < nvalid ? to_f(a.beta[ig]) : 0.f;
+        const float gv = l < nvalid ? to_f(graw) : 0.f;
+        const float bv = l < nvalid ? to_f(braw) : 0.f;
         const float gam = wave_prefix_sum(gv);
         const float gC = __shfl(gam, BLK - 1, 64);
         s_gam[l] = gam;
