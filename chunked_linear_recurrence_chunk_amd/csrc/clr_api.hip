@@ -26,14 +26,14 @@ bool gla_shape_ok(int dk, int dv) { return gdn_shape_ok(dk, dv) || (dk == 128 &&
 size_t esize(int dtype) { return dtype == CLR_BF16 ? 2 : 4; }
 
 // Basic shape validation shared by every entry point.  The fp32 backward
-// kernels are instantiated for dk = dv = 32 only.
+// kernels are instantiated for dk = dv <= 64.
 int check_shape(const clr_shape_t* s, bool gla, bool bwd) {
     if (!s) return CLR_EINVAL;
     if (s->B < 1 || s->H < 1 || s->T < 0 || s->dk < 1 || s->dv < 1) return CLR_EINVAL;
     if (s->dtype != CLR_F32 && s->dtype != CLR_BF16) return CLR_ENOTSUP;
     if (s->chunk != 0 && s->chunk != BLK) return CLR_ENOTSUP;  // the kernels' block size
     if (gla ? !gla_shape_ok(s->dk, s->dv) : !gdn_shape_ok(s->dk, s->dv)) return CLR_ENOTSUP;
-    if (bwd && s->dtype == CLR_F32 && !(s->dk == 32 && s->dv == 32)) return CLR_ENOTSUP;
+    if (bwd && s->dtype == CLR_F32 && (s->dk > 64 || s->dv > 64)) return CLR_ENOTSUP;
     // 64-bit element counts must stay addressable
     const double tok = (double)s->B * s->T * s->H * (s->dk > s->dv ? s->dk : s->dv);
     if (tok > 9.0e15) return CLR_EINVAL;
@@ -83,9 +83,10 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     return w;
 }
 
-// The fp32 KDA forward is instantiated for d <= 64 only, the backward for d = 32.
+// The fp32 KDA forward and backward are instantiated for d <= 64.
 bool kda_f32_unsupported(const clr_shape_t* s, bool bwd) {
-    return s->dtype == CLR_F32 && s->dk > (bwd ? 32 : 64);
+    (void)bwd;
+    return s->dtype == CLR_F32 && s->dk > 64;
 }
 
 // KDA: the Gated DeltaNet forward layouts the scan reads, exp(b_C) per key

@@ -14,8 +14,10 @@ namespace clr {
     CLR_CASE(E, 32, 32)       \
     CLR_CASE(E, 64, 64)       \
     CLR_CASE(E, 128, 128)
-// fp32 backward: the block-adjoint kernel's LDS tiles fit only for d = 32.
-#define CLR_FOR_GDN_BWD_SHAPES_F32(E) CLR_CASE(E, 32, 32)
+// fp32 backward: the block kernels' LDS tiles fit for d <= 64.
+#define CLR_FOR_GDN_BWD_SHAPES_F32(E) \
+    CLR_CASE(E, 32, 32)               \
+    CLR_CASE(E, 64, 64)
 // fp32 KDA forward: the prep kernel's LDS tiles fit for d <= 64.
 #define CLR_FOR_KDA_SHAPES_F32(E) \
     CLR_CASE(E, 32, 32)           \

@@ -34,7 +34,8 @@
  *     beta, dbeta       GDN: [B, T, H]     GLA: must be NULL     (shape.dtype)
  *     S_in, S_out, dS_out, dS_in   [B, H, dk, dv]  always float32
  * Supported head sizes: GDN (dk, dv) in {(32,32), (64,64), (128,128)};
- * GLA additionally (128, 256).  The float32 backward supports (32, 32) only.
+ * GLA additionally (128, 256).  The float32 backward supports (32, 32) and
+ * (64, 64).
  * Others, among them GDN and KDA at dk = dv = 256 (the block kernels' LDS
  * tiles and the scans' per-block operands would not fit a CU at that size),
  * return CLR_ENOTSUP.  Any T >= 0 (a ragged last 64-token block is
@@ -188,7 +189,7 @@ int mamba2_bwd(const clr_shape_t* shape, const void* q, const void* k, const voi
  *     o_t = S_t^T q_t,   alpha_t = exp(g_t) in R^dk (per key channel).
  * Same arguments as gdn_fwd / gdn_bwd except g and dg, which are
  * [B, T, H, dk] as for GLA; beta and dbeta are required.  Head sizes as for
- * GDN (fp32: forward d <= 64, backward d = 32; CLR_ENOTSUP otherwise).
+ * GDN (fp32: d <= 64; CLR_ENOTSUP otherwise).
  * Workspace: CLR_OP_KDA_FWD / CLR_OP_KDA_BWD.  The backward recomputes the
  * forward from S_in (as gdn_bwd does); dS_out may be NULL (zero).  The
  * per-block decays use 16-token sub-tiles with the same e^80 bound as the GLA

@@ -143,16 +143,18 @@ def test_bwd_validation():
     # GLA: beta / dbeta must be NULL
     sg = _shape(ops, T=64, H=1, dk=32, dv=32)
     assert lib.gla_bwd(ctypes.byref(sg), *ptrs, 1 << 40, None) == ops.CLR_EINVAL
-    # fp32 backward at d = 64 is not supported
-    s64 = _shape(ops, T=64, H=1, dk=64, dv=64, dtype=0)
-    assert lib.gdn_bwd(ctypes.byref(s64), *ptrs, 1 << 40, None) == ops.CLR_ENOTSUP
-    assert lib.kda_bwd(ctypes.byref(s64), *ptrs, 1 << 40, None) == ops.CLR_ENOTSUP
+    # fp32 backward at d = 128 is not supported (d <= 64 is)
+    s128 = _shape(ops, T=64, H=1, dk=128, dv=128, dtype=0)
+    assert lib.gdn_bwd(ctypes.byref(s128), *ptrs, 1 << 40, None) == ops.CLR_ENOTSUP
+    assert lib.kda_bwd(ctypes.byref(s128), *ptrs, 1 << 40, None) == ops.CLR_ENOTSUP
     # KDA needs beta and dbeta; its workspace is larger than the forward's
     bad = list(ptrs)
     bad[4] = None
     assert lib.kda_bwd(ctypes.byref(s), *bad, 1 << 40, None) == ops.CLR_EINVAL
     assert ops.workspace_bytes(s, ops.OP_KDA_BWD) > ops.workspace_bytes(s, ops.OP_KDA_FWD) > 0
-    assert ops.workspace_bytes(s64, ops.OP_KDA_BWD) == 0 and ops.workspace_bytes(s64, ops.OP_KDA_FWD) > 0
+    assert ops.workspace_bytes(s128, ops.OP_KDA_BWD) == 0 and ops.workspace_bytes(s128, ops.OP_KDA_FWD) == 0
+    s64 = _shape(ops, T=64, H=1, dk=64, dv=64, dtype=0)
+    assert ops.workspace_bytes(s64, ops.OP_KDA_BWD) > ops.workspace_bytes(s64, ops.OP_KDA_FWD) > 0
 
 
 def test_mamba2_and_shortconv_validation():
@@ -234,8 +236,8 @@ def test_range_status_rejects_on_the_host():
         assert lib.clr_range_status(ctypes.byref(_shape(ops, T=0)), op, fake, None) == ops.CLR_OK  # no blocks
     for op in (-1, 8):
         assert lib.clr_range_status(ctypes.byref(sh), op, fake, None) == ops.CLR_EINVAL
-    # the fp32 KDA backward exists for d = 32 only
-    f32 = _shape(ops, dk=64, dv=64, dtype=0)
+    # the fp32 KDA backward exists for d <= 64
+    f32 = _shape(ops, dk=128, dv=128, dtype=0)
     assert lib.clr_range_status(ctypes.byref(f32), ops.OP_KDA_BWD, fake, None) == ops.CLR_ENOTSUP
 
 
@@ -292,7 +294,7 @@ def test_binding_checks_shapes_and_dtypes_before_the_library():
 
 def test_shape_chunk_field_and_unsupported_sizes():
     """The kernel-level block is 64 tokens (chunk 0 or 64); Gated DeltaNet at
-    dk = dv = 256 and the fp32 backward beyond d = 32 are not built."""
+    dk = dv = 256 and the fp32 backward beyond d = 64 are not built."""
     ops, lib = _lib()
     base = ops.workspace_bytes(_shape(ops), ops.OP_GDN_FWD)
     s64 = _shape(ops)
@@ -308,5 +310,6 @@ def test_shape_chunk_field_and_unsupported_sizes():
     s256 = _shape(ops, dk=256, dv=256)
     assert lib.gdn_fwd(ctypes.byref(s256), *([None] * 9), 0, None) == ops.CLR_ENOTSUP
     assert lib.gdn_bwd(ctypes.byref(s256), *([None] * 15), 0, None) == ops.CLR_ENOTSUP
-    for d in (64, 128):
-        assert ops.workspace_bytes(_shape(ops, dk=d, dv=d, dtype=0), ops.OP_GDN_BWD) == 0
+    assert ops.workspace_bytes(_shape(ops, dk=128, dv=128, dtype=0), ops.OP_GDN_BWD) == 0
+    for d in (32, 64):
+        assert ops.workspace_bytes(_shape(ops, dk=d, dv=d, dtype=0), ops.OP_GDN_BWD) > 0

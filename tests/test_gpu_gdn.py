@@ -172,6 +172,7 @@ def _run_bwd(x, dtype, with_dS=True):
 BWD_CASES = [
     (1, 256, 1, 32, 32, "fp32", 21),
     (2, 200, 3, 32, 32, "fp32", 22),    # ragged tail
+    (1, 192, 2, 64, 64, "fp32", 27),
     (1, 512, 2, 128, 128, "bf16", 23),
     (2, 320, 2, 64, 64, "bf16", 24),
     (1, 100, 2, 128, 128, "bf16", 25),  # ragged, < 2 blocks

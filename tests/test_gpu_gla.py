@@ -12,6 +12,7 @@ CASES = [
     # (B, T, H, dk, dv, dtype, seed, gate_scale)
     (1, 256, 1, 32, 32, "fp32", 41, 1 / 16),
     (2, 200, 2, 32, 32, "fp32", 42, 1.0),        # ragged tail, strong gates
+    (1, 192, 2, 64, 64, "fp32", 47, 1 / 16),
     (2, 256, 2, 128, 256, "bf16", 43, 1 / 16),   # the GLA workload's head shape
     (1, 320, 2, 64, 64, "bf16", 44, 1 / 16),
     (1, 100, 3, 128, 128, "bf16", 45, 1 / 16),  # ragged, < 2 blocks

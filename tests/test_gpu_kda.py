@@ -65,6 +65,7 @@ def test_kda_chunked_equals_unchunked():
 BWD_CASES = [
     (1, 256, 1, 32, 32, "fp32", 81, 1 / 16),
     (2, 200, 2, 32, 32, "fp32", 82, 1.0),        # ragged tail, strong gates
+    (1, 200, 2, 64, 64, "fp32", 88, 1 / 16),     # ragged tail
     (1, 192, 2, 32, 32, "bf16", 83, 1 / 16),
     (2, 320, 2, 64, 64, "bf16", 84, 1 / 16),
     (1, 512, 2, 128, 128, "bf16", 85, 1 / 16),

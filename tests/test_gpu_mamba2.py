@@ -14,6 +14,7 @@ CASES = [
     # (B, T, H, dk, dv, dtype, seed, gate_scale)
     (1, 256, 1, 32, 32, "fp32", 61, 1 / 16),
     (2, 200, 2, 32, 32, "fp32", 62, 1.0),        # ragged tail, strong gates
+    (1, 192, 2, 64, 64, "fp32", 67, 1 / 16),
     (2, 256, 2, 128, 256, "bf16", 63, 1 / 16),   # the measured workload's head shape
     (1, 320, 2, 64, 64, "bf16", 64, 1 / 16),
     (1, 100, 3, 128, 128, "bf16", 65, 1 / 16),   # ragged, < 2 blocks
