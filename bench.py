@@ -319,16 +319,17 @@ def profile_summary(workload: str, d: str) -> None:
     args = f"--workload {workload}"
     md = [f"# rocprofv3 summary: {workload}", "",
           f"Workload: {cfg}; one launch processes one sequence chunk.", "",
-          "Commands (run from /tmp with TMPDIR=/tmp; R = repository root on the GPU box; "
-          "D = $R/gpurun_out/prof/" + workload + "):", "", "```",
+          "Commands (run from /tmp with TMPDIR=/tmp; R = repository root; O = an output directory, "
+          "D = $O/" + workload + "; the copy calibration goes to $O/copy, where the summary step looks "
+          "for it):", "", "```",
           f"rocprofv3 --kernel-trace --stats -T -f csv -d $D/kt -o run -- python3 $R/bench.py {args} --steps 5 --warmup 2 --no-cpu",
           f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d $D/fetch -o run -- python3 $R/bench.py {args} --steps 1 --warmup 1 --no-cpu",
           f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d $D/write -o run -- python3 $R/bench.py {args} --steps 1 --warmup 1 --no-cpu",
           "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -T -f csv "
           f"-d $D/mfma -o run -- python3 $R/bench.py {args} --steps 1 --warmup 1 --no-cpu",
-          "rocprofv3 --pmc FETCH_SIZE -T -f csv -d $R/gpurun_out/prof/copy/fetch -o run -- python3 $R/bench.py --calibrate-copy 1073741824",
-          "rocprofv3 --pmc WRITE_SIZE -T -f csv -d $R/gpurun_out/prof/copy/write -o run -- python3 $R/bench.py --calibrate-copy 1073741824",
-          f"python3 bench.py {args} --profile-summary gpurun_out/prof/{workload}", "```", "",
+          "rocprofv3 --pmc FETCH_SIZE -T -f csv -d $O/copy/fetch -o run -- python3 $R/bench.py --calibrate-copy 1073741824",
+          "rocprofv3 --pmc WRITE_SIZE -T -f csv -d $O/copy/write -o run -- python3 $R/bench.py --calibrate-copy 1073741824",
+          f"cd $R && python3 bench.py {args} --profile-summary $D", "```", "",
           f"Counter calibration (1 GiB device copy): FETCH_SIZE reads {cf['fetch']:.0f} KiB, WRITE_SIZE "
           f"{cf['write']:.0f} KiB per dispatch -> scale factors fetch x{f_scale:.3f}, write x{w_scale:.3f}.", "",
           "Matrix cores: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 is the bf16 matrix flops a launch executed; "
