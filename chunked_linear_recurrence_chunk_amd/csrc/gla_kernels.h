@@ -214,7 +214,8 @@ __device__ __forceinline__ Frag2<E> frag_row_decay2(const E* X, int PX, int row,
 // The b values are read four at a time (k is always inside the 64-token
 // tile, so every read is in bounds); the empty asm keeps the compiler from
 // moving each read under its range test, which serialises them, and outside
-// [klo, khi) the exponent is -inf, so the factor is exactly 0.
+// [klo, khi) the exponent is -inf, so the factor is exactly 0.  klo and khi
+// must be the same for every lane of the wave.
 template <typename E>
 __device__ __forceinline__ void col_decay_scales(const float* bs, int PB, int m, int k0, const float* ref, float sgn,
                                                  int klo, int khi, float (&sc)[8]) {
@@ -222,6 +223,15 @@ __device__ __forceinline__ void col_decay_scales(const float* bs, int PB, int m,
     const float rm = ref[m];
 #pragma unroll
     for (int hbl = 0; hbl < 2; ++hbl) {
+        // a 16-token half wholly outside [klo, khi) has every factor 0 (the same
+        // values the exponentials of -inf give); the range is the wave's, so the
+        // test is a scalar branch
+        const int kb = k0 + 16 * hbl;
+        if (__builtin_amdgcn_readfirstlane((kb + 16 <= klo || kb >= khi) ? 1 : 0)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[4 * hbl + i] = 0.f;
+            continue;
+        }
         float bv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) bv[i] = bs[(k0 + 16 * hbl + 4 * g + i) * PB + m];
