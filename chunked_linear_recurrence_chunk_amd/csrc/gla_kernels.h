@@ -550,12 +550,18 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     const float* bt = Bs + tl * PB;
     const float* refO = R > 0 ? Bs + (16 * R - 1) * PB : zrow;  // boundary before tile R
     const float* refD = Bs + (16 * R + 7) * PB;                 // middle of tile R
+    // The wave forms the P^T tiles sb = hf, hf + 2 that are <= R (below): the
+    // off-diagonal ones (sb < R) take qo, the diagonal one (sb = R) qd, so a
+    // wave builds only the decayed Q fragments it uses (a scalar test: R and
+    // hf are the wave's).
+    const bool need_qo = __builtin_amdgcn_readfirstlane(hf < R ? 1 : 0);
+    const bool need_qd = __builtin_amdgcn_readfirstlane((R & 1) == hf ? 1 : 0);
     Frag<E> qi[KK], qo[KK], qd[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         qi[kk] = frag_row_decay(Qs, PK, tl, 32 * kk, bt, zrow, 1.f);
-        qo[kk] = frag_row_decay(Qs, PK, tl, 32 * kk, bt, refO, 1.f);
-        qd[kk] = frag_row_decay(Qs, PK, tl, 32 * kk, bt, refD, 1.f);
+        qo[kk] = need_qo ? frag_row_decay(Qs, PK, tl, 32 * kk, bt, refO, 1.f) : Frag<E>{};
+        qd[kk] = need_qd ? frag_row_decay(Qs, PK, tl, 32 * kk, bt, refD, 1.f) : Frag<E>{};
     }
     // P^T[sb][R]: rows s, column t = tl.  Both waves of token tile R need
     // all of its tiles; wave (R, hf) forms the tiles sb = hf, hf + 2 (when
