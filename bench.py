@@ -55,7 +55,7 @@ for _p in ("gla", "m2"):
                       _p + "_scan_fwd": "v", _p + "_scan_fwd_rec": "v", _p + "_scan_bwd": "dO",
                       _p + "_bwd_intra": "q k v g dO dq dk dv dg"})
 # boundary states each scan reads or writes (fp32 [B, H, dk, dv])
-SCAN_STATES = {"gdn_scan_fwd": 2, "gdn_scan_pair": 3, "kda_scan_fwd": 2, "kda_scan_pair": 3,
+SCAN_STATES = {"gdn_scan_fwd": 2, "gdn_scan_pair": 3, "gdn_scan_rev": 2, "kda_scan_fwd": 2, "kda_scan_pair": 3,
                "gla_scan_fwd": 2, "gla_scan_fwd_rec": 1, "gla_scan_bwd": 2,
                "m2_scan_fwd": 2, "m2_scan_fwd_rec": 1, "m2_scan_bwd": 2}
 
@@ -146,6 +146,9 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
                           2 * (2 * CC * dv) + 2 * (2 * C * kv) + 4 * (2 * CC * dk))
     # one launch running the forward recompute and the reverse scan side by side
     W["gdn_scan_pair"] = tuple(x + y for x, y in zip(W["gdn_scan_fwd_rec"], W["gdn_scan_bwd"]))
+    # with saved activations the backward runs the reverse scan alone (and the
+    # forward scan also stores each block's state in the backward's layout)
+    W["gdn_scan_rev"] = W["gdn_scan_bwd"]
     return W.get(name)
 
 
@@ -439,6 +442,9 @@ def main():
                     help="value columns per work-group of the Gated DeltaNet forward scan (default: the library's, 16)")
     ap.add_argument("--fwd-split", type=int, default=None, metavar="PERMILLE",
                     help="split-and-overlap forward at PERMILLE/1000 of the blocks (0 = off, the default)")
+    ap.add_argument("--saved", action="store_true",
+                    help="Gated DeltaNet: keep each chunk's forward activations for its backward "
+                         "(gdn_fwd_save / gdn_bwd_saved) instead of recomputing them")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -498,8 +504,10 @@ def main():
         d = {k: dev(x[k], dtype) for k in keys}
         S_in = dev(x["S_in"], "fp32")
         if delta:
-            cls = stateflow.GdnChunked if cfg["kind"] == "gdn" else stateflow.KdaChunked
-            drv = cls(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
+            if cfg["kind"] == "gdn":
+                drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N, save=args.saved)
+            else:
+                drv = stateflow.KdaChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
         elif cfg["kind"] == "gla":
             drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
         else:

@@ -83,6 +83,18 @@ GdnWs carve_gdn(const clr_shape_t* s, bool bwd, char* base, size_t* total) {
     return w;
 }
 
+// Saved forward activations of the Gated DeltaNet layer: per block the
+// entering state (tiled h[d][v]) and U^T (tiled [dv][64]), element type.
+size_t saved_carve(const clr_shape_t* s, char* base, void** h, void** U) {
+    Carver c{base};
+    const size_t nb = nblocks(s), es = esize(s->dtype);
+    void* ph = c.take(nb * s->dk * s->dv * es);
+    void* pu = c.take(nb * BLK * s->dv * es);
+    if (h) *h = ph;
+    if (U) *U = pu;
+    return c.off;
+}
+
 // The fp32 KDA forward and backward are instantiated for d <= 64.
 bool kda_f32_unsupported(const clr_shape_t* s, bool bwd) {
     (void)bwd;
@@ -215,6 +227,12 @@ const char* clr_status_string(int s) {
     }
 }
 
+size_t clr_saved_bytes(const clr_shape_t* s) {
+    // the saved activations feed gdn_bwd_saved: the backward's shapes
+    if (check_shape(s, false, true) != CLR_OK) return 0;
+    return saved_carve(s, nullptr, nullptr, nullptr);
+}
+
 size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
     if (op == CLR_OP_KDA_FWD || op == CLR_OP_KDA_BWD) {
         const bool bwd = op == CLR_OP_KDA_BWD;
@@ -291,7 +309,8 @@ enum Kind { K_GDN, K_GLA, K_M2, K_KDA };
 
 static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void* k, const void* v,
                       const void* g, const void* beta, const float* S_in, void* o, float* S_out,
-                      void* ws, size_t ws_bytes, void* stream, bool noalloc = false) {
+                      void* ws, size_t ws_bytes, void* stream, bool noalloc = false,
+                      void* saved = nullptr, size_t saved_bytes = 0, bool save = false) {
     const bool gla = kind == K_GLA || kind == K_M2;  // GLA kernels and head sizes
     const bool has_beta = kind == K_GDN || kind == K_KDA;
     int rc = check_shape(s, gla, false);
@@ -307,10 +326,15 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
                   {v, ntok * s->dv * es, false}, {g, ntok * ((kind == K_GLA || kind == K_KDA) ? s->dk : 1) * es, false},
                   {beta, ntok * es, false},      {S_in, nst * 4, false},
                   {o, ntok * s->dv * es, true},  {S_out, nst * 4, true},
-                  {ws, ws_bytes, true}};
+                  {ws, ws_bytes, true},          {saved, saved_bytes, true}};
     // g and beta rows of GDN are only 2/4-byte aligned per token but the
     // tensors themselves must start 16-byte aligned.
-    if ((rc = check_bufs(bufs, 9))) return rc;
+    if ((rc = check_bufs(bufs, 10))) return rc;
+    if (save) {  // gdn_fwd_save: the saved activations feed gdn_bwd_saved
+        if ((rc = check_shape(s, false, true))) return rc;
+        const size_t need_s = clr_saved_bytes(s);
+        if (need_s && (!saved || saved_bytes < need_s || ((uintptr_t)saved & (ALIGN - 1)))) return CLR_EWORKSPACE;
+    }
     const size_t need = clr_workspace_bytes(s, kind == K_KDA ? CLR_OP_KDA_FWD : gla ? CLR_OP_GLA_FWD : CLR_OP_GDN_FWD);
     if (noalloc && need > (size_t)CLR_NOALLOC_SCRATCH_BYTES) return CLR_ESCRATCH;
     hipStream_t st = (hipStream_t)stream;
@@ -336,6 +360,7 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
         L.q = q; L.k = k; L.v = v; L.g = g; L.beta = beta; L.S_in = S_in; L.o = o; L.S_out = S_out;
         L.ws = carve_gdn(s, false, (char*)ws, nullptr);
         L.no_split = noalloc;
+        if (save) saved_carve(s, (char*)saved, &L.saved_h, &L.saved_U);
         return hip_status(launch_gdn_fwd(L, st));
     } else {
         GlaLaunch L{};
@@ -360,6 +385,13 @@ int gdn_fwd_noalloc(const clr_shape_t* s, const void* q, const void* k, const vo
     return fwd_common(K_GDN, s, q, k, v, g, beta, S_in, o, S_out, nullptr, 0, stream, /*noalloc=*/true);
 }
 
+int gdn_fwd_save(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+                 const void* beta, const float* S_in, void* o, float* S_out, void* saved, size_t saved_bytes,
+                 void* ws, size_t ws_bytes, void* stream) {
+    return fwd_common(K_GDN, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream, false, saved, saved_bytes,
+                      /*save=*/true);
+}
+
 int gla_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
             const void* beta, const float* S_in, void* o, float* S_out, void* ws, size_t ws_bytes,
             void* stream) {
@@ -381,7 +413,8 @@ int mamba2_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v
 static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void* k, const void* v,
                       const void* g, const void* beta, const float* S_in, const void* dO,
                       const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
-                      float* dS_in, void* ws, size_t ws_bytes, void* stream) {
+                      float* dS_in, void* ws, size_t ws_bytes, void* stream,
+                      const void* saved = nullptr, size_t saved_bytes = 0, bool use_saved = false) {
     const bool gla = kind == K_GLA || kind == K_M2;  // GLA kernels and head sizes
     const bool has_beta = kind == K_GDN || kind == K_KDA;
     int rc = kind == K_KDA ? check_shape(s, false, false) : check_shape(s, gla, true);
@@ -402,8 +435,12 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
                   {dq, ntok * s->dk * es, true},  {dk, ntok * s->dk * es, true},
                   {dv, ntok * s->dv * es, true},  {dg, gn, true},
                   {dbeta, ntok * es, true},       {dS_in, nst * 4, true},
-                  {ws, ws_bytes, true}};
-    if ((rc = check_bufs(bufs, 15))) return rc;
+                  {ws, ws_bytes, true},           {saved, saved_bytes, false}};
+    if ((rc = check_bufs(bufs, 16))) return rc;
+    if (use_saved) {
+        const size_t need_s = clr_saved_bytes(s);
+        if (need_s && (!saved || saved_bytes < need_s || ((uintptr_t)saved & (ALIGN - 1)))) return CLR_EWORKSPACE;
+    }
     const size_t need = clr_workspace_bytes(s, kind == K_KDA ? CLR_OP_KDA_BWD : gla ? CLR_OP_GLA_BWD : CLR_OP_GDN_BWD);
     hipStream_t st = (hipStream_t)stream;
     if (s->T == 0) return passthrough(dS_out, dS_in, nst, st);
@@ -421,6 +458,7 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
             return hip_status(launch_kda_bwd(L, st));
         }
         L.ws = carve_gdn(s, true, (char*)ws, nullptr);
+        if (use_saved) saved_carve(s, (char*)saved, &L.saved_h, &L.saved_U);
         return hip_status(launch_gdn_bwd(L, st));
     } else {
         GlaLaunch L{};
@@ -440,6 +478,14 @@ int gdn_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v, c
             void* stream) {
     return bwd_common(K_GDN, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
                       ws_bytes, stream);
+}
+
+int gdn_bwd_saved(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* S_in, const void* dO, const float* dS_out, const void* saved,
+                  size_t saved_bytes, void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dS_in, void* ws,
+                  size_t ws_bytes, void* stream) {
+    return bwd_common(K_GDN, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws, ws_bytes,
+                      stream, saved, saved_bytes, /*use_saved=*/true);
 }
 
 int kda_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,

@@ -74,6 +74,12 @@ struct GdnLaunch {
     float* dS_in;
     GdnWs ws;
     bool no_split = false;  // never take the two-stream split forward
+    // saved forward activations (Gated DeltaNet): per block the entering state
+    // in the backward's layout (tiled h[d][v]) and U^T (tiled), both in the
+    // element type.  The forward writes them; the backward reads them in place
+    // of its forward recompute.  Null: not saved / recompute.
+    void* saved_h = nullptr;
+    void* saved_U = nullptr;
 };
 
 template <typename E> struct GdnPrepArgs {
@@ -111,6 +117,9 @@ template <typename E> struct GdnScanArgs {
     E* Utok = nullptr;
     int T = 0;
     const E* KhT_lo = nullptr;
+    // Gated DeltaNet forward that saves its states for the backward: the state
+    // entering each block also in the backward's layout (tiled h[d][v])
+    E* hN = nullptr;
 };
 
 template <typename E> struct GdnOutArgs {

@@ -25,10 +25,16 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     sb.dh_lo = (E*)ws.dhT_lo;
     const int G = (int)scan_grid(DV / 16, L.B * L.H);
     constexpr int NCW = scan_can_split<E, DK>() ? 2 : 1, NP = scan_np_fast<NCW>;
-    launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV, false, NP, NCW>, dim3(2 * G),
-           dim3(scan_threads<NP, NCW>), st, sa, sb, G);
+    const bool saved = L.saved_h != nullptr;
+    if (saved)  // the forward's states and U are read below: the reverse scan alone
+        launch("gdn_scan_rev", gdn_scan_rev_kernel<E, DK, DV, false, NP, NCW>, dim3(G),
+               dim3(scan_threads<NP, NCW>), st, sb);
+    else
+        launch("gdn_scan_pair", gdn_scan_pair_kernel<E, DK, DV, false, NP, NCW>, dim3(2 * G),
+               dim3(scan_threads<NP, NCW>), st, sa, sb, G);
     GdnIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.beta, (const E*)L.dO,
-                       ws.gam, (const E*)ws.hT, (const E*)ws.dhT, (const E*)ws.UT, (const float*)ws.dUT,
+                       ws.gam, (const E*)(saved ? L.saved_h : ws.hT), (const E*)ws.dhT,
+                       (const E*)(saved ? L.saved_U : ws.UT), (const float*)ws.dUT,
                        (const E*)ws.TT,
                        (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, (E*)L.dbeta, L.T, L.H, L.NC};
     ia.dh_lo = (const E*)ws.dhT_lo;

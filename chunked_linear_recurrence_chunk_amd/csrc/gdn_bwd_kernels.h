@@ -343,6 +343,14 @@ __global__ __launch_bounds__((scan_threads<NP, NCW>)) void gdn_scan_pair_kernel(
     else gdn_scan_bwd_body<E, DK, DV, PCD, NP, NCW>(ba, blockIdx.x - G, smem);
 }
 
+// The reverse scan alone, for a backward that reads the states and U the
+// forward saved instead of recomputing them.
+template <typename E, int DK, int DV, bool PCD = false, int NP = NPROD, int NCW = 1>
+__global__ __launch_bounds__((scan_threads<NP, NCW>)) void gdn_scan_rev_kernel(GdnScanBwdArgs<E> ba) {
+    __shared__ __align__(16) char smem[ScanBwdGeom<E, DK, PCD, NCW>::LDS];
+    gdn_scan_bwd_body<E, DK, DV, PCD, NP, NCW>(ba, blockIdx.x, smem);
+}
+
 // ---------------------------------------------------------------------------
 // intra: one work-group (8 waves) per (block, head, batch).  Waves w and
 // w + 4 own the 16 tokens 16w..16w+15 of the block, both as "t" (rows of dQ)

@@ -19,7 +19,8 @@ struct GdnFwdStages {
     }
     void scan(int n0, int n1, const float* S_in, float* S_out, hipStream_t st) const {
         GdnScanArgs<E> sa{L.ws.eg, (const E*)L.ws.W, (const E*)L.ws.KhT, (const E*)L.ws.UtT, S_in, S_out,
-                          (E*)L.ws.hT, (E*)L.ws.UT, L.H, L.NC, L.B * L.H};
+                          (E*)L.ws.hT, L.saved_U ? L.saved_U : L.ws.UT, L.H, L.NC, L.B * L.H};
+        sa.hN = (E*)L.saved_h;
         sa.n0 = n0;
         sa.n1 = n1;
         if (scan_bv() == 32 && DV % 32 == 0) {
@@ -34,8 +35,8 @@ struct GdnFwdStages {
         }
     }
     void out(int n0, int n1, hipStream_t st) const {
-        GdnOutArgs<E> oa{(const E*)L.q, (const E*)L.k, L.ws.gam, (const E*)L.ws.hT, (const E*)L.ws.UT, (E*)L.o,
-                         L.T, L.H, L.NC};
+        GdnOutArgs<E> oa{(const E*)L.q, (const E*)L.k, L.ws.gam, (const E*)L.ws.hT,
+                         (const E*)(L.saved_U ? L.saved_U : L.ws.UT), (E*)L.o, L.T, L.H, L.NC};
         oa.n0 = n0;
         launch("gdn_out", gdn_out_kernel<E, DK, DV>, dim3(n1 - n0, L.H, L.B), dim3(256), st, oa);
     }

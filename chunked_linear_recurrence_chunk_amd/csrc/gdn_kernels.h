@@ -617,7 +617,7 @@ __device__ __forceinline__ void consumers_exchange(f32x4 (&X)[4], f32x4* xch, in
     }
 }
 
-template <typename E, int DK, int DV, bool HNAT, int NU, bool PCD = false, int C = 0, int NCW = 1>
+template <typename E, int DK, int DV, bool HNAT, int NU, bool PCD = false, int C = 0, int NCW = 1, bool HTILE = false>
 __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>, NCW>& o, f32x4 (&S)[DK / 16 / NCW],
                                               const GdnScanArgs<E>& a, size_t chunk, int vb, int l, E* tile,
                                               const char* slot, f32x4* xch) {
@@ -638,6 +638,11 @@ __device__ __forceinline__ void scan_fwd_step(ScanFwdOps<E, DK, ScanWsT<PCD, E>,
             for (int kk = 0; kk < KKC; ++kk) st8T(hT, vb * KK + C * KKC + kk, l, S[2 * kk], S[2 * kk + 1]);
         }
     }
+    // a forward that saves its states: the same state operand also in the
+    // backward's layout (the values the backward's recompute stores), through
+    // the wave's LDS tile where the work-group has one (HTILE)
+    if (a.hN) state_store<E, DK, DV, HTILE, C, NCW>(a.hN + chunk * DK * DV, fs, tile, 16 * vb, l);
+
     // -U = W S - Ut, accumulated onto the stored -Ut  (tiles: rows t = 16tb + 4g + i, col v0 + r);
     // with two consumers each forms W S over its key half, the first onto -Ut
     f32x4 U[4];
@@ -770,7 +775,9 @@ template <typename E, int DK, int DV, bool HNAT, bool PCD = false, int NCW_ = 1,
     static constexpr int SLOT = RingGeom<NU>::SLOT;
     // the state-store tile (KDA stores the state without one, and stages its
     // token-major U in the slot: its slots need all of the LDS)
-    static constexpr int TILE = HNAT && !PCD ? state_tile_bytes(DK, sizeof(E)) : 16;
+    // (the Gated DeltaNet forward scan of one slice keeps one too, for the
+    // states a forward that saves its activations also stores in that layout)
+    static constexpr int TILE = (HNAT || (NVS == 1 && sizeof(E) == 2)) && !PCD ? state_tile_bytes(DK, sizeof(E)) : 16;
     static_assert(BLK * 16 * (int)sizeof(E) <= NWU * RING_UNIT, "U staging fits the W units");
     static constexpr int NCW = NCW_;
     static_assert(NCW == 1 || (NCW == 2 && scan_can_split<E, DK>()), "consumer split");
@@ -802,7 +809,8 @@ __device__ __forceinline__ void gdn_scan_fwd_consume(const GdnScanArgs<E>& a, co
         ScanFwdOps<E, DK, UT_, NCW> o;
         const char* slot = ring + (n % P) * G::SLOT;
         scan_fwd_from_ring<E, DK, NU, UT_, key_parts<PCD, E>(), C, NCW>(o, slot, l, s);
-        scan_fwd_step<E, DK, DV, HNAT, NU, PCD, C, NCW>(o, S, a, bh * a.NC + n0 + n, vb, l, tile, slot, xch);
+        constexpr bool HTILE = !HNAT && NVS == 1 && !PCD && sizeof(E) == 2;  // the tile ScanFwdGeom keeps
+        scan_fwd_step<E, DK, DV, HNAT, NU, PCD, C, NCW, HTILE>(o, S, a, bh * a.NC + n0 + n, vb, l, tile, slot, xch);
         ring_barrier();
     }
     if (a.S_out) {

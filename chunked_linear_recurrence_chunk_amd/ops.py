@@ -66,6 +66,13 @@ def load(path: Optional[str] = None):
         f.restype = i
     lib.gdn_fwd_noalloc.argtypes = [sp] + [vp] * 9
     lib.gdn_fwd_noalloc.restype = i
+    if hasattr(lib, "gdn_fwd_save"):  # saved-activation pair (absent from older builds)
+        lib.clr_saved_bytes.argtypes = [sp]
+        lib.clr_saved_bytes.restype = sz
+        lib.gdn_fwd_save.argtypes = [sp] + [vp] * 9 + [sz, vp, sz, vp]
+        lib.gdn_fwd_save.restype = i
+        lib.gdn_bwd_saved.argtypes = [sp] + [vp] * 9 + [sz] + [vp] * 7 + [sz, vp]
+        lib.gdn_bwd_saved.restype = i
     for name in ("gdn_bwd", "gla_bwd", "mamba2_bwd", "kda_bwd"):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 15 + [sz, vp]
@@ -298,6 +305,65 @@ def gdn_fwd_noalloc(q, k, v, g, beta, S_in=None, o=None, S_out=None):
                                 _ptr(S_in), _ptr(o), _ptr(S_out), _stream())
     _check("gdn_fwd_noalloc", rc)
     return o, S_out
+
+
+def saved_bytes(shape: ClrShape) -> int:
+    """clr_saved_bytes: bytes of one Gated DeltaNet chunk call's saved
+    activations (the states entering its blocks and their U)."""
+    return int(load().clr_saved_bytes(ctypes.byref(shape)))
+
+
+def gdn_fwd_save(q, k, v, g, beta, S_in=None, saved=None, ws=None, o=None, S_out=None):
+    """gdn_fwd that also keeps the activations the backward needs (gdn_fwd_save):
+    returns (o, S_out, saved), ``saved`` a uint8 device tensor to hand to
+    gdn_bwd_saved for the same chunk (allocated here unless given)."""
+    import torch
+    _validate("gdn", q, k, v, g, beta, S_in)
+    _check_inputs(q, k, v, g, beta, S_in)
+    shape = make_shape(q, v)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = _out(o, (B, T, H, dv), q.dtype, q.device)
+    S_out = _out(S_out, (B, H, dk, dv), torch.float32, q.device)
+    ns = saved_bytes(shape)
+    if saved is None:
+        saved = torch.empty(max(ns, 256), dtype=torch.uint8, device=q.device)
+    if ws is None:
+        ws, n = _workspace(shape, OP_GDN_FWD, q.device)
+    else:
+        n = ws.numel()
+    rc = load().gdn_fwd_save(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S_in),
+                             _ptr(o), _ptr(S_out), _ptr(saved), saved.numel(), _ptr(ws), n, _stream())
+    _check("gdn_fwd_save", rc)
+    return o, S_out, saved
+
+
+def gdn_bwd_saved(q, k, v, g, beta, S_in, dO, dS_out, saved, ws=None, out=None):
+    """gdn_bwd reading the activations gdn_fwd_save kept for this chunk instead
+    of recomputing the forward (S_in is not read and may be None).  Returns
+    dict dq, dk, dv, dg, dbeta, dS_in."""
+    import torch
+    _validate("gdn", q, k, v, g, beta, S_in, dO, dS_out)
+    _check_inputs(q, k, v, g, beta, S_in, dO, dS_out, saved)
+    shape = make_shape(q, v)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    out = out or {}
+    dq = _out(out.get("dq"), q.shape, q.dtype, q.device)
+    dk_ = _out(out.get("dk"), k.shape, k.dtype, k.device)
+    dv_ = _out(out.get("dv"), v.shape, v.dtype, v.device)
+    dg = _out(out.get("dg"), g.shape, g.dtype, g.device)
+    dbeta = _out(out.get("dbeta"), beta.shape, beta.dtype, beta.device)
+    dS_in = _out(out.get("dS_in"), (B, H, dk, dv), torch.float32, q.device)
+    if ws is None:
+        ws, n = _workspace(shape, OP_GDN_BWD, q.device)
+    else:
+        n = ws.numel()
+    rc = load().gdn_bwd_saved(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S_in),
+                              _ptr(dO), _ptr(dS_out), _ptr(saved), saved.numel(), _ptr(dq), _ptr(dk_), _ptr(dv_),
+                              _ptr(dg), _ptr(dbeta), _ptr(dS_in), _ptr(ws), n, _stream())
+    _check("gdn_bwd_saved", rc)
+    return dict(dq=dq, dk=dk_, dv=dv_, dg=dg, dbeta=dbeta, dS_in=dS_in)
 
 
 def gla_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None, check_range=False):

@@ -31,12 +31,18 @@ def _sl(t, a, b):
 
 
 class GdnChunked:
-    """Forward/backward of one Gated DeltaNet layer over N sequence chunks."""
+    """Forward/backward of one Gated DeltaNet layer over N sequence chunks.
+
+    With ``save=True`` (Gated DeltaNet only) each chunk's forward also keeps
+    the activations its backward needs (gdn_fwd_save), and the backward reads
+    them (gdn_bwd_saved) instead of recomputing the chunk's forward from S^in:
+    more device memory (clr_saved_bytes per chunk until its backward), less
+    work."""
 
     kind = "gdn"
     _names = ("gdn_fwd", "gdn_bwd", "OP_GDN_FWD", "OP_GDN_BWD")
 
-    def __init__(self, q, k, v, g, beta, N: int):
+    def __init__(self, q, k, v, g, beta, N: int, save: bool = False):
         from . import ops
         self.ops = ops
         self.q, self.k, self.v, self.g, self.beta = q, k, v, g, beta
@@ -52,6 +58,10 @@ class GdnChunked:
         nbytes = max(ops.workspace_bytes(shape, getattr(ops, op_f)), ops.workspace_bytes(shape, getattr(ops, op_b)))
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         self.saved = [None] * N
+        if save and self.kind != "gdn":
+            raise ValueError("saved activations exist for the Gated DeltaNet layer only")
+        self.save = save
+        self.acts = [None] * N  # per chunk: the activations gdn_fwd_save kept
 
     def _chunk(self, i):
         a, b = self.bounds[i]
@@ -69,7 +79,11 @@ class GdnChunked:
             a, b = self.bounds[i]
             self.saved[i] = S
             view = o[:, a:b]
-            oi, S = self._fwd(*self._chunk(i), S, ws=self.ws, o=view if view.is_contiguous() else None)
+            ov = view if view.is_contiguous() else None
+            if self.save:
+                oi, S, self.acts[i] = self.ops.gdn_fwd_save(*self._chunk(i), S, ws=self.ws, o=ov)
+            else:
+                oi, S = self._fwd(*self._chunk(i), S, ws=self.ws, o=ov)
             if oi.data_ptr() != view.data_ptr():
                 view.copy_(oi)
         return o, S
@@ -86,7 +100,12 @@ class GdnChunked:
             a, b = self.bounds[i]
             views = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg", "dbeta")}
             out = {key: t for key, t in views.items() if t.is_contiguous()}
-            r = self._bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
+            if self.save:
+                r = self.ops.gdn_bwd_saved(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, self.acts[i],
+                                           ws=self.ws, out=out)
+                self.acts[i] = None
+            else:
+                r = self._bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
             for key, t in views.items():
                 if r[key].data_ptr() != t.data_ptr():
                     t.copy_(r[key])

@@ -133,6 +133,36 @@ int gdn_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* 
             const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
             float* dS_in, void* ws, size_t ws_bytes, void* stream);
 
+/* Gated DeltaNet forward and backward with saved activations.  The backward
+ * needs the state entering every 64-token block and the block's U (the
+ * delta-rule values, U = T Diag(beta) (V - Diag(Gam) K S)).  gdn_bwd
+ * recomputes them from S_in; the pair below keeps them instead, as the
+ * StateFlow paper's chunk backward may (Sec. 3.1, "Backward Computation":
+ * the chunk's intermediate activations are either kept from the forward or
+ * recomputed from its boundary state).
+ *   clr_saved_bytes(shape): bytes of one chunk call's saved activations, for
+ *     the shapes gdn_bwd supports (0 otherwise, and 0 when T == 0): per
+ *     64-token block dk x dv states and 64 x dv values, in shape.dtype.
+ *   gdn_fwd_save: gdn_fwd (same results, bit for bit) that also writes them
+ *     into `saved` (device memory of at least clr_saved_bytes, 256-byte
+ *     aligned, owned by the caller; its layout is the library's).  Its
+ *     workspace is CLR_OP_GDN_FWD's.
+ *   gdn_bwd_saved: gdn_bwd (same results, bit for bit) that reads `saved`, as
+ *     the gdn_fwd_save of the same chunk (same shape and inputs) left it, in
+ *     place of recomputing the forward; S_in is not read (it may be NULL).
+ *     Its workspace is CLR_OP_GDN_BWD's.
+ * Both return CLR_EWORKSPACE for a missing, small or misaligned `saved`, and
+ * CLR_EINVAL when it overlaps another buffer (an output, for gdn_fwd_save). */
+size_t clr_saved_bytes(const clr_shape_t* shape);
+int gdn_fwd_save(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+                 const void* g, const void* beta, const float* S_in, void* o, float* S_out,
+                 void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+int gdn_bwd_saved(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+                  const void* g, const void* beta, const float* S_in, const void* dO,
+                  const float* dS_out, const void* saved, size_t saved_bytes, void* dq, void* dk,
+                  void* dv, void* dg, void* dbeta, float* dS_in, void* ws, size_t ws_bytes,
+                  void* stream);
+
 /* Allocation-free Gated DeltaNet forward, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation).  Same operation, arguments, layouts and results as

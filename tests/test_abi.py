@@ -313,3 +313,40 @@ def test_shape_chunk_field_and_unsupported_sizes():
     assert ops.workspace_bytes(_shape(ops, dk=128, dv=128, dtype=0), ops.OP_GDN_BWD) == 0
     for d in (32, 64):
         assert ops.workspace_bytes(_shape(ops, dk=d, dv=d, dtype=0), ops.OP_GDN_BWD) > 0
+
+
+def test_saved_activation_entry_points_reject_on_the_host():
+    ops, lib = _lib()
+    s = _shape(ops, T=64, H=1, dk=32, dv=32)
+    n = ops.saved_bytes(s)
+    # one 64-token block: a 32 x 32 state and 64 x 32 values, bf16, 256-byte aligned parts
+    assert n == 2048 + 4096
+    assert ops.saved_bytes(_shape(ops, T=0)) == 0
+    assert ops.saved_bytes(_shape(ops, dk=128, dv=128, dtype=0)) == 0   # no fp32 backward at d = 128
+    assert ops.saved_bytes(_shape(ops, dk=96, dv=96)) == 0
+    P_ = _fake
+    # fwd: q k v g beta S_in o S_out | saved, nsaved | ws, nws
+    base = [P_(0x10000), P_(0x20000), P_(0x30000), P_(0x40000), P_(0x50000), None, P_(0x60000), P_(0x70000)]
+
+    def fwd(saved, nsaved, ws=0x100000, nws=1 << 40):
+        return lib.gdn_fwd_save(ctypes.byref(s), *base, None if saved is None else P_(saved), nsaved,
+                                None if ws is None else P_(ws), nws, None)
+    assert fwd(None, 0) == ops.CLR_EWORKSPACE                    # no saved buffer
+    assert fwd(0xA0000, n - 256) == ops.CLR_EWORKSPACE           # too small
+    assert fwd(0xA0010, n) == ops.CLR_EWORKSPACE                 # misaligned
+    assert fwd(0x60000, n) == ops.CLR_EINVAL                     # overlaps the output o
+    assert fwd(0xFF000, n) == ops.CLR_EINVAL                     # overlaps the workspace
+    assert fwd(0xA0000, n, ws=None) == ops.CLR_EWORKSPACE        # no workspace
+    # bwd: q k v g beta S_in dO dS_out | saved, nsaved | dq dk dv dg dbeta dS_in | ws, nws
+    outs = [P_(0x80000 + 0x10000 * i) for i in range(6)]
+
+    def bwd(saved, nsaved, o=outs):
+        return lib.gdn_bwd_saved(ctypes.byref(s), *base[:6], P_(0x60000), P_(0x70000),
+                                 None if saved is None else P_(saved), nsaved, *o, P_(0x100000), 1 << 40, None)
+    assert bwd(None, 0) == ops.CLR_EWORKSPACE
+    assert bwd(0xF0000, n - 256) == ops.CLR_EWORKSPACE
+    assert bwd(0xF0010, n) == ops.CLR_EWORKSPACE
+    assert bwd(0x80000, n) == ops.CLR_EINVAL                     # overlaps the output dq
+    bad = list(outs)
+    bad[0] = None
+    assert bwd(0xF0000, n, bad) == ops.CLR_EINVAL                # dq missing
