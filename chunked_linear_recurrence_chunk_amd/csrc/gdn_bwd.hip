@@ -17,6 +17,12 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     pa.Kh = (E*)ws.Kh;
     pa.dvlT = (E*)ws.dvlT;
     pa.Rt = (E*)ws.Rt;
+    const bool saved = L.saved_h != nullptr;
+    if (saved) {  // no forward recompute: its operands are not needed
+        pa.W = nullptr;
+        pa.KhT = nullptr;
+        pa.UtT = nullptr;
+    }
     launch("gdn_prep_bwd", gdn_prep_kernel<E, DK, DV, true>, gblk, dim3(512), st, pa);
     GdnScanArgs<E> sa{ws.eg, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, nullptr,
                       (E*)ws.hT, (E*)ws.UT, L.H, L.NC, L.B * L.H};
@@ -25,7 +31,6 @@ hipError_t launch_gdn_bwd_t(const GdnLaunch& L, hipStream_t st) {
     sb.dh_lo = (E*)ws.dhT_lo;
     const int G = (int)scan_grid(DV / 16, L.B * L.H);
     constexpr int NCW = scan_can_split<E, DK>() ? 2 : 1, NP = scan_np_fast<NCW>;
-    const bool saved = L.saved_h != nullptr;
     if (saved)  // the forward's states and U are read below: the reverse scan alone
         launch("gdn_scan_rev", gdn_scan_rev_kernel<E, DK, DV, false, NP, NCW>, dim3(G),
                dim3(scan_threads<NP, NCW>), st, sb);

@@ -321,13 +321,15 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), tw[j]);
-        st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
+        if (a.W) st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
         if constexpr (BWD) st4(Ws + (16 * tb + r) * PK + 16 * db + 4 * g, acc);
     }
     // Ut[t][v] = sum_s (T Diag(beta))[t][s] V[s][v]  -> stored negated as fp32 -Ut^T[v][t]
     // (tiled), so that the scan forms -U = W S - Ut by accumulating onto it
+    // (the forward scan's operands W, Ut and K^T are not written for a
+    // backward that reads saved states: a null W, UtT, KhT)
     float* Uout = a.UtT + chunk * BLK * DV;
-    {
+    if (a.UtT) {
         const Frag2<E> tu[2] = {tfrag(16 * tbw + r, 0, s_bet), tfrag(16 * tbw + r, 32, s_bet)};
 #pragma unroll
         for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
@@ -342,8 +344,10 @@ __global__ __launch_bounds__(512) void gdn_prep_kernel(GdnPrepArgs<E> a) {
     // 32j.., columns 16db..  (the decay exp(gamma_C - gamma_t) is applied to U
     // in the scan, so the keys are stored exactly)
     E* KTout = a.KhT + chunk * BLK * DK;
+    if (a.KhT) {
 #pragma unroll
-    for (int f = w8; f < 2 * ND; f += 8) st_fragT(KTout, f, l, ldfrag_tr(Ks, PK, 32 * (f & 1), 16 * (f >> 1), l));
+        for (int f = w8; f < 2 * ND; f += 8) st_fragT(KTout, f, l, ldfrag_tr(Ks, PK, 32 * (f & 1), 16 * (f >> 1), l));
+    }
     if constexpr (BWD) {
         static_assert(Lay::BWD_FITS, "Q where V was, W where Am was, dO where T1, T2 were");
         constexpr int PQ = PK, PO = PV, NVB = DV / 16;
