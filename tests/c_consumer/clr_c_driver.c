@@ -21,6 +21,11 @@
  *            as float32.
  *       Exit 0 on success; on a library or HIP error, the status text on
  *       stderr and exit 2.
+ *
+ *   clr_c_driver run-saved IN OUT
+ *       The same chain with gdn_fwd_save / gdn_bwd_saved: each chunk's
+ *       forward keeps its activations in a buffer of clr_saved_bytes, which
+ *       that chunk's backward reads instead of recomputing them.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -136,7 +141,7 @@ static int run_checks(void) {
 static int read_all(FILE* f, void* p, size_t n) { return fread(p, 1, n, f) == n ? 0 : 1; }
 static int write_all(FILE* f, const void* p, size_t n) { return fwrite(p, 1, n, f) == n ? 0 : 1; }
 
-static int run_chain(const char* in_path, const char* out_path) {
+static int run_chain(const char* in_path, const char* out_path, int save) {
     FILE* f = fopen(in_path, "rb");
     if (!f) {
         perror(in_path);
@@ -197,23 +202,36 @@ static int run_chain(const char* in_path, const char* out_path) {
     if (wsz == 0) return fail("clr_workspace_bytes", CLR_EINVAL);
     void* ws;
     HIPCHK(hipMalloc(&ws, wsz));
+    /* saved activations: one buffer per chunk, each held until that chunk's backward */
+    const size_t nsv = save ? clr_saved_bytes(&sh) : 0;
+    if (save && nsv == 0) return fail("clr_saved_bytes", CLR_ENOTSUP);
+    char* sv = NULL;
+    if (save) HIPCHK(hipMalloc((void**)&sv, (size_t)N * nsv));
 
     /* byte offset of chunk i in a [1, T, H, d] tensor */
 #define OFF(base, i, d_) ((char*)(base) + (size_t)(i) * L * H * (d_) * es)
     for (int i = 0; i < N; ++i) {
-        const int s = gdn_fwd(&sh, OFF(d[0], i, DK), OFF(d[1], i, DK), OFF(d[2], i, DV), OFF(d[3], i, 1),
-                              OFF(d[4], i, 1), S + (size_t)i * ns, OFF(od[0], i, DV), S + (size_t)(i + 1) * ns, ws,
-                              wsz, st);
-        if (s != CLR_OK) return fail("gdn_fwd", s);
+        const int s = save ? gdn_fwd_save(&sh, OFF(d[0], i, DK), OFF(d[1], i, DK), OFF(d[2], i, DV), OFF(d[3], i, 1),
+                                          OFF(d[4], i, 1), S + (size_t)i * ns, OFF(od[0], i, DV),
+                                          S + (size_t)(i + 1) * ns, sv + (size_t)i * nsv, nsv, ws, wsz, st)
+                           : gdn_fwd(&sh, OFF(d[0], i, DK), OFF(d[1], i, DK), OFF(d[2], i, DV), OFF(d[3], i, 1),
+                                     OFF(d[4], i, 1), S + (size_t)i * ns, OFF(od[0], i, DV),
+                                     S + (size_t)(i + 1) * ns, ws, wsz, st);
+        if (s != CLR_OK) return fail(save ? "gdn_fwd_save" : "gdn_fwd", s);
     }
     HIPCHK(hipMemcpyAsync(dS[N & 1], d[7], ns * 4, hipMemcpyDeviceToDevice, st));
     for (int i = N - 1; i >= 0; --i) {
         /* dS[(i + 1) & 1] holds dS_{i+1}^in = dS_i^out; the call writes dS_i^in */
-        const int s = gdn_bwd(&sh, OFF(d[0], i, DK), OFF(d[1], i, DK), OFF(d[2], i, DV), OFF(d[3], i, 1),
-                              OFF(d[4], i, 1), S + (size_t)i * ns, OFF(d[5], i, DV), dS[(i + 1) & 1],
-                              OFF(od[1], i, DK), OFF(od[2], i, DK), OFF(od[3], i, DV), OFF(od[4], i, 1),
-                              OFF(od[5], i, 1), dS[i & 1], ws, wsz, st);
-        if (s != CLR_OK) return fail("gdn_bwd", s);
+        const int s =
+            save ? gdn_bwd_saved(&sh, OFF(d[0], i, DK), OFF(d[1], i, DK), OFF(d[2], i, DV), OFF(d[3], i, 1),
+                                 OFF(d[4], i, 1), NULL, OFF(d[5], i, DV), dS[(i + 1) & 1], sv + (size_t)i * nsv, nsv,
+                                 OFF(od[1], i, DK), OFF(od[2], i, DK), OFF(od[3], i, DV), OFF(od[4], i, 1),
+                                 OFF(od[5], i, 1), dS[i & 1], ws, wsz, st)
+                 : gdn_bwd(&sh, OFF(d[0], i, DK), OFF(d[1], i, DK), OFF(d[2], i, DV), OFF(d[3], i, 1),
+                           OFF(d[4], i, 1), S + (size_t)i * ns, OFF(d[5], i, DV), dS[(i + 1) & 1],
+                           OFF(od[1], i, DK), OFF(od[2], i, DK), OFF(od[3], i, DV), OFF(od[4], i, 1),
+                           OFF(od[5], i, 1), dS[i & 1], ws, wsz, st);
+        if (s != CLR_OK) return fail(save ? "gdn_bwd_saved" : "gdn_bwd", s);
     }
 #undef OFF
     HIPCHK(hipStreamSynchronize(st));
@@ -253,13 +271,15 @@ static int run_chain(const char* in_path, const char* out_path) {
     HIPCHK(hipFree(dS[0]));
     HIPCHK(hipFree(dS[1]));
     HIPCHK(hipFree(ws));
+    if (sv) HIPCHK(hipFree(sv));
     HIPCHK(hipStreamDestroy(st));
     return 0;
 }
 
 int main(int argc, char** argv) {
     if (argc == 2 && !strcmp(argv[1], "check")) return run_checks();
-    if (argc == 4 && !strcmp(argv[1], "run")) return run_chain(argv[2], argv[3]);
-    fprintf(stderr, "usage: %s check | run IN OUT\n", argv[0]);
+    if (argc == 4 && !strcmp(argv[1], "run")) return run_chain(argv[2], argv[3], 0);
+    if (argc == 4 && !strcmp(argv[1], "run-saved")) return run_chain(argv[2], argv[3], 1);
+    fprintf(stderr, "usage: %s check | run IN OUT | run-saved IN OUT\n", argv[0]);
     return 64;
 }

@@ -4,9 +4,11 @@ PyTorch, no C++, only include/clr.h and the HIP runtime API.
 CPU: the program compiles as C11 against the public header and the library,
 and every host-side rejection it exercises returns the documented status.
 GPU: it runs one Gated DeltaNet layer over N sequence chunks in the StateFlow
-order (StateFlow paper, Sec. 3.1, Eqs. 5 and 7) on its own device buffers;
-its outputs match the fp64 oracle within the tolerances, and equal bit for
-bit what the Python binding's chunk driver returns for the same inputs.
+order (StateFlow paper, Sec. 3.1, Eqs. 5 and 7) on its own device buffers,
+recomputing each chunk's forward in its backward and, in a second run,
+keeping the activations instead (gdn_fwd_save / gdn_bwd_saved); its outputs
+match the fp64 oracle within the tolerances, and equal bit for bit what the
+Python binding's chunk driver returns for the same inputs in the same mode.
 """
 import os
 import subprocess
@@ -109,3 +111,20 @@ def test_c_program_chunk_chain_matches_oracle_and_binding(case, tmp_path):
     for key in ref:
         a = py[key].float().cpu().numpy()
         assert np.array_equal(a, got[key].astype(np.float32)), key
+
+    # and with saved activations (gdn_fwd_save / gdn_bwd_saved), against the
+    # oracle and the binding's chunk driver in the same mode
+    fsv = os.path.join(tmp_path, "out_saved.bin")
+    p = subprocess.run([_driver(), "run-saved", fin, fsv], capture_output=True, text=True, timeout=120)
+    assert p.returncode == 0, p.stderr
+    got_s = _read_outputs(fsv, B, T, H, dk, dv, dtype)
+    for key, r in ref.items():
+        e = rel_err(got_s[key], r)
+        assert e < tol(dtype, key), (key, e)
+    drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N, save=True)
+    o, S = drv.forward(to_dev(x["S_in"], "fp32"))
+    gr = drv.backward(d["dO"], to_dev(x["dS_out"], "fp32"))
+    torch.cuda.synchronize()
+    py = dict(o=o, S_out=S, **gr)
+    for key in ref:
+        assert np.array_equal(py[key].float().cpu().numpy(), got_s[key].astype(np.float32)), key
