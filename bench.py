@@ -649,7 +649,9 @@ def main():
                       if conv else
                       {"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "H": cfg["H"], "dk": cfg["dk"],
                        "dv": cfg["dv"], "seq_chunks": N, "block": 64,
-                       "scan_bv": ops.get_scan_bv(), "fwd_split_permille": ops.get_fwd_split()}),
+                       "scan_bv": ops.get_scan_bv(), "fwd_split_permille": ops.get_fwd_split(),
+                       "backward": "saved activations" if args.saved and cfg["kind"] == "gdn"
+                       else "recompute from S_in"}),
            "mfma_util": mfma_util,
            "peak_mem_gb": round(torch.cuda.max_memory_allocated() / 1e9, 3),
            "roofline": roofline, "phases": phases, "kernels": kernels}
