@@ -147,10 +147,15 @@ int gdn_bwd(const clr_shape_t* shape, const void* q, const void* k, const void* 
  *     into `saved` (device memory of at least clr_saved_bytes, 256-byte
  *     aligned, owned by the caller; its layout is the library's).  Its
  *     workspace is CLR_OP_GDN_FWD's.
- *   gdn_bwd_saved: gdn_bwd (same results, bit for bit) that reads `saved`, as
- *     the gdn_fwd_save of the same chunk (same shape and inputs) left it, in
+ *   gdn_bwd_saved: the operation of gdn_bwd, reading `saved`, as the
+ *     gdn_fwd_save of the same chunk (same shape and inputs) left it, in
  *     place of recomputing the forward; S_in is not read (it may be NULL).
- *     Its workspace is CLR_OP_GDN_BWD's.
+ *     Its results equal gdn_bwd's bit for bit where gdn_bwd's recompute
+ *     runs one wave per state slice (float32, and d = 32) and to rounding
+ *     otherwise (bf16 at d >= 64, where that recompute sums each block's
+ *     products over two halves of the key dimension: the states it gets
+ *     differ from the forward's in their last bits).  Its workspace is
+ *     CLR_OP_GDN_BWD's.
  * Both return CLR_EWORKSPACE for a missing, small or misaligned `saved`, and
  * CLR_EINVAL when it overlaps another buffer (an output, for gdn_fwd_save). */
 size_t clr_saved_bytes(const clr_shape_t* shape);
