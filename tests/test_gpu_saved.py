@@ -111,3 +111,36 @@ def test_saved_buffer_reused_for_a_second_chunk():
     assert torch.equal(o, outs[1][0])
     for key in g:
         assert torch.equal(g[key], outs[1][1][key]), key
+
+
+STRESS = [
+    # (T, H, d, dtype, N, gate, seed): the delta-rule stress input (almost no
+    # decay, beta = 0.99, keys repeated from 8 L2-normalised vectors)
+    (256, 2, 32, "fp32", 4, "slow", 321),
+    (2048, 4, 128, "bf16", 1, "zero", 322),
+    (8192, 4, 128, "bf16", 4, "slow", 323),
+]
+
+
+@pytest.mark.parametrize("case", STRESS, ids=[f"T{c[0]}H{c[1]}d{c[2]}-{c[3]}-N{c[4]}-{c[5]}" for c in STRESS])
+def test_saved_stress_matches_oracle(case):
+    import torch
+    from chunked_linear_recurrence_chunk_amd import inputs, stateflow
+    from oracle import oracle
+    T, H, d, dtype, N, gate, seed = case
+    print(f"[gdn saved] stress {case}", flush=True)
+    x = inputs.make_delta_stress("gdn", 1, T, H, d, d, dtype, seed, gate=gate)
+    dv, S_in, dS = _dev(x, dtype)
+    drv = stateflow.GdnChunked(dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"], N, save=True)
+    o, S = drv.forward(S_in)
+    gr = drv.backward(dv["dO"], dS)
+    torch.cuda.synchronize()
+    got = dict(o=o, S_out=S, **gr)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["S_in"])
+    o_ref, S_ref = oracle.gdn_fwd(*args)
+    ref = oracle.gdn_bwd(*args, x["dO"], x["dS_out"])
+    ref.update(o=o_ref, S_out=S_ref)
+    errs = {key: rel_err(to_np(got[key]), r) for key, r in ref.items()}
+    print("  errors", {key: f"{e:.2e}" for key, e in errs.items()}, flush=True)
+    bad = {key: e for key, e in errs.items() if not e < tol(dtype, key)}
+    assert not bad, bad
