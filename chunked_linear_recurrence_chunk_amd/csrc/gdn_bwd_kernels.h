@@ -454,6 +454,11 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
 
     const int tw = 16 * w + r;  // this lane's token as the column of transposed tiles
     const float gam_tw = s_gam[tw];
+    // Operand fragments that are exactly zero by structure, so their products
+    // are left out (the wave's token block w is the same for all its lanes):
+    // column tw of the lower-triangular T has no entries in rows 0..31 when
+    // w >= 2; the dPm^T tiles sb > w and the dPm tiles tb < w are zero.
+    const bool lo_half = __builtin_amdgcn_readfirstlane(w < 2 ? 1 : 0);
     const float gC = s_gam[BLK - 1];
     Frag<E> fdo[KV];
     Frag<E> fU[KV];
@@ -569,11 +574,13 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             const f32x4 qv = ld4(Qs + tw * PK + 16 * db + 4 * g);
             qdq += qv[0] * acc[0] + qv[1] * acc[1] + qv[2] * acc[2] + qv[3] * acc[3];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma2(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fpt[j]);
+            for (int j = 0; j < 2; ++j)
+                if (j == 0 || !lo_half) mma2(acc, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fpt[j]);
             if (tw < nvalid) st4(a.dq + (tok0 + tw) * ldk + (size_t)h * DK + 16 * db + 4 * g, acc);
             f32x4 acck = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma2(acck, ldfrag_tr(Qs, PK, 32 * j, 16 * db, l), fpm[j]);
+            for (int j = 0; j < 2; ++j)
+                if (j == 1 || lo_half) mma2(acck, ldfrag_tr(Qs, PK, 32 * j, 16 * db, l), fpm[j]);
             const f32x4 kv = ld4(Ks + tw * PK + 16 * db + 4 * g);
             kdk += kv[0] * accb[0] + kv[1] * accb[1] + kv[2] * accb[2] + kv[3] * accb[3];
             dKT[jd] = acck + accb * ek;
@@ -675,7 +682,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
         for (int sb = 0; sb < 4; ++sb) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag(dTT + (16 * sb + r) * PT + 32 * j + 4 * g), ftt[j]);
+            for (int j = 0; j < 2; ++j)
+                if (j == 1 || lo_half) mma(acc, ldfrag(dTT + (16 * sb + r) * PT + 32 * j + 4 * g), ftt[j]);
             XT[sb] = acc;
         }
         Frag<E> fx[2];
@@ -689,7 +697,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             const f32x4 kkg = kkgt[cb >> 1];  // K K^T * G tile (w, cb)
             if (cb <= w) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) mma(acc, fx[j], ldfrag_tr(TT, PT, 32 * j, 16 * cb, l));  // T rows 16cb + r
+                // T rows 16cb + r; for cb <= 1 they have no entries in columns 32..63
+                for (int j = 0; j < (cb <= 1 ? 1 : 2); ++j) mma(acc, fx[j], ldfrag_tr(TT, PT, 32 * j, 16 * cb, l));
             }
             const int c = 16 * cb + r;
             const f32x4 gr = ld4_now(s_gam + 16 * w + 4 * g), br = ld4_now(s_bet + 16 * w + 4 * g);
@@ -722,8 +731,9 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                mma2(acc, ldfrag2(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g, dUTl + (16 * vb + r) * PT + 32 * j + 4 * g),
-                     ftt[j]);
+                if (j == 1 || lo_half)
+                    mma2(acc, ldfrag2(dUTs + (16 * vb + r) * PT + 32 * j + 4 * g, dUTl + (16 * vb + r) * PT + 32 * j + 4 * g),
+                         ftt[j]);
             const f32x4 vv = ld4(Vs + tw * PV + 16 * vb + 4 * g);
             dbv += vv[0] * acc[0] + vv[1] * acc[1] + vv[2] * acc[2] + vv[3] * acc[3];
             if (tw < nvalid) st4(a.dv + (tok0 + tw) * ldv + (size_t)h * DV + 16 * vb + 4 * g, acc * bet_tw);
@@ -742,7 +752,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_intra_kernel(GdnIntraArgs<E> a) {
             const int db = hf * NDH + jd;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mma(acc, ldfrag_tr(dWs, PK, 32 * j, 16 * db, l), ftt[j]);
+            for (int j = 0; j < 2; ++j)
+                if (j == 1 || lo_half) mma(acc, ldfrag_tr(dWs, PK, 32 * j, 16 * db, l), ftt[j]);
             f32x4 accm = zero4();
 #pragma unroll
             for (int j = 0; j < 2; ++j) mma(accm, ldfrag_tr(Ks, PK, 32 * j, 16 * db, l), fms[j]);
