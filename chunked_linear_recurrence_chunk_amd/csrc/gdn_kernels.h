@@ -563,27 +563,42 @@ __device__ __forceinline__ void store_state_sel(E* h, const Frag<E> (&fs)[DK / 3
 constexpr int state_tile_bytes(int dk, int es) { return 16 * (dk + 8) * es; }
 // With two consumers (C, NCW = 2) each writes and reads back the columns of
 // its own key range of the shared tile.
+// The two halves of that store, for a wave that writes the tile and another
+// that reads it back: the row writes of this consumer's key range ...
+template <int DK, int C = 0, int NCW = 1>
+__device__ __forceinline__ void state_tile_write(const Frag<bf16> (&fs)[DK / 32 / NCW], bf16* tile, int l) {
+    constexpr int PS = DK + 8, KKC = DK / 32 / NCW;
+    const int r = l & 15, g = l >> 4;
+#pragma unroll
+    for (int kk = 0; kk < KKC; ++kk) {
+        const bf16x8 v = fs[kk].v;
+        const int c0 = 32 * (C * KKC + kk);
+        *(bf16x4*)(tile + r * PS + c0 + 4 * g) = bf16x4{v[0], v[1], v[2], v[3]};
+        *(bf16x4*)(tile + r * PS + c0 + 16 + 4 * g) = bf16x4{v[4], v[5], v[6], v[7]};
+    }
+}
+// ... and the transposing reads and stores of key blocks [db0, db0 + NDB)
+// (any wave: the read's lane mapping is a wave's).
+template <int DK, int DV, int NDB>
+__device__ __forceinline__ void state_tile_readout(bf16* h, const bf16* tile, int db0, int v0, int l) {
+    constexpr int PS = DK + 8;
+    const int r = l & 15, g = l >> 4, j = (l >> 2) & 3, q = l & 3;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int d0 = 16 * (db0 + db);
+        const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + (4 * g + j) * PS + d0 + 4 * q));
+        *(bf16x4*)(h + toff<bf16>(d0 + r, v0 + 4 * g, DV)) = x;
+    }
+}
+
 template <typename E, int DK, int DV, int C = 0, int NCW = 1>
 __device__ __forceinline__ void store_state_tr(E* h, const Frag<E> (&fs)[DK / 32 / NCW], E* tile, int v0, int l) {
     if constexpr (sizeof(E) == 2) {
-        constexpr int PS = DK + 8, KKC = DK / 32 / NCW, NDC = DK / 16 / NCW;
-        const int r = l & 15, g = l >> 4, j = (l >> 2) & 3, q = l & 3;
-#pragma unroll
-        for (int kk = 0; kk < KKC; ++kk) {
-            const bf16x8 v = fs[kk].v;
-            const int c0 = 32 * (C * KKC + kk);
-            *(bf16x4*)(tile + r * PS + c0 + 4 * g) = bf16x4{v[0], v[1], v[2], v[3]};
-            *(bf16x4*)(tile + r * PS + c0 + 16 + 4 * g) = bf16x4{v[4], v[5], v[6], v[7]};
-        }
+        constexpr int NDC = DK / 16 / NCW;
+        state_tile_write<DK, C, NCW>(fs, tile, l);
         // LDS operations of one wave complete in order
         asm volatile("" ::: "memory");
-#pragma unroll
-        for (int db = 0; db < NDC; ++db) {
-            const int d0 = 16 * (C * NDC + db);
-            const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(tile + (4 * g + j) * PS + d0 + 4 * q));
-            *(bf16x4*)(h + toff<E>(d0 + r, v0 + 4 * g, DV)) = x;
-        }
+        state_tile_readout<DK, DV, NDC>(h, tile, C * NDC, v0, l);
         asm volatile("" ::: "memory");
     } else {
         static_assert(NCW == 1, "fp32 states run with one consumer");
