@@ -52,12 +52,13 @@ KERNEL_IO = {
 }
 for _p in ("gla", "m2"):
     KERNEL_IO.update({_p + "_prep": "k g", _p + "_out": "q k g o", _p + "_prep_bwd": "q k g",
-                      _p + "_scan_fwd": "v", _p + "_scan_fwd_rec": "v", _p + "_scan_bwd": "dO",
+                      _p + "_scan_fwd": "v", _p + "_scan_fwd_rec": "v", _p + "_scan_fwd_save": "v",
+                      _p + "_scan_bwd": "dO",
                       _p + "_bwd_intra": "q k v g dO dq dk dv dg"})
 # boundary states each scan reads or writes (fp32 [B, H, dk, dv])
 SCAN_STATES = {"gdn_scan_fwd": 2, "gdn_scan_pair": 3, "gdn_scan_rev": 2, "kda_scan_fwd": 2, "kda_scan_pair": 3,
-               "gla_scan_fwd": 2, "gla_scan_fwd_rec": 1, "gla_scan_bwd": 2,
-               "m2_scan_fwd": 2, "m2_scan_fwd_rec": 1, "m2_scan_bwd": 2}
+               "gla_scan_fwd": 2, "gla_scan_fwd_rec": 1, "gla_scan_fwd_save": 2, "gla_scan_bwd": 2,
+               "m2_scan_fwd": 2, "m2_scan_fwd_rec": 1, "m2_scan_fwd_save": 2, "m2_scan_bwd": 2}
 
 
 def layer_io(name: str, kind: str, dk: int, dv: int, es: int) -> int:
@@ -119,6 +120,8 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
                                  + Cv * es + Cg * es,
                                  2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv)
         W[pre + "_scan_fwd_rec"] = W[pre + "_scan_fwd"]
+        # saved activations: each block's state a second time, in the backward's layout
+        W[pre + "_scan_fwd_save"] = (W[pre + "_scan_fwd"][0] + kv * es, W[pre + "_scan_fwd"][1])
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
     # the backward's prep also reads Q and dO and writes the reverse scan's
     # operands W^T, Kh, dvloc^T, R (element type) and T^T for the block adjoints;
@@ -443,8 +446,8 @@ def main():
     ap.add_argument("--fwd-split", type=int, default=None, metavar="PERMILLE",
                     help="split-and-overlap forward at PERMILLE/1000 of the blocks (0 = off, the default)")
     ap.add_argument("--saved", action="store_true",
-                    help="Gated DeltaNet: keep each chunk's forward activations for its backward "
-                         "(gdn_fwd_save / gdn_bwd_saved) instead of recomputing them")
+                    help="Gated DeltaNet, GLA, Mamba-2: keep each chunk's forward activations for its "
+                         "backward (*_fwd_save / *_bwd_saved) instead of recomputing them")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -507,11 +510,13 @@ def main():
             if cfg["kind"] == "gdn":
                 drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N, save=args.saved)
             else:
+                if args.saved:
+                    raise SystemExit("--saved: the KDA layer has no saved-activation pair")
                 drv = stateflow.KdaChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
         elif cfg["kind"] == "gla":
-            drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N)
+            drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N, save=args.saved)
         else:
-            drv = stateflow.Mamba2Chunked(d["q"], d["k"], d["v"], d["g"], N)
+            drv = stateflow.Mamba2Chunked(d["q"], d["k"], d["v"], d["g"], N, save=args.saved)
         o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device="cuda")
         grads = {k: torch.empty_like(d[k.replace("d", "", 1)] if k != "dbeta" else d["beta"])
                  for k in (("dq", "dk", "dv", "dg", "dbeta") if delta else ("dq", "dk", "dv", "dg"))}
@@ -650,7 +655,7 @@ def main():
                       {"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "H": cfg["H"], "dk": cfg["dk"],
                        "dv": cfg["dv"], "seq_chunks": N, "block": 64,
                        "scan_bv": ops.get_scan_bv(), "fwd_split_permille": ops.get_fwd_split(),
-                       "backward": "saved activations" if args.saved and cfg["kind"] == "gdn"
+                       "backward": "saved activations" if args.saved and cfg["kind"] != "kda"
                        else "recompute from S_in"}),
            "mfma_util": mfma_util,
            "peak_mem_gb": round(torch.cuda.max_memory_allocated() / 1e9, 3),

@@ -233,6 +233,17 @@ size_t clr_saved_bytes(const clr_shape_t* s) {
     return saved_carve(s, nullptr, nullptr, nullptr);
 }
 
+size_t clr_saved_bytes_op(const clr_shape_t* s, int op) {
+    switch (op) {
+        case CLR_OP_GDN_FWD: case CLR_OP_GDN_BWD: return clr_saved_bytes(s);
+        case CLR_OP_GLA_FWD: case CLR_OP_GLA_BWD: case CLR_OP_M2_FWD: case CLR_OP_M2_BWD:
+            // GLA and Mamba-2: per block the entering state, tiled [d][v]
+            if (check_shape(s, true, true) != CLR_OK) return 0;
+            return align_up(nblocks(s) * s->dk * s->dv * esize(s->dtype));
+        default: return 0;
+    }
+}
+
 size_t clr_workspace_bytes(const clr_shape_t* s, int op) {
     if (op == CLR_OP_KDA_FWD || op == CLR_OP_KDA_BWD) {
         const bool bwd = op == CLR_OP_KDA_BWD;
@@ -330,9 +341,9 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
     // g and beta rows of GDN are only 2/4-byte aligned per token but the
     // tensors themselves must start 16-byte aligned.
     if ((rc = check_bufs(bufs, 10))) return rc;
-    if (save) {  // gdn_fwd_save: the saved activations feed gdn_bwd_saved
-        if ((rc = check_shape(s, false, true))) return rc;
-        const size_t need_s = clr_saved_bytes(s);
+    if (save) {  // *_fwd_save: the saved activations feed the member's *_bwd_saved
+        if ((rc = check_shape(s, gla, true))) return rc;
+        const size_t need_s = clr_saved_bytes_op(s, kind == K_GDN ? CLR_OP_GDN_BWD : kind == K_GLA ? CLR_OP_GLA_BWD : CLR_OP_M2_BWD);
         if (need_s && (!saved || saved_bytes < need_s || ((uintptr_t)saved & (ALIGN - 1)))) return CLR_EWORKSPACE;
     }
     const size_t need = clr_workspace_bytes(s, kind == K_KDA ? CLR_OP_KDA_FWD : gla ? CLR_OP_GLA_FWD : CLR_OP_GDN_FWD);
@@ -369,6 +380,7 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
         L.scalar_gate = kind == K_M2;
         L.q = q; L.k = k; L.v = v; L.g = g; L.S_in = S_in; L.o = o; L.S_out = S_out;
         L.ws = carve_gla(s, false, (char*)ws, nullptr);
+        if (save) L.saved_h = saved;
         return hip_status(launch_gla_fwd(L, st));
     }
 }
@@ -396,6 +408,20 @@ int gla_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, c
             const void* beta, const float* S_in, void* o, float* S_out, void* ws, size_t ws_bytes,
             void* stream) {
     return fwd_common(K_GLA, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream);
+}
+
+int gla_fwd_save(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+                 const void* beta, const float* S_in, void* o, float* S_out, void* saved, size_t saved_bytes,
+                 void* ws, size_t ws_bytes, void* stream) {
+    return fwd_common(K_GLA, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream, false, saved, saved_bytes,
+                      /*save=*/true);
+}
+
+int mamba2_fwd_save(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, const float* S_in, void* o, float* S_out, void* saved, size_t saved_bytes,
+                    void* ws, size_t ws_bytes, void* stream) {
+    return fwd_common(K_M2, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream, false, saved, saved_bytes,
+                      /*save=*/true);
 }
 
 int kda_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
@@ -438,7 +464,7 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
                   {ws, ws_bytes, true},           {saved, saved_bytes, false}};
     if ((rc = check_bufs(bufs, 16))) return rc;
     if (use_saved) {
-        const size_t need_s = clr_saved_bytes(s);
+        const size_t need_s = clr_saved_bytes_op(s, kind == K_GDN ? CLR_OP_GDN_BWD : kind == K_GLA ? CLR_OP_GLA_BWD : CLR_OP_M2_BWD);
         if (need_s && (!saved || saved_bytes < need_s || ((uintptr_t)saved & (ALIGN - 1)))) return CLR_EWORKSPACE;
     }
     const size_t need = clr_workspace_bytes(s, kind == K_KDA ? CLR_OP_KDA_BWD : gla ? CLR_OP_GLA_BWD : CLR_OP_GDN_BWD);
@@ -468,6 +494,7 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
         L.q = q; L.k = k; L.v = v; L.g = g; L.S_in = S_in;
         L.dO = dO; L.dS_out = dS_out; L.dq = dq; L.dk_ = dk; L.dv_ = dv; L.dg = dg; L.dS_in = dS_in;
         L.ws = carve_gla(s, true, (char*)ws, nullptr);
+        if (use_saved) L.saved_h = const_cast<void*>(saved);
         return hip_status(launch_gla_bwd(L, st));
     }
 }
@@ -510,6 +537,22 @@ int mamba2_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v
                void* stream) {
     return bwd_common(K_M2, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
                       ws_bytes, stream);
+}
+
+int gla_bwd_saved(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* S_in, const void* dO, const float* dS_out, const void* saved,
+                  size_t saved_bytes, void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dS_in, void* ws,
+                  size_t ws_bytes, void* stream) {
+    return bwd_common(K_GLA, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws, ws_bytes,
+                      stream, saved, saved_bytes, /*use_saved=*/true);
+}
+
+int mamba2_bwd_saved(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* S_in, const void* dO, const float* dS_out, const void* saved,
+                     size_t saved_bytes, void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dS_in,
+                     void* ws, size_t ws_bytes, void* stream) {
+    return bwd_common(K_M2, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws, ws_bytes,
+                      stream, saved, saved_bytes, /*use_saved=*/true);
 }
 
 size_t clr_shortconv_workspace_bytes(const clr_conv_shape_t* s) {

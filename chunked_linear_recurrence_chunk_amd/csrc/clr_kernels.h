@@ -173,6 +173,9 @@ struct GlaLaunch {
     void *dq, *dk_, *dv_, *dg;
     float* dS_in;
     GlaWs ws;
+    // saved activations (gla_fwd_save / gla_bwd_saved and the Mamba-2 pair):
+    // per block the entering state, tiled [d][v]
+    void* saved_h = nullptr;
 };
 
 hipError_t launch_gla_fwd(const GlaLaunch& L, hipStream_t st);

@@ -16,7 +16,13 @@ hipError_t launch_gla_fwd_t(const GlaLaunch& L, hipStream_t st) {
     pa.range = ws.range;
     launch(SG ? "m2_prep" : "gla_prep", gla_prep_kernel<E, DK, false, SG>, gblk, dim3(256), st, pa);
     GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, L.S_out, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
-    launch(SG ? "m2_scan_fwd" : "gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
+    const dim3 sgrid(scan_grid(SL::NG, L.B * L.H));
+    if (L.saved_h) {  // the states once more, in the block adjoints' layout
+        sa.hN = (E*)L.saved_h;
+        launch(SG ? "m2_scan_fwd_save" : "gla_scan_fwd_save", gla_scan_fwd_kernel<E, DK, DV, false, true>, sgrid, dim3(SL::THREADS), st, sa);
+    } else {
+        launch(SG ? "m2_scan_fwd" : "gla_scan_fwd", gla_scan_fwd_kernel<E, DK, DV, false>, sgrid, dim3(SL::THREADS), st, sa);
+    }
     if (L.o) {
         GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)ws.hT, (E*)L.o, L.T, L.H, L.NC};
         launch(SG ? "m2_out" : "gla_out", gla_out_kernel<E, DK, DV, SG>, gblk, dim3(512), st, oa);
@@ -29,16 +35,20 @@ hipError_t launch_gla_bwd_t(const GlaLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GlaWs& ws = L.ws;
     using SL = GlaSlices<E, DK, DV>;
+    // with saved states the forward recompute (and the decayed keys it reads) drops out
+    const bool saved = L.saved_h != nullptr;
     GlaPrepArgs<E> pa{(const E*)L.q, (const E*)L.k, (const E*)L.g, L.T, L.H, L.NC,
-                      ws.eC, (E*)ws.KhT, (E*)ws.QgT, (E*)ws.Kh};
+                      ws.eC, saved ? nullptr : (E*)ws.KhT, (E*)ws.QgT, (E*)ws.Kh};
     pa.range = ws.range;
     launch(SG ? "m2_prep_bwd" : "gla_prep_bwd", gla_prep_kernel<E, DK, true, SG>, gblk, dim3(256), st, pa);
-    GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, nullptr, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
-    launch(SG ? "m2_scan_fwd_rec" : "gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
+    if (!saved) {
+        GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, nullptr, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
+        launch(SG ? "m2_scan_fwd_rec" : "gla_scan_fwd_rec", gla_scan_fwd_kernel<E, DK, DV, true>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sa);
+    }
     GlaScanBwdArgs<E> sb{ws.eC, (const E*)ws.Kh, (const E*)ws.QgT, (const E*)L.dO, L.dS_out, L.dS_in,
                          (E*)ws.dh, (E*)ws.dVs, L.T, L.H, L.NC, L.B * L.H};
     launch(SG ? "m2_scan_bwd" : "gla_scan_bwd", gla_scan_bwd_kernel<E, DK, DV>, dim3(scan_grid(SL::NG, L.B * L.H)), dim3(SL::THREADS), st, sb);
-    GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.dO, (const E*)L.g, (const E*)ws.hT,
+    GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.dO, (const E*)L.g, (const E*)(saved ? L.saved_h : ws.hT),
                        (const E*)ws.dh, (const E*)ws.dVs, (E*)L.dq, (E*)L.dk_, (E*)L.dv_, (E*)L.dg, L.T, L.H, L.NC};
     launch(SG ? "m2_bwd_intra" : "gla_bwd_intra", gla_bwd_intra_kernel<E, DK, DV, SG>, gblk, dim3(512), st, ia);
     return hipGetLastError();

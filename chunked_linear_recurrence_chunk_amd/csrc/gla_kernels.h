@@ -68,6 +68,9 @@ template <typename E> struct GlaScanArgs {
     float* S_out;
     E* hT;
     int T, H, NC, BH;
+    // saved activations: the state entering each block, also in the tiled
+    // [d][v] layout the block adjoints read (forward scan with HN only)
+    E* hN = nullptr;
 };
 template <typename E> struct GlaOutArgs {
     const E *q, *k, *v, *g;
@@ -328,12 +331,13 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaPrepArgs<E> a) {
     const float* bC = Bs + (BLK - 1) * PB;
     if (tid < DK) a.eC[chunk * DK + tid] = __expf(bC[tid]);
     // Kh^T (A: m = d, k = t) fragment (db, j) = B fragment of K * exp(b_C - b)
-    E* KhT = a.KhT + chunk * BLK * DK;
+    // (the backward that reads saved states has no scan to feed: KhT null)
+    E* KhT = a.KhT ? a.KhT + chunk * BLK * DK : nullptr;
     E* QgT = BWD ? a.QgT + chunk * BLK * DK : nullptr;
 #pragma unroll
     for (int f = w; f < 2 * ND; f += 4) {
         const int db = f >> 1, j = f & 1;
-        st_fragT(KhT, f, l, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, bC, -1.f, 0, BLK));
+        if (KhT) st_fragT(KhT, f, l, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, bC, -1.f, 0, BLK));
         if constexpr (BWD) st_fragT(QgT, f, l, frag_col_decay(Qs, PK, Bs, PB, 16 * db, 32 * j, zrow, 1.f, 0, BLK));
     }
     if constexpr (BWD) {
@@ -374,19 +378,23 @@ __device__ __forceinline__ const void* slice_src(const E* rows, size_t ld, int q
     return rows + (size_t)ts * ld + part * SL::VEC;
 }
 
-template <typename E, int DK, int DV, bool HNAT> struct GlaScanGeom : GlaSlices<E, DK, DV> {
+template <typename E, int DK, int DV, bool HNAT, bool HN = false> struct GlaScanGeom : GlaSlices<E, DK, DV> {
     using SL = GlaSlices<E, DK, DV>;
     static constexpr int ND = DK / 16, NKU = 2 * ND * SL::UPF;
     static constexpr int NU = NKU + SL::NS * SL::NVU + 1;  // Kh^T | V slices | exp(b_C)
     static constexpr int SLOT = RingGeom<NU, SL::NPW>::SLOT;
-    static constexpr int TILE = HNAT ? state_tile_bytes(DK, sizeof(E)) : 16;  // per consumer wave
+    static constexpr int TILE = HNAT || HN ? state_tile_bytes(DK, sizeof(E)) : 16;  // per consumer wave
     static constexpr int PF = (144 * 1024 - SL::NS * TILE) / SLOT;
     static constexpr int P = PF > 4 ? 4 : (PF < 2 ? 2 : PF);
 };
 
-template <typename E, int DK, int DV, bool HNAT>
+// HNAT: the saved states hT in the tiled [d][v] layout of the block adjoints
+// (backward recompute), else in the fragment tiles of the out kernel; HN: the
+// latter, and each state once more in the former at hN (saved activations).
+template <typename E, int DK, int DV, bool HNAT, bool HN = false>
 __global__ __launch_bounds__((GlaSlices<E, DK, DV>::THREADS)) void gla_scan_fwd_kernel(GlaScanArgs<E> a) {
-    using SG = GlaScanGeom<E, DK, DV, HNAT>;
+    static_assert(!(HNAT && HN), "one tiled [d][v] store per block");
+    using SG = GlaScanGeom<E, DK, DV, HNAT, HN>;
     constexpr int ND = SG::ND, KK = DK / 32, NS = SG::NS, NU = SG::NU, P = SG::P, NKU = SG::NKU, NVU = SG::NVU;
     constexpr int NPW = SG::NPW, UE = UNIT_ELEMS<E>, LE = LANE_ELEMS<E>;
     using G = RingGeom<NU, NPW>;
@@ -452,6 +460,12 @@ __global__ __launch_bounds__((GlaSlices<E, DK, DV>::THREADS)) void gla_scan_fwd_
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) st8T(hT, vb * KK + kk, l, S[2 * kk], S[2 * kk + 1]);
             }
+        }
+        if constexpr (HN) {
+            Frag<E> fs[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) fs[kk] = frag_from_acc<E>(S[2 * kk], S[2 * kk + 1]);
+            store_state_tr<E, DK, DV>(a.hN + (bh * NC + n) * DK * DV, fs, tile, v0, l);
         }
         const E* Vs = (const E*)(slot + (NKU + w * NVU) * RING_UNIT);
         const float* eCs = (const float*)(slot + (NU - 1) * RING_UNIT);

@@ -73,6 +73,15 @@ def load(path: Optional[str] = None):
         lib.gdn_fwd_save.restype = i
         lib.gdn_bwd_saved.argtypes = [sp] + [vp] * 9 + [sz] + [vp] * 7 + [sz, vp]
         lib.gdn_bwd_saved.restype = i
+    if hasattr(lib, "gla_fwd_save"):  # the GLA and Mamba-2 saved-activation pairs
+        lib.clr_saved_bytes_op.argtypes = [sp, i]
+        lib.clr_saved_bytes_op.restype = sz
+        for name in ("gla_fwd_save", "mamba2_fwd_save"):
+            getattr(lib, name).argtypes = [sp] + [vp] * 9 + [sz, vp, sz, vp]
+            getattr(lib, name).restype = i
+        for name in ("gla_bwd_saved", "mamba2_bwd_saved"):
+            getattr(lib, name).argtypes = [sp] + [vp] * 9 + [sz] + [vp] * 7 + [sz, vp]
+            getattr(lib, name).restype = i
     for name in ("gdn_bwd", "gla_bwd", "mamba2_bwd", "kda_bwd"):
         f = getattr(lib, name)
         f.argtypes = [sp] + [vp] * 15 + [sz, vp]
@@ -307,43 +316,42 @@ def gdn_fwd_noalloc(q, k, v, g, beta, S_in=None, o=None, S_out=None):
     return o, S_out
 
 
-def saved_bytes(shape: ClrShape) -> int:
-    """clr_saved_bytes: bytes of one Gated DeltaNet chunk call's saved
-    activations (the states entering its blocks and their U)."""
-    return int(load().clr_saved_bytes(ctypes.byref(shape)))
+def saved_bytes(shape: ClrShape, op: int = None) -> int:
+    """Bytes of one chunk call's saved activations: clr_saved_bytes (the Gated
+    DeltaNet pair: the states entering its blocks and their U) or, with ``op``,
+    clr_saved_bytes_op for the member that op names (GLA, Mamba-2: the
+    states)."""
+    if op is None:
+        return int(load().clr_saved_bytes(ctypes.byref(shape)))
+    return int(load().clr_saved_bytes_op(ctypes.byref(shape), op))
 
 
-def gdn_fwd_save(q, k, v, g, beta, S_in=None, saved=None, ws=None, o=None, S_out=None):
-    """gdn_fwd that also keeps the activations the backward needs (gdn_fwd_save):
-    returns (o, S_out, saved), ``saved`` a uint8 device tensor to hand to
-    gdn_bwd_saved for the same chunk (allocated here unless given)."""
+def _fwd_save(name, op, q, k, v, g, beta, S_in, saved, ws, o, S_out, check_range=False):
     import torch
-    _validate("gdn", q, k, v, g, beta, S_in)
+    _validate(name.split("_")[0], q, k, v, g, beta, S_in)
     _check_inputs(q, k, v, g, beta, S_in)
     shape = make_shape(q, v)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     o = _out(o, (B, T, H, dv), q.dtype, q.device)
     S_out = _out(S_out, (B, H, dk, dv), torch.float32, q.device)
-    ns = saved_bytes(shape)
+    ns = saved_bytes(shape, op)
     if saved is None:
         saved = torch.empty(max(ns, 256), dtype=torch.uint8, device=q.device)
     if ws is None:
-        ws, n = _workspace(shape, OP_GDN_FWD, q.device)
+        ws, n = _workspace(shape, op, q.device)
     else:
         n = ws.numel()
-    rc = load().gdn_fwd_save(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S_in),
-                             _ptr(o), _ptr(S_out), _ptr(saved), saved.numel(), _ptr(ws), n, _stream())
-    _check("gdn_fwd_save", rc)
+    rc = getattr(load(), name)(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S_in),
+                               _ptr(o), _ptr(S_out), _ptr(saved), saved.numel(), _ptr(ws), n, _stream())
+    _check(name, rc)
+    _range_check(name, shape, op, ws, check_range)
     return o, S_out, saved
 
 
-def gdn_bwd_saved(q, k, v, g, beta, S_in, dO, dS_out, saved, ws=None, out=None):
-    """gdn_bwd reading the activations gdn_fwd_save kept for this chunk instead
-    of recomputing the forward (S_in is not read and may be None).  Returns
-    dict dq, dk, dv, dg, dbeta, dS_in."""
+def _bwd_saved(name, op, q, k, v, g, beta, S_in, dO, dS_out, saved, ws, out, check_range=False):
     import torch
-    _validate("gdn", q, k, v, g, beta, S_in, dO, dS_out)
+    _validate(name.split("_")[0], q, k, v, g, beta, S_in, dO, dS_out)
     _check_inputs(q, k, v, g, beta, S_in, dO, dS_out, saved)
     shape = make_shape(q, v)
     B, T, H, dk = q.shape
@@ -353,17 +361,61 @@ def gdn_bwd_saved(q, k, v, g, beta, S_in, dO, dS_out, saved, ws=None, out=None):
     dk_ = _out(out.get("dk"), k.shape, k.dtype, k.device)
     dv_ = _out(out.get("dv"), v.shape, v.dtype, v.device)
     dg = _out(out.get("dg"), g.shape, g.dtype, g.device)
-    dbeta = _out(out.get("dbeta"), beta.shape, beta.dtype, beta.device)
+    dbeta = _out(out.get("dbeta"), beta.shape, beta.dtype, beta.device) if beta is not None else None
     dS_in = _out(out.get("dS_in"), (B, H, dk, dv), torch.float32, q.device)
     if ws is None:
-        ws, n = _workspace(shape, OP_GDN_BWD, q.device)
+        ws, n = _workspace(shape, op, q.device)
     else:
         n = ws.numel()
-    rc = load().gdn_bwd_saved(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S_in),
-                              _ptr(dO), _ptr(dS_out), _ptr(saved), saved.numel(), _ptr(dq), _ptr(dk_), _ptr(dv_),
-                              _ptr(dg), _ptr(dbeta), _ptr(dS_in), _ptr(ws), n, _stream())
-    _check("gdn_bwd_saved", rc)
-    return dict(dq=dq, dk=dk_, dv=dv_, dg=dg, dbeta=dbeta, dS_in=dS_in)
+    rc = getattr(load(), name)(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S_in),
+                               _ptr(dO), _ptr(dS_out), _ptr(saved), saved.numel(), _ptr(dq), _ptr(dk_), _ptr(dv_),
+                               _ptr(dg), _ptr(dbeta), _ptr(dS_in), _ptr(ws), n, _stream())
+    _check(name, rc)
+    _range_check(name, shape, op, ws, check_range)
+    r = dict(dq=dq, dk=dk_, dv=dv_, dg=dg, dS_in=dS_in)
+    if dbeta is not None:
+        r["dbeta"] = dbeta
+    return r
+
+
+def gdn_fwd_save(q, k, v, g, beta, S_in=None, saved=None, ws=None, o=None, S_out=None):
+    """gdn_fwd that also keeps the activations the backward needs (gdn_fwd_save):
+    returns (o, S_out, saved), ``saved`` a uint8 device tensor to hand to
+    gdn_bwd_saved for the same chunk (allocated here unless given)."""
+    return _fwd_save("gdn_fwd_save", OP_GDN_FWD, q, k, v, g, beta, S_in, saved, ws, o, S_out)
+
+
+def gdn_bwd_saved(q, k, v, g, beta, S_in, dO, dS_out, saved, ws=None, out=None):
+    """gdn_bwd reading the activations gdn_fwd_save kept for this chunk instead
+    of recomputing the forward (S_in is not read and may be None).  Returns
+    dict dq, dk, dv, dg, dbeta, dS_in."""
+    return _bwd_saved("gdn_bwd_saved", OP_GDN_BWD, q, k, v, g, beta, S_in, dO, dS_out, saved, ws, out)
+
+
+def gla_fwd_save(q, k, v, g, S_in=None, saved=None, ws=None, o=None, S_out=None, check_range=False):
+    """gla_fwd that also keeps the states the backward needs (gla_fwd_save):
+    returns (o, S_out, saved) for gla_bwd_saved of the same chunk."""
+    return _fwd_save("gla_fwd_save", OP_GLA_FWD, q, k, v, g, None, S_in, saved, ws, o, S_out, check_range)
+
+
+def gla_bwd_saved(q, k, v, g, S_in, dO, dS_out, saved, ws=None, out=None, check_range=False):
+    """gla_bwd reading the states gla_fwd_save kept (S_in is not read and may
+    be None).  Returns dict dq, dk, dv, dg, dS_in."""
+    return _bwd_saved("gla_bwd_saved", OP_GLA_BWD, q, k, v, g, None, S_in, dO, dS_out, saved, ws, out,
+                      check_range)
+
+
+def mamba2_fwd_save(q, k, v, g, S_in=None, saved=None, ws=None, o=None, S_out=None, check_range=False):
+    """mamba2_fwd that also keeps the states the backward needs: returns
+    (o, S_out, saved) for mamba2_bwd_saved of the same chunk."""
+    return _fwd_save("mamba2_fwd_save", OP_M2_FWD, q, k, v, g, None, S_in, saved, ws, o, S_out, check_range)
+
+
+def mamba2_bwd_saved(q, k, v, g, S_in, dO, dS_out, saved, ws=None, out=None, check_range=False):
+    """mamba2_bwd reading the states mamba2_fwd_save kept (S_in is not read
+    and may be None).  Returns dict dq, dk, dv, dg, dS_in."""
+    return _bwd_saved("mamba2_bwd_saved", OP_M2_BWD, q, k, v, g, None, S_in, dO, dS_out, saved, ws, out,
+                      check_range)
 
 
 def gla_fwd(q, k, v, g, S_in=None, want_state=True, ws=None, o=None, S_out=None, check_range=False):

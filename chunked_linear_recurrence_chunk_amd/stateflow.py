@@ -33,11 +33,11 @@ def _sl(t, a, b):
 class GdnChunked:
     """Forward/backward of one Gated DeltaNet layer over N sequence chunks.
 
-    With ``save=True`` (Gated DeltaNet only) each chunk's forward also keeps
-    the activations its backward needs (gdn_fwd_save), and the backward reads
-    them (gdn_bwd_saved) instead of recomputing the chunk's forward from S^in:
-    more device memory (clr_saved_bytes per chunk until its backward), less
-    work."""
+    With ``save=True`` each chunk's forward also keeps the activations its
+    backward needs (gdn_fwd_save), and the backward reads them (gdn_bwd_saved)
+    instead of recomputing the chunk's forward from S^in: more device memory
+    (clr_saved_bytes per chunk until its backward), less work.  The GLA and
+    Mamba-2 drivers below take the same flag; the KDA driver does not."""
 
     kind = "gdn"
     _names = ("gdn_fwd", "gdn_bwd", "OP_GDN_FWD", "OP_GDN_BWD")
@@ -59,7 +59,7 @@ class GdnChunked:
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         self.saved = [None] * N
         if save and self.kind != "gdn":
-            raise ValueError("saved activations exist for the Gated DeltaNet layer only")
+            raise ValueError("saved activations exist for the Gated DeltaNet, GLA and Mamba-2 layers only")
         self.save = save
         self.acts = [None] * N  # per chunk: the activations gdn_fwd_save kept
 
@@ -116,11 +116,15 @@ class GdnChunked:
 
 
 class GlaChunked(GdnChunked):
-    """Forward/backward of one GLA layer over N sequence chunks."""
+    """Forward/backward of one GLA layer over N sequence chunks (``save`` as
+    for the Gated DeltaNet driver: gla_fwd_save / gla_bwd_saved)."""
 
     kind = "gla"
 
-    def __init__(self, q, k, v, g, N: int):
+    def __init__(self, q, k, v, g, N: int, save: bool = False):
+        self._init(q, k, v, g, N, save, "gla", "GLA")
+
+    def _init(self, q, k, v, g, N, save, name, op):
         from . import ops
         self.ops = ops
         self.q, self.k, self.v, self.g, self.beta = q, k, v, g, None
@@ -131,10 +135,14 @@ class GlaChunked(GdnChunked):
         dv = v.shape[-1]
         import torch
         shape = ops.ClrShape(B, L, H, dk, dv, ops._dtype_code(q))
-        nbytes = max(ops.workspace_bytes(shape, ops.OP_GLA_FWD), ops.workspace_bytes(shape, ops.OP_GLA_BWD))
+        nbytes = max(ops.workspace_bytes(shape, getattr(ops, f"OP_{op}_FWD")),
+                     ops.workspace_bytes(shape, getattr(ops, f"OP_{op}_BWD")))
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         self.saved = [None] * N
-        self._fwd, self._bwd = ops.gla_fwd, ops.gla_bwd
+        self._fwd, self._bwd = getattr(ops, f"{name}_fwd"), getattr(ops, f"{name}_bwd")
+        self._fwd_save, self._bwd_saved = getattr(ops, f"{name}_fwd_save"), getattr(ops, f"{name}_bwd_saved")
+        self.save = save
+        self.acts = [None] * N  # per chunk: the states the forward kept
 
     def _chunk(self, i):
         a, b = self.bounds[i]
@@ -151,7 +159,11 @@ class GlaChunked(GdnChunked):
             a, b = self.bounds[i]
             self.saved[i] = S
             view = o[:, a:b]
-            oi, S = self._fwd(*self._chunk(i), S, ws=self.ws, o=view if view.is_contiguous() else None)
+            ov = view if view.is_contiguous() else None
+            if self.save:
+                oi, S, self.acts[i] = self._fwd_save(*self._chunk(i), S, ws=self.ws, o=ov)
+            else:
+                oi, S = self._fwd(*self._chunk(i), S, ws=self.ws, o=ov)
             if oi.data_ptr() != view.data_ptr():
                 view.copy_(oi)
         return o, S
@@ -166,7 +178,12 @@ class GlaChunked(GdnChunked):
             a, b = self.bounds[i]
             views = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg")}
             out = {key: t for key, t in views.items() if t.is_contiguous()}
-            r = self._bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
+            if self.save:
+                r = self._bwd_saved(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, self.acts[i],
+                                    ws=self.ws, out=out)
+                self.acts[i] = None
+            else:
+                r = self._bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)
             for key, t in views.items():
                 if r[key].data_ptr() != t.data_ptr():
                     t.copy_(r[key])
@@ -182,21 +199,8 @@ class Mamba2Chunked(GlaChunked):
 
     kind = "mamba2"
 
-    def __init__(self, q, k, v, g, N: int):
-        from . import ops
-        self.ops = ops
-        self.q, self.k, self.v, self.g, self.beta = q, k, v, g, None
-        self.N = N
-        self.bounds = _bounds(q.shape[1], N)
-        L = self.bounds[0][1]
-        B, _, H, dk = q.shape
-        dv = v.shape[-1]
-        import torch
-        shape = ops.ClrShape(B, L, H, dk, dv, ops._dtype_code(q))
-        nbytes = max(ops.workspace_bytes(shape, ops.OP_M2_FWD), ops.workspace_bytes(shape, ops.OP_M2_BWD))
-        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
-        self.saved = [None] * N
-        self._fwd, self._bwd = ops.mamba2_fwd, ops.mamba2_bwd
+    def __init__(self, q, k, v, g, N: int, save: bool = False):
+        self._init(q, k, v, g, N, save, "mamba2", "M2")
 
 
 class ShortConvChunked:

@@ -350,3 +350,57 @@ def test_saved_activation_entry_points_reject_on_the_host():
     bad = list(outs)
     bad[0] = None
     assert bwd(0xF0000, n, bad) == ops.CLR_EINVAL                # dq missing
+
+
+@pytest.mark.parametrize("member", ["gla", "mamba2"])
+def test_gla_saved_activation_entry_points_reject_on_the_host(member):
+    """gla_* / mamba2_* with saved states: size query and host-side rejections
+    (every call below fails validation, so nothing is launched)."""
+    ops, lib = _lib()
+    op_f, op_b = (ops.OP_GLA_FWD, ops.OP_GLA_BWD) if member == "gla" else (ops.OP_M2_FWD, ops.OP_M2_BWD)
+    s = _shape(ops, T=64, H=1, dk=32, dv=32)
+    n = ops.saved_bytes(s, op_f)
+    assert n == 32 * 32 * 2 == ops.saved_bytes(s, op_b)           # one block: a 32 x 32 bf16 state
+    assert ops.saved_bytes(_shape(ops, T=130, H=3, dk=128, dv=256), op_f) == 3 * 3 * 128 * 256 * 2
+    assert ops.saved_bytes(_shape(ops, T=0), op_f) == 0
+    assert ops.saved_bytes(_shape(ops, dk=128, dv=128, dtype=0), op_b) == 0   # no fp32 backward at d = 128
+    assert ops.saved_bytes(_shape(ops, dk=96, dv=96), op_f) == 0
+    assert ops.saved_bytes(s, ops.OP_KDA_FWD) == 0 and ops.saved_bytes(s, ops.OP_KDA_BWD) == 0
+    assert ops.saved_bytes(s, 99) == 0
+    g16 = ops.ClrShape(1, 64, 1, 128, 128, 1)
+    assert ops.saved_bytes(g16, ops.OP_GDN_FWD) == ops.saved_bytes(g16)
+    P_ = _fake
+    # fwd: q k v g beta(NULL) S_in o S_out | saved, nsaved | ws, nws
+    base = [P_(0x10000), P_(0x20000), P_(0x30000), P_(0x40000), None, None, P_(0x60000), P_(0x70000)]
+    fwd_f = getattr(lib, f"{member}_fwd_save")
+
+    def fwd(saved, nsaved, ws=0x100000, nws=1 << 40):
+        return fwd_f(ctypes.byref(s), *base, None if saved is None else P_(saved), nsaved,
+                     None if ws is None else P_(ws), nws, None)
+    assert fwd(None, 0) == ops.CLR_EWORKSPACE                    # no saved buffer
+    assert fwd(0xA0000, n - 256) == ops.CLR_EWORKSPACE           # too small
+    assert fwd(0xA0010, n) == ops.CLR_EWORKSPACE                 # misaligned
+    assert fwd(0x60000, n) == ops.CLR_EINVAL                     # overlaps the output o
+    assert fwd(0x100000 - n // 2, n) == ops.CLR_EINVAL           # overlaps the workspace
+    assert fwd(0xA0000, n, ws=None) == ops.CLR_EWORKSPACE        # no workspace
+    base_b = list(base)
+    base_b[4] = P_(0x50000)
+    assert fwd_f(ctypes.byref(s), *base_b, P_(0xA0000), n, P_(0x100000), 1 << 40, None) == ops.CLR_EINVAL  # beta given
+    # bwd: q k v g beta(NULL) S_in dO dS_out | saved, nsaved | dq dk dv dg dbeta(NULL) dS_in | ws, nws
+    outs = [P_(0x80000 + 0x10000 * i) for i in range(6)]
+    outs[4] = None
+    bwd_f = getattr(lib, f"{member}_bwd_saved")
+
+    def bwd(saved, nsaved, o=outs):
+        return bwd_f(ctypes.byref(s), *base[:6], P_(0x60000), P_(0x70000),
+                     None if saved is None else P_(saved), nsaved, *o, P_(0x100000), 1 << 40, None)
+    assert bwd(None, 0) == ops.CLR_EWORKSPACE
+    assert bwd(0xF0000, n - 256) == ops.CLR_EWORKSPACE
+    assert bwd(0xF0010, n) == ops.CLR_EWORKSPACE
+    assert bwd(0x80000, n) == ops.CLR_EINVAL                     # overlaps the output dq
+    bad = list(outs)
+    bad[0] = None
+    assert bwd(0xF0000, n, bad) == ops.CLR_EINVAL                # dq missing
+    bad = list(outs)
+    bad[4] = P_(0xC0000)
+    assert bwd(0xF0000, n, bad) == ops.CLR_EINVAL                # dbeta given
