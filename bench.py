@@ -51,7 +51,7 @@ KERNEL_IO = {
     "kda_bwd_wy": "v beta dv dbeta", "kda_bwd_intra": "q k g beta dO dq dk dg",
 }
 for _p in ("gla", "m2"):
-    KERNEL_IO.update({_p + "_prep": "k g", _p + "_out": "q k g o", _p + "_prep_bwd": "q k g",
+    KERNEL_IO.update({_p + "_prep": "k g", _p + "_out": "q k g o", _p + "_out_save": "q k g o", _p + "_prep_bwd": "q k g",
                       _p + "_scan_fwd": "v", _p + "_scan_fwd_rec": "v", _p + "_scan_fwd_save": "v",
                       _p + "_scan_bwd": "dO",
                       _p + "_bwd_intra": "q k v g dO dq dk dv dg"})
@@ -121,7 +121,9 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
                                  2 * (2 * CC * dv) + 2 * CC * dk + 2 * (2 * C * kv) + 2 * (2 * CC * dk) + 2 * CC * dv)
         W[pre + "_scan_fwd_rec"] = W[pre + "_scan_fwd"]
         # saved activations: each block's state a second time, in the backward's layout
+        # (stored by the output kernel, or by the scan when no output is asked for)
         W[pre + "_scan_fwd_save"] = (W[pre + "_scan_fwd"][0] + kv * es, W[pre + "_scan_fwd"][1])
+        W[pre + "_out_save"] = (W[pre + "_out"][0] + kv * es, W[pre + "_out"][1])
     W["gdn_scan_fwd_rec"] = W["gdn_scan_fwd"]
     # the backward's prep also reads Q and dO and writes the reverse scan's
     # operands W^T, Kh, dvloc^T, R (element type) and T^T for the block adjoints;

@@ -17,7 +17,9 @@ hipError_t launch_gla_fwd_t(const GlaLaunch& L, hipStream_t st) {
     launch(SG ? "m2_prep" : "gla_prep", gla_prep_kernel<E, DK, false, SG>, gblk, dim3(256), st, pa);
     GlaScanArgs<E> sa{ws.eC, (const E*)ws.KhT, (const E*)L.v, L.S_in, L.S_out, (E*)ws.hT, L.T, L.H, L.NC, L.B * L.H};
     const dim3 sgrid(scan_grid(SL::NG, L.B * L.H));
-    if (L.saved_h) {  // the states once more, in the block adjoints' layout
+    // saved activations: the out kernel stores the states once more, in the
+    // block adjoints' layout; without an output the scan does
+    if (L.saved_h && !L.o) {
         sa.hN = (E*)L.saved_h;
         launch(SG ? "m2_scan_fwd_save" : "gla_scan_fwd_save", gla_scan_fwd_kernel<E, DK, DV, false, true>, sgrid, dim3(SL::THREADS), st, sa);
     } else {
@@ -25,7 +27,12 @@ hipError_t launch_gla_fwd_t(const GlaLaunch& L, hipStream_t st) {
     }
     if (L.o) {
         GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)ws.hT, (E*)L.o, L.T, L.H, L.NC};
-        launch(SG ? "m2_out" : "gla_out", gla_out_kernel<E, DK, DV, SG>, gblk, dim3(512), st, oa);
+        if (L.saved_h) {
+            oa.hN = (E*)L.saved_h;
+            launch(SG ? "m2_out_save" : "gla_out_save", gla_out_kernel<E, DK, DV, SG, true>, gblk, dim3(512), st, oa);
+        } else {
+            launch(SG ? "m2_out" : "gla_out", gla_out_kernel<E, DK, DV, SG>, gblk, dim3(512), st, oa);
+        }
     }
     return hipGetLastError();
 }

@@ -77,6 +77,9 @@ template <typename E> struct GlaOutArgs {
     const E* hT;
     E* o;
     int T, H, NC;
+    // saved activations: the states once more, in the block adjoints' tiled
+    // [d][v] layout (out kernel with HN only)
+    E* hN = nullptr;
 };
 template <typename E> struct GlaScanBwdArgs {
     const float* eC;
@@ -505,12 +508,18 @@ template <typename E, int DK, int DV> struct GlaOutLds {
     static constexpr size_t total = o_V + (VLDS ? vbytes : sizeof(E) * BLK * PK);
 };
 
-template <typename E, int DK, int DV, bool SG>
+// HN: each h^T slice the kernel loads is also stored at hN in the block
+// adjoints' tiled [d][v] layout, through a per-wave LDS tile (the slices of
+// a half are spread over its four waves): the saved states of gla_fwd_save,
+// written here, off the scan's sequential chain.
+template <typename E, int DK, int DV, bool SG, bool HN = false>
 __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
     using Lay = GlaOutLds<E, DK, DV>;
     constexpr int NT = 512;
     constexpr int PK = Lay::PK, PV = Lay::PV, PB = Lay::PB, KK = DK / 32, NVH = DV / 32;  // value slices per half
+    constexpr int HTB = HN && sizeof(E) == 2 ? state_tile_bytes(DK, sizeof(E)) : 16;  // per wave
     __shared__ __align__(16) char lds[Lay::total];
+    __shared__ __align__(16) E htile[8 * HTB / sizeof(E)];
     __shared__ __align__(16) float zrow[DK];
     __shared__ float seg[256];
     // the P^T tiles (sb, R) in accumulator layout, one writer each
@@ -616,6 +625,11 @@ __global__ __launch_bounds__(512) void gla_out_kernel(GlaOutArgs<E> a) {
                 else mma(acc, ldfrag_tokcol(vbase, ldv, j, g, 16 * vb + r, nvalid), fp[j]);
             }
         if (tl < nvalid) st4(ob + (size_t)tl * ldv + 16 * vb + 4 * g, acc);
+        if constexpr (HN) {
+            if ((vb & 3) == R)  // R is the wave's: a scalar test
+                store_state_tr<E, DK, DV>(a.hN + chunk * DK * DV, fh[buf], htile + w8 * (HTB / (int)sizeof(E)),
+                                          16 * vb, l);
+        }
     };
 #pragma unroll
     for (int jv = 0; jv < NVH; ++jv) {

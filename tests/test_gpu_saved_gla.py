@@ -26,6 +26,8 @@ CASES = [
     ("mamba2", 1, 256, 1, 32, 32, "fp32", 57),
     ("mamba2", 2, 300, 2, 128, 256, "bf16", 58),  # ragged
     ("mamba2", 1, 1024, 8, 128, 256, "bf16", 59),
+    ("gla", 1, 192, 2, 64, 64, "fp32", 63),
+    ("mamba2", 2, 130, 2, 64, 64, "fp32", 64),   # ragged
 ]
 
 
@@ -91,6 +93,38 @@ def test_saved_chunked_equals_unchunked_and_plain(member):
     for key in res[0]:
         assert torch.equal(res[0][key], res[1][key]), key
         assert torch.equal(res[0][key], res[2][key]), key
+
+
+@pytest.mark.parametrize("member", ["gla", "mamba2"])
+def test_saved_forward_without_output(member):
+    """A saving forward with no output o: the scan stores the states for the
+    backward itself (the out kernel, which stores them otherwise, does not
+    run).  The backward that reads them equals the recomputing one."""
+    import torch
+    from chunked_linear_recurrence_chunk_amd import ops
+    print(f"[{member} saved] forward without o", flush=True)
+    B, T, H, dk, dv = 1, 320, 2, 128, 256
+    x = _make(member, B, T, H, dk, dv, "bf16", 65)
+    d, S_in, dS = _dev(x, "bf16")
+    args = (d["q"], d["k"], d["v"], d["g"])
+    shape = ops.make_shape(d["q"], d["v"])
+    op_f, op_b = (ops.OP_GLA_FWD, ops.OP_GLA_BWD) if member == "gla" else (ops.OP_M2_FWD, ops.OP_M2_BWD)
+    saved = torch.empty(ops.saved_bytes(shape, op_f), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(ops.workspace_bytes(shape, op) for op in (op_f, op_b)), dtype=torch.uint8, device="cuda")
+    S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    lib = ops.load()
+    rc = getattr(lib, f"{member}_fwd_save")(ops.ctypes.byref(shape), ops._ptr(d["q"]), ops._ptr(d["k"]),
+                                            ops._ptr(d["v"]), ops._ptr(d["g"]), None, ops._ptr(S_in), None,
+                                            ops._ptr(S_out), ops._ptr(saved), saved.numel(), ops._ptr(ws),
+                                            ws.numel(), ops._stream())
+    assert rc == 0, rc
+    g1 = getattr(ops, f"{member}_bwd_saved")(*args, None, d["dO"], dS, saved)
+    o0, S0 = getattr(ops, f"{member}_fwd")(*args, S_in)
+    g0 = getattr(ops, f"{member}_bwd")(*args, S_in, d["dO"], dS)
+    torch.cuda.synchronize()
+    assert torch.equal(S0, S_out)
+    for key in g0:
+        assert torch.equal(g0[key], g1[key]), key
 
 
 def test_saved_buffer_reused_across_members():
