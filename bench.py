@@ -56,7 +56,7 @@ for _p in ("gla", "m2"):
                       _p + "_scan_bwd": "dO",
                       _p + "_bwd_intra": "q k v g dO dq dk dv dg"})
 # boundary states each scan reads or writes (fp32 [B, H, dk, dv])
-SCAN_STATES = {"gdn_scan_fwd": 2, "gdn_scan_pair": 3, "gdn_scan_rev": 2, "kda_scan_fwd": 2, "kda_scan_pair": 3,
+SCAN_STATES = {"gdn_scan_fwd": 2, "gdn_scan_pair": 3, "gdn_scan_rev": 2, "kda_scan_fwd": 2, "kda_scan_pair": 3, "kda_scan_rev": 2,
                "gla_scan_fwd": 2, "gla_scan_fwd_rec": 1, "gla_scan_fwd_save": 2, "gla_scan_bwd": 2,
                "m2_scan_fwd": 2, "m2_scan_fwd_rec": 1, "m2_scan_fwd_save": 2, "m2_scan_bwd": 2}
 
@@ -142,6 +142,7 @@ def kernel_work(name: str, dk: int, dv: int, es: int, C: int = 64):
     # reverse scan: Kh as a hi/lo pair and W^T in, R and dvloc fp32, dh and dU out
     kda_scan_bwd = (dk * f4 + 3 * Ck * es + kv * f4 + Cv * f4 + kv * es + Cv * es, 2 * (2 * C * kv))
     W["kda_scan_pair"] = tuple(x + y for x, y in zip(W["kda_scan_fwd"], kda_scan_bwd))
+    W["kda_scan_rev"] = kda_scan_bwd  # saved activations: the reverse scan alone
     # the backward's prep also writes T^T, M and K e^b for the WY adjoint kernel
     W["kda_prep_bwd"] = (W["kda_prep"][0] + CC * es + CC * f4 + Ck * es, W["kda_prep"][1])
     W["kda_bwd_wy"] = (Ck * es + CC * es + CC * f4 + Cv * es + C * es + kv * es + Cv * es
@@ -240,13 +241,17 @@ def launch_name(mangled: str, kind: str) -> str:
         return "kda_scan_fwd" if flags[1] == "1" else "gdn_scan_fwd"
     if base == "gdn_scan_pair":  # <E, DK, DV, PCD, NP, NCW>
         return "kda_scan_pair" if flags[0] == "1" else "gdn_scan_pair"
+    if base == "gdn_scan_rev":  # <E, DK, DV, PCD, NP, NCW>
+        return "kda_scan_rev" if flags[0] == "1" else "gdn_scan_rev"
     if base.startswith("gla_"):
         pre = {"gla": "gla_", "mamba2": "m2_", "kda": "kda_"}.get(kind, "gla_")
         rest = base[4:]
         if rest == "prep":  # <E, DK, BWD, SG>
             rest = "prep_bwd" if flags[0] == "1" else "prep"
-        elif rest == "scan_fwd":  # <E, DK, DV, HNAT>
-            rest = "scan_fwd_rec" if flags[0] == "1" else "scan_fwd"
+        elif rest == "scan_fwd":  # <E, DK, DV, HNAT, HN>
+            rest = "scan_fwd_rec" if flags[0] == "1" else "scan_fwd_save" if flags[1:2] == ["1"] else "scan_fwd"
+        elif rest == "out" and kind != "kda":  # <E, DK, DV, SG, HN>
+            rest = "out_save" if flags[1:2] == ["1"] else "out"
         return pre + rest
     return base  # kda_prep serves both the forward and the backward's prep
 
@@ -448,7 +453,7 @@ def main():
     ap.add_argument("--fwd-split", type=int, default=None, metavar="PERMILLE",
                     help="split-and-overlap forward at PERMILLE/1000 of the blocks (0 = off, the default)")
     ap.add_argument("--saved", action="store_true",
-                    help="Gated DeltaNet, GLA, Mamba-2: keep each chunk's forward activations for its "
+                    help="keep each chunk's forward activations for its "
                          "backward (*_fwd_save / *_bwd_saved) instead of recomputing them")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (counter calibration)")
@@ -512,9 +517,7 @@ def main():
             if cfg["kind"] == "gdn":
                 drv = stateflow.GdnChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N, save=args.saved)
             else:
-                if args.saved:
-                    raise SystemExit("--saved: the KDA layer has no saved-activation pair")
-                drv = stateflow.KdaChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N)
+                drv = stateflow.KdaChunked(d["q"], d["k"], d["v"], d["g"], d["beta"], N, save=args.saved)
         elif cfg["kind"] == "gla":
             drv = stateflow.GlaChunked(d["q"], d["k"], d["v"], d["g"], N, save=args.saved)
         else:
@@ -657,7 +660,7 @@ def main():
                       {"workload": args.workload, "kind": cfg["kind"], "B": B, "T": T, "H": cfg["H"], "dk": cfg["dk"],
                        "dv": cfg["dv"], "seq_chunks": N, "block": 64,
                        "scan_bv": ops.get_scan_bv(), "fwd_split_permille": ops.get_fwd_split(),
-                       "backward": "saved activations" if args.saved and cfg["kind"] != "kda"
+                       "backward": "saved activations" if args.saved
                        else "recompute from S_in"}),
            "mfma_util": mfma_util,
            "peak_mem_gb": round(torch.cuda.max_memory_allocated() / 1e9, 3),

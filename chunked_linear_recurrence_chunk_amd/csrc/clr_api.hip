@@ -236,6 +236,10 @@ size_t clr_saved_bytes(const clr_shape_t* s) {
 size_t clr_saved_bytes_op(const clr_shape_t* s, int op) {
     switch (op) {
         case CLR_OP_GDN_FWD: case CLR_OP_GDN_BWD: return clr_saved_bytes(s);
+        case CLR_OP_KDA_FWD: case CLR_OP_KDA_BWD:
+            // KDA: the Gated DeltaNet layout (states, then U token-major in the U space)
+            if (check_shape(s, false, false) != CLR_OK || kda_f32_unsupported(s, true) || s->T == 0) return 0;
+            return saved_carve(s, nullptr, nullptr, nullptr);
         case CLR_OP_GLA_FWD: case CLR_OP_GLA_BWD: case CLR_OP_M2_FWD: case CLR_OP_M2_BWD:
             // GLA and Mamba-2: per block the entering state, tiled [d][v]
             if (check_shape(s, true, true) != CLR_OK) return 0;
@@ -317,6 +321,10 @@ int scratch_address(void** out) {
 
 // Which member of the family an entry point computes.
 enum Kind { K_GDN, K_GLA, K_M2, K_KDA };
+// the op whose saved-activation size a member's saving pair uses
+static int saved_op(Kind kind) {
+    return kind == K_GDN ? CLR_OP_GDN_BWD : kind == K_GLA ? CLR_OP_GLA_BWD : kind == K_M2 ? CLR_OP_M2_BWD : CLR_OP_KDA_BWD;
+}
 
 static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void* k, const void* v,
                       const void* g, const void* beta, const float* S_in, void* o, float* S_out,
@@ -342,8 +350,9 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
     // tensors themselves must start 16-byte aligned.
     if ((rc = check_bufs(bufs, 10))) return rc;
     if (save) {  // *_fwd_save: the saved activations feed the member's *_bwd_saved
-        if ((rc = check_shape(s, gla, true))) return rc;
-        const size_t need_s = clr_saved_bytes_op(s, kind == K_GDN ? CLR_OP_GDN_BWD : kind == K_GLA ? CLR_OP_GLA_BWD : CLR_OP_M2_BWD);
+        if ((rc = kind == K_KDA ? check_shape(s, false, false) : check_shape(s, gla, true))) return rc;
+        if (kind == K_KDA && kda_f32_unsupported(s, true)) return CLR_ENOTSUP;
+        const size_t need_s = clr_saved_bytes_op(s, saved_op(kind));
         if (need_s && (!saved || saved_bytes < need_s || ((uintptr_t)saved & (ALIGN - 1)))) return CLR_EWORKSPACE;
     }
     const size_t need = clr_workspace_bytes(s, kind == K_KDA ? CLR_OP_KDA_FWD : gla ? CLR_OP_GLA_FWD : CLR_OP_GDN_FWD);
@@ -362,6 +371,7 @@ static int fwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
         L.bf16 = s->dtype == CLR_BF16;
         L.q = q; L.k = k; L.v = v; L.g = g; L.beta = beta; L.S_in = S_in; L.o = o; L.S_out = S_out;
         L.ws = carve_kda(s, false, (char*)ws, nullptr);
+        if (save) saved_carve(s, (char*)saved, &L.saved_h, &L.saved_U);
         return hip_status(launch_kda_fwd(L, st));
     }
     if (!gla) {
@@ -424,6 +434,13 @@ int mamba2_fwd_save(const clr_shape_t* s, const void* q, const void* k, const vo
                       /*save=*/true);
 }
 
+int kda_fwd_save(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+                 const void* beta, const float* S_in, void* o, float* S_out, void* saved, size_t saved_bytes,
+                 void* ws, size_t ws_bytes, void* stream) {
+    return fwd_common(K_KDA, s, q, k, v, g, beta, S_in, o, S_out, ws, ws_bytes, stream, false, saved, saved_bytes,
+                      /*save=*/true);
+}
+
 int kda_fwd(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
             const void* beta, const float* S_in, void* o, float* S_out, void* ws, size_t ws_bytes,
             void* stream) {
@@ -464,7 +481,7 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
                   {ws, ws_bytes, true},           {saved, saved_bytes, false}};
     if ((rc = check_bufs(bufs, 16))) return rc;
     if (use_saved) {
-        const size_t need_s = clr_saved_bytes_op(s, kind == K_GDN ? CLR_OP_GDN_BWD : kind == K_GLA ? CLR_OP_GLA_BWD : CLR_OP_M2_BWD);
+        const size_t need_s = clr_saved_bytes_op(s, saved_op(kind));
         if (need_s && (!saved || saved_bytes < need_s || ((uintptr_t)saved & (ALIGN - 1)))) return CLR_EWORKSPACE;
     }
     const size_t need = clr_workspace_bytes(s, kind == K_KDA ? CLR_OP_KDA_BWD : gla ? CLR_OP_GLA_BWD : CLR_OP_GDN_BWD);
@@ -481,6 +498,7 @@ static int bwd_common(Kind kind, const clr_shape_t* s, const void* q, const void
         L.dS_in = dS_in;
         if (kind == K_KDA) {
             L.ws = carve_kda(s, true, (char*)ws, nullptr);
+            if (use_saved) saved_carve(s, (char*)saved, &L.saved_h, &L.saved_U);
             return hip_status(launch_kda_bwd(L, st));
         }
         L.ws = carve_gdn(s, true, (char*)ws, nullptr);
@@ -537,6 +555,14 @@ int mamba2_bwd(const clr_shape_t* s, const void* q, const void* k, const void* v
                void* stream) {
     return bwd_common(K_M2, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws,
                       ws_bytes, stream);
+}
+
+int kda_bwd_saved(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* S_in, const void* dO, const float* dS_out, const void* saved,
+                  size_t saved_bytes, void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dS_in, void* ws,
+                  size_t ws_bytes, void* stream) {
+    return bwd_common(K_KDA, s, q, k, v, g, beta, S_in, dO, dS_out, dq, dk, dv, dg, dbeta, dS_in, ws, ws_bytes,
+                      stream, saved, saved_bytes, /*use_saved=*/true);
 }
 
 int gla_bwd_saved(const clr_shape_t* s, const void* q, const void* k, const void* v, const void* g,

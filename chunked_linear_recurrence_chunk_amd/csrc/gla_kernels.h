@@ -1326,28 +1326,34 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaPrepArgs<E> a) {
             mma2(acc, frag_col_decay(Ks, PK, Bs, PB, 16 * db, 32 * j, zrow, 1.f, 0, BLK), t1[j]);
         st4(Wout + toff<E>(16 * tb + r, 16 * db + 4 * g, DK), acc);
     }
-    __syncthreads();  // every wave has its T1 rows: V takes T's place
-    store_rows<E, BLK, DV, PV, NT>(vx, Vs);
-    __syncthreads();
-    // Ut = T1 V, stored negated as fp32 -Ut^T (tiled)
-    float* Uout = a.UtT + chunk * BLK * DV;
+    // Ut and Kh^T feed only the forward scan: a backward that reads the
+    // forward's saved states passes them null (a kernel argument: uniform)
+    if (a.UtT) {
+        __syncthreads();  // every wave has its T1 rows: V takes T's place
+        store_rows<E, BLK, DV, PV, NT>(vx, Vs);
+        __syncthreads();
+        // Ut = T1 V, stored negated as fp32 -Ut^T (tiled)
+        float* Uout = a.UtT + chunk * BLK * DV;
 #pragma unroll
-    for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
-        const int tb = tbw, vb = tile / 4;
-        f32x4 acc = zero4();
+        for (int tile = w8; tile < 4 * (DV / 16); tile += 8) {
+            const int tb = tbw, vb = tile / 4;
+            f32x4 acc = zero4();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma2(acc, t1[j], ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
-        *(f32x4*)(Uout + toff<float>(16 * vb + r, 16 * tb + 4 * g, BLK)) = -acc;
+            for (int j = 0; j < 2; ++j) mma2(acc, t1[j], ldfrag_tr(Vs, PV, 32 * j, 16 * vb, l));
+            *(f32x4*)(Uout + toff<float>(16 * vb + r, 16 * tb + 4 * g, BLK)) = -acc;
+        }
     }
-    // Kh^T[d][t] = K[t][d] e^{b_C[d] - b_t[d]} (tiled, hi/lo pair), fragment (db, j)
-    E* KhT = a.KhT + chunk * BLK * DK;
-    E* KhTl = a.KhT_lo + chunk * BLK * DK;
+    if (a.KhT) {
+        // Kh^T[d][t] = K[t][d] e^{b_C[d] - b_t[d]} (tiled, hi/lo pair), fragment (db, j)
+        E* KhT = a.KhT + chunk * BLK * DK;
+        E* KhTl = a.KhT_lo + chunk * BLK * DK;
 #pragma unroll
-    for (int f = w8; f < 2 * ND; f += 8) {
-        const int db = f >> 1, j = f & 1;
-        const Frag2<E> x = frag_col_decay2(Ks, PK, Bs, PB, 16 * db, 32 * j, bC, -1.f, 0, BLK);
-        st_fragT(KhT, f, l, x.hi);
-        if constexpr (sizeof(E) == 2) st_fragT(KhTl, f, l, x.lo);
+        for (int f = w8; f < 2 * ND; f += 8) {
+            const int db = f >> 1, j = f & 1;
+            const Frag2<E> x = frag_col_decay2(Ks, PK, Bs, PB, 16 * db, 32 * j, bC, -1.f, 0, BLK);
+            st_fragT(KhT, f, l, x.hi);
+            if constexpr (sizeof(E) == 2) st_fragT(KhTl, f, l, x.lo);
+        }
     }
 }
 

@@ -378,13 +378,17 @@ hipError_t launch_kda_fwd_t(const GdnLaunch& L, hipStream_t st) {
     GdnScanArgs<E> sa{nullptr, (const E*)ws.W, (const E*)ws.KhT, (const E*)ws.UtT, L.S_in, L.S_out,
                       (E*)ws.hT, nullptr, L.H, L.NC, L.B * L.H};
     sa.eC = ws.eCk;
-    sa.Utok = (E*)ws.Utok;
+    // saved activations: U token-major in the caller's buffer, and the states
+    // once more in the backward's layout (the values its recompute stores)
+    E* Utok = L.saved_U ? (E*)L.saved_U : (E*)ws.Utok;
+    sa.Utok = Utok;
+    sa.hN = (E*)L.saved_h;
     sa.T = L.T;
     sa.KhT_lo = (const E*)ws.KhT_lo;
     launch("kda_scan_fwd", gdn_scan_fwd_kernel<E, DK, DV, false, true, scan_np_fast<1>>,
            dim3(scan_grid(DV / 16, L.B * L.H)), dim3(scan_threads<scan_np_fast<1>, 1>), st, sa);
     if (L.o) {
-        GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)ws.Utok, (const E*)L.g, (const E*)ws.hT,
+        GlaOutArgs<E> oa{(const E*)L.q, (const E*)L.k, (const E*)Utok, (const E*)L.g, (const E*)ws.hT,
                          (E*)L.o, L.T, L.H, L.NC};
         launch("kda_out", gla_out_kernel<E, DK, DV, false>, gblk, dim3(512), st, oa);
     }
@@ -395,8 +399,12 @@ template <typename E, int DK, int DV>
 hipError_t launch_kda_bwd_t(const GdnLaunch& L, hipStream_t st) {
     const dim3 gblk(L.NC, L.H, L.B);
     const GdnWs& ws = L.ws;
+    // with saved states and U the forward recompute (and the operands only it
+    // reads: Ut, Kh^T) drops out
+    const bool saved = L.saved_h != nullptr;
     KdaPrepArgs<E> pa{(const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta, L.T, L.H, L.NC,
-                      ws.eCk, (E*)ws.W, (E*)ws.KhT, (float*)ws.UtT, (E*)ws.KhT_lo};
+                      ws.eCk, (E*)ws.W, saved ? nullptr : (E*)ws.KhT, saved ? nullptr : (float*)ws.UtT,
+                      saved ? nullptr : (E*)ws.KhT_lo};
     pa.range = ws.range;
     pa.TT = (E*)ws.TT;
     pa.M = ws.KKG;
@@ -417,13 +425,19 @@ hipError_t launch_kda_bwd_t(const GdnLaunch& L, hipStream_t st) {
     sb.eC = ws.eCk;
     sb.Kh_lo = (const E*)ws.Kh_lo;
     const int G = (int)scan_grid(DV / 16, L.B * L.H);
-    launch("kda_scan_pair", gdn_scan_pair_kernel<E, DK, DV, true, scan_np_fast<1>, 1>, dim3(2 * G),
-           dim3(scan_threads<scan_np_fast<1>, 1>), st, sa, sb, G);
-    KdaWyArgs<E> wa{(const E*)L.v, (const E*)L.beta, (const E*)ws.hT, (const float*)ws.dUT, (const E*)ws.TT, ws.KKG,
+    if (saved)
+        launch("kda_scan_rev", gdn_scan_rev_kernel<E, DK, DV, true, scan_np_fast<1>, 1>, dim3(G),
+               dim3(scan_threads<scan_np_fast<1>, 1>), st, sb);
+    else
+        launch("kda_scan_pair", gdn_scan_pair_kernel<E, DK, DV, true, scan_np_fast<1>, 1>, dim3(2 * G),
+               dim3(scan_threads<scan_np_fast<1>, 1>), st, sa, sb, G);
+    const E* hT = saved ? (const E*)L.saved_h : (const E*)ws.hT;
+    const E* Utok = saved ? (const E*)L.saved_U : (const E*)ws.Utok;
+    KdaWyArgs<E> wa{(const E*)L.v, (const E*)L.beta, hT, (const float*)ws.dUT, (const E*)ws.TT, ws.KKG,
                     (const E*)ws.Kd, (E*)L.dv_, (E*)L.dbeta, ws.dM, ws.dX, L.T, L.H, L.NC};
     launch("kda_bwd_wy", kda_bwd_wy_kernel<E, DK, DV>, gblk, dim3(512), st, wa);
-    GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, (const E*)ws.Utok, (const E*)L.dO, (const E*)L.g,
-                       (const E*)ws.hT, (const E*)ws.dhT, nullptr, (E*)L.dq, (E*)L.dk_, nullptr, (E*)L.dg,
+    GlaIntraArgs<E> ia{(const E*)L.q, (const E*)L.k, Utok, (const E*)L.dO, (const E*)L.g,
+                       hT, (const E*)ws.dhT, nullptr, (E*)L.dq, (E*)L.dk_, nullptr, (E*)L.dg,
                        L.T, L.H, L.NC};
     ia.dM = ws.dM;
     ia.dX = ws.dX;

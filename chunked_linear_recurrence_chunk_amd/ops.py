@@ -76,10 +76,10 @@ def load(path: Optional[str] = None):
     if hasattr(lib, "gla_fwd_save"):  # the GLA and Mamba-2 saved-activation pairs
         lib.clr_saved_bytes_op.argtypes = [sp, i]
         lib.clr_saved_bytes_op.restype = sz
-        for name in ("gla_fwd_save", "mamba2_fwd_save"):
+        for name in ("gla_fwd_save", "mamba2_fwd_save", "kda_fwd_save"):
             getattr(lib, name).argtypes = [sp] + [vp] * 9 + [sz, vp, sz, vp]
             getattr(lib, name).restype = i
-        for name in ("gla_bwd_saved", "mamba2_bwd_saved"):
+        for name in ("gla_bwd_saved", "mamba2_bwd_saved", "kda_bwd_saved"):
             getattr(lib, name).argtypes = [sp] + [vp] * 9 + [sz] + [vp] * 7 + [sz, vp]
             getattr(lib, name).restype = i
     for name in ("gdn_bwd", "gla_bwd", "mamba2_bwd", "kda_bwd"):
@@ -320,7 +320,7 @@ def saved_bytes(shape: ClrShape, op: int = None) -> int:
     """Bytes of one chunk call's saved activations: clr_saved_bytes (the Gated
     DeltaNet pair: the states entering its blocks and their U) or, with ``op``,
     clr_saved_bytes_op for the member that op names (GLA, Mamba-2: the
-    states)."""
+    states; KDA: the states and U)."""
     if op is None:
         return int(load().clr_saved_bytes(ctypes.byref(shape)))
     return int(load().clr_saved_bytes_op(ctypes.byref(shape), op))
@@ -402,6 +402,19 @@ def gla_bwd_saved(q, k, v, g, S_in, dO, dS_out, saved, ws=None, out=None, check_
     """gla_bwd reading the states gla_fwd_save kept (S_in is not read and may
     be None).  Returns dict dq, dk, dv, dg, dS_in."""
     return _bwd_saved("gla_bwd_saved", OP_GLA_BWD, q, k, v, g, None, S_in, dO, dS_out, saved, ws, out,
+                      check_range)
+
+
+def kda_fwd_save(q, k, v, g, beta, S_in=None, saved=None, ws=None, o=None, S_out=None, check_range=False):
+    """kda_fwd that also keeps the states and U the backward needs: returns
+    (o, S_out, saved) for kda_bwd_saved of the same chunk."""
+    return _fwd_save("kda_fwd_save", OP_KDA_FWD, q, k, v, g, beta, S_in, saved, ws, o, S_out, check_range)
+
+
+def kda_bwd_saved(q, k, v, g, beta, S_in, dO, dS_out, saved, ws=None, out=None, check_range=False):
+    """kda_bwd reading what kda_fwd_save kept (S_in is not read and may be
+    None).  Returns dict dq, dk, dv, dg, dbeta, dS_in."""
+    return _bwd_saved("kda_bwd_saved", OP_KDA_BWD, q, k, v, g, beta, S_in, dO, dS_out, saved, ws, out,
                       check_range)
 
 

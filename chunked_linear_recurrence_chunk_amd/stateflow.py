@@ -36,8 +36,8 @@ class GdnChunked:
     With ``save=True`` each chunk's forward also keeps the activations its
     backward needs (gdn_fwd_save), and the backward reads them (gdn_bwd_saved)
     instead of recomputing the chunk's forward from S^in: more device memory
-    (clr_saved_bytes per chunk until its backward), less work.  The GLA and
-    Mamba-2 drivers below take the same flag; the KDA driver does not."""
+    (clr_saved_bytes per chunk until its backward), less work.  The GLA,
+    Mamba-2 and KDA drivers below take the same flag."""
 
     kind = "gdn"
     _names = ("gdn_fwd", "gdn_bwd", "OP_GDN_FWD", "OP_GDN_BWD")
@@ -58,8 +58,7 @@ class GdnChunked:
         nbytes = max(ops.workspace_bytes(shape, getattr(ops, op_f)), ops.workspace_bytes(shape, getattr(ops, op_b)))
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         self.saved = [None] * N
-        if save and self.kind != "gdn":
-            raise ValueError("saved activations exist for the Gated DeltaNet, GLA and Mamba-2 layers only")
+        self._fwd_save, self._bwd_saved = getattr(ops, fwd + "_save"), getattr(ops, bwd + "_saved")
         self.save = save
         self.acts = [None] * N  # per chunk: the activations gdn_fwd_save kept
 
@@ -81,7 +80,7 @@ class GdnChunked:
             view = o[:, a:b]
             ov = view if view.is_contiguous() else None
             if self.save:
-                oi, S, self.acts[i] = self.ops.gdn_fwd_save(*self._chunk(i), S, ws=self.ws, o=ov)
+                oi, S, self.acts[i] = self._fwd_save(*self._chunk(i), S, ws=self.ws, o=ov)
             else:
                 oi, S = self._fwd(*self._chunk(i), S, ws=self.ws, o=ov)
             if oi.data_ptr() != view.data_ptr():
@@ -101,8 +100,8 @@ class GdnChunked:
             views = {key: grads[key][:, a:b] for key in ("dq", "dk", "dv", "dg", "dbeta")}
             out = {key: t for key, t in views.items() if t.is_contiguous()}
             if self.save:
-                r = self.ops.gdn_bwd_saved(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, self.acts[i],
-                                           ws=self.ws, out=out)
+                r = self._bwd_saved(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, self.acts[i],
+                                    ws=self.ws, out=out)
                 self.acts[i] = None
             else:
                 r = self._bwd(*self._chunk(i), self.saved[i], _sl(dO, a, b), dS, ws=self.ws, out=out)

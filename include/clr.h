@@ -218,18 +218,19 @@ int mamba2_bwd(const clr_shape_t* shape, const void* q, const void* k, const voi
                const float* dS_out, void* dq, void* dk, void* dv, void* dg, void* dbeta,
                float* dS_in, void* ws, size_t ws_bytes, void* stream);
 
-/* GLA and Mamba-2 forward and backward with saved activations (StateFlow
+/* GLA, Mamba-2 and KDA forward and backward with saved activations (StateFlow
  * paper, Sec. 3.1, "Backward Computation": a chunk's intermediate activations
  * kept from its forward instead of recomputed from its boundary state).  The
  * backward needs the state entering every 64-token block; gla_bwd and
  * mamba2_bwd recompute it from S_in, the pairs below keep it.
  *   clr_saved_bytes_op(shape, op): bytes of one chunk call's saved
  *     activations for the member that op names (CLR_OP_GDN_*, CLR_OP_GLA_*,
- *     CLR_OP_M2_*; the forward and backward of a member give the same
- *     figure), for the shapes that member's backward supports; 0 otherwise,
- *     for the KDA ops, and when T == 0.  GLA and Mamba-2: per 64-token block
- *     one dk x dv state in shape.dtype.  With the Gated DeltaNet ops it
- *     equals clr_saved_bytes.
+ *     CLR_OP_M2_*, CLR_OP_KDA_*; the forward and backward of a member give
+ *     the same figure), for the shapes that member's backward supports; 0
+ *     otherwise and when T == 0.  GLA and Mamba-2: per 64-token block one
+ *     dk x dv state in shape.dtype.  KDA: the states and the delta-rule
+ *     values U, the same size as clr_saved_bytes.  With the Gated DeltaNet
+ *     ops it equals clr_saved_bytes.
  *   gla_fwd_save / mamba2_fwd_save: gla_fwd / mamba2_fwd (same results, bit
  *     for bit) that also write the states into `saved` (device memory of at
  *     least clr_saved_bytes_op, 256-byte aligned, owned by the caller; its
@@ -240,6 +241,9 @@ int mamba2_bwd(const clr_shape_t* shape, const void* q, const void* k, const voi
  *     read (it may be NULL).  The saved states are those the recompute
  *     forms, bit for bit, so the results equal gla_bwd's / mamba2_bwd's bit
  *     for bit.  Workspace: CLR_OP_GLA_BWD / CLR_OP_M2_BWD.
+ *   kda_fwd_save / kda_bwd_saved: the same for the KDA member (states and
+ *     U kept; the results equal kda_fwd's / kda_bwd's bit for bit).
+ *     Workspace: CLR_OP_KDA_FWD / CLR_OP_KDA_BWD.
  * Errors as for the Gated DeltaNet pair: CLR_EWORKSPACE for a missing, small
  * or misaligned `saved`, CLR_EINVAL when it overlaps another buffer. */
 size_t clr_saved_bytes_op(const clr_shape_t* shape, int op);
@@ -259,6 +263,14 @@ int mamba2_bwd_saved(const clr_shape_t* shape, const void* q, const void* k, con
                      const float* dS_out, const void* saved, size_t saved_bytes, void* dq, void* dk,
                      void* dv, void* dg, void* dbeta, float* dS_in, void* ws, size_t ws_bytes,
                      void* stream);
+int kda_fwd_save(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+                 const void* g, const void* beta, const float* S_in, void* o, float* S_out,
+                 void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+int kda_bwd_saved(const clr_shape_t* shape, const void* q, const void* k, const void* v,
+                  const void* g, const void* beta, const float* S_in, const void* dO,
+                  const float* dS_out, const void* saved, size_t saved_bytes, void* dq, void* dk,
+                  void* dv, void* dg, void* dbeta, float* dS_in, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /* KDA member of the family (StateFlow paper, Sec. 2.1, Eq. 1: F_t
  * diagonal-plus-low-rank), key-major:

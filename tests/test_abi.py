@@ -365,7 +365,9 @@ def test_gla_saved_activation_entry_points_reject_on_the_host(member):
     assert ops.saved_bytes(_shape(ops, T=0), op_f) == 0
     assert ops.saved_bytes(_shape(ops, dk=128, dv=128, dtype=0), op_b) == 0   # no fp32 backward at d = 128
     assert ops.saved_bytes(_shape(ops, dk=96, dv=96), op_f) == 0
-    assert ops.saved_bytes(s, ops.OP_KDA_FWD) == 0 and ops.saved_bytes(s, ops.OP_KDA_BWD) == 0
+    # KDA keeps the states and U: the Gated DeltaNet pair's size
+    assert ops.saved_bytes(s, ops.OP_KDA_FWD) == ops.saved_bytes(s, ops.OP_KDA_BWD) == ops.saved_bytes(s)
+    assert ops.saved_bytes(_shape(ops, dk=128, dv=128, dtype=0), ops.OP_KDA_BWD) == 0  # fp32 KDA: d <= 64
     assert ops.saved_bytes(s, 99) == 0
     g16 = ops.ClrShape(1, 64, 1, 128, 128, 1)
     assert ops.saved_bytes(g16, ops.OP_GDN_FWD) == ops.saved_bytes(g16)
@@ -404,3 +406,38 @@ def test_gla_saved_activation_entry_points_reject_on_the_host(member):
     bad = list(outs)
     bad[4] = P_(0xC0000)
     assert bwd(0xF0000, n, bad) == ops.CLR_EINVAL                # dbeta given
+
+
+def test_kda_saved_activation_entry_points_reject_on_the_host():
+    """kda_fwd_save / kda_bwd_saved: host-side rejections (every call below
+    fails validation, so nothing is launched)."""
+    ops, lib = _lib()
+    s = _shape(ops, T=64, H=1, dk=32, dv=32)
+    n = ops.saved_bytes(s, ops.OP_KDA_FWD)
+    assert n == 2048 + 4096
+    P_ = _fake
+    # fwd: q k v g beta S_in o S_out | saved, nsaved | ws, nws
+    base = [P_(0x10000), P_(0x20000), P_(0x30000), P_(0x40000), P_(0x50000), None, P_(0x60000), P_(0x70000)]
+
+    def fwd(saved, nsaved, ws=0x100000):
+        return lib.kda_fwd_save(ctypes.byref(s), *base, None if saved is None else P_(saved), nsaved,
+                                None if ws is None else P_(ws), 1 << 40, None)
+    assert fwd(None, 0) == ops.CLR_EWORKSPACE
+    assert fwd(0xA0000, n - 256) == ops.CLR_EWORKSPACE
+    assert fwd(0xA0010, n) == ops.CLR_EWORKSPACE
+    assert fwd(0x60000, n) == ops.CLR_EINVAL                     # overlaps the output o
+    assert fwd(0xA0000, n, ws=None) == ops.CLR_EWORKSPACE
+    s128 = _shape(ops, T=64, H=1, dk=128, dv=128, dtype=0)        # fp32 KDA at d = 128: unsupported
+    assert lib.kda_fwd_save(ctypes.byref(s128), *base, P_(0xA0000), 1 << 20, P_(0x100000), 1 << 40,
+                            None) == ops.CLR_ENOTSUP
+    outs = [P_(0x80000 + 0x10000 * i) for i in range(6)]
+
+    def bwd(saved, nsaved, o=outs):
+        return lib.kda_bwd_saved(ctypes.byref(s), *base[:6], P_(0x60000), P_(0x70000),
+                                 None if saved is None else P_(saved), nsaved, *o, P_(0x100000), 1 << 40, None)
+    assert bwd(None, 0) == ops.CLR_EWORKSPACE
+    assert bwd(0xF0000, n - 256) == ops.CLR_EWORKSPACE
+    assert bwd(0x80000, n) == ops.CLR_EINVAL                     # overlaps the output dq
+    bad = list(outs)
+    bad[4] = None
+    assert bwd(0xF0000, n, bad) == ops.CLR_EINVAL                # dbeta missing
